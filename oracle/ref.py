@@ -1,0 +1,390 @@
+"""Plain fp64 CPU oracle of the TokenGate gated-prefill step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only the tests, the package smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library.
+
+Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill with
+Learned Token Pruning" (Patel, Ranjan, Stoica, Zaharia, Guestrin), cited
+below as [TG] with its section and equation numbers.  Equation numbers are
+recovered by order of appearance (Eq. 1-2 in §3, Eq. 3-4 in §4.1, Eq. 5-8 in
+§4.2, Eq. 9-10 in §4.3).
+
+Every function computes the plain definition in float64 with numpy; there
+is no blocking, fusion or reordering beyond splitting query rows into
+batches to bound memory.  Where the pages leave a step open, the reading is
+named in the docstring (R-numbers match ``readings.py``).
+
+Pinning status: every function here is pinned by the not-gpu tests against
+closed forms, library routines, independent formulations of the paper's
+equations or brute force -- except the two documented readings marked
+"parity unpinned" in ``readings.py`` (the length factor of the temperature
+and the value of epsilon), whose only pinned consequence is that the length
+factor is 1 when nothing is pruned.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import readings as R
+
+
+# ---------------------------------------------------------------------------
+# gate module: scoring network and normalisation ([TG] §4.1, Eq. 3)
+# ---------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def ref_score(x: np.ndarray, w1: np.ndarray, b1: Optional[np.ndarray],
+              w2: np.ndarray, b2: float) -> np.ndarray:
+    """Raw gate scores b~_j = MLP_theta(a~_j^L), [TG] §4.1 Eq. 3 (left part).
+
+    The pages call the scorer a small MLP without giving its shape (R4); the
+    workloads fix it as d -> h (SiLU) -> 1 with biases:
+        u_j  = SiLU(W1 x_j + b1)          (w1 is [h, d], row = hidden unit)
+        b~_j = w2 . u_j + b2
+    x holds the scorer's input rows a~^L = LN2(a^L) directly (R5).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    pre = x @ w1.T
+    if b1 is not None:
+        pre = pre + np.asarray(b1, dtype=np.float64)[None, :]
+    u = silu(pre)
+    return u @ np.asarray(w2, dtype=np.float64) + float(b2)
+
+
+def ref_normalise(b_raw: np.ndarray, prunable: np.ndarray, cu_seqlens: Sequence[int],
+                  eps: float = R.EPS) -> Tuple[np.ndarray, np.ndarray]:
+    """Normalised scores, [TG] §4.1 Eq. 3 (right part), per sequence s:
+
+        r_s = sqrt( (1/|P_s|) * sum_{j in P_s} b~_j^2 + eps )     (R2: RMS)
+        b_j = b~_j / r_s   for j in P_s,     b_j = 0 for j in N_s (prompt).
+
+    A sequence with no prunable token has every b_j = 0 and r_s = 1.
+    Returns (b, r) with r one value per sequence.
+    """
+    b_raw = np.asarray(b_raw, dtype=np.float64)
+    prunable = np.asarray(prunable).astype(bool)
+    b = np.zeros_like(b_raw)
+    r = np.ones(len(cu_seqlens) - 1)
+    for s in range(len(cu_seqlens) - 1):
+        lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        P = np.nonzero(prunable[lo:hi])[0] + lo
+        if P.size == 0:
+            continue
+        mean_sq = np.mean(b_raw[P] ** 2)
+        r[s] = math.sqrt(mean_sq + eps)
+        b[P] = b_raw[P] / r[s]
+    return b, r
+
+
+# ---------------------------------------------------------------------------
+# top-K selector ([TG] §4.1 Eq. 4)
+# ---------------------------------------------------------------------------
+def rank_order(values: np.ndarray, index: np.ndarray) -> np.ndarray:
+    """Permutation that sorts candidates best-first under the strict order
+    (value descending, index ascending), with -0.0 equal to +0.0 and NaN
+    ranked below -inf (R11).  ``np.lexsort`` takes its last key as primary."""
+    v = np.asarray(values, dtype=np.float64).copy()
+    nan = np.isnan(v)
+    v[nan] = 0.0
+    v = v + 0.0                      # -0.0 -> +0.0
+    return np.lexsort((np.asarray(index), -v, nan.astype(np.int8)))
+
+
+def ref_select(b: np.ndarray, prunable: np.ndarray, cu_seqlens: Sequence[int],
+               k: Sequence[int]):
+    """Kept set S_s = top-K_{j in P_s}(b_j)  U  N_s, [TG] §4.1 Eq. 4.
+
+    K counts prunable tokens only (R12): K' = min(K_s, |P_s|); K >= |P_s| keeps
+    every document token, K = 0 keeps the prompt only; K < 0 is an error.
+    Ties are broken by lower index (R11).  The kept tokens of each sequence
+    are emitted in ascending original index (R14), sequences in input order.
+
+    Returns (kept_idx, kept_pos, kept_b, kept_cu_seqlens):
+      kept_idx -- global token index, kept_pos -- index within its sequence,
+      kept_b   -- b at the kept token, kept_cu_seqlens -- offsets per sequence.
+    """
+    b = np.asarray(b)
+    prunable = np.asarray(prunable).astype(bool)
+    idx_all, cu = [], [0]
+    for s in range(len(cu_seqlens) - 1):
+        lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        ks = int(k[s])
+        if ks < 0:
+            raise ValueError("budget K must be >= 0")
+        seq = np.arange(lo, hi)
+        P = seq[prunable[lo:hi]]
+        Nset = seq[~prunable[lo:hi]]
+        kp = min(ks, P.size)
+        top = P[rank_order(b[P], P)[:kp]]
+        S = np.sort(np.concatenate([top, Nset]))
+        idx_all.append(S)
+        cu.append(cu[-1] + S.size)
+    kept_idx = np.concatenate(idx_all).astype(np.int64) if idx_all else np.zeros(0, np.int64)
+    seq_of = np.searchsorted(np.asarray(cu_seqlens), kept_idx, side="right") - 1
+    kept_pos = kept_idx - np.asarray(cu_seqlens)[seq_of]
+    return kept_idx, kept_pos, b[kept_idx], np.asarray(cu, dtype=np.int64)
+
+
+def ref_kept_sizes(cu_seqlens: Sequence[int], n_prunable: Sequence[int],
+                   k: Sequence[int]) -> np.ndarray:
+    """|S_s| = min(K_s, |P_s|) + |N_s| as offsets (Eq. 4 with R12)."""
+    cu = [0]
+    for s in range(len(cu_seqlens) - 1):
+        n = int(cu_seqlens[s + 1]) - int(cu_seqlens[s])
+        cu.append(cu[-1] + min(int(k[s]), int(n_prunable[s])) + n - int(n_prunable[s]))
+    return np.asarray(cu, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# compaction of the kept rows ([TG] §4.1: pruned residuals stop at layer L)
+# ---------------------------------------------------------------------------
+def ref_gather(src: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """X_S = X[S]: the kept rows, in kept order, copied unchanged."""
+    return np.asarray(src)[np.asarray(idx, dtype=np.int64)].copy()
+
+
+# ---------------------------------------------------------------------------
+# token-gated attention ([TG] §4.2 Eq. 5-8)
+# ---------------------------------------------------------------------------
+def length_factor(m: np.ndarray, p: np.ndarray, mode: str = R.LEN_SCALE) -> np.ndarray:
+    """The length term of the temperature in [TG] Eq. 7 (R6).
+
+    m = kept keys visible to the query (itself included), p = the query's
+    1-based original position in its sequence.
+      "log_ratio": log m / log max(2, p)   (the reading used everywhere)
+      "swap":      log p / log max(2, m)   (rejected alternative, for study)
+      "off":       1
+    """
+    m = np.asarray(m, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    if mode == "log_ratio":
+        return np.log(m) / np.log(np.maximum(2.0, p))
+    if mode == "swap":
+        return np.log(p) / np.log(np.maximum(2.0, m))
+    if mode == "off":
+        return np.ones_like(m)
+    raise ValueError(mode)
+
+
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    mx = np.max(logits, axis=-1, keepdims=True)
+    e = np.exp(logits - mx)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def ref_gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
+                   sm_scale: Optional[float] = None, len_scale: str = R.LEN_SCALE,
+                   rows: Optional[np.ndarray] = None, row_block: int = 512) -> np.ndarray:
+    """Token-gated causal attention over the kept tokens, [TG] Eq. 8:
+
+        alpha_ij = softmax_{j in S, j <= i} ( tau_i^h * ( s * q_i.k_j + gain_h * b_j ) )
+        tau_i^h  = temp_h * length_factor(m_i, p_i)                (Eq. 7, R6)
+        O_i^h    = sum_j alpha_ij v_j
+
+    s = 1/sqrt(d_head) (R1); gain and temp are the post-softplus values (R7);
+    query head h reads KV head floor(h / (Hq/Hkv)) (R9); causality is by
+    original position, which equals compacted order because S is ascending
+    (R10).  m_i = compacted index within the sequence + 1, p_i = kept_pos + 1.
+
+    q: [T, Hq, dh], k/v: [T, Hkv, dh]; kept_b: [T]; kept_pos: [T] or None
+    (None means length factor 1); kept_cu: [n_seq+1].
+    ``rows``: optional global row indices to evaluate (others are left 0).
+    Returns O: [T, Hq, dh] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    kb = np.asarray(kept_b, dtype=np.float64)
+    T, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else float(sm_scale)
+    out = np.zeros((T, Hq, dh))
+    want = None if rows is None else set(int(r) for r in rows)
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        a = np.arange(n)
+        m = a + 1.0
+        if kept_pos is None:
+            lam = np.ones(n)
+        else:
+            p = np.asarray(kept_pos[lo:hi], dtype=np.float64) + 1.0
+            lam = length_factor(m, p, len_scale)
+        sel = a if want is None else np.array([r - lo for r in range(lo, hi) if r in want],
+                                               dtype=np.int64)
+        for h in range(Hq):
+            kv = h // G
+            K = k[lo:hi, kv, :]
+            V = v[lo:hi, kv, :]
+            bias = float(gain[h]) * kb[lo:hi]
+            for c0 in range(0, sel.size, row_block):
+                rr = sel[c0:c0 + row_block]
+                if rr.size == 0:
+                    continue
+                last = int(rr.max()) + 1                  # keys beyond are all masked
+                z = scale * (q[lo + rr, h, :] @ K[:last].T) + bias[None, :last]
+                tau = float(temp[h]) * lam[rr]
+                logits = tau[:, None] * z
+                logits[np.arange(last)[None, :] > rr[:, None]] = -np.inf
+                out[lo + rr, h, :] = _softmax_rows(logits) @ V[:last]
+    return out
+
+
+# --- independent formulations used to pin ref_gated_attn ------------------
+def ref_gated_attn_masked(q_full, k_full, v_full, b_full, keep_mask, cu_seqlens, gain, temp,
+                          sm_scale=None, len_scale: str = R.LEN_SCALE):
+    """Mask form of [TG] Eq. 8 on the full, uncompacted sequence: keys outside S
+    get -inf, m_i = #{j in S_s : j <= i}, p_i = i - start + 1; evaluated on the
+    rows of S only (other rows are returned as NaN)."""
+    q_full = np.asarray(q_full, np.float64)
+    k_full = np.asarray(k_full, np.float64)
+    v_full = np.asarray(v_full, np.float64)
+    N, Hq, dh = q_full.shape
+    G = Hq // k_full.shape[1]
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else sm_scale
+    out = np.full((N, Hq, dh), np.nan)
+    keep_mask = np.asarray(keep_mask).astype(bool)
+    for s in range(len(cu_seqlens) - 1):
+        lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        km = keep_mask[lo:hi]
+        counts = np.cumsum(km)                       # m_i for every position
+        pos = np.arange(1, hi - lo + 1, dtype=np.float64)
+        lam = length_factor(counts.astype(np.float64).clip(min=1), pos, len_scale)
+        for h in range(Hq):
+            kv = h // G
+            z = scale * q_full[lo:hi, h] @ k_full[lo:hi, kv].T + gain[h] * b_full[lo:hi][None, :]
+            logits = (temp[h] * lam)[:, None] * z
+            allowed = np.tril(np.ones((hi - lo, hi - lo), bool)) & km[None, :]
+            logits = np.where(allowed, logits, -np.inf)
+            rows = np.nonzero(km)[0]
+            out[lo + rows, h] = _softmax_rows(logits[rows]) @ v_full[lo:hi, kv]
+    return out
+
+
+def ref_gated_attn_multiplicative(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
+                                  sm_scale=None, len_scale: str = R.LEN_SCALE):
+    """[TG] Eq. 5 with the head-wise gate of Eq. 6 and the temperature of Eq. 7
+    applied as a power of the gate value:
+
+        g_j^h  = softmax_{j in S}( gain_h * b_j )              (over the whole S_s)
+        alpha_ij ∝ exp(tau_i * s * q_i.k_j) * (g_j^h)^tau_i,   j <= i
+
+    Equal to Eq. 8 because the softmax normaliser of g is constant in j."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, Hq, dh = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else sm_scale
+    out = np.zeros_like(q)
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        m = np.arange(1, n + 1, dtype=np.float64)
+        p = np.asarray(kept_pos[lo:hi], np.float64) + 1.0
+        lam = length_factor(m, p, len_scale)
+        for h in range(Hq):
+            gb = gain[h] * np.asarray(kept_b[lo:hi], np.float64)
+            g = np.exp(gb - gb.max())
+            g = g / g.sum()
+            tau = temp[h] * lam
+            for i in range(n):
+                w = np.exp(tau[i] * scale * (k[lo:lo + i + 1, h // G] @ q[lo + i, h]))
+                w = w * g[:i + 1] ** tau[i]
+                out[lo + i, h] = (w / w.sum()) @ v[lo:lo + i + 1, h // G]
+    return out
+
+
+def ref_gated_attn_loggate(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
+                           sm_scale=None, len_scale: str = R.LEN_SCALE):
+    """Additive-bias form: logits tau_i * (s q.k + gain_h * log g_j) with
+    g = softmax_{j in S}(b) taken once over the whole kept set S_s."""
+    q = np.asarray(q, np.float64)
+    kb = np.asarray(kept_b, np.float64)
+    T = q.shape[0]
+    logg = np.zeros(T)
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        if hi > lo:
+            z = kb[lo:hi]
+            mx = z.max()
+            logg[lo:hi] = z - (mx + math.log(np.sum(np.exp(z - mx))))
+    return ref_gated_attn(q, k, v, logg, kept_pos, kept_cu, gain, temp, sm_scale, len_scale)
+
+
+def ref_gated_attn_bruteforce(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
+                              sm_scale=None, len_scale: str = R.LEN_SCALE):
+    """Explicit scalar loops over (sequence, head, query, key), for tiny T."""
+    T, Hq, dh = np.shape(q)
+    Hkv = np.shape(k)[1]
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else sm_scale
+    out = np.zeros((T, Hq, dh))
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        for h in range(Hq):
+            kvh = (h * Hkv) // Hq
+            for i in range(lo, hi):
+                m = i - lo + 1
+                p = int(kept_pos[i]) + 1
+                if len_scale == "log_ratio":
+                    lam = math.log(m) / math.log(max(2, p))
+                elif len_scale == "swap":
+                    lam = math.log(p) / math.log(max(2, m))
+                else:
+                    lam = 1.0
+                tau = float(temp[h]) * lam
+                logits = []
+                for j in range(lo, i + 1):
+                    dot = 0.0
+                    for e in range(dh):
+                        dot += float(q[i][h][e]) * float(k[j][kvh][e])
+                    logits.append(tau * (scale * dot + float(gain[h]) * float(kept_b[j])))
+                mx = max(logits)
+                w = [math.exp(t - mx) for t in logits]
+                tot = sum(w)
+                for e in range(dh):
+                    acc = 0.0
+                    for jj, j in enumerate(range(lo, i + 1)):
+                        acc += w[jj] * float(v[j][kvh][e])
+                    out[i, h, e] = acc / tot
+    return out
+
+
+# ---------------------------------------------------------------------------
+# harness-level projection (outside the four library calls)
+# ---------------------------------------------------------------------------
+def ref_project(xs: np.ndarray, wq, wk, wv, hq: int, hkv: int, dh: int):
+    """Q = X_S Wq, K = X_S Wk, V = X_S Wv in fp64, reshaped to heads."""
+    xs = np.asarray(xs, np.float64)
+    T = xs.shape[0]
+    q = (xs @ np.asarray(wq, np.float64)).reshape(T, hq, dh)
+    k = (xs @ np.asarray(wk, np.float64)).reshape(T, hkv, dh)
+    v = (xs @ np.asarray(wv, np.float64)).reshape(T, hkv, dh)
+    return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# whole step
+# ---------------------------------------------------------------------------
+def ref_gate(x, w1, b1, w2, b2, prunable, cu_seqlens, k, eps: float = R.EPS):
+    """Score -> normalise -> select -> gather for one gated layer."""
+    b_raw = ref_score(x, w1, b1, w2, b2)
+    b, _ = ref_normalise(b_raw, prunable, cu_seqlens, eps)
+    kept_idx, kept_pos, kept_b, kept_cu = ref_select(b.astype(np.float32), prunable,
+                                                     cu_seqlens, k)
+    return b_raw, b, kept_idx, kept_pos, kept_b, kept_cu, ref_gather(x, kept_idx)

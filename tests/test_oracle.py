@@ -1,0 +1,428 @@
+"""Pins of the fp64 oracle against what the TokenGate pages and plain
+mathematics fix: closed forms, library routines, independent formulations of
+the paper's equations, invariants and brute force.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import readings as R
+from workloads import generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# scoring network ([TG] §4.1 Eq. 3, scorer shape from the workloads)
+# ---------------------------------------------------------------------------
+def test_silu_special_values():
+    assert O.silu(0.0) == 0.0
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert O.silu(-1.0) == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)
+    assert O.silu(800.0) == 800.0          # sigmoid saturates to 1
+    assert O.silu(-800.0) == 0.0           # e^800 overflows: z / inf = -0
+
+
+def test_score_one_hot_picks_silu_of_one_input():
+    rng = _rng(1)
+    T, d, h = 37, 12, 5
+    x = rng.standard_normal((T, d))
+    w1 = np.zeros((h, d))
+    w1[3, 7] = 1.0                      # hidden unit 3 reads input 7
+    w2 = np.zeros(h)
+    w2[3] = 1.0
+    b1 = np.zeros(h)
+    got = O.ref_score(x, w1, b1, w2, 0.0)
+    assert np.array_equal(got, x[:, 7] / (1.0 + np.exp(-x[:, 7])))
+    # biases enter before (b1) and after (b2) the activation
+    b1[3] = 0.25
+    got = O.ref_score(x, w1, b1, w2, -2.0)
+    z = x[:, 7] + 0.25
+    assert np.allclose(got, z / (1.0 + np.exp(-z)) - 2.0, rtol=0, atol=1e-15)
+
+
+def test_score_matches_torch_fp64():
+    rng = _rng(2)
+    T, d, h = 50, 24, 9
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((h, d))
+    b1 = rng.standard_normal(h)
+    w2 = rng.standard_normal(h)
+    lin1 = torch.nn.Linear(d, h).double()
+    lin2 = torch.nn.Linear(h, 1).double()
+    with torch.no_grad():
+        lin1.weight.copy_(torch.from_numpy(w1))
+        lin1.bias.copy_(torch.from_numpy(b1))
+        lin2.weight.copy_(torch.from_numpy(w2)[None])
+        lin2.bias.fill_(0.3)
+        want = lin2(torch.nn.functional.silu(lin1(torch.from_numpy(x))))[:, 0].numpy()
+    got = O.ref_score(x, w1, b1, w2, 0.3)
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# normalisation (Eq. 3, RMS reading R2)
+# ---------------------------------------------------------------------------
+def test_normalise_closed_forms():
+    b_raw = np.array([3.0, 4.0, 100.0, -7.0])
+    prunable = np.array([1, 1, 0, 0], np.uint8)
+    b, r = O.ref_normalise(b_raw, prunable, [0, 4], eps=0.0)
+    assert r[0] == math.sqrt(12.5)
+    assert b[0] == 3.0 / math.sqrt(12.5) and b[1] == 4.0 / math.sqrt(12.5)
+    assert b[2] == 0.0 and b[3] == 0.0                   # prompt tokens: b := 0
+    rng = _rng(3)
+    x = rng.standard_normal(200) * 3.0
+    pr = (rng.random(200) < 0.8).astype(np.uint8)
+    for eps in (0.0, 1e-6, 0.5):
+        b, _ = O.ref_normalise(x, pr, [0, 200], eps)
+        P = pr.astype(bool)
+        M = np.mean(x[P] ** 2)
+        assert np.mean(b[P] ** 2) == pytest.approx(M / (M + eps), rel=1e-13)
+        assert np.all(b[~P] == 0.0)
+    # positive rescaling of the scorer output leaves b unchanged when eps = 0
+    b1, _ = O.ref_normalise(x, pr, [0, 200], 0.0)
+    b2, _ = O.ref_normalise(7.5 * x, pr, [0, 200], 0.0)
+    assert np.allclose(b1, b2, rtol=1e-14, atol=0)
+    # all-zero raw scores give all-zero b
+    bz, _ = O.ref_normalise(np.zeros(10), np.ones(10, np.uint8), [0, 10], 1e-6)
+    assert np.all(bz == 0.0)
+
+
+def test_normalise_is_per_sequence():
+    x = np.array([1.0, 1.0, 10.0, 10.0, 10.0])
+    pr = np.ones(5, np.uint8)
+    b, r = O.ref_normalise(x, pr, [0, 2, 5], eps=0.0)
+    assert np.allclose(b, 1.0) and np.allclose(r, [1.0, 10.0])
+    # a sequence with no prunable token: nothing to normalise, b = 0
+    b, r = O.ref_normalise(x, np.array([0, 0, 1, 1, 1], np.uint8), [0, 2, 5], 0.0)
+    assert b[0] == 0.0 and b[1] == 0.0 and r[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# top-K selector (Eq. 4, readings R11, R12, R14)
+# ---------------------------------------------------------------------------
+def _beats(bt, t, bu, u):
+    """t ranks strictly before u: larger value first, NaN last, lower index on ties."""
+    nt, nu = math.isnan(bt), math.isnan(bu)
+    if nt != nu:
+        return nu
+    if not nt and bt != bu:
+        return bt > bu
+    return t < u
+
+
+def _brute_select(b, prunable, k):
+    P = [j for j in range(len(b)) if prunable[j]]
+    Nset = [j for j in range(len(b)) if not prunable[j]]
+    kp = min(k, len(P))
+    found = []
+    for T in itertools.combinations(P, kp):
+        rest = [u for u in P if u not in T]
+        if all(_beats(b[t], t, b[u], u) for t in T for u in rest):
+            found.append(T)
+    assert len(found) == 1                  # the strict order makes the subset unique
+    return sorted(list(found[0]) + Nset)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_select_bruteforce_small(seed):
+    rng = _rng(100 + seed)
+    n = int(rng.integers(1, 11))
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 0.5, 0.5])
+    b = rng.choice(pool, n) if seed % 2 else rng.standard_normal(n).round(1)
+    pr = (rng.random(n) < 0.7).astype(np.uint8)
+    for k in range(0, n + 2):
+        idx, pos, kb, cu = O.ref_select(b, pr, [0, n], [k])
+        assert list(idx) == _brute_select(list(b), list(pr), k)
+        assert np.array_equal(pos, idx)
+        assert cu[-1] == len(idx)
+
+
+def test_select_invariants_and_special_cases():
+    rng = _rng(7)
+    cu = [0, 50, 50, 130, 131]
+    n = cu[-1]
+    b = rng.standard_normal(n)
+    b[rng.random(n) < 0.1] = -np.inf
+    b[rng.random(n) < 0.05] = np.nan
+    pr = (rng.random(n) < 0.75).astype(np.uint8)
+    for ks in ([0, 0, 0, 0], [3, 5, 10, 1], [1000, 1, 1000, 1000], [40, 0, 2, 0]):
+        idx, pos, kb, kcu = O.ref_select(b, pr, cu, ks)
+        for s in range(4):
+            lo, hi = cu[s], cu[s + 1]
+            sel = idx[kcu[s]:kcu[s + 1]]
+            assert np.all((sel >= lo) & (sel < hi))
+            assert np.all(np.diff(sel) > 0)                       # ascending (R14)
+            nP = int(pr[lo:hi].sum())
+            prompt = np.arange(lo, hi)[pr[lo:hi] == 0]
+            assert set(prompt) <= set(sel)                         # prompt always kept
+            assert sel.size == min(ks[s], nP) + (hi - lo - nP)
+            assert np.array_equal(pos[kcu[s]:kcu[s + 1]], sel - lo)
+        assert np.array_equal(kcu, O.ref_kept_sizes(cu, [int(pr[cu[s]:cu[s + 1]].sum())
+                                                         for s in range(4)], ks))
+        assert np.array_equal(kb, b[idx], equal_nan=True)
+    # all-equal scores keep the first K document tokens
+    idx, *_ = O.ref_select(np.full(20, 0.3), np.ones(20, np.uint8), [0, 20], [6])
+    assert list(idx) == list(range(6))
+    # -0.0 and +0.0 are equal: the lower index wins
+    idx, *_ = O.ref_select(np.array([-0.0, 0.0, -0.0]), np.ones(3, np.uint8), [0, 3], [1])
+    assert list(idx) == [0]
+    with pytest.raises(ValueError):
+        O.ref_select(b, pr, cu, [-1, 0, 0, 0])
+
+
+def test_select_preset_budget_sweep_spikes_and_ties():
+    g = generate(2, with_x=False, with_proj=False)
+    b = g["b_preset"]
+    pr = g["prunable"]
+    n_doc = int(pr.sum())
+    spikes = np.nonzero(b == 6.0)[0]
+    assert spikes.size == round(0.05 * n_doc)
+    for kk in g["budgets"]:
+        idx, pos, kb, cu = O.ref_select(b, pr, g["cu_seqlens"], kk)
+        k = int(kk[0])
+        doc_kept = idx[idx < n_doc]
+        assert doc_kept.size == k
+        assert np.all(idx[doc_kept.size:] == np.arange(n_doc, b.size))
+        above = np.nonzero(b[:n_doc] > 6.0)[0]      # rare Gaussian draws beyond the spikes
+        if above.size <= k <= above.size + spikes.size:
+            # every +6 spike ties: after the larger values, the lowest indices win
+            want = np.sort(np.concatenate([above, spikes[:k - above.size]]))
+            assert np.array_equal(doc_kept, want)
+
+
+# ---------------------------------------------------------------------------
+# gather
+# ---------------------------------------------------------------------------
+def test_gather_bytewise_and_identity():
+    rng = _rng(9)
+    src = rng.integers(0, 2 ** 16, (40, 24), dtype=np.uint16)
+    idx = np.array([0, 3, 3, 39, 17])
+    out = O.ref_gather(src, idx)
+    for r, i in enumerate(idx):
+        assert out[r].tobytes() == src[i].tobytes()
+    idx, *_ = O.ref_select(rng.standard_normal(40), np.ones(40, np.uint8), [0, 40], [40])
+    assert np.array_equal(O.ref_gather(src, idx), src)
+
+
+# ---------------------------------------------------------------------------
+# token-gated attention (Eq. 5-8)
+# ---------------------------------------------------------------------------
+def _attn_case(seed, seqlens=(13, 1, 29), hq=4, hkv=2, dh=16, keep_frac=0.5, n_prompt=3):
+    rng = _rng(seed)
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int64)
+    N = int(cu[-1])
+    pr = np.ones(N, np.uint8)
+    for s in range(len(seqlens)):
+        pr[max(cu[s], cu[s + 1] - n_prompt):cu[s + 1]] = 0
+    b = rng.standard_normal(N)
+    b[pr == 0] = 0.0
+    ks = [int(keep_frac * int(pr[cu[s]:cu[s + 1]].sum())) for s in range(len(seqlens))]
+    idx, pos, kb, kcu = O.ref_select(b, pr, cu, ks)
+    qf = rng.standard_normal((N, hq, dh))
+    kf = rng.standard_normal((N, hkv, dh))
+    vf = rng.standard_normal((N, hkv, dh))
+    gain = rng.uniform(0.5, 1.5, hq)
+    temp = rng.uniform(0.8, 1.2, hq)
+    return dict(cu=cu, pr=pr, b=b, idx=idx, pos=pos, kb=kb, kcu=kcu, qf=qf, kf=kf, vf=vf,
+                q=qf[idx], k=kf[idx], v=vf[idx], gain=gain, temp=temp)
+
+
+def _sdpa(q, k, v, cu, scale=None):
+    """torch scaled_dot_product_attention (fp64, CPU) per sequence, GQA by
+    repeating consecutive KV heads."""
+    G = q.shape[1] // k.shape[1]
+    out = np.zeros_like(q)
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        if hi == lo:
+            continue
+        tq = torch.from_numpy(q[lo:hi]).permute(1, 0, 2)
+        tk = torch.from_numpy(k[lo:hi]).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        tv = torch.from_numpy(v[lo:hi]).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                             scale=scale)
+        out[lo:hi] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+def test_zero_scores_reduce_to_topk_causal_sdpa():
+    c = _attn_case(11)
+    hq = c["q"].shape[1]
+    zeros = np.zeros_like(c["kb"])
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], zeros, c["pos"], c["kcu"], c["gain"],
+                           np.ones(hq), len_scale="off")
+    assert np.allclose(got, _sdpa(c["q"], c["k"], c["v"], c["kcu"]), rtol=0, atol=1e-12)
+    # gain = 0 silences any score vector in the same way
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], np.zeros(hq),
+                           np.ones(hq), len_scale="off")
+    assert np.allclose(got, _sdpa(c["q"], c["k"], c["v"], c["kcu"]), rtol=0, atol=1e-12)
+
+
+def test_full_context_reduces_to_causal_sdpa_with_temperature():
+    c = _attn_case(12, keep_frac=1.0)
+    hq, dh = c["q"].shape[1], c["q"].shape[2]
+    assert c["idx"].size == c["cu"][-1]
+    zeros = np.zeros_like(c["kb"])
+    # the length factor is 1 at every position when nothing is pruned (R6)
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], zeros, c["pos"], c["kcu"], c["gain"],
+                           np.ones(hq))
+    assert np.allclose(got, _sdpa(c["q"], c["k"], c["v"], c["kcu"]), rtol=0, atol=1e-12)
+    # a uniform temperature t multiplies the logit scale
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], zeros, c["pos"], c["kcu"], c["gain"],
+                           np.full(hq, 0.7))
+    want = _sdpa(c["q"], c["k"], c["v"], c["kcu"], scale=0.7 / math.sqrt(dh))
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_uniform_kept_bias_cancels():
+    c = _attn_case(13)
+    base = O.ref_gated_attn(c["q"], c["k"], c["v"], np.zeros_like(c["kb"]), c["pos"], c["kcu"],
+                            c["gain"], c["temp"])
+    for cst in (0.37, -2.0, 5.0):
+        got = O.ref_gated_attn(c["q"], c["k"], c["v"], np.full_like(c["kb"], cst), c["pos"],
+                               c["kcu"], c["gain"], c["temp"])
+        assert np.allclose(got, base, rtol=0, atol=1e-12)
+
+
+def test_zero_queries_give_closed_form_score_weights():
+    """With q = 0 the logits are tau_i * gain_h * b_j, so each output row is the
+    softmax-of-scores average of the visible values."""
+    c = _attn_case(14)
+    q0 = np.zeros_like(c["q"])
+    got = O.ref_gated_attn(q0, c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"], c["temp"])
+    from scipy.special import softmax
+    hq, hkv = c["q"].shape[1], c["k"].shape[1]
+    for s in range(len(c["kcu"]) - 1):
+        lo, hi = int(c["kcu"][s]), int(c["kcu"][s + 1])
+        for i in range(lo, hi):
+            m, p = i - lo + 1, int(c["pos"][i]) + 1
+            for h in range(hq):
+                tau = c["temp"][h] * math.log(m) / math.log(max(2, p))
+                w = softmax(tau * c["gain"][h] * c["kb"][lo:i + 1])
+                assert np.allclose(got[i, h], w @ c["v"][lo:i + 1, h // (hq // hkv)],
+                                   rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_mask_form_equals_compacted_form(seed):
+    c = _attn_case(seed, seqlens=(40, 7, 25), keep_frac=0.4)
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"],
+                           c["temp"])
+    keep = np.zeros(c["cu"][-1], bool)
+    keep[c["idx"]] = True
+    full = O.ref_gated_attn_masked(c["qf"], c["kf"], c["vf"], c["b"], keep, c["cu"], c["gain"],
+                                   c["temp"])
+    assert np.allclose(got, full[c["idx"]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_multiplicative_and_loggate_forms_equal_eq8(seed):
+    c = _attn_case(seed)
+    args = (c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"], c["temp"])
+    eq8 = O.ref_gated_attn(*args)
+    assert np.allclose(O.ref_gated_attn_multiplicative(*args), eq8, rtol=0, atol=1e-12)
+    assert np.allclose(O.ref_gated_attn_loggate(*args), eq8, rtol=0, atol=1e-12)
+
+
+def test_bruteforce_tiny():
+    c = _attn_case(41, seqlens=(8, 3, 6), hq=2, hkv=1, dh=5)
+    args = (c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"], c["temp"])
+    for mode in ("log_ratio", "swap", "off"):
+        assert np.allclose(O.ref_gated_attn(*args, len_scale=mode),
+                           O.ref_gated_attn_bruteforce(*args, len_scale=mode), rtol=0, atol=1e-12)
+
+
+def test_causality_and_sequence_independence():
+    c = _attn_case(51, seqlens=(30, 20))
+    args = [c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"], c["temp"]]
+    base = O.ref_gated_attn(*args)
+    lo, hi = int(c["kcu"][0]), int(c["kcu"][1])
+    cut = lo + (hi - lo) // 2
+    k2, v2, kb2 = c["k"].copy(), c["v"].copy(), c["kb"].copy()
+    k2[cut + 1:hi] += 3.0
+    v2[cut + 1:hi] -= 1.0
+    kb2[cut + 1:hi] += 2.0
+    pert = O.ref_gated_attn(c["q"], k2, v2, kb2, *args[4:])
+    assert np.array_equal(pert[lo:cut + 1], base[lo:cut + 1])
+    # each sequence run alone gives the same rows as the packed batch
+    for s in range(2):
+        a, b_ = int(c["kcu"][s]), int(c["kcu"][s + 1])
+        alone = O.ref_gated_attn(c["q"][a:b_], c["k"][a:b_], c["v"][a:b_], c["kb"][a:b_],
+                                 c["pos"][a:b_], [0, b_ - a], c["gain"], c["temp"])
+        assert np.allclose(alone, base[a:b_], rtol=0, atol=1e-13)
+    # evaluating a subset of rows gives the same rows
+    rows = np.array([0, 3, hi + 2, hi + 5])
+    sub = O.ref_gated_attn(*args, rows=rows, row_block=2)
+    assert np.allclose(sub[rows], base[rows], rtol=0, atol=1e-14)
+
+
+def test_first_query_attends_to_itself_only():
+    c = _attn_case(61)
+    got = O.ref_gated_attn(c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"],
+                           c["temp"])
+    G = c["q"].shape[1] // c["k"].shape[1]
+    for s in range(len(c["kcu"]) - 1):
+        lo = int(c["kcu"][s])
+        if c["kcu"][s + 1] > lo:
+            for h in range(c["q"].shape[1]):
+                assert np.array_equal(got[lo, h], c["v"][lo, h // G])
+
+
+def test_length_factor_values():
+    m = np.array([1, 2, 5, 10])
+    p = np.array([1, 2, 20, 10])
+    lam = O.length_factor(m, p, "log_ratio")
+    assert lam[0] == 0.0 and lam[1] == 1.0 and lam[3] == 1.0
+    assert lam[2] == pytest.approx(math.log(5) / math.log(20), rel=1e-15)
+    assert np.all(O.length_factor(m, p, "off") == 1.0)
+
+
+# ---------------------------------------------------------------------------
+# pass-count cost model: the explainer page's worked example
+# ---------------------------------------------------------------------------
+def test_worked_example_pass_counts():
+    g = json.load(open(os.path.join(GOLDEN, "pass_counts_worked_example.json")))
+    i, e = g["inputs"], g["expected"]
+    full, gated = O.token_layer_passes(i["n_layers"], i["n_tokens"], i["gate_after_layer"],
+                                       i["kept"])
+    assert full == e["unpruned_token_layer_passes"]
+    assert gated == e["gated_token_layer_passes"]
+    assert (i["gate_after_layer"] + 1) * i["n_tokens"] == e["passes_below_gate"]
+    assert gated - e["passes_below_gate"] == e["passes_above_gate"]
+    assert round(full / gated, 1) == e["reduction_rounded_1dp"]
+    assert O.attention_pair_ratio(i["n_tokens"], i["kept"]) == e[
+        "attention_pair_reduction_per_upper_layer"]
+
+
+def test_causal_flop_count_matches_pair_count():
+    # 4*dh flops per (query head, causal pair); T(T+1)/2 pairs
+    T, hq, dh = 8704, 16, 128
+    assert O.causal_attention_flops([T], hq, dh) == 4 * dh * hq * (T * (T + 1) // 2)
+    assert O.causal_attention_flops([T], hq, dh) == 310_347_038_720
+
+
+# ---------------------------------------------------------------------------
+# whole gate on the tiny workload
+# ---------------------------------------------------------------------------
+def test_gate_on_tiny_workload():
+    g = generate(0)
+    out = O.ref_gate(g["x"], g["w1"], g["b1"], g["w2"], g["b2"], g["prunable"],
+                     g["cu_seqlens"], g["budgets"][0])
+    b_raw, b, idx, pos, kb, kcu, xs = out
+    assert idx.size == 192 and kcu[-1] == 192
+    assert np.all(idx[-64:] == np.arange(960, 1024))
+    assert np.all(b[960:] == 0.0)
+    assert np.array_equal(xs, g["x"][idx])
+    # the kept document tokens are exactly the 128 best normalised scores
+    order = np.argsort(-b[:960].astype(np.float32), kind="stable")
+    assert set(order[:128]) == set(idx[:128])
