@@ -1,0 +1,291 @@
+"""Benchmark of the TokenGate gated-prefill hot path on one MI355X.
+
+One step = tg_score + tg_select_topk + tg_gather + tg_gated_attn over the
+128k-token gated layer (Qwen3-1.7B shapes: hidden 2048, scorer 2048->256->1,
+16 query / 8 KV heads of dim 128, 130560 document + 512 prompt tokens, K=8192
+document tokens kept -> 8704 kept tokens), bf16, synthetic seeded inputs
+resident in HBM.  The Q/K/V projection of the kept rows is not one of the
+four calls: it is computed once before timing and the step reads it.
+
+Prints one JSON line (see the keys below).  --gpus N > 1 is refused: the
+path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill tokens/s at 128k ctx; gated-attn MFMA % peak; gate HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
+WORKLOAD = 3                        # 128k-token gated layer
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "learned_token_pruning_06_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, src_files):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        d = json.load(open(p))[kernel]
+    except Exception:
+        return None
+    if d.get("source_sha") != source_sha(src_files):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(g, t_kept_cu, n_rows_score=8192, n_attn_rows=96):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to the
+    whole step: score on the first n_rows_score rows (x linear), normalise +
+    select + gather on all 131072 tokens, attention on n_attn_rows query rows
+    spread over the kept tokens (x keys visited)."""
+    import numpy as np
+    import oracle as O
+    from workloads import bf16_to_f64, random_qkv
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = os.cpu_count()
+    wl = g["wl"]
+    T = wl.t_in
+    t0 = time.perf_counter()
+    xs = bf16_to_f64(g["x"][:n_rows_score])
+    b_raw_s = O.ref_score(xs, bf16_to_f64(g["w1"]), g["b1"], g["w2"], g["b2"])
+    t_score = (time.perf_counter() - t0) * (T / n_rows_score)
+    b_raw = np.tile(b_raw_s, T // n_rows_score + 1)[:T]
+    t0 = time.perf_counter()
+    b, _ = O.ref_normalise(b_raw, g["prunable"], g["cu_seqlens"])
+    idx, pos, kb, kc = O.ref_select(b.astype(np.float32), g["prunable"], g["cu_seqlens"],
+                                    g["budgets"][0])
+    xk = O.ref_gather(g["x"], idx)
+    t_gate = time.perf_counter() - t0
+    tk = int(kc[-1])
+    q, k, v = random_qkv(11, tk, wl.hq, wl.hkv, wl.dh)
+    qd, kd, vd = bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v)
+    rows = np.unique(np.linspace(0, tk - 1, n_attn_rows).astype(np.int64))
+    t0 = time.perf_counter()
+    O.ref_gated_attn(qd, kd, vd, kb, pos, kc, g["gain"], g["temp"], rows=rows)
+    t_att_s = time.perf_counter() - t0
+    keys_all = tk * (tk + 1) / 2.0
+    keys_s = float(np.sum(rows + 1))
+    t_attn = t_att_s * keys_all / keys_s
+    total = t_score + t_gate + t_attn
+    del xk
+    return {
+        "value": T / total, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: score on {n_rows_score}/{T} rows (scaled x{T / n_rows_score:.0f}), "
+                   f"normalise+select+gather on all {T} tokens, gated attention on {rows.size} of "
+                   f"{tk} query rows x all 16 heads (scaled by keys visited); projection excluded"),
+        "seconds_extrapolated": {"score": t_score, "normalise_select_gather": t_gate,
+                                 "attention": t_attn},
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-context", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="skip the CPU baseline and the full-context lane (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gated-prefill "
+              "path has no multi-GPU mode here", file=sys.stderr)
+        sys.exit(2)
+    if args.kernels_only:
+        args.no_cpu_baseline = True
+        args.no_full_context = True
+
+    import numpy as np
+    import torch
+    from learned_token_pruning_06_amd import ops
+    from workloads import generate, random_qkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    g = generate(WORKLOAD)
+    wl = g["wl"]
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    def tb(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = tb(g["x"])
+    w1 = tb(g["w1"])
+    b1 = torch.from_numpy(g["b1"]).to(dev)
+    w2 = torch.from_numpy(g["w2"]).to(dev)
+    pr = torch.from_numpy(g["prunable"]).to(dev)
+    cu = torch.from_numpy(g["cu_seqlens"]).to(dev)
+    kdev = torch.from_numpy(g["budgets"][0]).to(dev)
+    gain = torch.from_numpy(g["gain"]).to(dev)
+    temp = torch.from_numpy(g["temp"]).to(dev)
+    T = wl.t_in
+    n_prunable = [int(g["prunable"].sum())]
+    kept_cu_h, t_kept = ops.kept_sizes(g["cu_seqlens"], n_prunable, g["budgets"][0])
+    lib = ops.load()
+    b_raw = torch.empty(T, dtype=torch.float32, device=dev)
+    b = torch.empty(T, dtype=torch.float32, device=dev)
+    ws_s = ops.workspace(lib.tg_score_workspace_size(T, 1), dev)
+    ws_k = ops.workspace(lib.tg_select_workspace_size(T, 1), dev)
+    kept_idx = torch.empty(t_kept, dtype=torch.int32, device=dev)
+    kept_pos = torch.empty(t_kept, dtype=torch.int32, device=dev)
+    kept_b = torch.empty(t_kept, dtype=torch.float32, device=dev)
+    kept_cu = torch.empty(2, dtype=torch.int32, device=dev)
+    x_kept = torch.empty(t_kept, wl.d, dtype=torch.bfloat16, device=dev)
+
+    def gate():
+        ops.score(x, w1, w2, pr, cu, b1=b1, eps=1e-6, b_raw=b_raw, b=b, ws=ws_s)
+        ops.select_topk(b, pr, cu, kdev, t_kept, kept_idx, kept_pos, kept_b, kept_cu, ws_k)
+        ops.gather(x, kept_idx, out=x_kept)
+
+    # projection of the kept rows: outside the timed step (not one of the four calls)
+    gate()
+    wq, wk, wv = tb(g["wq"]), tb(g["wk"]), tb(g["wv"])
+    q = (x_kept @ wq).view(t_kept, wl.hq, wl.dh).contiguous()
+    k = (x_kept @ wk).view(t_kept, wl.hkv, wl.dh).contiguous()
+    v = (x_kept @ wv).view(t_kept, wl.hkv, wl.dh).contiguous()
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+    assert int(kept_cu[-1].item()) == t_kept
+
+    names = ["score", "select", "gather", "attn"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.score(x, w1, w2, pr, cu, b1=b1, eps=1e-6, b_raw=b_raw, b=b, ws=ws_s)
+        if ev is not None:
+            ev[1].record()
+        ops.select_topk(b, pr, cu, kdev, t_kept, kept_idx, kept_pos, kept_b, kept_cu, ws_k)
+        if ev is not None:
+            ev[2].record()
+        ops.gather(x, kept_idx, out=x_kept)
+        if ev is not None:
+            ev[3].record()
+        ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=t_kept, out=o)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    # timed region: exactly K steps, events on the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)      # us
+    avg = {n: float(np.mean(per[n])) for n in names}
+    med = {n: float(np.median(per[n])) for n in names}
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (wall / args.steps)
+    log(f"per-kernel mean us: {avg}; step {ms_per_step:.3f} ms")
+
+    # algorithmic work (what the method must move / compute)
+    attn_flops = 2.0 * wl.dh * wl.hq * t_kept * (t_kept + 1)
+    score_bytes = T * wl.d * 2 + wl.h * wl.d * 2 + T * (1 + 4 + 4 + 4 + 4)
+    select_bytes = T * (4 + 1) + t_kept * 12
+    gather_bytes = 2 * t_kept * wl.d * 2
+    attn_tflops = attn_flops / (avg["attn"] * 1e-6) / 1e12
+    score_gbs = score_bytes / (avg["score"] * 1e-6) / 1e9
+    gate_gbs = (score_bytes + select_bytes + gather_bytes) / (
+        (avg["score"] + avg["select"] + avg["gather"]) * 1e-6) / 1e9
+    kern = {"attn": ("mfma", attn_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", ["attn.hip", "common.h"]),
+            "score": ("hbm", score_gbs, PEAK_HBM_GBS, "GB/s", ["score.hip", "common.h"])}
+    dom = "attn" if avg["attn"] >= avg["score"] else "score"
+    bound, ach, peak, unit, srcs = kern[dom]
+    roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": traffic_for(dom, srcs),
+                "kernel": "gated_attn_bf16" if dom == "attn" else "score_mlp_bf16",
+                "avg_launch_us": round(avg[dom], 2)}
+
+    full = None
+    if not args.no_full_context:
+        # unpruned reference point: all 131072 tokens kept (stand-in Q/K/V)
+        qf, kf, vf = random_qkv(3, T, wl.hq, wl.hkv, wl.dh)
+        qf, kf, vf = tb(qf), tb(kf), tb(vf)
+        bf_ = b.clone()
+        posf = torch.arange(T, dtype=torch.int32, device=dev)
+        cuf = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        of = torch.empty_like(qf)
+        ops.gated_attn(qf, kf, vf, bf_, posf, cuf, gain, temp, max_len=T, out=of)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            ops.gated_attn(qf, kf, vf, bf_, posf, cuf, gain, temp, max_len=T, out=of)
+        e1.record()
+        torch.cuda.synchronize()
+        t_full = e0.elapsed_time(e1) / reps * 1e-3
+        fl = 2.0 * wl.dh * wl.hq * T * (T + 1)
+        full = {"attn_ms": round(t_full * 1e3, 3), "attn_tflops": round(fl / t_full / 1e12, 1),
+                "attn_frac_of_peak": round(fl / t_full / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "tokens_per_s_gate_plus_attn": round(
+                    T / (t_full + (avg["score"] + avg["select"]) * 1e-6), 1),
+                "note": "K = all tokens; gather is the identity and not run"}
+        del qf, kf, vf, of
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample (cpu_baseline)")
+        cpu = cpu_baseline(g, kept_cu_h)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian hidden states and random-init weights)",
+        "config": {"workload": "gated layer 128k: 130560 doc + 512 prompt tokens, K=8192",
+                   "t_in": T, "k": int(g["budgets"][0][0]), "t_kept": t_kept, "d": wl.d,
+                   "h": wl.h, "hq": wl.hq, "hkv": wl.hkv, "dh": wl.dh,
+                   "step": "score+select+gather+gated_attn (Q/K/V projection excluded)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us_mean": {n: round(avg[n], 2) for n in names},
+        "kernels_us_median": {n: round(med[n], 2) for n in names},
+        "attn_tflops": round(attn_tflops, 1),
+        "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "score_gbs": round(score_gbs, 1),
+        "gate_gbs": round(gate_gbs, 1),
+        "gate_frac_of_hbm_peak": round(gate_gbs / PEAK_HBM_GBS, 4),
+        "full_context": full,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

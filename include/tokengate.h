@@ -1,0 +1,183 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate gated-prefill hot path on gfx950.
+ *
+ * The four calls implement, for one gated layer L of a decoder:
+ *   tg_score        scoring network + per-sequence RMS normalisation
+ *   tg_select_topk  top-K of the prunable tokens, prompt tokens always kept
+ *   tg_gather       compaction of the kept rows
+ *   tg_gated_attn   token-gated causal attention over the kept tokens
+ * Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
+ * with Learned Token Pruning", §4.1 (Eq. 3-4) and §4.2 (Eq. 5-8).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers marked "dev" are device pointers (hipMalloc'd or any memory the
+ *   GPU can read); "host" pointers are ordinary host memory read during the
+ *   call.  The library never allocates, frees or synchronises: every call
+ *   only validates its arguments on the host and enqueues kernels on
+ *   `stream`, so it can be captured into a HIP graph.  Scratch memory is a
+ *   caller-owned workspace sized by the matching *_workspace_size query; its
+ *   contents need no initialisation and are overwritten by every call.
+ * - Token layout: sequences are packed back to back; cu_seqlens[s] is the
+ *   first token of sequence s, cu_seqlens[n_seq] the total.  Within a
+ *   sequence, any token may be prunable (document) or not (prompt).
+ * - Outputs must not alias inputs.  Calls that share a workspace must not
+ *   overlap in time (same stream is fine).
+ * - Errors: arguments are checked before anything is launched.  A bad
+ *   argument returns TG_ERR_INVALID_ARG, a valid but unimplemented shape or
+ *   dtype TG_ERR_UNSUPPORTED, a short workspace TG_ERR_WORKSPACE, a failed
+ *   launch TG_ERR_HIP; tg_last_error() then gives a thread-local message.
+ *   No call aborts the process.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_INVALID_ARG = 1,
+  TG_ERR_UNSUPPORTED = 2,
+  TG_ERR_WORKSPACE = 3,
+  TG_ERR_HIP = 4
+} tg_status;
+
+typedef enum tg_dtype { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+/* An opaque HIP stream (hipStream_t); NULL is the default stream. */
+typedef void* tg_stream;
+
+/* Static text for a status code; never NULL. */
+const char* tg_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* tg_last_error(void);
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int tg_version(void);
+
+/* ------------------------------------------------------------------------
+ * tg_score -- the gate's scoring network and score normalisation, §4.1 Eq. 3.
+ *
+ *   b~_j = w2 . SiLU(W1 x_j + b1) + b2                  for every token j
+ *   r_s  = sqrt(mean_{j in P_s} b~_j^2 + eps)            per sequence s
+ *   b_j  = b~_j / r_s  if prunable[j],  b_j = 0 otherwise
+ *
+ * x        dev  [t_in rows, d] of `dt`, row r at x + r * x_row_stride elements.
+ *                Rows are the scorer's input (the post-attention hidden state
+ *                after the block's second norm).
+ * w1       dev  [h, d] of `dt`, row-major (row j = input weights of hidden unit j).
+ * b1       dev  [h] f32, or NULL for zero.      w2  dev [h] f32.     b2  scalar.
+ * prunable dev  [t_in] u8, nonzero = document token (may be pruned).
+ * cu_seqlens dev [n_seq + 1] i32, non-decreasing, cu_seqlens[n_seq] == t_in.
+ * eps      >= 0; the normaliser of a sequence without prunable tokens is 1.
+ * b_raw    dev  [t_in] f32 out (b~), or NULL (then kept in the workspace).
+ * b        dev  [t_in] f32 out (normalised; 0 on prompt tokens).
+ * ws       dev  workspace of >= tg_score_workspace_size(t_in, n_seq) bytes.
+ * Supported: dt = TG_BF16 with d % 64 == 0 and h % 32 == 0, h <= 256; or
+ * dt = TG_F32 with h <= 1024.  x and w1 rows must be 16-byte aligned.
+ * Reduction order is fixed, so results are bitwise reproducible.
+ * ---------------------------------------------------------------------- */
+size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq);
+tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in,
+                   int32_t d, int32_t h, const void* w1, const float* b1, const float* w2,
+                   float b2, const uint8_t* prunable, const int32_t* cu_seqlens,
+                   int32_t n_seq, float eps, float* b_raw, float* b, void* ws,
+                   size_t ws_bytes, tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_kept_sizes -- host arithmetic for the output sizes of tg_select_topk,
+ * §4.1 Eq. 4: |S_s| = min(K_s, |P_s|) + |N_s|.  Lets the caller size every
+ * downstream buffer without reading anything back from the device.
+ *
+ * cu_seqlens_host [n_seq + 1], n_prunable_host [n_seq], k_host [n_seq]: host.
+ * kept_cu_seqlens_host [n_seq + 1] host out; *t_kept host out (total).
+ * K_s < 0 or n_prunable outside [0, len_s] is TG_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+tg_status tg_kept_sizes(const int32_t* cu_seqlens_host, const int32_t* n_prunable_host,
+                        const int32_t* k_host, int32_t n_seq, int32_t* kept_cu_seqlens_host,
+                        int64_t* t_kept);
+
+/* ------------------------------------------------------------------------
+ * tg_select_topk -- the top-K selector with forced keep of prompt tokens,
+ * §4.1 Eq. 4:  S_s = top-K_{j in P_s}(b_j)  U  N_s.
+ *
+ * Order: b descending, lower index first on ties; -0.0 == +0.0; NaN ranks
+ * below -inf.  K_s counts prunable tokens; K_s >= |P_s| keeps all of P_s;
+ * K_s == 0 keeps only the prompt tokens.
+ * b          dev [t_in] f32 scores (normally tg_score's output).
+ * prunable   dev [t_in] u8.          cu_seqlens dev [n_seq + 1] i32.
+ * k          dev [n_seq] i32 budgets, each >= 0 (negative budgets are read as 0).
+ * Outputs, ascending original index within each sequence, sequences in order:
+ *   kept_idx        dev [t_kept_capacity] i32, global token index
+ *   kept_pos        dev [t_kept_capacity] i32 (or NULL), index within its sequence
+ *   kept_b          dev [t_kept_capacity] f32 (or NULL), b at the kept token
+ *   kept_cu_seqlens dev [n_seq + 1] i32, offsets of each sequence's kept tokens
+ * t_kept_capacity: length of the three per-token outputs.  The exact count is
+ * tg_kept_sizes()'s t_kept; entries beyond the capacity are not written.
+ * ws dev workspace of >= tg_select_workspace_size(t_in, n_seq) bytes.
+ * Integer work throughout: the result is exact and reproducible.
+ * ---------------------------------------------------------------------- */
+size_t tg_select_workspace_size(int64_t t_in, int32_t n_seq);
+tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t* cu_seqlens,
+                         const int32_t* k, int32_t n_seq, int64_t t_in,
+                         int64_t t_kept_capacity, int32_t* kept_idx, int32_t* kept_pos,
+                         float* kept_b, int32_t* kept_cu_seqlens, void* ws, size_t ws_bytes,
+                         tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_gather -- compaction of the kept rows (§4.1: the residual stream of a
+ * pruned token stops at layer L; only kept rows go on to the layers above).
+ *
+ *   dst row r = src row idx[r],  r in [0, n_rows)   (bytes copied unchanged)
+ * src dev, row i at src + i * src_row_stride_bytes; n_src_rows rows.
+ * idx dev [n_rows] i32; an index outside [0, n_src_rows) writes a zero row.
+ * dst dev, row r at dst + r * dst_row_stride_bytes.
+ * row_bytes % 4 == 0 and 4-byte aligned rows are required; 16-byte multiples
+ * with 16-byte aligned rows take the vector path.
+ * ---------------------------------------------------------------------- */
+tg_status tg_gather(const void* src, int64_t src_row_stride_bytes, int64_t n_src_rows,
+                    int64_t row_bytes, const int32_t* idx, int64_t n_rows, void* dst,
+                    int64_t dst_row_stride_bytes, tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_gated_attn -- token-gated causal attention over the kept tokens,
+ * §4.2 Eq. 8 with the head-wise gain of Eq. 6 and the temperature of Eq. 7:
+ *
+ *   alpha_ij^h = softmax_{j in S, j <= i}( tau_i^h * (s * q_i^h . k_j + gain_h * b_j) )
+ *   tau_i^h    = temp_h * log(m_i) / log(max(2, p_i))
+ *   O_i^h      = sum_j alpha_ij^h v_j
+ *
+ * m_i = kept keys visible to query i (itself included) = its index within the
+ * sequence's kept tokens + 1; p_i = kept_pos[i] + 1, its original position.
+ * Causality is by original position, i.e. by kept order.  Query head h reads
+ * KV head h / (hq / hkv).  The gate g_j = softmax_S(gain_h * b_j) of Eq. 5-6
+ * is never formed: its normaliser is constant in j and cancels.
+ *
+ * q   dev [t_kept, hq, dh] of `dt`.     k, v dev [t_kept, hkv, dh] of `dt`.
+ * out dev [t_kept, hq, dh] of `dt` (accumulation in f32).
+ * kept_b dev [t_kept] f32 scores of the kept tokens (0 on prompt tokens).
+ * kept_pos dev [t_kept] i32 original index in the sequence, or NULL: then the
+ *   length factor is 1 (tau = temp).
+ * kept_cu_seqlens dev [n_seq + 1] i32; max_kept_seqlen = longest sequence
+ *   (host value, used only to size the launch; a larger one is harmless).
+ * gain, temp dev [hq] f32: positive post-softplus values of Eq. 6 and Eq. 7.
+ * sm_scale: s; <= 0 selects 1/sqrt(dh).
+ * Supported: dh in {64, 128}; hq % hkv == 0 with hq/hkv in {1, 2, 4} or a
+ * multiple of 4; dt = TG_BF16 (matrix cores) or TG_F32 (vector ALU).
+ * ---------------------------------------------------------------------- */
+tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                        int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                        const int32_t* kept_cu_seqlens, int32_t n_seq,
+                        int32_t max_kept_seqlen, int32_t hq, int32_t hkv, int32_t dh,
+                        const float* gain, const float* temp, float sm_scale,
+                        tg_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

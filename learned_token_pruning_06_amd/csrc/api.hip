@@ -1,0 +1,189 @@
+// Host side of the C ABI: argument validation, status codes, thread-local
+// error text and dispatch to the kernels.  Nothing here allocates device
+// memory or synchronises a stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/tokengate.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tg_status fail(tg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tg_status ok() {
+  g_err[0] = '\0';
+  return TG_OK;
+}
+
+tg_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TG_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_string(int s) {
+  switch (s) {
+    case TG_OK: return "TG_OK";
+    case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG";
+    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
+    case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE";
+    case TG_ERR_HIP: return "TG_ERR_HIP";
+    default: return "TG_UNKNOWN_STATUS";
+  }
+}
+
+const char* tg_last_error(void) { return g_err; }
+
+int tg_version(void) { return 10000; }
+
+// ----------------------------------------------------------------- score
+size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
+  if (t_in < 0 || n_seq < 0) return 0;
+  return tg::score_ws_bytes(t_in, n_seq);
+}
+
+tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
+                   int32_t h, const void* w1, const float* b1, const float* w2, float b2,
+                   const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq, float eps,
+                   float* b_raw, float* b, void* ws, size_t ws_bytes, tg_stream stream) {
+  if (t_in < 0 || n_seq < 1 || d < 1 || h < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_score: need t_in >= 0, n_seq >= 1, d >= 1, h >= 1");
+  if (t_in > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "tg_score: t_in too large");
+  if (!(eps >= 0.0f)) return fail(TG_ERR_INVALID_ARG, "tg_score: eps must be >= 0");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_score: bad dtype");
+  if (x_row_stride < d) return fail(TG_ERR_INVALID_ARG, "tg_score: x_row_stride < d");
+  if (!cu_seqlens || !w2 || !b || !ws) return fail(TG_ERR_INVALID_ARG, "tg_score: null pointer");
+  if (t_in > 0 && (!x || !w1 || !prunable))
+    return fail(TG_ERR_INVALID_ARG, "tg_score: null pointer");
+  const size_t es = dt == TG_BF16 ? 2 : 4;
+  if (dt == TG_BF16) {
+    if (d % 64 != 0 || h % 32 != 0 || h > 256)
+      return fail(TG_ERR_UNSUPPORTED, "tg_score: bf16 needs d %% 64 == 0, h %% 32 == 0, h <= 256");
+  } else if (h > 1024) {
+    return fail(TG_ERR_UNSUPPORTED, "tg_score: f32 needs h <= 1024");
+  }
+  if ((x && !aligned(x, 16)) || (w1 && !aligned(w1, 16)) || ((x_row_stride * es) % 16) != 0 ||
+      ((d * es) % 16) != 0)
+    return fail(TG_ERR_UNSUPPORTED, "tg_score: x and w1 rows must be 16-byte aligned");
+  if (ws_bytes < tg::score_ws_bytes(t_in, n_seq))
+    return fail(TG_ERR_WORKSPACE, "tg_score: workspace %zu < %zu bytes", ws_bytes,
+                tg::score_ws_bytes(t_in, n_seq));
+  hipError_t e = tg::launch_score(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, b2, prunable,
+                                  cu_seqlens, n_seq, eps, b_raw, b, ws, (hipStream_t)stream);
+  return from_hip(e, "tg_score launch");
+}
+
+// ---------------------------------------------------------------- select
+tg_status tg_kept_sizes(const int32_t* cu, const int32_t* n_prunable, const int32_t* k,
+                        int32_t n_seq, int32_t* kept_cu, int64_t* t_kept) {
+  if (n_seq < 0 || !cu || !n_prunable || !k || !kept_cu || !t_kept)
+    return fail(TG_ERR_INVALID_ARG, "tg_kept_sizes: bad arguments");
+  if (cu[0] != 0) return fail(TG_ERR_INVALID_ARG, "tg_kept_sizes: cu_seqlens[0] != 0");
+  int64_t acc = 0;
+  kept_cu[0] = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    int64_t len = (int64_t)cu[s + 1] - cu[s];
+    if (len < 0) return fail(TG_ERR_INVALID_ARG, "tg_kept_sizes: cu_seqlens decreases at %d", s);
+    if (k[s] < 0) return fail(TG_ERR_INVALID_ARG, "tg_kept_sizes: K[%d] < 0", s);
+    if (n_prunable[s] < 0 || n_prunable[s] > len)
+      return fail(TG_ERR_INVALID_ARG, "tg_kept_sizes: n_prunable[%d] outside [0, len]", s);
+    int64_t kp = k[s] < n_prunable[s] ? k[s] : n_prunable[s];
+    acc += kp + (len - n_prunable[s]);
+    if (acc > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_kept_sizes: total too large");
+    kept_cu[s + 1] = (int32_t)acc;
+  }
+  *t_kept = acc;
+  return ok();
+}
+
+size_t tg_select_workspace_size(int64_t t_in, int32_t n_seq) {
+  if (t_in < 0 || n_seq < 0) return 0;
+  return tg::select_ws_bytes(t_in, n_seq);
+}
+
+tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t* cu_seqlens,
+                         const int32_t* k, int32_t n_seq, int64_t t_in, int64_t cap,
+                         int32_t* kept_idx, int32_t* kept_pos, float* kept_b,
+                         int32_t* kept_cu_seqlens, void* ws, size_t ws_bytes, tg_stream stream) {
+  if (n_seq < 1 || t_in < 0 || cap < 0)
+    return fail(TG_ERR_INVALID_ARG, "tg_select_topk: need n_seq >= 1, t_in >= 0, capacity >= 0");
+  if (t_in > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "tg_select_topk: t_in too large");
+  if (!cu_seqlens || !k || !kept_cu_seqlens || !ws)
+    return fail(TG_ERR_INVALID_ARG, "tg_select_topk: null pointer");
+  if (t_in > 0 && (!b || !prunable)) return fail(TG_ERR_INVALID_ARG, "tg_select_topk: null pointer");
+  if (cap > 0 && !kept_idx) return fail(TG_ERR_INVALID_ARG, "tg_select_topk: kept_idx is null");
+  if (ws_bytes < tg::select_ws_bytes(t_in, n_seq))
+    return fail(TG_ERR_WORKSPACE, "tg_select_topk: workspace %zu < %zu bytes", ws_bytes,
+                tg::select_ws_bytes(t_in, n_seq));
+  hipError_t e = tg::launch_select(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx,
+                                   kept_pos, kept_b, kept_cu_seqlens, ws, (hipStream_t)stream);
+  return from_hip(e, "tg_select_topk launch");
+}
+
+// ---------------------------------------------------------------- gather
+tg_status tg_gather(const void* src, int64_t src_stride, int64_t n_src, int64_t row_bytes,
+                    const int32_t* idx, int64_t n_rows, void* dst, int64_t dst_stride,
+                    tg_stream stream) {
+  if (n_rows < 0 || n_src < 0 || row_bytes < 0)
+    return fail(TG_ERR_INVALID_ARG, "tg_gather: negative size");
+  if (n_rows == 0 || row_bytes == 0) return ok();
+  if (!src || !idx || !dst) return fail(TG_ERR_INVALID_ARG, "tg_gather: null pointer");
+  if (src_stride < row_bytes || dst_stride < row_bytes)
+    return fail(TG_ERR_INVALID_ARG, "tg_gather: row stride smaller than row_bytes");
+  if (row_bytes % 4 != 0 || src_stride % 4 != 0 || dst_stride % 4 != 0 || !aligned(src, 4) ||
+      !aligned(dst, 4))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gather: rows must be 4-byte multiples, 4-byte aligned");
+  if (n_rows > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_gather: too many rows");
+  hipError_t e = tg::launch_gather(src, src_stride, n_src, row_bytes, idx, n_rows, dst, dst_stride,
+                                   (hipStream_t)stream);
+  return from_hip(e, "tg_gather launch");
+}
+
+// ------------------------------------------------------------- attention
+tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                        int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                        const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
+                        int32_t hkv, int32_t dh, const float* gain, const float* temp,
+                        float sm_scale, tg_stream stream) {
+  if (t_kept < 0 || n_seq < 1 || max_len < 0 || hq < 1 || hkv < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: bad sizes");
+  if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: hq %% hkv != 0");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: bad dtype");
+  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: dh must be 64 or 128");
+  const int g = hq / hkv;
+  if (!((g <= 4 && 4 % g == 0) || (g > 4 && g % 4 == 0)))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: hq/hkv must be 1, 2, 4 or a multiple of 4");
+  if (t_kept > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: t_kept too large");
+  if (!kept_cu || !gain || !temp) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: null pointer");
+  if (t_kept == 0) return ok();
+  if (!q || !k || !v || !out || !kept_b)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: null pointer");
+  if (max_len > t_kept) max_len = (int32_t)t_kept;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: tensors must be 16-byte aligned");
+  hipError_t e;
+  if (dt == TG_BF16)
+    e = tg::launch_attn_bf16(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
+                             hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
+  else
+    e = tg::launch_attn_f32(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
+                            hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
+  return from_hip(e, "tg_gated_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Shared device helpers and internal launch entry points of libtokengate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TG_DEVINL __device__ __forceinline__
+
+namespace tg {
+
+// ---------------------------------------------------------------------------
+// sequence chunking without a lookup table
+//
+// Sequence s owns grid slots [slot0(s), slot0(s+1)) with
+//   slot0(s) = s + floor(cu[s] / CH).
+// slot0(s+1) - slot0(s) = 1 + floor(cu[s+1]/CH) - floor(cu[s]/CH)
+//                      >= 1 + floor(len_s/CH) >= ceil(len_s/CH),
+// so every chunk of every sequence has a slot; surplus slots exit at once.
+// A grid of n_seq + ceil(t_in / CH) slots covers every sequence.
+// ---------------------------------------------------------------------------
+TG_DEVINL int64_t slot0_of(const int32_t* cu, int s, int ch) {
+  return (int64_t)s + (int64_t)(cu[s] / ch);
+}
+
+// Largest s in [0, n_seq) with slot0(s) <= slot; -1 if none.
+TG_DEVINL int seq_of_slot(const int32_t* cu, int n_seq, int64_t slot, int ch) {
+  int lo = 0, hi = n_seq - 1, ans = -1;
+  while (lo <= hi) {
+    int mid = (lo + hi) >> 1;
+    if (slot0_of(cu, mid, ch) <= slot) {
+      ans = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return ans;
+}
+
+// ---------------------------------------------------------------------------
+// order-preserving 32-bit key of a score: a larger float gives a larger key,
+// -0.0 and +0.0 share a key, every NaN maps to 0 (below -inf, whose key is
+// 0x007FFFFF).
+// ---------------------------------------------------------------------------
+TG_DEVINL uint32_t score_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// wave / block reductions (wave64)
+// ---------------------------------------------------------------------------
+template <typename T>
+TG_DEVINL T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+TG_DEVINL float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+TG_DEVINL int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT % 64 == 0) in thread
+// order; returns the exclusive prefix and writes the block total.
+// `scratch` must hold NT/64 ints; contains a barrier.
+template <int NT>
+TG_DEVINL int block_excl_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v);
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    int s = scratch[i];
+    base += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load that does not keep the line in cache (streamed operands)
+TG_DEVINL uint4 ld_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+TG_DEVINL uint32_t ld_acquire_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace tg
+
+// ---------------------------------------------------------------------------
+// internal launchers (arguments already validated by api.hip)
+// ---------------------------------------------------------------------------
+namespace tg {
+
+constexpr int kScoreChunk = 2048;    // tokens per normalisation block
+constexpr int kSelChunk = 2048;      // tokens per selection block
+
+size_t score_ws_bytes(int64_t t_in, int n_seq);
+hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_in, int d, int h,
+                        const void* w1, const float* b1, const float* w2, float b2,
+                        const uint8_t* prunable, const int32_t* cu, int n_seq, float eps,
+                        float* b_raw, float* b, void* ws, hipStream_t st);
+
+size_t select_ws_bytes(int64_t t_in, int n_seq);
+hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t* cu,
+                         const int32_t* k, int n_seq, int64_t t_in, int64_t cap,
+                         int32_t* kept_idx, int32_t* kept_pos, float* kept_b,
+                         int32_t* kept_cu, void* ws, hipStream_t st);
+
+hipError_t launch_gather(const void* src, int64_t src_stride, int64_t n_src, int64_t row_bytes,
+                         const int32_t* idx, int64_t n_rows, void* dst, int64_t dst_stride,
+                         hipStream_t st);
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
+                            int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                            const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,
+                            int dh, const float* gain, const float* temp, float sm_scale,
+                            hipStream_t st);
+
+hipError_t launch_attn_f32(const void* q, const void* k, const void* v, void* out,
+                           int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                           const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,
+                           int dh, const float* gain, const float* temp, float sm_scale,
+                           hipStream_t st);
+
+}  // namespace tg

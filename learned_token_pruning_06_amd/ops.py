@@ -1,0 +1,189 @@
+"""Python binding of the TokenGate gated-prefill C ABI.
+
+Argument marshalling only: torch supplies device memory and the current
+stream, every step of the computation runs in libtokengate's HIP kernels.
+Each function mirrors the C call of the same name in include/tokengate.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import TG_BF16, TG_F32, check, load
+
+_DT = {torch.bfloat16: TG_BF16, torch.float32: TG_F32}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- score
+def score(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: torch.Tensor,
+          cu_seqlens: torch.Tensor, b1: Optional[torch.Tensor] = None, b2: float = 0.0,
+          eps: float = 1e-6, b_raw: Optional[torch.Tensor] = None,
+          b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """tg_score: raw scores b~ and normalised scores b (f32, one per token)."""
+    lib = load()
+    _need(x, "x", (torch.bfloat16, torch.float32), 2)
+    _need(w1, "w1", x.dtype, 2)
+    _need(w2, "w2", torch.float32, 1)
+    _need(prunable, "prunable", torch.uint8, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if b1 is not None:
+        _need(b1, "b1", torch.float32, 1)
+    t_in, d = x.shape
+    h = w1.shape[0]
+    n_seq = cu_seqlens.numel() - 1
+    dev = x.device
+    if b_raw is None:
+        b_raw = torch.empty(t_in, dtype=torch.float32, device=dev)
+    if b is None:
+        b = torch.empty(t_in, dtype=torch.float32, device=dev)
+    need = lib.tg_score_workspace_size(t_in, n_seq)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = lib.tg_score(_p(x), _DT[x.dtype], x.stride(0), t_in, d, h, _p(w1), _p(b1), _p(w2),
+                      float(b2), _p(prunable), _p(cu_seqlens), n_seq, float(eps), _p(b_raw), _p(b),
+                      _p(ws), ws.numel(), _stream(dev))
+    check("tg_score", st)
+    return b_raw, b
+
+
+# -------------------------------------------------------------------- select
+def kept_sizes(cu_seqlens_host: Sequence[int], n_prunable_host: Sequence[int],
+               k_host: Sequence[int]):
+    """tg_kept_sizes (host arithmetic): (kept_cu_seqlens as int32 array, t_kept)."""
+    lib = load()
+    cu = np.ascontiguousarray(cu_seqlens_host, dtype=np.int32)
+    npr = np.ascontiguousarray(n_prunable_host, dtype=np.int32)
+    kk = np.ascontiguousarray(k_host, dtype=np.int32)
+    n_seq = cu.size - 1
+    if npr.size != n_seq or kk.size != n_seq:
+        raise ValueError("n_prunable and k need one entry per sequence")
+    out = np.zeros(n_seq + 1, np.int32)
+    tk = ctypes.c_int64(0)
+    st = lib.tg_kept_sizes(cu.ctypes.data_as(ctypes.c_void_p), npr.ctypes.data_as(ctypes.c_void_p),
+                           kk.ctypes.data_as(ctypes.c_void_p), n_seq,
+                           out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(tk))
+    check("tg_kept_sizes", st)
+    return out, int(tk.value)
+
+
+def select_topk(b: torch.Tensor, prunable: torch.Tensor, cu_seqlens: torch.Tensor,
+                k: torch.Tensor, t_kept: int, kept_idx: Optional[torch.Tensor] = None,
+                kept_pos: Optional[torch.Tensor] = None, kept_b: Optional[torch.Tensor] = None,
+                kept_cu: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                with_pos: bool = True, with_b: bool = True):
+    """tg_select_topk: (kept_idx, kept_pos, kept_b, kept_cu_seqlens), all on device."""
+    lib = load()
+    _need(b, "b", torch.float32, 1)
+    _need(prunable, "prunable", torch.uint8, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(k, "k", torch.int32, 1)
+    t_in = b.numel()
+    n_seq = cu_seqlens.numel() - 1
+    dev = b.device
+    cap = int(t_kept)
+    if kept_idx is None:
+        kept_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if kept_pos is None and with_pos:
+        kept_pos = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if kept_b is None and with_b:
+        kept_b = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    if kept_cu is None:
+        kept_cu = torch.empty(n_seq + 1, dtype=torch.int32, device=dev)
+    need = lib.tg_select_workspace_size(t_in, n_seq)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = lib.tg_select_topk(_p(b), _p(prunable), _p(cu_seqlens), _p(k), n_seq, t_in, cap,
+                            _p(kept_idx), _p(kept_pos), _p(kept_b), _p(kept_cu), _p(ws), ws.numel(),
+                            _stream(dev))
+    check("tg_select_topk", st)
+    sl = slice(0, cap)
+    return (kept_idx[sl], None if kept_pos is None else kept_pos[sl],
+            None if kept_b is None else kept_b[sl], kept_cu)
+
+
+# -------------------------------------------------------------------- gather
+def gather(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """tg_gather: out[r] = src[idx[r]] over the first axis of a contiguous src."""
+    lib = load()
+    _need(src, "src")
+    _need(idx, "idx", torch.int32, 1)
+    if src.dim() < 1:
+        raise ValueError("src needs at least one dimension")
+    row_bytes = int(np.prod(src.shape[1:], dtype=np.int64)) * src.element_size()
+    n_rows = idx.numel()
+    if out is None:
+        out = torch.empty((n_rows,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    else:
+        _need(out, "out", src.dtype)
+    st = lib.tg_gather(_p(src), row_bytes, src.shape[0], row_bytes, _p(idx), n_rows, _p(out),
+                       row_bytes, _stream(src.device))
+    check("tg_gather", st)
+    return out
+
+
+# ----------------------------------------------------------------- attention
+def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.Tensor,
+               kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor, gain: torch.Tensor,
+               temp: torch.Tensor, max_len: Optional[int] = None,
+               sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
+    """tg_gated_attn: token-gated causal attention, q [T,Hq,dh], k/v [T,Hkv,dh]."""
+    lib = load()
+    _need(q, "q", (torch.bfloat16, torch.float32), 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    _need(kept_b, "kept_b", torch.float32, 1)
+    _need(kept_cu, "kept_cu", torch.int32, 1)
+    _need(gain, "gain", torch.float32, 1)
+    _need(temp, "temp", torch.float32, 1)
+    if kept_pos is not None:
+        _need(kept_pos, "kept_pos", torch.int32, 1)
+    t, hq, dh = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    n_seq = kept_cu.numel() - 1
+    st = lib.tg_gated_attn(_p(q), _p(k), _p(v), _DT[q.dtype], _p(out), t, _p(kept_b),
+                           _p(kept_pos), _p(kept_cu), n_seq, int(max_len if max_len else t), hq, hkv,
+                           dh, _p(gain), _p(temp), float(sm_scale or 0.0), _stream(q.device))
+    check("tg_gated_attn", st)
+    return out
+
+
+# ------------------------------------------------------------------ pipeline
+def gate_prefill(x, w1, w2, prunable, cu_seqlens, k, cu_seqlens_host, n_prunable_host, k_host,
+                 b1=None, b2: float = 0.0, eps: float = 1e-6):
+    """Score, select and gather one gated layer; returns a dict of device tensors
+    plus the host-side kept sizes."""
+    kept_cu_host, t_kept = kept_sizes(cu_seqlens_host, n_prunable_host, k_host)
+    b_raw, b = score(x, w1, w2, prunable, cu_seqlens, b1=b1, b2=b2, eps=eps)
+    kept_idx, kept_pos, kept_b, kept_cu = select_topk(b, prunable, cu_seqlens, k, t_kept)
+    x_kept = gather(x, kept_idx)
+    return dict(b_raw=b_raw, b=b, kept_idx=kept_idx, kept_pos=kept_pos, kept_b=kept_b,
+                kept_cu=kept_cu, kept_cu_host=kept_cu_host, t_kept=t_kept, x_kept=x_kept)

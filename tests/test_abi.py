@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/tokengate.h declares, and rejects bad arguments with status codes
+before anything is launched.  Every call below fails validation, so no
+kernel is ever enqueued (safe on a GPU host too)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+
+lib_mod = pytest.importorskip("learned_token_pruning_06_amd._lib")
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.fail("libtokengate.so is not built (run __graft_entry__.build())")
+    return lib_mod.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
+        assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
+    assert set(lib_mod.PROTOTYPES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tg_version() == 10000
+    for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
+                                 "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
+        assert lib.tg_status_string(code).decode() == name
+    assert lib.tg_status_string(99).decode() == "TG_UNKNOWN_STATUS"
+
+
+def _kept_sizes(lib, cu, npr, k):
+    cu = np.asarray(cu, np.int32)
+    npr = np.asarray(npr, np.int32)
+    k = np.asarray(k, np.int32)
+    out = np.zeros(cu.size, np.int32)
+    tk = ctypes.c_int64(-1)
+    st = lib.tg_kept_sizes(cu.ctypes.data_as(ctypes.c_void_p), npr.ctypes.data_as(ctypes.c_void_p),
+                           k.ctypes.data_as(ctypes.c_void_p), cu.size - 1,
+                           out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(tk))
+    return st, out, tk.value
+
+
+def test_kept_sizes_matches_oracle(lib):
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        n = int(rng.integers(1, 9))
+        lens = rng.integers(0, 300, n)
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        npr = np.array([rng.integers(0, L + 1) for L in lens])
+        k = rng.integers(0, 400, n)
+        st, out, tk = _kept_sizes(lib, cu, npr, k)
+        assert st == 0
+        want = O.ref_kept_sizes(cu, npr, k)
+        assert np.array_equal(out, want) and tk == want[-1]
+    # the five workloads
+    for cu, npr, k, t in [([0, 1024], [960], [128], 192), ([0, 16384], [15872], [1984], 2496),
+                          ([0, 131072], [130560], [8192], 8704),
+                          ([0, 131072], [130560], [131072], 131072)]:
+        assert _kept_sizes(lib, cu, npr, k)[2] == t
+
+
+def test_kept_sizes_rejects_bad_input(lib):
+    assert _kept_sizes(lib, [0, 10], [5], [-1])[0] == 1
+    assert _kept_sizes(lib, [0, 10], [11], [1])[0] == 1
+    assert _kept_sizes(lib, [0, 10, 5], [1, 0], [1, 1])[0] == 1
+    assert _kept_sizes(lib, [3, 10], [1], [1])[0] == 1
+
+
+def test_workspace_queries(lib):
+    assert lib.tg_score_workspace_size(131072, 1) >= 131072 * 4
+    assert lib.tg_select_workspace_size(131072, 4) >= 4 * 2048 * 4
+    assert lib.tg_score_workspace_size(-1, 1) == 0
+    assert lib.tg_select_workspace_size(0, 1) > 0
+
+
+def _score(lib, **kw):
+    a = dict(x=FAKE, dt=1, xs=2048, t=1024, d=2048, h=256, w1=FAKE, b1=None, w2=FAKE, b2=0.0,
+             pr=FAKE, cu=FAKE, n_seq=1, eps=1e-6, b_raw=FAKE, b=FAKE, ws=FAKE, wsb=0)
+    a.update(kw)
+    return lib.tg_score(a["x"], a["dt"], a["xs"], a["t"], a["d"], a["h"], a["w1"], a["b1"], a["w2"],
+                        a["b2"], a["pr"], a["cu"], a["n_seq"], a["eps"], a["b_raw"], a["b"], a["ws"],
+                        a["wsb"], None)
+
+
+def test_score_validation(lib):
+    assert _score(lib, t=-1) == 1
+    assert _score(lib, n_seq=0) == 1
+    assert _score(lib, eps=-1.0) == 1
+    assert _score(lib, dt=7) == 1
+    assert _score(lib, xs=100) == 1
+    assert _score(lib, w2=None) == 1
+    assert _score(lib, d=2000, xs=2000) == 2          # bf16 needs d % 64 == 0
+    assert _score(lib, h=48) == 2                     # h % 32
+    assert _score(lib, h=512) == 2                    # h <= 256 on the bf16 path
+    assert _score(lib, x=ctypes.c_void_p(0x10002)) == 2
+    assert _score(lib, wsb=16) == 3                   # workspace too small
+    assert "workspace" in lib.tg_last_error().decode()
+
+
+def test_select_validation(lib):
+    def sel(**kw):
+        a = dict(b=FAKE, pr=FAKE, cu=FAKE, k=FAKE, n_seq=1, t=1024, cap=192, idx=FAKE, ws=FAKE,
+                 wsb=0)
+        a.update(kw)
+        return lib.tg_select_topk(a["b"], a["pr"], a["cu"], a["k"], a["n_seq"], a["t"], a["cap"],
+                                  a["idx"], None, None, FAKE, a["ws"], a["wsb"], None)
+    assert sel(n_seq=0) == 1
+    assert sel(cap=-1) == 1
+    assert sel(t=-5) == 1
+    assert sel(k=None) == 1
+    assert sel(idx=None) == 1
+    assert sel(wsb=8) == 3
+
+
+def test_gather_validation(lib):
+    def ga(src=FAKE, ss=4096, nsrc=10, rb=4096, idx=FAKE, n=4, dst=FAKE, ds=4096):
+        return lib.tg_gather(src, ss, nsrc, rb, idx, n, dst, ds, None)
+    assert ga(n=-1) == 1
+    assert ga(rb=-4) == 1
+    assert ga(src=None) == 1
+    assert ga(ss=100, rb=4096) == 1
+    assert ga(rb=4094, ss=4096) == 2
+    assert ga(dst=ctypes.c_void_p(0x10001)) == 2
+    assert ga(n=0) == 0                                # nothing to do, nothing launched
+    assert ga(rb=0) == 0
+
+
+def test_attn_validation(lib):
+    def at(dt=1, t=100, n_seq=1, hq=16, hkv=8, dh=128, q=FAKE, gain=FAKE):
+        return lib.tg_gated_attn(q, FAKE, FAKE, dt, FAKE, t, FAKE, FAKE, FAKE, n_seq, t, hq, hkv,
+                                 dh, gain, FAKE, 0.0, None)
+    assert at(hq=16, hkv=6) == 1
+    assert at(dt=3) == 1
+    assert at(t=-1) == 1
+    assert at(n_seq=0) == 1
+    assert at(dh=96) == 2
+    assert at(hq=12, hkv=4) == 2                      # 3 query heads per KV head
+    assert at(gain=None) == 1
+    assert at(q=ctypes.c_void_p(0x10008)) == 2
+    assert at(t=0) == 0                                # empty: nothing launched

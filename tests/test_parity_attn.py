@@ -1,0 +1,214 @@
+"""tg_gated_attn against the oracle: rel-L2 <= 1e-2 (bf16) and <= 1e-5 (fp32).
+
+The bf16 bar is checked twice: against the oracle on the bf16-rounded
+Q/K/V the kernel sees (kernel error alone) and, for the workloads, against
+the oracle on the unrounded fp64 projections."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import (DEV, bf16_dev, f32_dev, i32_dev, rel_l2, round_bf16, say, to_f64, workload)
+from workloads import bf16_to_f64, random_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+def run_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dtype, sm_scale=None):
+    """q/k/v are fp64 arrays already on the dtype grid; returns fp64 output."""
+    from learned_token_pruning_06_amd import ops
+    if dtype == "bf16":
+        qt, kt, vt = bf16_dev(round_bf16(q)), bf16_dev(round_bf16(k)), bf16_dev(round_bf16(v))
+    else:
+        qt, kt, vt = f32_dev(q), f32_dev(k), f32_dev(v)
+    kc = np.asarray(kept_cu, np.int32)
+    out = ops.gated_attn(qt, kt, vt, f32_dev(kept_b),
+                         None if kept_pos is None else i32_dev(kept_pos), i32_dev(kc),
+                         f32_dev(gain), f32_dev(temp), max_len=int(np.diff(kc).max(initial=0)),
+                         sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+def synth_case(seed, lens, hq, hkv, dh, dtype, with_pos=True, prompt=0):
+    rng = np.random.default_rng(seed)
+    kc = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(kc[-1])
+    q = rng.standard_normal((T, hq, dh))
+    k = rng.standard_normal((T, hkv, dh))
+    v = rng.standard_normal((T, hkv, dh))
+    if dtype == "bf16":
+        q, k, v = (bf16_to_f64(round_bf16(a)) for a in (q, k, v))
+    else:
+        q, k, v = (a.astype(np.float32).astype(np.float64) for a in (q, k, v))
+    kb = rng.standard_normal(T).astype(np.float32).astype(np.float64)
+    pos = np.zeros(T, np.int64)
+    for s in range(len(lens)):
+        n = lens[s]
+        if n:
+            gaps = rng.integers(1, 6, n)
+            pos[kc[s]:kc[s + 1]] = np.cumsum(gaps) - 1 + rng.integers(0, 3)
+            if prompt:
+                kb[kc[s + 1] - min(prompt, n):kc[s + 1]] = 0.0
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    temp = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    return q, k, v, kb, (pos if with_pos else None), kc, gain, temp
+
+
+CASES = [
+    # seed, kept lengths, hq, hkv, dh, dtype
+    (1, [1], 16, 8, 128, "bf16"),
+    (2, [63, 64, 65], 16, 8, 128, "bf16"),
+    (3, [200, 0, 129, 1], 16, 8, 128, "bf16"),
+    (4, [700], 8, 8, 128, "bf16"),        # MHA
+    (5, [333, 257], 16, 4, 128, "bf16"),  # 4 query heads per KV head
+    (6, [500], 32, 4, 128, "bf16"),       # 8 query heads per KV head
+    (7, [300, 45], 8, 4, 64, "bf16"),     # head dim 64
+    (8, [513], 4, 4, 64, "bf16"),
+    (9, [192], 4, 4, 64, "f32"),
+    (10, [77, 0, 130], 16, 8, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}-{c[5]}-dh{c[4]}-g{c[2] // c[3]}"
+                                             for c in CASES])
+def test_attn_synthetic_shapes(case):
+    seed, lens, hq, hkv, dh, dtype = case
+    say(f"attn: seed={seed} lens={lens} hq={hq} hkv={hkv} dh={dh} {dtype}")
+    q, k, v, kb, pos, kc, gain, temp = synth_case(seed, lens, hq, hkv, dh, dtype, prompt=5)
+    got = run_attn(q, k, v, kb, pos, kc, gain, temp, dtype)
+    want = O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp)
+    err = rel_l2(got, want)
+    say(f"  rel-L2 {err:.3e}")
+    assert err <= TOL[dtype]
+    assert np.all(np.isfinite(got))
+
+
+def test_attn_without_positions_and_explicit_scale():
+    say("attn: kept_pos NULL (length factor 1) and sm_scale 0.05")
+    q, k, v, kb, _, kc, gain, temp = synth_case(21, [150, 90], 16, 8, 128, "bf16", with_pos=False)
+    got = run_attn(q, k, v, kb, None, kc, gain, temp, "bf16", sm_scale=0.05)
+    want = O.ref_gated_attn(q, k, v, kb, None, kc, gain, temp, sm_scale=0.05)
+    assert rel_l2(got, want) <= TOL["bf16"]
+
+
+def test_attn_large_scores_exercise_rescaling():
+    """Scores with a wide range move the running maximum by more than the
+    lazy-rescale slack several times along a row."""
+    say("attn: wide score range")
+    q, k, v, kb, pos, kc, gain, temp = synth_case(22, [1000], 16, 8, 128, "bf16")
+    kb = np.linspace(-20, 20, kb.size)
+    got = run_attn(q, k, v, kb, pos, kc, gain, temp * 3, "bf16")
+    want = O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp * 3)
+    assert rel_l2(got, want) <= TOL["bf16"]
+
+
+def test_attn_is_deterministic():
+    from learned_token_pruning_06_amd import ops
+    say("attn: repeat runs identical")
+    q, k, v, kb, pos, kc, gain, temp = synth_case(23, [400, 100], 16, 8, 128, "bf16")
+    args = (bf16_dev(round_bf16(q)), bf16_dev(round_bf16(k)), bf16_dev(round_bf16(v)),
+            f32_dev(kb), i32_dev(pos), i32_dev(kc), f32_dev(gain), f32_dev(temp))
+    o1 = ops.gated_attn(*args)
+    o2 = ops.gated_attn(*args)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------------------------ the workloads
+def _workload_attention(cfg, dtype, rows=None, budget=None):
+    """Oracle gate on the workload, oracle projections of the kept rows, then
+    the kernel on the rounded projections."""
+    g = workload(cfg)
+    wl = g["wl"]
+    bf = dtype == "bf16"
+    xd = bf16_to_f64(g["x"]) if bf else g["x"].astype(np.float64)
+    kk = g["budgets"][0] if budget is None else np.asarray(budget, np.int32)
+    if "b_preset" in g:
+        b = g["b_preset"].astype(np.float64)
+    else:
+        w1 = bf16_to_f64(g["w1"]) if bf else g["w1"]
+        b_raw = np.concatenate([O.ref_score(xd[s:s + 32768], w1, g["b1"], g["w2"], g["b2"])
+                                for s in range(0, xd.shape[0], 32768)])
+        b, _ = O.ref_normalise(b_raw, g["prunable"], g["cu_seqlens"])
+    idx, pos, kb, kc = O.ref_select(b.astype(np.float32), g["prunable"], g["cu_seqlens"], kk)
+    conv = bf16_to_f64 if bf else (lambda a: np.asarray(a, np.float64))
+    q, k, v = O.ref_project(xd[idx], conv(g["wq"]), conv(g["wk"]), conv(g["wv"]), wl.hq, wl.hkv,
+                            wl.dh)
+    if bf:
+        qr, kr, vr = (bf16_to_f64(round_bf16(a)) for a in (q, k, v))
+    else:
+        qr, kr, vr = (a.astype(np.float32).astype(np.float64) for a in (q, k, v))
+    got = run_attn(qr, kr, vr, kb, pos, kc, g["gain"], g["temp"], dtype)
+    want_r = O.ref_gated_attn(qr, kr, vr, kb, pos, kc, g["gain"], g["temp"], rows=rows)
+    want = O.ref_gated_attn(q, k, v, kb, pos, kc, g["gain"], g["temp"], rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    e1, e2 = rel_l2(got[sel], want_r[sel]), rel_l2(got[sel], want[sel])
+    say(f"attn workload {cfg}: rel-L2 vs rounded-input oracle {e1:.3e}, vs fp64 oracle {e2:.3e}")
+    assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
+
+
+def test_attn_tiny_fp32_workload():
+    say("attn: tiny fp32 workload")
+    _workload_attention(0, "f32")
+
+
+def test_attn_16k_bf16_workload():
+    say("attn: 16k bf16 workload")
+    _workload_attention(1, "bf16")
+
+
+def test_attn_budget_sweep_largest_budget_sampled_rows():
+    say("attn: 32k sweep, largest budget, sampled rows")
+    g = workload(2)
+    kmax = max(int(k[0]) for k in g["budgets"])
+    T = kmax + 512
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, 2, T - 1, T - 2], rng.integers(0, T, 40)]))
+    _workload_attention(2, "bf16", rows=rows, budget=[kmax])
+
+
+def test_attn_ragged_batch_sampled_rows():
+    say("attn: ragged 4-sequence batch, sampled rows")
+    g = workload(4)
+    wl = g["wl"]
+    kc = O.ref_kept_sizes(wl.cu_seqlens(), wl.seq_doc, wl.budgets[0])
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([kc[:-1], kc[1:] - 1, rng.integers(0, kc[-1], 60)]))
+    _workload_attention(4, "bf16", rows=rows)
+
+
+def test_attn_128k_pruned_sampled_rows():
+    say("attn: 128k workload, K=8192, sampled rows")
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 8703, 8702, 8191, 8192],
+                                     rng.integers(0, 8704, 48)]))
+    _workload_attention(3, "bf16", rows=rows)
+
+
+def test_attn_128k_full_context_sampled_rows():
+    """All 131072 tokens kept (the unpruned reference point).  Q/K/V are
+    stand-in N(0,1) draws (projecting every row on the host is too slow)."""
+    say("attn: 128k full-context lane, sampled rows")
+    T, hq, hkv, dh = 131072, 16, 8, 128
+    q, k, v = random_qkv(3, T, hq, hkv, dh)
+    rng = np.random.default_rng(33)
+    kb = rng.standard_normal(T).astype(np.float32).astype(np.float64)
+    kb[-512:] = 0.0
+    pos = np.arange(T)
+    kc = np.array([0, T])
+    g = workload(1)
+    from learned_token_pruning_06_amd import ops
+    out = ops.gated_attn(bf16_dev(q), bf16_dev(k), bf16_dev(v), f32_dev(kb), i32_dev(pos),
+                         i32_dev(kc), f32_dev(g["gain"]), f32_dev(g["temp"]), max_len=T)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 64, 131071, 131070, 65536], rng.integers(0, T, 10)]))
+    got = to_f64(out[torch.from_numpy(rows).to(DEV)])
+    qd, kd, vd = bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v)
+    want = O.ref_gated_attn(qd, kd, vd, kb, pos, kc, g["gain"], g["temp"], rows=rows)[rows]
+    err = rel_l2(got, want)
+    say(f"  full-context rel-L2 {err:.3e}")
+    assert err <= TOL["bf16"]
