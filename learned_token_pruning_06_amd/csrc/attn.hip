@@ -5,28 +5,30 @@
 //
 // Flash-style causal attention over the kept tokens of each sequence.
 // In the log2 domain the logit is c_i * (q_i.k_j + beta_j) with
-//   c_i = tau_i * s * log2(e)   (one scalar per query row)
+//   c_i = tau_i * s * log2(e)   (one scalar per query row, > 0)
 //   beta_j = gain_h * b_j / s   (one scalar per key and head),
 // so the per-key bias is loaded into the accumulator before the Q.K^T MFMAs
-// and costs no extra vector work; the temperature is the per-row scale that
-// flash attention applies anyway.
+// and costs no vector work, and the temperature is folded into the single
+// FMA that forms the exponent: p = exp2(c_i * acc - m_i).  Because c_i > 0
+// the running maximum is taken on the unscaled accumulator.
 //
 // Work decomposition (wave64, gfx950 v_mfma_f32_32x32x16_bf16):
-//  - a workgroup of 4 waves owns one block of query rows of one sequence and
-//    HPW query heads that share one KV head (GQA): every K/V tile loaded to
-//    LDS feeds all HPW heads;
-//  - a wave owns 64 query rows of one head.  It computes S^T = K.Q^T (keys
+//  - a workgroup of 8 waves owns one block of query rows of one sequence and
+//    HPW query heads that share one KV head (GQA): every K/V tile staged in
+//    LDS feeds all HPW heads; two waves per SIMD let the hardware overlap one
+//    wave's softmax (vector ALU) with the other's MFMAs;
+//  - a wave owns 32 query rows of one head.  It computes S^T = K.Q^T (keys
 //    on the MFMA M axis, queries on N), so each lane holds one query's
 //    logits: the softmax statistics are per-lane scalars plus one exchange
 //    between the two lane halves;
-//  - P^T from the accumulators is already the B operand of O^T = V^T.P^T
+//  - P^T from the accumulators is directly the B operand of O^T = V^T.P^T
 //    (keys permuted consistently between the two operands), so the output
 //    accumulator also holds one query per lane;
 //  - V is transposed while it is staged to LDS ([d][key]) so its MFMA operand
 //    reads are contiguous;
 //  - K/V tiles of 64 keys are double-buffered in LDS with one barrier per
-//    tile; causal tiles past a wave's rows are skipped, and query blocks are
-//    issued in decreasing amount of work (last block of a sequence first);
+//    tile; causal masking runs only on diagonal tiles, tiles past a wave's
+//    rows are skipped, and query blocks are issued longest first;
 //  - the running maximum is only moved when it grows by more than 2^8 in
 //    the exponent (exact: the normaliser absorbs the stale maximum).
 #include "common.h"
@@ -39,10 +41,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int BKV = 64;                 // keys per tile
+constexpr int NWAVE = 8;                // waves per workgroup
+constexpr int NTHR = 64 * NWAVE;
+constexpr int QW = 32;                  // query rows per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr float kMinScale = 1e-30f;     // keeps c_i > 0 so masked keys stay -inf
 
 TG_DEVINL bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+TG_DEVINL uint32_t word(const uint4& u, int i) {
+  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
+}
 
 TG_DEVINL uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -51,19 +61,19 @@ TG_DEVINL uint32_t pack_bf16x2(float a, float b) {
 
 template <int DH, int HPW>
 struct AttnCfg {
-  static constexpr int QB = 256 / HPW;          // query rows per workgroup
+  static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
   static constexpr int KROW = DH + 8;            // bf16 per K row in LDS (16 B pad)
   static constexpr int VROW = BKV + 4;           // bf16 per V^T row in LDS (8 B pad)
   static constexpr int KT = DH / 16;             // MFMA K-steps over the head dim
   static constexpr int DT = DH / 32;             // output tiles over the head dim
   static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile
-  static constexpr int KVPT = (KVEC + 255) / 256;
-  static constexpr int VPAIRS = 16 * (DH / 8);   // (4-key group, 8-dim chunk) pairs
-  static constexpr int VPPT = (VPAIRS + 255) / 256;
+  static constexpr int KVPT = (KVEC + NTHR - 1) / NTHR;
+  static constexpr int VUNITS = (BKV / 2) * (DH / 8);   // (2-key pair, 8-dim chunk) units
+  static constexpr int VUPT = (VUNITS + NTHR - 1) / NTHR;
 };
 
 template <int DH, int HPW>
-__global__ __launch_bounds__(256) void gated_attn_bf16(
+__global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
 
-  // ---- which (sequence, query block): last slots first (longest-first)
+  // ---- which (sequence, query block): last slots first (longest first)
   const int64_t slot = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int s = seq_of_slot(kept_cu, n_seq, slot, C::QB);
   if (s < 0) return;
@@ -93,34 +103,29 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
   const int hbase = kvh * G + (blockIdx.y % groups_y) * HPW;
   const int hl = wv % HPW;
   const int head = hbase + hl;
-  const int wq0 = q0 + 64 * (wv / HPW);          // first query row of this wave (in sequence)
-  const float s_eff = sm_scale;
+  const int wq0 = q0 + QW * (wv / HPW);          // first query row of this wave (in sequence)
 
-  // ---- per-lane query constants: c = tau * s * log2(e)
-  float cq[2];
-  bool qvalid[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int a = wq0 + 32 * nt + n;
-    qvalid[nt] = a < len;
+  // ---- per-lane query constant c = tau * s * log2(e), one query per lane
+  const int qa = wq0 + n;
+  const bool qvalid = qa < len;
+  float cq = kMinScale;
+  if (qvalid) {
     float lam = 1.0f;
-    if (kept_pos && qvalid[nt]) {
-      const float m = (float)(a + 1);
-      const float p = (float)(kept_pos[lo + a] + 1);
+    if (kept_pos) {
+      const float m = (float)(qa + 1);
+      const float p = (float)(kept_pos[lo + qa] + 1);
       lam = logf(m) / logf(fmaxf(2.0f, p));
     }
-    cq[nt] = qvalid[nt] ? temp[head] * lam * s_eff * kLog2e : 0.0f;
+    cq = fmaxf(temp[head] * lam * sm_scale * kLog2e, kMinScale);
   }
 
   // ---- Q fragments (B operand of S^T = K.Q^T): lane holds q[row][16kk + 8g .. +8]
-  bf16x8 qf[2][C::KT];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    int a = wq0 + 32 * nt + n;
-    a = a < len ? a : len - 1;
+  bf16x8 qf[C::KT];
+  {
+    const int a = qvalid ? qa : len - 1;
     const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)(lo + a) * hq + head) * DH);
 #pragma unroll
-    for (int kk = 0; kk < C::KT; ++kk) qf[nt][kk] = as_bf16x8(qp[2 * kk + g]);
+    for (int kk = 0; kk < C::KT; ++kk) qf[kk] = as_bf16x8(qp[2 * kk + g]);
   }
 
   // ---- loaders (global -> registers -> LDS) for one tile of 64 keys
@@ -130,37 +135,36 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
   const uint16_t* kb_ = k + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   const uint16_t* vb_ = v + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   // loader thread tid < 64*HPW stages key (tid % 64) for head (tid / 64)
-  const float my_bscale = tid < BKV * HPW ? gain[hbase + tid / BKV] / s_eff : 0.0f;
+  const float my_bscale = tid < BKV * HPW ? gain[hbase + tid / BKV] / sm_scale : 0.0f;
 
-  uint4 kreg[C::KVPT];
-  uint4 vreg[C::VPPT][4];
+  // prefetch registers for one tile: K as up to two 16-byte vectors per
+  // thread, V as one (2-key, 8-dim) unit per thread, one bias value
+  static_assert(C::KVPT <= 2 && C::VUPT == 1, "loader shape");
+  uint4 kreg0 = make_uint4(0, 0, 0, 0), kreg1 = make_uint4(0, 0, 0, 0);
+  uint4 vreg0 = make_uint4(0, 0, 0, 0), vreg1 = make_uint4(0, 0, 0, 0);
   float breg = 0.f;
+  // every thread loads; units past the tile wrap around (their stores are skipped)
+  const int kvi0 = tid % C::KVEC, kvi1 = (tid + NTHR) % C::KVEC;
+  const int vu = tid % C::VUNITS;
+  const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
 
   auto load_tile = [&](int t) {
     const int kv0 = t * BKV;
-#pragma unroll
-    for (int i = 0; i < C::KVPT; ++i) {
-      const int vi = tid + 256 * i;
-      if (vi < C::KVEC) {
-        const int key = vi / (DH / 8), ch = vi % (DH / 8);
-        int kr = kv0 + key;
-        kr = kr < len ? kr : len - 1;
-        kreg[i] = *reinterpret_cast<const uint4*>(kb_ + (int64_t)kr * kvstride + 8 * ch);
-      }
+    {
+      int kr = kv0 + kvi0 / (DH / 8);
+      kr = kr < len ? kr : len - 1;
+      kreg0 = *reinterpret_cast<const uint4*>(kb_ + (int64_t)kr * kvstride + 8 * (kvi0 % (DH / 8)));
     }
-#pragma unroll
-    for (int i = 0; i < C::VPPT; ++i) {
-      const int pi = tid + 256 * i;
-      if (pi < C::VPAIRS) {
-        const int kg = pi % 16, dc = pi / 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kr = kv0 + 4 * kg + r;
-          kr = kr < len ? kr : len - 1;
-          vreg[i][r] = *reinterpret_cast<const uint4*>(vb_ + (int64_t)kr * kvstride + 8 * dc);
-        }
-      }
+    if (C::KVPT == 2) {
+      int kr = kv0 + kvi1 / (DH / 8);
+      kr = kr < len ? kr : len - 1;
+      kreg1 = *reinterpret_cast<const uint4*>(kb_ + (int64_t)kr * kvstride + 8 * (kvi1 % (DH / 8)));
     }
+    int k0 = kv0 + 2 * vkp, k1 = k0 + 1;
+    k0 = k0 < len ? k0 : len - 1;
+    k1 = k1 < len ? k1 : len - 1;
+    vreg0 = *reinterpret_cast<const uint4*>(vb_ + (int64_t)k0 * kvstride + 8 * vdc);
+    vreg1 = *reinterpret_cast<const uint4*>(vb_ + (int64_t)k1 * kvstride + 8 * vdc);
     if (tid < BKV * HPW) {
       int kr = kv0 + (tid % BKV);
       kr = kr < len ? kr : len - 1;
@@ -168,47 +172,31 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
     }
   };
   auto store_tile = [&](int buf) {
+    if (tid < C::KVEC)
+      *reinterpret_cast<uint4*>(&sk[buf][(kvi0 / (DH / 8)) * C::KROW + 8 * (kvi0 % (DH / 8))]) = kreg0;
+    if (C::KVPT == 2 && tid + NTHR < C::KVEC)
+      *reinterpret_cast<uint4*>(&sk[buf][(kvi1 / (DH / 8)) * C::KROW + 8 * (kvi1 % (DH / 8))]) = kreg1;
+    if (tid < C::VUNITS) {
 #pragma unroll
-    for (int i = 0; i < C::KVPT; ++i) {
-      const int vi = tid + 256 * i;
-      if (vi < C::KVEC) {
-        const int key = vi / (DH / 8), ch = vi % (DH / 8);
-        *reinterpret_cast<uint4*>(&sk[buf][key * C::KROW + 8 * ch]) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPPT; ++i) {
-      const int pi = tid + 256 * i;
-      if (pi < C::VPAIRS) {
-        const int kg = pi % 16, dc = pi / 16;
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wi = e >> 1, sh = (e & 1) * 16;
-          const uint32_t a0 = (w0[wi] >> sh) & 0xffffu, a1 = (w1[wi] >> sh) & 0xffffu;
-          const uint32_t a2 = (w2[wi] >> sh) & 0xffffu, a3 = (w3[wi] >> sh) & 0xffffu;
-          uint2 pk = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-          *reinterpret_cast<uint2*>(&sv[buf][(8 * dc + e) * C::VROW + 4 * kg]) = pk;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a0 = word(vreg0, e >> 1), a1 = word(vreg1, e >> 1);
+        const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
+                                    : ((a0 & 0xffffu) | (a1 << 16));
+        *reinterpret_cast<uint32_t*>(&sv[buf][(8 * vdc + e) * C::VROW + 2 * vkp]) = pk;
       }
     }
     if (tid < BKV * HPW) sbias[buf][tid / BKV][tid % BKV] = breg * my_bscale;
   };
 
-  // ---- running state
-  floatx16 oacc[C::DT][2];
+  // ---- running state (one query per lane)
+  floatx16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  const int wq_last = wq0 + 63 < len - 1 ? wq0 + 63 : len - 1;   // last valid row of the wave
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float mrun = -INFINITY;
+  float lsum = 0.f;
+  const int wq_last = wq0 + QW - 1 < len - 1 ? wq0 + QW - 1 : len - 1;
   const bool wave_has_rows = wq0 < len;
 
   load_tile(0);
@@ -222,21 +210,18 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
     if (more) load_tile(t + 1);
 
     if (wave_has_rows && kv0 <= wq_last) {
-      // S^T = beta + K.Q^T  (keys: 32mt + 8(r/4) + 4g + r%4, queries: 32nt + n)
-      floatx16 sacc[2][2];
+      // S^T = beta + K.Q^T  (keys: 32mt + 8(r/4) + 4g + r%4, query: n)
+      floatx16 sacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const float4 bb =
               *reinterpret_cast<const float4*>(&sbias[buf][hl][32 * mt + 8 * r4 + 4 * g]);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            sacc[mt][nt][4 * r4 + 0] = bb.x;
-            sacc[mt][nt][4 * r4 + 1] = bb.y;
-            sacc[mt][nt][4 * r4 + 2] = bb.z;
-            sacc[mt][nt][4 * r4 + 3] = bb.w;
-          }
+          sacc[mt][4 * r4 + 0] = bb.x;
+          sacc[mt][4 * r4 + 1] = bb.y;
+          sacc[mt][4 * r4 + 2] = bb.z;
+          sacc[mt][4 * r4 + 3] = bb.w;
         }
 #pragma unroll
       for (int kk = 0; kk < C::KT; ++kk) {
@@ -244,72 +229,60 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
         for (int mt = 0; mt < 2; ++mt) {
           const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
               &sk[buf][(32 * mt + n) * C::KROW + 16 * kk + 8 * g]));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][kk], sacc[mt][nt],
-                                                                   0, 0, 0);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[mt], 0, 0, 0);
         }
       }
-      // scale to log2 units, causal mask on the diagonal tiles
-      const bool diag = kv0 + BKV - 1 > wq0;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int a = wq0 + 32 * nt + n;
+      // causal mask, only where the tile reaches past the wave's first row
+      if (kv0 + BKV - 1 > wq0) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float x = sacc[mt][nt][r] * cq[nt];
-            if (diag) {
-              const int kj = kv0 + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-              x = kj > a ? -INFINITY : x;
-            }
-            sacc[mt][nt][r] = x;
+            const int kj = kv0 + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+            sacc[mt][r] = kj > qa ? -INFINITY : sacc[mt][r];
           }
       }
-      // online softmax, one query per lane (two lane halves share a query)
-      bf16x8 pf[2][4];
+      // online softmax on the unscaled accumulator (c_i > 0)
+      float mx = sacc[0][0];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float mx = -INFINITY;
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
+      if (__any(mx > mrun + kRescaleSlack)) {
+        const float mnew = fmaxf(mrun, mx);
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        lsum *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const bool grow = mx > mrun[nt] + kRescaleSlack;
-        if (__any(grow)) {
-          const float mnew = fmaxf(mrun[nt], mx);
-          const float alpha = __builtin_amdgcn_exp2f(mrun[nt] - mnew);
-          lsum[nt] *= alpha;
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt)
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        mrun = mnew;
+      }
+      const float negm = mrun == -INFINITY ? 0.0f : -mrun;
+      float ls = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
-          mrun[nt] = mnew;
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], cq, negm));
+          sacc[mt][r] = p;
+          ls += p;
         }
-        const float mref = mrun[nt] == -INFINITY ? 0.0f : mrun[nt];
-        float ls = 0.f;
+      lsum += ls;
+      // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
+      // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
+      bf16x8 pf[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sacc[mt][nt][r] - mref);
-            sacc[mt][nt][r] = p;
-            ls += p;
-          }
-        lsum[nt] += ls;
-        // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
-        // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          uint4 u;
-          u.x = pack_bf16x2(sacc[kk >> 1][nt][8 * (kk & 1) + 0], sacc[kk >> 1][nt][8 * (kk & 1) + 1]);
-          u.y = pack_bf16x2(sacc[kk >> 1][nt][8 * (kk & 1) + 2], sacc[kk >> 1][nt][8 * (kk & 1) + 3]);
-          u.z = pack_bf16x2(sacc[kk >> 1][nt][8 * (kk & 1) + 4], sacc[kk >> 1][nt][8 * (kk & 1) + 5]);
-          u.w = pack_bf16x2(sacc[kk >> 1][nt][8 * (kk & 1) + 6], sacc[kk >> 1][nt][8 * (kk & 1) + 7]);
-          pf[nt][kk] = as_bf16x8(u);
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        const floatx16& sa = sacc[kk >> 1];
+        const int o = 8 * (kk & 1);
+        uint4 u;
+        u.x = pack_bf16x2(sa[o + 0], sa[o + 1]);
+        u.y = pack_bf16x2(sa[o + 2], sa[o + 3]);
+        u.z = pack_bf16x2(sa[o + 4], sa[o + 5]);
+        u.w = pack_bf16x2(sa[o + 6], sa[o + 7]);
+        pf[kk] = as_bf16x8(u);
       }
       // O^T += V^T . P^T  (A operand: V^T rows d = 32dt + n, keys as above)
 #pragma unroll
@@ -320,10 +293,7 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
           const uint2 lo2 = *reinterpret_cast<const uint2*>(vp);
           const uint2 hi2 = *reinterpret_cast<const uint2*>(vp + 8);
           const bf16x8 a = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[nt][kk], oacc[dt][nt],
-                                                                   0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[dt], 0, 0, 0);
         }
       }
     }
@@ -332,23 +302,19 @@ __global__ __launch_bounds__(256) void gated_attn_bf16(
   }
 
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  if (!qvalid) return;
+  const float inv = 1.0f / lt;
+  uint16_t* op = out + ((int64_t)(lo + qa) * hq + head) * DH;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int a = wq0 + 32 * nt + n;
-    const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32, 64);
-    if (!(a < len)) continue;
-    const float inv = 1.0f / lt;
-    uint16_t* op = out + ((int64_t)(lo + a) * hq + head) * DH;
+  for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        uint2 pk;
-        pk.x = pack_bf16x2(oacc[dt][nt][4 * r4 + 0] * inv, oacc[dt][nt][4 * r4 + 1] * inv);
-        pk.y = pack_bf16x2(oacc[dt][nt][4 * r4 + 2] * inv, oacc[dt][nt][4 * r4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * g) = pk;
-      }
-  }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      uint2 pk;
+      pk.x = pack_bf16x2(oacc[dt][4 * r4 + 0] * inv, oacc[dt][4 * r4 + 1] * inv);
+      pk.y = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + 32 * dt + 8 * r4 + 4 * g) = pk;
+    }
 }
 
 template <int DH, int HPW>
@@ -360,7 +326,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
   const int G = hq / hkv;
   const int groups_y = G / HPW;
   const dim3 grid((unsigned)(n_seq + (t_kept + QB - 1) / QB), (unsigned)(hkv * groups_y));
-  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW>), grid, dim3(NTHR), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), kept_b, kept_pos,
                      kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, gain, temp, sm_scale);

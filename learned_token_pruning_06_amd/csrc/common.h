@@ -99,10 +99,13 @@ TG_DEVINL int block_excl_scan(int v, int* scratch, int* total) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte loads/stores on a native vector type (HIP's uint4 is a struct with
+// a union inside, and copies of it can keep values in scratch memory)
+TG_DEVINL u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+TG_DEVINL void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 // 16-byte load that does not keep the line in cache (streamed operands)
-TG_DEVINL uint4 ld_nt16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+TG_DEVINL u32x4 ld_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 TG_DEVINL uint32_t ld_acquire_u32(const uint32_t* p) {

@@ -26,15 +26,15 @@ __global__ __launch_bounds__(kThreads) void gather_vec16(
     srow[i] = valid[i] ? s : 0;
   }
   for (int64_t vbase = 0; vbase < n_vec; vbase += kThreads * 2) {
-    uint4 buf[kRows][2];
+    u32x4 buf[kRows][2];
 #pragma unroll
     for (int i = 0; i < kRows; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t v = vbase + threadIdx.x + j * kThreads;
-        uint4 z = make_uint4(0, 0, 0, 0);
+        u32x4 z = {0u, 0u, 0u, 0u};
         if (valid[i] && v < n_vec)
-          z = ld_nt16(reinterpret_cast<const uint4*>(src + srow[i] * src_stride) + v);
+          z = ld_nt16(reinterpret_cast<const u32x4*>(src + srow[i] * src_stride) + v);
         buf[i][j] = z;
       }
 #pragma unroll
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void gather_vec16(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t v = vbase + threadIdx.x + j * kThreads;
-        if (v < n_vec) reinterpret_cast<uint4*>(dst + r * dst_stride)[v] = buf[i][j];
+        if (v < n_vec) reinterpret_cast<u32x4*>(dst + r * dst_stride)[v] = buf[i][j];
       }
     }
   }
