@@ -6,29 +6,35 @@
 // Flash-style causal attention over the kept tokens of each sequence.
 // In the log2 domain the logit is c_i * (q_i.k_j + beta_j) with
 //   c_i = tau_i * s * log2(e)   (one scalar per query row, > 0)
-//   beta_j = gain_h * b_j / s   (one scalar per key and head),
-// so the per-key bias is loaded into the accumulator before the Q.K^T MFMAs
-// and costs no vector work, and the temperature is folded into the single
-// FMA that forms the exponent: p = exp2(c_i * acc - m_i).  Because c_i > 0
-// the running maximum is taken on the unscaled accumulator.
+//   beta_j = gain_h * b_j / s   (one scalar per key and head).
+// beta rides in the matrix product itself: each staged K row carries 16
+// extra bf16 columns holding beta_j split into a high and a low bf16 part
+// for each head, and the query side multiplies them by a constant selector
+// vector, so one extra MFMA K-step adds beta_j to q.k exactly (to ~2^-17
+// relative).  The temperature folds into the single FMA that forms the
+// exponent, p = exp2(c_i * acc - m_i); because c_i > 0 the running maximum
+// is taken on the unscaled accumulator.
 //
 // Work decomposition (wave64, gfx950 v_mfma_f32_32x32x16_bf16):
 //  - a workgroup of 8 waves owns one block of query rows of one sequence and
 //    HPW query heads that share one KV head (GQA): every K/V tile staged in
-//    LDS feeds all HPW heads; two waves per SIMD let the hardware overlap one
-//    wave's softmax (vector ALU) with the other's MFMAs;
+//    LDS feeds all HPW heads; two waves per SIMD;
 //  - a wave owns 32 query rows of one head.  It computes S^T = K.Q^T (keys
 //    on the MFMA M axis, queries on N), so each lane holds one query's
 //    logits: the softmax statistics are per-lane scalars plus one exchange
 //    between the two lane halves;
 //  - P^T from the accumulators is directly the B operand of O^T = V^T.P^T
-//    (keys permuted consistently between the two operands), so the output
-//    accumulator also holds one query per lane;
-//  - V is transposed while it is staged to LDS ([d][key]) so its MFMA operand
-//    reads are contiguous;
-//  - K/V tiles of 64 keys are double-buffered in LDS with one barrier per
-//    tile; causal masking runs only on diagonal tiles, tiles past a wave's
-//    rows are skipped, and query blocks are issued longest first;
+//    with keys permuted consistently between the two operands; V is
+//    transposed into LDS ([d][key]) in that permuted key order, so each lane
+//    reads its 8 keys with one 16-byte load;
+//  - software pipelining: the Q.K^T MFMAs of tile t+1 are issued before the
+//    softmax of tile t, so the vector ALU and the matrix cores work at the
+//    same time; K/V tiles are triple-buffered in LDS with one barrier per
+//    tile;
+//  - causal masking runs only on diagonal tiles, tiles past a wave's rows
+//    are skipped, query blocks are issued longest first, and the blocks of
+//    one KV head share an XCD (blocks are dealt round-robin over the 8 XCDs,
+//    so the head index is taken from the low bits of the block index);
 //  - the running maximum is only moved when it grows by more than 2^8 in
 //    the exponent (exact: the normaliser absorbs the stale maximum).
 #include "common.h"
@@ -40,36 +46,52 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// Schedule switches (compile-time): TG_ATTN_PIPE issues the Q.K^T MFMAs of
+// tile t+1 before the softmax of tile t (costs 32 registers); TG_ATTN_PRIO
+// raises the wave priority while it issues MFMA runs.
+#ifndef TG_ATTN_PIPE
+#define TG_ATTN_PIPE 0
+#endif
+#ifndef TG_ATTN_PRIO
+#define TG_ATTN_PRIO 0
+#endif
+
 constexpr int BKV = 64;                 // keys per tile
 constexpr int NWAVE = 8;                // waves per workgroup
 constexpr int NTHR = 64 * NWAVE;
 constexpr int QW = 32;                  // query rows per wave
+constexpr int NBUF = 3;                 // LDS tile buffers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kMinScale = 1e-30f;     // keeps c_i > 0 so masked keys stay -inf
 
-TG_DEVINL bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-TG_DEVINL uint32_t word(const uint4& u, int i) {
-  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
-}
+TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 TG_DEVINL uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// position of key k of a tile in a V^T row: inside each group of 16 keys the
+// blocks [4..7] and [8..11] are swapped, so that the 8 keys one lane needs
+// for an MFMA K-step (16kk + 8(e/4) + 4g + e%4, e < 8) are contiguous
+TG_DEVINL int vpos(int k) {
+  const int r = k & 15;
+  return (k & ~15) | (r < 4 || r >= 12 ? r : (r < 8 ? r + 4 : r - 4));
+}
+
 template <int DH, int HPW>
 struct AttnCfg {
   static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
-  static constexpr int KROW = DH + 8;            // bf16 per K row in LDS (16 B pad)
-  static constexpr int VROW = BKV + 4;           // bf16 per V^T row in LDS (8 B pad)
+  static constexpr int KROW = DH + 24;           // K row: DH values, 16 bias columns, 8 pad
+  static constexpr int VROW = BKV + 8;           // V^T row: 64 keys, 8 pad
   static constexpr int KT = DH / 16;             // MFMA K-steps over the head dim
   static constexpr int DT = DH / 32;             // output tiles over the head dim
   static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile
   static constexpr int KVPT = (KVEC + NTHR - 1) / NTHR;
   static constexpr int VUNITS = (BKV / 2) * (DH / 8);   // (2-key pair, 8-dim chunk) units
-  static constexpr int VUPT = (VUNITS + NTHR - 1) / NTHR;
+  static constexpr int KTILE = BKV * KROW;       // bf16 per K buffer
+  static constexpr int VTILE = DH * VROW;        // bf16 per V^T buffer
 };
 
 template <int DH, int HPW>
@@ -77,19 +99,22 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
-    int t_kept, int hq, int hkv, int groups_y, const float* __restrict__ gain,
+    int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
     const float* __restrict__ temp, float sm_scale) {
   using C = AttnCfg<DH, HPW>;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][BKV * C::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][DH * C::VROW];
-  __shared__ __attribute__((aligned(16))) float sbias[2][HPW][BKV];
+  static_assert(C::KVPT <= 2 && C::VUNITS <= NTHR, "loader shape");
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF * C::VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
 
-  // ---- which (sequence, query block): last slots first (longest first)
-  const int64_t slot = (int64_t)gridDim.x - 1 - blockIdx.x;
+  // ---- block -> (head group, sequence, query block); head group from the
+  // low bits (one XCD per KV head), query slots last-first (longest first)
+  const int n_hg = hkv * groups_y;
+  const int hg = (int)(blockIdx.x % (unsigned)n_hg);
+  const int64_t slot = (int64_t)n_slots - 1 - (int64_t)(blockIdx.x / (unsigned)n_hg);
   const int s = seq_of_slot(kept_cu, n_seq, slot, C::QB);
   if (s < 0) return;
   // rows are clamped to [0, t_kept): inconsistent offsets cannot read out of bounds
@@ -99,8 +124,8 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   if (q0 >= len) return;
 
   const int G = hq / hkv;
-  const int kvh = blockIdx.y / groups_y;
-  const int hbase = kvh * G + (blockIdx.y % groups_y) * HPW;
+  const int kvh = hg / groups_y;
+  const int hbase = kvh * G + (hg % groups_y) * HPW;
   const int hl = wv % HPW;
   const int head = hbase + hl;
   const int wq0 = q0 + QW * (wv / HPW);          // first query row of this wave (in sequence)
@@ -119,73 +144,105 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     cq = fmaxf(temp[head] * lam * sm_scale * kLog2e, kMinScale);
   }
 
-  // ---- Q fragments (B operand of S^T = K.Q^T): lane holds q[row][16kk + 8g .. +8]
+  // ---- Q fragments (B operand of S^T = K.Q^T): lane holds q[row][16kk + 8g .. +8],
+  // plus the selector of this head's two bias columns (16 extra columns, lane half 0)
   bf16x8 qf[C::KT];
   {
     const int a = qvalid ? qa : len - 1;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)(lo + a) * hq + head) * DH);
+    const uint16_t* qp = q + ((int64_t)(lo + a) * hq + head) * DH;
 #pragma unroll
-    for (int kk = 0; kk < C::KT; ++kk) qf[kk] = as_bf16x8(qp[2 * kk + g]);
+    for (int kk = 0; kk < C::KT; ++kk) qf[kk] = as_bf16x8(ld16(qp + 16 * kk + 8 * g));
   }
+  bf16x8 qsel;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    qsel[e] = (__bf16)((g == 0 && (e >> 1) == hl) ? 1.0f : 0.0f);
 
-  // ---- loaders (global -> registers -> LDS) for one tile of 64 keys
+  // ---- tile loaders (global -> registers -> LDS)
   const int q_end = q0 + C::QB < len ? q0 + C::QB : len;
   const int n_tiles = (q_end + BKV - 1) / BKV;
   const int64_t kvstride = (int64_t)hkv * DH;     // elements between token rows of k, v
   const uint16_t* kb_ = k + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   const uint16_t* vb_ = v + (int64_t)lo * kvstride + (int64_t)kvh * DH;
-  // loader thread tid < 64*HPW stages key (tid % 64) for head (tid / 64)
-  const float my_bscale = tid < BKV * HPW ? gain[hbase + tid / BKV] / sm_scale : 0.0f;
-
-  // prefetch registers for one tile: K as up to two 16-byte vectors per
-  // thread, V as one (2-key, 8-dim) unit per thread, one bias value
-  static_assert(C::KVPT <= 2 && C::VUPT == 1, "loader shape");
-  uint4 kreg0 = make_uint4(0, 0, 0, 0), kreg1 = make_uint4(0, 0, 0, 0);
-  uint4 vreg0 = make_uint4(0, 0, 0, 0), vreg1 = make_uint4(0, 0, 0, 0);
-  float breg = 0.f;
   // every thread loads; units past the tile wrap around (their stores are skipped)
   const int kvi0 = tid % C::KVEC, kvi1 = (tid + NTHR) % C::KVEC;
   const int vu = tid % C::VUNITS;
   const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
+  const int vdst = vpos(2 * vkp);
+  float bsc[4];                                   // gain_h / s of the HPW heads
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
+
+  u32x4 kreg0 = {0u, 0u, 0u, 0u}, kreg1 = {0u, 0u, 0u, 0u};
+  u32x4 vreg0 = {0u, 0u, 0u, 0u}, vreg1 = {0u, 0u, 0u, 0u};
+  float breg = 0.f;
 
   auto load_tile = [&](int t) {
     const int kv0 = t * BKV;
     {
       int kr = kv0 + kvi0 / (DH / 8);
       kr = kr < len ? kr : len - 1;
-      kreg0 = *reinterpret_cast<const uint4*>(kb_ + (int64_t)kr * kvstride + 8 * (kvi0 % (DH / 8)));
+      kreg0 = ld16(kb_ + (int64_t)kr * kvstride + 8 * (kvi0 % (DH / 8)));
     }
     if (C::KVPT == 2) {
       int kr = kv0 + kvi1 / (DH / 8);
       kr = kr < len ? kr : len - 1;
-      kreg1 = *reinterpret_cast<const uint4*>(kb_ + (int64_t)kr * kvstride + 8 * (kvi1 % (DH / 8)));
+      kreg1 = ld16(kb_ + (int64_t)kr * kvstride + 8 * (kvi1 % (DH / 8)));
     }
     int k0 = kv0 + 2 * vkp, k1 = k0 + 1;
     k0 = k0 < len ? k0 : len - 1;
     k1 = k1 < len ? k1 : len - 1;
-    vreg0 = *reinterpret_cast<const uint4*>(vb_ + (int64_t)k0 * kvstride + 8 * vdc);
-    vreg1 = *reinterpret_cast<const uint4*>(vb_ + (int64_t)k1 * kvstride + 8 * vdc);
-    if (tid < BKV * HPW) {
-      int kr = kv0 + (tid % BKV);
-      kr = kr < len ? kr : len - 1;
-      breg = kept_b[lo + kr];
-    }
+    vreg0 = ld16(vb_ + (int64_t)k0 * kvstride + 8 * vdc);
+    vreg1 = ld16(vb_ + (int64_t)k1 * kvstride + 8 * vdc);
+    int kr = kv0 + (tid % BKV);
+    kr = kr < len ? kr : len - 1;
+    breg = kept_b[lo + kr];
   };
   auto store_tile = [&](int buf) {
+    uint16_t* skb = sk + buf * C::KTILE;
+    uint16_t* svb = sv + buf * C::VTILE;
     if (tid < C::KVEC)
-      *reinterpret_cast<uint4*>(&sk[buf][(kvi0 / (DH / 8)) * C::KROW + 8 * (kvi0 % (DH / 8))]) = kreg0;
+      st16(&skb[(kvi0 / (DH / 8)) * C::KROW + 8 * (kvi0 % (DH / 8))], kreg0);
     if (C::KVPT == 2 && tid + NTHR < C::KVEC)
-      *reinterpret_cast<uint4*>(&sk[buf][(kvi1 / (DH / 8)) * C::KROW + 8 * (kvi1 % (DH / 8))]) = kreg1;
+      st16(&skb[(kvi1 / (DH / 8)) * C::KROW + 8 * (kvi1 % (DH / 8))], kreg1);
     if (tid < C::VUNITS) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t a0 = word(vreg0, e >> 1), a1 = word(vreg1, e >> 1);
+        const uint32_t a0 = vreg0[e >> 1], a1 = vreg1[e >> 1];
         const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
                                     : ((a0 & 0xffffu) | (a1 << 16));
-        *reinterpret_cast<uint32_t*>(&sv[buf][(8 * vdc + e) * C::VROW + 2 * vkp]) = pk;
+        *reinterpret_cast<uint32_t*>(&svb[(8 * vdc + e) * C::VROW + vdst]) = pk;
       }
     }
-    if (tid < BKV * HPW) sbias[buf][tid / BKV][tid % BKV] = breg * my_bscale;
+    if (tid < BKV) {
+      // bias columns of key tid: (hi, lo) bf16 parts of gain_h * b / s per head
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float beta = breg * bsc[i];
+        const float hi = (float)(__bf16)beta;
+        w[i] = i < HPW ? pack_bf16x2(hi, beta - hi) : 0u;
+        w[4 + i] = 0u;
+      }
+      st16(&skb[tid * C::KROW + DH], (u32x4){w[0], w[1], w[2], w[3]});
+      st16(&skb[tid * C::KROW + DH + 8], (u32x4){w[4], w[5], w[6], w[7]});
+    }
+  };
+  // S^T of one tile: bias step (C = 0), then the head-dim K-steps
+  auto qk_tile = [&](int buf, floatx16& s0, floatx16& s1) {
+    const uint16_t* skb = sk + buf * C::KTILE;
+    const floatx16 zero = {};
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(ld16(&skb[n * C::KROW + DH + 8 * g])), qsel, zero, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(ld16(&skb[(32 + n) * C::KROW + DH + 8 * g])), qsel, zero, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::KT; ++kk) {
+      const bf16x8 a0 = as_bf16x8(ld16(&skb[n * C::KROW + 16 * kk + 8 * g]));
+      const bf16x8 a1 = as_bf16x8(ld16(&skb[(32 + n) * C::KROW + 16 * kk + 8 * g]));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
+    }
   };
 
   // ---- running state (one query per lane)
@@ -197,57 +254,51 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   float mrun = -INFINITY;
   float lsum = 0.f;
   const int wq_last = wq0 + QW - 1 < len - 1 ? wq0 + QW - 1 : len - 1;
-  const bool wave_has_rows = wq0 < len;
+  const int w_tiles = wq0 < len ? wq_last / BKV + 1 : 0;   // tiles this wave needs
 
   load_tile(0);
   store_tile(0);
+  if (n_tiles > 1) {
+    load_tile(1);
+    store_tile(1);
+  }
   __syncthreads();
+  floatx16 sc0, sc1;                 // S^T of the tile being finished
+  if (TG_ATTN_PIPE && w_tiles > 0) qk_tile(0, sc0, sc1);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
     const int kv0 = t * BKV;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile(t + 1);
+    const int bcur = t % NBUF;
+    const bool fetch = t + 2 < n_tiles;
+    if (fetch) load_tile(t + 2);
+#if TG_ATTN_PIPE
+    floatx16 sn0, sn1;               // S^T of the next tile
+    if (t + 1 < w_tiles) {
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+      qk_tile((t + 1) % NBUF, sn0, sn1);
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+    }
+#endif
 
-    if (wave_has_rows && kv0 <= wq_last) {
-      // S^T = beta + K.Q^T  (keys: 32mt + 8(r/4) + 4g + r%4, query: n)
-      floatx16 sacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 bb =
-              *reinterpret_cast<const float4*>(&sbias[buf][hl][32 * mt + 8 * r4 + 4 * g]);
-          sacc[mt][4 * r4 + 0] = bb.x;
-          sacc[mt][4 * r4 + 1] = bb.y;
-          sacc[mt][4 * r4 + 2] = bb.z;
-          sacc[mt][4 * r4 + 3] = bb.w;
-        }
-#pragma unroll
-      for (int kk = 0; kk < C::KT; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
-              &sk[buf][(32 * mt + n) * C::KROW + 16 * kk + 8 * g]));
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[mt], 0, 0, 0);
-        }
-      }
+    if (t < w_tiles) {
+#if !TG_ATTN_PIPE
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
+      qk_tile(bcur, sc0, sc1);
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+#endif
       // causal mask, only where the tile reaches past the wave's first row
       if (kv0 + BKV - 1 > wq0) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = kv0 + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-            sacc[mt][r] = kj > qa ? -INFINITY : sacc[mt][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int kj = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          sc0[r] = kj > qa ? -INFINITY : sc0[r];
+          sc1[r] = kj + 32 > qa ? -INFINITY : sc1[r];
+        }
       }
       // online softmax on the unscaled accumulator (c_i > 0)
-      float mx = sacc[0][0];
+      float mx = fmaxf(sc0[0], sc1[0]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc0[r], sc1[r]));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
       if (__any(mx > mrun + kRescaleSlack)) {
         const float mnew = fmaxf(mrun, mx);
@@ -262,43 +313,44 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
       const float negm = mrun == -INFINITY ? 0.0f : -mrun;
       float ls = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mt][r], cq, negm));
-          sacc[mt][r] = p;
-          ls += p;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[r], cq, negm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[r], cq, negm));
+        sc0[r] = p0;
+        sc1[r] = p1;
+        ls += p0 + p1;
+      }
       lsum += ls;
       // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
       // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
       bf16x8 pf[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const floatx16& sa = sacc[kk >> 1];
+        const floatx16& sa = (kk >> 1) ? sc1 : sc0;
         const int o = 8 * (kk & 1);
-        uint4 u;
-        u.x = pack_bf16x2(sa[o + 0], sa[o + 1]);
-        u.y = pack_bf16x2(sa[o + 2], sa[o + 3]);
-        u.z = pack_bf16x2(sa[o + 4], sa[o + 5]);
-        u.w = pack_bf16x2(sa[o + 6], sa[o + 7]);
+        const u32x4 u = {pack_bf16x2(sa[o + 0], sa[o + 1]), pack_bf16x2(sa[o + 2], sa[o + 3]),
+                         pack_bf16x2(sa[o + 4], sa[o + 5]), pack_bf16x2(sa[o + 6], sa[o + 7])};
         pf[kk] = as_bf16x8(u);
       }
-      // O^T += V^T . P^T  (A operand: V^T rows d = 32dt + n, keys as above)
+      // O^T += V^T . P^T  (A operand: V^T row d = 32dt + n, 8 permuted keys)
+      const uint16_t* svb = sv + bcur * C::VTILE;
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint16_t* vp = &sv[buf][(32 * dt + n) * C::VROW + 16 * kk + 4 * g];
-          const uint2 lo2 = *reinterpret_cast<const uint2*>(vp);
-          const uint2 hi2 = *reinterpret_cast<const uint2*>(vp + 8);
-          const bf16x8 a = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+          const bf16x8 a = as_bf16x8(ld16(&svb[(32 * dt + n) * C::VROW + 16 * kk + 8 * g]));
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[dt], 0, 0, 0);
         }
       }
+      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
     }
-    if (more) store_tile(buf ^ 1);
+    if (fetch) store_tile((t + 2) % NBUF);
     __syncthreads();
+#if TG_ATTN_PIPE
+    sc0 = sn0;
+    sc1 = sn1;
+#endif
   }
 
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4
@@ -325,11 +377,14 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
   constexpr int QB = AttnCfg<DH, HPW>::QB;
   const int G = hq / hkv;
   const int groups_y = G / HPW;
-  const dim3 grid((unsigned)(n_seq + (t_kept + QB - 1) / QB), (unsigned)(hkv * groups_y));
-  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW>), grid, dim3(NTHR), 0, st,
+  const int64_t n_slots = n_seq + (t_kept + QB - 1) / QB;
+  const int64_t blocks = n_slots * hkv * groups_y;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW>), dim3((unsigned)blocks), dim3(NTHR), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), kept_b, kept_pos,
-                     kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, gain, temp, sm_scale);
+                     kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, (int)n_slots, gain, temp,
+                     sm_scale);
   return hipGetLastError();
 }
 
