@@ -2,16 +2,20 @@
 //
 // Integer work on order-preserving 32-bit keys of the scores (common.h).
 // Per sequence, the K'-th largest key tau is found by a three-pass radix
-// select over 11/11/10-bit digits; each pass is one launch over all 2048-token
-// chunks of all sequences, histograms go from LDS to global with integer
-// atomics, and the block that arrives last for a sequence narrows the digit
-// (no spinning, no float atomics, so the result is exact and reproducible).
-// Then every token is kept if it is a prompt token, if key > tau, or if
-// key == tau and fewer than `need` earlier tokens of the sequence tie at tau
-// (lower index wins).  Two more launches count and write the kept tokens in
-// ascending original index.
+// select over 11/11/10-bit digits.  Each pass is one launch over all
+// 2048-token chunks of all sequences: a chunk's histogram is built in LDS and
+// added into the sequence's histogram for that pass with integer atomics.
+// There is no cross-block handshake inside a launch: every block of the next
+// launch re-derives the digits fixed so far from the (small) histograms of
+// the earlier passes, so all blocks reach the same tau and quota without
+// fences.  Then every token is kept if it is a prompt token, if key > tau, or
+// if key == tau and fewer than `need` earlier tokens of the sequence tie at
+// tau (lower index wins).  The kept count of a sequence, min(K, |P|) + |N|,
+// is known from the prunable count alone, so sequence offsets need no scan
+// of the selection itself; chunk offsets come from a per-sequence scan of
+// per-chunk counts.  Tokens are written in ascending original index.
 //
-// Launch sequence: init, pass0, pass1, pass2, count, write.
+// Launches: init, pass0, pass1, pass2, count, offsets, write.
 #include "common.h"
 
 namespace tg {
@@ -21,27 +25,26 @@ constexpr int CH = kSelChunk;          // tokens per block
 constexpr int NT = 256;                // threads per block
 constexpr int PER = CH / NT;           // tokens per thread
 constexpr int NB = 2048;               // histogram bins (11-bit digit)
+constexpr int HIST_WORDS = 2048 + 2048 + 1024;   // the three passes' histograms
 
 enum : int { MODE_NONE = 0, MODE_ALL = 1, MODE_RADIX = 2 };
 
-struct SeqState {
-  uint32_t n_prunable;   // |P_s| (pass 0 atomics)
-  uint32_t arrive;       // blocks of this sequence done with the current launch
-  uint32_t prefix;       // digits fixed so far; tau after pass 2
-  uint32_t need;         // keys still to take at the current prefix
-  int32_t mode;
-  int32_t kept_total;    // |S_s|
-  int32_t pad[2];
+// Selection state of a sequence as derived by one block.
+struct Sel {
+  int mode;
+  uint32_t prefix;   // digits fixed so far (tau after three passes)
+  uint32_t need;     // keys still to take among those matching the prefix
+  uint32_t pad;
 };
 
 struct SelWs {
-  SeqState* st;          // [n_seq]
-  uint32_t* hist;        // [n_seq][NB]
+  Sel* stage;            // [3][n_seq]: state after 1, 2 and 3 digits
+  uint32_t* hist;        // [n_seq][HIST_WORDS]
+  uint32_t* n_prunable;  // [n_seq]
   int32_t* blk_def;      // [n_slots] kept for sure (prompt, key > tau, or all)
   int32_t* blk_tie;      // [n_slots] prunable tokens with key == tau
   int32_t* blk_tie_off;  // [n_slots] ties in earlier chunks of the sequence
-  int32_t* blk_off;      // [n_slots] kept tokens in earlier chunks
-  uint32_t* globals;     // [0] sequences counted, [1] non-empty sequences
+  int32_t* blk_off;      // [n_slots] kept tokens in earlier chunks of the sequence
 };
 
 int64_t n_slots_of(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 1) / CH; }
@@ -50,10 +53,12 @@ SelWs carve(void* ws, int64_t t_in, int n_seq) {
   const int64_t ns = n_slots_of(t_in, n_seq);
   char* p = static_cast<char*>(ws);
   SelWs w;
-  w.st = reinterpret_cast<SeqState*>(p);
-  p += sizeof(SeqState) * (size_t)n_seq;
+  w.stage = reinterpret_cast<Sel*>(p);
+  p += sizeof(Sel) * 3 * (size_t)n_seq;
   w.hist = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * (size_t)n_seq * NB;
+  p += sizeof(uint32_t) * (size_t)n_seq * HIST_WORDS;
+  w.n_prunable = reinterpret_cast<uint32_t*>(p);
+  p += sizeof(uint32_t) * (size_t)n_seq;
   w.blk_def = reinterpret_cast<int32_t*>(p);
   p += sizeof(int32_t) * ns;
   w.blk_tie = reinterpret_cast<int32_t*>(p);
@@ -61,113 +66,103 @@ SelWs carve(void* ws, int64_t t_in, int n_seq) {
   w.blk_tie_off = reinterpret_cast<int32_t*>(p);
   p += sizeof(int32_t) * ns;
   w.blk_off = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * ns;
-  w.globals = reinterpret_cast<uint32_t*>(p);
   return w;
+}
+
+// Token range [lo, hi) of sequence s, clamped to [0, t_in): inconsistent
+// offsets cannot read out of bounds.
+TG_DEVINL void seq_range(const int32_t* cu, int s, int64_t t_in, int64_t& lo, int64_t& hi) {
+  lo = cu[s] < t_in ? cu[s] : t_in;
+  hi = cu[s + 1] < t_in ? cu[s + 1] : t_in;
+  if (hi < lo) hi = lo;
 }
 
 // Which chunk of which sequence this block handles; false if none.
 struct Chunk {
   int s;
-  int64_t slot, begin, end;
-  int nchunks;
+  int64_t slot, lo, begin, end;
 };
 
 TG_DEVINL bool locate(const int32_t* cu, int n_seq, int64_t t_in, Chunk& c) {
   c.slot = blockIdx.x;
   c.s = seq_of_slot(cu, n_seq, c.slot, CH);
   if (c.s < 0) return false;
-  // token ranges are clamped to [0, t_in): inconsistent offsets cannot read out of bounds
-  const int64_t lo = cu[c.s] < t_in ? cu[c.s] : t_in;
-  const int64_t hi = cu[c.s + 1] < t_in ? cu[c.s + 1] : t_in;
-  if (hi <= lo) return false;
-  const int64_t ci = c.slot - slot0_of(cu, c.s, CH);
-  c.begin = lo + ci * CH;
+  int64_t hi;
+  seq_range(cu, c.s, t_in, c.lo, hi);
+  if (hi <= c.lo) return false;
+  c.begin = c.lo + (c.slot - slot0_of(cu, c.s, CH)) * CH;
   if (c.begin >= hi) return false;
   c.end = c.begin + CH < hi ? c.begin + CH : hi;
-  c.nchunks = (int)((hi - lo + CH - 1) / CH);
   return true;
 }
 
-// Block-uniform "am I the last block of sequence s for this launch?".
-TG_DEVINL bool arrive_last(SeqState* st, int nchunks, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(&st->arrive, 1u, __ATOMIC_ACQ_REL,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old == (uint32_t)nchunks - 1);
-  }
-  __syncthreads();
-  const bool last = *flag;
-  if (last) __threadfence();
-  return last;
+TG_DEVINL Sel sel_start(const SelWs& w, const int32_t* kbud, int s) {
+  const uint32_t npr = w.n_prunable[s];
+  const int kb = kbud[s];
+  const uint32_t k = kb > 0 ? (uint32_t)kb : 0u;
+  const uint32_t kp = k < npr ? k : npr;
+  Sel st;
+  st.mode = kp == 0 ? MODE_NONE : (kp == npr ? MODE_ALL : MODE_RADIX);
+  st.prefix = 0u;
+  st.need = kp;
+  st.pad = 0u;
+  return st;
 }
 
-__global__ __launch_bounds__(NT) void sel_init(const int32_t* __restrict__ cu, int n_seq,
-                                              int64_t t_in, SelWs w,
-                                              int32_t* __restrict__ kept_cu) {
-  const int64_t gtid = (int64_t)blockIdx.x * NT + threadIdx.x;
-  const int64_t gsz = (int64_t)gridDim.x * NT;
-  for (int64_t i = gtid; i < (int64_t)n_seq * NB; i += gsz) w.hist[i] = 0u;
-  for (int64_t i = gtid; i < n_seq; i += gsz) {
-    SeqState z = {};
-    w.st[i] = z;
-  }
-  for (int64_t i = gtid; i <= n_seq; i += gsz) kept_cu[i] = 0;
-  if (blockIdx.x == 0) {
-    __shared__ int red[NT / 64];
-    int cnt = 0;
-    for (int s = threadIdx.x; s < n_seq; s += NT) {
-      const int64_t lo = cu[s] < t_in ? cu[s] : t_in;
-      const int64_t hi = cu[s + 1] < t_in ? cu[s + 1] : t_in;
-      cnt += hi > lo ? 1 : 0;
-    }
-    cnt = wave_sum(cnt);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int i = 0; i < NT / 64; ++i) tot += red[i];
-      w.globals[0] = 0u;
-      w.globals[1] = (uint32_t)tot;
-    }
-  }
-}
-
-// After pass `P`, narrow (prefix, need) from the histogram of sequence s.
-template <int P>
-TG_DEVINL void narrow(SeqState* st, uint32_t* ghist, int* sh) {
-  constexpr int nb = (P == 2) ? 1024 : 2048;
-  constexpr int per = nb / NT;
-  const uint32_t need = st->need;
+// Narrow (prefix, need) with the histogram `h` of NBINS bins (block-wide;
+// every thread returns the same result).  Contains barriers.
+template <int NBINS, int SHIFT>
+TG_DEVINL void sel_narrow(Sel& st, const uint32_t* h, int* sh) {
+  constexpr int per = NBINS / NT;
   uint32_t c[per];
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < per; ++i) {
-    const int bin = nb - 1 - (threadIdx.x * per + i);
-    c[i] = ld_acquire_u32(ghist + bin);
+    c[i] = h[NBINS - 1 - (threadIdx.x * per + i)];    // bins in descending order
     mine += (int)c[i];
   }
   int tot;
-  int above = block_excl_scan<NT>(mine, sh, &tot);
-  if ((uint32_t)above < need && (uint32_t)(above + mine) >= need) {
+  const int above = block_excl_scan<NT>(mine, sh, &tot);
+  if ((uint32_t)above < st.need && (uint32_t)(above + mine) >= st.need) {
     uint32_t acc = (uint32_t)above;
 #pragma unroll
     for (int i = 0; i < per; ++i) {
-      if (acc + c[i] >= need) {
-        const uint32_t bin = nb - 1 - (threadIdx.x * per + i);
-        const uint32_t prev = st->prefix;
-        st->prefix = (P == 0) ? bin : ((P == 1) ? ((prev << 11) | bin) : ((prev << 10) | bin));
-        st->need = need - acc;
+      if (acc + c[i] >= st.need) {
+        sh[NT / 64] = NBINS - 1 - (threadIdx.x * per + i);
+        sh[NT / 64 + 1] = (int)(st.need - acc);
         break;
       }
       acc += c[i];
     }
   }
-  // every thread clears the bins it read, ready for the next pass
-#pragma unroll
-  for (int i = 0; i < per; ++i) ghist[nb - 1 - (threadIdx.x * per + i)] = 0u;
+  __syncthreads();
+  st.prefix = (st.prefix << SHIFT) | (uint32_t)sh[NT / 64];
+  st.need = (uint32_t)sh[NT / 64 + 1];
+  __syncthreads();
+}
+
+// State after `digits` digits (1..3): the state stored by the previous
+// launch after digits-1 digits, narrowed once more with histogram digits-1.
+// The block of chunk 0 stores the result for the next launch (each launch
+// writes a different stage, so no block reads a slot being written).
+TG_DEVINL Sel sel_stage(const SelWs& w, const int32_t* kbud, int s, int n_seq, int digits,
+                        bool store, int* sh) {
+  Sel st = digits == 1 ? sel_start(w, kbud, s) : w.stage[(size_t)(digits - 2) * n_seq + s];
+  if (st.mode == MODE_RADIX) {
+    const uint32_t* hs = w.hist + (size_t)s * HIST_WORDS;
+    if (digits == 1) sel_narrow<2048, 11>(st, hs, sh);
+    else if (digits == 2) sel_narrow<2048, 11>(st, hs + 2048, sh);
+    else sel_narrow<1024, 10>(st, hs + 4096, sh);
+  }
+  if (store && threadIdx.x == 0) w.stage[(size_t)(digits - 1) * n_seq + s] = st;
+  return st;
+}
+
+__global__ __launch_bounds__(NT) void sel_init(int n_seq, SelWs w) {
+  const int64_t gtid = (int64_t)blockIdx.x * NT + threadIdx.x;
+  const int64_t gsz = (int64_t)gridDim.x * NT;
+  for (int64_t i = gtid; i < (int64_t)n_seq * HIST_WORDS; i += gsz) w.hist[i] = 0u;
+  for (int64_t i = gtid; i < n_seq; i += gsz) w.n_prunable[i] = 0u;
 }
 
 template <int P>
@@ -180,11 +175,11 @@ __global__ __launch_bounds__(NT) void sel_pass(const float* __restrict__ b,
   __shared__ int sh[NT / 64 + 2];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  SeqState* st = w.st + c.s;
-  uint32_t prefix = 0;
+  uint32_t* hs = w.hist + (size_t)c.s * HIST_WORDS;
+  Sel st = {MODE_RADIX, 0u, 0u, 0u};
   if (P > 0) {
-    if (st->mode != MODE_RADIX) return;
-    prefix = st->prefix;
+    st = sel_stage(w, kbud, c.s, n_seq, P, c.begin == c.lo, sh);
+    if (st.mode != MODE_RADIX) return;
   }
   for (int i = threadIdx.x; i < NB; i += NT) lh[i] = 0u;
   __syncthreads();
@@ -198,155 +193,134 @@ __global__ __launch_bounds__(NT) void sel_pass(const float* __restrict__ b,
       if (P == 0) {
         atomicAdd(&lh[key >> 21], 1u);
       } else if (P == 1) {
-        if ((key >> 21) == prefix) atomicAdd(&lh[(key >> 10) & 0x7ffu], 1u);
+        if ((key >> 21) == st.prefix) atomicAdd(&lh[(key >> 10) & 0x7ffu], 1u);
       } else {
-        if ((key >> 10) == prefix) atomicAdd(&lh[key & 0x3ffu], 1u);
+        if ((key >> 10) == st.prefix) atomicAdd(&lh[key & 0x3ffu], 1u);
       }
     }
   }
   __syncthreads();
-  uint32_t* gh = w.hist + (size_t)c.s * NB;
-  for (int i = threadIdx.x; i < NB; i += NT) {
+  uint32_t* gh = hs + (P == 0 ? 0 : (P == 1 ? 2048 : 4096));
+  for (int i = threadIdx.x; i < (P == 2 ? 1024 : 2048); i += NT) {
     const uint32_t v = lh[i];
     if (v) atomicAdd(gh + i, v);
   }
   if (P == 0) {
     np = wave_sum(np);
-    if ((threadIdx.x & 63) == 0 && np) atomicAdd(&st->n_prunable, (uint32_t)np);
+    if ((threadIdx.x & 63) == 0 && np) atomicAdd(&w.n_prunable[c.s], (uint32_t)np);
   }
-  if (!arrive_last(st, c.nchunks, &sh[NT / 64])) return;
-  // ---- last block of sequence s: narrow the digit
-  if (P == 0) {
-    const uint32_t npr = ld_acquire_u32(&st->n_prunable);
-    const int kb = kbud[c.s];
-    const uint32_t k = kb > 0 ? (uint32_t)kb : 0u;
-    const uint32_t kp = k < npr ? k : npr;
-    const int mode = kp == 0 ? MODE_NONE : (kp == npr ? MODE_ALL : MODE_RADIX);
-    if (mode != MODE_RADIX) {
-      // histogram left as is: later passes skip this sequence
-      if (threadIdx.x == 0) {
-        st->mode = mode;
-        st->arrive = 0u;
-      }
-      return;
-    }
-    if (threadIdx.x == 0) {
-      st->mode = mode;
-      st->need = kp;
-    }
-    __syncthreads();
-  }
-  narrow<P>(st, gh, sh);
-  if (threadIdx.x == 0) st->arrive = 0u;
 }
 
 __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
-                                               const int32_t* __restrict__ cu, int n_seq,
-                                               int64_t t_in, SelWs w,
-                                               int32_t* __restrict__ kept_cu) {
+                                               const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ kbud, int n_seq,
+                                               int64_t t_in, SelWs w) {
   __shared__ int sh[NT / 64 + 2];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  SeqState* st = w.st + c.s;
-  const int mode = st->mode;
-  const uint32_t tau = st->prefix;
+  const Sel st = sel_stage(w, kbud, c.s, n_seq, 3, c.begin == c.lo, sh);
   int def = 0, tie = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t j = c.begin + threadIdx.x + (int64_t)i * NT;
     if (j < c.end) {
-      if (!pr[j] || mode == MODE_ALL) {
+      if (!pr[j] || st.mode == MODE_ALL) {
         ++def;
-      } else if (mode == MODE_RADIX) {
+      } else if (st.mode == MODE_RADIX) {
         const uint32_t key = score_key(b[j]);
-        def += key > tau;
-        tie += key == tau;
+        def += key > st.prefix;
+        tie += key == st.prefix;
       }
     }
   }
-  def = wave_sum(def);
-  tie = wave_sum(tie);
-  if ((threadIdx.x & 63) == 0) {
-    sh[threadIdx.x >> 6] = def;
-  }
-  __syncthreads();
-  int tdef = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) tdef += sh[i];
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = tie;
-  __syncthreads();
+  int td, tt;
+  block_excl_scan<NT>(def, sh, &td);
+  block_excl_scan<NT>(tie, sh, &tt);
   if (threadIdx.x == 0) {
-    int ttie = 0;
-    for (int i = 0; i < NT / 64; ++i) ttie += sh[i];
-    w.blk_def[c.slot] = tdef;
-    w.blk_tie[c.slot] = ttie;
+    w.blk_def[c.slot] = td;
+    w.blk_tie[c.slot] = tt;
   }
-  if (!arrive_last(st, c.nchunks, &sh[NT / 64])) return;
-  // ---- last block of sequence s: offsets of its chunks, in chunk order
-  if (threadIdx.x == 0) {
-    const uint32_t need = mode == MODE_RADIX ? st->need : 0u;
-    const int64_t s0 = slot0_of(cu, c.s, CH);
-    int tie_off = 0, off = 0;
-    for (int i = 0; i < c.nchunks; ++i) {
-      const int64_t sl = s0 + i;
-      const int d = __hip_atomic_load(w.blk_def + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int t = __hip_atomic_load(w.blk_tie + sl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int take = (int)need - tie_off;
-      take = take < 0 ? 0 : (take > t ? t : take);
-      w.blk_tie_off[sl] = tie_off;
-      w.blk_off[sl] = off;
-      tie_off += t;
-      off += d + take;
+}
+
+// One block per sequence: offsets of its chunks (ties first, then kept
+// tokens, both in chunk order) and the sequence's offset in the output.
+__global__ __launch_bounds__(NT) void sel_offsets(const int32_t* __restrict__ cu,
+                                                 const int32_t* __restrict__ kbud, int n_seq,
+                                                 int64_t t_in, SelWs w,
+                                                 int32_t* __restrict__ kept_cu) {
+  __shared__ int sh[NT / 64 + 2];
+  const int s = blockIdx.x;
+  // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|
+  int acc = 0;
+  for (int base = 0; base < s; base += NT) {
+    const int i = base + threadIdx.x;
+    int v = 0;
+    if (i < s) {
+      int64_t lo, hi;
+      seq_range(cu, i, t_in, lo, hi);
+      const int npr = (int)w.n_prunable[i];
+      const int kb = kbud[i] > 0 ? kbud[i] : 0;
+      v = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
     }
-    st->kept_total = off;
-    st->arrive = 0u;
-    __threadfence();
-    const uint32_t old = __hip_atomic_fetch_add(&w.globals[0], 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    sh[NT / 64 + 1] = (old == w.globals[1] - 1u);
-  }
-  __syncthreads();
-  if (!sh[NT / 64 + 1]) return;
-  __threadfence();
-  // ---- last sequence overall: kept_cu_seqlens = exclusive scan of |S_s|
-  int run = 0;
-  for (int base = 0; base < n_seq; base += NT) {
-    const int s = base + threadIdx.x;
-    const int v = s < n_seq ? __hip_atomic_load(&w.st[s].kept_total, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                            : 0;
     int tot;
-    const int ex = block_excl_scan<NT>(v, sh, &tot);
-    if (s < n_seq) kept_cu[s] = run + ex;
-    run += tot;
+    block_excl_scan<NT>(v, sh, &tot);
+    acc += tot;
   }
-  if (threadIdx.x == 0) kept_cu[n_seq] = run;
+  int64_t lo, hi;
+  seq_range(cu, s, t_in, lo, hi);
+  const int npr = (int)w.n_prunable[s];
+  const int kb = kbud[s] > 0 ? kbud[s] : 0;
+  const int mine = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
+  if (threadIdx.x == 0) {
+    kept_cu[s] = acc;
+    if (s == n_seq - 1) kept_cu[n_seq] = acc + mine;
+  }
+  if (hi <= lo) return;
+  const Sel st = w.stage[2 * (size_t)n_seq + s];
+  const uint32_t need = st.mode == MODE_RADIX ? st.need : 0u;
+  const int nch = (int)((hi - lo + CH - 1) / CH);
+  const int64_t s0 = slot0_of(cu, s, CH);
+  int tie_run = 0, off_run = 0;
+  for (int base = 0; base < nch; base += NT) {
+    const int i = base + threadIdx.x;
+    const int t = i < nch ? w.blk_tie[s0 + i] : 0;
+    const int d = i < nch ? w.blk_def[s0 + i] : 0;
+    int tt;
+    const int tie_off = tie_run + block_excl_scan<NT>(t, sh, &tt);
+    int take = (int)need - tie_off;
+    take = take < 0 ? 0 : (take > t ? t : take);
+    int to;
+    const int off = off_run + block_excl_scan<NT>(d + take, sh, &to);
+    if (i < nch) {
+      w.blk_tie_off[s0 + i] = tie_off;
+      w.blk_off[s0 + i] = off;
+    }
+    tie_run += tt;
+    off_run += to;
+  }
 }
 
 __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
-                                               const int32_t* __restrict__ cu, int n_seq,
+                                               const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ kbud, int n_seq,
                                                int64_t t_in, SelWs w,
-                                               const int32_t* __restrict__ kept_cu,
-                                               int64_t cap, int32_t* __restrict__ kept_idx,
+                                               const int32_t* __restrict__ kept_cu, int64_t cap,
+                                               int32_t* __restrict__ kept_idx,
                                                int32_t* __restrict__ kept_pos,
                                                float* __restrict__ kept_b) {
   __shared__ int sh[NT / 64 + 2];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  const SeqState* st = w.st + c.s;
-  const int mode = st->mode;
-  const uint32_t tau = st->prefix;
-  const int need = mode == MODE_RADIX ? (int)st->need : 0;
+  const Sel st = w.stage[2 * (size_t)n_seq + c.s];
+  const int need = st.mode == MODE_RADIX ? (int)st.need : 0;
   const int tie_base = w.blk_tie_off[c.slot];
   const int64_t out_base = (int64_t)kept_cu[c.s] + w.blk_off[c.slot];
-  const int64_t seq_lo = cu[c.s] < t_in ? cu[c.s] : t_in;
   // contiguous tokens per thread, so thread order is index order
   const int64_t j0 = c.begin + (int64_t)threadIdx.x * PER;
   float bv[PER];
-  uint8_t fl[PER];     // bit0: kept for sure, bit1: tie at tau
+  uint8_t fl[PER];     // 1: kept for sure, 2: tie at tau
   int nt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -355,11 +329,11 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
     float v = 0.f;
     if (j < c.end) {
       v = b[j];
-      if (!pr[j] || mode == MODE_ALL) {
+      if (!pr[j] || st.mode == MODE_ALL) {
         f = 1;
-      } else if (mode == MODE_RADIX) {
+      } else if (st.mode == MODE_RADIX) {
         const uint32_t key = score_key(v);
-        f = key > tau ? 1 : (key == tau ? 2 : 0);
+        f = key > st.prefix ? 1 : (key == st.prefix ? 2 : 0);
       }
     }
     bv[i] = v;
@@ -384,7 +358,7 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
     if (fl[i]) {
       if (o < cap) {
         kept_idx[o] = (int32_t)(j0 + i);
-        if (kept_pos) kept_pos[o] = (int32_t)(j0 + i - seq_lo);
+        if (kept_pos) kept_pos[o] = (int32_t)(j0 + i - c.lo);
         if (kept_b) kept_b[o] = bv[i];
       }
       ++o;
@@ -396,8 +370,8 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
 
 size_t select_ws_bytes(int64_t t_in, int n_seq) {
   const int64_t ns = n_slots_of(t_in, n_seq);
-  size_t bytes = sizeof(SeqState) * (size_t)n_seq + sizeof(uint32_t) * (size_t)n_seq * NB +
-                 4 * sizeof(int32_t) * (size_t)ns + 2 * sizeof(uint32_t);
+  size_t bytes = sizeof(Sel) * 3 * (size_t)n_seq + sizeof(uint32_t) * (size_t)n_seq * HIST_WORDS +
+                 sizeof(uint32_t) * (size_t)n_seq + 4 * sizeof(int32_t) * (size_t)ns;
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -407,19 +381,21 @@ hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t*
                          void* ws, hipStream_t st) {
   SelWs w = carve(ws, t_in, n_seq);
   const int64_t ns = n_slots_of(t_in, n_seq);
-  int64_t init_blocks = ((int64_t)n_seq * NB + NT - 1) / NT;
+  int64_t init_blocks = ((int64_t)n_seq * HIST_WORDS + NT - 1) / NT;
   if (init_blocks > 1024) init_blocks = 1024;
-  if (init_blocks < 1) init_blocks = 1;
-  hipLaunchKernelGGL(sel_init, dim3((unsigned)init_blocks), dim3(NT), 0, st, cu, n_seq, t_in, w,
-                     kept_cu);
-  if (t_in == 0) return hipGetLastError();
+  hipLaunchKernelGGL(sel_init, dim3((unsigned)init_blocks), dim3(NT), 0, st, n_seq, w);
   const dim3 grid((unsigned)ns);
-  hipLaunchKernelGGL(sel_pass<0>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-  hipLaunchKernelGGL(sel_pass<1>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-  hipLaunchKernelGGL(sel_pass<2>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-  hipLaunchKernelGGL(sel_count, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w, kept_cu);
-  hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w, kept_cu,
-                     cap, kept_idx, kept_pos, kept_b);
+  if (t_in > 0) {
+    hipLaunchKernelGGL(sel_pass<0>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
+    hipLaunchKernelGGL(sel_pass<1>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
+    hipLaunchKernelGGL(sel_pass<2>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
+    hipLaunchKernelGGL(sel_count, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
+  }
+  hipLaunchKernelGGL(sel_offsets, dim3((unsigned)n_seq), dim3(NT), 0, st, cu, k, n_seq, t_in, w,
+                     kept_cu);
+  if (t_in > 0)
+    hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w,
+                       kept_cu, cap, kept_idx, kept_pos, kept_b);
   return hipGetLastError();
 }
 
