@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--no-full-context", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="skip the CPU baseline and the full-context lane (for profiling)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="after timing, run 3 plain device copies of MB MiB (reference for "
+                         "hardware byte counters); not part of the metric")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gated-prefill "
@@ -258,6 +261,16 @@ def main():
                     T / (t_full + (avg["score"] + avg["select"]) * 1e-6), 1),
                 "note": "K = all tokens; gather is the identity and not run"}
         del qf, kf, vf, of
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copies: 3 x {args.calibrate_copy} MiB read + written")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -37,6 +37,8 @@
 //    so the head index is taken from the low bits of the block index);
 //  - the running maximum is only moved when it grows by more than 2^8 in
 //    the exponent (exact: the normaliser absorbs the stale maximum).
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
@@ -46,21 +48,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// Schedule switches (compile-time): TG_ATTN_PIPE issues the Q.K^T MFMAs of
-// tile t+1 before the softmax of tile t (costs 32 registers); TG_ATTN_PRIO
-// raises the wave priority while it issues MFMA runs.
-#ifndef TG_ATTN_PIPE
-#define TG_ATTN_PIPE 0
-#endif
-#ifndef TG_ATTN_PRIO
-#define TG_ATTN_PRIO 0
-#endif
-
 constexpr int BKV = 64;                 // keys per tile
 constexpr int NWAVE = 8;                // waves per workgroup
 constexpr int NTHR = 64 * NWAVE;
 constexpr int QW = 32;                  // query rows per wave
-constexpr int NBUF = 3;                 // LDS tile buffers
+constexpr int NBUF = 2;                 // LDS tile buffers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kMinScale = 1e-30f;     // keeps c_i > 0 so masked keys stay -inf
@@ -158,17 +150,21 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   for (int e = 0; e < 8; ++e)
     qsel[e] = (__bf16)((g == 0 && (e >> 1) == hl) ? 1.0f : 0.0f);
 
-  // ---- tile loaders (global -> registers -> LDS)
+  // ---- tile loaders (global -> registers -> LDS), per-thread state fixed up front
   const int q_end = q0 + C::QB < len ? q0 + C::QB : len;
   const int n_tiles = (q_end + BKV - 1) / BKV;
   const int64_t kvstride = (int64_t)hkv * DH;     // elements between token rows of k, v
   const uint16_t* kb_ = k + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   const uint16_t* vb_ = v + (int64_t)lo * kvstride + (int64_t)kvh * DH;
-  // every thread loads; units past the tile wrap around (their stores are skipped)
+  // K: vectors tid and tid + NTHR of the tile (row key, 16-byte chunk ch)
   const int kvi0 = tid % C::KVEC, kvi1 = (tid + NTHR) % C::KVEC;
+  const int krow0 = kvi0 / (DH / 8), krow1 = kvi1 / (DH / 8);
+  const int kcol0 = 8 * (kvi0 % (DH / 8)), kcol1 = 8 * (kvi1 % (DH / 8));
+  const int kdst0 = krow0 * C::KROW + kcol0, kdst1 = krow1 * C::KROW + kcol1;
+  // V: unit (key pair vkp, 8-dim chunk vdc), transposed into V^T rows 8vdc..+8
   const int vu = tid % C::VUNITS;
   const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
-  const int vdst = vpos(2 * vkp);
+  const int vdst = (8 * vdc) * C::VROW + vpos(2 * vkp);
   float bsc[4];                                   // gain_h / s of the HPW heads
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
@@ -179,71 +175,55 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
 
   auto load_tile = [&](int t) {
     const int kv0 = t * BKV;
-    {
-      int kr = kv0 + kvi0 / (DH / 8);
-      kr = kr < len ? kr : len - 1;
-      kreg0 = ld16(kb_ + (int64_t)kr * kvstride + 8 * (kvi0 % (DH / 8)));
+    if (kv0 + BKV <= len) {                      // whole tile inside the sequence
+      const int64_t off = (int64_t)kv0 * kvstride;
+      kreg0 = ld16(kb_ + off + (int64_t)krow0 * kvstride + kcol0);
+      if (C::KVPT == 2) kreg1 = ld16(kb_ + off + (int64_t)krow1 * kvstride + kcol1);
+      vreg0 = ld16(vb_ + off + (int64_t)(2 * vkp) * kvstride + 8 * vdc);
+      vreg1 = ld16(vb_ + off + (int64_t)(2 * vkp + 1) * kvstride + 8 * vdc);
+      breg = kept_b[lo + kv0 + (tid % BKV)];
+    } else {                                     // last, partial tile: clamp rows
+      const int r0 = min(kv0 + krow0, len - 1), r1 = min(kv0 + krow1, len - 1);
+      kreg0 = ld16(kb_ + (int64_t)r0 * kvstride + kcol0);
+      if (C::KVPT == 2) kreg1 = ld16(kb_ + (int64_t)r1 * kvstride + kcol1);
+      const int v0 = min(kv0 + 2 * vkp, len - 1), v1 = min(kv0 + 2 * vkp + 1, len - 1);
+      vreg0 = ld16(vb_ + (int64_t)v0 * kvstride + 8 * vdc);
+      vreg1 = ld16(vb_ + (int64_t)v1 * kvstride + 8 * vdc);
+      breg = kept_b[lo + min(kv0 + (tid % BKV), len - 1)];
     }
-    if (C::KVPT == 2) {
-      int kr = kv0 + kvi1 / (DH / 8);
-      kr = kr < len ? kr : len - 1;
-      kreg1 = ld16(kb_ + (int64_t)kr * kvstride + 8 * (kvi1 % (DH / 8)));
-    }
-    int k0 = kv0 + 2 * vkp, k1 = k0 + 1;
-    k0 = k0 < len ? k0 : len - 1;
-    k1 = k1 < len ? k1 : len - 1;
-    vreg0 = ld16(vb_ + (int64_t)k0 * kvstride + 8 * vdc);
-    vreg1 = ld16(vb_ + (int64_t)k1 * kvstride + 8 * vdc);
-    int kr = kv0 + (tid % BKV);
-    kr = kr < len ? kr : len - 1;
-    breg = kept_b[lo + kr];
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* skb = sk + buf * C::KTILE;
-    uint16_t* svb = sv + buf * C::VTILE;
-    if (tid < C::KVEC)
-      st16(&skb[(kvi0 / (DH / 8)) * C::KROW + 8 * (kvi0 % (DH / 8))], kreg0);
-    if (C::KVPT == 2 && tid + NTHR < C::KVEC)
-      st16(&skb[(kvi1 / (DH / 8)) * C::KROW + 8 * (kvi1 % (DH / 8))], kreg1);
+  auto store_tile = [&](auto BUFC) {
+    constexpr int BUF = decltype(BUFC)::value;
+    uint16_t* skb = sk + BUF * C::KTILE;
+    uint16_t* svb = sv + BUF * C::VTILE;
+    if (tid < C::KVEC) st16(&skb[kdst0], kreg0);
+    if (C::KVPT == 2 && tid + NTHR < C::KVEC) st16(&skb[kdst1], kreg1);
     if (tid < C::VUNITS) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t a0 = vreg0[e >> 1], a1 = vreg1[e >> 1];
         const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
                                     : ((a0 & 0xffffu) | (a1 << 16));
-        *reinterpret_cast<uint32_t*>(&svb[(8 * vdc + e) * C::VROW + vdst]) = pk;
+        *reinterpret_cast<uint32_t*>(&svb[vdst + e * C::VROW]) = pk;
       }
     }
     if (tid < BKV) {
       // bias columns of key tid: (hi, lo) bf16 parts of gain_h * b / s per head
-      uint32_t w[8];
+      uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float beta = breg * bsc[i];
         const float hi = (float)(__bf16)beta;
         w[i] = i < HPW ? pack_bf16x2(hi, beta - hi) : 0u;
-        w[4 + i] = 0u;
       }
       st16(&skb[tid * C::KROW + DH], (u32x4){w[0], w[1], w[2], w[3]});
-      st16(&skb[tid * C::KROW + DH + 8], (u32x4){w[4], w[5], w[6], w[7]});
+      st16(&skb[tid * C::KROW + DH + 8], (u32x4){0u, 0u, 0u, 0u});
     }
   };
-  // S^T of one tile: bias step (C = 0), then the head-dim K-steps
-  auto qk_tile = [&](int buf, floatx16& s0, floatx16& s1) {
-    const uint16_t* skb = sk + buf * C::KTILE;
-    const floatx16 zero = {};
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(ld16(&skb[n * C::KROW + DH + 8 * g])), qsel, zero, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(ld16(&skb[(32 + n) * C::KROW + DH + 8 * g])), qsel, zero, 0, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < C::KT; ++kk) {
-      const bf16x8 a0 = as_bf16x8(ld16(&skb[n * C::KROW + 16 * kk + 8 * g]));
-      const bf16x8 a1 = as_bf16x8(ld16(&skb[(32 + n) * C::KROW + 16 * kk + 8 * g]));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
-    }
-  };
+
+  // per-lane LDS operand bases: every fragment read is base + constant offset
+  const uint16_t* klane = sk + n * C::KROW + 8 * g;
+  const uint16_t* vlane = sv + n * C::VROW + 8 * g;
 
   // ---- running state (one query per lane)
   floatx16 oacc[C::DT];
@@ -256,101 +236,100 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   const int wq_last = wq0 + QW - 1 < len - 1 ? wq0 + QW - 1 : len - 1;
   const int w_tiles = wq0 < len ? wq_last / BKV + 1 : 0;   // tiles this wave needs
 
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) {
-    load_tile(1);
-    store_tile(1);
-  }
-  __syncthreads();
-  floatx16 sc0, sc1;                 // S^T of the tile being finished
-  if (TG_ATTN_PIPE && w_tiles > 0) qk_tile(0, sc0, sc1);
-
-  for (int t = 0; t < n_tiles; ++t) {
+  // one tile of one wave: S^T = K'.Q'^T (bias step first), softmax, O^T += V^T.P^T
+  auto compute = [&](auto BUFC, int t) {
+    constexpr int BUF = decltype(BUFC)::value;
     const int kv0 = t * BKV;
-    const int bcur = t % NBUF;
-    const bool fetch = t + 2 < n_tiles;
-    if (fetch) load_tile(t + 2);
-#if TG_ATTN_PIPE
-    floatx16 sn0, sn1;               // S^T of the next tile
-    if (t + 1 < w_tiles) {
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
-      qk_tile((t + 1) % NBUF, sn0, sn1);
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
+    const uint16_t* kl = klane + BUF * C::KTILE;
+    const uint16_t* vl = vlane + BUF * C::VTILE;
+    const floatx16 zero = {};
+    floatx16 sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kl + DH)), qsel, zero,
+                                                           0, 0, 0);
+    floatx16 sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        as_bf16x8(ld16(kl + 32 * C::KROW + DH)), qsel, zero, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::KT; ++kk) {
+      sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kl + 16 * kk)), qf[kk], sc0,
+                                                    0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          as_bf16x8(ld16(kl + 32 * C::KROW + 16 * kk)), qf[kk], sc1, 0, 0, 0);
     }
-#endif
-
-    if (t < w_tiles) {
-#if !TG_ATTN_PIPE
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
-      qk_tile(bcur, sc0, sc1);
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
-#endif
-      // causal mask, only where the tile reaches past the wave's first row
-      if (kv0 + BKV - 1 > wq0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          sc0[r] = kj > qa ? -INFINITY : sc0[r];
-          sc1[r] = kj + 32 > qa ? -INFINITY : sc1[r];
-        }
-      }
-      // online softmax on the unscaled accumulator (c_i > 0)
-      float mx = fmaxf(sc0[0], sc1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc0[r], sc1[r]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
-      if (__any(mx > mrun + kRescaleSlack)) {
-        const float mnew = fmaxf(mrun, mx);
-        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        mrun = mnew;
-      }
-      const float negm = mrun == -INFINITY ? 0.0f : -mrun;
-      float ls = 0.f;
+    // causal mask, only where the tile reaches past the wave's first row
+    if (kv0 + BKV - 1 > wq0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[r], cq, negm));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[r], cq, negm));
-        sc0[r] = p0;
-        sc1[r] = p1;
-        ls += p0 + p1;
+        const int kj = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        sc0[r] = kj > qa ? -INFINITY : sc0[r];
+        sc1[r] = kj + 32 > qa ? -INFINITY : sc1[r];
       }
-      lsum += ls;
-      // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
-      // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
-      bf16x8 pf[4];
+    }
+    // online softmax on the unscaled accumulator (c_i > 0): 3-input max tree
+    float m4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m4[i] = fmaxf(fmaxf(fmaxf(sc0[4 * i], sc0[4 * i + 1]), fmaxf(sc0[4 * i + 2], sc0[4 * i + 3])),
+                    fmaxf(fmaxf(sc1[4 * i], sc1[4 * i + 1]), fmaxf(sc1[4 * i + 2], sc1[4 * i + 3])));
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
+    if (__any(mx > mrun + kRescaleSlack)) {
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      mrun = mnew;
+    }
+    const float negm = mrun == -INFINITY ? 0.0f : -mrun;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[r], cq, negm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[r], cq, negm));
+      sc0[r] = p0;
+      sc1[r] = p1;
+      l4[r & 3] += p0 + p1;
+    }
+    lsum += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
+    // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const floatx16& sa = (kk >> 1) ? sc1 : sc0;
+      const int o = 8 * (kk & 1);
+      const u32x4 u = {pack_bf16x2(sa[o + 0], sa[o + 1]), pack_bf16x2(sa[o + 2], sa[o + 3]),
+                       pack_bf16x2(sa[o + 4], sa[o + 5]), pack_bf16x2(sa[o + 6], sa[o + 7])};
+      pf[kk] = as_bf16x8(u);
+    }
+    // O^T += V^T . P^T  (A operand: V^T row d = 32dt + n, 8 permuted keys)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const floatx16& sa = (kk >> 1) ? sc1 : sc0;
-        const int o = 8 * (kk & 1);
-        const u32x4 u = {pack_bf16x2(sa[o + 0], sa[o + 1]), pack_bf16x2(sa[o + 2], sa[o + 3]),
-                         pack_bf16x2(sa[o + 4], sa[o + 5]), pack_bf16x2(sa[o + 6], sa[o + 7])};
-        pf[kk] = as_bf16x8(u);
+        const bf16x8 a = as_bf16x8(ld16(vl + 32 * dt * C::VROW + 16 * kk));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[dt], 0, 0, 0);
       }
-      // O^T += V^T . P^T  (A operand: V^T row d = 32dt + n, 8 permuted keys)
-      const uint16_t* svb = sv + bcur * C::VTILE;
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = as_bf16x8(ld16(&svb[(32 * dt + n) * C::VROW + 16 * kk + 8 * g]));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[dt], 0, 0, 0);
-        }
-      }
-      if (TG_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
     }
-    if (fetch) store_tile((t + 2) % NBUF);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  load_tile(0);
+  store_tile(B0{});
+  __syncthreads();
+  // double-buffered tiles, unrolled by two so every LDS offset is a constant
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t < w_tiles) compute(B0{}, t);
+    if (t + 1 < n_tiles) store_tile(B1{});
     __syncthreads();
-#if TG_ATTN_PIPE
-    sc0 = sn0;
-    sc1 = sn1;
-#endif
+    if (t + 1 >= n_tiles) break;
+    if (t + 2 < n_tiles) load_tile(t + 2);
+    if (t + 1 < w_tiles) compute(B1{}, t + 1);
+    if (t + 2 < n_tiles) store_tile(B0{});
+    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4

@@ -28,6 +28,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kRowsPerWG = 256;
 constexpr int kBK = 64;              // d per K-step
 constexpr int kRow = kBK + 8;        // bf16 per LDS row (144 B: rows start 4 banks apart)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -35,68 +37,52 @@ TG_DEVINL float silu_f(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
 }
 
-// One K-step of one wave: MFMAs on the W1 slice in LDS (A operand) and the
-// wave's 64 x rows staged in its private LDS tile (B operand, two row tiles).
+// One workgroup = 256 rows x all h columns, 8 waves: wave w owns rows
+// [64(w%4), +64) and the h tiles [MTA(w/4), +MTA) (two waves per SIMD, 128
+// accumulators each).  x is read with coalesced 16-byte loads two K-steps
+// ahead into registers, then staged into a double-buffered LDS tile shared by
+// the two waves of a row group; the W1 slice of each K-step is shared by all
+// waves through a double-buffered LDS tile.  One barrier per K-step.
 template <int MT>
-TG_DEVINL void score_kstep(floatx16 (&acc)[MT][2], const uint16_t* swb, const uint16_t* sxw,
-                           int n, int g) {
-#pragma unroll
-  for (int s = 0; s < kBK / 16; ++s) {
-    const bf16x8 bop0 = as_bf16x8(ld16(&sxw[n * kRow + 32 * g + 8 * s]));
-    const bf16x8 bop1 = as_bf16x8(ld16(&sxw[(32 + n) * kRow + 32 * g + 8 * s]));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 aop = as_bf16x8(ld16(&swb[(32 * mt + n) * kRow + 32 * g + 8 * s]));
-      acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop0, acc[mt][0], 0, 0, 0);
-      acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop1, acc[mt][1], 0, 0, 0);
-    }
-  }
-}
-
-// One workgroup = 256 rows x all h columns; wave w owns rows [64w, 64w + 64).
-// x is read with coalesced 16-byte loads (8 rows x 128 B per instruction),
-// two K-steps ahead, and written to a wave-private LDS tile from which the
-// MFMA B operands are read (a wave's LDS operations complete in order, so
-// the tile needs no barrier).  The W1 slice of each K-step is shared by the
-// four waves through a double-buffered LDS tile (one barrier per K-step),
-// staged through registers in two halves.
-template <int MT>
-__global__ __launch_bounds__(256) void score_mlp_bf16(
+__global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
     float b2, float* __restrict__ b_raw) {
   constexpr int H = 32 * MT;
+  constexpr int MTA = (MT + 1) / 2;          // h tiles of the first half
   constexpr int CPR = kBK / 8;               // 16-byte chunks per row slice (8)
-  constexpr int VPT = H * CPR / 256;         // W1 vectors per thread per K-step (= MT)
-  constexpr int NSPLIT = VPT % 2 == 0 ? 2 : 1;
-  constexpr int VPP = VPT / NSPLIT;
-  constexpr int RSTEP = 256 / CPR;           // W1 rows between a thread's vectors (32)
-  static_assert(H * CPR % 256 == 0, "loader shape");
+  constexpr int NV = H * CPR;                // W1 vectors per K-step
+  constexpr int VPT = (NV + kThreads - 1) / kThreads;
+  constexpr int RSTEP = kThreads / CPR;      // W1 rows between a thread's vectors (64)
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][H * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[4][64 * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][4][64 * kRow];
+  __shared__ float sred[4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wv * 64;
-  uint16_t* sxw = sx[wv];
+  const int rg = wv & 3, hh = wv >> 2;
+  const int mt0 = hh * MTA;
+  const int nmt = hh == 0 ? MTA : MT - MTA;  // h tiles of this wave (may be 0)
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + rg * 64;
 
-  // x loader: load j covers wave rows 8j + lane/8, 16-byte chunk lane%8
-  const uint16_t* xsrc[8];
+  // x loader: this wave loads 4 of the 8 row blocks of its row group;
+  // block j covers rows 8j + lane/8, 16-byte chunk lane%8
+  int64_t xrow[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = 2 * jj + hh;
     int64_t r = row0 + 8 * j + (lane >> 3);
-    r = r < t_in ? r : t_in - 1;
-    xsrc[j] = x + r * xs + 8 * (lane & 7);
+    xrow[jj] = (r < t_in ? r : t_in - 1) * xs + 8 * (lane & 7);
   }
   const int xdst = (lane >> 3) * kRow + 8 * (lane & 7);
   // W1 loader: thread vector i -> row tid / CPR + i * RSTEP, chunk tid % CPR
   const uint16_t* wsrc = w1 + (int64_t)(tid / CPR) * d + 8 * (tid % CPR);
   const int wdst = (tid / CPR) * kRow + 8 * (tid % CPR);
 
-  floatx16 acc[MT][2];
+  floatx16 acc[MTA][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MTA; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc[mt][0][r] = 0.f;
@@ -104,24 +90,24 @@ __global__ __launch_bounds__(256) void score_mlp_bf16(
     }
 
   const int nk = d / kBK;
-  u32x4 xa[8], xb[8];          // x of K-steps it+1 (xa) and it+2 (xb), or clamped repeats
-  u32x4 wreg[VPP];
+  u32x4 xa[4], xb[4];          // x of K-steps it+1 (xa) and it+2 (xb), clamped at the end
+  u32x4 wreg[VPT];
   // prologue: W1 slice 0 and x step 0 to LDS, x steps 1 and 2 to registers
 #pragma unroll
-  for (int p = 0; p < NSPLIT; ++p) {
+  for (int i = 0; i < VPT; ++i)
+    if (i * kThreads + tid < NV) wreg[i] = ld16(wsrc + (int64_t)i * RSTEP * d);
 #pragma unroll
-    for (int i = 0; i < VPP; ++i) wreg[i] = ld16(wsrc + (int64_t)(p * VPP + i) * RSTEP * d);
+  for (int i = 0; i < VPT; ++i)
+    if (i * kThreads + tid < NV) st16(&sw[0][wdst + i * RSTEP * kRow], wreg[i]);
 #pragma unroll
-    for (int i = 0; i < VPP; ++i) st16(&sw[0][wdst + (p * VPP + i) * RSTEP * kRow], wreg[i]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) st16(&sxw[xdst + 8 * j * kRow], ld_nt16(xsrc[j]));
+  for (int jj = 0; jj < 4; ++jj)
+    st16(&sx[0][rg][xdst + 8 * (2 * jj + hh) * kRow], ld_nt16(x + xrow[jj]));
   {
     const int k1 = (nk > 1 ? 1 : 0) * kBK, k2 = (nk > 2 ? 2 : nk - 1) * kBK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      xa[j] = ld_nt16(xsrc[j] + k1);
-      xb[j] = ld_nt16(xsrc[j] + k2);
+    for (int jj = 0; jj < 4; ++jj) {
+      xa[jj] = ld_nt16(x + xrow[jj] + k1);
+      xb[jj] = ld_nt16(x + xrow[jj] + k2);
     }
   }
   __syncthreads();
@@ -131,52 +117,70 @@ __global__ __launch_bounds__(256) void score_mlp_bf16(
     // next W1 slice (the last step re-reads its own: no branch, buffer unused)
     const int kw = (it + 1 < nk ? it + 1 : it) * kBK;
 #pragma unroll
-    for (int i = 0; i < VPP; ++i) wreg[i] = ld16(wsrc + (int64_t)i * RSTEP * d + kw);
-    score_kstep<MT>(acc, sw[buf], sxw, n, g);
+    for (int i = 0; i < VPT; ++i)
+      if (i * kThreads + tid < NV) wreg[i] = ld16(wsrc + (int64_t)i * RSTEP * d + kw);
+    const uint16_t* swb = sw[buf];
+    const uint16_t* sxw = sx[buf][rg];
 #pragma unroll
-    for (int i = 0; i < VPP; ++i) st16(&sw[buf ^ 1][wdst + i * RSTEP * kRow], wreg[i]);
-    if (NSPLIT == 2) {
+    for (int s = 0; s < kBK / 16; ++s) {
+      const bf16x8 bop0 = as_bf16x8(ld16(&sxw[n * kRow + 32 * g + 8 * s]));
+      const bf16x8 bop1 = as_bf16x8(ld16(&sxw[(32 + n) * kRow + 32 * g + 8 * s]));
 #pragma unroll
-      for (int i = 0; i < VPP; ++i) wreg[i] = ld16(wsrc + (int64_t)(VPP + i) * RSTEP * d + kw);
-#pragma unroll
-      for (int i = 0; i < VPP; ++i) st16(&sw[buf ^ 1][wdst + (VPP + i) * RSTEP * kRow], wreg[i]);
+      for (int mt = 0; mt < MTA; ++mt) {
+        if (mt < nmt) {
+          const bf16x8 aop =
+              as_bf16x8(ld16(&swb[(32 * (mt0 + mt) + n) * kRow + 32 * g + 8 * s]));
+          acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop0, acc[mt][0], 0, 0, 0);
+          acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop1, acc[mt][1], 0, 0, 0);
+        }
+      }
     }
-    // x of step it+1 to the wave's tile (after this step's reads, in order),
-    // then rotate the register ring and fetch step it+3
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (i * kThreads + tid < NV) st16(&sw[buf ^ 1][wdst + i * RSTEP * kRow], wreg[i]);
+    // x of step it+1 into the other LDS tile, rotate the ring, fetch step it+3
     const int k3 = (it + 3 < nk ? it + 3 : nk - 1) * kBK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      st16(&sxw[xdst + 8 * j * kRow], xa[j]);
-      xa[j] = xb[j];
-      xb[j] = ld_nt16(xsrc[j] + k3);
+    for (int jj = 0; jj < 4; ++jj) {
+      st16(&sx[buf ^ 1][rg][xdst + 8 * (2 * jj + hh) * kRow], xa[jj]);
+      xa[jj] = xb[jj];
+      xb[jj] = ld_nt16(x + xrow[jj] + k3);
     }
     __syncthreads();
   }
 
-  // epilogue: lane (n, g) holds h = 32mt + 8(r/4) + 4g + (r%4) of rows 32nt + n
+  // epilogue: lane (n, g) holds h = 32(mt0+mt) + 8(r/4) + 4g + (r%4) of rows 32nt + n;
+  // the two h halves of a row group are added through LDS
   float part0 = 0.f, part1 = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < MTA; ++mt) {
+    if (mt < nmt) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int h0 = 32 * mt + 8 * r4 + 4 * g;
-      const float4 bb = b1 ? *reinterpret_cast<const float4*>(b1 + h0) : make_float4(0, 0, 0, 0);
-      const float4 ww = *reinterpret_cast<const float4*>(w2 + h0);
-      part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 0] + bb.x), ww.x, part0);
-      part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 1] + bb.y), ww.y, part0);
-      part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 2] + bb.z), ww.z, part0);
-      part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 3] + bb.w), ww.w, part0);
-      part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 0] + bb.x), ww.x, part1);
-      part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 1] + bb.y), ww.y, part1);
-      part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 2] + bb.z), ww.z, part1);
-      part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 3] + bb.w), ww.w, part1);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int h0 = 32 * (mt0 + mt) + 8 * r4 + 4 * g;
+        const float4 bb = b1 ? *reinterpret_cast<const float4*>(b1 + h0) : make_float4(0, 0, 0, 0);
+        const float4 ww = *reinterpret_cast<const float4*>(w2 + h0);
+        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 0] + bb.x), ww.x, part0);
+        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 1] + bb.y), ww.y, part0);
+        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 2] + bb.z), ww.z, part0);
+        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 3] + bb.w), ww.w, part0);
+        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 0] + bb.x), ww.x, part1);
+        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 1] + bb.y), ww.y, part1);
+        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 2] + bb.z), ww.z, part1);
+        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 3] + bb.w), ww.w, part1);
+      }
     }
   }
   const float tot0 = part0 + __shfl_xor(part0, 32, 64);
   const float tot1 = part1 + __shfl_xor(part1, 32, 64);
-  if (g == 0) {
-    if (row0 + n < t_in) b_raw[row0 + n] = tot0 + b2;
-    if (row0 + 32 + n < t_in) b_raw[row0 + 32 + n] = tot1 + b2;
+  if (hh == 1 && g == 0) {
+    sred[rg][n] = tot0;
+    sred[rg][32 + n] = tot1;
+  }
+  __syncthreads();
+  if (hh == 0 && g == 0) {
+    if (row0 + n < t_in) b_raw[row0 + n] = (tot0 + sred[rg][n]) + b2;
+    if (row0 + 32 + n < t_in) b_raw[row0 + 32 + n] = (tot1 + sred[rg][32 + n]) + b2;
   }
 }
 
@@ -314,7 +318,7 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
     switch (h / 32) {
 #define TG_SCORE_CASE(M)                                                                    \
   case M:                                                                                   \
-    hipLaunchKernelGGL(score_mlp_bf16<M>, grid, dim3(256), 0, st, xp, x_row_stride, t_in, d, \
+    hipLaunchKernelGGL(score_mlp_bf16<M>, grid, dim3(kThreads), 0, st, xp, x_row_stride, t_in, d, \
                        wp, b1, w2, b2, braw);                                               \
     break;
       TG_SCORE_CASE(1) TG_SCORE_CASE(2) TG_SCORE_CASE(3) TG_SCORE_CASE(4)
