@@ -21,16 +21,18 @@
 //    LDS feeds all HPW heads; two waves per SIMD;
 //  - a wave owns 32 query rows of one head.  It computes S^T = K.Q^T (keys
 //    on the MFMA M axis, queries on N), so each lane holds one query's
-//    logits: the softmax statistics are per-lane scalars plus one exchange
-//    between the two lane halves;
+//    logits: the softmax statistics are per-lane scalars plus one swap
+//    between the two lane halves (v_permlane32_swap);
 //  - P^T from the accumulators is directly the B operand of O^T = V^T.P^T
 //    with keys permuted consistently between the two operands; V is
 //    transposed into LDS ([d][key]) in that permuted key order, so each lane
 //    reads its 8 keys with one 16-byte load;
-//  - software pipelining: the Q.K^T MFMAs of tile t+1 are issued before the
-//    softmax of tile t, so the vector ALU and the matrix cores work at the
-//    same time; K/V tiles are triple-buffered in LDS with one barrier per
-//    tile;
+//  - the softmax normaliser sums the bf16-rounded probabilities that enter
+//    the P.V product (v_dot2 against (1, 1)), so numerator and denominator
+//    carry the same weights;
+//  - K/V/bias tiles are double-buffered in LDS: tile t+1 is fetched from HBM
+//    into registers (buffer loads whose range ends at the sequence's last
+//    row, so a partial last tile reads zeros) while tile t is computed;
 //  - causal masking runs only on diagonal tiles, tiles past a wave's rows
 //    are skipped, query blocks are issued longest first, and the blocks of
 //    one KV head share an XCD (blocks are dealt round-robin over the 8 XCDs,
@@ -62,6 +64,46 @@ TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 TG_DEVINL uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// IEEE maximum (NaN-propagating): needs no input canonicalisation and maps
+// onto v_maximum3_f32
+TG_DEVINL float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// v_permlane32_swap on two copies of x leaves {x[l], x[l ^ 32]} in every
+// lane l, one in each register.  Written in asm because the compiler's
+// builtin for it hands back the first result for both.
+TG_DEVINL void half_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+TG_DEVINL float half_swap_max(float x) {
+  float a = x, b = x;
+  half_swap(a, b);
+  return __builtin_elementwise_maximum(a, b);
+}
+TG_DEVINL float half_swap_sum(float x) {
+  float a = x, b = x;
+  half_swap(a, b);
+  return a + b;
+}
+
+// sum of the two bf16 halves of w, accumulated in fp32
+TG_DEVINL float dot2_ones(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// raw buffer resource over [base, base + bytes): loads past the end return 0
+TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+TG_DEVINL u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+TG_DEVINL float buf_ldf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // position of key k of a tile in a V^T row: inside each group of 16 keys the
@@ -169,28 +211,30 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
 
+  // per-thread byte offsets inside a tile (rows of k and v are kvstride apart)
+  const int koff0 = (krow0 * (int)kvstride + kcol0) * 2;
+  const int koff1 = (krow1 * (int)kvstride + kcol1) * 2;
+  const int voff0 = ((2 * vkp) * (int)kvstride + 8 * vdc) * 2;
+  const int voff1 = voff0 + (int)kvstride * 2;
+  const int boff = (tid % BKV) * 4;
+
   u32x4 kreg0 = {0u, 0u, 0u, 0u}, kreg1 = {0u, 0u, 0u, 0u};
   u32x4 vreg0 = {0u, 0u, 0u, 0u}, vreg1 = {0u, 0u, 0u, 0u};
   float breg = 0.f;
 
   auto load_tile = [&](int t) {
     const int kv0 = t * BKV;
-    if (kv0 + BKV <= len) {                      // whole tile inside the sequence
-      const int64_t off = (int64_t)kv0 * kvstride;
-      kreg0 = ld16(kb_ + off + (int64_t)krow0 * kvstride + kcol0);
-      if (C::KVPT == 2) kreg1 = ld16(kb_ + off + (int64_t)krow1 * kvstride + kcol1);
-      vreg0 = ld16(vb_ + off + (int64_t)(2 * vkp) * kvstride + 8 * vdc);
-      vreg1 = ld16(vb_ + off + (int64_t)(2 * vkp + 1) * kvstride + 8 * vdc);
-      breg = kept_b[lo + kv0 + (tid % BKV)];
-    } else {                                     // last, partial tile: clamp rows
-      const int r0 = min(kv0 + krow0, len - 1), r1 = min(kv0 + krow1, len - 1);
-      kreg0 = ld16(kb_ + (int64_t)r0 * kvstride + kcol0);
-      if (C::KVPT == 2) kreg1 = ld16(kb_ + (int64_t)r1 * kvstride + kcol1);
-      const int v0 = min(kv0 + 2 * vkp, len - 1), v1 = min(kv0 + 2 * vkp + 1, len - 1);
-      vreg0 = ld16(vb_ + (int64_t)v0 * kvstride + 8 * vdc);
-      vreg1 = ld16(vb_ + (int64_t)v1 * kvstride + 8 * vdc);
-      breg = kept_b[lo + min(kv0 + (tid % BKV), len - 1)];
-    }
+    const int rows = len - kv0 < BKV ? len - kv0 : BKV;      // rows of this tile in the sequence
+    const int64_t off = (int64_t)kv0 * kvstride;
+    const int bytes = rows * (int)kvstride * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb_ + off, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb_ + off, bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(kept_b + lo + kv0, rows * 4);
+    kreg0 = buf_ld16(rk, koff0);
+    if (C::KVPT == 2) kreg1 = buf_ld16(rk, koff1);
+    vreg0 = buf_ld16(rv, voff0);
+    vreg1 = buf_ld16(rv, voff1);
+    breg = buf_ldf(rb, boff);
   };
   auto store_tile = [&](auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
@@ -232,6 +276,7 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float mrun = -INFINITY;
+  float negm = 0.f;                              // -mrun, 0 while mrun is -inf
   float lsum = 0.f;
   const int wq_last = wq0 + QW - 1 < len - 1 ? wq0 + QW - 1 : len - 1;
   const int w_tiles = wq0 < len ? wq_last / BKV + 1 : 0;   // tiles this wave needs
@@ -254,25 +299,30 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
       sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           as_bf16x8(ld16(kl + 32 * C::KROW + 16 * kk)), qf[kk], sc1, 0, 0, 0);
     }
-    // causal mask, only where the tile reaches past the wave's first row
+    // causal mask, only where the tile reaches past the wave's first row:
+    // key 8(r/4) + 4g + r%4 (+32 for sc1) of the tile is masked when it lies
+    // past this lane's query
     if (kv0 + BKV - 1 > wq0) {
+      const int dq = qa - kv0 - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kj = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        sc0[r] = kj > qa ? -INFINITY : sc0[r];
-        sc1[r] = kj + 32 > qa ? -INFINITY : sc1[r];
+        const int kr = 8 * (r >> 2) + (r & 3);
+        sc0[r] = kr > dq ? -INFINITY : sc0[r];
+        sc1[r] = kr + 32 > dq ? -INFINITY : sc1[r];
       }
     }
-    // online softmax on the unscaled accumulator (c_i > 0): 3-input max tree
-    float m4[4];
+    // online softmax on the unscaled accumulator (c_i > 0)
+    float ma = fmax3(sc0[0], sc0[1], sc0[2]);
+    float mb = fmax3(sc1[0], sc1[1], sc1[2]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      m4[i] = fmaxf(fmaxf(fmaxf(sc0[4 * i], sc0[4 * i + 1]), fmaxf(sc0[4 * i + 2], sc0[4 * i + 3])),
-                    fmaxf(fmaxf(sc1[4 * i], sc1[4 * i + 1]), fmaxf(sc1[4 * i + 2], sc1[4 * i + 3])));
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cq;
+    for (int r = 3; r < 15; r += 2) {
+      ma = fmax3(ma, sc0[r], sc0[r + 1]);
+      mb = fmax3(mb, sc1[r], sc1[r + 1]);
+    }
+    const float mx = half_swap_max(fmax3(ma, mb, __builtin_elementwise_maximum(sc0[15], sc1[15])))
+                     * cq;
     if (__any(mx > mrun + kRescaleSlack)) {
-      const float mnew = fmaxf(mrun, mx);
+      const float mnew = __builtin_elementwise_maximum(mrun, mx);
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       lsum *= alpha;
 #pragma unroll
@@ -280,29 +330,30 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       mrun = mnew;
+      negm = mnew == -INFINITY ? 0.0f : -mnew;
     }
-    const float negm = mrun == -INFINITY ? 0.0f : -mrun;
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    // p = exp2(c * acc - m), rounded to bf16 as P^T, the B operand of
+    // O^T = V^T.P^T: K-step kk holds keys 16kk + 8(e/4) + 4g + e%4, i.e.
+    // registers 8(kk%2) .. +8 of tile kk/2
+    uint32_t pw[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc0[r], cq, negm));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc1[r], cq, negm));
-      sc0[r] = p0;
-      sc1[r] = p1;
-      l4[r & 3] += p0 + p1;
+    for (int i = 0; i < 8; ++i) {
+      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc0[2 * i], cq, negm)),
+                          __builtin_amdgcn_exp2f(fmaf(sc0[2 * i + 1], cq, negm)));
+      pw[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc1[2 * i], cq, negm)),
+                              __builtin_amdgcn_exp2f(fmaf(sc1[2 * i + 1], cq, negm)));
     }
-    lsum += (l4[0] + l4[1]) + (l4[2] + l4[3]);
-    // P^T as the B operand of O^T = V^T.P^T: K-step kk holds keys
-    // 16kk + 8(e/4) + 4g + e%4, i.e. registers 8(kk%2) .. +8 of tile kk/2
+    float la = dot2_ones(pw[0], lsum), lb = dot2_ones(pw[1], 0.0f);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+      la = dot2_ones(pw[i], la);
+      lb = dot2_ones(pw[i + 1], lb);
+    }
+    lsum = la + lb;
     bf16x8 pf[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const floatx16& sa = (kk >> 1) ? sc1 : sc0;
-      const int o = 8 * (kk & 1);
-      const u32x4 u = {pack_bf16x2(sa[o + 0], sa[o + 1]), pack_bf16x2(sa[o + 2], sa[o + 3]),
-                       pack_bf16x2(sa[o + 4], sa[o + 5]), pack_bf16x2(sa[o + 6], sa[o + 7])};
-      pf[kk] = as_bf16x8(u);
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      pf[kk] = as_bf16x8((u32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
     // O^T += V^T . P^T  (A operand: V^T row d = 32dt + n, 8 permuted keys)
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
@@ -333,7 +384,7 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   }
 
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float lt = half_swap_sum(lsum);
   if (!qvalid) return;
   const float inv = 1.0f / lt;
   uint16_t* op = out + ((int64_t)(lo + qa) * hq + head) * DH;
