@@ -30,18 +30,31 @@
 //  - the softmax normaliser sums the bf16-rounded probabilities that enter
 //    the P.V product (v_dot2 against (1, 1)), so numerator and denominator
 //    carry the same weights;
-//  - K/V/bias tiles are double-buffered in LDS: tile t+1 is fetched from HBM
-//    into registers (buffer loads whose range ends at the sequence's last
-//    row, so a partial last tile reads zeros) while tile t is computed;
-//  - causal masking runs only on diagonal tiles, tiles past a wave's rows
-//    are skipped, query blocks are issued longest first, and the blocks of
-//    one KV head share an XCD (blocks are dealt round-robin over the 8 XCDs,
-//    so the head index is taken from the low bits of the block index);
+//  - K/V/bias tiles rotate through three LDS buffers: tile t+1 is fetched
+//    from HBM into registers (buffer loads whose range ends at the
+//    sequence's last row, so a partial last tile reads zeros) while tile t
+//    is computed;
+//  - the two waves that share a SIMD run half a tile apart (one does
+//    S then P.V of tile t, the other P.V of tile t-1 then S of tile t), so
+//    the matrix products of one overlap the softmax of the other;
+//  - inside a phase the instruction order is pinned with scheduling
+//    barriers so that LDS operand reads run four MFMAs ahead of their use;
+//  - workgroups are persistent (one per CU): the workgroups of one head
+//    group take its query blocks longest first in snake order, which
+//    balances the causal triangle; the blocks of one KV head share an XCD
+//    (workgroups are dealt round-robin over the 8 XCDs, so the head group is
+//    taken from the low bits of the workgroup index);
+//  - causal masking runs only on diagonal tiles and tiles past a wave's rows
+//    are skipped;
 //  - the running maximum is only moved when it grows by more than 2^8 in
 //    the exponent (exact: the normaliser absorbs the stale maximum).
 #include <type_traits>
 
 #include "common.h"
+
+#ifndef TG_ATTN_WAVES
+#define TG_ATTN_WAVES 8
+#endif
 
 namespace tg {
 namespace {
@@ -51,10 +64,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int BKV = 64;                 // keys per tile
-constexpr int NWAVE = 8;                // waves per workgroup
-constexpr int NTHR = 64 * NWAVE;
 constexpr int QW = 32;                  // query rows per wave
-constexpr int NBUF = 2;                 // LDS tile buffers
+constexpr int NBUF = 3;                 // LDS tile buffers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kMinScale = 1e-30f;     // keeps c_i > 0 so masked keys stay -inf
@@ -114,8 +125,9 @@ TG_DEVINL int vpos(int k) {
   return (k & ~15) | (r < 4 || r >= 12 ? r : (r < 8 ? r + 4 : r - 4));
 }
 
-template <int DH, int HPW>
+template <int DH, int HPW, int NWAVE>
 struct AttnCfg {
+  static constexpr int NTHR = 64 * NWAVE;        // threads per workgroup
   static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
   static constexpr int KROW = DH + 24;           // K row: DH values, 16 bias columns, 8 pad
   static constexpr int VROW = BKV + 8;           // V^T row: 64 keys, 8 pad
@@ -124,31 +136,24 @@ struct AttnCfg {
   static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile
   static constexpr int KVPT = (KVEC + NTHR - 1) / NTHR;
   static constexpr int VUNITS = (BKV / 2) * (DH / 8);   // (2-key pair, 8-dim chunk) units
+  static constexpr int VUPT = (VUNITS + NTHR - 1) / NTHR;
   static constexpr int KTILE = BKV * KROW;       // bf16 per K buffer
   static constexpr int VTILE = DH * VROW;        // bf16 per V^T buffer
 };
 
-template <int DH, int HPW>
-__global__ __launch_bounds__(NTHR) void gated_attn_bf16(
+template <int DH, int HPW, int NWAVE>
+__device__ __forceinline__ void gated_attn_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
-    int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
-    const float* __restrict__ temp, float sm_scale) {
-  using C = AttnCfg<DH, HPW>;
-  static_assert(C::KVPT <= 2 && C::VUNITS <= NTHR, "loader shape");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF * C::VTILE];
-
+    int t_kept, int hq, int hkv, int groups_y, int hg, int64_t slot,
+    const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale,
+    uint16_t* sk, uint16_t* sv) {
+  using C = AttnCfg<DH, HPW, NWAVE>;
+  constexpr int NTHR = C::NTHR;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-
-  // ---- block -> (head group, sequence, query block); head group from the
-  // low bits (one XCD per KV head), query slots last-first (longest first)
-  const int n_hg = hkv * groups_y;
-  const int hg = (int)(blockIdx.x % (unsigned)n_hg);
-  const int64_t slot = (int64_t)n_slots - 1 - (int64_t)(blockIdx.x / (unsigned)n_hg);
   const int s = seq_of_slot(kept_cu, n_seq, slot, C::QB);
   if (s < 0) return;
   // rows are clamped to [0, t_kept): inconsistent offsets cannot read out of bounds
@@ -198,28 +203,33 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   const int64_t kvstride = (int64_t)hkv * DH;     // elements between token rows of k, v
   const uint16_t* kb_ = k + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   const uint16_t* vb_ = v + (int64_t)lo * kvstride + (int64_t)kvh * DH;
-  // K: vectors tid and tid + NTHR of the tile (row key, 16-byte chunk ch)
-  const int kvi0 = tid % C::KVEC, kvi1 = (tid + NTHR) % C::KVEC;
-  const int krow0 = kvi0 / (DH / 8), krow1 = kvi1 / (DH / 8);
-  const int kcol0 = 8 * (kvi0 % (DH / 8)), kcol1 = 8 * (kvi1 % (DH / 8));
-  const int kdst0 = krow0 * C::KROW + kcol0, kdst1 = krow1 * C::KROW + kcol1;
-  // V: unit (key pair vkp, 8-dim chunk vdc), transposed into V^T rows 8vdc..+8
-  const int vu = tid % C::VUNITS;
-  const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
-  const int vdst = (8 * vdc) * C::VROW + vpos(2 * vkp);
   float bsc[4];                                   // gain_h / s of the HPW heads
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
 
-  // per-thread byte offsets inside a tile (rows of k and v are kvstride apart)
-  const int koff0 = (krow0 * (int)kvstride + kcol0) * 2;
-  const int koff1 = (krow1 * (int)kvstride + kcol1) * 2;
-  const int voff0 = ((2 * vkp) * (int)kvstride + 8 * vdc) * 2;
-  const int voff1 = voff0 + (int)kvstride * 2;
+  // K: 16-byte vectors tid + i*NTHR of the tile (row, 8-element chunk), to
+  // LDS row-major with the padded row stride; V: units (key pair, 8-dim
+  // chunk), transposed into V^T rows 8*chunk .. +8 at the permuted key slot.
+  // Offsets in global memory are bytes from the tile's first row (rows of k
+  // and v are kvstride elements apart).
+  int koff[C::KVPT], kdst[C::KVPT], voff[C::VUPT], vdst[C::VUPT];
+#pragma unroll
+  for (int i = 0; i < C::KVPT; ++i) {
+    const int kvi = (tid + i * NTHR) % C::KVEC;
+    const int row = kvi / (DH / 8), col = 8 * (kvi % (DH / 8));
+    koff[i] = (row * (int)kvstride + col) * 2;
+    kdst[i] = row * C::KROW + col;
+  }
+#pragma unroll
+  for (int i = 0; i < C::VUPT; ++i) {
+    const int vu = (tid + i * NTHR) % C::VUNITS;
+    const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
+    voff[i] = ((2 * vkp) * (int)kvstride + 8 * vdc) * 2;
+    vdst[i] = (8 * vdc) * C::VROW + vpos(2 * vkp);
+  }
   const int boff = (tid % BKV) * 4;
 
-  u32x4 kreg0 = {0u, 0u, 0u, 0u}, kreg1 = {0u, 0u, 0u, 0u};
-  u32x4 vreg0 = {0u, 0u, 0u, 0u}, vreg1 = {0u, 0u, 0u, 0u};
+  u32x4 kreg[C::KVPT], vreg[C::VUPT][2];
   float breg = 0.f;
 
   auto load_tile = [&](int t) {
@@ -230,27 +240,35 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb_ + off, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb_ + off, bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(kept_b + lo + kv0, rows * 4);
-    kreg0 = buf_ld16(rk, koff0);
-    if (C::KVPT == 2) kreg1 = buf_ld16(rk, koff1);
-    vreg0 = buf_ld16(rv, voff0);
-    vreg1 = buf_ld16(rv, voff1);
+#pragma unroll
+    for (int i = 0; i < C::KVPT; ++i)
+      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) kreg[i] = buf_ld16(rk, koff[i]);
+#pragma unroll
+    for (int i = 0; i < C::VUPT; ++i)
+      if (C::VUNITS % NTHR == 0 || tid + i * NTHR < C::VUNITS) {
+        vreg[i][0] = buf_ld16(rv, voff[i]);
+        vreg[i][1] = buf_ld16(rv, voff[i] + (int)kvstride * 2);
+      }
     breg = buf_ldf(rb, boff);
   };
   auto store_tile = [&](auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
     uint16_t* skb = sk + BUF * C::KTILE;
     uint16_t* svb = sv + BUF * C::VTILE;
-    if (tid < C::KVEC) st16(&skb[kdst0], kreg0);
-    if (C::KVPT == 2 && tid + NTHR < C::KVEC) st16(&skb[kdst1], kreg1);
-    if (tid < C::VUNITS) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a0 = vreg0[e >> 1], a1 = vreg1[e >> 1];
-        const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
-                                    : ((a0 & 0xffffu) | (a1 << 16));
-        *reinterpret_cast<uint32_t*>(&svb[vdst + e * C::VROW]) = pk;
+    for (int i = 0; i < C::KVPT; ++i)
+      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) st16(&skb[kdst[i]], kreg[i]);
+#pragma unroll
+    for (int i = 0; i < C::VUPT; ++i)
+      if (C::VUNITS % NTHR == 0 || tid + i * NTHR < C::VUNITS) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a0 = vreg[i][0][e >> 1], a1 = vreg[i][1][e >> 1];
+          const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
+                                      : ((a0 & 0xffffu) | (a1 << 16));
+          *reinterpret_cast<uint32_t*>(&svb[vdst[i] + e * C::VROW]) = pk;
+        }
       }
-    }
     if (tid < BKV) {
       // bias columns of key tid: (hi, lo) bf16 parts of gain_h * b / s per head
       uint32_t w[4];
@@ -281,46 +299,57 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
   const int wq_last = wq0 + QW - 1 < len - 1 ? wq0 + QW - 1 : len - 1;
   const int w_tiles = wq0 < len ? wq_last / BKV + 1 : 0;   // tiles this wave needs
 
-  // one tile of one wave: S^T = K'.Q'^T (bias step first), softmax, O^T += V^T.P^T
-  auto compute = [&](auto BUFC, int t) {
+  // Phase S of one tile of one wave: S^T = K'.Q'^T (bias step first), mask,
+  // running maximum and the probabilities P^T as bf16 words in pw.  The
+  // instruction order is fixed by scheduling barriers: K fragment reads run
+  // four MFMAs ahead of their use.
+  uint32_t pw[16];
+  auto phase_s = [&](auto BUFC, int t) {
     constexpr int BUF = decltype(BUFC)::value;
     const int kv0 = t * BKV;
     const uint16_t* kl = klane + BUF * C::KTILE;
-    const uint16_t* vl = vlane + BUF * C::VTILE;
-    const floatx16 zero = {};
-    floatx16 sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kl + DH)), qsel, zero,
-                                                           0, 0, 0);
-    floatx16 sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        as_bf16x8(ld16(kl + 32 * C::KROW + DH)), qsel, zero, 0, 0, 0);
+    // K fragment j of the tile: key half j & 1, K-step (j >> 1) - 1 (-1: bias columns)
+    auto kfrag = [&](int j) {
+      const int st = (j >> 1) - 1;
+      return ld16(kl + 32 * (j & 1) * C::KROW + (st < 0 ? DH : 16 * st));
+    };
+    constexpr int NK = 2 * (C::KT + 1);          // MFMAs of S^T
+    u32x4 kr[4];
 #pragma unroll
-    for (int kk = 0; kk < C::KT; ++kk) {
-      sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kl + 16 * kk)), qf[kk], sc0,
-                                                    0, 0, 0);
-      sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          as_bf16x8(ld16(kl + 32 * C::KROW + 16 * kk)), qf[kk], sc1, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) kr[j] = kfrag(j);
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 sc[2];
+    const floatx16 zero = {};
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const bf16x8 bop = j < 2 ? qsel : qf[(j >> 1) - 1];
+      sc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[j % 4]), bop,
+                                                          j < 2 ? zero : sc[j & 1], 0, 0, 0);
+      if (j + 4 < NK) kr[j % 4] = kfrag(j + 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // causal mask, only where the tile reaches past the wave's first row:
-    // key 8(r/4) + 4g + r%4 (+32 for sc1) of the tile is masked when it lies
-    // past this lane's query
+    // key 8(r/4) + 4g + r%4 (+32 for sc[1]) of the tile is masked when it
+    // lies past this lane's query
     if (kv0 + BKV - 1 > wq0) {
       const int dq = qa - kv0 - 4 * g;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kr = 8 * (r >> 2) + (r & 3);
-        sc0[r] = kr > dq ? -INFINITY : sc0[r];
-        sc1[r] = kr + 32 > dq ? -INFINITY : sc1[r];
+        const int kr_ = 8 * (r >> 2) + (r & 3);
+        sc[0][r] = kr_ > dq ? -INFINITY : sc[0][r];
+        sc[1][r] = kr_ + 32 > dq ? -INFINITY : sc[1][r];
       }
     }
     // online softmax on the unscaled accumulator (c_i > 0)
-    float ma = fmax3(sc0[0], sc0[1], sc0[2]);
-    float mb = fmax3(sc1[0], sc1[1], sc1[2]);
+    float ma = fmax3(sc[0][0], sc[0][1], sc[0][2]);
+    float mb = fmax3(sc[1][0], sc[1][1], sc[1][2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) {
-      ma = fmax3(ma, sc0[r], sc0[r + 1]);
-      mb = fmax3(mb, sc1[r], sc1[r + 1]);
+      ma = fmax3(ma, sc[0][r], sc[0][r + 1]);
+      mb = fmax3(mb, sc[1][r], sc[1][r + 1]);
     }
-    const float mx = half_swap_max(fmax3(ma, mb, __builtin_elementwise_maximum(sc0[15], sc1[15])))
-                     * cq;
+    const float mx =
+        half_swap_max(fmax3(ma, mb, __builtin_elementwise_maximum(sc[0][15], sc[1][15]))) * cq;
     if (__any(mx > mrun + kRescaleSlack)) {
       const float mnew = __builtin_elementwise_maximum(mrun, mx);
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
@@ -334,53 +363,98 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     }
     // p = exp2(c * acc - m), rounded to bf16 as P^T, the B operand of
     // O^T = V^T.P^T: K-step kk holds keys 16kk + 8(e/4) + 4g + e%4, i.e.
-    // registers 8(kk%2) .. +8 of tile kk/2
-    uint32_t pw[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc0[2 * i], cq, negm)),
-                          __builtin_amdgcn_exp2f(fmaf(sc0[2 * i + 1], cq, negm)));
-      pw[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc1[2 * i], cq, negm)),
-                              __builtin_amdgcn_exp2f(fmaf(sc1[2 * i + 1], cq, negm)));
-    }
-    float la = dot2_ones(pw[0], lsum), lb = dot2_ones(pw[1], 0.0f);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      la = dot2_ones(pw[i], la);
-      lb = dot2_ones(pw[i + 1], lb);
-    }
-    lsum = la + lb;
-    bf16x8 pf[4];
+    // registers 8(kk%2) .. +8 of sc[kk/2]; word w of group kk packs the
+    // pair 2w, 2w+1 of those eight
+    float la = lsum, lb = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      pf[kk] = as_bf16x8((u32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
-    // O^T += V^T . P^T  (A operand: V^T row d = 32dt + n, 8 permuted keys)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = as_bf16x8(ld16(vl + 32 * dt * C::VROW + 16 * kk));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], oacc[dt], 0, 0, 0);
+      for (int w = 0; w < 4; ++w) {
+        const floatx16& sa = sc[kk >> 1];
+        const int o = 8 * (kk & 1) + 2 * w;
+        pw[4 * kk + w] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sa[o], cq, negm)),
+                                     __builtin_amdgcn_exp2f(fmaf(sa[o + 1], cq, negm)));
+        if (w & 1)
+          lb = dot2_ones(pw[4 * kk + w], lb);
+        else
+          la = dot2_ones(pw[4 * kk + w], la);
       }
+    lsum = la + lb;
+  };
+
+  // O^T += V^T . P^T for the tile in buffer BUF and the P^T words in pw
+  // (A operand: V^T row d = 32dt + n, 8 permuted keys); V^T reads run four
+  // MFMAs ahead of their use
+  auto phase_pv = [&](auto BUFC) {
+    constexpr int BUF = decltype(BUFC)::value;
+    const uint16_t* vl = vlane + BUF * C::VTILE;
+    auto vfrag = [&](int i) { return ld16(vl + 32 * (i % C::DT) * C::VROW + 16 * (i / C::DT)); };
+    constexpr int NV = 4 * C::DT;
+    u32x4 vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = vfrag(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int kk = i / C::DT, dt = i % C::DT;
+      const bf16x8 pf = as_bf16x8((u32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2],
+                                          pw[4 * kk + 3]});
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[i % 4]), pf, oacc[dt], 0, 0,
+                                                         0);
+      if (i + 4 < NV) vr[i % 4] = vfrag(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // Tiles rotate through three LDS buffers; iteration t computes tile t while
+  // tile t+1 is fetched and stored.  The two waves that share a SIMD work
+  // half a tile apart: waves 0..3 run S(t) then P.V(t), waves 4..7 run
+  // P.V(t-1) then S(t), so one wave's matrix products overlap the other's
+  // softmax instead of both contending for the matrix core at once.
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  const bool lag = wv >= NWAVE / 2;
   load_tile(0);
   store_tile(B0{});
   __syncthreads();
-  // double-buffered tiles, unrolled by two so every LDS offset is a constant
-  for (int t = 0; t < n_tiles; t += 2) {
+  auto step = [&](auto BC, auto BP, auto BN, int t) {
     if (t + 1 < n_tiles) load_tile(t + 1);
-    if (t < w_tiles) compute(B0{}, t);
-    if (t + 1 < n_tiles) store_tile(B1{});
+    if (!lag) {
+      if (t < w_tiles) {
+        phase_s(BC, t);
+        phase_pv(BC);
+      }
+    } else {
+      if (t >= 1 && t - 1 < w_tiles) phase_pv(BP);
+      if (t < w_tiles) phase_s(BC, t);
+    }
+    if (t + 1 < n_tiles) store_tile(BN);
     __syncthreads();
-    if (t + 1 >= n_tiles) break;
-    if (t + 2 < n_tiles) load_tile(t + 2);
-    if (t + 1 < w_tiles) compute(B1{}, t + 1);
-    if (t + 2 < n_tiles) store_tile(B0{});
-    __syncthreads();
+  };
+  int t = 0;
+  for (; t < n_tiles; t += 3) {
+    step(B0{}, B2{}, B1{}, t);
+    if (t + 1 >= n_tiles) {
+      t += 1;
+      break;
+    }
+    step(B1{}, B0{}, B2{}, t + 1);
+    if (t + 2 >= n_tiles) {
+      t += 2;
+      break;
+    }
+    step(B2{}, B1{}, B0{}, t + 2);
+  }
+  // t == n_tiles here; the lagging waves still owe P.V of the last tile
+  if (lag && n_tiles - 1 < w_tiles) {
+    const int bl = (n_tiles - 1) % 3;
+    if (bl == 0)
+      phase_pv(B0{});
+    else if (bl == 1)
+      phase_pv(B1{});
+    else
+      phase_pv(B2{});
   }
 
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4
@@ -399,18 +473,79 @@ __global__ __launch_bounds__(NTHR) void gated_attn_bf16(
     }
 }
 
-template <int DH, int HPW>
+// two waves per SIMD: at most 256 registers per lane
+template <int DH, int HPW, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
+void gated_attn_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
+    const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
+    int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
+    const float* __restrict__ temp, float sm_scale) {
+  using C = AttnCfg<DH, HPW, NWAVE>;
+  static_assert(NWAVE % HPW == 0 && C::NTHR >= BKV, "workgroup shape");
+  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF * C::VTILE];
+
+  // ---- persistent workgroups: the head group comes from the low bits of the
+  // block index (blocks are dealt round-robin over the 8 XCDs, so the blocks
+  // of one KV head share an XCD and its L2); the pj blocks of a head group
+  // take its query slots last-first (longest first under the causal mask)
+  // in snake order, so every block gets a long and a short slot per pair of
+  // rounds
+  const int n_hg = hkv * groups_y;
+  const int hg = (int)(blockIdx.x % (unsigned)n_hg);
+  const int jb = (int)(blockIdx.x / (unsigned)n_hg);
+  const int pj = (int)(gridDim.x / (unsigned)n_hg);
+  for (int64_t round = 0;; ++round) {
+    const int64_t rank = round * pj + ((round & 1) ? pj - 1 - jb : jb);
+    if (rank >= n_slots) break;
+    gated_attn_item<DH, HPW, NWAVE>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept, hq,
+                                    hkv, groups_y, hg, n_slots - 1 - rank, gain, temp, sm_scale,
+                                    sk, sv);
+    __syncthreads();                               // LDS buffers are reused by the next slot
+  }
+}
+
+// compute units of the current device, cached per device
+hipError_t device_cu_count(int* n_cu) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *n_cu = cache[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n_cu < 1) *n_cu = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = *n_cu;
+  return hipSuccess;
+}
+
+template <int DH, int HPW, int NWAVE>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                       const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,
                       int n_seq, int hq, int hkv, const float* gain, const float* temp,
                       float sm_scale, hipStream_t st) {
-  constexpr int QB = AttnCfg<DH, HPW>::QB;
+  constexpr int QB = AttnCfg<DH, HPW, NWAVE>::QB;
   const int G = hq / hkv;
   const int groups_y = G / HPW;
   const int64_t n_slots = n_seq + (t_kept + QB - 1) / QB;
-  const int64_t blocks = n_slots * hkv * groups_y;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW>), dim3((unsigned)blocks), dim3(NTHR), 0, st,
+  const int n_hg = hkv * groups_y;
+  // persistent grid: one workgroup per CU (the register budget allows one),
+  // the same number for every head group
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
+  int64_t pj = n_cu / n_hg;
+  if (pj < 1) pj = 1;
+  if (pj > n_slots) pj = n_slots;
+  const int64_t blocks = (int64_t)n_hg * pj;
+  if (n_slots > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW, NWAVE>), dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), kept_b, kept_pos,
                      kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, (int)n_slots, gain, temp,
@@ -430,7 +565,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const int hpw = G >= 4 ? 4 : G;
 #define TG_ATTN(DHv, HPWv)                                                                     \
   if (dh == DHv && hpw == HPWv)                                                                \
-    return launch_cfg<DHv, HPWv>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
+    return launch_cfg<DHv, HPWv, TG_ATTN_WAVES>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
                                  hkv, gain, temp, sm_scale, st);
   TG_ATTN(128, 1) TG_ATTN(128, 2) TG_ATTN(128, 4)
   TG_ATTN(64, 1) TG_ATTN(64, 2) TG_ATTN(64, 4)
