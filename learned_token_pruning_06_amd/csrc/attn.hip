@@ -497,11 +497,21 @@ void gated_attn_bf16(
   const int hg = (int)(blockIdx.x % (unsigned)n_hg);
   const int jb = (int)(blockIdx.x / (unsigned)n_hg);
   const int pj = (int)(gridDim.x / (unsigned)n_hg);
+  // slots past the last query block of the last sequence hold no work: rank
+  // from the last real one
+  int64_t n_real = n_slots;
+  if (n_seq > 0) {
+    const int last_lo = kept_cu[n_seq - 1] < t_kept ? kept_cu[n_seq - 1] : t_kept;
+    const int last_hi = kept_cu[n_seq] < t_kept ? kept_cu[n_seq] : t_kept;
+    const int last_len = last_hi > last_lo ? last_hi - last_lo : 0;
+    const int64_t end = slot0_of(kept_cu, n_seq - 1, C::QB) + (last_len + C::QB - 1) / C::QB;
+    if (end >= 0 && end < n_real) n_real = end;
+  }
   for (int64_t round = 0;; ++round) {
     const int64_t rank = round * pj + ((round & 1) ? pj - 1 - jb : jb);
-    if (rank >= n_slots) break;
+    if (rank >= n_real) break;
     gated_attn_item<DH, HPW, NWAVE>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept, hq,
-                                    hkv, groups_y, hg, n_slots - 1 - rank, gain, temp, sm_scale,
+                                    hkv, groups_y, hg, n_real - 1 - rank, gain, temp, sm_scale,
                                     sk, sv);
     __syncthreads();                               // LDS buffers are reused by the next slot
   }
