@@ -54,11 +54,12 @@ def traffic_for(kernel: str, src_files):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(g, t_kept_cu, n_rows_score=8192, n_attn_rows=96):
-    """The fp64 oracle on a bounded sample of the same workload, scaled to the
-    whole step: score on the first n_rows_score rows (x linear), normalise +
-    select + gather on all 131072 tokens, attention on n_attn_rows query rows
-    spread over the kept tokens (x keys visited)."""
+def cpu_baseline(g, t_kept_cu, score_chunk=16384):
+    """The fp64 oracle on the whole step of the same workload: score and
+    normalise all 131072 tokens (x upcast in chunks of score_chunk rows),
+    select, gather, and the gated attention over all kept query rows and
+    heads.  Q/K/V are seeded stand-ins of the kept shape (the projection is
+    not part of the step)."""
     import numpy as np
     import oracle as O
     from workloads import bf16_to_f64, random_qkv
@@ -69,11 +70,13 @@ def cpu_baseline(g, t_kept_cu, n_rows_score=8192, n_attn_rows=96):
         blas = os.cpu_count()
     wl = g["wl"]
     T = wl.t_in
+    w1 = bf16_to_f64(g["w1"])
     t0 = time.perf_counter()
-    xs = bf16_to_f64(g["x"][:n_rows_score])
-    b_raw_s = O.ref_score(xs, bf16_to_f64(g["w1"]), g["b1"], g["w2"], g["b2"])
-    t_score = (time.perf_counter() - t0) * (T / n_rows_score)
-    b_raw = np.tile(b_raw_s, T // n_rows_score + 1)[:T]
+    b_raw = np.empty(T)
+    for r0 in range(0, T, score_chunk):
+        b_raw[r0:r0 + score_chunk] = O.ref_score(bf16_to_f64(g["x"][r0:r0 + score_chunk]), w1,
+                                                 g["b1"], g["w2"], g["b2"])
+    t_score = time.perf_counter() - t0
     t0 = time.perf_counter()
     b, _ = O.ref_normalise(b_raw, g["prunable"], g["cu_seqlens"])
     idx, pos, kb, kc = O.ref_select(b.astype(np.float32), g["prunable"], g["cu_seqlens"],
@@ -83,22 +86,17 @@ def cpu_baseline(g, t_kept_cu, n_rows_score=8192, n_attn_rows=96):
     tk = int(kc[-1])
     q, k, v = random_qkv(11, tk, wl.hq, wl.hkv, wl.dh)
     qd, kd, vd = bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v)
-    rows = np.unique(np.linspace(0, tk - 1, n_attn_rows).astype(np.int64))
     t0 = time.perf_counter()
-    O.ref_gated_attn(qd, kd, vd, kb, pos, kc, g["gain"], g["temp"], rows=rows)
-    t_att_s = time.perf_counter() - t0
-    keys_all = tk * (tk + 1) / 2.0
-    keys_s = float(np.sum(rows + 1))
-    t_attn = t_att_s * keys_all / keys_s
+    O.ref_gated_attn(qd, kd, vd, kb, pos, kc, g["gain"], g["temp"])
+    t_attn = time.perf_counter() - t0
     total = t_score + t_gate + t_attn
     del xk
     return {
         "value": T / total, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: score on {n_rows_score}/{T} rows (scaled x{T / n_rows_score:.0f}), "
-                   f"normalise+select+gather on all {T} tokens, gated attention on {rows.size} of "
-                   f"{tk} query rows x all 16 heads (scaled by keys visited); projection excluded"),
-        "seconds_extrapolated": {"score": t_score, "normalise_select_gather": t_gate,
-                                 "attention": t_attn},
+        "sample": (f"the whole step, not a sample: fp64 numpy oracle scores and normalises all {T} "
+                   f"tokens, selects, gathers, and runs the gated attention over all {tk} kept query "
+                   f"rows x {wl.hq} heads; Q/K/V projection excluded as on the GPU"),
+        "seconds": {"score": t_score, "normalise_select_gather": t_gate, "attention": t_attn},
         "host_cores_visible": len(os.sched_getaffinity(0)),
     }
 
@@ -113,8 +111,8 @@ def main():
     ap.add_argument("--kernels-only", action="store_true",
                     help="skip the CPU baseline and the full-context lane (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
-                    help="after timing, run 3 plain device copies of MB MiB (reference for "
-                         "hardware byte counters); not part of the metric")
+                    help="after timing, copy MB MiB 3 times with tg_gather and identity indices "
+                         "(reference for hardware byte counters); not part of the metric")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gated-prefill "
@@ -263,14 +261,18 @@ def main():
         del qf, kf, vf, of
 
     if args.calibrate_copy > 0:
-        n = args.calibrate_copy * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
+        # a plain copy of known size through tg_gather with identity indices:
+        # MB MiB read and MB MiB written per launch (counter calibration)
+        rows = args.calibrate_copy * (1 << 20) // 4096
+        src = torch.ones(rows, 2048, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
+        ident = torch.arange(rows, dtype=torch.int32, device=dev)
         for _ in range(3):
-            dst.copy_(src)
+            ops.gather(src, ident, out=dst)
         torch.cuda.synchronize()
-        log(f"calibration copies: 3 x {args.calibrate_copy} MiB read + written")
-        del src, dst
+        log(f"calibration copies: 3 x {args.calibrate_copy} MiB read + written by gather_vec16 "
+            f"({rows} rows of 4096 B)")
+        del src, dst, ident
 
     cpu = None
     if not args.no_cpu_baseline:
