@@ -12,10 +12,12 @@
 // if key == tau and fewer than `need` earlier tokens of the sequence tie at
 // tau (lower index wins).  The kept count of a sequence, min(K, |P|) + |N|,
 // is known from the prunable count alone, so sequence offsets need no scan
-// of the selection itself; chunk offsets come from a per-sequence scan of
-// per-chunk counts.  Tokens are written in ascending original index.
+// of the selection itself; a chunk's offset is the sum of the definite keeps
+// of the earlier chunks of its sequence plus min(need, their ties).  Tokens
+// are written in ascending original index.
 //
-// Launches: init, pass0, pass1, pass2, count, offsets, write.
+// Launches: init, pass0, pass1, pass2, count (+ kept_cu), write (each block
+// derives its chunk's offsets from the counts of the earlier chunks).
 #include "common.h"
 
 namespace tg {
@@ -43,8 +45,6 @@ struct SelWs {
   uint32_t* n_prunable;  // [n_seq]
   int32_t* blk_def;      // [n_slots] kept for sure (prompt, key > tau, or all)
   int32_t* blk_tie;      // [n_slots] prunable tokens with key == tau
-  int32_t* blk_tie_off;  // [n_slots] ties in earlier chunks of the sequence
-  int32_t* blk_off;      // [n_slots] kept tokens in earlier chunks of the sequence
 };
 
 int64_t n_slots_of(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 1) / CH; }
@@ -62,10 +62,6 @@ SelWs carve(void* ws, int64_t t_in, int n_seq) {
   w.blk_def = reinterpret_cast<int32_t*>(p);
   p += sizeof(int32_t) * ns;
   w.blk_tie = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * ns;
-  w.blk_tie_off = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * ns;
-  w.blk_off = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -215,8 +211,29 @@ __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
                                                const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ kbud, int n_seq,
-                                               int64_t t_in, SelWs w) {
+                                               int64_t t_in, SelWs w,
+                                               int32_t* __restrict__ kept_cu) {
   __shared__ int sh[NT / 64 + 2];
+  if (blockIdx.x == 0) {
+    // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|
+    int acc = 0;
+    for (int base = 0; base < n_seq; base += NT) {
+      const int i = base + threadIdx.x;
+      int v = 0;
+      if (i < n_seq) {
+        int64_t lo, hi;
+        seq_range(cu, i, t_in, lo, hi);
+        const int npr = (int)w.n_prunable[i];
+        const int kb = kbud[i] > 0 ? kbud[i] : 0;
+        v = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
+      }
+      int tot;
+      const int ex = block_excl_scan<NT>(v, sh, &tot);
+      if (i < n_seq) kept_cu[i] = acc + ex;
+      acc += tot;
+    }
+    if (threadIdx.x == 0) kept_cu[n_seq] = acc;
+  }
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
   const Sel st = sel_stage(w, kbud, c.s, n_seq, 3, c.begin == c.lo, sh);
@@ -243,64 +260,6 @@ __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
   }
 }
 
-// One block per sequence: offsets of its chunks (ties first, then kept
-// tokens, both in chunk order) and the sequence's offset in the output.
-__global__ __launch_bounds__(NT) void sel_offsets(const int32_t* __restrict__ cu,
-                                                 const int32_t* __restrict__ kbud, int n_seq,
-                                                 int64_t t_in, SelWs w,
-                                                 int32_t* __restrict__ kept_cu) {
-  __shared__ int sh[NT / 64 + 2];
-  const int s = blockIdx.x;
-  // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|
-  int acc = 0;
-  for (int base = 0; base < s; base += NT) {
-    const int i = base + threadIdx.x;
-    int v = 0;
-    if (i < s) {
-      int64_t lo, hi;
-      seq_range(cu, i, t_in, lo, hi);
-      const int npr = (int)w.n_prunable[i];
-      const int kb = kbud[i] > 0 ? kbud[i] : 0;
-      v = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
-    }
-    int tot;
-    block_excl_scan<NT>(v, sh, &tot);
-    acc += tot;
-  }
-  int64_t lo, hi;
-  seq_range(cu, s, t_in, lo, hi);
-  const int npr = (int)w.n_prunable[s];
-  const int kb = kbud[s] > 0 ? kbud[s] : 0;
-  const int mine = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
-  if (threadIdx.x == 0) {
-    kept_cu[s] = acc;
-    if (s == n_seq - 1) kept_cu[n_seq] = acc + mine;
-  }
-  if (hi <= lo) return;
-  const Sel st = w.stage[2 * (size_t)n_seq + s];
-  const uint32_t need = st.mode == MODE_RADIX ? st.need : 0u;
-  const int nch = (int)((hi - lo + CH - 1) / CH);
-  const int64_t s0 = slot0_of(cu, s, CH);
-  int tie_run = 0, off_run = 0;
-  for (int base = 0; base < nch; base += NT) {
-    const int i = base + threadIdx.x;
-    const int t = i < nch ? w.blk_tie[s0 + i] : 0;
-    const int d = i < nch ? w.blk_def[s0 + i] : 0;
-    int tt;
-    const int tie_off = tie_run + block_excl_scan<NT>(t, sh, &tt);
-    int take = (int)need - tie_off;
-    take = take < 0 ? 0 : (take > t ? t : take);
-    int to;
-    const int off = off_run + block_excl_scan<NT>(d + take, sh, &to);
-    if (i < nch) {
-      w.blk_tie_off[s0 + i] = tie_off;
-      w.blk_off[s0 + i] = off;
-    }
-    tie_run += tt;
-    off_run += to;
-  }
-}
-
 __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
                                                const int32_t* __restrict__ cu,
@@ -315,8 +274,21 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
   if (!locate(cu, n_seq, t_in, c)) return;
   const Sel st = w.stage[2 * (size_t)n_seq + c.s];
   const int need = st.mode == MODE_RADIX ? (int)st.need : 0;
-  const int tie_base = w.blk_tie_off[c.slot];
-  const int64_t out_base = (int64_t)kept_cu[c.s] + w.blk_off[c.slot];
+  // offsets of this chunk inside its sequence from the counts of the earlier
+  // chunks: ties are taken greedily in chunk order, so the earlier chunks
+  // took min(need, their ties) tied tokens in total
+  const int64_t s0 = slot0_of(cu, c.s, CH);
+  const int ci = (int)(c.slot - s0);
+  int dsum = 0, tsum = 0;
+  for (int i = threadIdx.x; i < ci; i += NT) {
+    dsum += w.blk_def[s0 + i];
+    tsum += w.blk_tie[s0 + i];
+  }
+  int tot_d, tot_t;
+  block_excl_scan<NT>(dsum, sh, &tot_d);
+  block_excl_scan<NT>(tsum, sh, &tot_t);
+  const int tie_base = tot_t;
+  const int64_t out_base = (int64_t)kept_cu[c.s] + tot_d + (tot_t < need ? tot_t : need);
   // contiguous tokens per thread, so thread order is index order
   const int64_t j0 = c.begin + (int64_t)threadIdx.x * PER;
   float bv[PER];
@@ -371,7 +343,7 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
 size_t select_ws_bytes(int64_t t_in, int n_seq) {
   const int64_t ns = n_slots_of(t_in, n_seq);
   size_t bytes = sizeof(Sel) * 3 * (size_t)n_seq + sizeof(uint32_t) * (size_t)n_seq * HIST_WORDS +
-                 sizeof(uint32_t) * (size_t)n_seq + 4 * sizeof(int32_t) * (size_t)ns;
+                 sizeof(uint32_t) * (size_t)n_seq + 2 * sizeof(int32_t) * (size_t)ns;
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -389,10 +361,10 @@ hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t*
     hipLaunchKernelGGL(sel_pass<0>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
     hipLaunchKernelGGL(sel_pass<1>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
     hipLaunchKernelGGL(sel_pass<2>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-    hipLaunchKernelGGL(sel_count, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
   }
-  hipLaunchKernelGGL(sel_offsets, dim3((unsigned)n_seq), dim3(NT), 0, st, cu, k, n_seq, t_in, w,
-                     kept_cu);
+  // every sequence's kept_cu entry is written by block 0 even when t_in == 0
+  hipLaunchKernelGGL(sel_count, dim3((unsigned)(ns > 0 ? ns : 1)), dim3(NT), 0, st, b, prunable, cu,
+                     k, n_seq, t_in, w, kept_cu);
   if (t_in > 0)
     hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w,
                        kept_cu, cap, kept_idx, kept_pos, kept_b);
