@@ -165,12 +165,11 @@ def main():
         ops.select_topk(b, pr, cu, kdev, t_kept, kept_idx, kept_pos, kept_b, kept_cu, ws_k)
         ops.gather(x, kept_idx, out=x_kept)
 
-    # projection of the kept rows: outside the timed step (not one of the four calls)
+    # projection of the kept rows with tg_qkv_proj: outside the timed step (not
+    # one of the four calls of the metric); timed on its own further below
     gate()
-    wq, wk, wv = tb(g["wq"]), tb(g["wk"]), tb(g["wv"])
-    q = (x_kept @ wq).view(t_kept, wl.hq, wl.dh).contiguous()
-    k = (x_kept @ wk).view(t_kept, wl.hkv, wl.dh).contiguous()
-    v = (x_kept @ wv).view(t_kept, wl.hkv, wl.dh).contiguous()
+    w_all = tb(np.ascontiguousarray(np.concatenate([g["wq"].T, g["wk"].T, g["wv"].T], axis=0)))
+    q, k, v = ops.qkv_proj(x_kept, w_all, wl.hq, wl.hkv, wl.dh)
     o = torch.empty_like(q)
     torch.cuda.synchronize()
     assert int(kept_cu[-1].item()) == t_kept
@@ -232,6 +231,28 @@ def main():
                 "frac": round(ach / peak, 4), "traffic": traffic_for(dom, srcs),
                 "kernel": "gated_attn_bf16" if dom == "attn" else "score_mlp_bf16",
                 "avg_launch_us": round(avg[dom], 2)}
+
+    # the projection of the kept rows (tg_qkv_proj), beside the step: our
+    # kernel and the torch (hipBLASLt) GEMMs on the same operands
+    def time_it(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3      # us
+    proj_flops = 2.0 * t_kept * wl.d * (wl.hq + 2 * wl.hkv) * wl.dh
+    wq_t, wk_t, wv_t = tb(g["wq"]), tb(g["wk"]), tb(g["wv"])
+    t_proj = time_it(lambda: ops.qkv_proj(x_kept, w_all, wl.hq, wl.hkv, wl.dh, q=q, k=k, v=v))
+    t_proj_torch = time_it(lambda: (x_kept @ wq_t, x_kept @ wk_t, x_kept @ wv_t))
+    proj = {"kernel": "tg_qkv_proj", "us": round(t_proj, 2),
+            "tflops": round(proj_flops / (t_proj * 1e-6) / 1e12, 1),
+            "torch_matmul_us": round(t_proj_torch, 2),
+            "note": "not part of the step: Q/K/V of the kept rows, 8704 x 2048 -> 2048+1024+1024"}
+    del wq_t, wk_t, wv_t
 
     full = None
     if not args.no_full_context:
@@ -298,6 +319,7 @@ def main():
         "gate_gbs": round(gate_gbs, 1),
         "gate_frac_of_hbm_peak": round(gate_gbs / PEAK_HBM_GBS, 4),
         "full_context": full,
+        "qkv_proj": proj,
     }
     print(json.dumps(out), flush=True)
 

@@ -6,6 +6,7 @@
  *   tg_select_topk  top-K of the prunable tokens, prompt tokens always kept
  *   tg_gather       compaction of the kept rows
  *   tg_gated_attn   token-gated causal attention over the kept tokens
+ * and, between the last two, tg_qkv_proj, the projections of the kept rows.
  * Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
  * with Learned Token Pruning", §4.1 (Eq. 3-4) and §4.2 (Eq. 5-8).
  *
@@ -175,6 +176,30 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
                         int32_t max_kept_seqlen, int32_t hq, int32_t hkv, int32_t dh,
                         const float* gain, const float* temp, float sm_scale,
                         tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_qkv_proj -- query, key and value projections of the kept rows: the
+ * step between tg_gather and tg_gated_attn (§4.1: the kept tokens continue
+ * through the layers above the gate; §4.2 Eq. 8 reads q, k, v of the kept
+ * tokens only).  One GEMM over the concatenated weight:
+ *
+ *   q[r, h, e] = sum_c x[r, c] * w[h * dh + e, c]                 (h < hq)
+ *   k[r, h, e] = sum_c x[r, c] * w[(hq + h) * dh + e, c]          (h < hkv)
+ *   v[r, h, e] = sum_c x[r, c] * w[(hq + hkv + h) * dh + e, c]    (h < hkv)
+ *
+ * with fp32 accumulation and the result rounded to bf16 (nearest even).
+ * x  dev [t, d] bf16 (normally tg_gather's output), row r at
+ *    x + r * x_row_stride elements.
+ * w  dev [(hq + 2 hkv) * dh, d] bf16: the rows of Wq, then Wk, then Wv, one
+ *    row per output feature (the nn.Linear weight layout).
+ * q  dev [t, hq, dh] bf16 out;  k, v dev [t, hkv, dh] bf16 out.
+ * Supported: dt = TG_BF16, d % 64 == 0, dh % 32 == 0,
+ * (hq + 2 hkv) * dh % 256 == 0, x_row_stride % 8 == 0 and < 2^22,
+ * 16-byte aligned x and w.  No rotary embedding or q/k norm is applied.
+ * ---------------------------------------------------------------------- */
+tg_status tg_qkv_proj(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t, int32_t d,
+                      const void* w, int32_t hq, int32_t hkv, int32_t dh, void* q, void* k,
+                      void* v, tg_stream stream);
 
 #ifdef __cplusplus
 }

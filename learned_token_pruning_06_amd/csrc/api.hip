@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10000; }
+int tg_version(void) { return 10100; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -152,6 +152,30 @@ tg_status tg_gather(const void* src, int64_t src_stride, int64_t n_src, int64_t 
   hipError_t e = tg::launch_gather(src, src_stride, n_src, row_bytes, idx, n_rows, dst, dst_stride,
                                    (hipStream_t)stream);
   return from_hip(e, "tg_gather launch");
+}
+
+// ------------------------------------------------------------ projection
+tg_status tg_qkv_proj(const void* x, tg_dtype dt, int64_t xs, int64_t t, int32_t d, const void* w,
+                      int32_t hq, int32_t hkv, int32_t dh, void* q, void* k, void* v,
+                      tg_stream stream) {
+  if (t < 0 || d < 1 || hq < 1 || hkv < 1 || dh < 1 || xs < d)
+    return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj: bad sizes");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj: bad dtype");
+  if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj: only bf16 is implemented");
+  const int64_t n_tot = (int64_t)(hq + 2 * (int64_t)hkv) * dh;
+  if (d % 64 != 0 || dh % 32 != 0 || n_tot % 256 != 0 || n_tot > INT32_MAX)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_qkv_proj: need d %% 64 == 0, dh %% 32 == 0, (hq + 2 hkv) * dh %% 256 == 0");
+  if (xs % 8 != 0 || xs >= ((int64_t)1 << 22) || (int64_t)d * 256 * 2 > INT32_MAX)
+    return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj: row stride must be a multiple of 8, < 2^22");
+  if (t > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj: too many rows");
+  if (t == 0) return ok();
+  if (!x || !w || !q || !k || !v) return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj: null pointer");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 8) || !aligned(k, 8) || !aligned(v, 8))
+    return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj: x, w 16-byte and q, k, v 8-byte aligned");
+  hipError_t e = tg::launch_qkv_proj(x, xs, t, d, w, hq * dh, hkv * dh, q, k, v,
+                                     (hipStream_t)stream);
+  return from_hip(e, "tg_qkv_proj launch");
 }
 
 // ------------------------------------------------------------- attention

@@ -138,6 +138,9 @@ hipError_t launch_gather(const void* src, int64_t src_stride, int64_t n_src, int
                          const int32_t* idx, int64_t n_rows, void* dst, int64_t dst_stride,
                          hipStream_t st);
 
+hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d, const void* w,
+                           int nq, int nkv, void* q, void* k, void* v, hipStream_t st);
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                             const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,

@@ -1,0 +1,170 @@
+// tg_qkv_proj: the query, key and value projections of the kept rows,
+//   Q = X_S Wq^T,  K = X_S Wk^T,  V = X_S Wv^T,
+// i.e. the step between the gather and the token-gated attention (TokenGate
+// §4.1: the kept tokens continue through the layers above the gate, whose
+// attention §4.2 Eq. 8 reads q, k and v of the kept tokens only).
+//
+// One bf16 GEMM  Y[t, n] = sum_d X[t, d] W[n, d]  over the concatenated
+// weight W = [Wq; Wk; Wv] ([n_tot, d], one row per output feature, the
+// nn.Linear layout), on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// The output columns are routed to q, k or v in the epilogue.
+//
+// A workgroup owns a 256-row x 256-column output tile; 8 waves (two per
+// SIMD), wave w owns rows [64(w%4), +64) and columns [128(w/4), +128), i.e.
+// 2 x 4 accumulator tiles of 32 x 32 in C^T orientation (columns on the MFMA
+// M axis, rows on N), so each lane ends up holding four consecutive output
+// columns of one row.  Each 64-wide K-step stages the X and W slices in
+// double-buffered, padded LDS tiles (global -> registers one step ahead ->
+// LDS; one barrier per step).  Rows past t read zeros through the buffer
+// range and are not stored.
+#include "common.h"
+
+namespace tg {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 256;           // rows and columns per workgroup
+constexpr int kBK = 64;              // d per K-step
+constexpr int kRow = kBK + 8;        // bf16 per LDS row (144 B: rows start 4 banks apart)
+constexpr int kThreads = 512;
+
+TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+TG_DEVINL uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7fffffff ? (bytes > 0 ? bytes : 0)
+                                                                    : 0x7fffffff),
+                                           0x00020000);
+}
+
+__global__ __launch_bounds__(kThreads) void qkv_proj_bf16(
+    const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
+    const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
+    uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTile * kRow];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int rg = wv & 3, ch = wv >> 2;
+  const int64_t row0 = (int64_t)blockIdx.x * kTile;
+  const int col0 = blockIdx.y * kTile;
+
+  // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
+  // of the K-step, for both X (rows of this tile) and W (its output features)
+  const int lrow = tid >> 3, lch = tid & 7;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row0 * xs, (t - row0) * xs * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (int64_t)col0 * d, (int64_t)kTile * d * 2);
+  int xoff[4], woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
+    woff[i] = ((lrow + 64 * i) * d + 8 * lch) * 2;
+  }
+  const int ldst = lrow * kRow + 8 * lch;
+  u32x4 xr[4], wr[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + 2 * k0, 0, 0));
+      wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + 2 * k0, 0, 0));
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
+      st16(&sw[buf][ldst + 64 * i * kRow], wr[i]);
+    }
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[mt][0][r] = 0.f;
+      acc[mt][1][r] = 0.f;
+    }
+
+  const int nsteps = d / kBK;
+  fetch(0);
+  stage(0);
+  if (nsteps > 1) fetch(kBK);
+  __syncthreads();
+  for (int it = 0; it < nsteps; ++it) {
+    const int buf = it & 1;
+    const uint16_t* xb = sx[buf] + (64 * rg + n) * kRow + 32 * g;
+    const uint16_t* wb = sw[buf] + (128 * ch + n) * kRow + 32 * g;
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      const bf16x8 b0 = as_bf16x8(ld16(xb + 8 * s));
+      const bf16x8 b1 = as_bf16x8(ld16(xb + 32 * kRow + 8 * s));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = as_bf16x8(ld16(wb + 32 * mt * kRow + 8 * s));
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mt][1], 0, 0, 0);
+      }
+    }
+    if (it + 1 < nsteps) {
+      stage(buf ^ 1);
+      if (it + 2 < nsteps) fetch((it + 2) * kBK);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane (n, g) holds columns 32mt + 8(r/4) + 4g + r%4 of this
+  // wave's column range, row 32 nt + n of its row range
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int cbase = col0 + 128 * ch + 32 * mt;      // 32 columns, one destination (dh % 32 == 0)
+    uint16_t* dst;
+    int ld, c0;
+    if (cbase < nq) {
+      dst = q; ld = nq; c0 = cbase;
+    } else if (cbase < nq + nkv) {
+      dst = k; ld = nkv; c0 = cbase - nq;
+    } else {
+      dst = v; ld = nkv; c0 = cbase - nq - nkv;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t row = row0 + 64 * rg + 32 * nt + n;
+      if (row < t) {
+        uint16_t* p = dst + row * ld + c0 + 4 * g;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[mt][nt][4 * r4 + 0], acc[mt][nt][4 * r4 + 1]);
+          pk.y = pack_bf16x2(acc[mt][nt][4 * r4 + 2], acc[mt][nt][4 * r4 + 3]);
+          *reinterpret_cast<uint2*>(p + 8 * r4) = pk;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d, const void* w,
+                           int nq, int nkv, void* q, void* k, void* v, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  const int n_tot = nq + 2 * nkv;
+  const dim3 grid((unsigned)((t + kTile - 1) / kTile), (unsigned)(n_tot / kTile));
+  hipLaunchKernelGGL(qkv_proj_bf16, grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x), x_row_stride, t, d,
+                     static_cast<const uint16_t*>(w), nq, nkv, static_cast<uint16_t*>(q),
+                     static_cast<uint16_t*>(k), static_cast<uint16_t*>(v));
+  return hipGetLastError();
+}
+
+}  // namespace tg

@@ -149,6 +149,28 @@ def gather(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = N
 
 
 # ----------------------------------------------------------------- attention
+def qkv_proj(x: torch.Tensor, w: torch.Tensor, hq: int, hkv: int, dh: int,
+             q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+             v: Optional[torch.Tensor] = None):
+    """tg_qkv_proj: q [T,Hq,dh], k/v [T,Hkv,dh] from the kept rows x [T,d] and the
+    concatenated weight w [(Hq+2Hkv)*dh, d] (rows of Wq, then Wk, then Wv)."""
+    lib = load()
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    t, d = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty(t, hq, dh, dtype=x.dtype, device=dev)
+    if k is None:
+        k = torch.empty(t, hkv, dh, dtype=x.dtype, device=dev)
+    if v is None:
+        v = torch.empty(t, hkv, dh, dtype=x.dtype, device=dev)
+    st = lib.tg_qkv_proj(_p(x), _DT[x.dtype], x.stride(0), t, d, _p(w), hq, hkv, dh, _p(q), _p(k),
+                         _p(v), _stream(dev))
+    check("tg_qkv_proj", st)
+    return q, k, v
+
+
 def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.Tensor,
                kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor, gain: torch.Tensor,
                temp: torch.Tensor, max_len: Optional[int] = None,

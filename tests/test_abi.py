@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10000
+    assert lib.tg_version() == 10100
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -159,3 +159,19 @@ def test_attn_validation(lib):
     assert at(gain=None) == 1
     assert at(q=ctypes.c_void_p(0x10008)) == 2
     assert at(t=0) == 0                                # empty: nothing launched
+
+
+def test_qkv_proj_validation(lib):
+    def pj(dt=1, xs=2048, t=100, d=2048, hq=16, hkv=8, dh=128, x=FAKE, q=FAKE):
+        return lib.tg_qkv_proj(x, dt, xs, t, d, FAKE, hq, hkv, dh, q, FAKE, FAKE, None)
+    assert pj(t=-1) == 1
+    assert pj(dt=3) == 1
+    assert pj(dt=0) == 2                               # fp32 projection not implemented
+    assert pj(xs=1000, d=2048) == 1                    # stride below the row length
+    assert pj(d=2000, xs=2048) == 2                    # d % 64 != 0
+    assert pj(dh=48) == 2                              # dh % 32 != 0
+    assert pj(hq=3, hkv=1, dh=64) == 2                 # 320 output features: not a multiple of 256
+    assert pj(xs=2052) == 2                            # stride not a multiple of 8
+    assert pj(x=None) == 1
+    assert pj(x=ctypes.c_void_p(0x10008)) == 2         # misaligned x
+    assert pj(t=0) == 0                                # empty: nothing launched

@@ -426,3 +426,38 @@ def test_gate_on_tiny_workload():
     # the kept document tokens are exactly the 128 best normalised scores
     order = np.argsort(-b[:960].astype(np.float32), kind="stable")
     assert set(order[:128]) == set(idx[:128])
+
+
+# ---------------------------------------------------------------------------
+# projection of the kept rows (the step between gather and attention)
+# ---------------------------------------------------------------------------
+def test_projection_identity_weights_return_the_rows():
+    rng = np.random.default_rng(31)
+    T, hq, hkv, dh = 5, 2, 1, 4
+    d = hq * dh
+    x = rng.standard_normal((T, d))
+    eye = np.eye(d)
+    q, k, v = O.ref_project(x, eye, eye[:, :hkv * dh], eye[:, hkv * dh:2 * hkv * dh], hq, hkv, dh)
+    assert np.array_equal(q.reshape(T, d), x)
+    assert np.array_equal(k.reshape(T, hkv * dh), x[:, :hkv * dh])
+    assert np.array_equal(v.reshape(T, hkv * dh), x[:, hkv * dh:])
+
+
+def test_projection_head_layout_and_linearity():
+    rng = np.random.default_rng(32)
+    T, d, hq, hkv, dh = 4, 6, 3, 1, 2
+    wq = rng.standard_normal((d, hq * dh))
+    wk = rng.standard_normal((d, hkv * dh))
+    wv = rng.standard_normal((d, hkv * dh))
+    x1, x2 = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    q1, k1, v1 = O.ref_project(x1, wq, wk, wv, hq, hkv, dh)
+    # head h, element e of row r is the dot product of row r with column h*dh+e
+    for r in range(T):
+        for h in range(hq):
+            for e in range(dh):
+                want = sum(x1[r, c] * wq[c, h * dh + e] for c in range(d))
+                assert abs(q1[r, h, e] - want) < 1e-12
+    q2, k2, v2 = O.ref_project(x2, wq, wk, wv, hq, hkv, dh)
+    q3, k3, v3 = O.ref_project(2.5 * x1 - x2, wq, wk, wv, hq, hkv, dh)
+    for a, b, c in ((q1, q2, q3), (k1, k2, k3), (v1, v2, v3)):
+        assert np.allclose(c, 2.5 * a - b, rtol=1e-12, atol=1e-12)
