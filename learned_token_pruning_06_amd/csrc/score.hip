@@ -39,10 +39,11 @@ TG_DEVINL float silu_f(float v) {
 
 // One workgroup = 256 rows x all h columns, 8 waves: wave w owns rows
 // [64(w%4), +64) and the h tiles [MTA(w/4), +MTA) (two waves per SIMD, 128
-// accumulators each).  x is read with coalesced 16-byte loads two K-steps
-// ahead into registers, then staged into a double-buffered LDS tile shared by
-// the two waves of a row group; the W1 slice of each K-step is shared by all
-// waves through a double-buffered LDS tile.  One barrier per K-step.
+// accumulators each).  Each 64-wide K-step of x and W1 is read with
+// coalesced 16-byte buffer loads (8 rows x 128 B per wave instruction) one
+// step ahead into registers, then staged into double-buffered, padded LDS
+// tiles shared by all waves; one barrier per K-step.  Rows past the end of x
+// (and hidden units past h) read zeros through the buffer ranges.
 template <int MT>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
@@ -50,35 +51,49 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     float b2, float* __restrict__ b_raw) {
   constexpr int H = 32 * MT;
   constexpr int MTA = (MT + 1) / 2;          // h tiles of the first half
-  constexpr int CPR = kBK / 8;               // 16-byte chunks per row slice (8)
-  constexpr int NV = H * CPR;                // W1 vectors per K-step
-  constexpr int VPT = (NV + kThreads - 1) / kThreads;
-  constexpr int RSTEP = kThreads / CPR;      // W1 rows between a thread's vectors (64)
+  constexpr int WV = (H + 63) / 64;          // W1 vectors per thread per K-step
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][H * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][4][64 * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kRowsPerWG * kRow];
   __shared__ float sred[4][64];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int rg = wv & 3, hh = wv >> 2;
   const int mt0 = hh * MTA;
   const int nmt = hh == 0 ? MTA : MT - MTA;  // h tiles of this wave (may be 0)
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + rg * 64;
+  const int64_t wg_row0 = (int64_t)blockIdx.x * kRowsPerWG;
+  const int64_t row0 = wg_row0 + rg * 64;
 
-  // x loader: this wave loads 4 of the 8 row blocks of its row group;
-  // block j covers rows 8j + lane/8, 16-byte chunk lane%8
-  int64_t xrow[4];
+  // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
+  const int lrow = tid >> 3, lch = tid & 7;
+  const int64_t xbytes = (t_in - wg_row0) * xs * 2;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + wg_row0 * xs), (short)0,
+      (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w1), (short)0, (int)((int64_t)H * d * 2), 0x00020000);
+  int xoff[4], woff[WV];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int j = 2 * jj + hh;
-    int64_t r = row0 + 8 * j + (lane >> 3);
-    xrow[jj] = (r < t_in ? r : t_in - 1) * xs + 8 * (lane & 7);
-  }
-  const int xdst = (lane >> 3) * kRow + 8 * (lane & 7);
-  // W1 loader: thread vector i -> row tid / CPR + i * RSTEP, chunk tid % CPR
-  const uint16_t* wsrc = w1 + (int64_t)(tid / CPR) * d + 8 * (tid % CPR);
-  const int wdst = (tid / CPR) * kRow + 8 * (tid % CPR);
+  for (int i = 0; i < 4; ++i) xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
+#pragma unroll
+  for (int i = 0; i < WV; ++i) woff[i] = ((lrow + 64 * i) * d + 8 * lch) * 2;
+  const int ldst = lrow * kRow + 8 * lch;
+  u32x4 xr[4], wr[WV];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + 2 * k0, 0, 0));
+#pragma unroll
+    for (int i = 0; i < WV; ++i)
+      wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + 2 * k0, 0, 0));
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
+#pragma unroll
+    for (int i = 0; i < WV; ++i)
+      if (lrow + 64 * i < H) st16(&sw[buf][ldst + 64 * i * kRow], wr[i]);
+  };
 
   floatx16 acc[MTA][2];
 #pragma unroll
@@ -90,61 +105,30 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     }
 
   const int nk = d / kBK;
-  u32x4 xa[4], xb[4];          // x of K-steps it+1 (xa) and it+2 (xb), clamped at the end
-  u32x4 wreg[VPT];
-  // prologue: W1 slice 0 and x step 0 to LDS, x steps 1 and 2 to registers
-#pragma unroll
-  for (int i = 0; i < VPT; ++i)
-    if (i * kThreads + tid < NV) wreg[i] = ld16(wsrc + (int64_t)i * RSTEP * d);
-#pragma unroll
-  for (int i = 0; i < VPT; ++i)
-    if (i * kThreads + tid < NV) st16(&sw[0][wdst + i * RSTEP * kRow], wreg[i]);
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    st16(&sx[0][rg][xdst + 8 * (2 * jj + hh) * kRow], ld_nt16(x + xrow[jj]));
-  {
-    const int k1 = (nk > 1 ? 1 : 0) * kBK, k2 = (nk > 2 ? 2 : nk - 1) * kBK;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      xa[jj] = ld_nt16(x + xrow[jj] + k1);
-      xb[jj] = ld_nt16(x + xrow[jj] + k2);
-    }
-  }
+  fetch(0);
+  stage(0);
+  if (nk > 1) fetch(kBK);
   __syncthreads();
-
   for (int it = 0; it < nk; ++it) {
     const int buf = it & 1;
-    // next W1 slice (the last step re-reads its own: no branch, buffer unused)
-    const int kw = (it + 1 < nk ? it + 1 : it) * kBK;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (i * kThreads + tid < NV) wreg[i] = ld16(wsrc + (int64_t)i * RSTEP * d + kw);
-    const uint16_t* swb = sw[buf];
-    const uint16_t* sxw = sx[buf][rg];
+    const uint16_t* xb = sx[buf] + (64 * rg + n) * kRow + 32 * g;
+    const uint16_t* wb = sw[buf] + (32 * mt0 + n) * kRow + 32 * g;
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const bf16x8 bop0 = as_bf16x8(ld16(&sxw[n * kRow + 32 * g + 8 * s]));
-      const bf16x8 bop1 = as_bf16x8(ld16(&sxw[(32 + n) * kRow + 32 * g + 8 * s]));
+      const bf16x8 bop0 = as_bf16x8(ld16(xb + 8 * s));
+      const bf16x8 bop1 = as_bf16x8(ld16(xb + 32 * kRow + 8 * s));
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) {
         if (mt < nmt) {
-          const bf16x8 aop =
-              as_bf16x8(ld16(&swb[(32 * (mt0 + mt) + n) * kRow + 32 * g + 8 * s]));
+          const bf16x8 aop = as_bf16x8(ld16(wb + 32 * mt * kRow + 8 * s));
           acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop0, acc[mt][0], 0, 0, 0);
           acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop1, acc[mt][1], 0, 0, 0);
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (i * kThreads + tid < NV) st16(&sw[buf ^ 1][wdst + i * RSTEP * kRow], wreg[i]);
-    // x of step it+1 into the other LDS tile, rotate the ring, fetch step it+3
-    const int k3 = (it + 3 < nk ? it + 3 : nk - 1) * kBK;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      st16(&sx[buf ^ 1][rg][xdst + 8 * (2 * jj + hh) * kRow], xa[jj]);
-      xa[jj] = xb[jj];
-      xb[jj] = ld_nt16(x + xrow[jj] + k3);
+    if (it + 1 < nk) {
+      stage(buf ^ 1);
+      if (it + 2 < nk) fetch((it + 2) * kBK);
     }
     __syncthreads();
   }
