@@ -254,6 +254,39 @@ def main():
             "note": "not part of the step: Q/K/V of the kept rows, 8704 x 2048 -> 2048+1024+1024"}
     del wq_t, wk_t, wv_t
 
+    # one decode step after the prefill (tg_gated_decode): the new token's
+    # query against the pruned cache of this layer (the kept rows' K/V plus
+    # the token itself).  The calls are replayed from a HIP graph so that the
+    # time is the GPU's, not the host's launch rate.
+    def decode_lane(kc, vc, cb, qpos, reps):
+        n = kc.shape[0]
+        qd = q[-1:].contiguous()
+        od = torch.empty_like(qd)
+        cud = torch.tensor([0, n], dtype=torch.int32, device=dev)
+        wsd = ops.workspace(lib.tg_gated_decode_workspace_size(1, wl.hq, wl.hkv, wl.dh, n), dev)
+        call = lambda: ops.gated_decode(qd, kc, vc, cb, qpos, cud, gain, temp, max_cache_len=n,
+                                        out=od, ws=wsd)
+        call()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(reps):
+                call()
+        gr.replay()
+        torch.cuda.synchronize()
+        t_us = time_it(gr.replay, reps=5) / reps
+        nbytes = 2.0 * n * wl.hkv * wl.dh * 2 + n * 4 + 2 * wl.hq * wl.dh * 2
+        return {"cache_rows": n, "us": round(t_us, 2), "gbs": round(nbytes / (t_us * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    kc = torch.cat([k, k[-1:]]).contiguous()
+    vc = torch.cat([v, v[-1:]]).contiguous()
+    cbd = torch.cat([kept_b, torch.zeros(1, dtype=torch.float32, device=dev)])
+    qpos = torch.tensor([T], dtype=torch.int32, device=dev)
+    decode = {"kernel": "tg_gated_decode", "pruned_cache": decode_lane(kc, vc, cbd, qpos, 50),
+              "note": "1 sequence, the new token against the kept rows + itself; "
+                      "graph replay of 50 steps, 2 launches each"}
+    del kc, vc
+
     full = None
     if not args.no_full_context:
         # unpruned reference point: all 131072 tokens kept (stand-in Q/K/V)
@@ -274,6 +307,8 @@ def main():
         torch.cuda.synchronize()
         t_full = e0.elapsed_time(e1) / reps * 1e-3
         fl = 2.0 * wl.dh * wl.hq * T * (T + 1)
+        # decode over the unpruned cache (the same 131072 rows, the last one new)
+        decode["full_cache"] = decode_lane(kf, vf, bf_, qpos, 10)
         full = {"attn_ms": round(t_full * 1e3, 3), "attn_tflops": round(fl / t_full / 1e12, 1),
                 "attn_frac_of_peak": round(fl / t_full / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "tokens_per_s_gate_plus_attn": round(
@@ -320,6 +355,7 @@ def main():
         "gate_frac_of_hbm_peak": round(gate_gbs / PEAK_HBM_GBS, 4),
         "full_context": full,
         "qkv_proj": proj,
+        "decode": decode,
     }
     print(json.dumps(out), flush=True)
 

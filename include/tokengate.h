@@ -6,7 +6,8 @@
  *   tg_select_topk  top-K of the prunable tokens, prompt tokens always kept
  *   tg_gather       compaction of the kept rows
  *   tg_gated_attn   token-gated causal attention over the kept tokens
- * and, between the last two, tg_qkv_proj, the projections of the kept rows.
+ * and, between the last two, tg_qkv_proj, the projections of the kept rows;
+ * tg_gated_decode runs one decode step over the pruned caches afterwards.
  * Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
  * with Learned Token Pruning", §4.1 (Eq. 3-4) and §4.2 (Eq. 5-8).
  *
@@ -200,6 +201,49 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
 tg_status tg_qkv_proj(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t, int32_t d,
                       const void* w, int32_t hq, int32_t hkv, int32_t dh, void* q, void* k,
                       void* v, tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_gated_decode -- one decode step of token-gated attention over pruned KV
+ * caches: a decode step attends to the cache and appends to it (§3, "Prefill,
+ * decode, and the KV cache"); above the gate the cache holds only the kept
+ * tokens (§4.1), and generated tokens are never pruned.  One new query token
+ * per sequence, its own key and value already appended as the sequence's
+ * last cache row:
+ *
+ *   logit_j^h = tau^h * (s * q^h . k_j + gain_h * b_j),   j over the cache
+ *   tau^h     = temp_h * log(m) / log(max(2, p))           (Eq. 7)
+ *   out^h     = sum_j softmax_j(logit^h) v_j               (Eq. 8)
+ *
+ * m = the sequence's cache length, p = q_pos + 1: the result equals the last
+ * query row of tg_gated_attn over the same rows.  Pruning the cache of a
+ * layer to the kept tokens is tg_gather over its [rows, hkv * dh] K and V.
+ *
+ * q        dev [n_seq, hq, dh] bf16, the new token of each sequence.
+ * k_cache, v_cache dev [t_cache, hkv, dh] bf16, sequences back to back.
+ * out      dev [n_seq, hq, dh] bf16 (accumulation in f32).
+ * cache_b  dev [t_cache] f32 scores of the cached tokens (0 on prompt and
+ *          generated tokens), or NULL for all zero.
+ * q_pos    dev [n_seq] i32 original 0-based position of the new token in its
+ *          sequence, or NULL: then the length factor is 1 (tau = temp).
+ * cache_cu_seqlens dev [n_seq + 1] i32, non-decreasing, last <= t_cache.  An
+ *          empty sequence gives zeros.
+ * max_cache_len: host value that sizes the key split (and the workspace);
+ *          any value is correct, the longest sequence's length is fastest.
+ * gain, temp dev [hq] f32, as for tg_gated_attn.  sm_scale: s; <= 0 selects
+ *          1/sqrt(dh).
+ * ws       dev workspace of >= tg_gated_decode_workspace_size(n_seq, hq, hkv,
+ *          dh, max_cache_len) bytes, 4-byte aligned.
+ * Supported: dt = TG_BF16, dh in {64, 128}, hq/hkv in {1, 2, 4, 8},
+ * t_cache < 2^31, n_seq <= 65535, 16-byte aligned q and caches.
+ * ---------------------------------------------------------------------- */
+size_t tg_gated_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t dh,
+                                      int64_t max_cache_len);
+tg_status tg_gated_decode(const void* q, const void* k_cache, const void* v_cache, tg_dtype dt,
+                          void* out, int64_t t_cache, const float* cache_b,
+                          const int32_t* q_pos, const int32_t* cache_cu_seqlens, int32_t n_seq,
+                          int64_t max_cache_len, int32_t hq, int32_t hkv, int32_t dh,
+                          const float* gain, const float* temp, float sm_scale, void* ws,
+                          size_t ws_bytes, tg_stream stream);
 
 #ifdef __cplusplus
 }

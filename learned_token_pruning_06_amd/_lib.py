@@ -37,6 +37,10 @@ PROTOTYPES = {
     "tg_gated_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp, c_vp,
                                      c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
                                      c_vp]),
+    "tg_gated_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i64]),
+    "tg_gated_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp, c_vp,
+                                       c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                       c_f32, c_vp, c_sz, c_vp]),
 }
 
 _lock = threading.Lock()

@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10100; }
+int tg_version(void) { return 10200; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -208,6 +208,48 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
     e = tg::launch_attn_f32(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
                             hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
   return from_hip(e, "tg_gated_attn launch");
+}
+
+// ----------------------------------------------------------------- decode
+size_t tg_gated_decode_workspace_size(int32_t n_seq, int32_t hq, int32_t hkv, int32_t dh,
+                                      int64_t max_cache_len) {
+  if (n_seq < 1 || hq < 1 || hkv < 1 || dh < 1 || max_cache_len < 0) return 0;
+  return tg::decode_ws_bytes(n_seq, hq, hkv, dh, max_cache_len);
+}
+
+tg_status tg_gated_decode(const void* q, const void* k_cache, const void* v_cache, tg_dtype dt,
+                          void* out, int64_t t_cache, const float* cache_b,
+                          const int32_t* q_pos, const int32_t* cache_cu, int32_t n_seq,
+                          int64_t max_cache_len, int32_t hq, int32_t hkv, int32_t dh,
+                          const float* gain, const float* temp, float sm_scale, void* ws,
+                          size_t ws_bytes, tg_stream stream) {
+  if (t_cache < 0 || n_seq < 1 || max_cache_len < 0 || hq < 1 || hkv < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_decode: bad sizes");
+  if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_decode: hq %% hkv != 0");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_gated_decode: bad dtype");
+  if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: only bf16 is implemented");
+  if (dh != 64 && dh != 128)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: dh must be 64 or 128");
+  const int g = hq / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: hq/hkv must be 1, 2, 4 or 8");
+  if (t_cache > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: t_cache too large");
+  if (n_seq > 65535) return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: more than 65535 sequences");
+  if ((int64_t)hkv * dh > (1 << 20))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: hkv * dh too large");
+  if (!q || !k_cache || !v_cache || !out || !cache_cu || !gain || !temp)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_decode: null pointer");
+  if (!ws) return fail(TG_ERR_INVALID_ARG, "tg_gated_decode: null workspace");
+  const size_t need = tg::decode_ws_bytes(n_seq, hq, hkv, dh, max_cache_len);
+  if (ws_bytes < need)
+    return fail(TG_ERR_WORKSPACE, "tg_gated_decode: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 2) ||
+      !aligned(ws, 4))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: q, k_cache, v_cache must be 16-byte aligned");
+  hipError_t e = tg::launch_decode(q, k_cache, v_cache, out, cache_b, cache_cu, q_pos, n_seq,
+                                   t_cache, max_cache_len, hq, hkv, dh, gain, temp, sm_scale, ws,
+                                   (hipStream_t)stream);
+  return from_hip(e, "tg_gated_decode launch");
 }
 
 }  // extern "C"

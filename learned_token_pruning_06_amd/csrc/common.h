@@ -141,6 +141,13 @@ hipError_t launch_gather(const void* src, int64_t src_stride, int64_t n_src, int
 hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d, const void* w,
                            int nq, int nkv, void* q, void* k, void* v, hipStream_t st);
 
+size_t decode_ws_bytes(int n_seq, int hq, int hkv, int dh, int64_t max_len);
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
+                         const float* cache_b, const int32_t* cache_cu, const int32_t* q_pos,
+                         int n_seq, int64_t t_cache, int64_t max_len, int hq, int hkv, int dh,
+                         const float* gain, const float* temp, float sm_scale, void* ws,
+                         hipStream_t st);
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                             const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,

@@ -198,6 +198,40 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
     return out
 
 
+def gated_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 cache_b: Optional[torch.Tensor], q_pos: Optional[torch.Tensor],
+                 cache_cu: torch.Tensor, gain: torch.Tensor, temp: torch.Tensor,
+                 max_cache_len: Optional[int] = None, sm_scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """tg_gated_decode: one new token per sequence, q [n_seq,Hq,dh], against
+    the caches k/v [T,Hkv,dh] whose last row per sequence is that token."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 3)
+    _need(v_cache, "v_cache", torch.bfloat16, 3)
+    _need(cache_cu, "cache_cu", torch.int32, 1)
+    _need(gain, "gain", torch.float32, 1)
+    _need(temp, "temp", torch.float32, 1)
+    if cache_b is not None:
+        _need(cache_b, "cache_b", torch.float32, 1)
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, 1)
+    n_seq, hq, dh = q.shape
+    t, hkv = k_cache.shape[0], k_cache.shape[1]
+    mx = int(max_cache_len if max_cache_len is not None else t)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = lib.tg_gated_decode_workspace_size(n_seq, hq, hkv, dh, mx)
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    st = lib.tg_gated_decode(_p(q), _p(k_cache), _p(v_cache), _DT[q.dtype], _p(out), t,
+                             _p(cache_b), _p(q_pos), _p(cache_cu), n_seq, mx, hq, hkv, dh,
+                             _p(gain), _p(temp), float(sm_scale or 0.0), _p(ws),
+                             ws.numel() * ws.element_size(), _stream(q.device))
+    check("tg_gated_decode", st)
+    return out
+
+
 # ------------------------------------------------------------------ pipeline
 def gate_prefill(x, w1, w2, prunable, cu_seqlens, k, cu_seqlens_host, n_prunable_host, k_host,
                  b1=None, b2: float = 0.0, eps: float = 1e-6):

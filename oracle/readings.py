@@ -23,6 +23,10 @@ R12 K counts prunable tokens; K >= |P| keeps all of P; K = 0 keeps only the
 R13 prompt tokens carry b = 0 and take part in every softmax.
 R14 kept tokens are emitted in ascending original index per sequence.
 R20 selection runs on the normalised scores rounded to fp32.
+R21 a decode step over a (pruned) cache is the last query row of the prefill
+    attention over the cache rows, with the new token's key and value
+    appended as the last row: m = cache length, p = its original position + 1,
+    and generated tokens carry b = 0 like prompt tokens (neither is pruned).
 EPS is PARITY UNPINNED (a choice, passed explicitly to both sides).
 """
 EPS = 1e-6

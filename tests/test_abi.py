@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10100
+    assert lib.tg_version() == 10200
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -175,3 +175,31 @@ def test_qkv_proj_validation(lib):
     assert pj(x=None) == 1
     assert pj(x=ctypes.c_void_p(0x10008)) == 2         # misaligned x
     assert pj(t=0) == 0                                # empty: nothing launched
+
+
+def test_gated_decode_validation(lib):
+    ws_size = lib.tg_gated_decode_workspace_size
+    # one record of (m, l, o[dh]) f32 per (sequence, query head, key chunk)
+    assert ws_size(1, 16, 8, 128, 8705) == 1 * 16 * 35 * 130 * 4
+    assert ws_size(64, 16, 8, 128, 3000) == 64 * 16 * 1 * 130 * 4   # chunks capped by the grid
+    assert ws_size(1, 16, 8, 128, 0) == 16 * 130 * 4
+    assert ws_size(0, 16, 8, 128, 10) == 0
+
+    def dc(dt=1, t=100, n_seq=1, mx=100, hq=16, hkv=8, dh=128, q=FAKE, ws=FAKE,
+           ws_bytes=1 << 20, gain=FAKE):
+        return lib.tg_gated_decode(q, FAKE, FAKE, dt, FAKE, t, None, None, FAKE, n_seq, mx, hq,
+                                   hkv, dh, gain, FAKE, 0.0, ws, ws_bytes, None)
+    assert dc(t=-1) == 1
+    assert dc(n_seq=0) == 1
+    assert dc(mx=-1) == 1
+    assert dc(hq=16, hkv=6) == 1
+    assert dc(dt=3) == 1
+    assert dc(dt=0) == 2                               # fp32 decode not implemented
+    assert dc(dh=96) == 2
+    assert dc(hq=16, hkv=1) == 2                       # 16 query heads per KV head
+    assert dc(gain=None) == 1
+    assert dc(ws=None) == 1
+    assert dc(ws_bytes=100) == 3                       # short workspace
+    assert dc(q=ctypes.c_void_p(0x10008)) == 2         # misaligned q
+    assert dc(n_seq=70000, ws_bytes=1 << 40) == 2
+
