@@ -5,7 +5,7 @@ the benchmark's CPU-baseline leg, never by the product path.  It shares no
 code with the HIP library under ``learned_token_pruning_06_amd``.
 """
 from . import readings
-from .ref import (silu, ref_score, ref_normalise, rank_order, ref_select, ref_kept_sizes,
+from .ref import (silu, ref_score, ref_rmsnorm, ref_score_prenorm, ref_normalise, rank_order, ref_select, ref_kept_sizes,
                   ref_gather, length_factor, ref_gated_attn, ref_gated_attn_masked,
                   ref_gated_attn_multiplicative, ref_gated_attn_loggate,
                   ref_gated_attn_bruteforce, ref_project, ref_gate)

@@ -27,6 +27,9 @@ R21 a decode step over a (pruned) cache is the last query row of the prefill
     attention over the cache rows, with the new token's key and value
     appended as the last row: m = cache length, p = its original position + 1,
     and generated tokens carry b = 0 like prompt tokens (neither is pruned).
+R22 LN2 (named, not defined, in §3 Eq. 1) is the RMSNorm of the Qwen3 family:
+    a / sqrt(mean(a^2) + eps) * gamma per row; eps is passed explicitly
+    (PARITY UNPINNED as a value, like EPS).
 EPS is PARITY UNPINNED (a choice, passed explicitly to both sides).
 """
 EPS = 1e-6

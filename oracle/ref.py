@@ -19,8 +19,8 @@ Pinning status: every function here is pinned by the not-gpu tests against
 closed forms, library routines, independent formulations of the paper's
 equations or brute force -- except the two documented readings marked
 "parity unpinned" in ``readings.py`` (the length factor of the temperature
-and the value of epsilon), whose only pinned consequence is that the length
-factor is 1 when nothing is pruned.
+and the values of epsilon in the score normalisation and in LN2), whose only
+pinned consequence is that the length factor is 1 when nothing is pruned.
 """
 from __future__ import annotations
 
@@ -59,6 +59,26 @@ def ref_score(x: np.ndarray, w1: np.ndarray, b1: Optional[np.ndarray],
         pre = pre + np.asarray(b1, dtype=np.float64)[None, :]
     u = silu(pre)
     return u @ np.asarray(w2, dtype=np.float64) + float(b2)
+
+
+def ref_rmsnorm(a: np.ndarray, gamma: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """The block's second norm, a~ = LN2(a), [TG] §3 Eq. 1, read as the
+    RMSNorm of the Qwen3 family (R22): each row divided by the root of its
+    mean square plus eps, then scaled by gamma (None = ones)."""
+    a = np.asarray(a, dtype=np.float64)
+    r = np.sqrt(np.mean(a * a, axis=-1, keepdims=True) + float(eps))
+    out = a / r
+    if gamma is not None:
+        out = out * np.asarray(gamma, dtype=np.float64)
+    return out
+
+
+def ref_score_prenorm(a: np.ndarray, gamma: Optional[np.ndarray], norm_eps: float,
+                      w1: np.ndarray, b1: Optional[np.ndarray], w2: np.ndarray,
+                      b2: float) -> np.ndarray:
+    """Raw gate scores from the post-attention residual a^L itself:
+    b~_j = MLP_theta(LN2(a_j^L)), [TG] §4.1 Eq. 3 with §3 Eq. 1's LN2 (R22)."""
+    return ref_score(ref_rmsnorm(a, gamma, norm_eps), w1, b1, w2, b2)
 
 
 def ref_normalise(b_raw: np.ndarray, prunable: np.ndarray, cu_seqlens: Sequence[int],

@@ -70,6 +70,52 @@ def test_score_matches_torch_fp64():
 
 
 # ---------------------------------------------------------------------------
+# LN2 before the scorer (§3 Eq. 1, RMSNorm reading R22)
+# ---------------------------------------------------------------------------
+def test_rmsnorm_closed_form_and_invariants():
+    # [3, 4]: mean square 12.5, so the row becomes [3, 4] / sqrt(12.5)
+    got = O.ref_rmsnorm(np.array([[3.0, 4.0]]), None, 0.0)
+    assert np.allclose(got, [[3.0 / math.sqrt(12.5), 4.0 / math.sqrt(12.5)]], rtol=1e-15, atol=0)
+    rng = _rng(40)
+    a = rng.standard_normal((20, 64)) * rng.uniform(0.1, 10.0, (20, 1))
+    y = O.ref_rmsnorm(a, None, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-14)     # unit RMS
+    assert np.allclose(O.ref_rmsnorm(7.5 * a, None, 0.0), y, rtol=1e-13)     # scale-free
+    g = rng.uniform(0.5, 2.0, 64)
+    assert np.allclose(O.ref_rmsnorm(a, g, 0.0), y * g[None, :], rtol=1e-15)
+    # eps enters under the root: a zero row stays zero, a tiny row is damped
+    z = O.ref_rmsnorm(np.zeros((1, 8)), None, 1e-6)
+    assert np.array_equal(z, np.zeros((1, 8)))
+
+
+def test_rmsnorm_matches_torch_fp64():
+    rng = _rng(41)
+    a = rng.standard_normal((33, 48)) * 3.0
+    g = rng.uniform(0.5, 1.5, 48)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(a), (48,), torch.from_numpy(g),
+                                        eps=1e-6).numpy()
+    assert np.allclose(O.ref_rmsnorm(a, g, 1e-6), want, rtol=1e-13, atol=1e-13)
+
+
+def test_prenorm_score_folds_gamma_into_w1():
+    """W1 (gamma * a / r) = (W1 diag(gamma)) (a / r): the norm weight folds
+    into the scorer's first layer, leaving only the division by the row RMS."""
+    rng = _rng(42)
+    T, d, h = 40, 32, 8
+    a = rng.standard_normal((T, d)) * rng.uniform(0.2, 5.0, (T, 1))
+    g = rng.uniform(0.5, 1.5, d)
+    w1 = rng.standard_normal((h, d)) / math.sqrt(d)
+    b1 = rng.standard_normal(h)
+    w2 = rng.standard_normal(h)
+    got = O.ref_score_prenorm(a, g, 1e-6, w1, b1, w2, 0.1)
+    folded = O.ref_score_prenorm(a, None, 1e-6, w1 * g[None, :], b1, w2, 0.1)
+    assert np.allclose(got, folded, rtol=1e-12, atol=1e-12)
+    # and it is the plain scorer on the normalised rows
+    r = np.sqrt(np.mean(a * a, axis=1, keepdims=True) + 1e-6)
+    assert np.allclose(got, O.ref_score(a / r * g, w1, b1, w2, 0.1), rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # normalisation (Eq. 3, RMS reading R2)
 # ---------------------------------------------------------------------------
 def test_normalise_closed_forms():
