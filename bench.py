@@ -254,6 +254,19 @@ def main():
             "note": "not part of the step: Q/K/V of the kept rows, 8704 x 2048 -> 2048+1024+1024"}
     del wq_t, wk_t, wv_t
 
+    # LN2 fused into the scorer (norm_eps >= 0, the norm weight folded into
+    # W1): the same rows taken as residuals, beside torch's separate RMSNorm
+    # pass over them, which the fusion removes
+    gam = torch.ones(wl.d, dtype=torch.bfloat16, device=dev)
+    t_score_ln2 = time_it(lambda: ops.score(x, w1, w2, pr, cu, b1=b1, eps=1e-6, b_raw=b_raw, b=b,
+                                            ws=ws_s, norm_eps=1e-6))
+    t_rms_torch = time_it(lambda: torch.nn.functional.rms_norm(x, (wl.d,), gam, 1e-6))
+    score_ln2 = {"kernel": "tg_score (norm_eps >= 0)", "us": round(t_score_ln2, 2),
+                 "plain_score_us": round(avg["score"], 2),
+                 "torch_rms_norm_us": round(t_rms_torch, 2),
+                 "note": "scorer with the block's RMSNorm fused; the torch time is the extra "
+                         "pass an unfused norm costs"}
+
     # one decode step after the prefill (tg_gated_decode): the new token's
     # query against the pruned cache of this layer (the kept rows' K/V plus
     # the token itself).  The calls are replayed from a HIP graph so that the
@@ -356,6 +369,7 @@ def main():
         "full_context": full,
         "qkv_proj": proj,
         "decode": decode,
+        "score_ln2": score_ln2,
     }
     print(json.dumps(out), flush=True)
 

@@ -70,12 +70,19 @@ int tg_version(void);
  *
  * x        dev  [t_in rows, d] of `dt`, row r at x + r * x_row_stride elements.
  *                Rows are the scorer's input (the post-attention hidden state
- *                after the block's second norm).
+ *                after the block's second norm), or the residual before that
+ *                norm when norm_eps >= 0.
  * w1       dev  [h, d] of `dt`, row-major (row j = input weights of hidden unit j).
  * b1       dev  [h] f32, or NULL for zero.      w2  dev [h] f32.     b2  scalar.
  * prunable dev  [t_in] u8, nonzero = document token (may be pruned).
  * cu_seqlens dev [n_seq + 1] i32, non-decreasing, cu_seqlens[n_seq] == t_in.
  * eps      >= 0; the normaliser of a sequence without prunable tokens is 1.
+ * norm_eps < 0: x rows are the scorer's input as they are.  norm_eps >= 0:
+ *          x rows are the residual a^L and the scorer applies the block's
+ *          second norm first (§3 Eq. 1, a~ = LN2(a), an RMSNorm):
+ *          x_j / sqrt(mean_c x_jc^2 + norm_eps), with the norm's weight g
+ *          folded into w1 by the caller (w1[j][c] * g[c]).  No extra pass
+ *          over x: the row sums of squares are taken while x is staged.
  * b_raw    dev  [t_in] f32 out (b~), or NULL (then kept in the workspace).
  * b        dev  [t_in] f32 out (normalised; 0 on prompt tokens).
  * ws       dev  workspace of >= tg_score_workspace_size(t_in, n_seq) bytes.
@@ -87,8 +94,8 @@ size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq);
 tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in,
                    int32_t d, int32_t h, const void* w1, const float* b1, const float* w2,
                    float b2, const uint8_t* prunable, const int32_t* cu_seqlens,
-                   int32_t n_seq, float eps, float* b_raw, float* b, void* ws,
-                   size_t ws_bytes, tg_stream stream);
+                   int32_t n_seq, float eps, float norm_eps, float* b_raw, float* b,
+                   void* ws, size_t ws_bytes, tg_stream stream);
 
 /* ------------------------------------------------------------------------
  * tg_kept_sizes -- host arithmetic for the output sizes of tg_select_topk,

@@ -26,7 +26,8 @@ PROTOTYPES = {
     "tg_version": (ctypes.c_int, []),
     "tg_score_workspace_size": (c_sz, [c_i64, c_i32]),
     "tg_score": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
-                                c_f32, c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+                                c_f32, c_vp, c_vp, c_i32, c_f32, c_f32, c_vp, c_vp, c_vp, c_sz,
+                                c_vp]),
     "tg_kept_sizes": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
     "tg_select_workspace_size": (c_sz, [c_i64, c_i32]),
     "tg_select_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_vp, c_vp,

@@ -60,11 +60,13 @@ size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
 tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
                    int32_t h, const void* w1, const float* b1, const float* w2, float b2,
                    const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq, float eps,
-                   float* b_raw, float* b, void* ws, size_t ws_bytes, tg_stream stream) {
+                   float norm_eps, float* b_raw, float* b, void* ws, size_t ws_bytes,
+                   tg_stream stream) {
   if (t_in < 0 || n_seq < 1 || d < 1 || h < 1)
     return fail(TG_ERR_INVALID_ARG, "tg_score: need t_in >= 0, n_seq >= 1, d >= 1, h >= 1");
   if (t_in > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "tg_score: t_in too large");
   if (!(eps >= 0.0f)) return fail(TG_ERR_INVALID_ARG, "tg_score: eps must be >= 0");
+  if (norm_eps != norm_eps) return fail(TG_ERR_INVALID_ARG, "tg_score: norm_eps is NaN");
   if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_score: bad dtype");
   if (x_row_stride < d) return fail(TG_ERR_INVALID_ARG, "tg_score: x_row_stride < d");
   if (!cu_seqlens || !w2 || !b || !ws) return fail(TG_ERR_INVALID_ARG, "tg_score: null pointer");
@@ -84,7 +86,8 @@ tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_i
     return fail(TG_ERR_WORKSPACE, "tg_score: workspace %zu < %zu bytes", ws_bytes,
                 tg::score_ws_bytes(t_in, n_seq));
   hipError_t e = tg::launch_score(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, b2, prunable,
-                                  cu_seqlens, n_seq, eps, b_raw, b, ws, (hipStream_t)stream);
+                                  cu_seqlens, n_seq, eps, norm_eps, b_raw, b, ws,
+                                  (hipStream_t)stream);
   return from_hip(e, "tg_score launch");
 }
 

@@ -126,7 +126,7 @@ size_t score_ws_bytes(int64_t t_in, int n_seq);
 hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_in, int d, int h,
                         const void* w1, const float* b1, const float* w2, float b2,
                         const uint8_t* prunable, const int32_t* cu, int n_seq, float eps,
-                        float* b_raw, float* b, void* ws, hipStream_t st);
+                        float norm_eps, float* b_raw, float* b, void* ws, hipStream_t st);
 
 size_t select_ws_bytes(int64_t t_in, int n_seq);
 hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t* cu,

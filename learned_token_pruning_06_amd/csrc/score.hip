@@ -6,12 +6,19 @@
 // bf16 path: a skinny GEMM C^T[h, row] = W1[h, d] . x[row, d]^T on MFMA
 // (v_mfma_f32_32x32x16_bf16), with the SiLU / w2 epilogue fused so only one
 // float per row leaves the kernel.  Each workgroup owns 256 rows and all h
-// columns (so the epilogue reduction over h stays in the workgroup): every
-// wave holds 64 rows x h in accumulators, streams its own x rows straight
-// from HBM into B-operand registers (one K-step of prefetch), and shares the
-// W1 K-slice through padded LDS.  The transposed orientation puts one row per
-// lane, so the reduction over h is in-lane plus one cross-half exchange.
-// Bound: HBM (2*d bytes per row) near the MFMA ridge; see the roofline notes.
+// columns (so the epilogue reduction over h stays in the workgroup); every
+// 64-wide K-step of x and W1 goes global -> registers (one step ahead) ->
+// padded, double-buffered LDS shared by the 8 waves.  The transposed
+// orientation puts one row per lane, so the reduction over h is in-lane plus
+// one cross-half exchange.  Bound: HBM (2*d bytes per row) near the MFMA
+// ridge.
+//
+// Optional LN2 (§3 Eq. 1: the scorer reads a~ = LN2(a), an RMSNorm): with
+// the norm weight folded into W1 by the caller, W1 (g * a / r) = (W1 g) a / r,
+// so the kernel multiplies the raw rows a and divides each row's
+// accumulators by r = sqrt(mean(a^2) + eps) in the epilogue.  The sums of
+// squares are taken from the x registers as they are staged, so the norm
+// costs no extra pass over the rows.
 //
 // Normalisation: per-sequence sums of squares in 2048-token chunks (fp64
 // partials, fixed reduction order), then every chunk reduces its sequence's
@@ -33,6 +40,13 @@ constexpr int kThreads = 64 * kWaves;
 
 TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// acc += lo^2 + hi^2 of a bf16 pair.  Written as one v_dot2_f32_bf16 with the
+// same register for both sources: the builtin, given one value twice, was
+// compiled to four dot products of the first word of a 16-byte vector.
+TG_DEVINL void sq_acc(float& acc, uint32_t w) {
+  asm("v_dot2_f32_bf16 %0, %1, %1, %0" : "+v"(acc) : "v"(w));
+}
+
 TG_DEVINL float silu_f(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
 }
@@ -44,17 +58,18 @@ TG_DEVINL float silu_f(float v) {
 // step ahead into registers, then staged into double-buffered, padded LDS
 // tiles shared by all waves; one barrier per K-step.  Rows past the end of x
 // (and hidden units past h) read zeros through the buffer ranges.
-template <int MT>
+template <int MT, bool NORM>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
-    float b2, float* __restrict__ b_raw) {
+    float b2, float norm_eps, float* __restrict__ b_raw) {
   constexpr int H = 32 * MT;
   constexpr int MTA = (MT + 1) / 2;          // h tiles of the first half
   constexpr int WV = (H + 63) / 64;          // W1 vectors per thread per K-step
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][H * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][kRowsPerWG * kRow];
   __shared__ float sred[4][64];
+  __shared__ float sinv[NORM ? kRowsPerWG : 1];     // 1 / RMS of each row (LN2)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
@@ -87,9 +102,16 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     for (int i = 0; i < WV; ++i)
       wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + 2 * k0, 0, 0));
   };
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};             // sums of squares of rows lrow + 64 i
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sq_acc(ss[i], xr[i][w]);
+    }
 #pragma unroll
     for (int i = 0; i < WV; ++i)
       if (lrow + 64 * i < H) st16(&sw[buf][ldst + 64 * i * kRow], wr[i]);
@@ -133,6 +155,22 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     __syncthreads();
   }
 
+  // LN2: the 8 threads of a loader row hold its partial sums of squares
+  float inv0 = 1.0f, inv1 = 1.0f;
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = ss[i];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if (lch == 0) sinv[lrow + 64 * i] = 1.0f / sqrtf(v / (float)d + norm_eps);
+    }
+    __syncthreads();
+    inv0 = sinv[64 * rg + n];
+    inv1 = sinv[64 * rg + 32 + n];
+  }
+
   // epilogue: lane (n, g) holds h = 32(mt0+mt) + 8(r/4) + 4g + (r%4) of rows 32nt + n;
   // the two h halves of a row group are added through LDS
   float part0 = 0.f, part1 = 0.f;
@@ -144,14 +182,14 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
         const int h0 = 32 * (mt0 + mt) + 8 * r4 + 4 * g;
         const float4 bb = b1 ? *reinterpret_cast<const float4*>(b1 + h0) : make_float4(0, 0, 0, 0);
         const float4 ww = *reinterpret_cast<const float4*>(w2 + h0);
-        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 0] + bb.x), ww.x, part0);
-        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 1] + bb.y), ww.y, part0);
-        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 2] + bb.z), ww.z, part0);
-        part0 = fmaf(silu_f(acc[mt][0][4 * r4 + 3] + bb.w), ww.w, part0);
-        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 0] + bb.x), ww.x, part1);
-        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 1] + bb.y), ww.y, part1);
-        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 2] + bb.z), ww.z, part1);
-        part1 = fmaf(silu_f(acc[mt][1][4 * r4 + 3] + bb.w), ww.w, part1);
+        part0 = fmaf(silu_f(fmaf(acc[mt][0][4 * r4 + 0], inv0, bb.x)), ww.x, part0);
+        part0 = fmaf(silu_f(fmaf(acc[mt][0][4 * r4 + 1], inv0, bb.y)), ww.y, part0);
+        part0 = fmaf(silu_f(fmaf(acc[mt][0][4 * r4 + 2], inv0, bb.z)), ww.z, part0);
+        part0 = fmaf(silu_f(fmaf(acc[mt][0][4 * r4 + 3], inv0, bb.w)), ww.w, part0);
+        part1 = fmaf(silu_f(fmaf(acc[mt][1][4 * r4 + 0], inv1, bb.x)), ww.x, part1);
+        part1 = fmaf(silu_f(fmaf(acc[mt][1][4 * r4 + 1], inv1, bb.y)), ww.y, part1);
+        part1 = fmaf(silu_f(fmaf(acc[mt][1][4 * r4 + 2], inv1, bb.z)), ww.z, part1);
+        part1 = fmaf(silu_f(fmaf(acc[mt][1][4 * r4 + 3], inv1, bb.w)), ww.w, part1);
       }
     }
   }
@@ -168,23 +206,31 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   }
 }
 
-// fp32 scorer on the vector ALU: one wave per row, lanes over hidden units.
+// fp32 scorer on the vector ALU: one wave per row, lanes over hidden units
+// (with LN2, the row's RMS first: lanes over the row, then a wave sum).
 __global__ __launch_bounds__(256) void score_mlp_f32(const float* __restrict__ x, int64_t xs,
                                                      int64_t t_in, int d, int h,
                                                      const float* __restrict__ w1,
                                                      const float* __restrict__ b1,
                                                      const float* __restrict__ w2, float b2,
-                                                     float* __restrict__ b_raw) {
+                                                     float norm_eps, float* __restrict__ b_raw) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= t_in) return;
   const float* xp = x + row * xs;
+  float inv = 1.0f;
+  if (norm_eps >= 0.0f) {
+    float ss = 0.f;
+    for (int e = lane; e < d; e += 64) ss = fmaf(xp[e], xp[e], ss);
+    ss = wave_sum(ss);
+    inv = 1.0f / sqrtf(ss / (float)d + norm_eps);
+  }
   float part = 0.f;
   for (int j = lane; j < h; j += 64) {
     const float* wp = w1 + (int64_t)j * d;
     float acc = 0.f;
     for (int e = 0; e < d; ++e) acc = fmaf(xp[e], wp[e], acc);
-    const float v = acc + (b1 ? b1[j] : 0.f);
+    const float v = fmaf(acc, inv, b1 ? b1[j] : 0.f);
     part = fmaf(v / (1.0f + expf(-v)), w2[j], part);
   }
   part = wave_sum(part);
@@ -290,7 +336,7 @@ size_t score_ws_bytes(int64_t t_in, int n_seq) {
 hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_in, int d, int h,
                         const void* w1, const float* b1, const float* w2, float b2,
                         const uint8_t* prunable, const int32_t* cu, int n_seq, float eps,
-                        float* b_raw, float* b, void* ws, hipStream_t st) {
+                        float norm_eps, float* b_raw, float* b, void* ws, hipStream_t st) {
   Partial* part = static_cast<Partial*>(ws);
   size_t off = (sizeof(Partial) * (size_t)n_slots(t_in, n_seq) + 255) & ~(size_t)255;
   float* braw = b_raw ? b_raw : reinterpret_cast<float*>(static_cast<char*>(ws) + off);
@@ -300,10 +346,14 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* wp = static_cast<const uint16_t*>(w1);
     switch (h / 32) {
-#define TG_SCORE_CASE(M)                                                                    \
-  case M:                                                                                   \
-    hipLaunchKernelGGL(score_mlp_bf16<M>, grid, dim3(kThreads), 0, st, xp, x_row_stride, t_in, d, \
-                       wp, b1, w2, b2, braw);                                               \
+#define TG_SCORE_CASE(M)                                                                     \
+  case M:                                                                                    \
+    if (norm_eps >= 0.0f)                                                                    \
+      hipLaunchKernelGGL((score_mlp_bf16<M, true>), grid, dim3(kThreads), 0, st, xp,          \
+                         x_row_stride, t_in, d, wp, b1, w2, b2, norm_eps, braw);              \
+    else                                                                                     \
+      hipLaunchKernelGGL((score_mlp_bf16<M, false>), grid, dim3(kThreads), 0, st, xp,         \
+                         x_row_stride, t_in, d, wp, b1, w2, b2, norm_eps, braw);              \
     break;
       TG_SCORE_CASE(1) TG_SCORE_CASE(2) TG_SCORE_CASE(3) TG_SCORE_CASE(4)
       TG_SCORE_CASE(5) TG_SCORE_CASE(6) TG_SCORE_CASE(7) TG_SCORE_CASE(8)
@@ -313,7 +363,8 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
   } else {
     const dim3 grid((unsigned)((t_in + 3) / 4));
     hipLaunchKernelGGL(score_mlp_f32, grid, dim3(256), 0, st, static_cast<const float*>(x),
-                       x_row_stride, t_in, d, h, static_cast<const float*>(w1), b1, w2, b2, braw);
+                       x_row_stride, t_in, d, h, static_cast<const float*>(w1), b1, w2, b2,
+                       norm_eps, braw);
   }
   const dim3 g2((unsigned)n_slots(t_in, n_seq));
   hipLaunchKernelGGL(score_partial, g2, dim3(256), 0, st, braw, prunable, cu, n_seq, t_in, part);

@@ -45,8 +45,11 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 def score(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: torch.Tensor,
           cu_seqlens: torch.Tensor, b1: Optional[torch.Tensor] = None, b2: float = 0.0,
           eps: float = 1e-6, b_raw: Optional[torch.Tensor] = None,
-          b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
-    """tg_score: raw scores b~ and normalised scores b (f32, one per token)."""
+          b: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+          norm_eps: Optional[float] = None):
+    """tg_score: raw scores b~ and normalised scores b (f32, one per token).
+    With norm_eps set, x holds the residual rows and the scorer applies the
+    RMSNorm first (its weight already folded into w1)."""
     lib = load()
     _need(x, "x", (torch.bfloat16, torch.float32), 2)
     _need(w1, "w1", x.dtype, 2)
@@ -67,7 +70,8 @@ def score(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: torch.T
     if ws is None:
         ws = workspace(need, dev)
     st = lib.tg_score(_p(x), _DT[x.dtype], x.stride(0), t_in, d, h, _p(w1), _p(b1), _p(w2),
-                      float(b2), _p(prunable), _p(cu_seqlens), n_seq, float(eps), _p(b_raw), _p(b),
+                      float(b2), _p(prunable), _p(cu_seqlens), n_seq, float(eps),
+                      float(-1.0 if norm_eps is None else norm_eps), _p(b_raw), _p(b),
                       _p(ws), ws.numel(), _stream(dev))
     check("tg_score", st)
     return b_raw, b

@@ -96,17 +96,19 @@ def test_workspace_queries(lib):
 
 def _score(lib, **kw):
     a = dict(x=FAKE, dt=1, xs=2048, t=1024, d=2048, h=256, w1=FAKE, b1=None, w2=FAKE, b2=0.0,
-             pr=FAKE, cu=FAKE, n_seq=1, eps=1e-6, b_raw=FAKE, b=FAKE, ws=FAKE, wsb=0)
+             pr=FAKE, cu=FAKE, n_seq=1, eps=1e-6, norm_eps=-1.0, b_raw=FAKE, b=FAKE, ws=FAKE,
+             wsb=0)
     a.update(kw)
     return lib.tg_score(a["x"], a["dt"], a["xs"], a["t"], a["d"], a["h"], a["w1"], a["b1"], a["w2"],
-                        a["b2"], a["pr"], a["cu"], a["n_seq"], a["eps"], a["b_raw"], a["b"], a["ws"],
-                        a["wsb"], None)
+                        a["b2"], a["pr"], a["cu"], a["n_seq"], a["eps"], a["norm_eps"], a["b_raw"],
+                        a["b"], a["ws"], a["wsb"], None)
 
 
 def test_score_validation(lib):
     assert _score(lib, t=-1) == 1
     assert _score(lib, n_seq=0) == 1
     assert _score(lib, eps=-1.0) == 1
+    assert _score(lib, norm_eps=float("nan")) == 1
     assert _score(lib, dt=7) == 1
     assert _score(lib, xs=100) == 1
     assert _score(lib, w2=None) == 1

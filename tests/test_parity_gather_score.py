@@ -109,3 +109,110 @@ def test_score_is_deterministic():
     r1 = ops.score(*args)
     r2 = ops.score(*args)
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+# ---------------------------------------------------------------------------
+# tg_score with LN2 fused (norm_eps >= 0): x holds the residual rows, the
+# norm weight is folded into W1 by the caller (here: the fp32 product rounded
+# to bf16, the same folded weights go to the oracle).
+# ---------------------------------------------------------------------------
+NORM_EPS = 1e-6
+
+
+def _prenorm_case(seed, T, d, h, lens, bf16=True, pow2_gamma=False):
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    scale = np.exp(rng.uniform(np.log(0.05), np.log(20.0), (T, 1)))
+    a = (rng.standard_normal((T, d)) * scale).astype(np.float32)
+    gamma = (2.0 ** rng.integers(-2, 3, d) if pow2_gamma
+             else rng.uniform(0.5, 1.5, d)).astype(np.float32)
+    w1 = (rng.standard_normal((h, d)) / np.sqrt(d)).astype(np.float32)
+    if bf16:
+        a = f32_to_bf16_bits(a)
+        w1 = f32_to_bf16_bits(w1)
+        w1f = f32_to_bf16_bits(bf16_to_f32(w1) * gamma[None, :])
+    else:
+        w1f = w1 * gamma[None, :]
+    b1 = (0.1 * rng.standard_normal(h)).astype(np.float32)
+    w2 = (rng.standard_normal(h) / np.sqrt(h)).astype(np.float32)
+    pr = (rng.random(T) < 0.9).astype(np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(a=a, gamma=gamma, w1=w1, w1f=w1f, b1=b1, w2=w2, b2=-0.125, prunable=pr,
+                cu_seqlens=cu)
+
+
+def bf16_to_f32(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def _run_prenorm(c, bf16):
+    from learned_token_pruning_06_amd import ops
+    at = bf16_dev(c["a"]) if bf16 else f32_dev(c["a"])
+    wt = bf16_dev(c["w1f"]) if bf16 else f32_dev(c["w1f"])
+    b_raw, b = ops.score(at, wt, f32_dev(c["w2"]), u8_dev(c["prunable"]), i32_dev(c["cu_seqlens"]),
+                         b1=f32_dev(c["b1"]), b2=c["b2"], eps=O.readings.EPS, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    return b_raw.cpu().numpy().astype(np.float64), b.cpu().numpy().astype(np.float64)
+
+
+def _f64(bits_or_f32, bf16):
+    return bf16_to_f32(bits_or_f32).astype(np.float64) if bf16 else np.asarray(bits_or_f32, np.float64)
+
+
+@pytest.mark.parametrize("T,d,h,lens", [(300, 64, 32, [100, 0, 200]), (1111, 128, 96, [1111]),
+                                        (2560, 2048, 256, [1, 255, 256, 257, 1791]),
+                                        (16384, 2048, 256, [16384])])
+def test_score_with_fused_rmsnorm_bf16(T, d, h, lens):
+    say(f"score+LN2 bf16: T={T} d={d} h={h}")
+    c = _prenorm_case(20 + T, T, d, h, lens)
+    got_raw, got_b = _run_prenorm(c, True)
+    ref_raw = O.ref_score_prenorm(_f64(c["a"], True), None, NORM_EPS, _f64(c["w1f"], True),
+                                  c["b1"], c["w2"], c["b2"])
+    ref_b, _ = O.ref_normalise(ref_raw, c["prunable"], c["cu_seqlens"], O.readings.EPS)
+    e_raw, e_b = score_err(got_raw, ref_raw), score_err(got_b, ref_b)
+    say(f"  max rel err raw={e_raw:.3e} normalised={e_b:.3e}")
+    assert e_raw <= SCORE_TOL and e_b <= SCORE_TOL
+
+
+def test_score_with_fused_rmsnorm_power_of_two_gamma_is_the_unfolded_oracle():
+    """With a power-of-two norm weight the fold is exact in bf16, so the GPU
+    result on the folded W1 meets the oracle that normalises with gamma and
+    multiplies by the unfolded W1."""
+    say("score+LN2 bf16: exact fold")
+    c = _prenorm_case(31, 2048, 2048, 256, [1000, 1048], pow2_gamma=True)
+    assert np.array_equal(bf16_to_f32(c["w1f"]), bf16_to_f32(c["w1"]) * c["gamma"][None, :])
+    got_raw, _ = _run_prenorm(c, True)
+    ref_raw = O.ref_score_prenorm(_f64(c["a"], True), c["gamma"], NORM_EPS, _f64(c["w1"], True),
+                                  c["b1"], c["w2"], c["b2"])
+    assert score_err(got_raw, ref_raw) <= SCORE_TOL
+
+
+def test_score_with_fused_rmsnorm_fp32():
+    say("score+LN2 fp32: tiny shape")
+    c = _prenorm_case(32, 1024, 256, 64, [1024], bf16=False)
+    got_raw, got_b = _run_prenorm(c, False)
+    ref_raw = O.ref_score_prenorm(c["a"], None, NORM_EPS, c["w1f"], c["b1"], c["w2"], c["b2"])
+    ref_b, _ = O.ref_normalise(ref_raw, c["prunable"], c["cu_seqlens"], O.readings.EPS)
+    assert score_err(got_raw, ref_raw) <= SCORE_TOL and score_err(got_b, ref_b) <= SCORE_TOL
+
+
+def test_score_with_fused_rmsnorm_128k_sampled_rows():
+    """The 128k workload's rows taken as residuals (scaled per row), at full
+    size; raw scores compared on every 97th row."""
+    from learned_token_pruning_06_amd import ops
+    from workloads import f32_to_bf16_bits
+    say("score+LN2 bf16: 128k rows, sampled")
+    g = workload(3)
+    rng = np.random.default_rng(33)
+    T, d = g["x"].shape
+    rows = np.arange(0, T, 97)
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    w1f = f32_to_bf16_bits(bf16_to_f32(g["w1"]) * gamma[None, :])
+    b_raw, _ = ops.score(bf16_dev(g["x"]), bf16_dev(w1f), f32_dev(g["w2"]), u8_dev(g["prunable"]),
+                         i32_dev(g["cu_seqlens"]), b1=f32_dev(g["b1"]), b2=g["b2"],
+                         eps=O.readings.EPS, norm_eps=NORM_EPS)
+    torch.cuda.synchronize()
+    got = b_raw.cpu().numpy().astype(np.float64)[rows]
+    ref = O.ref_score_prenorm(bf16_to_f32(g["x"][rows]).astype(np.float64), None, NORM_EPS,
+                              bf16_to_f32(w1f).astype(np.float64), g["b1"], g["w2"], g["b2"])
+    assert score_err(got, ref) <= SCORE_TOL
