@@ -16,8 +16,8 @@ batches to bound memory.  Where the pages leave a step open, the reading is
 named in the docstring (R-numbers match ``readings.py``).
 
 Pinning status: every function here is pinned by the not-gpu tests against
-closed forms, library routines, independent formulations of the paper's
-equations or brute force -- except the two documented readings marked
+closed forms, library routines (torch autograd for the backward), central
+differences, independent formulations of the paper's equations or brute force -- except the two documented readings marked
 "parity unpinned" in ``readings.py`` (the length factor of the temperature
 and the values of epsilon in the score normalisation and in LN2), whose only
 pinned consequence is that the length factor is 1 when nothing is pruned.
@@ -383,6 +383,82 @@ def ref_gated_attn_bruteforce(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
                         acc += w[jj] * float(v[j][kvh][e])
                     out[i, h, e] = acc / tot
     return out
+
+
+# ---------------------------------------------------------------------------
+# backward of token-gated attention ([TG] §4.3: the gate's scores receive a
+# gradient through the attention of Eq. 8)
+# ---------------------------------------------------------------------------
+def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
+                       sm_scale: Optional[float] = None, len_scale: str = R.LEN_SCALE,
+                       row_block: int = 512):
+    """Gradients of L = sum(O * dout) through the token-gated attention of
+    [TG] Eq. 8 (gain of Eq. 6, temperature of Eq. 7), by the chain rule on
+
+        z_ij = s q_i.k_j + gain_h b_j,   l_ij = tau_i z_ij   (j <= i),
+        P_i  = softmax_j(l_i),           O_i  = sum_j P_ij v_j:
+
+        dP_ij  = dout_i . v_j
+        dl_ij  = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+        dv_j   = sum_i P_ij dout_i
+        dq_i   = s tau_i sum_j dl_ij k_j
+        dk_j   = s sum_i tau_i dl_ij q_i
+        db_j   = sum_{h,i} tau_i gain_h dl_ij          (the gate's gradient path)
+        dgain_h = sum_{i,j} tau_i b_j dl_ij
+        dtemp_h = sum_{i,j} lambda_i z_ij dl_ij          (tau_i = temp_h lambda_i)
+
+    KV gradients add up over the query heads that share a KV head (R9);
+    tau_i's length factor depends on positions only, so it carries no
+    gradient.  Query rows are processed in blocks of ``row_block``.
+    Returns (dq [T,Hq,dh], dk [T,Hkv,dh], dv [T,Hkv,dh], db [T], dgain [Hq],
+    dtemp [Hq]), float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    kb = np.asarray(kept_b, dtype=np.float64)
+    T, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else float(sm_scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    db = np.zeros(T)
+    dgain, dtemp = np.zeros(Hq), np.zeros(Hq)
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        a = np.arange(n)
+        if kept_pos is None:
+            lam = np.ones(n)
+        else:
+            lam = length_factor(a + 1.0, np.asarray(kept_pos[lo:hi], np.float64) + 1.0, len_scale)
+        for h in range(Hq):
+            kvh = h // G
+            K, V = k[lo:hi, kvh, :], v[lo:hi, kvh, :]
+            g = float(gain[h])
+            for r0 in range(0, n, row_block):
+                rr = a[r0:r0 + row_block]
+                last = int(rr[-1]) + 1
+                Q, dO = q[lo + rr, h, :], do[lo + rr, h, :]
+                tau = float(temp[h]) * lam[rr]
+                z = scale * (Q @ K[:last].T) + g * kb[lo:lo + last][None, :]
+                causal = np.arange(last)[None, :] <= rr[:, None]
+                logits = np.where(causal, tau[:, None] * z, -np.inf)
+                P = _softmax_rows(logits)
+                dP = dO @ V[:last].T
+                dl = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+                dv[lo:lo + last, kvh, :] += P.T @ dO
+                tdl = tau[:, None] * dl
+                dq[lo + rr, h, :] = scale * (tdl @ K[:last])
+                dk[lo:lo + last, kvh, :] += scale * (tdl.T @ Q)
+                db[lo:lo + last] += g * np.sum(tdl, axis=0)
+                dgain[h] += float(np.sum(tdl * kb[lo:lo + last][None, :]))
+                zc = np.where(causal, z, 0.0)
+                dtemp[h] += float(np.sum(lam[rr][:, None] * zc * dl))
+    return dq, dk, dv, db, dgain, dtemp
 
 
 # ---------------------------------------------------------------------------

@@ -507,3 +507,88 @@ def test_projection_head_layout_and_linearity():
     q3, k3, v3 = O.ref_project(2.5 * x1 - x2, wq, wk, wv, hq, hkv, dh)
     for a, b, c in ((q1, q2, q3), (k1, k2, k3), (v1, v2, v3)):
         assert np.allclose(c, 2.5 * a - b, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# backward of token-gated attention (§4.3 gradient path through Eq. 8)
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, lens=(5, 7), hq=4, hkv=2, dh=8):
+    rng = _rng(seed)
+    kc = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(kc[-1])
+    q = rng.standard_normal((T, hq, dh))
+    k = rng.standard_normal((T, hkv, dh))
+    v = rng.standard_normal((T, hkv, dh))
+    kb = rng.standard_normal(T)
+    pos = np.concatenate([np.sort(rng.choice(40, n, replace=False)) for n in lens]).astype(np.int64)
+    gain = rng.uniform(0.5, 1.5, hq)
+    temp = rng.uniform(0.8, 1.2, hq)
+    do = rng.standard_normal((T, hq, dh))
+    return q, k, v, kb, pos, kc, gain, temp, do
+
+
+def _loss(q, k, v, kb, pos, kc, gain, temp, do):
+    return float(np.sum(O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp) * do))
+
+
+def test_attn_bwd_matches_central_differences():
+    """Every gradient against (L(x+h) - L(x-h)) / 2h of L = sum(O * dout),
+    on several entries of each input."""
+    args = list(_bwd_case(50))
+    dq, dk, dv, db, dg, dt = O.ref_gated_attn_bwd(*args)
+    grads = {0: dq, 1: dk, 2: dv, 3: db, 6: dg, 7: dt}
+    rng = _rng(51)
+    eps = 1e-6
+    for ai, gr in grads.items():
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in np.shape(args[ai]))
+            plus = [np.array(a, dtype=np.float64, copy=True) if i == ai else a for i, a in enumerate(args)]
+            minus = [np.array(a, dtype=np.float64, copy=True) if i == ai else a for i, a in enumerate(args)]
+            plus[ai][idx] += eps
+            minus[ai][idx] -= eps
+            fd = (_loss(*plus) - _loss(*minus)) / (2 * eps)
+            assert abs(fd - gr[idx]) <= 1e-6 * max(1.0, abs(fd)), (ai, idx, fd, gr[idx])
+
+
+def test_attn_bwd_matches_torch_autograd_fp64():
+    """The same loss written with torch ops (masked softmax attention with an
+    additive bias and a per-query temperature), differentiated by autograd."""
+    q, k, v, kb, pos, kc, gain, temp, do = _bwd_case(52, lens=(9, 1, 6), hq=6, hkv=3, dh=4)
+    T, hq, dh = q.shape
+    G = hq // k.shape[1]
+    tq, tk, tv, tb, tg, tt = (torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                              for a in (q, k, v, kb, gain, temp))
+    out = []
+    for s in range(len(kc) - 1):
+        lo, hi = int(kc[s]), int(kc[s + 1])
+        n = hi - lo
+        m = torch.arange(1, n + 1, dtype=torch.float64)
+        p = torch.tensor(pos[lo:hi] + 1, dtype=torch.float64)
+        lam = torch.log(m) / torch.log(torch.clamp(p, min=2.0))
+        for h in range(hq):
+            z = tq[lo:hi, h] @ tk[lo:hi, h // G].T / math.sqrt(dh) + tg[h] * tb[lo:hi][None, :]
+            lg = (tt[h] * lam)[:, None] * z
+            lg = lg.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+            out.append((torch.softmax(lg, dim=1) @ tv[lo:hi, h // G] * torch.tensor(do[lo:hi, h])).sum())
+    torch.stack(out).sum().backward()
+    got = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do)
+    for g_np, t in zip(got, (tq, tk, tv, tb, tg, tt)):
+        assert np.allclose(g_np, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_attn_bwd_invariants():
+    """Shifting every b of a sequence by c shifts each row's logits by a
+    constant, so the scores' gradient sums to zero per sequence; and since
+    each row of P sums to 1, dv summed over keys equals dout summed over the
+    queries and query heads of each KV head."""
+    q, k, v, kb, pos, kc, gain, temp, do = _bwd_case(53, lens=(11, 4, 8), hq=4, hkv=2, dh=8)
+    dq, dk, dv, db, dg, dt = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do)
+    for s in range(len(kc) - 1):
+        assert abs(np.sum(db[kc[s]:kc[s + 1]])) < 1e-12
+        for kvh in range(2):
+            want = do[kc[s]:kc[s + 1], 2 * kvh:2 * kvh + 2].sum(axis=(0, 1))
+            assert np.allclose(dv[kc[s]:kc[s + 1], kvh].sum(axis=0), want, rtol=1e-12, atol=1e-12)
+    # row blocks do not change the result
+    again = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do, row_block=3)
+    for a, b in zip(again, (dq, dk, dv, db, dg, dt)):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-14)
