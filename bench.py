@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "gated-prefill tokens/s at 128k ctx; gated-attn MFMA % peak; gate HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3            # MI355X fp32 vector ALU
 WORKLOAD = 3                        # 128k-token gated layer
 
 
@@ -267,6 +268,22 @@ def main():
                  "note": "scorer with the block's RMSNorm fused; the torch time is the extra "
                          "pass an unfused norm costs"}
 
+    # the attention's backward (tg_gated_attn_bwd) on the step's kept rows:
+    # fp32 on the vector ALU; algorithmic work 10 dh flop per (query, key)
+    # pair and head (the five products of the backward)
+    dout = torch.randn_like(q)
+    ws_b = ops.workspace(lib.tg_gated_attn_bwd_workspace_size(t_kept, 1, wl.hq, wl.hkv), dev)
+    t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain, temp,
+                                               ws=ws_b), reps=2)
+    bwd_flops = 10.0 * wl.dh * wl.hq * t_kept * (t_kept + 1) / 2
+    attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1),
+                "tflops": round(bwd_flops / (t_bwd * 1e-6) / 1e12, 2),
+                "bound": "alu", "peak_tflops_fp32": PEAK_FP32_TFLOPS,
+                "frac_of_fp32_peak": round(bwd_flops / (t_bwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                "note": "8704 kept rows, bf16 inputs, fp32 arithmetic and gradients; scores "
+                        "recomputed in 3 passes (18 dh flop per pair done)"}
+    del dout, ws_b
+
     # one decode step after the prefill (tg_gated_decode): the new token's
     # query against the pruned cache of this layer (the kept rows' K/V plus
     # the token itself).  The calls are replayed from a HIP graph so that the
@@ -370,6 +387,7 @@ def main():
         "qkv_proj": proj,
         "decode": decode,
         "score_ln2": score_ln2,
+        "attn_bwd": attn_bwd,
     }
     print(json.dumps(out), flush=True)
 

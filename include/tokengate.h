@@ -7,7 +7,8 @@
  *   tg_gather       compaction of the kept rows
  *   tg_gated_attn   token-gated causal attention over the kept tokens
  * and, between the last two, tg_qkv_proj, the projections of the kept rows;
- * tg_gated_decode runs one decode step over the pruned caches afterwards.
+ * tg_gated_decode runs one decode step over the pruned caches afterwards;
+ * tg_gated_attn_bwd gives the attention's gradients for training.
  * Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
  * with Learned Token Pruning", §4.1 (Eq. 3-4) and §4.2 (Eq. 5-8).
  *
@@ -184,6 +185,40 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
                         int32_t max_kept_seqlen, int32_t hq, int32_t hkv, int32_t dh,
                         const float* gain, const float* temp, float sm_scale,
                         tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_gated_attn_bwd -- gradients of tg_gated_attn: the path by which the
+ * loss reaches the gate's scores (§4.3: token-gated attention gives top-K a
+ * gradient), and the gradients of gain (Eq. 6) and temperature (Eq. 7).
+ * With z_ij = s q_i.k_j + gain_h b_j, l_ij = tau_i z_ij (j <= i), P the
+ * row softmax of l, dP_ij = dout_i . v_j, D_i = sum_j P_ij dP_ij and
+ * dl_ij = P_ij (dP_ij - D_i):
+ *
+ *   dv_j = sum_i P_ij dout_i              dq_i = s tau_i sum_j dl_ij k_j
+ *   dk_j = s sum_i tau_i dl_ij q_i        db_j = sum_{h,i} tau_i gain_h dl_ij
+ *   dgain_h = sum_ij tau_i b_j dl_ij      dtemp_h = sum_ij lambda_i z_ij dl_ij
+ *
+ * (tau_i = temp_h lambda_i; KV gradients sum over the query heads sharing a
+ * KV head.)  Arguments as for tg_gated_attn, plus:
+ * dout dev [t_kept, hq, dh] of `dt`: the gradient of the loss w.r.t. out.
+ * dq   dev [t_kept, hq, dh] f32 out;  dk, dv dev [t_kept, hkv, dh] f32 out.
+ * db   dev [t_kept] f32 out (rows past kept_cu_seqlens[n_seq] get 0).
+ * dgain, dtemp dev [hq] f32 out.
+ * ws   dev workspace of >= tg_gated_attn_bwd_workspace_size(t_kept, n_seq,
+ *      hq, hkv) bytes, 4-byte aligned.
+ * The softmax statistics are recomputed, so the forward output is not an
+ * input.  Arithmetic is fp32 on the vector ALU for both dtypes; results are
+ * bitwise reproducible.  Supported: dh in {64, 128}, hq % hkv == 0,
+ * 16-byte aligned tensors.
+ * ---------------------------------------------------------------------- */
+size_t tg_gated_attn_bwd_workspace_size(int64_t t_kept, int32_t n_seq, int32_t hq, int32_t hkv);
+tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                            tg_dtype dt, int64_t t_kept, const float* kept_b,
+                            const int32_t* kept_pos, const int32_t* kept_cu_seqlens,
+                            int32_t n_seq, int32_t hq, int32_t hkv, int32_t dh,
+                            const float* gain, const float* temp, float sm_scale, float* dq,
+                            float* dk, float* dv, float* db, float* dgain, float* dtemp,
+                            void* ws, size_t ws_bytes, tg_stream stream);
 
 /* ------------------------------------------------------------------------
  * tg_qkv_proj -- query, key and value projections of the kept rows: the

@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10200; }
+int tg_version(void) { return 10300; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -253,6 +253,45 @@ tg_status tg_gated_decode(const void* q, const void* k_cache, const void* v_cach
                                    t_cache, max_cache_len, hq, hkv, dh, gain, temp, sm_scale, ws,
                                    (hipStream_t)stream);
   return from_hip(e, "tg_gated_decode launch");
+}
+
+// ------------------------------------------------------- attention backward
+size_t tg_gated_attn_bwd_workspace_size(int64_t t_kept, int32_t n_seq, int32_t hq, int32_t hkv) {
+  if (t_kept < 0 || n_seq < 1 || hq < 1 || hkv < 1) return 0;
+  return tg::attn_bwd_ws_bytes(t_kept, n_seq, hq, hkv);
+}
+
+tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                            tg_dtype dt, int64_t t_kept, const float* kept_b,
+                            const int32_t* kept_pos, const int32_t* kept_cu, int32_t n_seq,
+                            int32_t hq, int32_t hkv, int32_t dh, const float* gain,
+                            const float* temp, float sm_scale, float* dq, float* dk, float* dv,
+                            float* db, float* dgain, float* dtemp, void* ws, size_t ws_bytes,
+                            tg_stream stream) {
+  if (t_kept < 0 || n_seq < 1 || hq < 1 || hkv < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: bad sizes");
+  if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: hq %% hkv != 0");
+  if (dt != TG_F32 && dt != TG_BF16)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: bad dtype");
+  if (dh != 64 && dh != 128)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: dh must be 64 or 128");
+  if (hq > 65535 || t_kept > INT32_MAX - 4096)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: sizes too large");
+  if (!kept_cu || !gain || !temp || !dgain || !dtemp || !ws)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: null pointer");
+  if (t_kept > 0 && (!q || !k || !v || !dout || !kept_b || !dq || !dk || !dv || !db))
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: null pointer");
+  const size_t need = tg::attn_bwd_ws_bytes(t_kept, n_seq, hq, hkv);
+  if (ws_bytes < need)
+    return fail(TG_ERR_WORKSPACE, "tg_gated_attn_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)) ||
+      (dout && !aligned(dout, 16)) || (dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)) ||
+      (dv && !aligned(dv, 16)) || !aligned(ws, 4))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: tensors must be 16-byte aligned");
+  hipError_t e = tg::launch_attn_bwd(q, k, v, dout, (int)dt, t_kept, kept_b, kept_pos, kept_cu,
+                                     n_seq, hq, hkv, dh, gain, temp, sm_scale, dq, dk, dv, db,
+                                     dgain, dtemp, ws, (hipStream_t)stream);
+  return from_hip(e, "tg_gated_attn_bwd launch");
 }
 
 }  // extern "C"

@@ -148,6 +148,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
                          const float* gain, const float* temp, float sm_scale, void* ws,
                          hipStream_t st);
 
+size_t attn_bwd_ws_bytes(int64_t t, int n_seq, int hq, int hkv);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dt,
+                           int64_t t, const float* kept_b, const int32_t* kept_pos,
+                           const int32_t* cu, int n_seq, int hq, int hkv, int dh,
+                           const float* gain, const float* temp, float sm_scale, float* dq,
+                           float* dk, float* dv, float* db, float* dgain, float* dtemp, void* ws,
+                           hipStream_t st);
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                             const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,

@@ -202,6 +202,44 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
     return out
 
 
+def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                   kept_b: torch.Tensor, kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor,
+                   gain: torch.Tensor, temp: torch.Tensor, sm_scale: Optional[float] = None,
+                   ws: Optional[torch.Tensor] = None):
+    """tg_gated_attn_bwd: returns (dq, dk, dv, db, dgain, dtemp), all f32."""
+    lib = load()
+    _need(q, "q", (torch.bfloat16, torch.float32), 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    _need(dout, "dout", q.dtype, 3)
+    _need(kept_b, "kept_b", torch.float32, 1)
+    _need(kept_cu, "kept_cu", torch.int32, 1)
+    _need(gain, "gain", torch.float32, 1)
+    _need(temp, "temp", torch.float32, 1)
+    if kept_pos is not None:
+        _need(kept_pos, "kept_pos", torch.int32, 1)
+    t, hq, dh = q.shape
+    hkv = k.shape[1]
+    n_seq = kept_cu.numel() - 1
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((t, hq, dh), **f32)
+    dk = torch.empty((t, hkv, dh), **f32)
+    dv = torch.empty((t, hkv, dh), **f32)
+    db = torch.empty(t, **f32)
+    dgain = torch.empty(hq, **f32)
+    dtemp = torch.empty(hq, **f32)
+    nbytes = lib.tg_gated_attn_bwd_workspace_size(t, n_seq, hq, hkv)
+    if ws is None:
+        ws = workspace(nbytes, q.device)
+    st = lib.tg_gated_attn_bwd(_p(q), _p(k), _p(v), _p(dout), _DT[q.dtype], t, _p(kept_b),
+                               _p(kept_pos), _p(kept_cu), n_seq, hq, hkv, dh, _p(gain), _p(temp),
+                               float(sm_scale or 0.0), _p(dq), _p(dk), _p(dv), _p(db), _p(dgain),
+                               _p(dtemp), _p(ws), ws.numel() * ws.element_size(),
+                               _stream(q.device))
+    check("tg_gated_attn_bwd", st)
+    return dq, dk, dv, db, dgain, dtemp
+
+
 def gated_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  cache_b: Optional[torch.Tensor], q_pos: Optional[torch.Tensor],
                  cache_cu: torch.Tensor, gain: torch.Tensor, temp: torch.Tensor,

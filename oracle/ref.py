@@ -391,7 +391,7 @@ def ref_gated_attn_bruteforce(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
 # ---------------------------------------------------------------------------
 def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
                        sm_scale: Optional[float] = None, len_scale: str = R.LEN_SCALE,
-                       row_block: int = 512):
+                       row_block: int = 512, error_scales: bool = False):
     """Gradients of L = sum(O * dout) through the token-gated attention of
     [TG] Eq. 8 (gain of Eq. 6, temperature of Eq. 7), by the chain rule on
 
@@ -412,6 +412,13 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
     gradient.  Query rows are processed in blocks of ``row_block``.
     Returns (dq [T,Hq,dh], dk [T,Hkv,dh], dv [T,Hkv,dh], db [T], dgain [Hq],
     dtemp [Hq]), float64.
+
+    dgain and dtemp sum terms of both signs over every (query, key) pair
+    (each row of dl sums to zero).  With ``error_scales`` the function also
+    returns, per head, the sums over the pairs of |weight| * P (|dP| + |D|)
+    (weight tau b for gain, lambda z for temperature): a rounding error of
+    relative size u in dP or D moves each sum by at most u times that scale,
+    which is what a tolerance for a finite-precision result is measured by.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -425,6 +432,7 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     db = np.zeros(T)
     dgain, dtemp = np.zeros(Hq), np.zeros(Hq)
+    sgain, stemp = np.zeros(Hq), np.zeros(Hq)
     for s in range(len(kept_cu) - 1):
         lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
         n = hi - lo
@@ -458,6 +466,12 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
                 dgain[h] += float(np.sum(tdl * kb[lo:lo + last][None, :]))
                 zc = np.where(causal, z, 0.0)
                 dtemp[h] += float(np.sum(lam[rr][:, None] * zc * dl))
+                if error_scales:
+                    sens = P * (np.abs(dP) + np.abs(np.sum(P * dP, axis=1, keepdims=True)))
+                    sgain[h] += float(np.sum(np.abs(tau[:, None] * kb[lo:lo + last][None, :]) * sens))
+                    stemp[h] += float(np.sum(np.abs(lam[rr][:, None] * zc) * sens))
+    if error_scales:
+        return dq, dk, dv, db, dgain, dtemp, sgain, stemp
     return dq, dk, dv, db, dgain, dtemp
 
 

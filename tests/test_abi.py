@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10200
+    assert lib.tg_version() == 10300
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -204,4 +204,28 @@ def test_gated_decode_validation(lib):
     assert dc(ws_bytes=100) == 3                       # short workspace
     assert dc(q=ctypes.c_void_p(0x10008)) == 2         # misaligned q
     assert dc(n_seq=70000, ws_bytes=1 << 40) == 2
+
+
+def test_gated_attn_bwd_validation(lib):
+    ws_size = lib.tg_gated_attn_bwd_workspace_size
+    # f32 lse and D per (row, head) and b gradient per (KV head, row), 2 slack floats for
+    # alignment, f64 gain / temperature partials per (query tile, head)
+    assert ws_size(1000, 2, 16, 8) == 4 * (2 * 1000 * 16 + 1000 * 8 + 2) + 8 * (2 + 16) * 16 * 2
+    assert ws_size(-1, 1, 16, 8) == 0
+
+    def bw(dt=1, t=100, n_seq=1, hq=16, hkv=8, dh=128, q=FAKE, gain=FAKE, ws=FAKE,
+           ws_bytes=1 << 30, dq=FAKE):
+        return lib.tg_gated_attn_bwd(q, FAKE, FAKE, FAKE, dt, t, FAKE, None, FAKE, n_seq, hq, hkv,
+                                     dh, gain, FAKE, 0.0, dq, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                     ws_bytes, None)
+    assert bw(t=-1) == 1
+    assert bw(n_seq=0) == 1
+    assert bw(hq=16, hkv=6) == 1
+    assert bw(dt=5) == 1
+    assert bw(dh=96) == 2
+    assert bw(gain=None) == 1
+    assert bw(ws=None) == 1
+    assert bw(dq=None) == 1
+    assert bw(ws_bytes=64) == 3
+    assert bw(q=ctypes.c_void_p(0x10008)) == 2
 

@@ -1,0 +1,119 @@
+"""tg_gated_attn_bwd against the oracle's backward (ref_gated_attn_bwd, fp64,
+pinned by central differences and torch autograd).
+
+The kernels compute in fp32 for both input dtypes and return fp32
+gradients, so the oracle is fed exactly the values the kernel reads (bf16
+inputs rounded the same way) and the bar is an fp32 one.  For dq, dk, dv and
+db the rel-L2 bar is 1e-5: fp32 products and sums over <= 2^12 terms, with
+the cancellation in dl = P (dP - D), measure below 1.6e-6, so the bar keeps a
+margin of about 6.  dgain and dtemp are sums of terms of both signs over every
+(query, key) pair of a head, so their bar is relative to the oracle's error
+scale for that sum (the sum of |weight| P (|dP| + |D|) over the pairs) plus
+the value itself: |got - ref| <= 1e-5 (|ref| + scale)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import bf16_dev, f32_dev, i32_dev, rel_l2, round_bf16, say
+from workloads import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+NAMES = ("dq", "dk", "dv", "db", "dgain", "dtemp")
+
+
+def bwd_case(seed, lens, hq, hkv, dh, dtype, with_pos=True):
+    rng = np.random.default_rng(seed)
+    kc = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(kc[-1])
+
+    def grid(shape, scale=1.0):
+        a = rng.standard_normal(shape) * scale
+        if dtype == "bf16":
+            return bf16_to_f64(round_bf16(a))
+        return a.astype(np.float32).astype(np.float64)
+    q, k, v = grid((T, hq, dh)), grid((T, hkv, dh)), grid((T, hkv, dh))
+    do = grid((T, hq, dh), 0.5)
+    kb = rng.standard_normal(T).astype(np.float32).astype(np.float64)
+    pos = np.zeros(T, np.int64)
+    for s, n in enumerate(lens):
+        if n:
+            pos[kc[s]:kc[s + 1]] = np.cumsum(rng.integers(1, 6, n)) - 1
+            kb[kc[s + 1] - min(8, n):kc[s + 1]] = 0.0         # prompt tokens carry b = 0
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    temp = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    return q, k, v, do, kb, (pos if with_pos else None), kc, gain, temp
+
+
+def run_bwd(q, k, v, do, kb, pos, kc, gain, temp, dtype):
+    from learned_token_pruning_06_amd import ops
+    if dtype == "bf16":
+        dev = [bf16_dev(round_bf16(a)) for a in (q, k, v, do)]
+    else:
+        dev = [f32_dev(a) for a in (q, k, v, do)]
+    out = ops.gated_attn_bwd(*dev, f32_dev(kb), None if pos is None else i32_dev(pos),
+                             i32_dev(kc), f32_dev(gain), f32_dev(temp))
+    torch.cuda.synchronize()
+    return [t.cpu().numpy().astype(np.float64) for t in out]
+
+
+def check(case, dtype, tol=TOL):
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    got = run_bwd(*case, dtype)
+    *ref, sgain, stemp = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do,
+                                              error_scales=True)
+    scale = {"dgain": sgain, "dtemp": stemp}
+    errs = {}
+    for name, g, r in zip(NAMES, got, ref):
+        if name in scale:
+            errs[name] = float(np.max(np.abs(g - r) / (np.abs(r) + scale[name])))
+        else:
+            errs[name] = rel_l2(g, r)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e <= tol, f"{name}: {e:.3e} > {tol}"
+    return got, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dh,hq,hkv", [(128, 16, 8), (64, 4, 2), (128, 8, 8), (64, 16, 2)])
+def test_bwd_matches_oracle(dtype, dh, hq, hkv):
+    lens = [1, 5, 31, 32, 33, 64, 65, 130]
+    say(f"attn bwd {dtype} dh={dh} hq={hq} hkv={hkv} lens={lens}")
+    check(bwd_case(100 + dh + hq + hkv, lens, hq, hkv, dh, dtype), dtype)
+
+
+def test_bwd_without_positions():
+    say("attn bwd: kept_pos = NULL (length factor 1)")
+    check(bwd_case(7, [40, 97], 16, 8, 128, "f32", with_pos=False), "f32")
+
+
+def test_bwd_invariants_on_the_gpu():
+    """The score gradient sums to zero over each sequence (a constant shift of
+    b cancels in every row's softmax); dv summed over the keys of a sequence
+    equals dout summed over its queries and the query heads of the KV head."""
+    case = bwd_case(8, [300, 1, 77], 16, 8, 128, "f32")
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    dq, dk, dv, db, dg, dt = run_bwd(*case, "f32")
+    for s in range(3):
+        lo, hi = kc[s], kc[s + 1]
+        assert abs(db[lo:hi].sum()) <= 1e-5 * max(1.0, np.abs(db[lo:hi]).sum())
+        for kvh in range(8):
+            want = do[lo:hi, 2 * kvh:2 * kvh + 2].sum(axis=(0, 1))
+            assert np.allclose(dv[lo:hi, kvh].sum(axis=0), want, rtol=1e-4, atol=1e-4)
+
+
+def test_bwd_deterministic():
+    case = bwd_case(9, [500, 260], 16, 8, 128, "bf16")
+    a, b = run_bwd(*case, "bf16"), run_bwd(*case, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_16k_layer_kept_tokens():
+    """The kept rows of the 16k-token gated layer (1984 kept document tokens
+    + 512 prompt tokens), bf16 inputs."""
+    say("attn bwd: 2496 kept rows, 16q/8kv, dh 128, bf16")
+    check(bwd_case(10, [2496], 16, 8, 128, "bf16"), "bf16")
