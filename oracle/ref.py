@@ -476,6 +476,57 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
 
 
 # ---------------------------------------------------------------------------
+# backward of the gate's scorer ([TG] §4.1 Eq. 3 read backwards: the gradient
+# that reaches the kept scores b through the attention flows on to the
+# scoring network's weights)
+# ---------------------------------------------------------------------------
+def ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db_kept,
+                  eps: float = R.EPS):
+    """Gradients of L = sum_r db_kept[r] * b[kept_idx[r]] w.r.t. the scorer's
+    input rows and parameters, by the chain rule through Eq. 3:
+
+      normalisation, per sequence s with prunable set P and
+      r = sqrt(mean_P b~^2 + eps), C = sum_{j in P} db_j b~_j:
+        db~_k = db_k / r - b~_k C / (|P| r^3)      for k in P
+        db~_k = 0                                   for prompt tokens (b := 0)
+      (db_j is db_kept at kept tokens and 0 at pruned ones: the selection
+      passes no gradient, and pruned tokens still feel r.)
+      scorer, z = W1 x + b1, u = SiLU(z), b~ = w2 . u + b2:
+        dz = db~ w2 * SiLU'(z),  SiLU'(z) = sigma(z) (1 + z (1 - sigma(z)))
+        dW1 = sum_j dz_j x_j^T,  db1 = sum_j dz_j,  dw2 = sum_j db~_j u_j,
+        db2 = sum_j db~_j,       dx_j = W1^T dz_j.
+
+    x [T, d], w1 [h, d], b1 [h] or None, w2 [h], b2 scalar; kept_idx,
+    kept_cu, db_kept as returned by the selector and the attention's backward.
+    Returns (dx [T, d], dw1 [h, d], db1 [h], dw2 [h], db2), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    T = x.shape[0]
+    pre = x @ w1.T
+    if b1 is not None:
+        pre = pre + np.asarray(b1, dtype=np.float64)[None, :]
+    sig = 1.0 / (1.0 + np.exp(-pre))
+    u = pre * sig
+    b_raw = u @ w2 + float(b2)
+    db = np.zeros(T)
+    db[np.asarray(kept_idx, dtype=np.int64)] = np.asarray(db_kept, dtype=np.float64)
+    prunable = np.asarray(prunable).astype(bool)
+    dbt = np.zeros(T)
+    for s in range(len(cu_seqlens) - 1):
+        lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        P = np.nonzero(prunable[lo:hi])[0] + lo
+        if P.size == 0:
+            continue
+        r = math.sqrt(np.mean(b_raw[P] ** 2) + eps)
+        C = float(np.sum(db[P] * b_raw[P]))
+        dbt[P] = db[P] / r - b_raw[P] * C / (P.size * r ** 3)
+    dz = dbt[:, None] * w2[None, :] * sig * (1.0 + pre * (1.0 - sig))
+    return dz @ w1, dz.T @ x, dz.sum(axis=0), u.T @ dbt, float(dbt.sum())
+
+
+# ---------------------------------------------------------------------------
 # harness-level projection (outside the four library calls)
 # ---------------------------------------------------------------------------
 def ref_project(xs: np.ndarray, wq, wk, wv, hq: int, hkv: int, dh: int):

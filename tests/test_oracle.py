@@ -592,3 +592,75 @@ def test_attn_bwd_invariants():
     again = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do, row_block=3)
     for a, b in zip(again, (dq, dk, dv, db, dg, dt)):
         assert np.allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# backward of the scorer (Eq. 3 through the normalisation and the MLP)
+# ---------------------------------------------------------------------------
+def _score_bwd_case(seed, lens=(9, 7), d=6, h=5):
+    rng = _rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((h, d)) / math.sqrt(d)
+    b1 = 0.1 * rng.standard_normal(h)
+    w2 = rng.standard_normal(h) / math.sqrt(h)
+    pr = np.ones(T, np.uint8)
+    for s in range(len(lens)):
+        pr[cu[s + 1] - 2:cu[s + 1]] = 0                   # two prompt tokens per sequence
+    k = [3, 2, 4][:len(lens)]
+    raw = O.ref_score(x, w1, b1, w2, 0.2)
+    b, _ = O.ref_normalise(raw, pr, cu, 1e-6)
+    kept_idx, _, _, kept_cu = O.ref_select(b, pr, cu, k)
+    db_kept = rng.standard_normal(len(kept_idx))
+    return x, w1, b1, w2, pr, cu, kept_idx, kept_cu, db_kept
+
+
+def _score_loss(x, w1, b1, w2, b2, pr, cu, kept_idx, db_kept):
+    b, _ = O.ref_normalise(O.ref_score(x, w1, b1, w2, b2), pr, cu, 1e-6)
+    return float(np.sum(np.asarray(db_kept) * b[np.asarray(kept_idx)]))
+
+
+def test_score_bwd_matches_central_differences():
+    """The kept set is held fixed (selection passes no gradient); the loss is
+    sum_r db_kept[r] * b[kept_idx[r]], and every pruned token still enters
+    through the sequence's normaliser."""
+    x, w1, b1, w2, pr, cu, ki, kc, dbk = _score_bwd_case(60)
+    dx, dw1, db1, dw2, db2 = O.ref_score_bwd(x, w1, b1, w2, 0.2, pr, cu, ki, kc, dbk, eps=1e-6)
+    base = dict(x=x, w1=w1, b1=b1, w2=w2)
+    grads = dict(x=dx, w1=dw1, b1=db1, w2=dw2)
+    rng = _rng(61)
+    e = 1e-6
+    for name, g in grads.items():
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in np.shape(base[name]))
+            vals = []
+            for sgn in (1, -1):
+                a = {n: np.array(v, copy=True) for n, v in base.items()}
+                a[name][idx] += sgn * e
+                vals.append(_score_loss(a["x"], a["w1"], a["b1"], a["w2"], 0.2, pr, cu, ki, dbk))
+            fd = (vals[0] - vals[1]) / (2 * e)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+    # b2 shifts every raw score of a sequence equally, which the RMS does not cancel
+    fd = (_score_loss(x, w1, b1, w2, 0.2 + e, pr, cu, ki, dbk)
+          - _score_loss(x, w1, b1, w2, 0.2 - e, pr, cu, ki, dbk)) / (2 * e)
+    assert abs(fd - db2) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_score_bwd_matches_torch_autograd_fp64():
+    x, w1, b1, w2, pr, cu, ki, kc, dbk = _score_bwd_case(62, lens=(12, 5, 9), d=8, h=4)
+    tx, tw1, tb1, tw2 = (torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                         for a in (x, w1, b1, w2))
+    tb2 = torch.tensor(0.2, dtype=torch.float64, requires_grad=True)
+    raw = torch.nn.functional.silu(tx @ tw1.T + tb1) @ tw2 + tb2
+    parts = []
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        m = torch.tensor(pr[lo:hi].astype(bool))
+        rs = torch.sqrt(torch.mean(raw[lo:hi][m] ** 2) + 1e-6)
+        parts.append(torch.where(m, raw[lo:hi] / rs, torch.zeros_like(raw[lo:hi])))
+    b = torch.cat(parts)
+    (b[torch.tensor(ki)] * torch.tensor(dbk)).sum().backward()
+    got = O.ref_score_bwd(x, w1, b1, w2, 0.2, pr, cu, ki, kc, dbk, eps=1e-6)
+    for g, t in zip(got, (tx, tw1, tb1, tw2, tb2)):
+        assert np.allclose(g, t.grad.numpy(), rtol=1e-11, atol=1e-12)
