@@ -284,6 +284,19 @@ def main():
                         "recomputed in 3 passes (18 dh flop per pair done)"}
     del dout, ws_b
 
+    # the scorer's backward (tg_score_bwd) from a gradient at the kept scores:
+    # recompute z, then dW1 and dx (3 products of 2 d h flop per token)
+    db_k = torch.randn(t_kept, dtype=torch.float32, device=dev)
+    ws_sb = ops.workspace(lib.tg_score_bwd_workspace_size(T, 1, wl.d, wl.h), dev)
+    t_sbwd = time_it(lambda: ops.score_bwd(x, w1, w2, pr, cu, b_raw, kept_idx, kept_cu, db_k,
+                                           b1=b1, ws=ws_sb), reps=2)
+    sbwd_flops = 3 * 2.0 * T * wl.d * wl.h
+    score_bwd = {"kernel": "tg_score_bwd", "us": round(t_sbwd, 1),
+                 "tflops": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12, 2), "bound": "alu",
+                 "frac_of_fp32_peak": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                 "note": "131072 tokens, d 2048, h 256, bf16 rows, fp32 arithmetic; dx included"}
+    del db_k, ws_sb
+
     # one decode step after the prefill (tg_gated_decode): the new token's
     # query against the pruned cache of this layer (the kept rows' K/V plus
     # the token itself).  The calls are replayed from a HIP graph so that the
@@ -388,6 +401,7 @@ def main():
         "decode": decode,
         "score_ln2": score_ln2,
         "attn_bwd": attn_bwd,
+        "score_bwd": score_bwd,
     }
     print(json.dumps(out), flush=True)
 

@@ -8,7 +8,7 @@
  *   tg_gated_attn   token-gated causal attention over the kept tokens
  * and, between the last two, tg_qkv_proj, the projections of the kept rows;
  * tg_gated_decode runs one decode step over the pruned caches afterwards;
- * tg_gated_attn_bwd gives the attention's gradients for training.
+ * tg_gated_attn_bwd and tg_score_bwd give the gradients for training.
  * Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill
  * with Learned Token Pruning", §4.1 (Eq. 3-4) and §4.2 (Eq. 5-8).
  *
@@ -219,6 +219,40 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
                             const float* gain, const float* temp, float sm_scale, float* dq,
                             float* dk, float* dv, float* db, float* dgain, float* dtemp,
                             void* ws, size_t ws_bytes, tg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tg_score_bwd -- gradients of the gate's scorer (§4.1 Eq. 3) from the
+ * gradient that reaches the kept scores through the attention (§4.3), for
+ * L = sum_r db_kept[r] * b[kept_idx[r]] with the kept set held fixed (the
+ * selection passes no gradient).  Per sequence, with P its prunable tokens,
+ * r = sqrt(mean_P b~^2 + eps) and C = sum over kept prunable j of db_j b~_j:
+ *
+ *   db~_k = [k kept] db_k / r - b~_k C / (|P| r^3)  (k in P; 0 on prompt tokens)
+ *   dz_k  = db~_k w2 * SiLU'(W1 x_k + b1)
+ *   dW1 = sum_k dz_k x_k^T   db1 = sum_k dz_k   dw2 = sum_k db~_k SiLU(z_k)
+ *   db2 = sum_k db~_k        dx_k = W1^T dz_k
+ *
+ * x, dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable, cu_seqlens, n_seq,
+ *   eps: as for tg_score (plain rows: the LN2-fused form has no backward).
+ * b_raw    dev [t_in] f32: b~ of the forward (tg_score's b_raw output).
+ * kept_idx, kept_cu_seqlens dev: tg_select_topk's outputs; t_kept rows.
+ * db_kept  dev [t_kept] f32: gradient w.r.t. the kept scores (the db of
+ *          tg_gated_attn_bwd, or any other).
+ * dx       dev [t_in, d] f32 out, or NULL to skip it.
+ * dw1 dev [h, d] f32 out; db1, dw2 dev [h] f32 out; db2 dev [1] f32 out.
+ * ws       dev workspace of >= tg_score_bwd_workspace_size(t_in, n_seq, d, h)
+ *          bytes, 256-byte aligned (it holds dz, [t_in, h] f32).
+ * fp32 arithmetic on the vector ALU, fixed reduction orders (bitwise
+ * reproducible).  Supported: d % 64 == 0, h % 64 == 0.
+ * ---------------------------------------------------------------------- */
+size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32_t h);
+tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
+                       int32_t h, const void* w1, const float* b1, const float* w2,
+                       const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq,
+                       float eps, const float* b_raw, const int32_t* kept_idx,
+                       const int32_t* kept_cu_seqlens, int64_t t_kept, const float* db_kept,
+                       float* dx, float* dw1, float* db1, float* dw2, float* db2, void* ws,
+                       size_t ws_bytes, tg_stream stream);
 
 /* ------------------------------------------------------------------------
  * tg_qkv_proj -- query, key and value projections of the kept rows: the

@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10300; }
+int tg_version(void) { return 10400; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -292,6 +292,44 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
                                      n_seq, hq, hkv, dh, gain, temp, sm_scale, dq, dk, dv, db,
                                      dgain, dtemp, ws, (hipStream_t)stream);
   return from_hip(e, "tg_gated_attn_bwd launch");
+}
+
+// ---------------------------------------------------------- scorer backward
+size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32_t h) {
+  if (t_in < 0 || n_seq < 1 || d < 1 || h < 1) return 0;
+  return tg::score_bwd_ws_bytes(t_in, n_seq, d, h);
+}
+
+tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
+                       int32_t h, const void* w1, const float* b1, const float* w2,
+                       const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq,
+                       float eps, const float* b_raw, const int32_t* kept_idx,
+                       const int32_t* kept_cu, int64_t t_kept, const float* db_kept, float* dx,
+                       float* dw1, float* db1, float* dw2, float* db2, void* ws, size_t ws_bytes,
+                       tg_stream stream) {
+  if (t_in < 0 || t_kept < 0 || n_seq < 1 || d < 1 || h < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: bad sizes");
+  if (!(eps >= 0.0f)) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: eps must be >= 0");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: bad dtype");
+  if (x_row_stride < d) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: x_row_stride < d");
+  if (d % 64 != 0 || h % 64 != 0)
+    return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: needs d %% 64 == 0 and h %% 64 == 0");
+  if (t_in > INT32_MAX - 4096 || t_kept > t_in)
+    return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: sizes too large");
+  if (!cu_seqlens || !kept_cu || !w2 || !dw1 || !db1 || !dw2 || !db2 || !ws)
+    return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: null pointer");
+  if (t_in > 0 && (!x || !w1 || !prunable || !b_raw))
+    return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: null pointer");
+  if (t_kept > 0 && (!kept_idx || !db_kept))
+    return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: null pointer");
+  const size_t need = tg::score_bwd_ws_bytes(t_in, n_seq, d, h);
+  if (ws_bytes < need)
+    return fail(TG_ERR_WORKSPACE, "tg_score_bwd: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: ws must be 256-byte aligned");
+  hipError_t e = tg::launch_score_bwd(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable,
+                                      cu_seqlens, n_seq, eps, b_raw, kept_idx, kept_cu, t_kept,
+                                      db_kept, dx, dw1, db1, dw2, db2, ws, (hipStream_t)stream);
+  return from_hip(e, "tg_score_bwd launch");
 }
 
 }  // extern "C"

@@ -148,6 +148,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
                          const float* gain, const float* temp, float sm_scale, void* ws,
                          hipStream_t st);
 
+size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h);
+hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
+                            const void* w1, const float* b1, const float* w2, const uint8_t* pr,
+                            const int32_t* cu, int n_seq, float eps, const float* b_raw,
+                            const int32_t* kept_idx, const int32_t* kept_cu, int64_t t_kept,
+                            const float* db_kept, float* dx, float* dw1, float* db1, float* dw2,
+                            float* db2, void* ws, hipStream_t st);
+
 size_t attn_bwd_ws_bytes(int64_t t, int n_seq, int hq, int hkv);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dt,
                            int64_t t, const float* kept_b, const int32_t* kept_pos,

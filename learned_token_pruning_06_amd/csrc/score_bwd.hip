@@ -1,0 +1,416 @@
+// tg_score_bwd: gradients of the gate's scorer (TokenGate §4.1 Eq. 3) from
+// the gradient that reaches the kept scores b through the attention (§4.3).
+// Per sequence, with prunable set P, r = sqrt(mean_P b~^2 + eps) and
+// C = sum_{kept j in P} db_j b~_j:
+//   db~_k = [k kept] db_k / r - b~_k C / (|P| r^3)   (k in P; 0 on prompt tokens)
+// then through z = W1 x + b1, u = SiLU(z), b~ = w2 . u + b2:
+//   dz = db~ w2 SiLU'(z),  dW1 = sum_j dz_j x_j^T,  dx_j = W1^T dz_j,
+//   db1 = sum_j dz_j,      dw2 = sum_j db~_j u_j,    db2 = sum_j db~_j.
+//
+// fp32 on the vector ALU, seven launches, fixed reduction orders:
+//   sbwd_seq    per sequence: r, |P| and C (fp64 sums) -> 1/r and C/(|P| r^3)
+//   sbwd_dbt    per token: the normaliser term (every prunable token)
+//   sbwd_kept   per kept row: adds db / r at its token
+//   sbwd_dz     per 64 tokens x 64 hidden units: recomputes z (K = d), writes
+//               dz and the block's dw2, db1, db2 partial sums
+//   sbwd_dw1    per 64 hidden x 64 input columns and token split: dz^T x
+//   sbwd_dx     per 64 tokens x 64 input columns: dz W1 (K = h)
+//   sbwd_finish sums the partials.
+// The products are register-blocked micro-GEMMs over padded fp32 LDS tiles,
+// each thread owning 4 x 4 outputs (rows 4ty + r, columns tx + 16c).
+#include "common.h"
+
+namespace tg {
+namespace {
+
+constexpr int kThr = 256;
+constexpr int kT = 64;              // output tile edge
+constexpr int kKC = 32;             // reduction chunk
+constexpr int kSplitMax = 8;        // token splits of dW1
+
+TG_DEVINL float ldf(const float* p) { return *p; }
+TG_DEVINL float ldf(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+
+TG_DEVINL int seq_of_row(const int32_t* cu, int n_seq, int64_t row) {
+  int lo = 0, hi = n_seq - 1, ans = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) {
+      ans = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return ans;
+}
+
+// ---- per sequence: 1/r and C / (|P| r^3)
+__global__ __launch_bounds__(kThr) void sbwd_seq(const float* __restrict__ b_raw,
+                                                 const uint8_t* __restrict__ pr,
+                                                 const int32_t* __restrict__ cu,
+                                                 const int32_t* __restrict__ kept_idx,
+                                                 const int32_t* __restrict__ kept_cu,
+                                                 const float* __restrict__ db_kept, int64_t t,
+                                                 int64_t t_kept, float eps,
+                                                 float2* __restrict__ seqc) {
+  __shared__ double s1[kThr / 64], s2[kThr / 64];
+  __shared__ int64_t sn[kThr / 64];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int64_t lo = cu[s] < t ? cu[s] : t, hi = cu[s + 1] < t ? cu[s + 1] : t;
+  const int64_t klo = kept_cu[s] < t_kept ? kept_cu[s] : t_kept;
+  const int64_t khi = kept_cu[s + 1] < t_kept ? kept_cu[s + 1] : t_kept;
+  double sq = 0.0, c = 0.0;
+  int64_t n = 0;
+  for (int64_t j = lo + tid; j < hi; j += kThr)
+    if (pr[j]) {
+      const double v = b_raw[j];
+      sq = fma(v, v, sq);
+      ++n;
+    }
+  for (int64_t r = klo + tid; r < khi; r += kThr) {
+    const int64_t j = kept_idx[r];
+    if (j >= 0 && j < t && pr[j]) c = fma((double)db_kept[r], (double)b_raw[j], c);
+  }
+  sq = wave_sum(sq);
+  c = wave_sum(c);
+  n = wave_sum(n);
+  if ((tid & 63) == 0) {
+    s1[tid >> 6] = sq;
+    s2[tid >> 6] = c;
+    sn[tid >> 6] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double SQ = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+    const double CC = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+    const int64_t N = sn[0] + sn[1] + sn[2] + sn[3];
+    float2 out = make_float2(0.0f, 0.0f);
+    if (N > 0) {
+      const double r = sqrt(SQ / (double)N + (double)eps);
+      out = make_float2((float)(1.0 / r), (float)(CC / ((double)N * r * r * r)));
+    }
+    seqc[s] = out;
+  }
+}
+
+// ---- per token: db~ = -b~ C / (|P| r^3) on prunable tokens, 0 elsewhere
+__global__ __launch_bounds__(kThr) void sbwd_dbt(const float* __restrict__ b_raw,
+                                                 const uint8_t* __restrict__ pr,
+                                                 const int32_t* __restrict__ cu, int n_seq,
+                                                 int64_t t, const float2* __restrict__ seqc,
+                                                 float* __restrict__ dbt) {
+  const int64_t j = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (j >= t) return;
+  const int s = seq_of_row(cu, n_seq, j);
+  const bool in = s >= 0 && j < cu[s + 1];
+  dbt[j] = (in && pr[j]) ? -b_raw[j] * seqc[s].y : 0.0f;
+}
+
+// ---- per kept row: db~ += db / r at the kept token (prunable only: b := 0 on prompts)
+__global__ __launch_bounds__(kThr) void sbwd_kept(const uint8_t* __restrict__ pr,
+                                                  const int32_t* __restrict__ kept_idx,
+                                                  const int32_t* __restrict__ kept_cu, int n_seq,
+                                                  int64_t t, int64_t t_kept,
+                                                  const float* __restrict__ db_kept,
+                                                  const float2* __restrict__ seqc,
+                                                  float* __restrict__ dbt) {
+  const int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (r >= t_kept) return;
+  const int s = seq_of_row(kept_cu, n_seq, r);
+  if (s < 0 || r >= kept_cu[s + 1]) return;
+  const int64_t j = kept_idx[r];
+  if (j >= 0 && j < t && pr[j]) dbt[j] = fmaf(db_kept[r], seqc[s].x, dbt[j]);
+}
+
+// ---- dz for 64 tokens x 64 hidden units; z recomputed over d
+template <typename T>
+__global__ __launch_bounds__(kThr) void sbwd_dz(const T* __restrict__ x, int64_t xs, int64_t t,
+                                                int d, int h, const T* __restrict__ w1,
+                                                const float* __restrict__ b1,
+                                                const float* __restrict__ w2,
+                                                const float* __restrict__ dbt,
+                                                float* __restrict__ dz, float* __restrict__ dw2p,
+                                                float* __restrict__ db1p,
+                                                float* __restrict__ db2p) {
+  constexpr int LD = kKC + 4;
+  __shared__ __attribute__((aligned(16))) float sx[kT * LD], sw[kT * LD];
+  __shared__ float sred[2][16][kT];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int64_t j0 = (int64_t)blockIdx.x * kT;
+  const int h0 = blockIdx.y * kT;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += kKC) {
+    __syncthreads();
+    for (int u = tid; u < kT * kKC; u += kThr) {
+      const int r = u / kKC, c = u % kKC;
+      sx[r * LD + c] = j0 + r < t ? ldf(x + (j0 + r) * xs + k0 + c) : 0.0f;
+      sw[r * LD + c] = ldf(w1 + (int64_t)(h0 + r) * d + k0 + c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kKC; k += 4) {
+      float4 a[4], b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = *reinterpret_cast<const float4*>(sx + (4 * ty + r) * LD + k);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] = *reinterpret_cast<const float4*>(sw + (tx + 16 * c) * LD + k);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float v = acc[r][c];
+          v = fmaf(a[r].x, b[c].x, v);
+          v = fmaf(a[r].y, b[c].y, v);
+          v = fmaf(a[r].z, b[c].z, v);
+          acc[r][c] = fmaf(a[r].w, b[c].w, v);
+        }
+    }
+  }
+  float pu[4] = {0.f, 0.f, 0.f, 0.f}, pz[4] = {0.f, 0.f, 0.f, 0.f};   // per hidden column c
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t j = j0 + 4 * ty + r;
+    const float g = j < t ? dbt[j] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int hid = h0 + tx + 16 * c;
+      const float z = acc[r][c] + (b1 ? b1[hid] : 0.0f);
+      const float sg = 1.0f / (1.0f + expf(-z));
+      const float dzv = g * w2[hid] * sg * fmaf(z, 1.0f - sg, 1.0f);
+      if (j < t) dz[j * h + hid] = dzv;
+      pu[c] = fmaf(g, z * sg, pu[c]);
+      pz[c] += dzv;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    sred[0][ty][tx + 16 * c] = pu[c];
+    sred[1][ty][tx + 16 * c] = pz[c];
+  }
+  __syncthreads();
+  if (tid < kT) {
+    float a = 0.0f, b = 0.0f;
+    for (int y = 0; y < 16; ++y) {
+      a += sred[0][y][tid];
+      b += sred[1][y][tid];
+    }
+    dw2p[(int64_t)blockIdx.x * h + h0 + tid] = a;
+    db1p[(int64_t)blockIdx.x * h + h0 + tid] = b;
+  }
+  if (blockIdx.y == 0 && tid == 64) {
+    float a = 0.0f;
+    for (int r = 0; r < kT; ++r) a += j0 + r < t ? dbt[j0 + r] : 0.0f;
+    db2p[blockIdx.x] = a;
+  }
+}
+
+// ---- dW1 partial of one token split: [64 hidden x 64 columns] += dz^T x
+template <typename T>
+__global__ __launch_bounds__(kThr) void sbwd_dw1(const T* __restrict__ x, int64_t xs, int64_t t,
+                                                 int d, int h, const float* __restrict__ dz,
+                                                 int64_t per_split, float* __restrict__ dw1p) {
+  constexpr int LD = kT + 4;
+  __shared__ __attribute__((aligned(16))) float sz[kKC * LD], sx[kKC * LD];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int h0 = blockIdx.x * kT, c0 = blockIdx.y * kT;
+  const int64_t jb = (int64_t)blockIdx.z * per_split;
+  const int64_t je = jb + per_split < t ? jb + per_split : t;
+  float acc[4][4] = {};
+  for (int64_t j0 = jb; j0 < je; j0 += kKC) {
+    __syncthreads();
+    for (int u = tid; u < kKC * kT; u += kThr) {
+      const int r = u / kT, c = u % kT;
+      const bool ok = j0 + r < je;
+      sz[r * LD + c] = ok ? dz[(j0 + r) * h + h0 + c] : 0.0f;
+      sx[r * LD + c] = ok ? ldf(x + (j0 + r) * xs + c0 + c) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < kKC; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(sz + k * LD + 4 * ty);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float b = sx[k * LD + tx + 16 * c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r][c] = fmaf(av[r], b, acc[r][c]);
+      }
+    }
+  }
+  float* out = dw1p + (int64_t)blockIdx.z * h * d;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[(int64_t)(h0 + 4 * ty + r) * d + c0 + tx + 16 * c] = acc[r][c];
+}
+
+// ---- dx for 64 tokens x 64 columns: dz W1 over the hidden units
+template <typename T>
+__global__ __launch_bounds__(kThr) void sbwd_dx(int64_t t, int d, int h, const T* __restrict__ w1,
+                                                const float* __restrict__ dz,
+                                                float* __restrict__ dx) {
+  constexpr int LDZ = kT + 4, LDW = kT + 4;
+  __shared__ __attribute__((aligned(16))) float szt[kKC * LDZ], sw[kKC * LDW];
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int64_t j0 = (int64_t)blockIdx.x * kT;
+  const int c0 = blockIdx.y * kT;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < h; k0 += kKC) {
+    __syncthreads();
+    for (int u = tid; u < kKC * kT; u += kThr) {
+      const int r = u / kKC, k = u % kKC;          // token r, hidden k0 + k (transposed store)
+      szt[k * LDZ + r] = j0 + r < t ? dz[(j0 + r) * h + k0 + k] : 0.0f;
+      const int kk = u / kT, c = u % kT;
+      sw[kk * LDW + c] = ldf(w1 + (int64_t)(k0 + kk) * d + c0 + c);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < kKC; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(szt + k * LDZ + 4 * ty);
+      const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float b = sw[k * LDW + tx + 16 * c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r][c] = fmaf(av[r], b, acc[r][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t j = j0 + 4 * ty + r;
+    if (j < t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dx[j * d + c0 + tx + 16 * c] = acc[r][c];
+  }
+}
+
+// ---- sums of the partials
+__global__ __launch_bounds__(kThr) void sbwd_finish(int64_t hd, int h, int n_split, int64_t n_tb,
+                                                    const float* __restrict__ dw1p,
+                                                    const float* __restrict__ dw2p,
+                                                    const float* __restrict__ db1p,
+                                                    const float* __restrict__ db2p,
+                                                    float* __restrict__ dw1,
+                                                    float* __restrict__ dw2,
+                                                    float* __restrict__ db1,
+                                                    float* __restrict__ db2) {
+  const int64_t nb = (hd + kThr - 1) / kThr;
+  if (blockIdx.x < nb) {
+    const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
+    if (e < hd) {
+      float a = 0.0f;
+      for (int sp = 0; sp < n_split; ++sp) a += dw1p[sp * hd + e];
+      dw1[e] = a;
+    }
+    return;
+  }
+  for (int hid = threadIdx.x; hid < h; hid += kThr) {
+    float a = 0.0f, b = 0.0f;
+    for (int64_t blk = 0; blk < n_tb; ++blk) {
+      a += dw2p[blk * h + hid];
+      b += db1p[blk * h + hid];
+    }
+    dw2[hid] = a;
+    db1[hid] = b;
+  }
+  if (threadIdx.x == 0) {
+    float a = 0.0f;
+    for (int64_t blk = 0; blk < n_tb; ++blk) a += db2p[blk];
+    *db2 = a;
+  }
+}
+
+struct Layout {
+  int64_t n_tb, per_split;
+  int n_split;
+  size_t seqc, dbt, dz, dw2p, db1p, db2p, dw1p, total;
+};
+
+Layout layout(int64_t t, int n_seq, int d, int h) {
+  Layout L;
+  L.n_tb = (t + kT - 1) / kT;
+  const int64_t tiles = (int64_t)(h / kT) * (d / kT);
+  int ns = (int)((1024 + tiles - 1) / tiles);
+  if (ns > kSplitMax) ns = kSplitMax;
+  if (ns < 1) ns = 1;
+  int64_t per = (t + ns - 1) / ns;
+  per = ((per + kKC - 1) / kKC) * kKC;
+  if (per < kKC) per = kKC;
+  L.per_split = per;
+  L.n_split = ns;
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  size_t off = 0;
+  L.seqc = off; off += al(sizeof(float2) * (size_t)n_seq);
+  L.dbt = off; off += al(sizeof(float) * (size_t)t);
+  L.dz = off; off += al(sizeof(float) * (size_t)t * h);
+  L.dw2p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
+  L.db1p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
+  L.db2p = off; off += al(sizeof(float) * (size_t)L.n_tb);
+  L.dw1p = off; off += al(sizeof(float) * (size_t)ns * h * d);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const void* w1v,
+                    const float* b1, const float* w2, const uint8_t* pr, const int32_t* cu,
+                    int n_seq, float eps, const float* b_raw, const int32_t* kept_idx,
+                    const int32_t* kept_cu, int64_t t_kept, const float* db_kept, float* dx,
+                    float* dw1, float* db1, float* dw2, float* db2, void* ws, hipStream_t st) {
+  const Layout L = layout(t, n_seq, d, h);
+  char* w = static_cast<char*>(ws);
+  float2* seqc = reinterpret_cast<float2*>(w + L.seqc);
+  float* dbt = reinterpret_cast<float*>(w + L.dbt);
+  float* dz = reinterpret_cast<float*>(w + L.dz);
+  float* dw2p = reinterpret_cast<float*>(w + L.dw2p);
+  float* db1p = reinterpret_cast<float*>(w + L.db1p);
+  float* db2p = reinterpret_cast<float*>(w + L.db2p);
+  float* dw1p = reinterpret_cast<float*>(w + L.dw1p);
+  const T* x = static_cast<const T*>(xv);
+  const T* w1 = static_cast<const T*>(w1v);
+  hipLaunchKernelGGL(sbwd_seq, dim3(n_seq), dim3(kThr), 0, st, b_raw, pr, cu, kept_idx, kept_cu,
+                     db_kept, t, t_kept, eps, seqc);
+  if (t > 0)
+    hipLaunchKernelGGL(sbwd_dbt, dim3((unsigned)((t + kThr - 1) / kThr)), dim3(kThr), 0, st, b_raw,
+                       pr, cu, n_seq, t, seqc, dbt);
+  if (t_kept > 0)
+    hipLaunchKernelGGL(sbwd_kept, dim3((unsigned)((t_kept + kThr - 1) / kThr)), dim3(kThr), 0, st,
+                       pr, kept_idx, kept_cu, n_seq, t, t_kept, db_kept, seqc, dbt);
+  if (t > 0) {
+    hipLaunchKernelGGL((sbwd_dz<T>), dim3((unsigned)L.n_tb, h / kT), dim3(kThr), 0, st, x, xs, t,
+                       d, h, w1, b1, w2, dbt, dz, dw2p, db1p, db2p);
+    hipLaunchKernelGGL((sbwd_dw1<T>), dim3(h / kT, d / kT, L.n_split), dim3(kThr), 0, st, x, xs, t,
+                       d, h, dz, L.per_split, dw1p);
+    if (dx)
+      hipLaunchKernelGGL((sbwd_dx<T>), dim3((unsigned)L.n_tb, d / kT), dim3(kThr), 0, st, t, d, h,
+                         w1, dz, dx);
+  }
+  const int64_t hd = (int64_t)h * d;
+  hipLaunchKernelGGL(sbwd_finish, dim3((unsigned)((hd + kThr - 1) / kThr + 1)), dim3(kThr), 0, st,
+                     hd, h, t > 0 ? L.n_split : 0, L.n_tb, dw1p, dw2p, db1p, db2p, dw1, dw2, db1,
+                     db2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h) {
+  return layout(t, n_seq, d, h).total;
+}
+
+hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
+                            const void* w1, const float* b1, const float* w2, const uint8_t* pr,
+                            const int32_t* cu, int n_seq, float eps, const float* b_raw,
+                            const int32_t* kept_idx, const int32_t* kept_cu, int64_t t_kept,
+                            const float* db_kept, float* dx, float* dw1, float* db1, float* dw2,
+                            float* db2, void* ws, hipStream_t st) {
+  if (dt == 1)
+    return launch_t<uint16_t>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, b_raw, kept_idx,
+                              kept_cu, t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
+  return launch_t<float>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, b_raw, kept_idx, kept_cu,
+                         t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
+}
+
+}  // namespace tg

@@ -202,6 +202,44 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
     return out
 
 
+def score_bwd(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: torch.Tensor,
+              cu_seqlens: torch.Tensor, b_raw: torch.Tensor, kept_idx: torch.Tensor,
+              kept_cu: torch.Tensor, db_kept: torch.Tensor, b1: Optional[torch.Tensor] = None,
+              eps: float = 1e-6, want_dx: bool = True, ws: Optional[torch.Tensor] = None):
+    """tg_score_bwd: returns (dx or None, dw1, db1, dw2, db2), all f32."""
+    lib = load()
+    _need(x, "x", (torch.bfloat16, torch.float32), 2)
+    _need(w1, "w1", x.dtype, 2)
+    _need(w2, "w2", torch.float32, 1)
+    _need(prunable, "prunable", torch.uint8, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(b_raw, "b_raw", torch.float32, 1)
+    _need(kept_idx, "kept_idx", torch.int32, 1)
+    _need(kept_cu, "kept_cu", torch.int32, 1)
+    _need(db_kept, "db_kept", torch.float32, 1)
+    if b1 is not None:
+        _need(b1, "b1", torch.float32, 1)
+    t, d = x.shape
+    h = w1.shape[0]
+    n_seq = cu_seqlens.numel() - 1
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty((t, d), **f32) if want_dx else None
+    dw1 = torch.empty((h, d), **f32)
+    db1 = torch.empty(h, **f32)
+    dw2 = torch.empty(h, **f32)
+    db2 = torch.empty(1, **f32)
+    nbytes = lib.tg_score_bwd_workspace_size(t, n_seq, d, h)
+    if ws is None:
+        ws = workspace(nbytes, x.device)
+    st = lib.tg_score_bwd(_p(x), _DT[x.dtype], x.stride(0), t, d, h, _p(w1), _p(b1), _p(w2),
+                          _p(prunable), _p(cu_seqlens), n_seq, float(eps), _p(b_raw),
+                          _p(kept_idx), _p(kept_cu), kept_idx.numel(), _p(db_kept), _p(dx),
+                          _p(dw1), _p(db1), _p(dw2), _p(db2), _p(ws),
+                          ws.numel() * ws.element_size(), _stream(x.device))
+    check("tg_score_bwd", st)
+    return dx, dw1, db1, dw2, db2
+
+
 def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
                    kept_b: torch.Tensor, kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor,
                    gain: torch.Tensor, temp: torch.Tensor, sm_scale: Optional[float] = None,

@@ -481,7 +481,7 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
 # scoring network's weights)
 # ---------------------------------------------------------------------------
 def ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db_kept,
-                  eps: float = R.EPS):
+                  eps: float = R.EPS, error_scales: bool = False):
     """Gradients of L = sum_r db_kept[r] * b[kept_idx[r]] w.r.t. the scorer's
     input rows and parameters, by the chain rule through Eq. 3:
 
@@ -498,7 +498,9 @@ def ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db
 
     x [T, d], w1 [h, d], b1 [h] or None, w2 [h], b2 scalar; kept_idx,
     kept_cu, db_kept as returned by the selector and the attention's backward.
-    Returns (dx [T, d], dw1 [h, d], db1 [h], dw2 [h], db2), float64.
+    Returns (dx [T, d], dw1 [h, d], db1 [h], dw2 [h], db2), float64; with
+    ``error_scales`` also sum_k |db~_k|, the scale of db2's sum of terms of
+    both signs (a finite-precision result is measured against it).
     """
     x = np.asarray(x, dtype=np.float64)
     w1 = np.asarray(w1, dtype=np.float64)
@@ -523,7 +525,10 @@ def ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db
         C = float(np.sum(db[P] * b_raw[P]))
         dbt[P] = db[P] / r - b_raw[P] * C / (P.size * r ** 3)
     dz = dbt[:, None] * w2[None, :] * sig * (1.0 + pre * (1.0 - sig))
-    return dz @ w1, dz.T @ x, dz.sum(axis=0), u.T @ dbt, float(dbt.sum())
+    out = (dz @ w1, dz.T @ x, dz.sum(axis=0), u.T @ dbt, float(dbt.sum()))
+    if error_scales:
+        return out + (float(np.sum(np.abs(dbt))),)
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10300
+    assert lib.tg_version() == 10400
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -228,4 +228,27 @@ def test_gated_attn_bwd_validation(lib):
     assert bw(dq=None) == 1
     assert bw(ws_bytes=64) == 3
     assert bw(q=ctypes.c_void_p(0x10008)) == 2
+
+
+def test_score_bwd_validation(lib):
+    assert lib.tg_score_bwd_workspace_size(1000, 1, 2048, 256) > 1000 * 256 * 4   # holds dz
+    assert lib.tg_score_bwd_workspace_size(-1, 1, 2048, 256) == 0
+
+    def sb(dt=1, t=100, d=2048, h=256, xs=2048, n_seq=1, tk=10, eps=1e-6, x=FAKE, ws=FAKE,
+           ws_bytes=1 << 34, dw1=FAKE):
+        return lib.tg_score_bwd(x, dt, xs, t, d, h, FAKE, None, FAKE, FAKE, FAKE, n_seq, eps, FAKE,
+                                FAKE, FAKE, tk, FAKE, None, dw1, FAKE, FAKE, FAKE, ws, ws_bytes,
+                                None)
+    assert sb(t=-1) == 1
+    assert sb(n_seq=0) == 1
+    assert sb(eps=-1.0) == 1
+    assert sb(dt=4) == 1
+    assert sb(xs=100) == 1
+    assert sb(d=2000, xs=2000) == 2
+    assert sb(h=96) == 2
+    assert sb(tk=200) == 2                              # more kept rows than tokens
+    assert sb(x=None) == 1
+    assert sb(dw1=None) == 1
+    assert sb(ws_bytes=8) == 3
+    assert sb(ws=ctypes.c_void_p(0x10010)) == 2         # workspace not 256-byte aligned
 
