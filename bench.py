@@ -27,7 +27,12 @@ METRIC = "gated-prefill tokens/s at 128k ctx; gated-attn MFMA % peak; gate HBM G
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0               # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3            # MI355X fp32 vector ALU
-WORKLOAD = 3                        # 128k-token gated layer
+WORKLOAD = 3                        # 128k-token gated layer (the metric's configuration)
+WORKLOAD_NAMES = {
+    1: "gated layer 16k: 15872 doc + 512 prompt tokens, K=1984",
+    3: "gated layer 128k: 130560 doc + 512 prompt tokens, K=8192",
+    4: "ragged batch: 4 sequences of 8192/24576/49152/65536 tokens, K = 1/16 of each doc part",
+}
 
 
 def log(msg):
@@ -111,6 +116,8 @@ def main():
     ap.add_argument("--no-full-context", action="store_true")
     ap.add_argument("--kernels-only", action="store_true",
                     help="skip the CPU baseline and the full-context lane (for profiling)")
+    ap.add_argument("--workload", type=int, default=WORKLOAD, choices=sorted(WORKLOAD_NAMES),
+                    help="input configuration; the side lanes run on the default one only")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="after timing, copy MB MiB 3 times with tg_gather and identity indices "
                          "(reference for hardware byte counters); not part of the metric")
@@ -131,7 +138,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    g = generate(WORKLOAD)
+    g = generate(args.workload)
+    lanes = args.workload == WORKLOAD
     wl = g["wl"]
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
@@ -148,17 +156,21 @@ def main():
     gain = torch.from_numpy(g["gain"]).to(dev)
     temp = torch.from_numpy(g["temp"]).to(dev)
     T = wl.t_in
-    n_prunable = [int(g["prunable"].sum())]
+    cu_h = np.asarray(g["cu_seqlens"], np.int64)
+    n_seq = len(cu_h) - 1
+    n_prunable = [int(g["prunable"][cu_h[s]:cu_h[s + 1]].sum()) for s in range(n_seq)]
     kept_cu_h, t_kept = ops.kept_sizes(g["cu_seqlens"], n_prunable, g["budgets"][0])
+    kept_lens = np.diff(np.asarray(kept_cu_h, np.int64))
+    max_kept = int(kept_lens.max(initial=0))
     lib = ops.load()
     b_raw = torch.empty(T, dtype=torch.float32, device=dev)
     b = torch.empty(T, dtype=torch.float32, device=dev)
-    ws_s = ops.workspace(lib.tg_score_workspace_size(T, 1), dev)
-    ws_k = ops.workspace(lib.tg_select_workspace_size(T, 1), dev)
+    ws_s = ops.workspace(lib.tg_score_workspace_size(T, n_seq), dev)
+    ws_k = ops.workspace(lib.tg_select_workspace_size(T, n_seq), dev)
     kept_idx = torch.empty(t_kept, dtype=torch.int32, device=dev)
     kept_pos = torch.empty(t_kept, dtype=torch.int32, device=dev)
     kept_b = torch.empty(t_kept, dtype=torch.float32, device=dev)
-    kept_cu = torch.empty(2, dtype=torch.int32, device=dev)
+    kept_cu = torch.empty(n_seq + 1, dtype=torch.int32, device=dev)
     x_kept = torch.empty(t_kept, wl.d, dtype=torch.bfloat16, device=dev)
 
     def gate():
@@ -189,7 +201,7 @@ def main():
         ops.gather(x, kept_idx, out=x_kept)
         if ev is not None:
             ev[3].record()
-        ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=t_kept, out=o)
+        ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=max_kept, out=o)
         if ev is not None:
             ev[4].record()
 
@@ -216,7 +228,7 @@ def main():
     log(f"per-kernel mean us: {avg}; step {ms_per_step:.3f} ms")
 
     # algorithmic work (what the method must move / compute)
-    attn_flops = 2.0 * wl.dh * wl.hq * t_kept * (t_kept + 1)
+    attn_flops = 2.0 * wl.dh * wl.hq * float(np.sum(kept_lens * (kept_lens + 1)))
     score_bytes = T * wl.d * 2 + wl.h * wl.d * 2 + T * (1 + 4 + 4 + 4 + 4)
     select_bytes = T * (4 + 1) + t_kept * 12
     gather_bytes = 2 * t_kept * wl.d * 2
@@ -233,8 +245,6 @@ def main():
                 "kernel": "gated_attn_bf16" if dom == "attn" else "score_mlp_bf16",
                 "avg_launch_us": round(avg[dom], 2)}
 
-    # the projection of the kept rows (tg_qkv_proj), beside the step: our
-    # kernel and the torch (hipBLASLt) GEMMs on the same operands
     def time_it(fn, reps=10):
         fn()
         torch.cuda.synchronize()
@@ -245,93 +255,98 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3      # us
-    proj_flops = 2.0 * t_kept * wl.d * (wl.hq + 2 * wl.hkv) * wl.dh
-    wq_t, wk_t, wv_t = tb(g["wq"]), tb(g["wk"]), tb(g["wv"])
-    t_proj = time_it(lambda: ops.qkv_proj(x_kept, w_all, wl.hq, wl.hkv, wl.dh, q=q, k=k, v=v))
-    t_proj_torch = time_it(lambda: (x_kept @ wq_t, x_kept @ wk_t, x_kept @ wv_t))
-    proj = {"kernel": "tg_qkv_proj", "us": round(t_proj, 2),
-            "tflops": round(proj_flops / (t_proj * 1e-6) / 1e12, 1),
-            "torch_matmul_us": round(t_proj_torch, 2),
-            "note": "not part of the step: Q/K/V of the kept rows, 8704 x 2048 -> 2048+1024+1024"}
-    del wq_t, wk_t, wv_t
 
-    # LN2 fused into the scorer (norm_eps >= 0, the norm weight folded into
-    # W1): the same rows taken as residuals, beside torch's separate RMSNorm
-    # pass over them, which the fusion removes
-    gam = torch.ones(wl.d, dtype=torch.bfloat16, device=dev)
-    t_score_ln2 = time_it(lambda: ops.score(x, w1, w2, pr, cu, b1=b1, eps=1e-6, b_raw=b_raw, b=b,
-                                            ws=ws_s, norm_eps=1e-6))
-    t_rms_torch = time_it(lambda: torch.nn.functional.rms_norm(x, (wl.d,), gam, 1e-6))
-    score_ln2 = {"kernel": "tg_score (norm_eps >= 0)", "us": round(t_score_ln2, 2),
-                 "plain_score_us": round(avg["score"], 2),
-                 "torch_rms_norm_us": round(t_rms_torch, 2),
-                 "note": "scorer with the block's RMSNorm fused; the torch time is the extra "
-                         "pass an unfused norm costs"}
+    proj = score_ln2 = attn_bwd = score_bwd = decode = None
+    if lanes:
+        # the projection of the kept rows (tg_qkv_proj), beside the step: our
+        # kernel and the torch (hipBLASLt) GEMMs on the same operands
+        proj_flops = 2.0 * t_kept * wl.d * (wl.hq + 2 * wl.hkv) * wl.dh
+        wq_t, wk_t, wv_t = tb(g["wq"]), tb(g["wk"]), tb(g["wv"])
+        t_proj = time_it(lambda: ops.qkv_proj(x_kept, w_all, wl.hq, wl.hkv, wl.dh, q=q, k=k, v=v))
+        t_proj_torch = time_it(lambda: (x_kept @ wq_t, x_kept @ wk_t, x_kept @ wv_t))
+        proj = {"kernel": "tg_qkv_proj", "us": round(t_proj, 2),
+                "tflops": round(proj_flops / (t_proj * 1e-6) / 1e12, 1),
+                "torch_matmul_us": round(t_proj_torch, 2),
+                "note": "not part of the step: Q/K/V of the kept rows, 8704 x 2048 -> 2048+1024+1024"}
+        del wq_t, wk_t, wv_t
 
-    # the attention's backward (tg_gated_attn_bwd) on the step's kept rows:
-    # fp32 on the vector ALU; algorithmic work 10 dh flop per (query, key)
-    # pair and head (the five products of the backward)
-    dout = torch.randn_like(q)
-    ws_b = ops.workspace(lib.tg_gated_attn_bwd_workspace_size(t_kept, 1, wl.hq, wl.hkv), dev)
-    t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain, temp,
-                                               ws=ws_b), reps=2)
-    bwd_flops = 10.0 * wl.dh * wl.hq * t_kept * (t_kept + 1) / 2
-    attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1),
-                "tflops": round(bwd_flops / (t_bwd * 1e-6) / 1e12, 2),
-                "bound": "alu", "peak_tflops_fp32": PEAK_FP32_TFLOPS,
-                "frac_of_fp32_peak": round(bwd_flops / (t_bwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
-                "note": "8704 kept rows, bf16 inputs, fp32 arithmetic and gradients; scores "
-                        "recomputed in 3 passes (18 dh flop per pair done)"}
-    del dout, ws_b
+        # LN2 fused into the scorer (norm_eps >= 0, the norm weight folded into
+        # W1): the same rows taken as residuals, beside torch's separate RMSNorm
+        # pass over them, which the fusion removes
+        gam = torch.ones(wl.d, dtype=torch.bfloat16, device=dev)
+        t_score_ln2 = time_it(lambda: ops.score(x, w1, w2, pr, cu, b1=b1, eps=1e-6, b_raw=b_raw, b=b,
+                                                ws=ws_s, norm_eps=1e-6))
+        t_rms_torch = time_it(lambda: torch.nn.functional.rms_norm(x, (wl.d,), gam, 1e-6))
+        score_ln2 = {"kernel": "tg_score (norm_eps >= 0)", "us": round(t_score_ln2, 2),
+                     "plain_score_us": round(avg["score"], 2),
+                     "torch_rms_norm_us": round(t_rms_torch, 2),
+                     "note": "scorer with the block's RMSNorm fused; the torch time is the extra "
+                             "pass an unfused norm costs"}
 
-    # the scorer's backward (tg_score_bwd) from a gradient at the kept scores:
-    # recompute z, then dW1 and dx (3 products of 2 d h flop per token)
-    db_k = torch.randn(t_kept, dtype=torch.float32, device=dev)
-    ws_sb = ops.workspace(lib.tg_score_bwd_workspace_size(T, 1, wl.d, wl.h), dev)
-    t_sbwd = time_it(lambda: ops.score_bwd(x, w1, w2, pr, cu, b_raw, kept_idx, kept_cu, db_k,
-                                           b1=b1, ws=ws_sb), reps=2)
-    sbwd_flops = 3 * 2.0 * T * wl.d * wl.h
-    score_bwd = {"kernel": "tg_score_bwd", "us": round(t_sbwd, 1),
-                 "tflops": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12, 2), "bound": "alu",
-                 "frac_of_fp32_peak": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
-                 "note": "131072 tokens, d 2048, h 256, bf16 rows, fp32 arithmetic; dx included"}
-    del db_k, ws_sb
+        # the attention's backward (tg_gated_attn_bwd) on the step's kept rows:
+        # fp32 on the vector ALU; algorithmic work 10 dh flop per (query, key)
+        # pair and head (the five products of the backward)
+        dout = torch.randn_like(q)
+        ws_b = ops.workspace(lib.tg_gated_attn_bwd_workspace_size(t_kept, 1, wl.hq, wl.hkv), dev)
+        t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain, temp,
+                                                   ws=ws_b), reps=2)
+        bwd_flops = 10.0 * wl.dh * wl.hq * t_kept * (t_kept + 1) / 2
+        attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1),
+                    "tflops": round(bwd_flops / (t_bwd * 1e-6) / 1e12, 2),
+                    "bound": "alu", "peak_tflops_fp32": PEAK_FP32_TFLOPS,
+                    "frac_of_fp32_peak": round(bwd_flops / (t_bwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                    "note": "8704 kept rows, bf16 inputs, fp32 arithmetic and gradients; scores "
+                            "recomputed in 3 passes (18 dh flop per pair done)"}
+        del dout, ws_b
 
-    # one decode step after the prefill (tg_gated_decode): the new token's
-    # query against the pruned cache of this layer (the kept rows' K/V plus
-    # the token itself).  The calls are replayed from a HIP graph so that the
-    # time is the GPU's, not the host's launch rate.
-    def decode_lane(kc, vc, cb, qpos, reps):
-        n = kc.shape[0]
-        qd = q[-1:].contiguous()
-        od = torch.empty_like(qd)
-        cud = torch.tensor([0, n], dtype=torch.int32, device=dev)
-        wsd = ops.workspace(lib.tg_gated_decode_workspace_size(1, wl.hq, wl.hkv, wl.dh, n), dev)
-        call = lambda: ops.gated_decode(qd, kc, vc, cb, qpos, cud, gain, temp, max_cache_len=n,
-                                        out=od, ws=wsd)
-        call()
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for _ in range(reps):
-                call()
-        gr.replay()
-        torch.cuda.synchronize()
-        t_us = time_it(gr.replay, reps=5) / reps
-        nbytes = 2.0 * n * wl.hkv * wl.dh * 2 + n * 4 + 2 * wl.hq * wl.dh * 2
-        return {"cache_rows": n, "us": round(t_us, 2), "gbs": round(nbytes / (t_us * 1e-6) / 1e9, 1),
-                "frac_of_hbm_peak": round(nbytes / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    kc = torch.cat([k, k[-1:]]).contiguous()
-    vc = torch.cat([v, v[-1:]]).contiguous()
-    cbd = torch.cat([kept_b, torch.zeros(1, dtype=torch.float32, device=dev)])
-    qpos = torch.tensor([T], dtype=torch.int32, device=dev)
-    decode = {"kernel": "tg_gated_decode", "pruned_cache": decode_lane(kc, vc, cbd, qpos, 50),
-              "note": "1 sequence, the new token against the kept rows + itself; "
-                      "graph replay of 50 steps, 2 launches each"}
-    del kc, vc
+        # the scorer's backward (tg_score_bwd) from a gradient at the kept scores:
+        # recompute z, then dW1 and dx (3 products of 2 d h flop per token)
+        db_k = torch.randn(t_kept, dtype=torch.float32, device=dev)
+        ws_sb = ops.workspace(lib.tg_score_bwd_workspace_size(T, 1, wl.d, wl.h), dev)
+        t_sbwd = time_it(lambda: ops.score_bwd(x, w1, w2, pr, cu, b_raw, kept_idx, kept_cu, db_k,
+                                               b1=b1, ws=ws_sb), reps=2)
+        sbwd_flops = 3 * 2.0 * T * wl.d * wl.h
+        score_bwd = {"kernel": "tg_score_bwd", "us": round(t_sbwd, 1),
+                     "tflops": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12, 2), "bound": "alu",
+                     "frac_of_fp32_peak": round(sbwd_flops / (t_sbwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                     "note": "131072 tokens, d 2048, h 256, bf16 rows, fp32 arithmetic; dx included"}
+        del db_k, ws_sb
+
+        # one decode step after the prefill (tg_gated_decode): the new token's
+        # query against the pruned cache of this layer (the kept rows' K/V plus
+        # the token itself).  The calls are replayed from a HIP graph so that the
+        # time is the GPU's, not the host's launch rate.
+        def decode_lane(kc, vc, cb, qpos, reps):
+            n = kc.shape[0]
+            qd = q[-1:].contiguous()
+            od = torch.empty_like(qd)
+            cud = torch.tensor([0, n], dtype=torch.int32, device=dev)
+            wsd = ops.workspace(lib.tg_gated_decode_workspace_size(1, wl.hq, wl.hkv, wl.dh, n), dev)
+            call = lambda: ops.gated_decode(qd, kc, vc, cb, qpos, cud, gain, temp, max_cache_len=n,
+                                            out=od, ws=wsd)
+            call()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(reps):
+                    call()
+            gr.replay()
+            torch.cuda.synchronize()
+            t_us = time_it(gr.replay, reps=5) / reps
+            nbytes = 2.0 * n * wl.hkv * wl.dh * 2 + n * 4 + 2 * wl.hq * wl.dh * 2
+            return {"cache_rows": n, "us": round(t_us, 2), "gbs": round(nbytes / (t_us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        kc = torch.cat([k, k[-1:]]).contiguous()
+        vc = torch.cat([v, v[-1:]]).contiguous()
+        cbd = torch.cat([kept_b, torch.zeros(1, dtype=torch.float32, device=dev)])
+        qpos = torch.tensor([T], dtype=torch.int32, device=dev)
+        decode = {"kernel": "tg_gated_decode", "pruned_cache": decode_lane(kc, vc, cbd, qpos, 50),
+                  "note": "1 sequence, the new token against the kept rows + itself; "
+                          "graph replay of 50 steps, 2 launches each"}
+        del kc, vc
 
     full = None
-    if not args.no_full_context:
+    if lanes and not args.no_full_context:
         # unpruned reference point: all 131072 tokens kept (stand-in Q/K/V)
         qf, kf, vf = random_qkv(3, T, wl.hq, wl.hkv, wl.dh)
         qf, kf, vf = tb(qf), tb(kf), tb(vf)
@@ -383,8 +398,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian hidden states and random-init weights)",
-        "config": {"workload": "gated layer 128k: 130560 doc + 512 prompt tokens, K=8192",
-                   "t_in": T, "k": int(g["budgets"][0][0]), "t_kept": t_kept, "d": wl.d,
+        "config": {"workload": WORKLOAD_NAMES[args.workload],
+                   "t_in": T, "k": [int(v) for v in g["budgets"][0]], "t_kept": t_kept, "d": wl.d,
                    "h": wl.h, "hq": wl.hq, "hkv": wl.hkv, "dh": wl.dh,
                    "step": "score+select+gather+gated_attn (Q/K/V projection excluded)"},
         "roofline": roofline,
