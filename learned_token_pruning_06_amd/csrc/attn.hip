@@ -517,23 +517,6 @@ void gated_attn_bf16(
   }
 }
 
-// compute units of the current device, cached per device
-hipError_t device_cu_count(int* n_cu) {
-  static int cache[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *n_cu = cache[dev];
-    return hipSuccess;
-  }
-  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (*n_cu < 1) *n_cu = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = *n_cu;
-  return hipSuccess;
-}
-
 template <int DH, int HPW, int NWAVE>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                       const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,

@@ -119,6 +119,24 @@ TG_DEVINL uint32_t ld_acquire_u32(const uint32_t* p) {
 // ---------------------------------------------------------------------------
 namespace tg {
 
+// compute units of the current device, cached per device (host side; sizes
+// the persistent attention grid and the scorer's row tiles)
+inline hipError_t device_cu_count(int* n_cu) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *n_cu = cache[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n_cu < 1) *n_cu = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = *n_cu;
+  return hipSuccess;
+}
+
 constexpr int kScoreChunk = 2048;    // tokens per normalisation block
 constexpr int kSelChunk = 2048;      // tokens per selection block
 

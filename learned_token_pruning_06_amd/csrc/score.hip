@@ -32,7 +32,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsPerWG = 256;
 constexpr int kBK = 64;              // d per K-step
 constexpr int kRow = kBK + 8;        // bf16 per LDS row (144 B: rows start 4 banks apart)
 constexpr int kWaves = 8;
@@ -58,25 +57,29 @@ TG_DEVINL float silu_f(float v) {
 // step ahead into registers, then staged into double-buffered, padded LDS
 // tiles shared by all waves; one barrier per K-step.  Rows past the end of x
 // (and hidden units past h) read zeros through the buffer ranges.
-template <int MT, bool NORM>
+template <int MT, bool NORM, int RG>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
     float b2, float norm_eps, float* __restrict__ b_raw) {
   constexpr int H = 32 * MT;
-  constexpr int MTA = (MT + 1) / 2;          // h tiles of the first half
+  constexpr int ROWS = 64 * RG;              // rows per workgroup (RG groups of 64)
+  constexpr int HS = kWaves / RG;            // waves sharing a row group, splitting h
+  constexpr int MTA = (MT + HS - 1) / HS;    // h tiles per wave (the last may have fewer)
+  constexpr int XV = RG;                     // x vectors per thread per K-step
   constexpr int WV = (H + 63) / 64;          // W1 vectors per thread per K-step
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][H * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kRowsPerWG * kRow];
-  __shared__ float sred[4][64];
-  __shared__ float sinv[NORM ? kRowsPerWG : 1];     // 1 / RMS of each row (LN2)
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][ROWS * kRow];
+  __shared__ float sred[HS][RG][64];
+  __shared__ float sinv[NORM ? ROWS : 1];    // 1 / RMS of each row (LN2)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
-  const int rg = wv & 3, hh = wv >> 2;
+  const int rg = wv % RG, hh = wv / RG;
   const int mt0 = hh * MTA;
-  const int nmt = hh == 0 ? MTA : MT - MTA;  // h tiles of this wave (may be 0)
-  const int64_t wg_row0 = (int64_t)blockIdx.x * kRowsPerWG;
+  // h tiles of this wave (may be <= 0 when HS does not divide MT)
+  const int nmt = MT % HS == 0 ? MTA : (MT - mt0 < MTA ? MT - mt0 : MTA);
+  const int64_t wg_row0 = (int64_t)blockIdx.x * ROWS;
   const int64_t row0 = wg_row0 + rg * 64;
 
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
@@ -87,28 +90,30 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
       (int)(xbytes < 0x7fffffff ? xbytes : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(w1), (short)0, (int)((int64_t)H * d * 2), 0x00020000);
-  int xoff[4], woff[WV];
+  int xoff[XV], woff[WV];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
+  for (int i = 0; i < XV; ++i) xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
 #pragma unroll
   for (int i = 0; i < WV; ++i) woff[i] = ((lrow + 64 * i) * d + 8 * lch) * 2;
   const int ldst = lrow * kRow + 8 * lch;
-  u32x4 xr[4], wr[WV];
+  u32x4 xr[XV], wr[WV];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < XV; ++i)
       xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + 2 * k0, 0, 0));
 #pragma unroll
     for (int i = 0; i < WV; ++i)
       wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + 2 * k0, 0, 0));
   };
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};             // sums of squares of rows lrow + 64 i
+  float ss[XV];                                   // sums of squares of rows lrow + 64 i
+#pragma unroll
+  for (int i = 0; i < XV; ++i) ss[i] = 0.f;
   auto stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
+    for (int i = 0; i < XV; ++i) st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
     if constexpr (NORM) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < XV; ++i)
 #pragma unroll
         for (int w = 0; w < 4; ++w) sq_acc(ss[i], xr[i][w]);
     }
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   float inv0 = 1.0f, inv1 = 1.0f;
   if constexpr (NORM) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < XV; ++i) {
       float v = ss[i];
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
@@ -195,14 +200,20 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   }
   const float tot0 = part0 + __shfl_xor(part0, 32, 64);
   const float tot1 = part1 + __shfl_xor(part1, 32, 64);
-  if (hh == 1 && g == 0) {
-    sred[rg][n] = tot0;
-    sred[rg][32 + n] = tot1;
+  if (hh > 0 && g == 0) {
+    sred[hh][rg][n] = tot0;
+    sred[hh][rg][32 + n] = tot1;
   }
   __syncthreads();
   if (hh == 0 && g == 0) {
-    if (row0 + n < t_in) b_raw[row0 + n] = (tot0 + sred[rg][n]) + b2;
-    if (row0 + 32 + n < t_in) b_raw[row0 + 32 + n] = (tot1 + sred[rg][32 + n]) + b2;
+    float a0 = tot0, a1 = tot1;
+#pragma unroll
+    for (int k = 1; k < HS; ++k) {
+      a0 += sred[k][rg][n];
+      a1 += sred[k][rg][32 + n];
+    }
+    if (row0 + n < t_in) b_raw[row0 + n] = a0 + b2;
+    if (row0 + 32 + n < t_in) b_raw[row0 + 32 + n] = a1 + b2;
   }
 }
 
@@ -342,24 +353,37 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
   float* braw = b_raw ? b_raw : reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   if (t_in == 0) return hipSuccess;
   if (dt == 1) {
-    const dim3 grid((unsigned)((t_in + kRowsPerWG - 1) / kRowsPerWG));
+    // rows per workgroup: 256 when that still gives a workgroup per CU,
+    // else 128 or 64 (short inputs), so that small batches fill the chip
+    int n_cu = 0;
+    const hipError_t ce = device_cu_count(&n_cu);
+    if (ce != hipSuccess) return ce;
+    const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
+    const dim3 grid((unsigned)((t_in + 64 * rg - 1) / (64 * rg)));
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* wp = static_cast<const uint16_t*>(w1);
-    switch (h / 32) {
-#define TG_SCORE_CASE(M)                                                                     \
-  case M:                                                                                    \
-    if (norm_eps >= 0.0f)                                                                    \
-      hipLaunchKernelGGL((score_mlp_bf16<M, true>), grid, dim3(kThreads), 0, st, xp,          \
-                         x_row_stride, t_in, d, wp, b1, w2, b2, norm_eps, braw);              \
-    else                                                                                     \
-      hipLaunchKernelGGL((score_mlp_bf16<M, false>), grid, dim3(kThreads), 0, st, xp,         \
-                         x_row_stride, t_in, d, wp, b1, w2, b2, norm_eps, braw);              \
+#define TG_SCORE_LAUNCH(M, N, R)                                                              \
+  hipLaunchKernelGGL((score_mlp_bf16<M, N, R>), grid, dim3(kThreads), 0, st, xp, x_row_stride, \
+                     t_in, d, wp, b1, w2, b2, norm_eps, braw)
+#define TG_SCORE_CASE(M)                                                                      \
+  case M:                                                                                     \
+    if (norm_eps >= 0.0f) {                                                                   \
+      if (rg == 4) TG_SCORE_LAUNCH(M, true, 4);                                               \
+      else if (rg == 2) TG_SCORE_LAUNCH(M, true, 2);                                          \
+      else TG_SCORE_LAUNCH(M, true, 1);                                                       \
+    } else {                                                                                  \
+      if (rg == 4) TG_SCORE_LAUNCH(M, false, 4);                                              \
+      else if (rg == 2) TG_SCORE_LAUNCH(M, false, 2);                                         \
+      else TG_SCORE_LAUNCH(M, false, 1);                                                      \
+    }                                                                                         \
     break;
+    switch (h / 32) {
       TG_SCORE_CASE(1) TG_SCORE_CASE(2) TG_SCORE_CASE(3) TG_SCORE_CASE(4)
       TG_SCORE_CASE(5) TG_SCORE_CASE(6) TG_SCORE_CASE(7) TG_SCORE_CASE(8)
-#undef TG_SCORE_CASE
       default: return hipErrorInvalidValue;
     }
+#undef TG_SCORE_CASE
+#undef TG_SCORE_LAUNCH
   } else {
     const dim3 grid((unsigned)((t_in + 3) / 4));
     hipLaunchKernelGGL(score_mlp_f32, grid, dim3(256), 0, st, static_cast<const float*>(x),

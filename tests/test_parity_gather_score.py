@@ -95,6 +95,25 @@ def test_score_ragged_tail_and_small_h():
         _check_score(g, True, f"T={T}")
 
 
+@pytest.mark.parametrize("T,lens", [(16384, [16384]), (40000, [39000, 1000]),
+                                    (70000, [1, 69999])])
+def test_score_row_tile_heights(T, lens):
+    """The scorer takes 64-, 128- or 256-row workgroups depending on how many
+    rows there are per CU: 16384 rows use 64-row tiles, 40000 rows 128-row
+    tiles and 70000 rows 256-row tiles (each with a ragged last tile)."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(T)
+    say(f"score: row-tile height case T={T}")
+    x = f32_to_bf16_bits(rng.standard_normal((T, 2048)).astype(np.float32))
+    w1 = f32_to_bf16_bits((rng.standard_normal((256, 2048)) / np.sqrt(2048)).astype(np.float32))
+    b1 = (0.1 * rng.standard_normal(256)).astype(np.float32)
+    w2 = (rng.standard_normal(256) / 16.0).astype(np.float32)
+    pr = (rng.random(T) < 0.9).astype(np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    _check_score(dict(x=x, w1=w1, b1=b1, w2=w2, b2=-0.5, prunable=pr, cu_seqlens=cu), True,
+                 f"T={T}")
+
+
 def test_score_128k_bf16_full_size():
     say("score: 128k bf16 workload (full size)")
     _check_score(workload(3), True, "128k bf16")
