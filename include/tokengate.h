@@ -207,9 +207,11 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
  * ws   dev workspace of >= tg_gated_attn_bwd_workspace_size(t_kept, n_seq,
  *      hq, hkv) bytes, 4-byte aligned.
  * The softmax statistics are recomputed, so the forward output is not an
- * input.  Arithmetic is fp32 on the vector ALU for both dtypes; results are
- * bitwise reproducible.  Supported: dh in {64, 128}, hq % hkv == 0,
- * 16-byte aligned tensors.
+ * input.  TG_F32: fp32 arithmetic on the vector ALU.  TG_BF16: matrix cores
+ * with fp32 accumulation; P and dS enter the dv, dk and dq products rounded
+ * to bf16, while db, dgain and dtemp are formed from the fp32 values.
+ * Results are bitwise reproducible.  Supported: dh in {64, 128},
+ * hq % hkv == 0, 16-byte aligned tensors.
  * ---------------------------------------------------------------------- */
 size_t tg_gated_attn_bwd_workspace_size(int64_t t_kept, int32_t n_seq, int32_t hq, int32_t hkv);
 tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const void* dout,

@@ -7,8 +7,9 @@
 //   dk_j = s sum_i tau_i dl_ij q_i    db_j = sum_{h,i} tau_i g_h dl_ij
 //   dg_h = sum_ij tau_i b_j dl_ij     dtemp_h = sum_ij lambda_i z_ij dl_ij
 //
-// fp32 arithmetic on the vector ALU (bf16 or fp32 inputs, fp32 gradients),
-// in four launches, all with a fixed reduction order (bitwise reproducible):
+// fp32 inputs: fp32 arithmetic on the vector ALU, in four launches, all with
+// a fixed reduction order (bitwise reproducible); bf16 inputs run the
+// matrix-core passes of attn_bwd_mfma.hip and share the last launch:
 //   1. bwd_stats  per (64-query tile, head): log2-sum-exp of each row and
 //                 D_i, by an online merge over 32-key tiles (no O needed);
 //   2. bwd_dkdv   per (32-key tile, KV head): loops over the G heads and the
@@ -23,6 +24,8 @@
 // 4 x 2 block of the 64 x 32 score tile (rows 4ty + r, columns tx + 16c)
 // and 2 x 8 or 4 x 8 blocks of the gradient tiles.  Attention scores are
 // recomputed in passes 2 and 3 (P is never stored in HBM).
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
@@ -475,6 +478,16 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* dou
   const T* vp = static_cast<const T*>(v);
   const T* op = static_cast<const T*>(dout);
   const int64_t nq = qslots(t, n_seq), nk = kslots(t, n_seq);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    // bf16: the matrix-core passes, then the shared final sums
+    const hipError_t e = launch_attn_bwd_mfma(q, k, v, dout, t, kept_b, kept_pos, cu, n_seq, hq,
+                                              hkv, DH, gain, temp, sm, lse2, dsum, dq, dk, dv,
+                                              dbpart, gpart, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_finish, dim3((unsigned)((t + kThr - 1) / kThr + 1)), dim3(kThr), 0, st,
+                       dbpart, gpart, cu, n_seq, t, hq, hkv, nq, db, dgain, dtemp);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_stats<DH, T>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp,
                      op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum);
   hipLaunchKernelGGL((bwd_dkdv<DH, T>), dim3((unsigned)nk, hkv), dim3(kThr), 0, st, qp, kp, vp,

@@ -175,6 +175,12 @@ hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d,
                             float* db2, void* ws, hipStream_t st);
 
 size_t attn_bwd_ws_bytes(int64_t t, int n_seq, int hq, int hkv);
+hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
+                                int64_t t, const float* kept_b, const int32_t* kept_pos,
+                                const int32_t* cu, int n_seq, int hq, int hkv, int dh,
+                                const float* gain, const float* temp, float sm, float* lse2,
+                                float* dsum, float* dq, float* dk, float* dv, float* dbpart,
+                                double* gpart, hipStream_t st);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dt,
                            int64_t t, const float* kept_b, const int32_t* kept_pos,
                            const int32_t* cu, int n_seq, int hq, int hkv, int dh,

@@ -1,12 +1,14 @@
 """tg_gated_attn_bwd against the oracle's backward (ref_gated_attn_bwd, fp64,
 pinned by central differences and torch autograd).
 
-The kernels compute in fp32 for both input dtypes and return fp32
-gradients, so the oracle is fed exactly the values the kernel reads (bf16
-inputs rounded the same way) and the bar is an fp32 one.  For dq, dk, dv and
-db the rel-L2 bar is 1e-5: fp32 products and sums over <= 2^12 terms, with
-the cancellation in dl = P (dP - D), measure below 1.6e-6, so the bar keeps a
-margin of about 6.  dgain and dtemp are sums of terms of both signs over every
+The oracle is fed exactly the values the kernels read (bf16 inputs rounded
+the same way).  fp32 inputs run in fp32 on the vector ALU: for dq, dk, dv
+and db the rel-L2 bar is 1e-5 (fp32 products and sums over <= 2^12 terms,
+with the cancellation in dl = P (dP - D), measure below 1.6e-6).  bf16
+inputs run on the matrix cores, where P and dS enter the dv, dk and dq
+products rounded to bf16 (relative 2^-9 per term): those three take the
+bf16 attention bar, rel-L2 <= 1e-2; db, dgain and dtemp come from the fp32
+values and keep the fp32 bars.  dgain and dtemp are sums of terms of both signs over every
 (query, key) pair of a head, so their bar is relative to the oracle's error
 scale for that sum (the sum of |weight| P (|dP| + |D|) over the pairs) plus
 the value itself: |got - ref| <= 1e-5 (|ref| + scale)."""
@@ -59,6 +61,9 @@ def run_bwd(q, k, v, do, kb, pos, kc, gain, temp, dtype):
     return [t.cpu().numpy().astype(np.float64) for t in out]
 
 
+BF16_TOL = {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2}
+
+
 def check(case, dtype, tol=TOL):
     q, k, v, do, kb, pos, kc, gain, temp = case
     got = run_bwd(*case, dtype)
@@ -73,7 +78,8 @@ def check(case, dtype, tol=TOL):
             errs[name] = rel_l2(g, r)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for name, e in errs.items():
-        assert e <= tol, f"{name}: {e:.3e} > {tol}"
+        bar = BF16_TOL.get(name, tol) if dtype == "bf16" else tol
+        assert e <= bar, f"{name}: {e:.3e} > {bar}"
     return got, ref
 
 
