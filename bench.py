@@ -284,19 +284,20 @@ def main():
                              "pass an unfused norm costs"}
 
         # the attention's backward (tg_gated_attn_bwd) on the step's kept rows:
-        # fp32 on the vector ALU; algorithmic work 10 dh flop per (query, key)
-        # pair and head (the five products of the backward)
+        # bf16 inputs run on the matrix cores; algorithmic work 10 dh flop
+        # per (query, key) pair and head (the five products of the backward)
         dout = torch.randn_like(q)
         ws_b = ops.workspace(lib.tg_gated_attn_bwd_workspace_size(t_kept, 1, wl.hq, wl.hkv), dev)
-        t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain, temp,
-                                                   ws=ws_b), reps=2)
+        t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain,
+                                                   temp, ws=ws_b), reps=3)
         bwd_flops = 10.0 * wl.dh * wl.hq * t_kept * (t_kept + 1) / 2
-        attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1),
-                    "tflops": round(bwd_flops / (t_bwd * 1e-6) / 1e12, 2),
-                    "bound": "alu", "peak_tflops_fp32": PEAK_FP32_TFLOPS,
-                    "frac_of_fp32_peak": round(bwd_flops / (t_bwd * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
-                    "note": "8704 kept rows, bf16 inputs, fp32 arithmetic and gradients; scores "
-                            "recomputed in 3 passes (18 dh flop per pair done)"}
+        bwd_tf = bwd_flops / (t_bwd * 1e-6) / 1e12
+        attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1), "tflops": round(bwd_tf, 1),
+                    "bound": "mfma", "peak_tflops": PEAK_BF16_TFLOPS,
+                    "frac_of_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                    "note": "8704 kept rows, bf16 inputs on the matrix cores (P, dS in bf16), "
+                            "fp32 gradients; scores recomputed in 3 passes (18 dh flop per pair "
+                            "done)"}
         del dout, ws_b
 
         # the scorer's backward (tg_score_bwd) from a gradient at the kept scores:
