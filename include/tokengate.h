@@ -243,9 +243,14 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
  * dx       dev [t_in, d] f32 out, or NULL to skip it.
  * dw1 dev [h, d] f32 out; db1, dw2 dev [h] f32 out; db2 dev [1] f32 out.
  * ws       dev workspace of >= tg_score_bwd_workspace_size(t_in, n_seq, d, h)
- *          bytes, 256-byte aligned (it holds dz, [t_in, h] f32).
- * fp32 arithmetic on the vector ALU, fixed reduction orders (bitwise
- * reproducible).  Supported: d % 64 == 0, h % 64 == 0.
+ *          bytes, 256-byte aligned (it holds dz and, on the matrix-core
+ *          path, transposed copies of dz, x and w1).
+ * f32 rows, and bf16 rows with h != 256 or d % 256 != 0: fp32 arithmetic on
+ * the vector ALU.  bf16 rows with h == 256 and d % 256 == 0: dz is recomputed
+ * on the matrix cores with the forward's tiling and rounded to bf16 for the
+ * dW1 and dx products (fp32 accumulation); db1, dw2 and db2 stay fp32.  Fixed
+ * reduction orders on both paths (bitwise reproducible).  Supported:
+ * d % 64 == 0, h % 64 == 0, x and w1 rows 16-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32_t h);
 tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,

@@ -326,6 +326,9 @@ tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t
   if (ws_bytes < need)
     return fail(TG_ERR_WORKSPACE, "tg_score_bwd: workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned(ws, 256)) return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: ws must be 256-byte aligned");
+  const int64_t es = dt == TG_BF16 ? 2 : 4;
+  if ((x && !aligned(x, 16)) || (w1 && !aligned(w1, 16)) || ((x_row_stride * es) % 16) != 0)
+    return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: x and w1 rows must be 16-byte aligned");
   hipError_t e = tg::launch_score_bwd(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable,
                                       cu_seqlens, n_seq, eps, b_raw, kept_idx, kept_cu, t_kept,
                                       db_kept, dx, dw1, db1, dw2, db2, ws, (hipStream_t)stream);

@@ -167,6 +167,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
                          hipStream_t st);
 
 size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h);
+hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const void* w1,
+                           const float* b1, const float* w2, const float* dbt, void* dz, void* dzt,
+                           int64_t ldt, float* dw2p, float* db1p, float* db2p, int64_t* blocks,
+                           hipStream_t st);
+int64_t score_dz_blocks(int64_t t_in, int n_cu);
+hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void* w, int64_t ldw,
+                               int n, int64_t kdim, int splits, float* y, int64_t ldy,
+                               hipStream_t st);
 hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
                             const void* w1, const float* b1, const float* w2, const uint8_t* pr,
                             const int32_t* cu, int n_seq, float eps, const float* b_raw,

@@ -45,10 +45,15 @@ TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            0x00020000);
 }
 
-__global__ __launch_bounds__(kThreads) void qkv_proj_bf16(
+// F32OUT: the same GEMM for other callers, Y[t, n] (fp32, row stride ldy)
+// over the K range [k_per * z, +k_per) of workgroup z (split-K partials at
+// Y + z * ys), with W's rows ldw elements apart.
+template <bool F32OUT>
+__global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
-    uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+    uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t ldw, int k_per,
+    float* __restrict__ y, int64_t ldy, int64_t ys) {
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTile * kRow];
   const int tid = threadIdx.x;
@@ -57,17 +62,26 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_bf16(
   const int rg = wv & 3, ch = wv >> 2;
   const int64_t row0 = (int64_t)blockIdx.x * kTile;
   const int col0 = blockIdx.y * kTile;
+  if constexpr (F32OUT) {                        // this workgroup's K range
+    const int64_t kb = (int64_t)blockIdx.z * k_per;
+    x += kb;
+    w += kb;
+    d = (int)((d - kb) < k_per ? (d - kb) : k_per);
+    y += (int64_t)blockIdx.z * ys;
+  } else {
+    ldw = d;
+  }
 
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
   // of the K-step, for both X (rows of this tile) and W (its output features)
   const int lrow = tid >> 3, lch = tid & 7;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row0 * xs, (t - row0) * xs * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (int64_t)col0 * d, (int64_t)kTile * d * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (int64_t)col0 * ldw, (int64_t)kTile * ldw * 2);
   int xoff[4], woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
-    woff[i] = ((lrow + 64 * i) * d + 8 * lch) * 2;
+    woff[i] = (int)(((int64_t)(lrow + 64 * i) * ldw + 8 * lch) * 2);
   }
   const int ldst = lrow * kRow + 8 * lch;
   u32x4 xr[4], wr[4];
@@ -124,6 +138,23 @@ __global__ __launch_bounds__(kThreads) void qkv_proj_bf16(
 
   // epilogue: lane (n, g) holds columns 32mt + 8(r/4) + 4g + r%4 of this
   // wave's column range, row 32 nt + n of its row range
+  if constexpr (F32OUT) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t row = row0 + 64 * rg + 32 * nt + n;
+        if (row < t) {
+          float* p = y + row * ldy + col0 + 128 * ch + 32 * mt + 4 * g;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<float4*>(p + 8 * r4) =
+                make_float4(acc[mt][nt][4 * r4], acc[mt][nt][4 * r4 + 1], acc[mt][nt][4 * r4 + 2],
+                            acc[mt][nt][4 * r4 + 3]);
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int cbase = col0 + 128 * ch + 32 * mt;      // 32 columns, one destination (dh % 32 == 0)
@@ -160,10 +191,25 @@ hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d
   if (t == 0) return hipSuccess;
   const int n_tot = nq + 2 * nkv;
   const dim3 grid((unsigned)((t + kTile - 1) / kTile), (unsigned)(n_tot / kTile));
-  hipLaunchKernelGGL(qkv_proj_bf16, grid, dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(gemm_abt_bf16<false>, grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), x_row_stride, t, d,
                      static_cast<const uint16_t*>(w), nq, nkv, static_cast<uint16_t*>(q),
-                     static_cast<uint16_t*>(k), static_cast<uint16_t*>(v));
+                     static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), (int64_t)d, d,
+                     nullptr, (int64_t)0, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void* w, int64_t ldw,
+                               int n, int64_t kdim, int splits, float* y, int64_t ldy,
+                               hipStream_t st) {
+  if (m == 0) return hipSuccess;
+  int64_t k_per = (kdim + splits - 1) / splits;
+  k_per = (k_per + kBK - 1) / kBK * kBK;
+  const dim3 grid((unsigned)((m + kTile - 1) / kTile), (unsigned)(n / kTile), (unsigned)splits);
+  hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x), xs, m, (int)kdim,
+                     static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
+                     (int)k_per, y, ldy, m * ldy);
   return hipGetLastError();
 }
 

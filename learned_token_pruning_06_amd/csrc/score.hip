@@ -57,11 +57,21 @@ TG_DEVINL float silu_f(float v) {
 // step ahead into registers, then staged into double-buffered, padded LDS
 // tiles shared by all waves; one barrier per K-step.  Rows past the end of x
 // (and hidden units past h) read zeros through the buffer ranges.
-template <int MT, bool NORM, int RG>
+struct DzOut {                  // outputs of the backward epilogue (BWD)
+  const float* dbt;             // [t_in] gradient at the raw scores
+  uint16_t* dz;                 // [t_in][H] bf16
+  uint16_t* dzt;                // [H][ldt] bf16 (transposed)
+  int64_t ldt;
+  float* dw2p;                  // [blocks][H] per-workgroup sums of dbt * SiLU(z)
+  float* db1p;                  // [blocks][H] per-workgroup sums of dz
+  float* db2p;                  // [blocks]    per-workgroup sums of dbt
+};
+
+template <int MT, bool NORM, int RG, bool BWD = false>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
-    float b2, float norm_eps, float* __restrict__ b_raw) {
+    float b2, float norm_eps, float* __restrict__ b_raw, DzOut bo = DzOut{}) {
   constexpr int H = 32 * MT;
   constexpr int ROWS = 64 * RG;              // rows per workgroup (RG groups of 64)
   constexpr int HS = kWaves / RG;            // waves sharing a row group, splitting h
@@ -174,6 +184,84 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     __syncthreads();
     inv0 = sinv[64 * rg + n];
     inv1 = sinv[64 * rg + 32 + n];
+  }
+
+  if constexpr (BWD) {
+    // backward epilogue: z = acc + b1, dz = dbt w2 SiLU'(z) (bf16, both
+    // layouts) and this workgroup's sums over its rows of dbt SiLU(z) and dz
+    // for each hidden unit: in-lane over the two row tiles, a reduce-scatter
+    // over the 32 row lanes (lane n ends with value pair 2n, 2n + 1), then
+    // the RG row groups in order through LDS.
+    const int64_t ra = row0 + n, rb = row0 + 32 + n;
+    const float ga = ra < t_in ? bo.dbt[ra] : 0.0f, gb = rb < t_in ? bo.dbt[rb] : 0.0f;
+    float* red = reinterpret_cast<float*>(&sx[0][0]);          // [2][RG][H], K-loop buffers are free
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+      if (mt >= nmt) continue;
+      float vw[16], vb[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int h0 = 32 * (mt0 + mt) + 8 * r4 + 4 * g;
+        uint32_t pa[2] = {0u, 0u}, pb[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float bb = b1 ? b1[h0 + e] : 0.0f, ww = w2[h0 + e];
+          const float za = acc[mt][0][r] + bb, zb = acc[mt][1][r] + bb;
+          const float sa = 1.0f / (1.0f + __expf(-za)), sb2 = 1.0f / (1.0f + __expf(-zb));
+          const float da = ga * ww * sa * fmaf(za, 1.0f - sa, 1.0f);
+          const float db = gb * ww * sb2 * fmaf(zb, 1.0f - sb2, 1.0f);
+          vw[r] = fmaf(ga, za * sa, gb * zb * sb2);
+          vb[r] = da + db;
+          const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)da);
+          const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)db);
+          if (ra < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + ra] = ua;
+          if (rb < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + rb] = ub;
+          pa[e >> 1] |= (uint32_t)ua << (16 * (e & 1));
+          pb[e >> 1] |= (uint32_t)ub << (16 * (e & 1));
+        }
+        if (ra < t_in) *reinterpret_cast<uint2*>(bo.dz + ra * H + h0) = make_uint2(pa[0], pa[1]);
+        if (rb < t_in) *reinterpret_cast<uint2*>(bo.dz + rb * H + h0) = make_uint2(pb[0], pb[1]);
+      }
+      // sum over the 32 row lanes: reduce-scatter over lane bits 4..1 (lane n
+      // ends with register n / 2), then add the bit-0 partner
+#pragma unroll
+      for (int o = 16, c = 16; o >= 2; o >>= 1, c >>= 1) {
+        const bool up = (lane & o) != 0;
+#pragma unroll
+        for (int kk = 0; kk < c / 2; ++kk) {
+          const float kw = up ? vw[kk + c / 2] : vw[kk], xw = up ? vw[kk] : vw[kk + c / 2];
+          const float kb = up ? vb[kk + c / 2] : vb[kk], xb = up ? vb[kk] : vb[kk + c / 2];
+          vw[kk] = kw + __shfl_xor(xw, o, 64);
+          vb[kk] = kb + __shfl_xor(xb, o, 64);
+        }
+      }
+      const float tw = vw[0] + __shfl_xor(vw[0], 1, 64);
+      const float tb = vb[0] + __shfl_xor(vb[0], 1, 64);
+      if ((n & 1) == 0) {
+        const int r = n >> 1;
+        const int hid = 32 * (mt0 + mt) + 8 * (r / 4) + 4 * g + (r % 4);
+        red[(0 * RG + rg) * H + hid] = tw;
+        red[(1 * RG + rg) * H + hid] = tb;
+      }
+    }
+    __syncthreads();
+    for (int hid = tid; hid < H; hid += kThreads) {
+      float a = 0.0f, b = 0.0f;
+#pragma unroll
+      for (int k = 0; k < RG; ++k) {
+        a += red[(0 * RG + k) * H + hid];
+        b += red[(1 * RG + k) * H + hid];
+      }
+      bo.dw2p[(int64_t)blockIdx.x * H + hid] = a;
+      bo.db1p[(int64_t)blockIdx.x * H + hid] = b;
+    }
+    if (tid == kThreads - 1) {
+      float a = 0.0f;
+      for (int r = 0; r < ROWS; ++r) a += wg_row0 + r < t_in ? bo.dbt[wg_row0 + r] : 0.0f;
+      bo.db2p[blockIdx.x] = a;
+    }
+    return;
   }
 
   // epilogue: lane (n, g) holds h = 32(mt0+mt) + 8(r/4) + 4g + (r%4) of rows 32nt + n;
@@ -336,6 +424,38 @@ __global__ __launch_bounds__(256) void score_norm(const float* __restrict__ b_ra
 int64_t n_slots(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 1) / CH; }
 
 }  // namespace
+
+// Backward helper: z recomputed with the forward tiling (MT = 8, no LN2),
+// with the backward epilogue.  Returns the number of workgroups (the
+// partial-sum rows) through *blocks.
+hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const void* w1,
+                           const float* b1, const float* w2, const float* dbt, void* dz, void* dzt,
+                           int64_t ldt, float* dw2p, float* db1p, float* db2p, int64_t* blocks,
+                           hipStream_t st) {
+  int n_cu = 0;
+  const hipError_t ce = device_cu_count(&n_cu);
+  if (ce != hipSuccess) return ce;
+  const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
+  const int64_t nb = (t_in + 64 * rg - 1) / (64 * rg);
+  *blocks = nb;
+  if (t_in == 0) return hipSuccess;
+  DzOut bo{dbt, static_cast<uint16_t*>(dz), static_cast<uint16_t*>(dzt), ldt, dw2p, db1p, db2p};
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* wp = static_cast<const uint16_t*>(w1);
+#define TG_DZ(R)                                                                                \
+  hipLaunchKernelGGL((score_mlp_bf16<8, false, R, true>), dim3((unsigned)nb), dim3(kThreads), 0, \
+                     st, xp, xs, t_in, d, wp, b1, w2, 0.0f, -1.0f, nullptr, bo)
+  if (rg == 4) TG_DZ(4);
+  else if (rg == 2) TG_DZ(2);
+  else TG_DZ(1);
+#undef TG_DZ
+  return hipGetLastError();
+}
+
+int64_t score_dz_blocks(int64_t t_in, int n_cu) {
+  const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
+  return (t_in + 64 * rg - 1) / (64 * rg);
+}
 
 size_t score_ws_bytes(int64_t t_in, int n_seq) {
   size_t bytes = sizeof(Partial) * (size_t)n_slots(t_in, n_seq);

@@ -7,8 +7,16 @@
 //   dz = db~ w2 SiLU'(z),  dW1 = sum_j dz_j x_j^T,  dx_j = W1^T dz_j,
 //   db1 = sum_j dz_j,      dw2 = sum_j db~_j u_j,    db2 = sum_j db~_j.
 //
-// fp32 on the vector ALU, seven launches, fixed reduction orders:
-//   sbwd_seq    per sequence: r, |P| and C (fp64 sums) -> 1/r and C/(|P| r^3)
+// bf16 inputs with h = 256 and d % 256 == 0 run the products on the matrix
+// cores: z is recomputed by the scorer's own MFMA tiling with a backward
+// epilogue (dz in bf16 in both layouts, per-workgroup dw2 / db1 / db2 sums),
+// x and W1 are transposed once, and dW1 = dz^T x (split over token ranges)
+// and dx = dz W1 run on the projection's GEMM core with fp32 output.  dz
+// enters both products rounded to bf16.  Otherwise (fp32 inputs, other
+// shapes) everything is fp32 on the vector ALU, seven launches, fixed
+// reduction orders:
+//   sbwd_part, sbwd_cpart, sbwd_seq   per 2048-token / kept-row chunk, then
+//               per sequence: r, |P| and C (fp64 sums) -> 1/r, C/(|P| r^3)
 //   sbwd_dbt    per token: the normaliser term (every prunable token)
 //   sbwd_kept   per kept row: adds db / r at its token
 //   sbwd_dz     per 64 tokens x 64 hidden units: recomputes z (K = d), writes
@@ -18,6 +26,8 @@
 //   sbwd_finish sums the partials.
 // The products are register-blocked micro-GEMMs over padded fp32 LDS tiles,
 // each thread owning 4 x 4 outputs (rows 4ty + r, columns tx + 16c).
+#include <type_traits>
+
 #include "common.h"
 
 namespace tg {
@@ -45,53 +55,100 @@ TG_DEVINL int seq_of_row(const int32_t* cu, int n_seq, int64_t row) {
   return ans;
 }
 
-// ---- per sequence: 1/r and C / (|P| r^3)
-__global__ __launch_bounds__(kThr) void sbwd_seq(const float* __restrict__ b_raw,
-                                                 const uint8_t* __restrict__ pr,
-                                                 const int32_t* __restrict__ cu,
-                                                 const int32_t* __restrict__ kept_idx,
-                                                 const int32_t* __restrict__ kept_cu,
-                                                 const float* __restrict__ db_kept, int64_t t,
-                                                 int64_t t_kept, float eps,
-                                                 float2* __restrict__ seqc) {
-  __shared__ double s1[kThr / 64], s2[kThr / 64];
+// ---- per sequence: 1/r and C / (|P| r^3), from chunk partials (fp64)
+constexpr int kCh = 2048;            // tokens (or kept rows) per partial
+
+struct SqPart {
+  double sq;
+  int64_t n;
+};
+
+// sum of b~^2 and count over the prunable tokens of one 2048-token chunk
+__global__ __launch_bounds__(kThr) void sbwd_part(const float* __restrict__ b_raw,
+                                                  const uint8_t* __restrict__ pr,
+                                                  const int32_t* __restrict__ cu, int n_seq,
+                                                  int64_t t, SqPart* __restrict__ part) {
+  __shared__ double s1[kThr / 64];
   __shared__ int64_t sn[kThr / 64];
-  const int s = blockIdx.x, tid = threadIdx.x;
-  const int64_t lo = cu[s] < t ? cu[s] : t, hi = cu[s + 1] < t ? cu[s + 1] : t;
-  const int64_t klo = kept_cu[s] < t_kept ? kept_cu[s] : t_kept;
-  const int64_t khi = kept_cu[s + 1] < t_kept ? kept_cu[s + 1] : t_kept;
-  double sq = 0.0, c = 0.0;
+  const int64_t slot = blockIdx.x;
+  const int s = seq_of_slot(cu, n_seq, slot, kCh);
+  double sq = 0.0;
   int64_t n = 0;
-  for (int64_t j = lo + tid; j < hi; j += kThr)
-    if (pr[j]) {
-      const double v = b_raw[j];
-      sq = fma(v, v, sq);
-      ++n;
-    }
-  for (int64_t r = klo + tid; r < khi; r += kThr) {
-    const int64_t j = kept_idx[r];
-    if (j >= 0 && j < t && pr[j]) c = fma((double)db_kept[r], (double)b_raw[j], c);
+  if (s >= 0) {
+    const int64_t lo = cu[s] < t ? cu[s] : t, hi = cu[s + 1] < t ? cu[s + 1] : t;
+    const int64_t b0 = lo + (slot - slot0_of(cu, s, kCh)) * kCh;
+    const int64_t e0 = b0 + kCh < hi ? b0 + kCh : hi;
+    for (int64_t j = b0 + threadIdx.x; j < e0; j += kThr)
+      if (pr[j]) {
+        const double v = b_raw[j];
+        sq = fma(v, v, sq);
+        ++n;
+      }
   }
   sq = wave_sum(sq);
-  c = wave_sum(c);
   n = wave_sum(n);
-  if ((tid & 63) == 0) {
-    s1[tid >> 6] = sq;
-    s2[tid >> 6] = c;
-    sn[tid >> 6] = n;
+  if ((threadIdx.x & 63) == 0) {
+    s1[threadIdx.x >> 6] = sq;
+    sn[threadIdx.x >> 6] = n;
   }
   __syncthreads();
-  if (tid == 0) {
-    const double SQ = (s1[0] + s1[1]) + (s1[2] + s1[3]);
-    const double CC = (s2[0] + s2[1]) + (s2[2] + s2[3]);
-    const int64_t N = sn[0] + sn[1] + sn[2] + sn[3];
-    float2 out = make_float2(0.0f, 0.0f);
-    if (N > 0) {
-      const double r = sqrt(SQ / (double)N + (double)eps);
-      out = make_float2((float)(1.0 / r), (float)(CC / ((double)N * r * r * r)));
-    }
-    seqc[s] = out;
+  if (threadIdx.x == 0) {
+    part[slot].sq = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+    part[slot].n = sn[0] + sn[1] + sn[2] + sn[3];
   }
+}
+
+// sum of db * b~ over the kept prunable rows of one 2048-row chunk
+__global__ __launch_bounds__(kThr) void sbwd_cpart(const float* __restrict__ b_raw,
+                                                   const uint8_t* __restrict__ pr,
+                                                   const int32_t* __restrict__ kept_idx,
+                                                   const int32_t* __restrict__ kept_cu, int n_seq,
+                                                   int64_t t, int64_t t_kept,
+                                                   const float* __restrict__ db_kept,
+                                                   double* __restrict__ cpart) {
+  __shared__ double s1[kThr / 64];
+  const int64_t slot = blockIdx.x;
+  const int s = seq_of_slot(kept_cu, n_seq, slot, kCh);
+  double c = 0.0;
+  if (s >= 0) {
+    const int64_t lo = kept_cu[s] < t_kept ? kept_cu[s] : t_kept;
+    const int64_t hi = kept_cu[s + 1] < t_kept ? kept_cu[s + 1] : t_kept;
+    const int64_t b0 = lo + (slot - slot0_of(kept_cu, s, kCh)) * kCh;
+    const int64_t e0 = b0 + kCh < hi ? b0 + kCh : hi;
+    for (int64_t r = b0 + threadIdx.x; r < e0; r += kThr) {
+      const int64_t j = kept_idx[r];
+      if (j >= 0 && j < t && pr[j]) c = fma((double)db_kept[r], (double)b_raw[j], c);
+    }
+  }
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) s1[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) cpart[slot] = (s1[0] + s1[1]) + (s1[2] + s1[3]);
+}
+
+// per sequence: its chunk partials in order -> (1/r, C / (|P| r^3))
+__global__ __launch_bounds__(64) void sbwd_seq(const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ kept_cu,
+                                               const SqPart* __restrict__ part,
+                                               const double* __restrict__ cpart, float eps,
+                                               float2* __restrict__ seqc) {
+  const int s = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int64_t p0 = slot0_of(cu, s, kCh), p1 = slot0_of(cu, s + 1, kCh);
+  const int64_t c0 = slot0_of(kept_cu, s, kCh), c1 = slot0_of(kept_cu, s + 1, kCh);
+  double SQ = 0.0, CC = 0.0;
+  int64_t N = 0;
+  for (int64_t i = p0; i < p1; ++i) {
+    SQ += part[i].sq;
+    N += part[i].n;
+  }
+  for (int64_t i = c0; i < c1; ++i) CC += cpart[i];
+  float2 out = make_float2(0.0f, 0.0f);
+  if (N > 0) {
+    const double r = sqrt(SQ / (double)N + (double)eps);
+    out = make_float2((float)(1.0 / r), (float)(CC / ((double)N * r * r * r)));
+  }
+  seqc[s] = out;
 }
 
 // ---- per token: db~ = -b~ C / (|P| r^3) on prunable tokens, 0 elsewhere
@@ -296,6 +353,7 @@ __global__ __launch_bounds__(kThr) void sbwd_finish(int64_t hd, int h, int n_spl
                                                     float* __restrict__ dw2,
                                                     float* __restrict__ db1,
                                                     float* __restrict__ db2) {
+  __shared__ float sa[kThr / 64], sb[kThr / 64];
   const int64_t nb = (hd + kThr - 1) / kThr;
   if (blockIdx.x < nb) {
     const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
@@ -306,49 +364,123 @@ __global__ __launch_bounds__(kThr) void sbwd_finish(int64_t hd, int h, int n_spl
     }
     return;
   }
-  for (int hid = threadIdx.x; hid < h; hid += kThr) {
-    float a = 0.0f, b = 0.0f;
-    for (int64_t blk = 0; blk < n_tb; ++blk) {
+  // block nb + hid sums hidden unit hid over the token blocks; the last block does db2
+  const int64_t hid = blockIdx.x - nb;
+  float a = 0.0f, b = 0.0f;
+  for (int64_t blk = threadIdx.x; blk < n_tb; blk += kThr) {
+    if (hid < h) {
       a += dw2p[blk * h + hid];
       b += db1p[blk * h + hid];
+    } else {
+      a += db2p[blk];
     }
-    dw2[hid] = a;
-    db1[hid] = b;
   }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if ((threadIdx.x & 63) == 0) {
+    sa[threadIdx.x >> 6] = a;
+    sb[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    float a = 0.0f;
-    for (int64_t blk = 0; blk < n_tb; ++blk) a += db2p[blk];
-    *db2 = a;
+    const float ta = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    const float tb = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+    if (hid < h) {
+      dw2[hid] = ta;
+      db1[hid] = tb;
+    } else {
+      *db2 = ta;
+    }
   }
 }
 
+// bf16 [R rows][C cols] (row stride ld_in) -> [C][ldo], zeros where r >= R;
+// 64 x 64 tiles through LDS with 16-byte global loads and stores (C, ldo
+// and ld_in multiples of 8, as the callers guarantee)
+__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ in,
+                                                      int64_t ld_in, int64_t R, int64_t C,
+                                                      uint16_t* __restrict__ out, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  for (int u = threadIdx.x; u < 64 * 8; u += 256) {
+    const int rr = u / 8, ch = u % 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + rr < R && c0 + 8 * ch < C) v = ld16(in + (r0 + rr) * ld_in + c0 + 8 * ch);
+    st16(&tile[rr][8 * ch], v);
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < 64 * 8; u += 256) {
+    const int cc = u / 8, ch = u % 8;                  // output row c0 + cc, rows 8ch .. +8
+    if (c0 + cc < C && r0 + 8 * ch < ldo) {
+      u32x4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = (uint32_t)tile[8 * ch + 2 * k][cc] | ((uint32_t)tile[8 * ch + 2 * k + 1][cc] << 16);
+      st16(out + (c0 + cc) * ldo + r0 + 8 * ch, v);
+    }
+  }
+}
+
+// zeros in columns [c0, c1) of a [rows][ld] bf16 array
+__global__ __launch_bounds__(256) void fill_zero_u16(uint16_t* __restrict__ p, int64_t rows,
+                                                     int64_t ld, int64_t c0, int64_t c1) {
+  const int64_t w = c1 - c0;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < rows * w) p[(e / w) * ld + c0 + e % w] = 0;
+}
+
+bool mfma_path(int dt, int d, int h) { return dt == 1 && h == 256 && d % 256 == 0; }
+
 struct Layout {
-  int64_t n_tb, per_split;
+  int64_t n_tb, per_split, tp;
   int n_split;
-  size_t seqc, dbt, dz, dw2p, db1p, db2p, dw1p, total;
+  bool mfma;
+  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, dzt, xt, w1t, total;
 };
 
-Layout layout(int64_t t, int n_seq, int d, int h) {
+Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_cu) {
   Layout L;
-  L.n_tb = (t + kT - 1) / kT;
-  const int64_t tiles = (int64_t)(h / kT) * (d / kT);
-  int ns = (int)((1024 + tiles - 1) / tiles);
-  if (ns > kSplitMax) ns = kSplitMax;
-  if (ns < 1) ns = 1;
-  int64_t per = (t + ns - 1) / ns;
-  per = ((per + kKC - 1) / kKC) * kKC;
-  if (per < kKC) per = kKC;
-  L.per_split = per;
-  L.n_split = ns;
+  L.mfma = mfma_path(dt, d, h);
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  if (L.mfma) {
+    // dz in bf16 [t][h] and transposed [h][tp] (tp = t rounded up to 64),
+    // x^T [d][tp], W1^T [d][h]; dW1 split over token ranges of whole 64-steps
+    L.tp = (t + 63) / 64 * 64;
+    L.n_tb = score_dz_blocks(t, n_cu);
+    const int64_t steps = L.tp / 64 > 0 ? L.tp / 64 : 1;
+    const int64_t ns = 32 < steps ? 32 : steps;
+    const int64_t per_steps = (steps + ns - 1) / ns;
+    L.per_split = per_steps * 64;
+    L.n_split = (int)((steps + per_steps - 1) / per_steps);
+  } else {
+    L.tp = t;
+    L.n_tb = (t + kT - 1) / kT;
+    const int64_t tiles = (int64_t)(h / kT) * (d / kT);
+    int ns = (int)((1024 + tiles - 1) / tiles);
+    if (ns > kSplitMax) ns = kSplitMax;
+    if (ns < 1) ns = 1;
+    int64_t per = (t + ns - 1) / ns;
+    per = ((per + kKC - 1) / kKC) * kKC;
+    if (per < kKC) per = kKC;
+    L.per_split = per;
+    L.n_split = ns;
+  }
   size_t off = 0;
   L.seqc = off; off += al(sizeof(float2) * (size_t)n_seq);
+  L.part = off; off += al(sizeof(SqPart) * (size_t)(n_seq + (t + kCh - 1) / kCh));
+  L.cpart = off; off += al(sizeof(double) * (size_t)(n_seq + (t_kept + kCh - 1) / kCh));
   L.dbt = off; off += al(sizeof(float) * (size_t)t);
-  L.dz = off; off += al(sizeof(float) * (size_t)t * h);
+  L.dz = off; off += al((L.mfma ? sizeof(uint16_t) : sizeof(float)) * (size_t)t * h);
   L.dw2p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
   L.db1p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
   L.db2p = off; off += al(sizeof(float) * (size_t)L.n_tb);
-  L.dw1p = off; off += al(sizeof(float) * (size_t)ns * h * d);
+  L.dw1p = off; off += al(sizeof(float) * (size_t)L.n_split * h * d);
+  L.dzt = L.xt = L.w1t = off;
+  if (L.mfma) {
+    L.dzt = off; off += al(sizeof(uint16_t) * (size_t)h * L.tp);
+    L.xt = off; off += al(sizeof(uint16_t) * (size_t)d * L.tp);
+    L.w1t = off; off += al(sizeof(uint16_t) * (size_t)d * h);
+  }
   L.total = off;
   return L;
 }
@@ -359,7 +491,10 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
                     int n_seq, float eps, const float* b_raw, const int32_t* kept_idx,
                     const int32_t* kept_cu, int64_t t_kept, const float* db_kept, float* dx,
                     float* dw1, float* db1, float* dw2, float* db2, void* ws, hipStream_t st) {
-  const Layout L = layout(t, n_seq, d, h);
+  int n_cu = 0;
+  const hipError_t ce = device_cu_count(&n_cu);
+  if (ce != hipSuccess) return ce;
+  const Layout L = layout(t, t_kept, n_seq, d, h, std::is_same<T, uint16_t>::value ? 1 : 0, n_cu);
   char* w = static_cast<char*>(ws);
   float2* seqc = reinterpret_cast<float2*>(w + L.seqc);
   float* dbt = reinterpret_cast<float*>(w + L.dbt);
@@ -370,15 +505,46 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
   float* dw1p = reinterpret_cast<float*>(w + L.dw1p);
   const T* x = static_cast<const T*>(xv);
   const T* w1 = static_cast<const T*>(w1v);
-  hipLaunchKernelGGL(sbwd_seq, dim3(n_seq), dim3(kThr), 0, st, b_raw, pr, cu, kept_idx, kept_cu,
-                     db_kept, t, t_kept, eps, seqc);
+  SqPart* part = reinterpret_cast<SqPart*>(w + L.part);
+  double* cpart = reinterpret_cast<double*>(w + L.cpart);
+  hipLaunchKernelGGL(sbwd_part, dim3((unsigned)(n_seq + (t + kCh - 1) / kCh)), dim3(kThr), 0, st,
+                     b_raw, pr, cu, n_seq, t, part);
+  hipLaunchKernelGGL(sbwd_cpart, dim3((unsigned)(n_seq + (t_kept + kCh - 1) / kCh)), dim3(kThr), 0,
+                     st, b_raw, pr, kept_idx, kept_cu, n_seq, t, t_kept, db_kept, cpart);
+  hipLaunchKernelGGL(sbwd_seq, dim3(n_seq), dim3(64), 0, st, cu, kept_cu, part, cpart, eps, seqc);
   if (t > 0)
     hipLaunchKernelGGL(sbwd_dbt, dim3((unsigned)((t + kThr - 1) / kThr)), dim3(kThr), 0, st, b_raw,
                        pr, cu, n_seq, t, seqc, dbt);
   if (t_kept > 0)
     hipLaunchKernelGGL(sbwd_kept, dim3((unsigned)((t_kept + kThr - 1) / kThr)), dim3(kThr), 0, st,
                        pr, kept_idx, kept_cu, n_seq, t, t_kept, db_kept, seqc, dbt);
-  if (t > 0) {
+  if (L.mfma && t > 0) {
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      uint16_t* dzb = reinterpret_cast<uint16_t*>(w + L.dz);
+      uint16_t* dzt = reinterpret_cast<uint16_t*>(w + L.dzt);
+      uint16_t* xt = reinterpret_cast<uint16_t*>(w + L.xt);
+      uint16_t* w1t = reinterpret_cast<uint16_t*>(w + L.w1t);
+      int64_t nb = 0;
+      hipError_t e = launch_score_dz(x, xs, t, d, w1, b1, w2, dbt, dzb, dzt, L.tp, dw2p, db1p,
+                                     db2p, &nb, st);
+      if (e != hipSuccess) return e;
+      if (L.tp > t)
+        hipLaunchKernelGGL(fill_zero_u16, dim3((unsigned)((h * (L.tp - t) + 255) / 256)), dim3(256),
+                           0, st, dzt, (int64_t)h, L.tp, t, L.tp);
+      hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(d / 64), (unsigned)(L.tp / 64)), dim3(256),
+                         0, st, x, xs, t, (int64_t)d, xt, L.tp);
+      hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(d / 64), (unsigned)((h + 63) / 64)),
+                         dim3(256), 0, st, w1, (int64_t)d, (int64_t)h, (int64_t)d, w1t, (int64_t)h);
+      // dW1[h][c] = sum_j dz^T[h][j] x^T[c][j]  (token splits, fp32 partials)
+      e = launch_gemm_abt_f32(dzt, L.tp, h, xt, L.tp, d, L.tp, L.n_split, dw1p, d, st);
+      if (e != hipSuccess) return e;
+      // dx[j][c] = sum_h dz[j][h] W1^T[c][h]
+      if (dx) {
+        e = launch_gemm_abt_f32(dzb, h, t, w1t, h, d, h, 1, dx, d, st);
+        if (e != hipSuccess) return e;
+      }
+    }
+  } else if (t > 0) {
     hipLaunchKernelGGL((sbwd_dz<T>), dim3((unsigned)L.n_tb, h / kT), dim3(kThr), 0, st, x, xs, t,
                        d, h, w1, b1, w2, dbt, dz, dw2p, db1p, db2p);
     hipLaunchKernelGGL((sbwd_dw1<T>), dim3(h / kT, d / kT, L.n_split), dim3(kThr), 0, st, x, xs, t,
@@ -388,7 +554,7 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
                          w1, dz, dx);
   }
   const int64_t hd = (int64_t)h * d;
-  hipLaunchKernelGGL(sbwd_finish, dim3((unsigned)((hd + kThr - 1) / kThr + 1)), dim3(kThr), 0, st,
+  hipLaunchKernelGGL(sbwd_finish, dim3((unsigned)((hd + kThr - 1) / kThr + h + 1)), dim3(kThr), 0, st,
                      hd, h, t > 0 ? L.n_split : 0, L.n_tb, dw1p, dw2p, db1p, db2p, dw1, dw2, db1,
                      db2);
   return hipGetLastError();
@@ -397,7 +563,13 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
 }  // namespace
 
 size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h) {
-  return layout(t, n_seq, d, h).total;
+  // enough for either arithmetic path (the dtype is not an argument here)
+  int n_cu = 0;
+  if (device_cu_count(&n_cu) != hipSuccess || n_cu < 1) n_cu = 1;
+  // kept rows never exceed t (checked by the entry point)
+  const size_t a = layout(t, t, n_seq, d, h, 0, n_cu).total;
+  const size_t b = layout(t, t, n_seq, d, h, 1, n_cu).total;
+  return a > b ? a : b;
 }
 
 hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,

@@ -1,10 +1,13 @@
 """tg_score_bwd against the oracle's scorer backward (ref_score_bwd, fp64,
 pinned by central differences and torch autograd).
 
-The kernels compute in fp32 for both input dtypes; the oracle is fed the
-values the kernel reads (bf16 rows and weights rounded the same way, the
-forward's raw scores rounded to fp32 as the kernel receives them).  Bar:
-rel-L2 <= 1e-5 for dx, dW1, db1 and dw2 (fp32 sums over <= 2^14 terms);
+The oracle is fed the values the kernel reads (bf16 rows and weights
+rounded the same way, the forward's raw scores rounded to fp32 as the
+kernel receives them).  fp32 arithmetic (fp32 inputs, or shapes outside the
+matrix-core path): rel-L2 <= 1e-5 for dx, dW1, db1 and dw2 (fp32 sums over
+<= 2^14 terms).  bf16 inputs with h = 256 and d % 256 == 0 run dW1 and dx on
+the matrix cores with dz rounded to bf16 (relative 2^-9 per term): those two
+take the bf16 bar, rel-L2 <= 1e-2; db1 and dw2 come from the fp32 values.
 db2 is a sum of terms of both signs over every prunable token, so its bar
 is |got - ref| <= 1e-5 (|ref| + sum |db~|)."""
 import numpy as np
@@ -55,6 +58,7 @@ def run(c, dtype):
 
 
 def check(c, dtype):
+    mfma = dtype == "bf16" and c["w1"].shape[0] == 256 and c["x"].shape[1] % 256 == 0
     got = run(c, dtype)
     *ref, scale = O.ref_score_bwd(c["x"], c["w1"], c["b1"], c["w2"], c["b2"], c["pr"], c["cu"],
                                   c["kept_idx"], c["kept_cu"], c["db_kept"], eps=EPS,
@@ -63,7 +67,8 @@ def check(c, dtype):
     errs["db2"] = abs(float(got[4][0]) - ref[4]) / (abs(ref[4]) + scale)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
-        assert e <= TOL, f"{n}: {e:.3e}"
+        bar = 1e-2 if (mfma and n in ("dx", "dw1")) else TOL
+        assert e <= bar, f"{n}: {e:.3e} > {bar}"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
