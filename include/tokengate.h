@@ -87,8 +87,9 @@ int tg_version(void);
  * b_raw    dev  [t_in] f32 out (b~), or NULL (then kept in the workspace).
  * b        dev  [t_in] f32 out (normalised; 0 on prompt tokens).
  * ws       dev  workspace of >= tg_score_workspace_size(t_in, n_seq) bytes.
- * Supported: dt = TG_BF16 with d % 64 == 0 and h % 32 == 0, h <= 256; or
- * dt = TG_F32 with h <= 1024.  x and w1 rows must be 16-byte aligned.
+ * Supported: dt = TG_BF16 with d % 64 == 0 and h % 32 == 0, h <= 256,
+ * x_row_stride < 2^22; or dt = TG_F32 with h <= 1024.  x and w1 rows must
+ * be 16-byte aligned.
  * Reduction order is fixed, so results are bitwise reproducible.
  * ---------------------------------------------------------------------- */
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq);
@@ -250,7 +251,8 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
  * on the matrix cores with the forward's tiling and rounded to bf16 for the
  * dW1 and dx products (fp32 accumulation); db1, dw2 and db2 stay fp32.  Fixed
  * reduction orders on both paths (bitwise reproducible).  Supported:
- * d % 64 == 0, h % 64 == 0, x and w1 rows 16-byte aligned.
+ * d % 64 == 0, h % 64 == 0, x_row_stride and d < 2^22, x and w1 rows
+ * 16-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32_t h);
 tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,

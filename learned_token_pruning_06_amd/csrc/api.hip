@@ -76,6 +76,8 @@ tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_i
   if (dt == TG_BF16) {
     if (d % 64 != 0 || h % 32 != 0 || h > 256)
       return fail(TG_ERR_UNSUPPORTED, "tg_score: bf16 needs d %% 64 == 0, h %% 32 == 0, h <= 256");
+    if (x_row_stride >= ((int64_t)1 << 22))     // 256 rows of 32-bit buffer offsets
+      return fail(TG_ERR_UNSUPPORTED, "tg_score: bf16 needs x_row_stride < 2^22");
   } else if (h > 1024) {
     return fail(TG_ERR_UNSUPPORTED, "tg_score: f32 needs h <= 1024");
   }
@@ -314,6 +316,8 @@ tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t
   if (x_row_stride < d) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: x_row_stride < d");
   if (d % 64 != 0 || h % 64 != 0)
     return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: needs d %% 64 == 0 and h %% 64 == 0");
+  if (x_row_stride >= ((int64_t)1 << 22) || d >= (1 << 22))
+    return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: needs x_row_stride, d < 2^22");
   if (t_in > INT32_MAX - 4096 || t_kept > t_in)
     return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: sizes too large");
   if (!cu_seqlens || !kept_cu || !w2 || !dw1 || !db1 || !dw2 || !db2 || !ws)

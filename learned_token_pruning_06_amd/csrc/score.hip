@@ -67,6 +67,88 @@ struct DzOut {                  // outputs of the backward epilogue (BWD)
   float* db2p;                  // [blocks]    per-workgroup sums of dbt
 };
 
+// Backward epilogue shared by the scorer kernels: z = acc + b1,
+// dz = dbt w2 SiLU'(z) (bf16, both layouts) and the workgroup's sums over its
+// rows of dbt SiLU(z) and dz for each hidden unit: in-lane over the two row
+// tiles, a reduce-scatter over the 32 row lanes (lane n ends with value pair
+// 2n, 2n + 1), then the RG row groups in order through LDS (red: [2][RG][H]
+// floats).  Every thread of the workgroup calls it.
+template <int H, int MTA, int RG>
+TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, int64_t row0,
+                           int64_t wg_row0, int64_t t_in, const float* __restrict__ b1,
+                           const float* __restrict__ w2, const DzOut& bo, float* red, int tid,
+                           int nthreads) {
+  const int lane = tid & 63, n = lane & 31, g = lane >> 5;
+  const int64_t ra = row0 + n, rb = row0 + 32 + n;
+  const float ga = ra < t_in ? bo.dbt[ra] : 0.0f, gb = rb < t_in ? bo.dbt[rb] : 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt) {
+    if (mt >= nmt) continue;
+    float vw[16], vb[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int h0 = 32 * (mt0 + mt) + 8 * r4 + 4 * g;
+      uint32_t pa[2] = {0u, 0u}, pb[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        const float bb = b1 ? b1[h0 + e] : 0.0f, ww = w2[h0 + e];
+        const float za = acc[mt][0][r] + bb, zb = acc[mt][1][r] + bb;
+        const float sa = 1.0f / (1.0f + __expf(-za)), sb2 = 1.0f / (1.0f + __expf(-zb));
+        const float da = ga * ww * sa * fmaf(za, 1.0f - sa, 1.0f);
+        const float db = gb * ww * sb2 * fmaf(zb, 1.0f - sb2, 1.0f);
+        vw[r] = fmaf(ga, za * sa, gb * zb * sb2);
+        vb[r] = da + db;
+        const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)da);
+        const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)db);
+        if (ra < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + ra] = ua;
+        if (rb < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + rb] = ub;
+        pa[e >> 1] |= (uint32_t)ua << (16 * (e & 1));
+        pb[e >> 1] |= (uint32_t)ub << (16 * (e & 1));
+      }
+      if (ra < t_in) *reinterpret_cast<uint2*>(bo.dz + ra * H + h0) = make_uint2(pa[0], pa[1]);
+      if (rb < t_in) *reinterpret_cast<uint2*>(bo.dz + rb * H + h0) = make_uint2(pb[0], pb[1]);
+    }
+    // sum over the 32 row lanes: reduce-scatter over lane bits 4..1 (lane n
+    // ends with register n / 2), then add the bit-0 partner
+#pragma unroll
+    for (int o = 16, c = 16; o >= 2; o >>= 1, c >>= 1) {
+      const bool up = (lane & o) != 0;
+#pragma unroll
+      for (int kk = 0; kk < c / 2; ++kk) {
+        const float kw = up ? vw[kk + c / 2] : vw[kk], xw = up ? vw[kk] : vw[kk + c / 2];
+        const float kb = up ? vb[kk + c / 2] : vb[kk], xb = up ? vb[kk] : vb[kk + c / 2];
+        vw[kk] = kw + __shfl_xor(xw, o, 64);
+        vb[kk] = kb + __shfl_xor(xb, o, 64);
+      }
+    }
+    const float tw = vw[0] + __shfl_xor(vw[0], 1, 64);
+    const float tb = vb[0] + __shfl_xor(vb[0], 1, 64);
+    if ((n & 1) == 0) {
+      const int r = n >> 1;
+      const int hid = 32 * (mt0 + mt) + 8 * (r / 4) + 4 * g + (r % 4);
+      red[(0 * RG + rg) * H + hid] = tw;
+      red[(1 * RG + rg) * H + hid] = tb;
+    }
+  }
+  __syncthreads();
+  for (int hid = tid; hid < H; hid += nthreads) {
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      a += red[(0 * RG + k) * H + hid];
+      b += red[(1 * RG + k) * H + hid];
+    }
+    bo.dw2p[(int64_t)blockIdx.x * H + hid] = a;
+    bo.db1p[(int64_t)blockIdx.x * H + hid] = b;
+  }
+  if (tid == nthreads - 1) {
+    float a = 0.0f;
+    for (int r = 0; r < 64 * RG; ++r) a += wg_row0 + r < t_in ? bo.dbt[wg_row0 + r] : 0.0f;
+    bo.db2p[blockIdx.x] = a;
+  }
+}
+
 template <int MT, bool NORM, int RG, bool BWD = false>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
@@ -187,80 +269,8 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   }
 
   if constexpr (BWD) {
-    // backward epilogue: z = acc + b1, dz = dbt w2 SiLU'(z) (bf16, both
-    // layouts) and this workgroup's sums over its rows of dbt SiLU(z) and dz
-    // for each hidden unit: in-lane over the two row tiles, a reduce-scatter
-    // over the 32 row lanes (lane n ends with value pair 2n, 2n + 1), then
-    // the RG row groups in order through LDS.
-    const int64_t ra = row0 + n, rb = row0 + 32 + n;
-    const float ga = ra < t_in ? bo.dbt[ra] : 0.0f, gb = rb < t_in ? bo.dbt[rb] : 0.0f;
     float* red = reinterpret_cast<float*>(&sx[0][0]);          // [2][RG][H], K-loop buffers are free
-#pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-      if (mt >= nmt) continue;
-      float vw[16], vb[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int h0 = 32 * (mt0 + mt) + 8 * r4 + 4 * g;
-        uint32_t pa[2] = {0u, 0u}, pb[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const float bb = b1 ? b1[h0 + e] : 0.0f, ww = w2[h0 + e];
-          const float za = acc[mt][0][r] + bb, zb = acc[mt][1][r] + bb;
-          const float sa = 1.0f / (1.0f + __expf(-za)), sb2 = 1.0f / (1.0f + __expf(-zb));
-          const float da = ga * ww * sa * fmaf(za, 1.0f - sa, 1.0f);
-          const float db = gb * ww * sb2 * fmaf(zb, 1.0f - sb2, 1.0f);
-          vw[r] = fmaf(ga, za * sa, gb * zb * sb2);
-          vb[r] = da + db;
-          const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)da);
-          const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)db);
-          if (ra < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + ra] = ua;
-          if (rb < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + rb] = ub;
-          pa[e >> 1] |= (uint32_t)ua << (16 * (e & 1));
-          pb[e >> 1] |= (uint32_t)ub << (16 * (e & 1));
-        }
-        if (ra < t_in) *reinterpret_cast<uint2*>(bo.dz + ra * H + h0) = make_uint2(pa[0], pa[1]);
-        if (rb < t_in) *reinterpret_cast<uint2*>(bo.dz + rb * H + h0) = make_uint2(pb[0], pb[1]);
-      }
-      // sum over the 32 row lanes: reduce-scatter over lane bits 4..1 (lane n
-      // ends with register n / 2), then add the bit-0 partner
-#pragma unroll
-      for (int o = 16, c = 16; o >= 2; o >>= 1, c >>= 1) {
-        const bool up = (lane & o) != 0;
-#pragma unroll
-        for (int kk = 0; kk < c / 2; ++kk) {
-          const float kw = up ? vw[kk + c / 2] : vw[kk], xw = up ? vw[kk] : vw[kk + c / 2];
-          const float kb = up ? vb[kk + c / 2] : vb[kk], xb = up ? vb[kk] : vb[kk + c / 2];
-          vw[kk] = kw + __shfl_xor(xw, o, 64);
-          vb[kk] = kb + __shfl_xor(xb, o, 64);
-        }
-      }
-      const float tw = vw[0] + __shfl_xor(vw[0], 1, 64);
-      const float tb = vb[0] + __shfl_xor(vb[0], 1, 64);
-      if ((n & 1) == 0) {
-        const int r = n >> 1;
-        const int hid = 32 * (mt0 + mt) + 8 * (r / 4) + 4 * g + (r % 4);
-        red[(0 * RG + rg) * H + hid] = tw;
-        red[(1 * RG + rg) * H + hid] = tb;
-      }
-    }
-    __syncthreads();
-    for (int hid = tid; hid < H; hid += kThreads) {
-      float a = 0.0f, b = 0.0f;
-#pragma unroll
-      for (int k = 0; k < RG; ++k) {
-        a += red[(0 * RG + k) * H + hid];
-        b += red[(1 * RG + k) * H + hid];
-      }
-      bo.dw2p[(int64_t)blockIdx.x * H + hid] = a;
-      bo.db1p[(int64_t)blockIdx.x * H + hid] = b;
-    }
-    if (tid == kThreads - 1) {
-      float a = 0.0f;
-      for (int r = 0; r < ROWS; ++r) a += wg_row0 + r < t_in ? bo.dbt[wg_row0 + r] : 0.0f;
-      bo.db2p[blockIdx.x] = a;
-    }
+    dz_epilogue<H, MTA, RG>(acc, nmt, mt0, rg, row0, wg_row0, t_in, b1, w2, bo, red, tid, kThreads);
     return;
   }
 

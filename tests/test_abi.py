@@ -116,6 +116,7 @@ def test_score_validation(lib):
     assert _score(lib, h=48) == 2                     # h % 32
     assert _score(lib, h=512) == 2                    # h <= 256 on the bf16 path
     assert _score(lib, x=ctypes.c_void_p(0x10002)) == 2
+    assert _score(lib, xs=1 << 22) == 2               # 32-bit buffer offsets over 256 rows
     assert _score(lib, wsb=16) == 3                   # workspace too small
     assert "workspace" in lib.tg_last_error().decode()
 
@@ -251,4 +252,7 @@ def test_score_bwd_validation(lib):
     assert sb(dw1=None) == 1
     assert sb(ws_bytes=8) == 3
     assert sb(ws=ctypes.c_void_p(0x10010)) == 2         # workspace not 256-byte aligned
+    assert sb(x=ctypes.c_void_p(0x10002)) == 2          # rows must be 16-byte aligned
+    assert sb(xs=2052) == 2
+    assert sb(xs=1 << 22) == 2
 

@@ -114,6 +114,24 @@ def test_score_row_tile_heights(T, lens):
                  f"T={T}")
 
 
+@pytest.mark.parametrize("d", [128, 384])
+def test_score_256_row_tiles_short_rows(d):
+    """256-row tiles with rows of 128 and 384 elements: one and three turns
+    of the four-slice ring, the last slices fetched again at the tail."""
+    from workloads import f32_to_bf16_bits
+    T = 70000
+    rng = np.random.default_rng(d)
+    say(f"score: 256-row tiles, T={T} d={d}")
+    x = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w1 = f32_to_bf16_bits((rng.standard_normal((256, d)) / np.sqrt(d)).astype(np.float32))
+    b1 = (0.1 * rng.standard_normal(256)).astype(np.float32)
+    w2 = (rng.standard_normal(256) / 16.0).astype(np.float32)
+    pr = (rng.random(T) < 0.9).astype(np.uint8)
+    cu = np.array([0, 12345, T], np.int32)
+    _check_score(dict(x=x, w1=w1, b1=b1, w2=w2, b2=0.25, prunable=pr, cu_seqlens=cu), True,
+                 f"T={T} d={d}")
+
+
 def test_score_128k_bf16_full_size():
     say("score: 128k bf16 workload (full size)")
     _check_score(workload(3), True, "128k bf16")

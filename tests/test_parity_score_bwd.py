@@ -90,6 +90,14 @@ def test_score_bwd_16k_layer():
     check(sbwd_case(3, 16384, 2048, 256, [16384], [1984], "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("d", [256, 512])
+def test_score_bwd_256_row_tiles(d):
+    """70000 tokens: the recomputation of z takes 256-row tiles (the ragged
+    last one holds 112 rows); bf16 rows on the matrix-core path."""
+    say(f"score bwd bf16: 70000 tokens, d {d}, h 256")
+    check(sbwd_case(5 + d, 70000, d, 256, [1, 40000, 29999], [1, 3000, 2000], "bf16"), "bf16")
+
+
 def test_score_bwd_deterministic():
     c = sbwd_case(4, 3000, 2048, 256, [3000], [400], "bf16")
     a, b = run(c, "bf16"), run(c, "bf16")
