@@ -377,11 +377,23 @@ __global__ __launch_bounds__(256) void score_partial(const float* __restrict__ b
   int s, nch;
   int64_t begin, end;
   if (!locate(cu, n_seq, t_in, blockIdx.x, s, begin, end, nch)) return;
+  // a chunk is at most CH = 8 * 256 tokens: all loads first, then the sums
+  // (in the same per-thread order as a strided loop)
+  constexpr int PER = CH / 256;
+  uint8_t pv[PER];
+  float bv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t j = begin + threadIdx.x + (int64_t)i * 256;
+    pv[i] = j < end ? pr[j] : (uint8_t)0;
+    bv[i] = j < end ? b_raw[j] : 0.0f;
+  }
   double acc = 0.0;
   int64_t cnt = 0;
-  for (int64_t j = begin + threadIdx.x; j < end; j += 256) {
-    if (pr[j]) {
-      const double v = b_raw[j];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (pv[i]) {
+      const double v = bv[i];
       acc = fma(v, v, acc);
       ++cnt;
     }
@@ -428,7 +440,20 @@ __global__ __launch_bounds__(256) void score_norm(const float* __restrict__ b_ra
   const double tot = ((sd[0] + sd[1]) + sd[2]) + sd[3];
   const int64_t n = sc[0] + sc[1] + sc[2] + sc[3];
   const float r = n > 0 ? (float)sqrt(tot / (double)n + (double)eps) : 1.0f;
-  for (int64_t j = begin + threadIdx.x; j < end; j += 256) b[j] = pr[j] ? b_raw[j] / r : 0.0f;
+  constexpr int PER = CH / 256;
+  uint8_t pv[PER];
+  float bv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t j = begin + threadIdx.x + (int64_t)i * 256;
+    pv[i] = j < end ? pr[j] : (uint8_t)0;
+    bv[i] = j < end ? b_raw[j] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t j = begin + threadIdx.x + (int64_t)i * 256;
+    if (j < end) b[j] = pv[i] ? bv[i] / r : 0.0f;
+  }
 }
 
 int64_t n_slots(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 1) / CH; }

@@ -179,12 +179,20 @@ __global__ __launch_bounds__(NT) void sel_pass(const float* __restrict__ b,
   }
   for (int i = threadIdx.x; i < NB; i += NT) lh[i] = 0u;
   __syncthreads();
-  int np = 0;
+  // all loads first (one memory latency per thread, not one per token)
+  uint8_t pv[PER];
+  float bv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t j = c.begin + threadIdx.x + (int64_t)i * NT;
-    if (j < c.end && pr[j]) {
-      const uint32_t key = score_key(b[j]);
+    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
+    bv[i] = j < c.end ? b[j] : 0.0f;
+  }
+  int np = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (pv[i]) {
+      const uint32_t key = score_key(bv[i]);
       ++np;
       if (P == 0) {
         atomicAdd(&lh[key >> 21], 1u);
@@ -237,15 +245,23 @@ __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
   const Sel st = sel_stage(w, kbud, c.s, n_seq, 3, c.begin == c.lo, sh);
-  int def = 0, tie = 0;
+  uint8_t pv[PER], in[PER];
+  float bv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t j = c.begin + threadIdx.x + (int64_t)i * NT;
-    if (j < c.end) {
-      if (!pr[j] || st.mode == MODE_ALL) {
+    in[i] = j < c.end;
+    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
+    bv[i] = j < c.end ? b[j] : 0.0f;
+  }
+  int def = 0, tie = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (in[i]) {
+      if (!pv[i] || st.mode == MODE_ALL) {
         ++def;
       } else if (st.mode == MODE_RADIX) {
-        const uint32_t key = score_key(b[j]);
+        const uint32_t key = score_key(bv[i]);
         def += key > st.prefix;
         tie += key == st.prefix;
       }
@@ -294,21 +310,26 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
   float bv[PER];
   uint8_t fl[PER];     // 1: kept for sure, 2: tie at tau
   int nt = 0;
+  uint8_t pv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t j = j0 + i;
+    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
+    bv[i] = j < c.end ? b[j] : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t j = j0 + i;
     uint8_t f = 0;
-    float v = 0.f;
+    const float v = bv[i];
     if (j < c.end) {
-      v = b[j];
-      if (!pr[j] || st.mode == MODE_ALL) {
+      if (!pv[i] || st.mode == MODE_ALL) {
         f = 1;
       } else if (st.mode == MODE_RADIX) {
         const uint32_t key = score_key(v);
         f = key > st.prefix ? 1 : (key == st.prefix ? 2 : 0);
       }
     }
-    bv[i] = v;
     fl[i] = f;
     nt += f >> 1;
   }
