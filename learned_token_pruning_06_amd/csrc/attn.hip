@@ -23,10 +23,10 @@
 //    on the MFMA M axis, queries on N), so each lane holds one query's
 //    logits: the softmax statistics are per-lane scalars plus one swap
 //    between the two lane halves (v_permlane32_swap);
-//  - P^T from the accumulators is directly the B operand of O^T = V^T.P^T
-//    with keys permuted consistently between the two operands; V is
-//    transposed into LDS ([d][key]) in that permuted key order, so each lane
-//    reads its 8 keys with one 16-byte load;
+//  - P^T from the accumulators is directly the B operand of O^T = V^T.P^T;
+//    the keys of P^T's K-steps come in runs of four, and V stays row-major
+//    in LDS: two transposing reads (ds_read_b64_tr_b16) hand each lane the
+//    two runs of four keys of its head dimension;
 //  - the softmax normaliser sums the bf16-rounded probabilities that enter
 //    the P.V product (v_dot2 against (1, 1)), so numerator and denominator
 //    carry the same weights;
@@ -62,6 +62,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int BKV = 64;                 // keys per tile
 constexpr int QW = 32;                  // query rows per wave
@@ -117,28 +118,19 @@ TG_DEVINL float buf_ldf(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// position of key k of a tile in a V^T row: inside each group of 16 keys the
-// blocks [4..7] and [8..11] are swapped, so that the 8 keys one lane needs
-// for an MFMA K-step (16kk + 8(e/4) + 4g + e%4, e < 8) are contiguous
-TG_DEVINL int vpos(int k) {
-  const int r = k & 15;
-  return (k & ~15) | (r < 4 || r >= 12 ? r : (r < 8 ? r + 4 : r - 4));
-}
-
 template <int DH, int HPW, int NWAVE>
 struct AttnCfg {
   static constexpr int NTHR = 64 * NWAVE;        // threads per workgroup
   static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
   static constexpr int KROW = DH + 24;           // K row: DH values, 16 bias columns, 8 pad
-  static constexpr int VROW = BKV + 8;           // V^T row: 64 keys, 8 pad
+  static constexpr int VROW = DH + 16;           // V row: DH values, 16 pad (rows 32 B apart mod 256 B)
   static constexpr int KT = DH / 16;             // MFMA K-steps over the head dim
   static constexpr int DT = DH / 32;             // output tiles over the head dim
   static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile
   static constexpr int KVPT = (KVEC + NTHR - 1) / NTHR;
-  static constexpr int VUNITS = (BKV / 2) * (DH / 8);   // (2-key pair, 8-dim chunk) units
-  static constexpr int VUPT = (VUNITS + NTHR - 1) / NTHR;
+  static constexpr int VVPT = (KVEC + NTHR - 1) / NTHR;  // V: same 16-byte vectors as K
   static constexpr int KTILE = BKV * KROW;       // bf16 per K buffer
-  static constexpr int VTILE = DH * VROW;        // bf16 per V^T buffer
+  static constexpr int VTILE = BKV * VROW;       // bf16 per V buffer (row-major)
 };
 
 template <int DH, int HPW, int NWAVE>
@@ -207,29 +199,22 @@ __device__ __forceinline__ void gated_attn_item(
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
 
-  // K: 16-byte vectors tid + i*NTHR of the tile (row, 8-element chunk), to
-  // LDS row-major with the padded row stride; V: units (key pair, 8-dim
-  // chunk), transposed into V^T rows 8*chunk .. +8 at the permuted key slot.
-  // Offsets in global memory are bytes from the tile's first row (rows of k
-  // and v are kvstride elements apart).
-  int koff[C::KVPT], kdst[C::KVPT], voff[C::VUPT], vdst[C::VUPT];
+  // K and V: 16-byte vectors tid + i*NTHR of the tile (row, 8-element
+  // chunk), to LDS row-major with their padded row strides.  Offsets in
+  // global memory are bytes from the tile's first row (rows of k and v are
+  // kvstride elements apart).
+  int koff[C::KVPT], kdst[C::KVPT], vdst[C::KVPT];
 #pragma unroll
   for (int i = 0; i < C::KVPT; ++i) {
     const int kvi = (tid + i * NTHR) % C::KVEC;
     const int row = kvi / (DH / 8), col = 8 * (kvi % (DH / 8));
     koff[i] = (row * (int)kvstride + col) * 2;
     kdst[i] = row * C::KROW + col;
-  }
-#pragma unroll
-  for (int i = 0; i < C::VUPT; ++i) {
-    const int vu = (tid + i * NTHR) % C::VUNITS;
-    const int vkp = vu % (BKV / 2), vdc = vu / (BKV / 2);
-    voff[i] = ((2 * vkp) * (int)kvstride + 8 * vdc) * 2;
-    vdst[i] = (8 * vdc) * C::VROW + vpos(2 * vkp);
+    vdst[i] = row * C::VROW + col;
   }
   const int boff = (tid % BKV) * 4;
 
-  u32x4 kreg[C::KVPT], vreg[C::VUPT][2];
+  u32x4 kreg[C::KVPT], vreg[C::KVPT];
   float breg = 0.f;
 
   auto load_tile = [&](int t) {
@@ -244,11 +229,8 @@ __device__ __forceinline__ void gated_attn_item(
     for (int i = 0; i < C::KVPT; ++i)
       if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) kreg[i] = buf_ld16(rk, koff[i]);
 #pragma unroll
-    for (int i = 0; i < C::VUPT; ++i)
-      if (C::VUNITS % NTHR == 0 || tid + i * NTHR < C::VUNITS) {
-        vreg[i][0] = buf_ld16(rv, voff[i]);
-        vreg[i][1] = buf_ld16(rv, voff[i] + (int)kvstride * 2);
-      }
+    for (int i = 0; i < C::KVPT; ++i)
+      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) vreg[i] = buf_ld16(rv, koff[i]);
     breg = buf_ldf(rb, boff);
   };
   auto store_tile = [&](auto BUFC) {
@@ -259,16 +241,8 @@ __device__ __forceinline__ void gated_attn_item(
     for (int i = 0; i < C::KVPT; ++i)
       if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) st16(&skb[kdst[i]], kreg[i]);
 #pragma unroll
-    for (int i = 0; i < C::VUPT; ++i)
-      if (C::VUNITS % NTHR == 0 || tid + i * NTHR < C::VUNITS) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a0 = vreg[i][0][e >> 1], a1 = vreg[i][1][e >> 1];
-          const uint32_t pk = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u))
-                                      : ((a0 & 0xffffu) | (a1 << 16));
-          *reinterpret_cast<uint32_t*>(&svb[vdst[i] + e * C::VROW]) = pk;
-        }
-      }
+    for (int i = 0; i < C::KVPT; ++i)
+      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) st16(&svb[vdst[i]], vreg[i]);
     if (tid < BKV) {
       // bias columns of key tid: (hi, lo) bf16 parts of gain_h * b / s per head
       uint32_t w[4];
@@ -285,7 +259,12 @@ __device__ __forceinline__ void gated_attn_item(
 
   // per-lane LDS operand bases: every fragment read is base + constant offset
   const uint16_t* klane = sk + n * C::KROW + 8 * g;
-  const uint16_t* vlane = sv + n * C::VROW + 8 * g;
+  // V fragments by transposing reads: within each 16-lane group, lane s
+  // points at row 4kg + s/4 (kg = lane/32), columns 16((lane/16)%2) + 4(s%4)
+  // .. +4; the read hands lane i of the group the 4 keys of that row block
+  // at column 16((lane/16)%2) + i, i.e. the A operand of dim lane%32
+  const uint16_t* vlane =
+      sv + (4 * (lane >> 5) + ((lane & 15) >> 2)) * C::VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // ---- running state (one query per lane)
   floatx16 oacc[C::DT];
@@ -383,12 +362,21 @@ __device__ __forceinline__ void gated_attn_item(
   };
 
   // O^T += V^T . P^T for the tile in buffer BUF and the P^T words in pw
-  // (A operand: V^T row d = 32dt + n, 8 permuted keys); V^T reads run four
-  // MFMAs ahead of their use
+  // (A operand: dim 32dt + n, the 8 keys of K-step kk in P^T's order); the
+  // V reads run four MFMAs ahead of their use
   auto phase_pv = [&](auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
     const uint16_t* vl = vlane + BUF * C::VTILE;
-    auto vfrag = [&](int i) { return ld16(vl + 32 * (i % C::DT) * C::VROW + 16 * (i / C::DT)); };
+    // keys 16kk + 4kg + 0..3 and 16kk + 8 + 4kg + 0..3 of dims 32dt + lane%32
+    auto vfrag = [&](int i) {
+      const uint16_t* p = vl + 16 * (i / C::DT) * C::VROW + 32 * (i % C::DT);
+      const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(p));
+      const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(p + 8 * C::VROW));
+      const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+      return (u32x4){ua.x, ua.y, ub.x, ub.y};
+    };
     constexpr int NV = 4 * C::DT;
     u32x4 vr[4];
 #pragma unroll
