@@ -52,9 +52,6 @@
 
 #include "common.h"
 
-#ifndef TG_ATTN_WAVES
-#define TG_ATTN_WAVES 8
-#endif
 
 namespace tg {
 namespace {
@@ -65,6 +62,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int BKV = 64;                 // keys per tile
+constexpr int kAttnWaves = 8;           // waves per workgroup (two per SIMD)
 constexpr int QW = 32;                  // query rows per wave
 constexpr int NBUF = 3;                 // LDS tile buffers
 constexpr float kLog2e = 1.4426950408889634f;
@@ -546,7 +544,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const int hpw = G >= 4 ? 4 : G;
 #define TG_ATTN(DHv, HPWv)                                                                     \
   if (dh == DHv && hpw == HPWv)                                                                \
-    return launch_cfg<DHv, HPWv, TG_ATTN_WAVES>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
+    return launch_cfg<DHv, HPWv, kAttnWaves>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
                                  hkv, gain, temp, sm_scale, st);
   TG_ATTN(128, 1) TG_ATTN(128, 2) TG_ATTN(128, 4)
   TG_ATTN(64, 1) TG_ATTN(64, 2) TG_ATTN(64, 4)
