@@ -280,6 +280,8 @@ def ref_gated_attn_masked(q_full, k_full, v_full, b_full, keep_mask, cu_seqlens,
     for s in range(len(cu_seqlens) - 1):
         lo, hi = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
         km = keep_mask[lo:hi]
+        if not km.any():                             # no kept rows: nothing to evaluate
+            continue
         counts = np.cumsum(km)                       # m_i for every position
         pos = np.arange(1, hi - lo + 1, dtype=np.float64)
         lam = length_factor(counts.astype(np.float64).clip(min=1), pos, len_scale)

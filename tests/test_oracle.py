@@ -9,6 +9,8 @@ import os
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
 
 import oracle as O
 from oracle import readings as R
@@ -190,6 +192,22 @@ def test_select_bruteforce_small(seed):
         idx, pos, kb, cu = O.ref_select(b, pr, [0, n], [k])
         assert list(idx) == _brute_select(list(b), list(pr), k)
         assert np.array_equal(pos, idx)
+        assert cu[-1] == len(idx)
+
+
+@settings(max_examples=300, derandomize=True, deadline=None, database=None)
+@given(vals=st.lists(st.sampled_from([0.0, -0.0, 1.0, -1.0, 0.5, 2.5, math.inf, -math.inf,
+                                      math.nan]), max_size=9),
+       mask_bits=st.integers(0, 2 ** 9 - 1), extra=st.integers(0, 2))
+def test_select_bruteforce_hypothesis(vals, mask_bits, extra):
+    """Every budget from 0 to |P| + 2 on hypothesis-drawn tiny inputs drawn
+    from a tie-heavy pool with signed zeros, infinities and NaN."""
+    n = len(vals)
+    b = np.array(vals, np.float64)
+    pr = np.array([(mask_bits >> j) & 1 for j in range(n)], np.uint8)
+    for k in range(0, int(pr.sum()) + 1 + extra):
+        idx, _, _, cu = O.ref_select(b, pr, [0, n], [k])
+        assert list(idx) == _brute_select(list(b), list(pr), k)
         assert cu[-1] == len(idx)
 
 
@@ -378,6 +396,28 @@ def test_multiplicative_and_loggate_forms_equal_eq8(seed):
     eq8 = O.ref_gated_attn(*args)
     assert np.allclose(O.ref_gated_attn_multiplicative(*args), eq8, rtol=0, atol=1e-12)
     assert np.allclose(O.ref_gated_attn_loggate(*args), eq8, rtol=0, atol=1e-12)
+
+
+@settings(max_examples=60, derandomize=True, deadline=None, database=None)
+@given(seqlens=st.lists(st.integers(0, 12), min_size=1, max_size=3),
+       heads=st.sampled_from([(1, 1), (2, 1), (4, 2), (4, 4)]), dh=st.integers(1, 6),
+       keep_frac=st.sampled_from([0.0, 0.3, 0.7, 1.0]), n_prompt=st.integers(0, 4),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_attention_forms_agree_hypothesis(seqlens, heads, dh, keep_frac, n_prompt, seed):
+    """On hypothesis-drawn tiny cases the vectorised oracle, the explicit
+    double loop, and the full-length masked form evaluated on the kept rows
+    agree (empty sequences, no prompt tokens, nothing pruned included)."""
+    hq, hkv = heads
+    c = _attn_case(seed, seqlens=tuple(seqlens), hq=hq, hkv=hkv, dh=dh, keep_frac=keep_frac,
+                   n_prompt=n_prompt)
+    args = (c["q"], c["k"], c["v"], c["kb"], c["pos"], c["kcu"], c["gain"], c["temp"])
+    got = O.ref_gated_attn(*args)
+    assert np.allclose(got, O.ref_gated_attn_bruteforce(*args), rtol=0, atol=1e-12)
+    keep = np.zeros(c["cu"][-1], bool)
+    keep[c["idx"]] = True
+    full = O.ref_gated_attn_masked(c["qf"], c["kf"], c["vf"], c["b"], keep, c["cu"], c["gain"],
+                                   c["temp"])
+    assert np.allclose(got, full[c["idx"]], rtol=0, atol=1e-12)
 
 
 def test_bruteforce_tiny():
