@@ -56,6 +56,26 @@ def test_select_hypothesis(lens, mode, density, seed, kpick):
     check_select(b, pr, cu, k, f"lens={lens}")
 
 
+@settings(max_examples=10, **SETTINGS)
+@given(lens=st.lists(st.integers(0, 700), min_size=65, max_size=90),
+       mode=st.integers(0, 4), seed=st.integers(0, 2 ** 31 - 1),
+       kpick=st.integers(0, 5))
+def test_select_hypothesis_many_sequences(lens, mode, seed, kpick):
+    """65 .. 90 short sequences per batch (many sequences share a chunk
+    boundary region and the kept_cu offsets run over all of them)."""
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    b = rng.standard_normal(T) if mode < 3 else rng.integers(-2, 3, T).astype(np.float64)
+    pr = (rng.random(T) < 0.8).astype(np.uint8)
+    k = []
+    for s in range(len(lens)):
+        n_p = int(pr[cu[s]:cu[s + 1]].sum())
+        k.append([0, 1, max(n_p - 1, 0), n_p, n_p + 7, n_p // 3][(kpick + s) % 6])
+    say(f"select hypothesis: {len(lens)} sequences, T={T}")
+    check_select(b, pr, cu, k, f"{len(lens)} sequences")
+
+
 @settings(max_examples=25, **SETTINGS)
 @given(n_src=st.integers(1, 4000), n_rows=st.integers(1, 4000), row_words=st.integers(1, 700),
        seed=st.integers(0, 2 ** 31 - 1))

@@ -112,6 +112,34 @@ def test_select_large_single_sequence_full_and_pruned():
         check_select(b, pr, cu, [k], f"k={k}")
 
 
+@pytest.mark.parametrize("lens", [[140000, 130000], [300000]])
+def test_select_long_batches(lens):
+    """Batches of 270000 and 300000 tokens: 132 and 147 blocks of 2048
+    tokens, sequences spanning many chunks, a block of exact ties."""
+    say(f"select: long batch, lens={lens}")
+    rng = np.random.default_rng(sum(lens))
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    b = rng.standard_normal(T).astype(np.float32)
+    b[rng.random(T) < 0.01] = 1.5                   # a block of exact ties
+    pr = (rng.random(T) < 0.97).astype(np.uint8)
+    for k in ([8192] * len(lens), [0] * len(lens), [10 ** 6] * len(lens)):
+        check_select(b, pr, cu, k, f"k={k[0]}")
+
+
+def test_select_many_sequences():
+    """80 sequences of 0 .. 3000 tokens with heavy ties and per-sequence budgets."""
+    rng = np.random.default_rng(71)
+    lens = [int(v) for v in rng.integers(0, 3000, 80)]
+    say(f"select: {len(lens)} sequences")
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    b = rng.integers(-4, 5, T).astype(np.float32)   # heavy ties
+    pr = (rng.random(T) < 0.8).astype(np.uint8)
+    k = [int(v) for v in rng.integers(0, 2000, 80)]
+    check_select(b, pr, cu, k, "80 sequences")
+
+
 def test_select_is_deterministic():
     say("select: repeat runs are identical")
     b, pr, cu, k = generate_ragged_scores()
