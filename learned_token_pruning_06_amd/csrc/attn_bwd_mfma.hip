@@ -24,8 +24,7 @@
 // index contiguous where it is an A operand or the B' operand of C = A.B'^T
 // (one 16-byte read per lane and K-step); where the contraction runs down
 // the rows of a row-major tile (dO and Q in the dV/dK products, K in dQ)
-// the B operand is gathered with eight 16-bit reads whose 32 lanes touch 64
-// consecutive bytes.
+// the B operand is two transposing 8-byte reads (ds_read_b64_tr_b16).
 #include "common.h"
 
 namespace tg {
@@ -56,19 +55,30 @@ TG_DEVINL void mma_abt(floatx16& acc, const uint16_t* A, int lda, const uint16_t
   }
 }
 
+// 4 consecutive rows of one column per lane by a transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group, output element e of lane
+// i is element i % 4 of the 8 bytes that lane 4e + i / 4 addresses, so lane
+// s pointing at row s / 4, columns 4(s % 4) .. +4 hands lane i the rows
+// 0 .. 3 of column i
+TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p)));
+}
+
 // acc[32 x 32] += A[32 rows][K] . B[K][32 cols]; A k-contiguous, B row-major
-// (its 32 columns contiguous), gathered down the rows
+// (its 32 columns contiguous) in LDS, 8-byte aligned rows: the B operand of
+// lane (n, kg), rows 16s + 8kg .. +8 of column n, is two transposing reads
 template <int KSTEPS>
 TG_DEVINL void mma_ab_rows(floatx16& acc, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                            int lane) {
   const int r = lane & 31, kg = lane >> 5;
+  const uint16_t* bp = B + (8 * kg + ((lane & 15) >> 2)) * ldb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     const bf16x8 a = as_bf16x8(ld16(A + r * lda + 16 * s + 8 * kg));
-    bf16x8 b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      b[e] = __builtin_bit_cast(__bf16, B[(16 * s + 8 * kg + e) * ldb + r]);
+    const uint2 lo = ld_tr4(bp + 16 * s * ldb), hi = ld_tr4(bp + (16 * s + 4) * ldb);
+    const bf16x8 b = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
   }
 }
