@@ -175,6 +175,11 @@ int64_t score_dz_blocks(int64_t t_in, int n_cu);
 hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void* w, int64_t ldw,
                                int n, int64_t kdim, int splits, float* y, int64_t ldy,
                                hipStream_t st);
+// The same with W stored K-major, W[k][n] (rows ldw elements apart, w_rows
+// valid rows): Y[m, n] = sum_k X[m, k] W[k, n] over each split's K range.
+hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const void* w,
+                                     int64_t ldw, int64_t w_rows, int n, int64_t kdim, int splits,
+                                     float* y, int64_t ldy, hipStream_t st);
 hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
                             const void* w1, const float* b1, const float* w2, const uint8_t* pr,
                             const int32_t* cu, int n_seq, float eps, const float* b_raw,

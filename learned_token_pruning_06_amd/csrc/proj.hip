@@ -48,55 +48,83 @@ TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // F32OUT: the same GEMM for other callers, Y[t, n] (fp32, row stride ldy)
 // over the K range [k_per * z, +k_per) of workgroup z (split-K partials at
 // Y + z * ys), with W's rows ldw elements apart.
-template <bool F32OUT>
+// WROWS (with F32OUT): W is stored K-major instead, W[k][n] with rows ldw
+// elements apart and w_rows valid rows (later ones read as zeros).  Its
+// K-step tile is staged as [64 k][256 n] (rows padded to 272 elements) and
+// the A operand, 8 consecutive k of one column, is two transposing reads
+// (ds_read_b64_tr_b16): within each 16-lane group, output element e of lane
+// i is element i % 4 of the 8 bytes that lane 4e + i / 4 addresses.
+constexpr int kRowW = kTile + 16;    // bf16 per K-major W row (rows 8 banks apart)
+
+TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p)));
+}
+
+template <bool F32OUT, bool WROWS = false>
 __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
     uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t ldw, int k_per,
-    float* __restrict__ y, int64_t ldy, int64_t ys) {
+    float* __restrict__ y, int64_t ldy, int64_t ys, int64_t w_rows = 0) {
+  static_assert(F32OUT || !WROWS, "K-major W is for the fp32-output form");
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][WROWS ? kBK * kRowW : kTile * kRow];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int rg = wv & 3, ch = wv >> 2;
   const int64_t row0 = (int64_t)blockIdx.x * kTile;
   const int col0 = blockIdx.y * kTile;
+  int64_t w_bytes = (int64_t)kTile * ldw * 2;   // W rows of this tile (row-major W)
   if constexpr (F32OUT) {                        // this workgroup's K range
     const int64_t kb = (int64_t)blockIdx.z * k_per;
     x += kb;
-    w += kb;
+    if constexpr (WROWS) {
+      w += kb * ldw;
+      w_bytes = ((w_rows - kb) < 0 ? 0 : (w_rows - kb)) * ldw * 2 - (int64_t)col0 * 2;
+    } else {
+      w += kb;
+    }
     d = (int)((d - kb) < k_per ? (d - kb) : k_per);
     y += (int64_t)blockIdx.z * ys;
   } else {
     ldw = d;
+    w_bytes = (int64_t)kTile * ldw * 2;
   }
 
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
   // of the K-step, for both X (rows of this tile) and W (its output features)
   const int lrow = tid >> 3, lch = tid & 7;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row0 * xs, (t - row0) * xs * 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (int64_t)col0 * ldw, (int64_t)kTile * ldw * 2);
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(WROWS ? w + col0 : w + (int64_t)col0 * ldw, w_bytes);
+  // K-major W: thread vector i covers k-row (tid / 32) + 16 i, 16-byte chunk tid % 32
+  const int wrow = tid >> 5, wch = tid & 31;
   int xoff[4], woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
-    woff[i] = (int)(((int64_t)(lrow + 64 * i) * ldw + 8 * lch) * 2);
+    woff[i] = WROWS ? (int)(((int64_t)(wrow + 16 * i) * ldw + 8 * wch) * 2)
+                    : (int)(((int64_t)(lrow + 64 * i) * ldw + 8 * lch) * 2);
   }
   const int ldst = lrow * kRow + 8 * lch;
+  const int wdst = WROWS ? wrow * kRowW + 8 * wch : ldst;
   u32x4 xr[4], wr[4];
   auto fetch = [&](int k0) {
+    const int wk = WROWS ? (int)(2 * (int64_t)k0 * ldw) : 2 * k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + 2 * k0, 0, 0));
-      wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + 2 * k0, 0, 0));
+      wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + wk, 0, 0));
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
-      st16(&sw[buf][ldst + 64 * i * kRow], wr[i]);
+      st16(&sw[buf][wdst + (WROWS ? 16 * i * kRowW : 64 * i * kRow)], wr[i]);
     }
   };
 
@@ -118,13 +146,23 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const int buf = it & 1;
     const uint16_t* xb = sx[buf] + (64 * rg + n) * kRow + 32 * g;
     const uint16_t* wb = sw[buf] + (128 * ch + n) * kRow + 32 * g;
+    // K-major W: lane (m, g) needs k = 32g + 8s .. +8 of column 128ch + 32mt + m
+    const uint16_t* wt = sw[buf] + (32 * g + ((lane & 15) >> 2)) * kRowW + 128 * ch +
+                         16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       const bf16x8 b0 = as_bf16x8(ld16(xb + 8 * s));
       const bf16x8 b1 = as_bf16x8(ld16(xb + 32 * kRow + 8 * s));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = as_bf16x8(ld16(wb + 32 * mt * kRow + 8 * s));
+        bf16x8 a;
+        if constexpr (WROWS) {
+          const uint2 lo = ld_tr4(wt + 8 * s * kRowW + 32 * mt);
+          const uint2 hi = ld_tr4(wt + (8 * s + 4) * kRowW + 32 * mt);
+          a = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
+        } else {
+          a = as_bf16x8(ld16(wb + 32 * mt * kRow + 8 * s));
+        }
         acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mt][0], 0, 0, 0);
         acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mt][1], 0, 0, 0);
       }
@@ -195,7 +233,21 @@ hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d
                      static_cast<const uint16_t*>(x), x_row_stride, t, d,
                      static_cast<const uint16_t*>(w), nq, nkv, static_cast<uint16_t*>(q),
                      static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), (int64_t)d, d,
-                     nullptr, (int64_t)0, (int64_t)0);
+                     nullptr, (int64_t)0, (int64_t)0, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const void* w,
+                                     int64_t ldw, int64_t w_rows, int n, int64_t kdim, int splits,
+                                     float* y, int64_t ldy, hipStream_t st) {
+  if (m == 0) return hipSuccess;
+  int64_t k_per = (kdim + splits - 1) / splits;
+  k_per = (k_per + kBK - 1) / kBK * kBK;
+  const dim3 grid((unsigned)((m + kTile - 1) / kTile), (unsigned)(n / kTile), (unsigned)splits);
+  hipLaunchKernelGGL((gemm_abt_bf16<true, true>), grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x), xs, m, (int)kdim,
+                     static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
+                     (int)k_per, y, ldy, m * ldy, w_rows);
   return hipGetLastError();
 }
 
@@ -209,7 +261,7 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
   hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy);
+                     (int)k_per, y, ldy, m * ldy, (int64_t)0);
   return hipGetLastError();
 }
 

@@ -10,8 +10,10 @@
 // bf16 inputs with h = 256 and d % 256 == 0 run the products on the matrix
 // cores: z is recomputed by the scorer's own MFMA tiling with a backward
 // epilogue (dz in bf16 in both layouts, per-workgroup dw2 / db1 / db2 sums),
-// x and W1 are transposed once, and dW1 = dz^T x (split over token ranges)
-// and dx = dz W1 run on the projection's GEMM core with fp32 output.  dz
+// W1 is transposed once (x is read as stored: the GEMM core's K-major form
+// stages its token-major tiles and transposes them on the LDS reads), and
+// dW1 = dz^T x (split over token ranges) and dx = dz W1 run on the
+// projection's GEMM core with fp32 output.  dz
 // enters both products rounded to bf16.  Otherwise (fp32 inputs, other
 // shapes) everything is fp32 on the vector ALU, seven launches, fixed
 // reduction orders:
@@ -435,7 +437,7 @@ struct Layout {
   int64_t n_tb, per_split, tp;
   int n_split;
   bool mfma;
-  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, dzt, xt, w1t, total;
+  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, dzt, w1t, total;
 };
 
 Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_cu) {
@@ -444,7 +446,7 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   if (L.mfma) {
     // dz in bf16 [t][h] and transposed [h][tp] (tp = t rounded up to 64),
-    // x^T [d][tp], W1^T [d][h]; dW1 split over token ranges of whole 64-steps
+    // W1^T [d][h]; dW1 split over token ranges of whole 64-steps
     L.tp = (t + 63) / 64 * 64;
     L.n_tb = score_dz_blocks(t, n_cu);
     const int64_t steps = L.tp / 64 > 0 ? L.tp / 64 : 1;
@@ -475,10 +477,9 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
   L.db1p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
   L.db2p = off; off += al(sizeof(float) * (size_t)L.n_tb);
   L.dw1p = off; off += al(sizeof(float) * (size_t)L.n_split * h * d);
-  L.dzt = L.xt = L.w1t = off;
+  L.dzt = L.w1t = off;
   if (L.mfma) {
     L.dzt = off; off += al(sizeof(uint16_t) * (size_t)h * L.tp);
-    L.xt = off; off += al(sizeof(uint16_t) * (size_t)d * L.tp);
     L.w1t = off; off += al(sizeof(uint16_t) * (size_t)d * h);
   }
   L.total = off;
@@ -522,7 +523,6 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
     if constexpr (std::is_same<T, uint16_t>::value) {
       uint16_t* dzb = reinterpret_cast<uint16_t*>(w + L.dz);
       uint16_t* dzt = reinterpret_cast<uint16_t*>(w + L.dzt);
-      uint16_t* xt = reinterpret_cast<uint16_t*>(w + L.xt);
       uint16_t* w1t = reinterpret_cast<uint16_t*>(w + L.w1t);
       int64_t nb = 0;
       hipError_t e = launch_score_dz(x, xs, t, d, w1, b1, w2, dbt, dzb, dzt, L.tp, dw2p, db1p,
@@ -531,12 +531,11 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
       if (L.tp > t)
         hipLaunchKernelGGL(fill_zero_u16, dim3((unsigned)((h * (L.tp - t) + 255) / 256)), dim3(256),
                            0, st, dzt, (int64_t)h, L.tp, t, L.tp);
-      hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(d / 64), (unsigned)(L.tp / 64)), dim3(256),
-                         0, st, x, xs, t, (int64_t)d, xt, L.tp);
       hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(d / 64), (unsigned)((h + 63) / 64)),
                          dim3(256), 0, st, w1, (int64_t)d, (int64_t)h, (int64_t)d, w1t, (int64_t)h);
-      // dW1[h][c] = sum_j dz^T[h][j] x^T[c][j]  (token splits, fp32 partials)
-      e = launch_gemm_abt_f32(dzt, L.tp, h, xt, L.tp, d, L.tp, L.n_split, dw1p, d, st);
+      // dW1[h][c] = sum_j dz^T[h][j] x[j][c]  (x read as stored; token splits,
+      // fp32 partials)
+      e = launch_gemm_ab_kmajor_f32(dzt, L.tp, h, x, xs, t, d, L.tp, L.n_split, dw1p, d, st);
       if (e != hipSuccess) return e;
       // dx[j][c] = sum_h dz[j][h] W1^T[c][h]
       if (dx) {
