@@ -177,20 +177,34 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   // epilogue: lane (n, g) holds columns 32mt + 8(r/4) + 4g + r%4 of this
   // wave's column range, row 32 nt + n of its row range
   if constexpr (F32OUT) {
+    // fp32 rows leave through LDS (the K loop's tiles are free after its last
+    // barrier): per half of the wave's columns, the wave's 64 x 64 block goes
+    // to its own 16 KB region, then 16 lanes write 256 contiguous bytes of a
+    // row, 4 rows per store
+    constexpr int kLd = 68;                      // floats per staged row (rows 4 banks apart)
+    float* stage = reinterpret_cast<float*>(wv < 4 ? &sx[0][0] : &sw[0][0]) + (wv & 3) * 64 * kLd;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int64_t row = row0 + 64 * rg + 32 * nt + n;
-        if (row < t) {
-          float* p = y + row * ldy + col0 + 128 * ch + 32 * mt + 4 * g;
+      for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *reinterpret_cast<float4*>(p + 8 * r4) =
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int mt = 2 * hf + m2;
+            *reinterpret_cast<float4*>(stage + (32 * nt + n) * kLd + 32 * m2 + 8 * r4 + 4 * g) =
                 make_float4(acc[mt][nt][4 * r4], acc[mt][nt][4 * r4 + 1], acc[mt][nt][4 * r4 + 2],
                             acc[mt][nt][4 * r4 + 3]);
-        }
+          }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 4 * i + (lane >> 4), c4 = lane & 15;
+        const int64_t row = row0 + 64 * rg + rr;
+        const float4 v4 = *reinterpret_cast<const float4*>(stage + rr * kLd + 4 * c4);
+        if (row < t)
+          *reinterpret_cast<float4*>(y + row * ldy + col0 + 128 * ch + 64 * hf + 4 * c4) = v4;
       }
+    }
     return;
   }
 #pragma unroll
