@@ -75,7 +75,6 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int rg = wv & 3, ch = wv >> 2;
-  const int64_t row0 = (int64_t)blockIdx.x * kTile;
   const int col0 = blockIdx.y * kTile;
   int64_t w_bytes = (int64_t)kTile * ldw * 2;   // W rows of this tile (row-major W)
   if constexpr (F32OUT) {                        // this workgroup's K range
@@ -94,6 +93,12 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     w_bytes = (int64_t)kTile * ldw * 2;
   }
 
+  // row tiles blockIdx.x, + gridDim.x, ...: the fp32 form runs fewer
+  // workgroups than row tiles, so a tile's stores drain while the next
+  // tile's loads and products run
+  const int64_t m_tiles = (t + kTile - 1) / kTile;
+  for (int64_t rt = blockIdx.x; rt < m_tiles; rt += gridDim.x) {
+  const int64_t row0 = rt * kTile;
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
   // of the K-step, for both X (rows of this tile) and W (its output features)
   const int lrow = tid >> 3, lch = tid & 7;
@@ -205,8 +210,7 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
           *reinterpret_cast<float4*>(y + row * ldy + col0 + 128 * ch + 64 * hf + 4 * c4) = v4;
       }
     }
-    return;
-  }
+  } else {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int cbase = col0 + 128 * ch + 32 * mt;      // 32 columns, one destination (dh % 32 == 0)
@@ -234,6 +238,9 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
       }
     }
   }
+  }
+  __syncthreads();                               // LDS is restaged by the next row tile
+  }
 }
 
 }  // namespace
@@ -251,13 +258,27 @@ hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d
   return hipGetLastError();
 }
 
+// fp32 forms: one workgroup per CU in all (the kernel holds 147 KB of LDS),
+// each looping over row tiles; 0 in x when the CU count is unavailable
+dim3 f32_grid(int64_t m, int n, int splits) {
+  int n_cu = 0;
+  if (device_cu_count(&n_cu) != hipSuccess) return dim3(0, 1, 1);
+  const int64_t m_tiles = (m + kTile - 1) / kTile;
+  const int64_t others = (int64_t)(n / kTile) * splits;
+  int64_t gx = others > 0 ? n_cu / others : 1;
+  if (gx < 1) gx = 1;
+  if (gx > m_tiles) gx = m_tiles;
+  return dim3((unsigned)gx, (unsigned)(n / kTile), (unsigned)splits);
+}
+
 hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const void* w,
                                      int64_t ldw, int64_t w_rows, int n, int64_t kdim, int splits,
                                      float* y, int64_t ldy, hipStream_t st) {
   if (m == 0) return hipSuccess;
   int64_t k_per = (kdim + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
-  const dim3 grid((unsigned)((m + kTile - 1) / kTile), (unsigned)(n / kTile), (unsigned)splits);
+  const dim3 grid = f32_grid(m, n, splits);
+  if (grid.x == 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_abt_bf16<true, true>), grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
@@ -271,7 +292,8 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
   if (m == 0) return hipSuccess;
   int64_t k_per = (kdim + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
-  const dim3 grid((unsigned)((m + kTile - 1) / kTile), (unsigned)(n / kTile), (unsigned)splits);
+  const dim3 grid = f32_grid(m, n, splits);
+  if (grid.x == 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
