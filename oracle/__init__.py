@@ -9,5 +9,6 @@ from .ref import (silu, ref_score, ref_rmsnorm, ref_score_prenorm, ref_normalise
                   ref_gather, length_factor, ref_gated_attn, ref_gated_attn_masked,
                   ref_gated_attn_multiplicative, ref_gated_attn_loggate,
                   ref_gated_attn_bruteforce, ref_gated_attn_bwd, ref_score_bwd, ref_project,
+                  ref_rope, ref_project_qk_rope,
                   ref_gate)
 from .costs import token_layer_passes, attention_pair_ratio, causal_attention_flops

@@ -30,6 +30,14 @@ R21 a decode step over a (pruned) cache is the last query row of the prefill
 R22 LN2 (named, not defined, in §3 Eq. 1) is the RMSNorm of the Qwen3 family:
     a / sqrt(mean(a^2) + eps) * gamma per row; eps is passed explicitly
     (PARITY UNPINNED as a value, like EPS).
+R23 the projections of the kept rows (before the gated attention) may apply
+    the Qwen3 family's per-head RMSNorm to q and k (over head_dim, one
+    [head_dim] weight shared by all heads of q, another for k) and then the
+    rotary embedding in the rotate-half layout at each kept token's original
+    position in its sequence: pair (e, e + dh/2) of a head rotates by
+    pos * theta^(-2e/dh).  Neither is on the pages; the oracle's form is
+    pinned by an independent complex-number rotation, by the relative-position
+    property of rotated dot products and by the norm's closed forms.
 EPS is PARITY UNPINNED (a choice, passed explicitly to both sides).
 """
 EPS = 1e-6

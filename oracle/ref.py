@@ -546,6 +546,41 @@ def ref_project(xs: np.ndarray, wq, wk, wv, hq: int, hkv: int, dh: int):
     return q, k, v
 
 
+def ref_rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half layout (R23): for every head
+    vector x of row t (x[t, h, :], length dh) and pair e < dh/2 with angle
+    a = pos[t] * theta**(-2e/dh):
+        x[e]        -> x[e] cos a - x[e + dh/2] sin a
+        x[e + dh/2] -> x[e + dh/2] cos a + x[e] sin a."""
+    x = np.asarray(x, np.float64)
+    dh = x.shape[-1]
+    half = dh // 2
+    inv = float(theta) ** (-2.0 * np.arange(half) / dh)
+    ang = np.asarray(pos, np.float64)[:, None] * inv[None, :]          # [T, dh/2]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def ref_project_qk_rope(xs: np.ndarray, wq, wk, wv, hq: int, hkv: int, dh: int, pos,
+                        q_norm: Optional[np.ndarray], k_norm: Optional[np.ndarray],
+                        norm_eps: float, theta: float):
+    """The projections with the Qwen3-style per-head RMSNorm of q and k and
+    the rotary embedding at the kept tokens' original positions (R23): Q, K, V
+    as in ref_project, then q <- RMSNorm_dh(q) * q_norm, k <- RMSNorm_dh(k) *
+    k_norm (skipped when the weight is None), then RoPE on q and k (skipped
+    when theta <= 0).  v is the plain projection."""
+    q, k, v = ref_project(xs, wq, wk, wv, hq, hkv, dh)
+    if q_norm is not None:
+        q = ref_rmsnorm(q, q_norm, norm_eps)
+    if k_norm is not None:
+        k = ref_rmsnorm(k, k_norm, norm_eps)
+    if theta > 0:
+        q = ref_rope(q, pos, theta)
+        k = ref_rope(k, pos, theta)
+    return q, k, v
+
+
 # ---------------------------------------------------------------------------
 # whole step
 # ---------------------------------------------------------------------------

@@ -529,6 +529,64 @@ def test_projection_identity_weights_return_the_rows():
     assert np.array_equal(v.reshape(T, hkv * dh), x[:, hkv * dh:])
 
 
+# rotary embedding and q/k norm of the projections (reading R23)
+def test_rope_tiny_worked_example():
+    """dh = 4, theta = 10000: pair (x0, x2) turns at frequency 1, pair (x1, x3)
+    at 10000**(-1/2) = 0.01; position 1."""
+    x = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 1, 4)
+    got = O.ref_rope(x, np.array([1]), 10000.0).reshape(4)
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    want = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_equals_complex_rotation_and_preserves_pairs():
+    rng = _rng(61)
+    T, H, dh, theta = 7, 3, 16, 1e6
+    x = rng.standard_normal((T, H, dh))
+    pos = rng.integers(0, 200000, T)
+    got = O.ref_rope(x, pos, theta)
+    half = dh // 2
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(
+        1j * np.outer(pos, theta ** (-np.arange(0, dh, 2) / dh)))[:, None, :]
+    assert np.allclose(got[..., :half], z.real, rtol=0, atol=1e-12)
+    assert np.allclose(got[..., half:], z.imag, rtol=0, atol=1e-12)
+    pair_norm = lambda a: np.hypot(a[..., :half], a[..., half:])
+    assert np.allclose(pair_norm(got), pair_norm(x), rtol=1e-13)
+    assert np.array_equal(O.ref_rope(x, np.zeros(T, np.int64), theta), x)
+
+
+def test_rope_dot_products_depend_on_relative_position():
+    rng = _rng(62)
+    dh = 64
+    q = rng.standard_normal((1, 1, dh))
+    k = rng.standard_normal((1, 1, dh))
+    for m, n in [(0, 5), (17, 400), (1000, 1001), (90000, 131071)]:
+        a = float(np.sum(O.ref_rope(q, [m], 1e6) * O.ref_rope(k, [n], 1e6)))
+        b = float(np.sum(O.ref_rope(q, [0], 1e6) * O.ref_rope(k, [n - m], 1e6)))
+        assert abs(a - b) <= 1e-9 * (1 + abs(b))
+
+
+def test_project_qk_rope_composition():
+    """No norm weights and theta <= 0 give the plain projection; the norm
+    leaves each q and k head with unit RMS (unit weight, eps 0) and the
+    rotation keeps it."""
+    rng = _rng(63)
+    T, d, hq, hkv, dh = 9, 24, 4, 2, 8
+    xs = rng.standard_normal((T, d))
+    wq, wk, wv = (rng.standard_normal((d, h * dh)) for h in (hq, hkv, hkv))
+    pos = rng.integers(0, 5000, T)
+    plain = O.ref_project(xs, wq, wk, wv, hq, hkv, dh)
+    same = O.ref_project_qk_rope(xs, wq, wk, wv, hq, hkv, dh, pos, None, None, 1e-6, 0.0)
+    for a, b in zip(plain, same):
+        assert np.array_equal(a, b)
+    q, k, v = O.ref_project_qk_rope(xs, wq, wk, wv, hq, hkv, dh, pos, np.ones(dh), np.ones(dh),
+                                    0.0, 1e6)
+    for a in (q, k):
+        assert np.allclose(np.sqrt(np.mean(a * a, axis=-1)), 1.0, rtol=1e-12)
+    assert np.array_equal(v, plain[2])
+
+
 def test_projection_head_layout_and_linearity():
     rng = np.random.default_rng(32)
     T, d, hq, hkv, dh = 4, 6, 3, 1, 2
