@@ -288,6 +288,34 @@ tg_status tg_qkv_proj(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t 
                       void* v, tg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * tg_qkv_proj_rope -- tg_qkv_proj followed, in the same kernel, by the
+ * per-head treatment of q and k in the Qwen3 family: an RMSNorm over each
+ * head's dh values, then the rotary embedding at each kept token's original
+ * position (the pages give neither; kept_pos from tg_select_topk holds the
+ * positions, §4.1: pruned tokens leave gaps, kept ones keep their place):
+ *
+ *   q[r, h, :] <- q[r, h, :] / sqrt(mean_e q[r, h, e]^2 + norm_eps) * q_norm
+ *   (k likewise with k_norm; skipped for a NULL weight), then for each pair
+ *   e < dh/2 with a = pos[r] * rope_theta^(-2e/dh):
+ *   (x[e], x[e + dh/2]) <- (x[e] cos a - x[e + dh/2] sin a,
+ *                           x[e + dh/2] cos a + x[e] sin a)   for x in q, k.
+ *
+ * The norm and the rotation run in fp32 on the accumulators; the angle is
+ * reduced to one turn in fp64.  v is as in tg_qkv_proj.
+ * pos     dev [t] i32 positions (required when rope_theta > 0).
+ * q_norm, k_norm dev [dh] f32 or NULL.  norm_eps >= 0.
+ * rope_theta > 1 turns the rotation on, <= 0 off (values in (0, 1] are
+ * rejected).
+ * Supported: as tg_qkv_proj, with dh in {64, 128} and hq * dh, hkv * dh
+ * multiples of 128.
+ * ---------------------------------------------------------------------- */
+tg_status tg_qkv_proj_rope(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t,
+                           int32_t d, const void* w, int32_t hq, int32_t hkv, int32_t dh,
+                           const int32_t* pos, const float* q_norm, const float* k_norm,
+                           float norm_eps, float rope_theta, void* q, void* k, void* v,
+                           tg_stream stream);
+
+/* ------------------------------------------------------------------------
  * tg_gated_decode -- one decode step of token-gated attention over pruned KV
  * caches: a decode step attends to the cache and appends to it (§3, "Prefill,
  * decode, and the KV cache"); above the gate the cache holds only the kept

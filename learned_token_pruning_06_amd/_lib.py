@@ -35,6 +35,9 @@ PROTOTYPES = {
     "tg_gather": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "tg_qkv_proj": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i32, c_vp, c_i32, c_i32,
                                    c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "tg_qkv_proj_rope": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i32, c_vp, c_i32,
+                                        c_i32, c_i32, c_vp, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp,
+                                        c_vp, c_vp]),
     "tg_gated_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp, c_vp,
                                      c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
                                      c_vp]),

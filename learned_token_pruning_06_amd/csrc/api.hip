@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10400; }
+int tg_version(void) { return 10500; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -181,6 +181,41 @@ tg_status tg_qkv_proj(const void* x, tg_dtype dt, int64_t xs, int64_t t, int32_t
   hipError_t e = tg::launch_qkv_proj(x, xs, t, d, w, hq * dh, hkv * dh, q, k, v,
                                      (hipStream_t)stream);
   return from_hip(e, "tg_qkv_proj launch");
+}
+
+tg_status tg_qkv_proj_rope(const void* x, tg_dtype dt, int64_t xs, int64_t t, int32_t d,
+                           const void* w, int32_t hq, int32_t hkv, int32_t dh, const int32_t* pos,
+                           const float* q_norm, const float* k_norm, float norm_eps,
+                           float rope_theta, void* q, void* k, void* v, tg_stream stream) {
+  if (t < 0 || d < 1 || hq < 1 || hkv < 1 || dh < 1 || xs < d)
+    return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: bad sizes");
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: bad dtype");
+  if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj_rope: only bf16 is implemented");
+  if (rope_theta != rope_theta || (rope_theta > 0.0f && rope_theta <= 1.0f))
+    return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: rope_theta must be > 1, or <= 0 for none");
+  if ((q_norm || k_norm) && !(norm_eps >= 0.0f))
+    return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: norm_eps must be >= 0");
+  if (rope_theta > 0.0f && t > 0 && !pos)
+    return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: positions are needed for the rotation");
+  const int64_t nq = (int64_t)hq * dh, nkv = (int64_t)hkv * dh;
+  if ((dh != 64 && dh != 128) || nq % 128 != 0 || nkv % 128 != 0)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_qkv_proj_rope: need dh in {64, 128} and hq * dh, hkv * dh multiples of 128");
+  const int64_t n_tot = nq + 2 * nkv;
+  if (d % 64 != 0 || n_tot % 256 != 0 || n_tot > INT32_MAX)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_qkv_proj_rope: need d %% 64 == 0, (hq + 2 hkv) * dh %% 256 == 0");
+  if (xs % 8 != 0 || xs >= ((int64_t)1 << 22) || (int64_t)d * 256 * 2 > INT32_MAX)
+    return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj_rope: row stride must be a multiple of 8, < 2^22");
+  if (t > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj_rope: too many rows");
+  if (t == 0) return ok();
+  if (!x || !w || !q || !k || !v) return fail(TG_ERR_INVALID_ARG, "tg_qkv_proj_rope: null pointer");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 8) || !aligned(k, 8) || !aligned(v, 8))
+    return fail(TG_ERR_UNSUPPORTED, "tg_qkv_proj_rope: x, w 16-byte and q, k, v 8-byte aligned");
+  hipError_t e = tg::launch_qkv_proj_rope(x, xs, t, d, w, (int)nq, (int)nkv, dh, pos, q_norm,
+                                          k_norm, norm_eps, rope_theta, q, k, v,
+                                          (hipStream_t)stream);
+  return from_hip(e, "tg_qkv_proj_rope launch");
 }
 
 // ------------------------------------------------------------- attention

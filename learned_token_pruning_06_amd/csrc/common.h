@@ -158,6 +158,13 @@ hipError_t launch_gather(const void* src, int64_t src_stride, int64_t n_src, int
 
 hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d, const void* w,
                            int nq, int nkv, void* q, void* k, void* v, hipStream_t st);
+// The same with the per-head RMSNorm of q and k (weights qn, kn over dh, null
+// to skip) and the rotate-half rotary embedding at pos[row] (rope_theta > 1,
+// or <= 0 to skip); dh is 64 or 128, nq and nkv multiples of 128.
+hipError_t launch_qkv_proj_rope(const void* x, int64_t x_row_stride, int64_t t, int d,
+                                const void* w, int nq, int nkv, int dh, const int32_t* pos,
+                                const float* qn, const float* kn, float eps, float rope_theta,
+                                void* q, void* k, void* v, hipStream_t st);
 
 size_t decode_ws_bytes(int n_seq, int hq, int hkv, int dh, int64_t max_len);
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,

@@ -62,13 +62,30 @@ TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
       uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p)));
 }
 
-template <bool F32OUT, bool WROWS = false>
+// QKE (bf16 form): the q and k columns get the per-head RMSNorm over dh
+// (weight qn / kn, skipped when null) and then the rotate-half rotary
+// embedding at position pos[row] (skipped when log2_theta is 0) before they
+// are rounded; dh is 64 or 128 and q, k, v start on 128-column boundaries,
+// so the 128 columns of a wave are one or two whole heads of one tensor.
+struct QkEpi {
+  const int32_t* pos;
+  const float* qn;
+  const float* kn;
+  float eps;
+  int dh;
+  double log2_theta;            // log2 of the rotary base; 0 turns the rotation off
+};
+
+template <bool F32OUT, bool WROWS = false, bool QKE = false>
 __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
     uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t ldw, int k_per,
-    float* __restrict__ y, int64_t ldy, int64_t ys, int64_t w_rows = 0) {
+    float* __restrict__ y, int64_t ldy, int64_t ys, int64_t w_rows = 0, QkEpi ep = QkEpi{}) {
   static_assert(F32OUT || !WROWS, "K-major W is for the fp32-output form");
+  static_assert(!(F32OUT && QKE), "the q/k epilogue is for the bf16 form");
+  __shared__ double s_turns[64];                  // QKE: rotation per position, in turns
+  __shared__ float s_norm[2][128];                 // QKE: the q and k norm weights
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][WROWS ? kBK * kRowW : kTile * kRow];
   const int tid = threadIdx.x;
@@ -76,6 +93,14 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   const int n = lane & 31, g = lane >> 5;
   const int rg = wv & 3, ch = wv >> 2;
   const int col0 = blockIdx.y * kTile;
+  if constexpr (QKE) {                            // published by the K loop's first barrier
+    if (tid < ep.dh / 2)
+      s_turns[tid] = exp2(-2.0 * tid / ep.dh * ep.log2_theta) * 0.15915494309189535;
+    if (tid < ep.dh) {
+      s_norm[0][tid] = ep.qn ? ep.qn[tid] : 1.0f;
+      s_norm[1][tid] = ep.kn ? ep.kn[tid] : 1.0f;
+    }
+  }
   int64_t w_bytes = (int64_t)kTile * ldw * 2;   // W rows of this tile (row-major W)
   if constexpr (F32OUT) {                        // this workgroup's K range
     const int64_t kb = (int64_t)blockIdx.z * k_per;
@@ -211,6 +236,64 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
       }
     }
   } else {
+  if constexpr (QKE) {
+    const int wbase = col0 + 128 * ch;               // the wave's 128 columns: q, k or v
+    if (wbase < nq + nkv) {
+      const bool norm = wbase < nq ? ep.qn != nullptr : ep.kn != nullptr;
+      const float* nw = s_norm[wbase < nq ? 0 : 1];
+      const int dh = ep.dh;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (norm) {
+          // per head: sum of squares over the lane's 64 values of the row and
+          // its partner lane (n, 1 - g), then scale by weight / RMS
+          float ss0 = 0.f, ss1 = 0.f;                  // heads of mt 0-1 and 2-3 (dh 64)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float a = acc[mt][nt][r];
+              if (mt < 2) ss0 = fmaf(a, a, ss0);
+              else ss1 = fmaf(a, a, ss1);
+            }
+          ss0 += __shfl_xor(ss0, 32, 64);
+          ss1 += __shfl_xor(ss1, 32, 64);
+          const float inv0 = dh == 128 ? 1.0f / sqrtf((ss0 + ss1) / 128.0f + ep.eps)
+                                       : 1.0f / sqrtf(ss0 / 64.0f + ep.eps);
+          const float inv1 = dh == 128 ? inv0 : 1.0f / sqrtf(ss1 / 64.0f + ep.eps);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);   // column in the wave
+              acc[mt][nt][r] *= (mt < 2 ? inv0 : inv1) * nw[c % dh];
+            }
+        }
+        if (ep.log2_theta > 0.0) {
+          // rotate pair (e, e + dh/2): e in columns of mt (dh 128: mt 0, 1 with
+          // partners mt + 2; dh 64: mt 0, 2 with partners mt + 1)
+          const int64_t row = row0 + 64 * rg + 32 * nt + n;
+          const double p = row < t ? (double)ep.pos[row] : 0.0;
+#pragma unroll
+          for (int pi = 0; pi < 2; ++pi) {
+            const int mlo = dh == 128 ? pi : 2 * pi, mhi = dh == 128 ? pi + 2 : 2 * pi + 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int e = (dh == 128 ? 32 * pi : 0) + 8 * (r >> 2) + 4 * g + (r & 3);
+              // the angle in turns, reduced to [-1/2, 1/2] in fp64; the
+              // hardware sine and cosine take turns
+              const double turns = p * s_turns[e];
+              const float fr = (float)(turns - rint(turns));
+              const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+              const float x1 = acc[mlo][nt][r], x2 = acc[mhi][nt][r];
+              acc[mlo][nt][r] = x1 * cs - x2 * sn;
+              acc[mhi][nt][r] = x2 * cs + x1 * sn;
+            }
+          }
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int cbase = col0 + 128 * ch + 32 * mt;      // 32 columns, one destination (dh % 32 == 0)
@@ -254,7 +337,24 @@ hipError_t launch_qkv_proj(const void* x, int64_t x_row_stride, int64_t t, int d
                      static_cast<const uint16_t*>(x), x_row_stride, t, d,
                      static_cast<const uint16_t*>(w), nq, nkv, static_cast<uint16_t*>(q),
                      static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), (int64_t)d, d,
-                     nullptr, (int64_t)0, (int64_t)0, (int64_t)0);
+                     nullptr, (int64_t)0, (int64_t)0, (int64_t)0, QkEpi{});
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_rope(const void* x, int64_t x_row_stride, int64_t t, int d,
+                                const void* w, int nq, int nkv, int dh, const int32_t* pos,
+                                const float* qn, const float* kn, float eps, float rope_theta,
+                                void* q, void* k, void* v, hipStream_t st) {
+  if (t == 0) return hipSuccess;
+  const int n_tot = nq + 2 * nkv;
+  const dim3 grid((unsigned)((t + kTile - 1) / kTile), (unsigned)(n_tot / kTile));
+  // rope_theta > 1 (checked by the caller) gives log2_theta > 0; <= 0 turns RoPE off
+  QkEpi ep{pos, qn, kn, eps, dh, rope_theta > 1.0f ? log2((double)rope_theta) : 0.0};
+  hipLaunchKernelGGL((gemm_abt_bf16<false, false, true>), grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x), x_row_stride, t, d,
+                     static_cast<const uint16_t*>(w), nq, nkv, static_cast<uint16_t*>(q),
+                     static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), (int64_t)d, d,
+                     nullptr, (int64_t)0, (int64_t)0, (int64_t)0, ep);
   return hipGetLastError();
 }
 
@@ -282,7 +382,7 @@ hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const
   hipLaunchKernelGGL((gemm_abt_bf16<true, true>), grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy, w_rows);
+                     (int)k_per, y, ldy, m * ldy, w_rows, QkEpi{});
   return hipGetLastError();
 }
 
@@ -297,7 +397,7 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
   hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy, (int64_t)0);
+                     (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{});
   return hipGetLastError();
 }
 

@@ -175,6 +175,38 @@ def qkv_proj(x: torch.Tensor, w: torch.Tensor, hq: int, hkv: int, dh: int,
     return q, k, v
 
 
+def qkv_proj_rope(x: torch.Tensor, w: torch.Tensor, hq: int, hkv: int, dh: int,
+                  pos: Optional[torch.Tensor] = None, q_norm: Optional[torch.Tensor] = None,
+                  k_norm: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                  rope_theta: float = 0.0, q: Optional[torch.Tensor] = None,
+                  k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None):
+    """tg_qkv_proj_rope: qkv_proj plus the per-head RMSNorm of q and k
+    (q_norm, k_norm [dh] fp32, None to skip) and the rotary embedding at
+    positions pos [T] int32 (rope_theta > 1; 0 for none)."""
+    lib = load()
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    if pos is not None:
+        _need(pos, "pos", torch.int32, 1)
+    if q_norm is not None:
+        _need(q_norm, "q_norm", torch.float32, 1)
+    if k_norm is not None:
+        _need(k_norm, "k_norm", torch.float32, 1)
+    t, d = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty(t, hq, dh, dtype=x.dtype, device=dev)
+    if k is None:
+        k = torch.empty(t, hkv, dh, dtype=x.dtype, device=dev)
+    if v is None:
+        v = torch.empty(t, hkv, dh, dtype=x.dtype, device=dev)
+    st = lib.tg_qkv_proj_rope(_p(x), _DT[x.dtype], x.stride(0), t, d, _p(w), hq, hkv, dh,
+                              _p(pos), _p(q_norm), _p(k_norm), float(norm_eps),
+                              float(rope_theta), _p(q), _p(k), _p(v), _stream(dev))
+    check("tg_qkv_proj_rope", st)
+    return q, k, v
+
+
 def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.Tensor,
                kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor, gain: torch.Tensor,
                temp: torch.Tensor, max_len: Optional[int] = None,

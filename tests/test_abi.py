@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10400
+    assert lib.tg_version() == 10500
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -178,6 +178,32 @@ def test_qkv_proj_validation(lib):
     assert pj(x=None) == 1
     assert pj(x=ctypes.c_void_p(0x10008)) == 2         # misaligned x
     assert pj(t=0) == 0                                # empty: nothing launched
+
+
+def test_qkv_proj_rope_validation(lib):
+    def pr(dt=1, xs=2048, t=100, d=2048, hq=16, hkv=8, dh=128, pos=FAKE, qn=FAKE, kn=FAKE,
+           eps=1e-6, theta=1e6, x=FAKE, q=FAKE):
+        return lib.tg_qkv_proj_rope(x, dt, xs, t, d, FAKE, hq, hkv, dh, pos, qn, kn, eps, theta,
+                                    q, FAKE, FAKE, None)
+    assert pr(t=-1) == 1
+    assert pr(dt=3) == 1
+    assert pr(dt=0) == 2                               # fp32 projection not implemented
+    assert pr(theta=1.0) == 1                          # a base in (0, 1] is rejected
+    assert pr(theta=0.5) == 1
+    assert pr(theta=float("nan")) == 1
+    assert pr(pos=None) == 1                           # rotation without positions
+    assert pr(eps=-1.0) == 1
+    assert pr(eps=float("nan")) == 1
+    assert pr(dh=96, hq=8, hkv=4) == 2                 # dh outside {64, 128}
+    assert pr(dh=64, hq=2, hkv=1) == 2                 # 128 q, 64 k columns: k not 128-aligned
+    assert pr(dh=64, hq=3, hkv=2) == 2                 # 192 q columns
+    assert pr(xs=1000, d=2048) == 1
+    assert pr(d=2000, xs=2048) == 2
+    assert pr(xs=2052) == 2
+    assert pr(x=None) == 1
+    assert pr(q=ctypes.c_void_p(0x10004)) == 2         # misaligned q
+    assert pr(t=0) == 0                                # empty: nothing launched
+    assert pr(t=0, pos=None) == 0
 
 
 def test_gated_decode_validation(lib):
