@@ -587,6 +587,19 @@ def test_project_qk_rope_composition():
     assert np.array_equal(v, plain[2])
 
 
+def test_qk_norm_worked_example():
+    """One head of dh = 4, [3, 4, 0, 0]: mean square 25/4, RMS 2.5, so the
+    normalised head is [1.2, 1.6, 0, 0]; the weight [1, 2, 3, 4] scales it
+    element by element to [1.2, 3.2, 0, 0].  Rotation off."""
+    xs = np.array([[1.0, 0.0]])
+    wq = np.array([[3.0, 4.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]])
+    wk = np.array([[0.0, 0.0, 0.0, 2.0], [0.0, 0.0, 0.0, 0.0]])
+    q, k, _ = O.ref_project_qk_rope(xs, wq, wk, wk, 1, 1, 4, [0], np.array([1.0, 2.0, 3.0, 4.0]),
+                                    None, 0.0, 0.0)
+    assert np.allclose(q.reshape(4), [1.2, 3.2, 0.0, 0.0], rtol=0, atol=1e-15)
+    assert np.array_equal(k.reshape(4), [0.0, 0.0, 0.0, 2.0])        # no k weight: untouched
+
+
 def test_projection_head_layout_and_linearity():
     rng = np.random.default_rng(32)
     T, d, hq, hkv, dh = 4, 6, 3, 1, 2
