@@ -179,22 +179,31 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     // K-major W: lane (m, g) needs k = 32g + 8s .. +8 of column 128ch + 32mt + m
     const uint16_t* wt = sw[buf] + (32 * g + ((lane & 15) >> 2)) * kRowW + 128 * ch +
                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // operands of 16-wide substep s + 1 are read from LDS while the MFMAs of
+    // substep s run: one read after each MFMA, the order pinned
+    bf16x8 bo[2][2], ao[2][4];
+    auto ld_op = [&](int s, int c, int i) {
+      if (i < 2) {
+        bo[c][i] = as_bf16x8(ld16(xb + 32 * i * kRow + 8 * s));
+      } else if constexpr (WROWS) {
+        const uint2 lo = ld_tr4(wt + 8 * s * kRowW + 32 * (i - 2));
+        const uint2 hi = ld_tr4(wt + (8 * s + 4) * kRowW + 32 * (i - 2));
+        ao[c][i - 2] = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
+      } else {
+        ao[c][i - 2] = as_bf16x8(ld16(wb + 32 * (i - 2) * kRow + 8 * s));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < 6; ++i) ld_op(0, 0, i);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const bf16x8 b0 = as_bf16x8(ld16(xb + 8 * s));
-      const bf16x8 b1 = as_bf16x8(ld16(xb + 32 * kRow + 8 * s));
+      const int c = s & 1;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        bf16x8 a;
-        if constexpr (WROWS) {
-          const uint2 lo = ld_tr4(wt + 8 * s * kRowW + 32 * mt);
-          const uint2 hi = ld_tr4(wt + (8 * s + 4) * kRowW + 32 * mt);
-          a = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
-        } else {
-          a = as_bf16x8(ld16(wb + 32 * mt * kRow + 8 * s));
-        }
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mt][1], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        acc[j >> 1][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[c][j >> 1], bo[c][j & 1],
+                                                                     acc[j >> 1][j & 1], 0, 0, 0);
+        if (s + 1 < kBK / 16 && j < 6) ld_op(s + 1, c ^ 1, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (it + 1 < nsteps) {
