@@ -92,7 +92,20 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int rg = wv & 3, ch = wv >> 2;
-  const int col0 = blockIdx.y * kTile;
+  // (column tile, K split) of this workgroup.  K-major W (one row tile): the
+  // column tiles of a split share its X slice, so they are placed on one XCD
+  // (workgroups are dealt round-robin over the 8 XCDs, each with its own L2)
+  int by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (WROWS) {
+    const int tiles = gridDim.y * gridDim.z;
+    if (gridDim.x == 1 && tiles % 8 == 0) {
+      const int lin = blockIdx.y + gridDim.y * blockIdx.z;
+      const int l = (lin % 8) * (tiles / 8) + lin / 8;
+      by = l % gridDim.y;
+      bz = l / gridDim.y;
+    }
+  }
+  const int col0 = by * kTile;
   if constexpr (QKE) {                            // published by the K loop's first barrier
     if (tid < ep.dh / 2)
       s_turns[tid] = exp2(-2.0 * tid / ep.dh * ep.log2_theta) * 0.15915494309189535;
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   }
   int64_t w_bytes = (int64_t)kTile * ldw * 2;   // W rows of this tile (row-major W)
   if constexpr (F32OUT) {                        // this workgroup's K range
-    const int64_t kb = (int64_t)blockIdx.z * k_per;
+    const int64_t kb = (int64_t)bz * k_per;
     x += kb;
     if constexpr (WROWS) {
       w += kb * ldw;
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
       w += kb;
     }
     d = (int)((d - kb) < k_per ? (d - kb) : k_per);
-    y += (int64_t)blockIdx.z * ys;
+    y += (int64_t)bz * ys;
   } else {
     ldw = d;
     w_bytes = (int64_t)kTile * ldw * 2;
