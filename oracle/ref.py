@@ -263,6 +263,37 @@ def ref_gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp,
     return out
 
 
+def ref_gated_attn_lse2(q, k, kept_b, kept_pos, kept_cu, gain, temp,
+                        sm_scale: Optional[float] = None, len_scale: str = R.LEN_SCALE) -> np.ndarray:
+    """The softmax normaliser of [TG] Eq. 8 per query row and head, in base 2:
+    lse2[i, h] = log2 sum_{j in S, j <= i} exp(tau_i^h (s q_i.k_j + gain_h b_j)),
+    the logits exactly as in ref_gated_attn.  alpha_ij = 2^(logit_ij log2 e -
+    lse2_i) is then the attention weight.  Returns [T, Hq] float64 (rows past
+    kept_cu[-1] are 0)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    kb = np.asarray(kept_b, dtype=np.float64)
+    T, Hq, dh = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else float(sm_scale)
+    out = np.zeros((T, Hq))
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        m = np.arange(n) + 1.0
+        lam = np.ones(n) if kept_pos is None else length_factor(
+            m, np.asarray(kept_pos[lo:hi], dtype=np.float64) + 1.0, len_scale)
+        for h in range(Hq):
+            z = scale * (q[lo:hi, h, :] @ k[lo:hi, h // G, :].T) + float(gain[h]) * kb[None, lo:hi]
+            logits = (float(temp[h]) * lam)[:, None] * z
+            logits[np.arange(n)[None, :] > np.arange(n)[:, None]] = -np.inf
+            mx = np.max(logits, axis=1)
+            out[lo:hi, h] = (mx + np.log(np.sum(np.exp(logits - mx[:, None]), axis=1))) / math.log(2.0)
+    return out
+
+
 # --- independent formulations used to pin ref_gated_attn ------------------
 def ref_gated_attn_masked(q_full, k_full, v_full, b_full, keep_mask, cu_seqlens, gain, temp,
                           sm_scale=None, len_scale: str = R.LEN_SCALE):

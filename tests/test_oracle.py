@@ -775,3 +775,47 @@ def test_score_bwd_matches_torch_autograd_fp64():
     got = O.ref_score_bwd(x, w1, b1, w2, 0.2, pr, cu, ki, kc, dbk, eps=1e-6)
     for g, t in zip(got, (tx, tw1, tb1, tw2, tb2)):
         assert np.allclose(g, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+# softmax normaliser of the gated attention, base 2 (the backward's statistic)
+def test_attn_lse2_closed_forms():
+    """Zero queries and zero scores make every visible logit 0, so row i of a
+    sequence has lse2 = log2(i + 1); a sequence's first row sees only itself,
+    so lse2 = tau (s q.k + gain b) / ln 2, here with s = 1/sqrt(2),
+    q.k = 2, gain 1.5, b 0.5, temp 0.75: 0.75 (sqrt 2 + 0.75) / ln 2."""
+    T, hq, hkv, dh = 7, 2, 1, 2
+    cu = np.array([0, 3, 7])
+    z = O.ref_gated_attn_lse2(np.zeros((T, hq, dh)), np.ones((T, hkv, dh)), np.zeros(T), None, cu,
+                              np.ones(hq), np.ones(hq))
+    want = np.log2(np.array([1, 2, 3, 1, 2, 3, 4], np.float64))
+    assert np.allclose(z, want[:, None], rtol=0, atol=1e-15)
+    q = np.zeros((1, 1, 2)); q[0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 2)); k[0, 0, 0] = 2.0
+    got = O.ref_gated_attn_lse2(q, k, np.array([0.5]), None, np.array([0, 1]), np.array([1.5]),
+                                np.array([0.75]))
+    assert abs(got[0, 0] - 0.75 * (math.sqrt(2.0) + 0.75) / math.log(2.0)) <= 1e-14
+
+
+def test_attn_lse2_normalises_the_attention():
+    """2^(logit log2 e - lse2) are the attention weights: they sum to one over
+    the visible keys, and applied to V they give ref_gated_attn's output."""
+    rng = _rng(71)
+    T, hq, hkv, dh = 40, 4, 2, 8
+    cu = np.array([0, 13, 13, 40])
+    q, k, v = (rng.standard_normal((T, h, dh)) for h in (hq, hkv, hkv))
+    kb = rng.standard_normal(T)
+    pos = np.concatenate([np.sort(rng.choice(100, 13, replace=False)),
+                          np.sort(rng.choice(300, 27, replace=False))])
+    gain, temp = rng.uniform(0.5, 1.5, hq), rng.uniform(0.8, 1.2, hq)
+    lse2 = O.ref_gated_attn_lse2(q, k, kb, pos, cu, gain, temp)
+    ref = O.ref_gated_attn(q, k, v, kb, pos, cu, gain, temp)
+    s = 1.0 / math.sqrt(dh)
+    for a, b in ((0, 13), (13, 40)):
+        n = b - a
+        lam = O.length_factor(np.arange(n) + 1.0, pos[a:b] + 1.0)
+        for h in range(hq):
+            logit = (temp[h] * lam)[:, None] * (s * q[a:b, h] @ k[a:b, h // 2].T + gain[h] * kb[None, a:b])
+            w = np.exp2(logit * math.log2(math.e) - lse2[a:b, h, None])
+            w[np.triu_indices(n, 1)] = 0.0
+            assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+            assert np.allclose(w @ v[a:b, h // 2], ref[a:b, h], rtol=0, atol=1e-12)
