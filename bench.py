@@ -286,19 +286,29 @@ def main():
         # the attention's backward (tg_gated_attn_bwd) on the step's kept rows:
         # bf16 inputs run on the matrix cores; algorithmic work 10 dh flop
         # per (query, key) pair and head (the five products of the backward)
+        # The forward hands the backward its output and row statistic (lse2),
+        # as a training step does; the time without them is reported beside.
         dout = torch.randn_like(q)
         ws_b = ops.workspace(lib.tg_gated_attn_bwd_workspace_size(t_kept, 1, wl.hq, wl.hkv), dev)
+        fwd_lse2 = torch.empty((wl.hq, t_kept), dtype=torch.float32, device=dev)
+        fwd_out = ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=max_kept,
+                                 lse2=fwd_lse2)
         t_bwd = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu, gain,
-                                                   temp, ws=ws_b), reps=3)
+                                                   temp, ws=ws_b, fwd_out=fwd_out,
+                                                   fwd_lse2=fwd_lse2), reps=3)
+        t_bwd_re = time_it(lambda: ops.gated_attn_bwd(q, k, v, dout, kept_b, kept_pos, kept_cu,
+                                                      gain, temp, ws=ws_b), reps=3)
         bwd_flops = 10.0 * wl.dh * wl.hq * t_kept * (t_kept + 1) / 2
         bwd_tf = bwd_flops / (t_bwd * 1e-6) / 1e12
         attn_bwd = {"kernel": "tg_gated_attn_bwd", "us": round(t_bwd, 1), "tflops": round(bwd_tf, 1),
                     "bound": "mfma", "peak_tflops": PEAK_BF16_TFLOPS,
                     "frac_of_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                    "us_statistics_recomputed": round(t_bwd_re, 1),
                     "note": "8704 kept rows, bf16 inputs on the matrix cores (P, dS in bf16), "
-                            "fp32 gradients; scores recomputed in 3 passes (18 dh flop per pair "
-                            "done)"}
-        del dout, ws_b
+                            "fp32 gradients; the forward's output and lse2 are passed in, so the "
+                            "scores are recomputed in 2 passes (14 dh flop per pair done); "
+                            "without them a third pass recomputes the statistics"}
+        del dout, ws_b, fwd_lse2, fwd_out
 
         # the scorer's backward (tg_score_bwd) from a gradient at the kept scores:
         # recompute z, then dW1 and dx (3 products of 2 d h flop per token),

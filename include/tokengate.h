@@ -177,6 +177,10 @@ tg_status tg_gather(const void* src, int64_t src_row_stride_bytes, int64_t n_src
  *   (host value, used only to size the launch; a larger one is harmless).
  * gain, temp dev [hq] f32: positive post-softplus values of Eq. 6 and Eq. 7.
  * sm_scale: s; <= 0 selects 1/sqrt(dh).
+ * lse2 dev [hq, t_kept] f32 out (head-major), or NULL (TG_BF16 only): each row's
+ *   log2 sum_{j <= i} exp(l_ij), with l_ij the logit above, i.e. the softmax
+ *   normaliser in base 2.  tg_gated_attn_bwd can take it with `out` instead
+ *   of recomputing it.
  * Supported: dh in {64, 128}; hq % hkv == 0 with hq/hkv in {1, 2, 4} or a
  * multiple of 4; dt = TG_BF16 (matrix cores) or TG_F32 (vector ALU).
  * ---------------------------------------------------------------------- */
@@ -184,7 +188,7 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
                         int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                         const int32_t* kept_cu_seqlens, int32_t n_seq,
                         int32_t max_kept_seqlen, int32_t hq, int32_t hkv, int32_t dh,
-                        const float* gain, const float* temp, float sm_scale,
+                        const float* gain, const float* temp, float sm_scale, float* lse2,
                         tg_stream stream);
 
 /* ------------------------------------------------------------------------
@@ -205,10 +209,15 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
  * dq   dev [t_kept, hq, dh] f32 out;  dk, dv dev [t_kept, hkv, dh] f32 out.
  * db   dev [t_kept] f32 out (rows past kept_cu_seqlens[n_seq] get 0).
  * dgain, dtemp dev [hq] f32 out.
+ * fwd_out, fwd_lse2: the forward's `out` and `lse2` for the same inputs, or
+ *      both NULL.  Given (TG_BF16 only; 16- and 4-byte aligned), D_i is taken
+ *      as dout_i . out_i (equal to sum_j P_ij dP_ij, since out_i =
+ *      sum_j P_ij v_j) and fwd_lse2 as the softmax normaliser, so the pass
+ *      that recomputes both from q, k, v and dout is skipped.  D then
+ *      carries out's bf16 rounding.  NULL: the statistics are recomputed.
  * ws   dev workspace of >= tg_gated_attn_bwd_workspace_size(t_kept, n_seq,
  *      hq, hkv) bytes, 4-byte aligned.
- * The softmax statistics are recomputed, so the forward output is not an
- * input.  TG_F32: fp32 arithmetic on the vector ALU.  TG_BF16: matrix cores
+ * TG_F32: fp32 arithmetic on the vector ALU.  TG_BF16: matrix cores
  * with fp32 accumulation; P and dS enter the dv, dk and dq products rounded
  * to bf16, while db, dgain and dtemp are formed from the fp32 values.
  * Results are bitwise reproducible.  Supported: dh in {64, 128},
@@ -221,7 +230,8 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
                             int32_t n_seq, int32_t hq, int32_t hkv, int32_t dh,
                             const float* gain, const float* temp, float sm_scale, float* dq,
                             float* dk, float* dv, float* db, float* dgain, float* dtemp,
-                            void* ws, size_t ws_bytes, tg_stream stream);
+                            const void* fwd_out, const float* fwd_lse2, void* ws,
+                            size_t ws_bytes, tg_stream stream);
 
 /* ------------------------------------------------------------------------
  * tg_score_bwd -- gradients of the gate's scorer (§4.1 Eq. 3) from the

@@ -49,7 +49,7 @@ const char* tg_status_string(int s) {
 
 const char* tg_last_error(void) { return g_err; }
 
-int tg_version(void) { return 10500; }
+int tg_version(void) { return 10600; }
 
 // ----------------------------------------------------------------- score
 size_t tg_score_workspace_size(int64_t t_in, int32_t n_seq) {
@@ -223,7 +223,7 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
                         int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                         const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
                         int32_t hkv, int32_t dh, const float* gain, const float* temp,
-                        float sm_scale, tg_stream stream) {
+                        float sm_scale, float* lse2, tg_stream stream) {
   if (t_kept < 0 || n_seq < 1 || max_len < 0 || hq < 1 || hkv < 1)
     return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: bad sizes");
   if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: hq %% hkv != 0");
@@ -240,10 +240,14 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
   if (max_len > t_kept) max_len = (int32_t)t_kept;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: tensors must be 16-byte aligned");
+  if (lse2 && dt != TG_BF16)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 is written by the bf16 path only");
+  if (lse2 && !aligned(lse2, 4))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 must be 4-byte aligned");
   hipError_t e;
   if (dt == TG_BF16)
     e = tg::launch_attn_bf16(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
-                             hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
+                             hkv, dh, gain, temp, sm_scale, lse2, (hipStream_t)stream);
   else
     e = tg::launch_attn_f32(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
                             hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
@@ -303,8 +307,8 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
                             const int32_t* kept_pos, const int32_t* kept_cu, int32_t n_seq,
                             int32_t hq, int32_t hkv, int32_t dh, const float* gain,
                             const float* temp, float sm_scale, float* dq, float* dk, float* dv,
-                            float* db, float* dgain, float* dtemp, void* ws, size_t ws_bytes,
-                            tg_stream stream) {
+                            float* db, float* dgain, float* dtemp, const void* fwd_out,
+                            const float* fwd_lse2, void* ws, size_t ws_bytes, tg_stream stream) {
   if (t_kept < 0 || n_seq < 1 || hq < 1 || hkv < 1)
     return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: bad sizes");
   if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: hq %% hkv != 0");
@@ -325,9 +329,15 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
       (dout && !aligned(dout, 16)) || (dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)) ||
       (dv && !aligned(dv, 16)) || !aligned(ws, 4))
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: tensors must be 16-byte aligned");
+  if ((fwd_out == nullptr) != (fwd_lse2 == nullptr))
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_bwd: give both fwd_out and fwd_lse2, or neither");
+  if (fwd_out && dt != TG_BF16)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: saved forward state is for bf16 only");
+  if (fwd_out && (!aligned(fwd_out, 16) || !aligned(fwd_lse2, 4)))
+    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: fwd_out 16-byte, fwd_lse2 4-byte aligned");
   hipError_t e = tg::launch_attn_bwd(q, k, v, dout, (int)dt, t_kept, kept_b, kept_pos, kept_cu,
                                      n_seq, hq, hkv, dh, gain, temp, sm_scale, dq, dk, dv, db,
-                                     dgain, dtemp, ws, (hipStream_t)stream);
+                                     dgain, dtemp, fwd_out, fwd_lse2, ws, (hipStream_t)stream);
   return from_hip(e, "tg_gated_attn_bwd launch");
 }
 

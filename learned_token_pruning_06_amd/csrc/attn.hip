@@ -138,7 +138,7 @@ __device__ __forceinline__ void gated_attn_item(
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int hg, int64_t slot,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale,
-    uint16_t* sk, uint16_t* sv) {
+    float* __restrict__ lse2, uint16_t* sk, uint16_t* sv) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   constexpr int NTHR = C::NTHR;
   const int tid = threadIdx.x;
@@ -447,6 +447,11 @@ __device__ __forceinline__ void gated_attn_item(
   const float lt = half_swap_sum(lsum);
   if (!qvalid) return;
   const float inv = 1.0f / lt;
+  // optional row statistic for the backward: log2 sum_j exp2(c_i acc_ij), in
+  // the units of the exponent, head-major [hq][t_kept] so the 32 queries of
+  // a wave store 128 contiguous bytes (both lane halves hold it; the first
+  // stores)
+  if (lse2 && g == 0) lse2[(int64_t)head * t_kept + lo + qa] = mrun + __log2f(lt);
   uint16_t* op = out + ((int64_t)(lo + qa) * hq + head) * DH;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
@@ -467,7 +472,7 @@ void gated_attn_bf16(
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
-    const float* __restrict__ temp, float sm_scale) {
+    const float* __restrict__ temp, float sm_scale, float* __restrict__ lse2) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   static_assert(NWAVE % HPW == 0 && C::NTHR >= BKV, "workgroup shape");
   __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
@@ -498,7 +503,7 @@ void gated_attn_bf16(
     if (rank >= n_real) break;
     gated_attn_item<DH, HPW, NWAVE>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept, hq,
                                     hkv, groups_y, hg, n_real - 1 - rank, gain, temp, sm_scale,
-                                    sk, sv);
+                                    lse2, sk, sv);
     __syncthreads();                               // LDS buffers are reused by the next slot
   }
 }
@@ -507,7 +512,7 @@ template <int DH, int HPW, int NWAVE>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                       const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,
                       int n_seq, int hq, int hkv, const float* gain, const float* temp,
-                      float sm_scale, hipStream_t st) {
+                      float sm_scale, float* lse2, hipStream_t st) {
   constexpr int QB = AttnCfg<DH, HPW, NWAVE>::QB;
   const int G = hq / hkv;
   const int groups_y = G / HPW;
@@ -528,7 +533,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), kept_b, kept_pos,
                      kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, (int)n_slots, gain, temp,
-                     sm_scale);
+                     sm_scale, lse2);
   return hipGetLastError();
 }
 
@@ -537,7 +542,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                             const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,
                             int n_seq, int max_len, int hq, int hkv, int dh, const float* gain,
-                            const float* temp, float sm_scale, hipStream_t st) {
+                            const float* temp, float sm_scale, float* lse2, hipStream_t st) {
   (void)max_len;
   if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)dh);
   const int G = hq / hkv;
@@ -545,7 +550,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
 #define TG_ATTN(DHv, HPWv)                                                                     \
   if (dh == DHv && hpw == HPWv)                                                                \
     return launch_cfg<DHv, HPWv, kAttnWaves>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
-                                 hkv, gain, temp, sm_scale, st);
+                                 hkv, gain, temp, sm_scale, lse2, st);
   TG_ATTN(128, 1) TG_ATTN(128, 2) TG_ATTN(128, 4)
   TG_ATTN(64, 1) TG_ATTN(64, 2) TG_ATTN(64, 4)
 #undef TG_ATTN

@@ -465,8 +465,8 @@ template <int DH, typename T>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* dout, int64_t t,
                     const float* kept_b, const int32_t* kept_pos, const int32_t* cu, int n_seq,
                     int hq, int hkv, const float* gain, const float* temp, float sm, float* dq,
-                    float* dk, float* dv, float* db, float* dgain, float* dtemp, void* ws,
-                    hipStream_t st) {
+                    float* dk, float* dv, float* db, float* dgain, float* dtemp,
+                    const void* fwd_out, const float* fwd_lse2, void* ws, hipStream_t st) {
   float* lse2 = static_cast<float*>(ws);
   float* dsum = lse2 + t * hq;
   float* dbpart = dsum + t * hq;
@@ -482,7 +482,7 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* dou
     // bf16: the matrix-core passes, then the shared final sums
     const hipError_t e = launch_attn_bwd_mfma(q, k, v, dout, t, kept_b, kept_pos, cu, n_seq, hq,
                                               hkv, DH, gain, temp, sm, lse2, dsum, dq, dk, dv,
-                                              dbpart, gpart, st);
+                                              dbpart, gpart, fwd_out, fwd_lse2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_finish, dim3((unsigned)((t + kThr - 1) / kThr + 1)), dim3(kThr), 0, st,
                        dbpart, gpart, cu, n_seq, t, hq, hkv, nq, db, dgain, dtemp);
@@ -512,12 +512,12 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            int64_t t, const float* kept_b, const int32_t* kept_pos,
                            const int32_t* cu, int n_seq, int hq, int hkv, int dh,
                            const float* gain, const float* temp, float sm_scale, float* dq,
-                           float* dk, float* dv, float* db, float* dgain, float* dtemp, void* ws,
-                           hipStream_t st) {
+                           float* dk, float* dv, float* db, float* dgain, float* dtemp,
+                           const void* fwd_out, const float* fwd_lse2, void* ws, hipStream_t st) {
   if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)dh);
 #define TG_BWD(DHv, Tv)                                                                         \
   return launch_t<DHv, Tv>(q, k, v, dout, t, kept_b, kept_pos, cu, n_seq, hq, hkv, gain, temp, \
-                           sm_scale, dq, dk, dv, db, dgain, dtemp, ws, st);
+                           sm_scale, dq, dk, dv, db, dgain, dtemp, fwd_out, fwd_lse2, ws, st);
   if (dt == 1) {
     if (dh == 128) { TG_BWD(128, uint16_t) }
     if (dh == 64) { TG_BWD(64, uint16_t) }

@@ -310,9 +310,33 @@ __global__ __launch_bounds__(kThr) void bwdm_stats(
       Ut = fmaf(su_[p][tid], f, Ut);
     }
     const int64_t row = sq.lo + q0 + tid;
-    lse2[row * hq + h] = mx + __log2f(Lt);
+    lse2[(int64_t)h * t + row] = mx + __log2f(Lt);
     dsum[row * hq + h] = Ut / Lt;
   }
+}
+
+// ---- pass 1 from saved forward state: D per (query, head) as dO_i . O_i,
+// which equals sum_j P_ij dP_ij because O_i = sum_j P_ij V_j and
+// dP_ij = dO_i . V_j.  DH / 8 lanes per (row, head), 16 bytes each.
+template <int DH>
+__global__ __launch_bounds__(256) void bwdm_dsum(const uint16_t* __restrict__ o,
+                                                 const uint16_t* __restrict__ dout, int64_t pairs,
+                                                 float* __restrict__ dsum) {
+  constexpr int L = DH / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t p = gid / L;
+  float acc = 0.0f;
+  if (p < pairs) {
+    const u32x4 a = ld16(o + gid * 8), b = ld16(dout + gid * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (p < pairs && (threadIdx.x % L) == 0) dsum[p] = acc;
 }
 
 // P and dl = P (dP - D) of this wave's 8 elements
@@ -372,7 +396,7 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
       const int i = q0 + tid;
       const bool ok = i < sq.len;
       ptau = ok ? temp[h] * length_lambda(kept_pos, sq.lo + i, i) : 0.0f;
-      plse = ok ? lse2[(sq.lo + i) * hq + h] : 0.0f;
+      plse = ok ? lse2[(int64_t)h * t + sq.lo + i] : 0.0f;
       pD = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
     }
   };
@@ -486,7 +510,7 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
     const float lam = ok ? length_lambda(kept_pos, sq.lo + i, i) : 0.0f;
     slam[tid] = lam;
     stau[tid] = temp[h] * lam;
-    slse[tid] = ok ? lse2[(sq.lo + i) * hq + h] : 0.0f;
+    slse[tid] = ok ? lse2[(int64_t)h * t + sq.lo + i] : 0.0f;
     sD[tid] = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
   }
   load_rows<DH>(sQ, q, sq.lo, sq.len, q0, hq, h);
@@ -572,20 +596,28 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 const int32_t* cu, int n_seq, int hq, int hkv, int dh,
                                 const float* gain, const float* temp, float sm, float* lse2,
                                 float* dsum, float* dq, float* dk, float* dv, float* dbpart,
-                                double* gpart, hipStream_t st) {
+                                double* gpart, const void* fwd_out, const float* fwd_lse2,
+                                hipStream_t st) {
   const int64_t nq = n_seq + (t + kB - 1) / kB;
+  const bool saved = fwd_out != nullptr && fwd_lse2 != nullptr;
+  const float* lse = saved ? fwd_lse2 : lse2;
+  const int64_t dsum_blocks = (t * hq * (dh / 8) + 255) / 256;
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kp = static_cast<const uint16_t*>(k);
   const uint16_t* vp = static_cast<const uint16_t*>(v);
   const uint16_t* op = static_cast<const uint16_t*>(dout);
 #define TG_BWDM(DHv)                                                                             \
-  hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp,  \
-                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum);   \
+  if (saved)                                                                                     \
+    hipLaunchKernelGGL((bwdm_dsum<DHv>), dim3((unsigned)dsum_blocks), dim3(256), 0, st,          \
+                       static_cast<const uint16_t*>(fwd_out), op, t * hq, dsum);                 \
+  else                                                                                           \
+    hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp, \
+                       op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum); \
   hipLaunchKernelGGL((bwdm_dkdv<DHv>), dim3((unsigned)nq, hkv), dim3(kThr), 0, st, qp, kp, vp,  \
-                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum,    \
+                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum,     \
                      dk, dv, dbpart);                                                            \
   hipLaunchKernelGGL((bwdm_dq<DHv>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp, op, \
-                     kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum, dq,    \
+                     kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, dq,     \
                      gpart);
   if (dh == 128) {
     TG_BWDM(128)

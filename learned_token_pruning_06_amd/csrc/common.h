@@ -195,24 +195,30 @@ hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d,
                             float* db2, void* ws, hipStream_t st);
 
 size_t attn_bwd_ws_bytes(int64_t t, int n_seq, int hq, int hkv);
+// fwd_out and fwd_lse2 (both or neither; bf16 only): the forward's output
+// and row statistics.  With them D = rowsum(dO . O) replaces the statistics
+// pass and fwd_lse2 is used as the rows' log2-sum-exp.
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
                                 int64_t t, const float* kept_b, const int32_t* kept_pos,
                                 const int32_t* cu, int n_seq, int hq, int hkv, int dh,
                                 const float* gain, const float* temp, float sm, float* lse2,
                                 float* dsum, float* dq, float* dk, float* dv, float* dbpart,
-                                double* gpart, hipStream_t st);
+                                double* gpart, const void* fwd_out, const float* fwd_lse2,
+                                hipStream_t st);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dt,
                            int64_t t, const float* kept_b, const int32_t* kept_pos,
                            const int32_t* cu, int n_seq, int hq, int hkv, int dh,
                            const float* gain, const float* temp, float sm_scale, float* dq,
-                           float* dk, float* dv, float* db, float* dgain, float* dtemp, void* ws,
-                           hipStream_t st);
+                           float* dk, float* dv, float* db, float* dgain, float* dtemp,
+                           const void* fwd_out, const float* fwd_lse2, void* ws, hipStream_t st);
 
+// lse2 (optional, [hq][t_kept]): each row's log2-sum-exp of its scaled
+// logits, the statistic the backward recomputes otherwise
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                             const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,
                             int dh, const float* gain, const float* temp, float sm_scale,
-                            hipStream_t st);
+                            float* lse2, hipStream_t st);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, void* out,
                            int64_t t_kept, const float* kept_b, const int32_t* kept_pos,

@@ -210,8 +210,12 @@ def qkv_proj_rope(x: torch.Tensor, w: torch.Tensor, hq: int, hkv: int, dh: int,
 def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.Tensor,
                kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor, gain: torch.Tensor,
                temp: torch.Tensor, max_len: Optional[int] = None,
-               sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
-    """tg_gated_attn: token-gated causal attention, q [T,Hq,dh], k/v [T,Hkv,dh]."""
+               sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+               lse2: Optional[torch.Tensor] = None):
+    """tg_gated_attn: token-gated causal attention, q [T,Hq,dh], k/v [T,Hkv,dh].
+    lse2 (optional, f32 [Hq, T], bf16 only) receives each row's softmax
+    normaliser in base 2, which gated_attn_bwd can take instead of
+    recomputing it."""
     lib = load()
     _need(q, "q", (torch.bfloat16, torch.float32), 3)
     _need(k, "k", q.dtype, 3)
@@ -224,12 +228,17 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
         _need(kept_pos, "kept_pos", torch.int32, 1)
     t, hq, dh = q.shape
     hkv = k.shape[1]
+    if lse2 is not None:
+        _need(lse2, "lse2", torch.float32, 2)
+        if tuple(lse2.shape) != (hq, t):
+            raise ValueError(f"lse2 must be [{hq}, {t}], got {tuple(lse2.shape)}")
     if out is None:
         out = torch.empty_like(q)
     n_seq = kept_cu.numel() - 1
     st = lib.tg_gated_attn(_p(q), _p(k), _p(v), _DT[q.dtype], _p(out), t, _p(kept_b),
                            _p(kept_pos), _p(kept_cu), n_seq, int(max_len if max_len else t), hq, hkv,
-                           dh, _p(gain), _p(temp), float(sm_scale or 0.0), _stream(q.device))
+                           dh, _p(gain), _p(temp), float(sm_scale or 0.0), _p(lse2),
+                           _stream(q.device))
     check("tg_gated_attn", st)
     return out
 
@@ -275,8 +284,11 @@ def score_bwd(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: tor
 def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
                    kept_b: torch.Tensor, kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor,
                    gain: torch.Tensor, temp: torch.Tensor, sm_scale: Optional[float] = None,
-                   ws: Optional[torch.Tensor] = None):
-    """tg_gated_attn_bwd: returns (dq, dk, dv, db, dgain, dtemp), all f32."""
+                   ws: Optional[torch.Tensor] = None, fwd_out: Optional[torch.Tensor] = None,
+                   fwd_lse2: Optional[torch.Tensor] = None):
+    """tg_gated_attn_bwd: returns (dq, dk, dv, db, dgain, dtemp), all f32.
+    fwd_out and fwd_lse2 (both or neither, bf16 only): the forward's output
+    and lse2, which replace the recomputation of the softmax statistics."""
     lib = load()
     _need(q, "q", (torch.bfloat16, torch.float32), 3)
     _need(k, "k", q.dtype, 3)
@@ -290,6 +302,14 @@ def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
         _need(kept_pos, "kept_pos", torch.int32, 1)
     t, hq, dh = q.shape
     hkv = k.shape[1]
+    if fwd_out is not None:
+        _need(fwd_out, "fwd_out", q.dtype, 3)
+        if fwd_out.shape != q.shape:
+            raise ValueError("fwd_out must have q's shape")
+    if fwd_lse2 is not None:
+        _need(fwd_lse2, "fwd_lse2", torch.float32, 2)
+        if tuple(fwd_lse2.shape) != (hq, t):
+            raise ValueError(f"fwd_lse2 must be [{hq}, {t}]")
     n_seq = kept_cu.numel() - 1
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty((t, hq, dh), **f32)
@@ -304,8 +324,8 @@ def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torc
     st = lib.tg_gated_attn_bwd(_p(q), _p(k), _p(v), _p(dout), _DT[q.dtype], t, _p(kept_b),
                                _p(kept_pos), _p(kept_cu), n_seq, hq, hkv, dh, _p(gain), _p(temp),
                                float(sm_scale or 0.0), _p(dq), _p(dk), _p(dv), _p(db), _p(dgain),
-                               _p(dtemp), _p(ws), ws.numel() * ws.element_size(),
-                               _stream(q.device))
+                               _p(dtemp), _p(fwd_out), _p(fwd_lse2), _p(ws),
+                               ws.numel() * ws.element_size(), _stream(q.device))
     check("tg_gated_attn_bwd", st)
     return dq, dk, dv, db, dgain, dtemp
 

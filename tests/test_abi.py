@@ -42,7 +42,7 @@ def test_header_declarations_are_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tg_version() == 10500
+    assert lib.tg_version() == 10600
     for code, name in enumerate(["TG_OK", "TG_ERR_INVALID_ARG", "TG_ERR_UNSUPPORTED",
                                  "TG_ERR_WORKSPACE", "TG_ERR_HIP"]):
         assert lib.tg_status_string(code).decode() == name
@@ -150,9 +150,11 @@ def test_gather_validation(lib):
 
 
 def test_attn_validation(lib):
-    def at(dt=1, t=100, n_seq=1, hq=16, hkv=8, dh=128, q=FAKE, gain=FAKE):
+    def at(dt=1, t=100, n_seq=1, hq=16, hkv=8, dh=128, q=FAKE, gain=FAKE, lse2=None):
         return lib.tg_gated_attn(q, FAKE, FAKE, dt, FAKE, t, FAKE, FAKE, FAKE, n_seq, t, hq, hkv,
-                                 dh, gain, FAKE, 0.0, None)
+                                 dh, gain, FAKE, 0.0, lse2, None)
+    assert at(dt=0, lse2=FAKE) == 2                    # the fp32 path writes no lse2
+    assert at(lse2=ctypes.c_void_p(0x10002)) == 2      # misaligned lse2
     assert at(hq=16, hkv=6) == 1
     assert at(dt=3) == 1
     assert at(t=-1) == 1
@@ -241,10 +243,14 @@ def test_gated_attn_bwd_validation(lib):
     assert ws_size(-1, 1, 16, 8) == 0
 
     def bw(dt=1, t=100, n_seq=1, hq=16, hkv=8, dh=128, q=FAKE, gain=FAKE, ws=FAKE,
-           ws_bytes=1 << 30, dq=FAKE):
+           ws_bytes=1 << 30, dq=FAKE, fo=None, fl=None):
         return lib.tg_gated_attn_bwd(q, FAKE, FAKE, FAKE, dt, t, FAKE, None, FAKE, n_seq, hq, hkv,
-                                     dh, gain, FAKE, 0.0, dq, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
-                                     ws_bytes, None)
+                                     dh, gain, FAKE, 0.0, dq, FAKE, FAKE, FAKE, FAKE, FAKE, fo, fl,
+                                     ws, ws_bytes, None)
+    assert bw(fo=FAKE) == 1                            # saved output without its lse2
+    assert bw(fl=FAKE) == 1
+    assert bw(dt=0, fo=FAKE, fl=FAKE) == 2             # saved state is for bf16 only
+    assert bw(fo=ctypes.c_void_p(0x10008), fl=FAKE) == 2
     assert bw(t=-1) == 1
     assert bw(n_seq=0) == 1
     assert bw(hq=16, hkv=6) == 1

@@ -1,0 +1,113 @@
+"""The forward's row statistic and the backward that takes it.
+
+tg_gated_attn's optional lse2 output against ref_gated_attn_lse2 (fp64).
+The kernel forms the normaliser from bf16-rounded probabilities (the ones
+that enter P.V, each within 2^-9 relative), so its base-2 log is within
+2^-9 / ln 2 = 2.8e-3 of the exact one, plus the fp32 error of the logits;
+the bar is |got - ref| <= 3e-3 + 1e-5 |ref|.
+
+tg_gated_attn_bwd with fwd_out and fwd_lse2 against ref_gated_attn_bwd,
+with the saved state taken (a) from the oracle (its output rounded to bf16,
+its lse2 to fp32) and (b) from tg_gated_attn itself, the pipeline a training
+step runs.  D = dout . out then carries out's bf16 rounding (2^-9 relative),
+which reaches every gradient through dl = P (dP - D): all six take the bf16
+bar, rel-L2 <= 1e-2, and dgain, dtemp the same bar relative to the oracle's
+error scale plus the value."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import bf16_dev, f32_dev, i32_dev, rel_l2, round_bf16, say
+from test_parity_attn_bwd import NAMES, bwd_case
+from workloads import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+BAR = 1e-2
+
+
+def _dev(case):
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    return ([bf16_dev(round_bf16(a)) for a in (q, k, v, do)], f32_dev(kb),
+            None if pos is None else i32_dev(pos), i32_dev(kc), f32_dev(gain), f32_dev(temp))
+
+
+@pytest.mark.parametrize("dh,hq,hkv,lens", [(128, 16, 8, [1, 5, 31, 64, 65, 130]),
+                                            (64, 4, 1, [300, 0, 77]),
+                                            (128, 8, 8, [2496])])
+def test_forward_lse2_matches_oracle(dh, hq, hkv, lens):
+    from learned_token_pruning_06_amd import ops
+    case = bwd_case(200 + dh + hq, lens, hq, hkv, dh, "bf16")
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    (qd, kd, vd, _), kbd, posd, kcd, gd, td = _dev(case)
+    t = q.shape[0]
+    lse2 = torch.full((hq, t), float("nan"), device=qd.device)
+    say(f"attn lse2: dh={dh} {hq}/{hkv} lens={lens}")
+    ops.gated_attn(qd, kd, vd, kbd, posd, kcd, gd, td, lse2=lse2)
+    torch.cuda.synchronize()
+    got = lse2.cpu().numpy().astype(np.float64).T
+    ref = O.ref_gated_attn_lse2(q, k, kb, pos, kc, gain, temp)
+    err = float(np.max(np.abs(got - ref) - 1e-5 * np.abs(ref)))
+    say(f"  worst |d lse2| beyond 1e-5 |ref|: {err:.2e}")
+    assert np.all(np.isfinite(got))
+    assert err <= 3e-3
+
+
+def _check(got, case, tag):
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    *ref, sgain, stemp = O.ref_gated_attn_bwd(q, k, v, kb, pos, kc, gain, temp, do,
+                                              error_scales=True)
+    scale = {"dgain": sgain, "dtemp": stemp}
+    errs = {}
+    for name, g, r in zip(NAMES, got, ref):
+        g = g.cpu().numpy().astype(np.float64)
+        errs[name] = (float(np.max(np.abs(g - r) / (np.abs(r) + scale[name])))
+                      if name in scale else rel_l2(g, r))
+    say(f"  {tag}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e <= BAR, f"{name}: {e:.3e} > {BAR}"
+
+
+@pytest.mark.parametrize("source", ["oracle", "forward"])
+@pytest.mark.parametrize("dh,hq,hkv,lens", [(128, 16, 8, [1, 5, 31, 32, 33, 64, 65, 130]),
+                                            (64, 16, 2, [200, 57]),
+                                            (128, 16, 8, [2496])])
+def test_bwd_with_saved_state_matches_oracle(source, dh, hq, hkv, lens):
+    from learned_token_pruning_06_amd import ops
+    case = bwd_case(300 + dh + hq + len(lens), lens, hq, hkv, dh, "bf16")
+    q, k, v, do, kb, pos, kc, gain, temp = case
+    (qd, kd, vd, dod), kbd, posd, kcd, gd, td = _dev(case)
+    t = q.shape[0]
+    say(f"attn bwd, saved state from the {source}: dh={dh} {hq}/{hkv} lens={lens}")
+    if source == "oracle":
+        fo = bf16_dev(round_bf16(O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp)))
+        fl = f32_dev(np.ascontiguousarray(O.ref_gated_attn_lse2(q, k, kb, pos, kc, gain, temp).T))
+    else:
+        fl = torch.empty((hq, t), dtype=torch.float32, device=qd.device)
+        fo = ops.gated_attn(qd, kd, vd, kbd, posd, kcd, gd, td, lse2=fl)
+    got = ops.gated_attn_bwd(qd, kd, vd, dod, kbd, posd, kcd, gd, td, fwd_out=fo, fwd_lse2=fl)
+    torch.cuda.synchronize()
+    _check(got, case, source)
+
+
+def test_bwd_saved_state_close_to_recomputed():
+    """Both modes on the same inputs agree to the bf16 bar, and the saved-state
+    mode is deterministic."""
+    from learned_token_pruning_06_amd import ops
+    case = bwd_case(400, [700, 301], 16, 8, 128, "bf16")
+    (qd, kd, vd, dod), kbd, posd, kcd, gd, td = _dev(case)
+    fl = torch.empty((16, qd.shape[0]), dtype=torch.float32, device=qd.device)
+    fo = ops.gated_attn(qd, kd, vd, kbd, posd, kcd, gd, td, lse2=fl)
+    a = ops.gated_attn_bwd(qd, kd, vd, dod, kbd, posd, kcd, gd, td)
+    b = ops.gated_attn_bwd(qd, kd, vd, dod, kbd, posd, kcd, gd, td, fwd_out=fo, fwd_lse2=fl)
+    c = ops.gated_attn_bwd(qd, kd, vd, dod, kbd, posd, kcd, gd, td, fwd_out=fo, fwd_lse2=fl)
+    torch.cuda.synchronize()
+    for name, x, y, z in zip(NAMES, a, b, c):
+        assert torch.equal(y, z), name
+        if name in ("dq", "dk", "dv", "db"):
+            e = rel_l2(y.cpu().numpy().astype(np.float64), x.cpu().numpy().astype(np.float64))
+            say(f"  {name}: saved vs recomputed rel-L2 {e:.2e}")
+            assert e <= BAR
