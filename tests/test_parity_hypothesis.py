@@ -128,3 +128,34 @@ def test_attn_hypothesis(lens, heads, dh, dtype, with_pos, prompt, seed):
     ref = O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp)
     err = rel_l2(got, ref)
     assert err <= ATTN_TOL[dtype], f"rel-L2 {err:.3e}"
+
+
+# head layouts the fused norm + rotary projection takes: hq * dh and hkv * dh
+# multiples of 128, (hq + 2 hkv) * dh a multiple of 256
+ROPE_HEADS = [(4, 2, 64), (2, 1, 128), (8, 4, 64), (4, 1, 128), (8, 2, 64), (6, 1, 128)]
+
+
+@settings(max_examples=15, **SETTINGS)
+@given(t=st.one_of(st.sampled_from([1, 255, 256, 257, 511]), st.integers(1, 700)),
+       d=st.sampled_from([64, 128, 192, 256, 512]), heads=st.sampled_from(ROPE_HEADS),
+       norm=st.sampled_from(["none", "q", "k", "both"]),
+       theta=st.sampled_from([0.0, 1e4, 5e5, 1e6]), seed=st.integers(0, 2 ** 31 - 1))
+def test_proj_rope_hypothesis(t, d, heads, norm, theta, seed):
+    """tg_qkv_proj_rope on drawn shapes, norm weights and rotary bases, with
+    positions anywhere below 2^20, against ref_project_qk_rope under the
+    element bound of test_parity_proj (one bf16 rounding plus 1e-3 of the
+    RMS)."""
+    from test_parity_proj import _check_rope
+    hq, hkv, dh = heads
+    rng = np.random.default_rng(seed)
+    bf = lambda a: f32_to_bf16_bits(np.asarray(a, np.float32))
+    x = bf(rng.standard_normal((t, d)))
+    s = 1.0 / np.sqrt(d)
+    wq, wk, wv = (bf(rng.standard_normal((d, n * dh)) * s) for n in (hq, hkv, hkv))
+    pos = rng.integers(0, 1 << 20, t).astype(np.int32)
+    wts = lambda: (1.0 + 0.3 * rng.standard_normal(dh)).astype(np.float32)
+    qn = wts() if norm in ("q", "both") else None
+    kn = wts() if norm in ("k", "both") else None
+    say(f"proj+rope hypothesis: t={t} d={d} {hq}/{hkv}x{dh} norm={norm} theta={theta:g}")
+    _check_rope(x, wq, wk, wv, hq, hkv, dh, pos if theta > 0 else None, qn, kn, theta,
+                f"t={t} d={d}")
