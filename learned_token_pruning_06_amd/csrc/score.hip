@@ -498,7 +498,10 @@ hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const
   int n_cu = 0;
   const hipError_t ce = device_cu_count(&n_cu);
   if (ce != hipSuccess) return ce;
-  const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
+  // at most 128 rows per workgroup: the backward epilogue does not fit the
+  // 256-row tile's registers (44 spills there; 900 against 920 us for the
+  // whole scorer backward at 131072 rows)
+  const int rg = (t_in + 127) / 128 >= n_cu ? 2 : 1;
   const int64_t nb = (t_in + 64 * rg - 1) / (64 * rg);
   *blocks = nb;
   if (t_in == 0) return hipSuccess;
@@ -516,7 +519,7 @@ hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const
 }
 
 int64_t score_dz_blocks(int64_t t_in, int n_cu) {
-  const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
+  const int rg = (t_in + 127) / 128 >= n_cu ? 2 : 1;
   return (t_in + 64 * rg - 1) / (64 * rg);
 }
 
