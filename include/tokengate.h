@@ -140,6 +140,31 @@ tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t*
                          tg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * tg_select_topk_noalloc -- tg_select_topk for callers that cannot allocate
+ * device memory at all (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same selection, the same kernels
+ * and the same arguments without ws / ws_bytes.  Its scratch memory is a
+ * static device array of TG_SELECT_SCRATCH_BYTES bytes, one per GPU, held
+ * by the library until the process ends; the call itself allocates nothing.
+ *
+ * Limit: tg_select_workspace_size(t_in, n_seq) must not exceed
+ * TG_SELECT_SCRATCH_BYTES (8 MiB: e.g. a single sequence of 2 million
+ * tokens, or 64 sequences of 128k); larger calls return TG_ERR_WORKSPACE
+ * before anything is launched.  The first call on a device looks up that
+ * device's copy of the array (a failure there is TG_ERR_HIP).
+ * Every call on one GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (different streams, or other host threads) race and give
+ * wrong results; calls in order on one stream are fine.  Nothing needs to
+ * be cleared between calls: the selector zeroes what it counts into.
+ * ---------------------------------------------------------------------- */
+#define TG_SELECT_SCRATCH_BYTES ((size_t)8 << 20)
+tg_status tg_select_topk_noalloc(const float* b, const uint8_t* prunable,
+                                 const int32_t* cu_seqlens, const int32_t* k, int32_t n_seq,
+                                 int64_t t_in, int64_t t_kept_capacity, int32_t* kept_idx,
+                                 int32_t* kept_pos, float* kept_b, int32_t* kept_cu_seqlens,
+                                 tg_stream stream);
+
+/* ------------------------------------------------------------------------
  * tg_gather -- compaction of the kept rows (§4.1: the residual stream of a
  * pruned token stops at layer L; only kept rows go on to the layers above).
  *

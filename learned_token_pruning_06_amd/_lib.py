@@ -32,6 +32,8 @@ PROTOTYPES = {
     "tg_select_workspace_size": (c_sz, [c_i64, c_i32]),
     "tg_select_topk": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_vp, c_vp,
                                       c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "tg_select_topk_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_vp,
+                                              c_vp, c_vp, c_vp, c_vp]),
     "tg_gather": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp]),
     "tg_qkv_proj": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i32, c_vp, c_i32, c_i32,
                                    c_i32, c_vp, c_vp, c_vp, c_vp]),

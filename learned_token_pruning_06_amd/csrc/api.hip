@@ -34,6 +34,28 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 }  // namespace
 
+static_assert(tg::kSelScratchBytes == TG_SELECT_SCRATCH_BYTES, "scratch size");
+
+hipError_t tg::device_cu_count(int* n_cu) {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n_cu = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*n_cu < 1) *n_cu = 1;
+  if (cached) cache[dev].store(*n_cu, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 extern "C" {
 
 const char* tg_status_string(int s) {
@@ -138,6 +160,35 @@ tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t*
   hipError_t e = tg::launch_select(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx,
                                    kept_pos, kept_b, kept_cu_seqlens, ws, (hipStream_t)stream);
   return from_hip(e, "tg_select_topk launch");
+}
+
+tg_status tg_select_topk_noalloc(const float* b, const uint8_t* prunable,
+                                 const int32_t* cu_seqlens, const int32_t* k, int32_t n_seq,
+                                 int64_t t_in, int64_t cap, int32_t* kept_idx, int32_t* kept_pos,
+                                 float* kept_b, int32_t* kept_cu_seqlens, tg_stream stream) {
+  if (n_seq < 1 || t_in < 0 || cap < 0)
+    return fail(TG_ERR_INVALID_ARG,
+                "tg_select_topk_noalloc: need n_seq >= 1, t_in >= 0, capacity >= 0");
+  if (t_in > INT32_MAX - 4096)
+    return fail(TG_ERR_UNSUPPORTED, "tg_select_topk_noalloc: t_in too large");
+  if (!cu_seqlens || !k || !kept_cu_seqlens)
+    return fail(TG_ERR_INVALID_ARG, "tg_select_topk_noalloc: null pointer");
+  if (t_in > 0 && (!b || !prunable))
+    return fail(TG_ERR_INVALID_ARG, "tg_select_topk_noalloc: null pointer");
+  if (cap > 0 && !kept_idx)
+    return fail(TG_ERR_INVALID_ARG, "tg_select_topk_noalloc: kept_idx is null");
+  const size_t need = tg::select_ws_bytes(t_in, n_seq);
+  if (need > TG_SELECT_SCRATCH_BYTES)
+    return fail(TG_ERR_WORKSPACE,
+                "tg_select_topk_noalloc: t_in = %lld, n_seq = %d need %zu bytes of scratch, "
+                "more than the static %zu",
+                (long long)t_in, (int)n_seq, need, (size_t)TG_SELECT_SCRATCH_BYTES);
+  void* ws = nullptr;
+  hipError_t e = tg::select_scratch(&ws);
+  if (e != hipSuccess) return from_hip(e, "tg_select_topk_noalloc: scratch address");
+  e = tg::launch_select(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx, kept_pos, kept_b,
+                        kept_cu_seqlens, ws, (hipStream_t)stream);
+  return from_hip(e, "tg_select_topk_noalloc launch");
 }
 
 // ---------------------------------------------------------------- gather

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #define TG_DEVINL __device__ __forceinline__
 
 namespace tg {
@@ -119,23 +121,18 @@ TG_DEVINL uint32_t ld_acquire_u32(const uint32_t* p) {
 // ---------------------------------------------------------------------------
 namespace tg {
 
-// compute units of the current device, cached per device (host side; sizes
-// the persistent attention grid and the scorer's row tiles)
-inline hipError_t device_cu_count(int* n_cu) {
-  static int cache[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *n_cu = cache[dev];
-    return hipSuccess;
-  }
-  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (*n_cu < 1) *n_cu = 1;
-  if (dev >= 0 && dev < 64) cache[dev] = *n_cu;
-  return hipSuccess;
-}
+constexpr int kMaxDevices = 64;      // devices the per-device host caches cover
+
+// compute units of the current device (host side; sizes the persistent
+// attention grid and the scorer's row tiles), cached per device; the cache
+// entries are atomics, so concurrent first calls race benignly (both store
+// the same value)
+hipError_t device_cu_count(int* n_cu);
+
+// Bytes of the selector's static scratch array (tg_select_topk_noalloc).
+constexpr size_t kSelScratchBytes = (size_t)8 << 20;
+// Device address of this GPU's copy of that array (looked up once per device).
+hipError_t select_scratch(void** ptr);
 
 constexpr int kScoreChunk = 2048;    // tokens per normalisation block
 constexpr int kSelChunk = 2048;      // tokens per selection block

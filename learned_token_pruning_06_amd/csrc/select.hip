@@ -18,7 +18,15 @@
 //
 // Launches: init, pass0, pass1, pass2, count (+ kept_cu), write (each block
 // derives its chunk's offsets from the counts of the earlier chunks).
+#include <mutex>
+
 #include "common.h"
+
+// Scratch memory of the allocation-free selector (tg_select_topk_noalloc):
+// one copy per GPU, held until the process ends.  Host code never passes
+// this name to a kernel: the device address comes from hipGetSymbolAddress
+// (select_scratch below), once per device.
+static __device__ __align__(256) unsigned char scratch[tg::kSelScratchBytes];
 
 namespace tg {
 namespace {
@@ -360,6 +368,25 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
 }
 
 }  // namespace
+
+hipError_t select_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t select_ws_bytes(int64_t t_in, int n_seq) {
   const int64_t ns = n_slots_of(t_in, n_seq);

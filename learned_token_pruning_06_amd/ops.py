@@ -132,6 +132,26 @@ def select_topk(b: torch.Tensor, prunable: torch.Tensor, cu_seqlens: torch.Tenso
             None if kept_b is None else kept_b[sl], kept_cu)
 
 
+def select_topk_noalloc(b: torch.Tensor, prunable: torch.Tensor, cu_seqlens: torch.Tensor,
+                        k: torch.Tensor, kept_idx: torch.Tensor, kept_pos: Optional[torch.Tensor],
+                        kept_b: Optional[torch.Tensor], kept_cu: torch.Tensor):
+    """tg_select_topk_noalloc: the selection into caller-provided outputs
+    (capacity = kept_idx.numel()), with the library's static scratch memory
+    instead of a workspace; nothing is allocated."""
+    lib = load()
+    _need(b, "b", torch.float32, 1)
+    _need(prunable, "prunable", torch.uint8, 1)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(k, "k", torch.int32, 1)
+    _need(kept_idx, "kept_idx", torch.int32, 1)
+    _need(kept_cu, "kept_cu", torch.int32, 1)
+    n_seq = cu_seqlens.numel() - 1
+    st = lib.tg_select_topk_noalloc(_p(b), _p(prunable), _p(cu_seqlens), _p(k), n_seq, b.numel(),
+                                    kept_idx.numel(), _p(kept_idx), _p(kept_pos), _p(kept_b),
+                                    _p(kept_cu), _stream(b.device))
+    check("tg_select_topk_noalloc", st)
+
+
 # -------------------------------------------------------------------- gather
 def gather(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = None):
     """tg_gather: out[r] = src[idx[r]] over the first axis of a contiguous src."""

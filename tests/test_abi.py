@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -134,6 +134,31 @@ def test_select_validation(lib):
     assert sel(k=None) == 1
     assert sel(idx=None) == 1
     assert sel(wsb=8) == 3
+
+
+def test_select_noalloc_validation(lib):
+    """Argument checks and the static scratch limit (8 MiB) are tested before
+    the library looks up its scratch array, so none of these touches a GPU."""
+    def sel(**kw):
+        a = dict(b=FAKE, pr=FAKE, cu=FAKE, k=FAKE, n_seq=1, t=1024, cap=192, idx=FAKE, kcu=FAKE)
+        a.update(kw)
+        return lib.tg_select_topk_noalloc(a["b"], a["pr"], a["cu"], a["k"], a["n_seq"], a["t"],
+                                          a["cap"], a["idx"], None, None, a["kcu"], None)
+    assert sel(n_seq=0) == 1
+    assert sel(cap=-1) == 1
+    assert sel(t=-5) == 1
+    assert sel(k=None) == 1
+    assert sel(kcu=None) == 1
+    assert sel(idx=None) == 1
+    limit = 8 << 20
+    # the largest single sequence the scratch holds, and one chunk past it
+    t = 1 << 21
+    while lib.tg_select_workspace_size(t, 1) <= limit:
+        t += 2048
+    assert sel(t=t) == 3
+    assert "scratch" in lib.tg_last_error().decode()
+    assert lib.tg_select_workspace_size(t - 2048, 1) <= limit
+    assert sel(n_seq=4096, t=4096) == 3          # many sequences: histograms per sequence
 
 
 def test_gather_validation(lib):

@@ -1,0 +1,101 @@
+"""tg_select_topk_noalloc (the selector on the library's static scratch
+array) against tg_select_topk (the same kernels on a caller workspace) and
+the oracle: bit-exact, on calls in a row whose inputs shrink, so that
+whatever the previous call left in the shared scratch cannot leak into the
+next result."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import DEV, f32_dev, i32_dev, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, lens, n_prompt, frac):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    b = rng.standard_normal(T).astype(np.float32)
+    b[rng.random(T) < 0.05] = 6.0                 # a block of exact ties
+    pr = np.ones(T, np.uint8)
+    k = []
+    for s in range(len(lens)):
+        p = min(n_prompt, lens[s])
+        pr[cu[s + 1] - p:cu[s + 1]] = 0
+        k.append(int(frac * (lens[s] - p)))
+    b[pr == 0] = 0.0
+    return b, pr, cu, np.array(k, np.int32)
+
+
+def _both(b, pr, cu, k):
+    from learned_token_pruning_06_amd import ops
+    n_seq = cu.size - 1
+    npr = [int(pr[cu[s]:cu[s + 1]].sum()) for s in range(n_seq)]
+    kept_cu_h, t_kept = ops.kept_sizes(cu, npr, k)
+    bt, prt, cut, kt = f32_dev(b), u8_dev(pr), i32_dev(cu), i32_dev(k)
+    # the workspace entry point, on a workspace filled with 0xFF
+    ws = torch.full((int(ops.load().tg_select_workspace_size(b.size, n_seq)) + 256,), 255,
+                    dtype=torch.uint8, device=DEV)
+    ref = ops.select_topk(bt, prt, cut, kt, t_kept, ws=ws)
+    # the allocation-free one into preallocated outputs (poisoned)
+    cap = max(t_kept, 1)
+    idx = torch.full((cap,), -7, dtype=torch.int32, device=DEV)
+    pos = torch.full((cap,), -7, dtype=torch.int32, device=DEV)
+    kb = torch.full((cap,), float("nan"), dtype=torch.float32, device=DEV)
+    kcu = torch.full((n_seq + 1,), -7, dtype=torch.int32, device=DEV)
+    ops.select_topk_noalloc(bt, prt, cut, kt, idx[:t_kept] if t_kept else idx[:0],
+                            pos, kb, kcu)
+    torch.cuda.synchronize()
+    got = (idx[:t_kept].cpu().numpy(), pos[:t_kept].cpu().numpy(),
+           kb[:t_kept].cpu().numpy(), kcu.cpu().numpy())
+    want = tuple(None if t is None else t.cpu().numpy() for t in ref)
+    return got, want, kept_cu_h
+
+
+def _check(seed, lens, n_prompt, frac):
+    b, pr, cu, k = _case(seed, lens, n_prompt, frac)
+    say(f"no-alloc select: {len(lens)} sequences, T={int(cu[-1])}, k={k.tolist()[:4]}")
+    got, want, kept_cu_h = _both(b, pr, cu, k)
+    orc = O.ref_select(b, pr, cu, k)
+    for i, name in enumerate(("kept_idx", "kept_pos", "kept_b", "kept_cu")):
+        g, w = got[i], want[i]
+        if name == "kept_b":
+            g, w = g.view(np.uint32), np.asarray(w, np.float32).view(np.uint32)
+        assert np.array_equal(g, w), f"{name}: allocation-free call differs from tg_select_topk"
+        o = np.asarray(orc[i], np.float32).view(np.uint32) if name == "kept_b" else orc[i]
+        assert np.array_equal(g, o), f"{name}: allocation-free call differs from the oracle"
+    assert np.array_equal(got[3], kept_cu_h)
+
+
+def test_noalloc_select_calls_in_a_row_shrinking():
+    # first the 128k layer's selection, then smaller inputs on the same scratch
+    _check(3, [131072], 512, 8192 / 130560)
+    _check(4, [5000, 0, 1777, 2049], 64, 0.3)
+    _check(5, [300], 16, 0.5)
+
+
+def test_noalloc_select_more_sequences_fewer_tokens():
+    _check(6, [40000, 30000], 512, 1 / 16)
+    rng = np.random.default_rng(7)
+    _check(8, [int(x) for x in rng.integers(0, 400, 70)], 8, 0.25)
+
+
+def test_noalloc_select_rejects_inputs_beyond_the_scratch():
+    from learned_token_pruning_06_amd import ops
+    from learned_token_pruning_06_amd._lib import TokenGateError
+    lib = ops.load()
+    t = 1 << 21
+    while lib.tg_select_workspace_size(t, 1) <= (8 << 20):
+        t += 2048
+    b = torch.zeros(t, dtype=torch.float32, device=DEV)
+    pr = torch.ones(t, dtype=torch.uint8, device=DEV)
+    cu = i32_dev([0, t])
+    k = i32_dev([10])
+    idx = torch.empty(10, dtype=torch.int32, device=DEV)
+    kcu = torch.empty(2, dtype=torch.int32, device=DEV)
+    with pytest.raises(TokenGateError, match="TG_ERR_WORKSPACE"):
+        ops.select_topk_noalloc(b, pr, cu, k, idx, None, None, kcu)
+    # a call that fits still works after the rejected one
+    _check(9, [2048, 1], 1, 0.5)
