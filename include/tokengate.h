@@ -148,8 +148,8 @@ tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t*
  * by the library until the process ends; the call itself allocates nothing.
  *
  * Limit: tg_select_workspace_size(t_in, n_seq) must not exceed
- * TG_SELECT_SCRATCH_BYTES (8 MiB: e.g. a single sequence of 2 million
- * tokens, or 64 sequences of 128k); larger calls return TG_ERR_WORKSPACE
+ * TG_SELECT_SCRATCH_BYTES (8 MiB: e.g. one sequence of up to 3.2 million
+ * tokens, or 64 sequences of 32k); larger calls return TG_ERR_WORKSPACE
  * before anything is launched.  The first call on a device looks up that
  * device's copy of the array (a failure there is TG_ERR_HIP).
  * Every call on one GPU shares that GPU's array, so calls that overlap in

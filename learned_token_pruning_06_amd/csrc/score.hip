@@ -20,10 +20,14 @@
 // squares are taken from the x registers as they are staged, so the norm
 // costs no extra pass over the rows.
 //
-// Normalisation: per-sequence sums of squares in 2048-token chunks (fp64
-// partials, fixed reduction order), then every chunk reduces its sequence's
-// partials in the same fixed order and divides.  No float atomics, so the
-// result is bitwise reproducible.
+// Normalisation: the scoring kernel's epilogue writes, for every sequence
+// that meets its rows, an fp64 partial sum of the squared raw scores of the
+// sequence's prunable rows (and their count).  Rows of a workgroup and of a
+// sequence are contiguous ranges, so (sequence s, workgroup g) pairs that
+// meet are told apart by s + g: that is the partial's slot.  A second kernel,
+// one block per 2048-token chunk, adds the partials of its sequence in a
+// fixed order and divides.  No float atomics, so the result is bitwise
+// reproducible.
 #include "common.h"
 
 namespace tg {
@@ -149,11 +153,68 @@ TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, in
   }
 }
 
+struct Partial {
+  double sumsq;
+  int64_t count;
+};
+
+constexpr int kPartRows = 64;        // rows per workgroup of every scoring kernel: at least 64
+
+// Largest s in [0, n_seq) with cu[s] <= row (0 if none): the first sequence
+// that can meet rows from `row` on.
+TG_DEVINL int seq_at_row(const int32_t* cu, int n_seq, int64_t row) {
+  int lo = 0, hi = n_seq - 1, ans = 0;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)cu[mid] <= row) {
+      ans = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return ans;
+}
+
+// Per-sequence partial sums of the workgroup's rows [r0, r0 + rows) (rows
+// past t_in excluded): sq[i] is row r0 + i's squared raw score if it is
+// prunable, else 0, and pf[i] its prunable flag.  Wave w takes sequences
+// s_a + w, s_a + w + NW, ...; each sum runs over the rows in index order per
+// lane and then a fixed butterfly, so the result is reproducible.  Every
+// thread calls it after sq and pf are written (and a barrier).
+template <int NW>
+TG_DEVINL void seq_partials(const double* sq, const int* pf, int64_t r0, int rows, int64_t t_in,
+                            const int32_t* cu, int n_seq, int s_a, Partial* part) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r1 = r0 + rows < t_in ? r0 + rows : t_in;
+  for (int s = s_a + wv; s < n_seq; s += NW) {
+    int64_t lo = cu[s], hi = cu[s + 1];
+    lo = lo < 0 ? 0 : (lo > t_in ? t_in : lo);
+    hi = hi < lo ? lo : (hi > t_in ? t_in : hi);
+    if (lo >= r1) break;
+    const int64_t a = lo > r0 ? lo : r0, e = hi < r1 ? hi : r1;
+    if (a >= e) continue;
+    double acc = 0.0;
+    int cnt = 0;
+    for (int64_t r = a + lane; r < e; r += 64) {
+      acc += sq[r - r0];
+      cnt += pf[r - r0];
+    }
+    acc = wave_sum(acc);
+    cnt = wave_sum(cnt);
+    if (lane == 0) {
+      part[(int64_t)s + blockIdx.x].sumsq = acc;
+      part[(int64_t)s + blockIdx.x].count = cnt;
+    }
+  }
+}
+
 template <int MT, bool NORM, int RG, bool BWD = false>
 __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t_in, int d,
     const uint16_t* __restrict__ w1, const float* __restrict__ b1, const float* __restrict__ w2,
-    float b2, float norm_eps, float* __restrict__ b_raw, DzOut bo = DzOut{}) {
+    float b2, float norm_eps, float* __restrict__ b_raw, const uint8_t* __restrict__ pr,
+    const int32_t* __restrict__ cu, int n_seq, Partial* __restrict__ part, DzOut bo = DzOut{}) {
   constexpr int H = 32 * MT;
   constexpr int ROWS = 64 * RG;              // rows per workgroup (RG groups of 64)
   constexpr int HS = kWaves / RG;            // waves sharing a row group, splitting h
@@ -169,6 +230,8 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][ROWS * kRow];
   __shared__ float sred[HS][RG][64];
   __shared__ float sinv[NORM ? ROWS : 1];    // 1 / RMS of each row (LN2)
+  __shared__ double ssq[BWD ? 1 : ROWS];     // squared raw scores of prunable rows
+  __shared__ int spf[BWD ? 1 : ROWS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
@@ -178,6 +241,15 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
   const int nmt = MT % HS == 0 ? MTA : (MT - mt0 < MTA ? MT - mt0 : MTA);
   const int64_t wg_row0 = (int64_t)blockIdx.x * ROWS;
   const int64_t row0 = wg_row0 + rg * 64;
+  // for the normalisation partials: the first sequence that can meet this
+  // workgroup's rows, and the prunable flags of the rows this lane will hold
+  int s_a = 0;
+  uint8_t pfa = 0, pfb = 0;
+  if constexpr (!BWD) {
+    s_a = seq_at_row(cu, n_seq, wg_row0);
+    if (row0 + n < t_in) pfa = pr[row0 + n];
+    if (row0 + 32 + n < t_in) pfb = pr[row0 + 32 + n];
+  }
 
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
   const int lrow = tid >> 3, lch = tid & 7;
@@ -338,46 +410,71 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
       a0 += sred[k][rg][n];
       a1 += sred[k][rg][32 + n];
     }
-    if (row0 + n < t_in) b_raw[row0 + n] = a0 + b2;
-    if (row0 + 32 + n < t_in) b_raw[row0 + 32 + n] = a1 + b2;
+    const float v0 = a0 + b2, v1 = a1 + b2;
+    const bool in0 = row0 + n < t_in, in1 = row0 + 32 + n < t_in;
+    if (in0) b_raw[row0 + n] = v0;
+    if (in1) b_raw[row0 + 32 + n] = v1;
+    const bool p0 = in0 && pfa, p1 = in1 && pfb;
+    ssq[64 * rg + n] = p0 ? (double)v0 * (double)v0 : 0.0;
+    ssq[64 * rg + 32 + n] = p1 ? (double)v1 * (double)v1 : 0.0;
+    spf[64 * rg + n] = p0;
+    spf[64 * rg + 32 + n] = p1;
   }
+  __syncthreads();
+  seq_partials<kWaves>(ssq, spf, wg_row0, ROWS, t_in, cu, n_seq, s_a, part);
 }
 
-// fp32 scorer on the vector ALU: one wave per row, lanes over hidden units
-// (with LN2, the row's RMS first: lanes over the row, then a wave sum).
+// fp32 scorer on the vector ALU: 64 rows per block, one wave per row at a
+// time (wave w takes rows w, w + 4, ...), lanes over hidden units (with LN2,
+// the row's RMS first: lanes over the row, then a wave sum); then the
+// normalisation partials of the block's rows.
 __global__ __launch_bounds__(256) void score_mlp_f32(const float* __restrict__ x, int64_t xs,
                                                      int64_t t_in, int d, int h,
                                                      const float* __restrict__ w1,
                                                      const float* __restrict__ b1,
                                                      const float* __restrict__ w2, float b2,
-                                                     float norm_eps, float* __restrict__ b_raw) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= t_in) return;
-  const float* xp = x + row * xs;
-  float inv = 1.0f;
-  if (norm_eps >= 0.0f) {
-    float ss = 0.f;
-    for (int e = lane; e < d; e += 64) ss = fmaf(xp[e], xp[e], ss);
-    ss = wave_sum(ss);
-    inv = 1.0f / sqrtf(ss / (float)d + norm_eps);
+                                                     float norm_eps, float* __restrict__ b_raw,
+                                                     const uint8_t* __restrict__ pr,
+                                                     const int32_t* __restrict__ cu, int n_seq,
+                                                     Partial* __restrict__ part) {
+  __shared__ double ssq[kPartRows];
+  __shared__ int spf[kPartRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * kPartRows;
+  for (int i = wv; i < kPartRows; i += 4) {
+    const int64_t row = r0 + i;
+    double sq = 0.0;
+    int pf = 0;
+    if (row < t_in) {
+      const float* xp = x + row * xs;
+      float inv = 1.0f;
+      if (norm_eps >= 0.0f) {
+        float ss = 0.f;
+        for (int e = lane; e < d; e += 64) ss = fmaf(xp[e], xp[e], ss);
+        ss = wave_sum(ss);
+        inv = 1.0f / sqrtf(ss / (float)d + norm_eps);
+      }
+      float acc_h = 0.f;
+      for (int j = lane; j < h; j += 64) {
+        const float* wp = w1 + (int64_t)j * d;
+        float acc = 0.f;
+        for (int e = 0; e < d; ++e) acc = fmaf(xp[e], wp[e], acc);
+        const float v = fmaf(acc, inv, b1 ? b1[j] : 0.f);
+        acc_h = fmaf(v / (1.0f + expf(-v)), w2[j], acc_h);
+      }
+      const float val = wave_sum(acc_h) + b2;
+      if (lane == 0) b_raw[row] = val;
+      pf = pr[row] != 0;
+      sq = pf ? (double)val * (double)val : 0.0;
+    }
+    if (lane == 0) {
+      ssq[i] = sq;
+      spf[i] = pf;
+    }
   }
-  float part = 0.f;
-  for (int j = lane; j < h; j += 64) {
-    const float* wp = w1 + (int64_t)j * d;
-    float acc = 0.f;
-    for (int e = 0; e < d; ++e) acc = fmaf(xp[e], wp[e], acc);
-    const float v = fmaf(acc, inv, b1 ? b1[j] : 0.f);
-    part = fmaf(v / (1.0f + expf(-v)), w2[j], part);
-  }
-  part = wave_sum(part);
-  if (lane == 0) b_raw[row] = part + b2;
+  __syncthreads();
+  seq_partials<4>(ssq, spf, r0, kPartRows, t_in, cu, n_seq, seq_at_row(cu, n_seq, r0), part);
 }
-
-struct Partial {
-  double sumsq;
-  int64_t count;
-};
 
 constexpr int CH = kScoreChunk;
 
@@ -396,17 +493,20 @@ TG_DEVINL bool locate(const int32_t* cu, int n_seq, int64_t t_in, int64_t slot, 
   return true;
 }
 
-__global__ __launch_bounds__(256) void score_partial(const float* __restrict__ b_raw,
-                                                     const uint8_t* __restrict__ pr,
-                                                     const int32_t* __restrict__ cu, int n_seq,
-                                                     int64_t t_in, Partial* __restrict__ part) {
+// b = b~ / r on the prunable tokens of one 2048-token chunk, 0 on the others,
+// with r = sqrt(sum / count + eps) from the sequence's partials (slots s + g
+// for the scoring workgroups g that meet it, `rows` rows each), added in a
+// fixed order by every chunk of the sequence.
+__global__ __launch_bounds__(256) void score_norm(const float* __restrict__ b_raw,
+                                                  const uint8_t* __restrict__ pr,
+                                                  const int32_t* __restrict__ cu, int n_seq,
+                                                  int64_t t_in, const Partial* __restrict__ part,
+                                                  int rows, float eps, float* __restrict__ b) {
   __shared__ double sd[4];
   __shared__ int64_t sc[4];
   int s, nch;
   int64_t begin, end;
   if (!locate(cu, n_seq, t_in, blockIdx.x, s, begin, end, nch)) return;
-  // a chunk is at most CH = 8 * 256 tokens: all loads first, then the sums
-  // (in the same per-thread order as a strided loop)
   constexpr int PER = CH / 256;
   uint8_t pv[PER];
   float bv[PER];
@@ -416,47 +516,23 @@ __global__ __launch_bounds__(256) void score_partial(const float* __restrict__ b
     pv[i] = j < end ? pr[j] : (uint8_t)0;
     bv[i] = j < end ? b_raw[j] : 0.0f;
   }
+  const int64_t lo = cu[s] < t_in ? cu[s] : t_in;
+  const int64_t hi = cu[s + 1] < t_in ? cu[s + 1] : t_in;
+  const int64_t g0 = lo / rows, ng = (hi - 1) / rows - g0 + 1;
+  const Partial* ps = part + s + g0;
+  // thread t adds partials t, t + 256, ... in order, eight loads in flight
   double acc = 0.0;
   int64_t cnt = 0;
+  for (int64_t base = threadIdx.x; base < ng; base += 8 * 256) {
+    Partial v[8];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (pv[i]) {
-      const double v = bv[i];
-      acc = fma(v, v, acc);
-      ++cnt;
+    for (int k = 0; k < 8; ++k)
+      v[k] = base + 256 * k < ng ? ps[base + 256 * k] : Partial{0.0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc += v[k].sumsq;
+      cnt += v[k].count;
     }
-  }
-  acc = wave_sum(acc);
-  cnt = wave_sum(cnt);
-  if ((threadIdx.x & 63) == 0) {
-    sd[threadIdx.x >> 6] = acc;
-    sc[threadIdx.x >> 6] = cnt;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    part[blockIdx.x].sumsq = ((sd[0] + sd[1]) + sd[2]) + sd[3];
-    part[blockIdx.x].count = sc[0] + sc[1] + sc[2] + sc[3];
-  }
-}
-
-__global__ __launch_bounds__(256) void score_norm(const float* __restrict__ b_raw,
-                                                  const uint8_t* __restrict__ pr,
-                                                  const int32_t* __restrict__ cu, int n_seq,
-                                                  int64_t t_in, const Partial* __restrict__ part,
-                                                  float eps,
-                                                  float* __restrict__ b) {
-  __shared__ double sd[4];
-  __shared__ int64_t sc[4];
-  int s, nch;
-  int64_t begin, end;
-  if (!locate(cu, n_seq, t_in, blockIdx.x, s, begin, end, nch)) return;
-  // every chunk of the sequence reduces the same partials in the same order
-  const int64_t p0 = slot0_of(cu, s, CH);
-  double acc = 0.0;
-  int64_t cnt = 0;
-  for (int i = threadIdx.x; i < nch; i += 256) {
-    acc += part[p0 + i].sumsq;
-    cnt += part[p0 + i].count;
   }
   acc = wave_sum(acc);
   cnt = wave_sum(cnt);
@@ -468,15 +544,6 @@ __global__ __launch_bounds__(256) void score_norm(const float* __restrict__ b_ra
   const double tot = ((sd[0] + sd[1]) + sd[2]) + sd[3];
   const int64_t n = sc[0] + sc[1] + sc[2] + sc[3];
   const float r = n > 0 ? (float)sqrt(tot / (double)n + (double)eps) : 1.0f;
-  constexpr int PER = CH / 256;
-  uint8_t pv[PER];
-  float bv[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t j = begin + threadIdx.x + (int64_t)i * 256;
-    pv[i] = j < end ? pr[j] : (uint8_t)0;
-    bv[i] = j < end ? b_raw[j] : 0.0f;
-  }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t j = begin + threadIdx.x + (int64_t)i * 256;
@@ -510,7 +577,8 @@ hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const
   const uint16_t* wp = static_cast<const uint16_t*>(w1);
 #define TG_DZ(R)                                                                                \
   hipLaunchKernelGGL((score_mlp_bf16<8, false, R, true>), dim3((unsigned)nb), dim3(kThreads), 0, \
-                     st, xp, xs, t_in, d, wp, b1, w2, 0.0f, -1.0f, nullptr, bo)
+                     st, xp, xs, t_in, d, wp, b1, w2, 0.0f, -1.0f, nullptr, nullptr, nullptr, \
+                     0, nullptr, bo)
   if (rg == 4) TG_DZ(4);
   else if (rg == 2) TG_DZ(2);
   else TG_DZ(1);
@@ -523,8 +591,13 @@ int64_t score_dz_blocks(int64_t t_in, int n_cu) {
   return (t_in + 64 * rg - 1) / (64 * rg);
 }
 
+// partial slots: n_seq + (scoring workgroups), every workgroup >= kPartRows rows
+int64_t n_parts(int64_t t_in, int n_seq) {
+  return (int64_t)n_seq + (t_in + kPartRows - 1) / kPartRows;
+}
+
 size_t score_ws_bytes(int64_t t_in, int n_seq) {
-  size_t bytes = sizeof(Partial) * (size_t)n_slots(t_in, n_seq);
+  size_t bytes = sizeof(Partial) * (size_t)n_parts(t_in, n_seq);
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += sizeof(float) * (size_t)t_in;   // b~ when the caller passes no b_raw
   return (bytes + 255) & ~(size_t)255;
@@ -535,9 +608,10 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
                         const uint8_t* prunable, const int32_t* cu, int n_seq, float eps,
                         float norm_eps, float* b_raw, float* b, void* ws, hipStream_t st) {
   Partial* part = static_cast<Partial*>(ws);
-  size_t off = (sizeof(Partial) * (size_t)n_slots(t_in, n_seq) + 255) & ~(size_t)255;
+  size_t off = (sizeof(Partial) * (size_t)n_parts(t_in, n_seq) + 255) & ~(size_t)255;
   float* braw = b_raw ? b_raw : reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   if (t_in == 0) return hipSuccess;
+  int part_rows = kPartRows;
   if (dt == 1) {
     // rows per workgroup: 256 when that still gives a workgroup per CU,
     // else 128 or 64 (short inputs), so that small batches fill the chip
@@ -546,11 +620,12 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
     if (ce != hipSuccess) return ce;
     const int rg = (t_in + 255) / 256 >= n_cu ? 4 : (t_in + 127) / 128 >= n_cu ? 2 : 1;
     const dim3 grid((unsigned)((t_in + 64 * rg - 1) / (64 * rg)));
+    part_rows = 64 * rg;
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const uint16_t* wp = static_cast<const uint16_t*>(w1);
 #define TG_SCORE_LAUNCH(M, N, R)                                                              \
   hipLaunchKernelGGL((score_mlp_bf16<M, N, R>), grid, dim3(kThreads), 0, st, xp, x_row_stride, \
-                     t_in, d, wp, b1, w2, b2, norm_eps, braw)
+                     t_in, d, wp, b1, w2, b2, norm_eps, braw, prunable, cu, n_seq, part)
 #define TG_SCORE_CASE(M)                                                                      \
   case M:                                                                                     \
     if (norm_eps >= 0.0f) {                                                                   \
@@ -571,15 +646,14 @@ hipError_t launch_score(const void* x, int dt, int64_t x_row_stride, int64_t t_i
 #undef TG_SCORE_CASE
 #undef TG_SCORE_LAUNCH
   } else {
-    const dim3 grid((unsigned)((t_in + 3) / 4));
+    const dim3 grid((unsigned)((t_in + kPartRows - 1) / kPartRows));
     hipLaunchKernelGGL(score_mlp_f32, grid, dim3(256), 0, st, static_cast<const float*>(x),
                        x_row_stride, t_in, d, h, static_cast<const float*>(w1), b1, w2, b2,
-                       norm_eps, braw);
+                       norm_eps, braw, prunable, cu, n_seq, part);
   }
   const dim3 g2((unsigned)n_slots(t_in, n_seq));
-  hipLaunchKernelGGL(score_partial, g2, dim3(256), 0, st, braw, prunable, cu, n_seq, t_in, part);
-  hipLaunchKernelGGL(score_norm, g2, dim3(256), 0, st, braw, prunable, cu, n_seq, t_in, part, eps,
-                     b);
+  hipLaunchKernelGGL(score_norm, g2, dim3(256), 0, st, braw, prunable, cu, n_seq, t_in, part,
+                     part_rows, eps, b);
   return hipGetLastError();
 }
 

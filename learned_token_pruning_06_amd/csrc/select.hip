@@ -1,23 +1,35 @@
 // tg_select_topk: S_s = top-K_{j in P_s}(b_j)  U  N_s   (TokenGate §4.1 Eq. 4)
 //
 // Integer work on order-preserving 32-bit keys of the scores (common.h).
-// Per sequence, the K'-th largest key tau is found by a three-pass radix
-// select over 11/11/10-bit digits.  Each pass is one launch over all
-// 2048-token chunks of all sequences: a chunk's histogram is built in LDS and
-// added into the sequence's histogram for that pass with integer atomics.
-// There is no cross-block handshake inside a launch: every block of the next
-// launch re-derives the digits fixed so far from the (small) histograms of
-// the earlier passes, so all blocks reach the same tau and quota without
-// fences.  Then every token is kept if it is a prompt token, if key > tau, or
-// if key == tau and fewer than `need` earlier tokens of the sequence tie at
-// tau (lower index wins).  The kept count of a sequence, min(K, |P|) + |N|,
-// is known from the prunable count alone, so sequence offsets need no scan
-// of the selection itself; a chunk's offset is the sum of the definite keeps
-// of the earlier chunks of its sequence plus min(need, their ties).  Tokens
-// are written in ascending original index.
+// Per sequence, the K'-th largest key tau (K' = min(K, |P|)) is found by a
+// three-digit radix select over the key bits 31..24, 23..12 and 11..0.
+// The sequence's tokens are cut into 2048-token chunks, one block each, and
+// the selection runs in four launches with no cross-block handshake inside a
+// launch: every block re-derives what it needs from what earlier launches
+// wrote.
 //
-// Launches: init, pass0, pass1, pass2, count (+ kept_cu), write (each block
-// derives its chunk's offsets from the counts of the earlier chunks).
+//   pass0  each chunk writes the histogram of its prunable tokens' top digit
+//          (256 bins) to a record of its own, so nothing has to be zeroed
+//          first; the blocks also zero the per-sequence histograms of the
+//          two later digits.
+//   pass1  each block adds up its sequence's chunk histograms (the sum of the
+//          bins is |P|), picks the top digit of tau and how many keys are
+//          still needed among those that share it, and adds the middle digit
+//          of those keys into the sequence's histogram (integer atomics).
+//   pass2  each block picks the middle digit from that histogram and adds
+//          the low digit of the keys sharing the top 20 bits into the last
+//          histogram.  It also records, per chunk, how many tokens are kept
+//          whatever the low digit (prompt tokens, keys above the 20-bit
+//          prefix, or every token when K' = |P|) and the low digits of the
+//          tokens that share the prefix (the candidates).  Block 0 writes
+//          kept_cu_seqlens: a sequence keeps min(K, |P|) + |N| tokens.
+//   write  each block picks the low digit, hence tau and the number `need`
+//          of tokens equal to tau that are kept (lower index first).  The
+//          chunk's output offset is the earlier chunks' definite keeps plus
+//          their candidates above tau plus min(need, their candidates equal
+//          to tau), since ties are taken in index order; then its own kept
+//          tokens are written in ascending index.
+#include <cstddef>
 #include <mutex>
 
 #include "common.h"
@@ -34,42 +46,68 @@ namespace {
 constexpr int CH = kSelChunk;          // tokens per block
 constexpr int NT = 256;                // threads per block
 constexpr int PER = CH / NT;           // tokens per thread
-constexpr int NB = 2048;               // histogram bins (11-bit digit)
-constexpr int HIST_WORDS = 2048 + 2048 + 1024;   // the three passes' histograms
+constexpr int NB0 = 256;               // bins of the top digit (key bits 31..24)
+constexpr int NB1 = 4096;              // bins of the middle and low digits (23..12, 11..0)
 
 enum : int { MODE_NONE = 0, MODE_ALL = 1, MODE_RADIX = 2 };
 
-// Selection state of a sequence as derived by one block.
+// Selection state of a sequence: digits fixed so far and how many keys are
+// still to be taken among those that match them.
 struct Sel {
   int mode;
-  uint32_t prefix;   // digits fixed so far (tau after three passes)
-  uint32_t need;     // keys still to take among those matching the prefix
-  uint32_t pad;
+  uint32_t prefix;
+  uint32_t need;
+  uint32_t npr;      // |P| of the sequence
 };
 
+// Per-chunk record.
+constexpr int NSMALL = 28;             // candidate digits kept in the record itself
+struct Slot {
+  uint32_t h0[NB0];  // pass0: top-digit histogram of the chunk's prunable tokens
+  uint32_t def;      // pass2: tokens kept whatever the low digit
+  uint32_t ncand;    // pass2: prunable tokens whose key shares the 20-bit prefix
+  uint16_t small[NSMALL];  // pass2: their low digits when ncand <= NSMALL
+};
+static_assert(sizeof(Slot) % 16 == 0 && offsetof(Slot, def) % 16 == 0 &&
+                  sizeof(Slot) - offsetof(Slot, def) == 64,
+              "slot records are read with 16-byte loads");
+
 struct SelWs {
-  Sel* stage;            // [3][n_seq]: state after 1, 2 and 3 digits
-  uint32_t* hist;        // [n_seq][HIST_WORDS]
+  Sel* stage;            // [2][n_seq]: state after the top and the middle digit
   uint32_t* n_prunable;  // [n_seq]
-  int32_t* blk_def;      // [n_slots] kept for sure (prompt, key > tau, or all)
-  int32_t* blk_tie;      // [n_slots] prunable tokens with key == tau
+  uint32_t* hist1;       // [n_seq][NB1] middle digit
+  uint32_t* hist2;       // [n_seq][NB1] low digit
+  Slot* slot;            // [n_slots]
+  uint16_t* cand;        // [n_slots][CH] low digits of the candidates
 };
 
 int64_t n_slots_of(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 1) / CH; }
 
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t ws_layout(int64_t t_in, int n_seq, size_t off[6]) {
+  const size_t ns = (size_t)n_slots_of(t_in, n_seq);
+  size_t p = 0;
+  off[0] = p; p = align256(p + sizeof(Sel) * 2 * (size_t)n_seq);
+  off[1] = p; p = align256(p + sizeof(uint32_t) * (size_t)n_seq);
+  off[2] = p; p = align256(p + sizeof(uint32_t) * NB1 * (size_t)n_seq);
+  off[3] = p; p = align256(p + sizeof(uint32_t) * NB1 * (size_t)n_seq);
+  off[4] = p; p = align256(p + sizeof(Slot) * ns);
+  off[5] = p; p = align256(p + sizeof(uint16_t) * CH * ns);
+  return p;
+}
+
 SelWs carve(void* ws, int64_t t_in, int n_seq) {
-  const int64_t ns = n_slots_of(t_in, n_seq);
+  size_t off[6];
+  ws_layout(t_in, n_seq, off);
   char* p = static_cast<char*>(ws);
   SelWs w;
-  w.stage = reinterpret_cast<Sel*>(p);
-  p += sizeof(Sel) * 3 * (size_t)n_seq;
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * (size_t)n_seq * HIST_WORDS;
-  w.n_prunable = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * (size_t)n_seq;
-  w.blk_def = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * ns;
-  w.blk_tie = reinterpret_cast<int32_t*>(p);
+  w.stage = reinterpret_cast<Sel*>(p + off[0]);
+  w.n_prunable = reinterpret_cast<uint32_t*>(p + off[1]);
+  w.hist1 = reinterpret_cast<uint32_t*>(p + off[2]);
+  w.hist2 = reinterpret_cast<uint32_t*>(p + off[3]);
+  w.slot = reinterpret_cast<Slot*>(p + off[4]);
+  w.cand = reinterpret_cast<uint16_t*>(p + off[5]);
   return w;
 }
 
@@ -78,13 +116,16 @@ SelWs carve(void* ws, int64_t t_in, int n_seq) {
 TG_DEVINL void seq_range(const int32_t* cu, int s, int64_t t_in, int64_t& lo, int64_t& hi) {
   lo = cu[s] < t_in ? cu[s] : t_in;
   hi = cu[s + 1] < t_in ? cu[s + 1] : t_in;
+  if (lo < 0) lo = 0;
   if (hi < lo) hi = lo;
 }
 
 // Which chunk of which sequence this block handles; false if none.
 struct Chunk {
   int s;
-  int64_t slot, lo, begin, end;
+  int ci;             // chunk index within the sequence
+  int64_t slot, s0;   // this block's slot and the sequence's first slot
+  int64_t lo, begin, end;
 };
 
 TG_DEVINL bool locate(const int32_t* cu, int n_seq, int64_t t_in, Chunk& c) {
@@ -94,37 +135,57 @@ TG_DEVINL bool locate(const int32_t* cu, int n_seq, int64_t t_in, Chunk& c) {
   int64_t hi;
   seq_range(cu, c.s, t_in, c.lo, hi);
   if (hi <= c.lo) return false;
-  c.begin = c.lo + (c.slot - slot0_of(cu, c.s, CH)) * CH;
+  c.s0 = slot0_of(cu, c.s, CH);
+  c.ci = (int)(c.slot - c.s0);
+  c.begin = c.lo + (int64_t)c.ci * CH;
   if (c.begin >= hi) return false;
   c.end = c.begin + CH < hi ? c.begin + CH : hi;
   return true;
 }
 
-TG_DEVINL Sel sel_start(const SelWs& w, const int32_t* kbud, int s) {
-  const uint32_t npr = w.n_prunable[s];
-  const int kb = kbud[s];
+TG_DEVINL int n_chunks(int64_t lo, int64_t hi) { return (int)((hi - lo + CH - 1) / CH); }
+
+// The chunk's tokens, CH / NT per thread: thread t holds tokens
+// begin + t * PER + i (contiguous, so thread order is index order).  Tokens
+// past the chunk read as prompt tokens with score 0 and are flagged !in.
+struct Tokens {
+  float b[PER];
+  uint8_t pr[PER];
+  bool in[PER];
+};
+
+TG_DEVINL void load_tokens(const float* b, const uint8_t* pr, const Chunk& c, Tokens& tk) {
+  const int64_t j0 = c.begin + (int64_t)threadIdx.x * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t j = j0 + i;
+    tk.in[i] = j < c.end;
+    tk.pr[i] = tk.in[i] ? pr[j] : (uint8_t)0;
+    tk.b[i] = tk.in[i] ? b[j] : 0.0f;
+  }
+}
+
+TG_DEVINL Sel sel_start(uint32_t npr, int kb) {
   const uint32_t k = kb > 0 ? (uint32_t)kb : 0u;
   const uint32_t kp = k < npr ? k : npr;
   Sel st;
   st.mode = kp == 0 ? MODE_NONE : (kp == npr ? MODE_ALL : MODE_RADIX);
   st.prefix = 0u;
   st.need = kp;
-  st.pad = 0u;
+  st.npr = npr;
   return st;
 }
 
-// Narrow (prefix, need) with the histogram `h` of NBINS bins (block-wide;
-// every thread returns the same result).  Contains barriers.
+// Narrow (prefix, need) with a histogram of NBINS bins, read from global
+// memory (h) or given per thread (c, NBINS / NT bins of thread t, counted
+// from the top: bins NBINS-1 - (t * per + i)).  Block-wide; every thread
+// returns the same result.  Contains barriers.
 template <int NBINS, int SHIFT>
-TG_DEVINL void sel_narrow(Sel& st, const uint32_t* h, int* sh) {
+TG_DEVINL void sel_narrow_vals(Sel& st, const uint32_t (&c)[NBINS / NT], int* sh) {
   constexpr int per = NBINS / NT;
-  uint32_t c[per];
   int mine = 0;
 #pragma unroll
-  for (int i = 0; i < per; ++i) {
-    c[i] = h[NBINS - 1 - (threadIdx.x * per + i)];    // bins in descending order
-    mine += (int)c[i];
-  }
+  for (int i = 0; i < per; ++i) mine += (int)c[i];
   int tot;
   const int above = block_excl_scan<NT>(mine, sh, &tot);
   if ((uint32_t)above < st.need && (uint32_t)(above + mine) >= st.need) {
@@ -145,93 +206,145 @@ TG_DEVINL void sel_narrow(Sel& st, const uint32_t* h, int* sh) {
   __syncthreads();
 }
 
-// State after `digits` digits (1..3): the state stored by the previous
-// launch after digits-1 digits, narrowed once more with histogram digits-1.
-// The block of chunk 0 stores the result for the next launch (each launch
-// writes a different stage, so no block reads a slot being written).
-TG_DEVINL Sel sel_stage(const SelWs& w, const int32_t* kbud, int s, int n_seq, int digits,
-                        bool store, int* sh) {
-  Sel st = digits == 1 ? sel_start(w, kbud, s) : w.stage[(size_t)(digits - 2) * n_seq + s];
-  if (st.mode == MODE_RADIX) {
-    const uint32_t* hs = w.hist + (size_t)s * HIST_WORDS;
-    if (digits == 1) sel_narrow<2048, 11>(st, hs, sh);
-    else if (digits == 2) sel_narrow<2048, 11>(st, hs + 2048, sh);
-    else sel_narrow<1024, 10>(st, hs + 4096, sh);
+// The same with the histogram in global memory: read with coalesced 16-byte
+// loads into LDS (stage, NBINS words, 16-byte aligned), then each thread takes
+// its NBINS / NT bins from there.
+template <int NBINS, int SHIFT>
+TG_DEVINL void sel_narrow(Sel& st, const uint32_t* h, uint32_t* stage, int* sh) {
+  constexpr int per = NBINS / NT;
+  constexpr int NV = NBINS / 4 / NT;           // 16-byte vectors per thread
+  u32x4 v[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = ld16(h + 4 * (threadIdx.x + k * NT));
+#pragma unroll
+  for (int k = 0; k < NV; ++k) st16(stage + 4 * (threadIdx.x + k * NT), v[k]);
+  __syncthreads();
+  uint32_t c[per];
+#pragma unroll
+  for (int i = 0; i < per; ++i) c[i] = stage[NBINS - 1 - (threadIdx.x * per + i)];
+  sel_narrow_vals<NBINS, SHIFT>(st, c, sh);     // starts with a barrier-protected scan
+}
+
+// ---------------------------------------------------------------- pass 0
+__global__ __launch_bounds__(NT) void sel_pass0(const float* __restrict__ b,
+                                               const uint8_t* __restrict__ pr,
+                                               const int32_t* __restrict__ cu, int n_seq,
+                                               int64_t t_in, SelWs w) {
+  __shared__ uint32_t lh[NB0];
+  // zero the later digits' histograms of every sequence (read-modify-written
+  // by pass1 and pass2, which start after this launch ends)
+  {
+    const int64_t n = (int64_t)n_seq * NB1;
+    const int64_t gsz = (int64_t)gridDim.x * NT;
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += gsz) {
+      w.hist1[i] = 0u;
+      w.hist2[i] = 0u;
+    }
   }
-  if (store && threadIdx.x == 0) w.stage[(size_t)(digits - 1) * n_seq + s] = st;
+  Chunk c;
+  if (!locate(cu, n_seq, t_in, c)) return;
+  Tokens tk;
+  load_tokens(b, pr, c, tk);
+  lh[threadIdx.x] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (tk.pr[i]) atomicAdd(&lh[score_key(tk.b[i]) >> 24], 1u);
+  __syncthreads();
+  w.slot[c.slot].h0[threadIdx.x] = lh[threadIdx.x];
+}
+
+// State after the top digit: the chunk histograms of the sequence added up
+// (integer sums, so every block of the sequence gets the same result).
+// Thread t adds bins 4 (t % 64) .. +4 of every fourth chunk starting at
+// t / 64, eight 16-byte loads in flight at a time; the four partial sums of
+// a bin meet in LDS (red4: [4][NB0]).
+TG_DEVINL Sel stage0(const SelWs& w, int kb, const Chunk& c, int nch, int64_t ns,
+                     uint32_t* red4, int* sh) {
+  const int vi = threadIdx.x & 63, cp = threadIdx.x >> 6;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int base = cp; base < nch; base += 64) {
+    u32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int64_t sl = c.s0 + base + 4 * k;
+      v[k] = (base + 4 * k < nch && sl >= 0 && sl < ns) ? ld16(&w.slot[sl].h0[4 * vi])
+                                                       : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc += v[k];
+  }
+  *reinterpret_cast<u32x4*>(&red4[cp * NB0 + 4 * vi]) = acc;
+  __syncthreads();
+  const uint32_t v = red4[threadIdx.x] + red4[NB0 + threadIdx.x] + red4[2 * NB0 + threadIdx.x] +
+                     red4[3 * NB0 + threadIdx.x];
+  __syncthreads();
+  red4[threadIdx.x] = v;
+  int tot;
+  block_excl_scan<NT>((int)v, sh, &tot);
+  uint32_t* red = red4;
+  Sel st = sel_start((uint32_t)tot, kb);
+  if (st.mode == MODE_RADIX) {
+    uint32_t cv[NB0 / NT];
+#pragma unroll
+    for (int i = 0; i < NB0 / NT; ++i) cv[i] = red[NB0 - 1 - (threadIdx.x * (NB0 / NT) + i)];
+    sel_narrow_vals<NB0, 8>(st, cv, sh);
+  }
   return st;
 }
 
-__global__ __launch_bounds__(NT) void sel_init(int n_seq, SelWs w) {
-  const int64_t gtid = (int64_t)blockIdx.x * NT + threadIdx.x;
-  const int64_t gsz = (int64_t)gridDim.x * NT;
-  for (int64_t i = gtid; i < (int64_t)n_seq * HIST_WORDS; i += gsz) w.hist[i] = 0u;
-  for (int64_t i = gtid; i < n_seq; i += gsz) w.n_prunable[i] = 0u;
-}
-
-template <int P>
-__global__ __launch_bounds__(NT) void sel_pass(const float* __restrict__ b,
-                                              const uint8_t* __restrict__ pr,
-                                              const int32_t* __restrict__ cu,
-                                              const int32_t* __restrict__ kbud, int n_seq,
-                                              int64_t t_in, SelWs w) {
-  __shared__ uint32_t lh[NB];
+// ---------------------------------------------------------------- pass 1
+__global__ __launch_bounds__(NT) void sel_pass1(const float* __restrict__ b,
+                                               const uint8_t* __restrict__ pr,
+                                               const int32_t* __restrict__ cu,
+                                               const int32_t* __restrict__ kbud, int n_seq,
+                                               int64_t t_in, SelWs w) {
+  __shared__ uint32_t lh[NB1];
+  __shared__ __attribute__((aligned(16))) uint32_t red4[4 * NB0];
   __shared__ int sh[NT / 64 + 2];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  uint32_t* hs = w.hist + (size_t)c.s * HIST_WORDS;
-  Sel st = {MODE_RADIX, 0u, 0u, 0u};
-  if (P > 0) {
-    st = sel_stage(w, kbud, c.s, n_seq, P, c.begin == c.lo, sh);
-    if (st.mode != MODE_RADIX) return;
+  const int kb = kbud[c.s];
+  Tokens tk;
+  load_tokens(b, pr, c, tk);              // issued before the histogram sums
+  int64_t lo, hi;
+  seq_range(cu, c.s, t_in, lo, hi);
+  const Sel st = stage0(w, kb, c, n_chunks(lo, hi), (int64_t)gridDim.x, red4, sh);
+  if (c.ci == 0 && threadIdx.x == 0) {
+    w.stage[c.s] = st;
+    w.n_prunable[c.s] = st.npr;
   }
-  for (int i = threadIdx.x; i < NB; i += NT) lh[i] = 0u;
+  if (st.mode != MODE_RADIX) return;
+  for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
   __syncthreads();
-  // all loads first (one memory latency per thread, not one per token)
-  uint8_t pv[PER];
-  float bv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int64_t j = c.begin + threadIdx.x + (int64_t)i * NT;
-    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
-    bv[i] = j < c.end ? b[j] : 0.0f;
-  }
-  int np = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (pv[i]) {
-      const uint32_t key = score_key(bv[i]);
-      ++np;
-      if (P == 0) {
-        atomicAdd(&lh[key >> 21], 1u);
-      } else if (P == 1) {
-        if ((key >> 21) == st.prefix) atomicAdd(&lh[(key >> 10) & 0x7ffu], 1u);
-      } else {
-        if ((key >> 10) == st.prefix) atomicAdd(&lh[key & 0x3ffu], 1u);
-      }
+    if (tk.pr[i]) {
+      const uint32_t key = score_key(tk.b[i]);
+      if ((key >> 24) == st.prefix) atomicAdd(&lh[(key >> 12) & 0xfffu], 1u);
     }
   }
   __syncthreads();
-  uint32_t* gh = hs + (P == 0 ? 0 : (P == 1 ? 2048 : 4096));
-  for (int i = threadIdx.x; i < (P == 2 ? 1024 : 2048); i += NT) {
+  uint32_t* gh = w.hist1 + (size_t)c.s * NB1;
+  for (int i = threadIdx.x; i < NB1; i += NT) {
     const uint32_t v = lh[i];
     if (v) atomicAdd(gh + i, v);
   }
-  if (P == 0) {
-    np = wave_sum(np);
-    if ((threadIdx.x & 63) == 0 && np) atomicAdd(&w.n_prunable[c.s], (uint32_t)np);
-  }
 }
 
-__global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
+// ---------------------------------------------------------------- pass 2
+__global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
                                                const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ kbud, int n_seq,
                                                int64_t t_in, SelWs w,
                                                int32_t* __restrict__ kept_cu) {
+  __shared__ __attribute__((aligned(16))) uint32_t lh[NB1];
   __shared__ int sh[NT / 64 + 2];
+  __shared__ uint32_t ncand;
   if (blockIdx.x == 0) {
-    // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|
+    // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|; an empty
+    // sequence was seen by no pass1 block and has |P| = 0
     int acc = 0;
     for (int base = 0; base < n_seq; base += NT) {
       const int i = base + threadIdx.x;
@@ -239,7 +352,7 @@ __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
       if (i < n_seq) {
         int64_t lo, hi;
         seq_range(cu, i, t_in, lo, hi);
-        const int npr = (int)w.n_prunable[i];
+        const int npr = hi > lo ? (int)w.n_prunable[i] : 0;
         const int kb = kbud[i] > 0 ? kbud[i] : 0;
         v = (kb < npr ? kb : npr) + (int)(hi - lo) - npr;
       }
@@ -252,90 +365,133 @@ __global__ __launch_bounds__(NT) void sel_count(const float* __restrict__ b,
   }
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  const Sel st = sel_stage(w, kbud, c.s, n_seq, 3, c.begin == c.lo, sh);
-  uint8_t pv[PER], in[PER];
-  float bv[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t j = c.begin + threadIdx.x + (int64_t)i * NT;
-    in[i] = j < c.end;
-    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
-    bv[i] = j < c.end ? b[j] : 0.0f;
+  Tokens tk;
+  load_tokens(b, pr, c, tk);
+  Sel st = w.stage[c.s];
+  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, w.hist1 + (size_t)c.s * NB1, lh, sh);
+  if (c.ci == 0 && threadIdx.x == 0) w.stage[n_seq + c.s] = st;
+  if (st.mode == MODE_RADIX) {
+    for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
   }
-  int def = 0, tie = 0;
+  if (threadIdx.x == 0) ncand = 0u;
+  __syncthreads();
+  uint16_t* cl = w.cand + (size_t)c.slot * CH;
+  int def = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if (in[i]) {
-      if (!pv[i] || st.mode == MODE_ALL) {
+    if (!tk.in[i]) continue;
+    if (!tk.pr[i] || st.mode == MODE_ALL) {
+      ++def;
+    } else if (st.mode == MODE_RADIX) {
+      const uint32_t key = score_key(tk.b[i]);
+      const uint32_t hi20 = key >> 12;
+      if (hi20 > st.prefix) {
         ++def;
-      } else if (st.mode == MODE_RADIX) {
-        const uint32_t key = score_key(bv[i]);
-        def += key > st.prefix;
-        tie += key == st.prefix;
+      } else if (hi20 == st.prefix) {
+        const uint32_t d = key & 0xfffu;
+        atomicAdd(&lh[d], 1u);
+        const uint32_t at = atomicAdd(&ncand, 1u);   // at most CH candidates per chunk
+        cl[at] = (uint16_t)d;
+        if (at < (uint32_t)NSMALL) w.slot[c.slot].small[at] = (uint16_t)d;
       }
     }
   }
-  int td, tt;
-  block_excl_scan<NT>(def, sh, &td);
-  block_excl_scan<NT>(tie, sh, &tt);
+  int td;
+  block_excl_scan<NT>(def, sh, &td);                  // contains barriers
   if (threadIdx.x == 0) {
-    w.blk_def[c.slot] = td;
-    w.blk_tie[c.slot] = tt;
+    w.slot[c.slot].def = (uint32_t)td;
+    w.slot[c.slot].ncand = ncand;
+  }
+  if (st.mode == MODE_RADIX) {
+    uint32_t* gh = w.hist2 + (size_t)c.s * NB1;
+    for (int i = threadIdx.x; i < NB1; i += NT) {
+      const uint32_t v = lh[i];
+      if (v) atomicAdd(gh + i, v);
+    }
   }
 }
 
+// ----------------------------------------------------------------- write
 __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
-                                               const int32_t* __restrict__ cu,
-                                               const int32_t* __restrict__ kbud, int n_seq,
+                                               const int32_t* __restrict__ cu, int n_seq,
                                                int64_t t_in, SelWs w,
                                                const int32_t* __restrict__ kept_cu, int64_t cap,
                                                int32_t* __restrict__ kept_idx,
                                                int32_t* __restrict__ kept_pos,
                                                float* __restrict__ kept_b) {
+  __shared__ __attribute__((aligned(16))) uint32_t hs[NB1];
   __shared__ int sh[NT / 64 + 2];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
-  const Sel st = w.stage[2 * (size_t)n_seq + c.s];
+  Tokens tk;
+  load_tokens(b, pr, c, tk);
+  const int64_t kept0 = kept_cu[c.s];
+  Sel st = w.stage[n_seq + c.s];
+  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, w.hist2 + (size_t)c.s * NB1, hs, sh);
+  const uint32_t tau = st.prefix;                  // the K'-th largest key (RADIX)
+  const uint32_t d2 = tau & 0xfffu;
   const int need = st.mode == MODE_RADIX ? (int)st.need : 0;
-  // offsets of this chunk inside its sequence from the counts of the earlier
-  // chunks: ties are taken greedily in chunk order, so the earlier chunks
-  // took min(need, their ties) tied tokens in total
-  const int64_t s0 = slot0_of(cu, c.s, CH);
-  const int ci = (int)(c.slot - s0);
-  int dsum = 0, tsum = 0;
-  for (int i = threadIdx.x; i < ci; i += NT) {
-    dsum += w.blk_def[s0 + i];
-    tsum += w.blk_tie[s0 + i];
+  // the earlier chunks of the sequence: definite keeps, candidates above tau
+  // and candidates equal to tau (one thread per earlier chunk; the candidate
+  // digits are read 32 at a time, four 16-byte loads in flight)
+  int dsum = 0, gsum = 0, tsum = 0;
+  for (int i = threadIdx.x; i < c.ci; i += NT) {
+    const int64_t sl = c.s0 + i;
+    if (sl < 0 || sl >= (int64_t)gridDim.x) continue;
+    // def, ncand and the short list: the record's last 64 bytes
+    const u32x4* tail = reinterpret_cast<const u32x4*>(&w.slot[sl].def);
+    u32x4 t4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t4[k] = ld16(tail + k);
+    dsum += (int)t4[0][0];
+    if (st.mode == MODE_RADIX) {
+      const int n = (int)(t4[0][1] < (uint32_t)CH ? t4[0][1] : (uint32_t)CH);
+      if (n <= NSMALL) {
+#pragma unroll
+        for (int m = 0; m < NSMALL; ++m) {
+          const uint32_t wd = t4[(2 + m / 2) / 4][(2 + m / 2) % 4];
+          const uint32_t d = (wd >> (16 * (m & 1))) & 0xffffu;
+          gsum += m < n && d > d2;
+          tsum += m < n && d == d2;
+        }
+        continue;
+      }
+      const uint16_t* cl = w.cand + (size_t)sl * CH;
+      for (int e0 = 0; e0 < n; e0 += 32) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          v[k] = e0 + 8 * k < n ? ld16(cl + e0 + 8 * k) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t d = (v[k][m >> 1] >> (16 * (m & 1))) & 0xffffu;
+            const bool ok = e0 + 8 * k + m < n;
+            gsum += ok && d > d2;
+            tsum += ok && d == d2;
+          }
+      }
+    }
   }
-  int tot_d, tot_t;
+  int tot_d, tot_g, tot_t;
   block_excl_scan<NT>(dsum, sh, &tot_d);
+  block_excl_scan<NT>(gsum, sh, &tot_g);
   block_excl_scan<NT>(tsum, sh, &tot_t);
   const int tie_base = tot_t;
-  const int64_t out_base = (int64_t)kept_cu[c.s] + tot_d + (tot_t < need ? tot_t : need);
-  // contiguous tokens per thread, so thread order is index order
-  const int64_t j0 = c.begin + (int64_t)threadIdx.x * PER;
-  float bv[PER];
+  const int64_t out_base = kept0 + tot_d + tot_g + (tot_t < need ? tot_t : need);
   uint8_t fl[PER];     // 1: kept for sure, 2: tie at tau
   int nt = 0;
-  uint8_t pv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int64_t j = j0 + i;
-    pv[i] = j < c.end ? pr[j] : (uint8_t)0;
-    bv[i] = j < c.end ? b[j] : 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t j = j0 + i;
     uint8_t f = 0;
-    const float v = bv[i];
-    if (j < c.end) {
-      if (!pv[i] || st.mode == MODE_ALL) {
+    if (tk.in[i]) {
+      if (!tk.pr[i] || st.mode == MODE_ALL) {
         f = 1;
       } else if (st.mode == MODE_RADIX) {
-        const uint32_t key = score_key(v);
-        f = key > st.prefix ? 1 : (key == st.prefix ? 2 : 0);
+        const uint32_t key = score_key(tk.b[i]);
+        f = key > tau ? 1 : (key == tau ? 2 : 0);
       }
     }
     fl[i] = f;
@@ -352,15 +508,16 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
     }
     nk += fl[i];
   }
-  int tk;
-  int64_t o = out_base + block_excl_scan<NT>(nk, sh, &tk);
+  int tk_tot;
+  int64_t o = out_base + block_excl_scan<NT>(nk, sh, &tk_tot);
+  const int64_t j0 = c.begin + (int64_t)threadIdx.x * PER;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (fl[i]) {
-      if (o < cap) {
+      if (o >= 0 && o < cap) {
         kept_idx[o] = (int32_t)(j0 + i);
         if (kept_pos) kept_pos[o] = (int32_t)(j0 + i - c.lo);
-        if (kept_b) kept_b[o] = bv[i];
+        if (kept_b) kept_b[o] = tk.b[i];
       }
       ++o;
     }
@@ -389,10 +546,8 @@ hipError_t select_scratch(void** ptr) {
 }
 
 size_t select_ws_bytes(int64_t t_in, int n_seq) {
-  const int64_t ns = n_slots_of(t_in, n_seq);
-  size_t bytes = sizeof(Sel) * 3 * (size_t)n_seq + sizeof(uint32_t) * (size_t)n_seq * HIST_WORDS +
-                 sizeof(uint32_t) * (size_t)n_seq + 2 * sizeof(int32_t) * (size_t)ns;
-  return (bytes + 255) & ~(size_t)255;
+  size_t off[6];
+  return ws_layout(t_in, n_seq, off);
 }
 
 hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t* cu,
@@ -401,21 +556,18 @@ hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t*
                          void* ws, hipStream_t st) {
   SelWs w = carve(ws, t_in, n_seq);
   const int64_t ns = n_slots_of(t_in, n_seq);
-  int64_t init_blocks = ((int64_t)n_seq * HIST_WORDS + NT - 1) / NT;
-  if (init_blocks > 1024) init_blocks = 1024;
-  hipLaunchKernelGGL(sel_init, dim3((unsigned)init_blocks), dim3(NT), 0, st, n_seq, w);
   const dim3 grid((unsigned)ns);
   if (t_in > 0) {
-    hipLaunchKernelGGL(sel_pass<0>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-    hipLaunchKernelGGL(sel_pass<1>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
-    hipLaunchKernelGGL(sel_pass<2>, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
+    hipLaunchKernelGGL(sel_pass0, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w);
+    hipLaunchKernelGGL(sel_pass1, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
   }
-  // every sequence's kept_cu entry is written by block 0 even when t_in == 0
-  hipLaunchKernelGGL(sel_count, dim3((unsigned)(ns > 0 ? ns : 1)), dim3(NT), 0, st, b, prunable, cu,
+  // every sequence's kept_cu entry is written by block 0, also when t_in == 0
+  // (the pass1 state it reads is then never used: every sequence is empty)
+  hipLaunchKernelGGL(sel_pass2, dim3((unsigned)(ns > 0 ? ns : 1)), dim3(NT), 0, st, b, prunable, cu,
                      k, n_seq, t_in, w, kept_cu);
   if (t_in > 0)
-    hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w,
-                       kept_cu, cap, kept_idx, kept_pos, kept_b);
+    hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w, kept_cu,
+                       cap, kept_idx, kept_pos, kept_b);
   return hipGetLastError();
 }
 

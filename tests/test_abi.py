@@ -151,13 +151,17 @@ def test_select_noalloc_validation(lib):
     assert sel(kcu=None) == 1
     assert sel(idx=None) == 1
     limit = 8 << 20
-    # the largest single sequence the scratch holds, and one chunk past it
-    t = 1 << 21
-    while lib.tg_select_workspace_size(t, 1) <= limit:
-        t += 2048
-    assert sel(t=t) == 3
+    # the smallest single sequence that no longer fits (bisection)
+    lo, hi = 2048, 1 << 28
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if lib.tg_select_workspace_size(mid, 1) <= limit:
+            lo = mid
+        else:
+            hi = mid
+    assert sel(t=hi) == 3
     assert "scratch" in lib.tg_last_error().decode()
-    assert lib.tg_select_workspace_size(t - 2048, 1) <= limit
+    assert lib.tg_select_workspace_size(131072, 1) <= limit     # the 128k layer fits
     assert sel(n_seq=4096, t=4096) == 3          # many sequences: histograms per sequence
 
 

@@ -132,6 +132,27 @@ def test_score_256_row_tiles_short_rows(d):
                  f"T={T} d={d}")
 
 
+def test_score_256_row_tiles_many_short_sequences():
+    """256-row tiles holding several sequences each, empty ones among them:
+    every (sequence, workgroup) pair that meets writes its own partial sum of
+    the normalisation."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(77)
+    lens = [int(v) for v in rng.integers(0, 600, 260)]
+    lens[3] = lens[4] = lens[100] = 0
+    T = sum(lens)
+    d = 256
+    say(f"score: 256-row tiles, {len(lens)} sequences, T={T}")
+    x = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    w1 = f32_to_bf16_bits((rng.standard_normal((256, d)) / np.sqrt(d)).astype(np.float32))
+    b1 = (0.1 * rng.standard_normal(256)).astype(np.float32)
+    w2 = (rng.standard_normal(256) / 16.0).astype(np.float32)
+    pr = (rng.random(T) < 0.7).astype(np.uint8)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    _check_score(dict(x=x, w1=w1, b1=b1, w2=w2, b2=0.1, prunable=pr, cu_seqlens=cu), True,
+                 f"{len(lens)} sequences")
+
+
 def test_score_128k_bf16_full_size():
     say("score: 128k bf16 workload (full size)")
     _check_score(workload(3), True, "128k bf16")

@@ -86,9 +86,13 @@ def test_noalloc_select_rejects_inputs_beyond_the_scratch():
     from learned_token_pruning_06_amd import ops
     from learned_token_pruning_06_amd._lib import TokenGateError
     lib = ops.load()
-    t = 1 << 21
-    while lib.tg_select_workspace_size(t, 1) <= (8 << 20):
-        t += 2048
+    lo, t = 2048, 1 << 28          # t: the smallest single sequence that does not fit
+    while t - lo > 1:
+        mid = (lo + t) // 2
+        if lib.tg_select_workspace_size(mid, 1) <= (8 << 20):
+            lo = mid
+        else:
+            t = mid
     b = torch.zeros(t, dtype=torch.float32, device=DEV)
     pr = torch.ones(t, dtype=torch.uint8, device=DEV)
     cu = i32_dev([0, t])
