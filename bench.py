@@ -30,6 +30,8 @@ PEAK_FP32_TFLOPS = 157.3            # MI355X fp32 vector ALU
 WORKLOAD = 3                        # 128k-token gated layer (the metric's configuration)
 WORKLOAD_NAMES = {
     1: "gated layer 16k: 15872 doc + 512 prompt tokens, K=1984",
+    2: "budget sweep 32k: 32256 doc + 512 prompt tokens, 8 calls with K log-uniform in [1, 16128], "
+       "preset scores with ties and +6 spikes",
     3: "gated layer 128k: 130560 doc + 512 prompt tokens, K=8192",
     4: "ragged batch: 4 sequences of 8192/24576/49152/65536 tokens, K = 1/16 of each doc part",
 }
@@ -58,6 +60,80 @@ def traffic_for(kernel: str, src_files):
     if d.get("source_sha") != source_sha(src_files):
         return None
     return d.get("bytes_per_launch")
+
+
+def mfma_counters_for(kernel: str, src_files):
+    """Matrix-core counters per launch from committed rocprofv3 runs
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs, and the bf16
+    MFMA flops the hardware counted), if they were taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", "pmc_mfma.json")
+    try:
+        d = json.load(open(p))[kernel]
+    except Exception:
+        return None
+    if d.get("source_sha") != source_sha(src_files):
+        return None
+    return {k: d[k] for k in ("mfma_busy", "mfma_flops_per_launch") if k in d}
+
+
+def budget_sweep(g, dev, reps=10):
+    """The 32k budget sweep: for each of the 8 drawn budgets, tg_select_topk on
+    the preset scores, tg_gather of the kept rows and tg_gated_attn over them
+    (Q/K/V: seeded stand-ins of the kept shape; the attention's cost depends
+    only on the shapes).  Mean us per call over `reps` back-to-back calls."""
+    import numpy as np
+    import torch
+    from learned_token_pruning_06_amd import ops
+    from workloads import random_qkv
+    wl = g["wl"]
+    lib = ops.load()
+    T = wl.t_in
+    tb = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    b = torch.from_numpy(np.asarray(g["b_preset"], np.float32)).to(dev)
+    pr = torch.from_numpy(g["prunable"]).to(dev)
+    cu = torch.from_numpy(g["cu_seqlens"]).to(dev)
+    x = tb(g["x"])
+    gain = torch.from_numpy(g["gain"]).to(dev)
+    temp = torch.from_numpy(g["temp"]).to(dev)
+    n_pr = int(g["prunable"].sum())
+    kmax = max(int(k[0]) for k in g["budgets"])
+    tmax = min(kmax, n_pr) + (T - n_pr)
+    q_all, k_all, v_all = (tb(a) for a in random_qkv(22, tmax, wl.hq, wl.hkv, wl.dh))
+    ws = ops.workspace(lib.tg_select_workspace_size(T, 1), dev)
+
+    def time_it(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    rows = []
+    for kk in g["budgets"]:
+        K = int(kk[0])
+        _, tk = ops.kept_sizes(g["cu_seqlens"], [n_pr], [K])
+        kdev = torch.tensor([K], dtype=torch.int32, device=dev)
+        ki = torch.empty(tk, dtype=torch.int32, device=dev)
+        kp, kb = torch.empty_like(ki), torch.empty(tk, dtype=torch.float32, device=dev)
+        kc = torch.empty(2, dtype=torch.int32, device=dev)
+        xk = torch.empty(tk, wl.d, dtype=torch.bfloat16, device=dev)
+        q, k, v = q_all[:tk], k_all[:tk], v_all[:tk]
+        o = torch.empty_like(q)
+        t_sel = time_it(lambda: ops.select_topk(b, pr, cu, kdev, tk, ki, kp, kb, kc, ws))
+        t_gat = time_it(lambda: ops.gather(x, ki, out=xk))
+        t_att = time_it(lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=tk, out=o))
+        fl = 2.0 * wl.dh * wl.hq * tk * (tk + 1)
+        rows.append({"k": K, "t_kept": int(tk), "select_us": round(t_sel, 2),
+                     "gather_us": round(t_gat, 2), "attn_us": round(t_att, 2),
+                     "attn_tflops": round(fl / (t_att * 1e-6) / 1e12, 1),
+                     "attn_frac_of_bf16_peak": round(fl / (t_att * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    del q_all, k_all, v_all, x
+    return rows
 
 
 def cpu_baseline(g, t_kept_cu, score_chunk=16384):
@@ -138,6 +214,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
+    if args.workload == 2:
+        run_sweep(args, dev)
+        return
     g = generate(args.workload)
     lanes = args.workload == WORKLOAD
     wl = g["wl"]
@@ -244,6 +323,9 @@ def main():
                 "frac": round(ach / peak, 4), "traffic": traffic_for(dom, srcs),
                 "kernel": "gated_attn_bf16" if dom == "attn" else "score_mlp_bf16",
                 "avg_launch_us": round(avg[dom], 2)}
+    mc = mfma_counters_for(dom, srcs)
+    if mc is not None:
+        roofline.update(mc)
 
     def time_it(fn, reps=10):
         fn()
@@ -359,6 +441,11 @@ def main():
                           "graph replay of 50 steps, 2 launches each"}
         del kc, vc
 
+    sweep = None
+    if lanes:
+        # the 32k budget sweep (8 drawn budgets on preset scores) as a lane
+        sweep = budget_sweep(generate(2), dev)
+
     full = None
     if lanes and not args.no_full_context:
         # unpruned reference point: all 131072 tokens kept (stand-in Q/K/V)
@@ -404,7 +491,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the oracle on a bounded sample (cpu_baseline)")
+        log("timing the oracle on the whole step (cpu_baseline)")
         cpu = cpu_baseline(g, kept_cu_h)
 
     out = {
@@ -431,6 +518,48 @@ def main():
         "score_ln2": score_ln2,
         "attn_bwd": attn_bwd,
         "score_bwd": score_bwd,
+        "budget_sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_sweep(args, dev):
+    """--workload 2: the 8-call budget sweep as the measured step (the scores
+    are preset, so a call is select + gather + attention)."""
+    import numpy as np
+    import torch
+    from workloads import generate
+    g = generate(2)
+    wl = g["wl"]
+    log("inputs generated (budget sweep)")
+    for _ in range(max(args.warmup, 1)):
+        budget_sweep(g, dev, reps=1)
+    t0 = time.perf_counter()
+    rows = budget_sweep(g, dev, reps=args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = [r["select_us"] + r["gather_us"] + r["attn_us"] for r in rows]
+    T = wl.t_in
+    value = T * len(rows) / (sum(per_call) * 1e-6)
+    fl = sum(2.0 * wl.dh * wl.hq * r["t_kept"] * (r["t_kept"] + 1) for r in rows)
+    att = sum(r["attn_us"] for r in rows)
+    ach = fl / (att * 1e-6) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sum(per_call) * 1e-3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (preset bf16-grid Gaussian scores with +6 spikes; stand-in Q/K/V)",
+        "config": {"workload": WORKLOAD_NAMES[2], "t_in": T, "k": [r["k"] for r in rows],
+                   "d": wl.d, "hq": wl.hq, "hkv": wl.hkv, "dh": wl.dh,
+                   "step": "8 calls of select+gather+gated_attn (scores preset, no scorer)"},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "gated_attn_bf16",
+                     "avg_launch_us": round(att / len(rows), 2)},
+        "cpu_baseline": None,
+        "budget_sweep": rows,
+        "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
 
