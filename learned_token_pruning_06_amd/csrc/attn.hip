@@ -121,7 +121,13 @@ struct AttnCfg {
   static constexpr int NTHR = 64 * NWAVE;        // threads per workgroup
   static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
   static constexpr int KROW = DH + 24;           // K row: DH values, 16 bias columns, 8 pad
-  static constexpr int VROW = DH + 16;           // V row: DH values, 16 pad (rows 32 B apart mod 256 B)
+  // V row: DH values, 32 pad.  V is read only by transposing 8-byte reads,
+  // which the LDS serves 32 lanes (256 B) at a time: lanes 0..31 address
+  // rows r = 0..3 at byte 32h + 8c (h = 0, 1; c = 0..3), so rows must start
+  // 64 B apart mod 256 B for the 32 addresses to fall on distinct banks.
+  // (With rows 32 B apart, 27% of the kernel's LDS-active cycles were bank
+  // conflicts.)
+  static constexpr int VROW = DH + 32;
   static constexpr int KT = DH / 16;             // MFMA K-steps over the head dim
   static constexpr int DT = DH / 32;             // output tiles over the head dim
   static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile

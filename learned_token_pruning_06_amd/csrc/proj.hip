@@ -54,7 +54,11 @@ TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // the A operand, 8 consecutive k of one column, is two transposing reads
 // (ds_read_b64_tr_b16): within each 16-lane group, output element e of lane
 // i is element i % 4 of the 8 bytes that lane 4e + i / 4 addresses.
-constexpr int kRowW = kTile + 16;    // bf16 per K-major W row (rows 8 banks apart)
+// bf16 per K-major W row: the tile is read only by transposing 8-byte reads,
+// served 32 lanes (256 B) at a time over rows r = 0..3 at byte 32h + 8c, so
+// rows start 64 B apart mod 256 B (576 B) to keep the 32 addresses on
+// distinct banks (544 B rows gave 28% of the LDS-active cycles in conflicts)
+constexpr int kRowW = kTile + 32;
 
 TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
