@@ -147,6 +147,23 @@ TG_DEVINL bool tile_of_slot(const int32_t* cu, int n_seq, int64_t t, int64_t slo
   return t0 < sq.len;
 }
 
+// Work item of block b in the one-dimensional grids of the three passes.
+// Blocks are dealt round-robin over the 8 XCDs, each with its own L2, so the
+// KV head is taken from the low bits of the block index: with 8 KV heads
+// every XCD works on one head group, and its workgroups share the K/V (or
+// Q/dO) tiles of that group in its L2.  Per-head passes (hq heads) put the
+// G query heads of a group on consecutive blocks of one XCD; `reverse`
+// deals the slots last-first (the longest causal work first when each slot
+// is a query tile).
+TG_DEVINL void work_item(int64_t b, int hkv, int g_heads, int64_t n_slots, bool reverse,
+                         int64_t& slot, int& kvh, int& hh) {
+  kvh = (int)(b % hkv);
+  const int64_t r = b / hkv;
+  hh = (int)(r % g_heads);
+  slot = r / g_heads;
+  if (reverse) slot = n_slots - 1 - slot;
+}
+
 // Phase A of every pass: waves 0-3 compute S^T = K.Q^T for tile (kt, qt) =
 // (w & 1, w >> 1), waves 4-7 compute dP^T = V.dO^T for the same tile.  The
 // elementwise work is then split evenly: registers 0-7 of a lane (key rows
@@ -214,7 +231,7 @@ __global__ __launch_bounds__(kThr) void bwdm_stats(
     const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
     const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm,
-    float* __restrict__ lse2, float* __restrict__ dsum) {
+    float* __restrict__ lse2, float* __restrict__ dsum, int64_t n_slots) {
   constexpr int LD = DH + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
       sV[kB * LD];
@@ -222,8 +239,11 @@ __global__ __launch_bounds__(kThr) void bwdm_stats(
   __shared__ float stau[kB], sb[kB], sm_[4][kB], sl_[4][kB], su_[4][kB];
   Seq sq;
   int q0;
-  if (!tile_of_slot(cu, n_seq, t, blockIdx.x, sq, q0)) return;
-  const int h = blockIdx.y, kvh = h / (hq / hkv);
+  int64_t slot;
+  int kvh, hh;
+  work_item(blockIdx.x, hkv, hq / hkv, n_slots, true, slot, kvh, hh);
+  if (!tile_of_slot(cu, n_seq, t, slot, sq, q0)) return;
+  const int h = kvh * (hq / hkv) + hh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, g = lane >> 5, w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
     const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm,
     const float* __restrict__ lse2, const float* __restrict__ dsum, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dbpart) {
+    float* __restrict__ dv, float* __restrict__ dbpart, int64_t n_slots) {
   constexpr int LD = DH + 8, NDT = DH / 32;            // 32-wide d tiles
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
       sV[kB * LD];
@@ -367,8 +387,11 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
   __shared__ float stau[kB], slse[kB], sD[kB], sb[kB];
   Seq sq;
   int k0;
-  if (!tile_of_slot(cu, n_seq, t, blockIdx.x, sq, k0)) return;
-  const int kvh = blockIdx.y, G = hq / hkv;
+  int64_t slot;
+  int kvh, hh0;
+  work_item(blockIdx.x, hkv, 1, n_slots, false, slot, kvh, hh0);
+  if (!tile_of_slot(cu, n_seq, t, slot, sq, k0)) return;
+  const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, w4 = wv & 3, qt = w4 >> 1;
@@ -383,9 +406,13 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
     aK[j] = 0.0f;
   }
   float dbacc = 0.0f;
-  // iterations (head hh, query tile q0) in order; the next one's Q, dO and
-  // row scalars are fetched while the current one is computed
+  // iterations (head hh, query tile q0), query tiles from the last one down
+  // to the diagonal, so that the workgroups of one head group that run
+  // together read the same Q and dO tiles at about the same time; the next
+  // iteration's Q, dO and row scalars are fetched while the current one is
+  // computed
   const int qfirst = (k0 / kB) * kB;
+  const int qlast = ((sq.len - 1) / kB) * kB;
   Pf<DH> pq, po;
   float ptau = 0.0f, plse = 0.0f, pD = 0.0f;
   auto fetch = [&](int hh, int q0) {
@@ -400,11 +427,11 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
       pD = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
     }
   };
-  fetch(0, qfirst);
+  fetch(0, qlast);
   for (int hh = 0; hh < G; ++hh) {
     const int h = kvh * G + hh;
     const float gh = gain[h];
-    for (int q0 = qfirst; q0 < sq.len; q0 += kB) {
+    for (int q0 = qlast; q0 >= qfirst; q0 -= kB) {
       __syncthreads();
       pq.store(sQ);
       po.store(sO);
@@ -413,8 +440,8 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
         slse[tid] = plse;
         sD[tid] = pD;
       }
-      if (q0 + kB < sq.len) fetch(hh, q0 + kB);
-      else if (hh + 1 < G) fetch(hh + 1, qfirst);
+      if (q0 - kB >= qfirst) fetch(hh, q0 - kB);
+      else if (hh + 1 < G) fetch(hh + 1, qlast);
       __syncthreads();
       floatx16 acc;
       phase_a<DH>(acc, wv, lane, sK, sV, sQ, sO, sX);
@@ -480,7 +507,7 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
     const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm,
     const float* __restrict__ lse2, const float* __restrict__ dsum, float* __restrict__ dq,
-    double* __restrict__ gpart) {
+    double* __restrict__ gpart, int64_t n_slots) {
   constexpr int LD = DH + 8, NDT = DH / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
       sV[kB * LD];
@@ -488,15 +515,18 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
   __shared__ float sX[kB * kLX];
   __shared__ float stau[kB], slam[kB], slse[kB], sD[kB], sb[kB];
   __shared__ double sred[2][kThr / 64];
-  const int h = blockIdx.y, kvh = h / (hq / hkv);
+  int64_t slot;
+  int kvh, hh;
+  work_item(blockIdx.x, hkv, hq / hkv, n_slots, true, slot, kvh, hh);
+  const int h = kvh * (hq / hkv) + hh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, w4 = wv & 3, qt = w4 >> 1;
   const int ct = wv & 1, dt = wv >> 1;                  // phase C: queries 32ct, d 32dt
-  double* gp = gpart + ((int64_t)blockIdx.x * hq + h) * 2;
+  double* gp = gpart + (slot * hq + h) * 2;
   Seq sq;
   int q0;
-  if (!tile_of_slot(cu, n_seq, t, blockIdx.x, sq, q0)) {
+  if (!tile_of_slot(cu, n_seq, t, slot, sq, q0)) {
     if (tid == 0) {                                    // every slot leaves a partial
       gp[0] = 0.0;
       gp[1] = 0.0;
@@ -611,14 +641,15 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     hipLaunchKernelGGL((bwdm_dsum<DHv>), dim3((unsigned)dsum_blocks), dim3(256), 0, st,          \
                        static_cast<const uint16_t*>(fwd_out), op, t * hq, dsum);                 \
   else                                                                                           \
-    hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp, \
-                       op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2, dsum); \
-  hipLaunchKernelGGL((bwdm_dkdv<DHv>), dim3((unsigned)nq, hkv), dim3(kThr), 0, st, qp, kp, vp,  \
+    hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, \
+                       vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2,    \
+                       dsum, nq);                                                                \
+  hipLaunchKernelGGL((bwdm_dkdv<DHv>), dim3((unsigned)(nq * hkv)), dim3(kThr), 0, st, qp, kp, vp, \
                      op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum,     \
-                     dk, dv, dbpart);                                                            \
-  hipLaunchKernelGGL((bwdm_dq<DHv>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp, op, \
-                     kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, dq,     \
-                     gpart);
+                     dk, dv, dbpart, nq);                                                        \
+  hipLaunchKernelGGL((bwdm_dq<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, vp,  \
+                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, dq, \
+                     gpart, nq);
   if (dh == 128) {
     TG_BWDM(128)
   } else if (dh == 64) {

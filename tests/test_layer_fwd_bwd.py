@@ -10,14 +10,22 @@ ref_gated_attn_bwd and ref_score_bwd on its own values only.
 
 The kept set must match exactly (the scores agree to ~1e-6 and this seed
 has no near-tie at the budget boundary).  The chained floating-point results
-carry the bf16 rounding of the projections, so they are held to the bf16
-attention bar, rel-L2 <= 1e-2."""
+carry the bf16 rounding of the projections, so end to end they are held to
+the bf16 attention bar, rel-L2 <= 1e-2.  Each stage is also checked on its
+own, against the oracle fed the values that stage read on the GPU, at that
+stage's bar: the scores within 1e-5 (rms floor); q, k, v within one bf16
+rounding plus 1e-3 of their RMS; the attention output at the bf16 bars
+(global, per head, per row); dq, dk, dv at 1e-2 (P and dS enter the
+products in bf16); db within 1e-5 rel-L2 and dgain, dtemp within 1e-5 of
+their error scale; the scorer's dW1, db1, dw2 within 1e-5 and db2 within
+1e-5 of its error scale."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from gpu_util import DEV, bf16_dev, f32_dev, i32_dev, rel_l2, say, to_f64, u8_dev
+from gpu_util import (DEV, bf16_dev, check_attn, f32_dev, i32_dev, rel_l2, say, score_err,
+                      to_f64, u8_dev)
 from workloads import bf16_to_f64, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -94,3 +102,32 @@ def test_gated_layer_forward_and_backward_chain():
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= 1e-2, f"{n}: rel-L2 {e:.3e}"
+
+    # ---- each stage against the oracle fed that stage's GPU inputs
+    say("layer chain: stage by stage")
+    g_b, g_raw = b.cpu().numpy().astype(np.float64), b_raw.cpu().numpy().astype(np.float64)
+    assert score_err(g_raw, r_raw) <= 1e-5 and score_err(g_b, r_b) <= 1e-5, "scores"
+    for name, got, ref in (("q", q, r_q), ("k", k, r_k), ("v", v, r_v)):
+        gg = to_f64(got)
+        over = float(np.max(np.abs(gg - ref) - (2.0 ** -8 * np.abs(ref)
+                                                  + 1e-3 * np.sqrt(np.mean(ref ** 2)))))
+        assert over <= 0.0, f"{name}: beyond one bf16 rounding by {over:.2e}"
+    gq, gk, gv = to_f64(q), to_f64(k), to_f64(v)
+    g_kb, g_pos = kb.cpu().numpy().astype(np.float64), pos.cpu().numpy()
+    s_out = O.ref_gated_attn(gq, gk, gv, g_kb, g_pos, r_kc, gain, temp)
+    check_attn(to_f64(out), s_out, "bf16", "layer chain, attention stage")
+    *s_g, s_sg, s_st = O.ref_gated_attn_bwd(gq, gk, gv, g_kb, g_pos, r_kc, gain, temp, r_do,
+                                            error_scales=True)
+    stage = {"dq": rel_l2(to_f64(dq), s_g[0]), "dk": rel_l2(to_f64(dk), s_g[1]),
+             "dv": rel_l2(to_f64(dv), s_g[2]), "db": rel_l2(to_f64(db), s_g[3]),
+             "dgain": float(np.max(np.abs(to_f64(dg) - s_g[4]) / (np.abs(s_g[4]) + s_sg))),
+             "dtemp": float(np.max(np.abs(to_f64(dt) - s_g[5]) / (np.abs(s_g[5]) + s_st)))}
+    *s_sb, s_scale = O.ref_score_bwd(xd, w1d, b1, w2, b2, pr, cu, idx.cpu().numpy(), r_kc,
+                                     to_f64(db), eps=O.readings.EPS, error_scales=True)
+    stage.update({"dw1": rel_l2(to_f64(dw1), s_sb[1]), "db1": rel_l2(to_f64(db1), s_sb[2]),
+                  "dw2": rel_l2(to_f64(dw2), s_sb[3]),
+                  "db2": abs(float(to_f64(db2)[0]) - s_sb[4]) / (abs(s_sb[4]) + s_scale)})
+    say("  stage " + " ".join(f"{n}={e:.2e}" for n, e in stage.items()))
+    bars = {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2}
+    for n, e in stage.items():
+        assert e <= bars.get(n, 1e-5), f"stage {n}: {e:.3e}"
