@@ -393,6 +393,44 @@ tg_status tg_gated_decode(const void* q, const void* k_cache, const void* v_cach
                           const float* gain, const float* temp, float sm_scale, void* ws,
                           size_t ws_bytes, tg_stream stream);
 
+/* ------------------------------------------------------------------------
+ * Device-side contract checks (debugging aid, off by default).
+ *
+ * Some preconditions depend on device data the host never reads.  When they
+ * are broken the kernels still stay inside their buffers (offsets are
+ * clamped, out-of-range gather indices give zero rows, selected tokens past
+ * the capacity are dropped), but the results are meaningless.  With
+ * tg_set_contract_checks(1), every later call on this process also enqueues
+ * small check kernels on its stream that OR one bit per broken rule into a
+ * per-GPU flag word:
+ *   TG_CONTRACT_OFFSETS          cu_seqlens of tg_score, tg_select_topk(_noalloc),
+ *                                tg_score_bwd: cu[0] < 0, decreasing, or past t_in
+ *   TG_CONTRACT_NEGATIVE_BUDGET  a budget k[s] < 0 (tg_select_topk reads it as 0;
+ *                                §4.1 Eq. 4 defines K >= 0)
+ *   TG_CONTRACT_CAPACITY         t_kept_capacity below the kept count (tokens dropped)
+ *   TG_CONTRACT_INDEX            tg_gather (or tg_score_bwd's kept_idx) index
+ *                                outside [0, n_src)
+ *   TG_CONTRACT_KEPT_OFFSETS     kept_cu_seqlens / cache_cu_seqlens of tg_gated_attn,
+ *                                tg_gated_attn_bwd, tg_gated_decode, tg_score_bwd:
+ *                                negative, decreasing, or past the row count
+ *   TG_CONTRACT_POSITIONS        kept_pos negative or not strictly increasing within
+ *                                a sequence (§4.2 Eq. 8: causality by original
+ *                                position is then not the order of the rows)
+ * The checks cost a few microseconds per call and are meant for debugging.
+ * tg_contract_status waits for the work queued on `stream`, returns the
+ * word in *flags (host) and clears it; unlike every other call it
+ * synchronises the stream.  Checks of calls on other streams are ordered
+ * only by the caller's own synchronisation.
+ * ---------------------------------------------------------------------- */
+#define TG_CONTRACT_OFFSETS 0x1u
+#define TG_CONTRACT_NEGATIVE_BUDGET 0x2u
+#define TG_CONTRACT_CAPACITY 0x4u
+#define TG_CONTRACT_INDEX 0x8u
+#define TG_CONTRACT_KEPT_OFFSETS 0x10u
+#define TG_CONTRACT_POSITIONS 0x20u
+tg_status tg_set_contract_checks(int32_t on);
+tg_status tg_contract_status(uint32_t* flags, tg_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

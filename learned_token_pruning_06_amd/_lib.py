@@ -15,6 +15,8 @@ LIB_PATH = os.environ.get("TG_LIBRARY", os.path.join(_PKG, "libtokengate.so"))
 
 TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_HIP = range(5)
 TG_F32, TG_BF16 = 0, 1
+CONTRACT_BITS = {"offsets": 0x1, "negative_budget": 0x2, "capacity": 0x4, "index": 0x8,
+                 "kept_offsets": 0x10, "positions": 0x20}
 
 c_vp, c_i32, c_i64, c_f32, c_sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                    ctypes.c_float, ctypes.c_size_t)
@@ -52,6 +54,8 @@ PROTOTYPES = {
                                          c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                          c_sz, c_vp]),
+    "tg_set_contract_checks": (ctypes.c_int, [c_i32]),
+    "tg_contract_status": (ctypes.c_int, [c_vp, c_vp]),
     "tg_gated_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i64]),
     "tg_gated_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp, c_vp,
                                        c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,

@@ -36,6 +36,26 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 static_assert(tg::kSelScratchBytes == TG_SELECT_SCRATCH_BYTES, "scratch size");
 
+namespace {
+// the selection with its contract checks when they are on: offsets and
+// budgets before, the kept count against the capacity after
+hipError_t select_checked(const float* b, const uint8_t* pr, const int32_t* cu, const int32_t* k,
+                          int n_seq, int64_t t_in, int64_t cap, int32_t* kept_idx,
+                          int32_t* kept_pos, float* kept_b, int32_t* kept_cu, void* ws,
+                          hipStream_t st) {
+  const bool chk = tg::contract_checks_on();
+  hipError_t e = hipSuccess;
+  if (chk) {
+    e = tg::contract_offsets(cu, n_seq, t_in, TG_CONTRACT_OFFSETS, st);
+    if (e == hipSuccess) e = tg::contract_budgets(k, n_seq, st);
+    if (e != hipSuccess) return e;
+  }
+  e = tg::launch_select(b, pr, cu, k, n_seq, t_in, cap, kept_idx, kept_pos, kept_b, kept_cu, ws, st);
+  if (e == hipSuccess && chk) e = tg::contract_capacity(kept_cu, n_seq, cap, st);
+  return e;
+}
+}  // namespace
+
 hipError_t tg::device_cu_count(int* n_cu) {
   static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
@@ -109,6 +129,11 @@ tg_status tg_score(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_i
   if (ws_bytes < tg::score_ws_bytes(t_in, n_seq))
     return fail(TG_ERR_WORKSPACE, "tg_score: workspace %zu < %zu bytes", ws_bytes,
                 tg::score_ws_bytes(t_in, n_seq));
+  if (tg::contract_checks_on()) {
+    const hipError_t ce = tg::contract_offsets(cu_seqlens, n_seq, t_in, TG_CONTRACT_OFFSETS,
+                                               (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_score contract check");
+  }
   hipError_t e = tg::launch_score(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, b2, prunable,
                                   cu_seqlens, n_seq, eps, norm_eps, b_raw, b, ws,
                                   (hipStream_t)stream);
@@ -157,8 +182,8 @@ tg_status tg_select_topk(const float* b, const uint8_t* prunable, const int32_t*
   if (ws_bytes < tg::select_ws_bytes(t_in, n_seq))
     return fail(TG_ERR_WORKSPACE, "tg_select_topk: workspace %zu < %zu bytes", ws_bytes,
                 tg::select_ws_bytes(t_in, n_seq));
-  hipError_t e = tg::launch_select(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx,
-                                   kept_pos, kept_b, kept_cu_seqlens, ws, (hipStream_t)stream);
+  hipError_t e = select_checked(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx, kept_pos,
+                                kept_b, kept_cu_seqlens, ws, (hipStream_t)stream);
   return from_hip(e, "tg_select_topk launch");
 }
 
@@ -186,8 +211,8 @@ tg_status tg_select_topk_noalloc(const float* b, const uint8_t* prunable,
   void* ws = nullptr;
   hipError_t e = tg::select_scratch(&ws);
   if (e != hipSuccess) return from_hip(e, "tg_select_topk_noalloc: scratch address");
-  e = tg::launch_select(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx, kept_pos, kept_b,
-                        kept_cu_seqlens, ws, (hipStream_t)stream);
+  e = select_checked(b, prunable, cu_seqlens, k, n_seq, t_in, cap, kept_idx, kept_pos, kept_b,
+                     kept_cu_seqlens, ws, (hipStream_t)stream);
   return from_hip(e, "tg_select_topk_noalloc launch");
 }
 
@@ -205,6 +230,10 @@ tg_status tg_gather(const void* src, int64_t src_stride, int64_t n_src, int64_t 
       !aligned(dst, 4))
     return fail(TG_ERR_UNSUPPORTED, "tg_gather: rows must be 4-byte multiples, 4-byte aligned");
   if (n_rows > INT32_MAX) return fail(TG_ERR_UNSUPPORTED, "tg_gather: too many rows");
+  if (tg::contract_checks_on()) {
+    const hipError_t ce = tg::contract_indices(idx, n_rows, n_src, (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_gather contract check");
+  }
   hipError_t e = tg::launch_gather(src, src_stride, n_src, row_bytes, idx, n_rows, dst, dst_stride,
                                    (hipStream_t)stream);
   return from_hip(e, "tg_gather launch");
@@ -295,6 +324,13 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 is written by the bf16 path only");
   if (lse2 && !aligned(lse2, 4))
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 must be 4-byte aligned");
+  if (tg::contract_checks_on()) {
+    hipError_t ce = tg::contract_offsets(kept_cu, n_seq, t_kept, TG_CONTRACT_KEPT_OFFSETS,
+                                         (hipStream_t)stream);
+    if (ce == hipSuccess && kept_pos)
+      ce = tg::contract_positions(kept_pos, kept_cu, n_seq, t_kept, (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_gated_attn contract check");
+  }
   hipError_t e;
   if (dt == TG_BF16)
     e = tg::launch_attn_bf16(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
@@ -341,6 +377,11 @@ tg_status tg_gated_decode(const void* q, const void* k_cache, const void* v_cach
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 2) ||
       !aligned(ws, 4))
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_decode: q, k_cache, v_cache must be 16-byte aligned");
+  if (tg::contract_checks_on()) {
+    const hipError_t ce = tg::contract_offsets(cache_cu, n_seq, t_cache, TG_CONTRACT_KEPT_OFFSETS,
+                                               (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_gated_decode contract check");
+  }
   hipError_t e = tg::launch_decode(q, k_cache, v_cache, out, cache_b, cache_cu, q_pos, n_seq,
                                    t_cache, max_cache_len, hq, hkv, dh, gain, temp, sm_scale, ws,
                                    (hipStream_t)stream);
@@ -386,6 +427,13 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: saved forward state is for bf16 only");
   if (fwd_out && (!aligned(fwd_out, 16) || !aligned(fwd_lse2, 4)))
     return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_bwd: fwd_out 16-byte, fwd_lse2 4-byte aligned");
+  if (tg::contract_checks_on()) {
+    hipError_t ce = tg::contract_offsets(kept_cu, n_seq, t_kept, TG_CONTRACT_KEPT_OFFSETS,
+                                         (hipStream_t)stream);
+    if (ce == hipSuccess && kept_pos)
+      ce = tg::contract_positions(kept_pos, kept_cu, n_seq, t_kept, (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_gated_attn_bwd contract check");
+  }
   hipError_t e = tg::launch_attn_bwd(q, k, v, dout, (int)dt, t_kept, kept_b, kept_pos, kept_cu,
                                      n_seq, hq, hkv, dh, gain, temp, sm_scale, dq, dk, dv, db,
                                      dgain, dtemp, fwd_out, fwd_lse2, ws, (hipStream_t)stream);
@@ -429,10 +477,35 @@ tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t
   const int64_t es = dt == TG_BF16 ? 2 : 4;
   if ((x && !aligned(x, 16)) || (w1 && !aligned(w1, 16)) || ((x_row_stride * es) % 16) != 0)
     return fail(TG_ERR_UNSUPPORTED, "tg_score_bwd: x and w1 rows must be 16-byte aligned");
+  if (tg::contract_checks_on()) {
+    hipError_t ce = tg::contract_offsets(cu_seqlens, n_seq, t_in, TG_CONTRACT_OFFSETS,
+                                         (hipStream_t)stream);
+    if (ce == hipSuccess)
+      ce = tg::contract_offsets(kept_cu, n_seq, t_kept, TG_CONTRACT_KEPT_OFFSETS,
+                                (hipStream_t)stream);
+    if (ce == hipSuccess && t_kept > 0)
+      ce = tg::contract_indices(kept_idx, t_kept, t_in, (hipStream_t)stream);
+    if (ce != hipSuccess) return from_hip(ce, "tg_score_bwd contract check");
+  }
   hipError_t e = tg::launch_score_bwd(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable,
                                       cu_seqlens, n_seq, eps, b_raw, kept_idx, kept_cu, t_kept,
                                       db_kept, dx, dw1, db1, dw2, db2, ws, (hipStream_t)stream);
   return from_hip(e, "tg_score_bwd launch");
+}
+
+// ------------------------------------------------------ contract checks
+tg_status tg_set_contract_checks(int32_t on) {
+  tg::set_contract_checks(on != 0);
+  return ok();
+}
+
+tg_status tg_contract_status(uint32_t* flags, tg_stream stream) {
+  if (!flags) return fail(TG_ERR_INVALID_ARG, "tg_contract_status: flags is null");
+  unsigned int f = 0u;
+  const hipError_t e = tg::contract_read_and_clear(&f, (hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e, "tg_contract_status");
+  *flags = f;
+  return ok();
 }
 
 }  // extern "C"

@@ -129,6 +129,20 @@ constexpr int kMaxDevices = 64;      // devices the per-device host caches cover
 // the same value)
 hipError_t device_cu_count(int* n_cu);
 
+// Device-side contract checks (contract.hip): on/off switch, and launchers
+// of the check kernels, each ORing its TG_CONTRACT_* bit into this device's
+// flag word.
+bool contract_checks_on();
+void set_contract_checks(bool on);
+hipError_t contract_offsets(const int32_t* cu, int n, int64_t limit, unsigned int bit,
+                            hipStream_t st);
+hipError_t contract_budgets(const int32_t* k, int n, hipStream_t st);
+hipError_t contract_capacity(const int32_t* kept_cu, int n, int64_t cap, hipStream_t st);
+hipError_t contract_indices(const int32_t* idx, int64_t n, int64_t n_src, hipStream_t st);
+hipError_t contract_positions(const int32_t* pos, const int32_t* cu, int n_seq, int64_t t,
+                              hipStream_t st);
+hipError_t contract_read_and_clear(unsigned int* out, hipStream_t st);
+
 // Bytes of the selector's static scratch array (tg_select_topk_noalloc).
 constexpr size_t kSelScratchBytes = (size_t)8 << 20;
 // Device address of this GPU's copy of that array (looked up once per device).

@@ -152,6 +152,22 @@ def select_topk_noalloc(b: torch.Tensor, prunable: torch.Tensor, cu_seqlens: tor
     check("tg_select_topk_noalloc", st)
 
 
+def set_contract_checks(on: bool = True):
+    """tg_set_contract_checks: enqueue device-side contract checks with every
+    later call (debugging aid)."""
+    check("tg_set_contract_checks", load().tg_set_contract_checks(1 if on else 0))
+
+
+def contract_status(device=None):
+    """tg_contract_status: the set of broken rules since the last read (names
+    from _lib.CONTRACT_BITS), after the current stream's work; clears them."""
+    from ._lib import CONTRACT_BITS
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    flags = ctypes.c_uint32(0)
+    check("tg_contract_status", load().tg_contract_status(ctypes.byref(flags), _stream(dev)))
+    return {name for name, bit in CONTRACT_BITS.items() if flags.value & bit}
+
+
 # -------------------------------------------------------------------- gather
 def gather(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = None):
     """tg_gather: out[r] = src[idx[r]] over the first axis of a contiguous src."""

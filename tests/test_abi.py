@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -163,6 +163,15 @@ def test_select_noalloc_validation(lib):
     assert "scratch" in lib.tg_last_error().decode()
     assert lib.tg_select_workspace_size(131072, 1) <= limit     # the 128k layer fits
     assert sel(n_seq=4096, t=4096) == 3          # many sequences: histograms per sequence
+
+
+def test_contract_switch_and_status_validation(lib):
+    """Switching the device-side checks is host-only; a null flags pointer is
+    rejected before anything touches a device."""
+    assert lib.tg_set_contract_checks(1) == 0
+    assert lib.tg_set_contract_checks(0) == 0
+    assert lib.tg_contract_status(None, None) == 1
+    assert "null" in lib.tg_last_error().decode()
 
 
 def test_gather_validation(lib):
