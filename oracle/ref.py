@@ -564,6 +564,36 @@ def ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db
     return out
 
 
+def ref_score_prenorm_bwd(a, gamma, norm_eps: float, w1, b1, w2, b2, prunable, cu_seqlens,
+                          kept_idx, kept_cu, db_kept, eps: float = R.EPS,
+                          error_scales: bool = False):
+    """The same gradients when the scorer reads the residual a^L and applies
+    the block's second norm itself, b~_j = MLP(LN2(a_j)) ([TG] §4.1 Eq. 3
+    with §3 Eq. 1's LN2, read as an RMSNorm, R22).  With
+    r_j = sqrt(mean_c a_jc^2 + norm_eps) and x_j = gamma * a_j / r_j,
+    ref_score_bwd at x gives dx, dW1, db1, dw2, db2; the norm then passes
+        dgamma = sum_j dx_j * a_j / r_j
+        da_j   = gamma * dx_j / r_j - a_j (sum_c gamma_c dx_jc a_jc) / (d r_j^3)
+    (the derivative of a_j / r_j is I / r_j - a_j a_j^T / (d r_j^3)).
+    gamma None means ones (dgamma is still returned).
+    Returns (da [T, d], dw1 [h, d], dgamma [d], db1 [h], dw2 [h], db2); with
+    ``error_scales`` also ref_score_bwd's scale of db2.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    d = a.shape[1]
+    g = np.ones(d) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    r = np.sqrt(np.mean(a * a, axis=1) + float(norm_eps))
+    x = ref_rmsnorm(a, g, norm_eps)
+    got = ref_score_bwd(x, w1, b1, w2, b2, prunable, cu_seqlens, kept_idx, kept_cu, db_kept,
+                        eps=eps, error_scales=error_scales)
+    dx, dw1, db1, dw2, db2 = got[:5]
+    dgamma = np.sum(dx * a / r[:, None], axis=0)
+    gdx = dx * g[None, :]
+    da = gdx / r[:, None] - a * (np.sum(gdx * a, axis=1) / (d * r ** 3))[:, None]
+    out = (da, dw1, dgamma, db1, dw2, db2)
+    return out + tuple(got[5:])
+
+
 # ---------------------------------------------------------------------------
 # harness-level projection (outside the four library calls)
 # ---------------------------------------------------------------------------

@@ -777,6 +777,90 @@ def test_score_bwd_matches_torch_autograd_fp64():
         assert np.allclose(g, t.grad.numpy(), rtol=1e-11, atol=1e-12)
 
 
+def _prenorm_loss(a, g, ne, w1, b1, w2, b2, pr, cu, kept_idx, db_kept):
+    raw = O.ref_score_prenorm(a, g, ne, w1, b1, w2, b2)
+    b, _ = O.ref_normalise(raw, pr, cu, 1e-6)
+    return float(np.sum(np.asarray(db_kept) * b[np.asarray(kept_idx)]))
+
+
+def test_score_prenorm_bwd_matches_central_differences():
+    """The LN2-fused scorer's gradients w.r.t. the residual rows, W1, the
+    norm's weight, b1, w2 and b2 against central differences of the loss
+    through the forward oracle (kept set fixed, as for the plain form)."""
+    x, w1, b1, w2, pr, cu, ki, kc, dbk = _score_bwd_case(63)
+    rng = _rng(64)
+    a = 3.0 * x + 0.5                                # rows far from unit RMS
+    g = rng.uniform(0.5, 1.5, a.shape[1])
+    ne = 1e-3
+    da, dw1, dg, db1, dw2, db2 = O.ref_score_prenorm_bwd(a, g, ne, w1, b1, w2, 0.2, pr, cu, ki,
+                                                         kc, dbk, eps=1e-6)
+    base = dict(a=a, g=g, w1=w1, b1=b1, w2=w2)
+    grads = dict(a=da, g=dg, w1=dw1, b1=db1, w2=dw2)
+    e = 1e-6
+    for name, grad in grads.items():
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in np.shape(base[name]))
+            vals = []
+            for sgn in (1, -1):
+                p = {n: np.array(v, copy=True) for n, v in base.items()}
+                p[name][idx] += sgn * e
+                vals.append(_prenorm_loss(p["a"], p["g"], ne, p["w1"], p["b1"], p["w2"], 0.2, pr,
+                                          cu, ki, dbk))
+            fd = (vals[0] - vals[1]) / (2 * e)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    fd = (_prenorm_loss(a, g, ne, w1, b1, w2, 0.2 + e, pr, cu, ki, dbk)
+          - _prenorm_loss(a, g, ne, w1, b1, w2, 0.2 - e, pr, cu, ki, dbk)) / (2 * e)
+    assert abs(fd - db2) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_score_prenorm_bwd_matches_torch_rms_norm_autograd():
+    """Against autograd through torch's own RMSNorm routine in fp64."""
+    x, w1, b1, w2, pr, cu, ki, kc, dbk = _score_bwd_case(65, lens=(12, 5, 9), d=8, h=4)
+    rng = _rng(66)
+    a = 2.0 * x - 0.3
+    g = rng.uniform(0.5, 1.5, a.shape[1])
+    ta, tg, tw1, tb1, tw2 = (torch.tensor(v, dtype=torch.float64, requires_grad=True)
+                             for v in (a, g, w1, b1, w2))
+    tb2 = torch.tensor(0.2, dtype=torch.float64, requires_grad=True)
+    xn = torch.nn.functional.rms_norm(ta, (a.shape[1],), weight=tg, eps=1e-3)
+    raw = torch.nn.functional.silu(xn @ tw1.T + tb1) @ tw2 + tb2
+    parts = []
+    for s in range(len(cu) - 1):
+        lo, hi = int(cu[s]), int(cu[s + 1])
+        m = torch.tensor(pr[lo:hi].astype(bool))
+        rs = torch.sqrt(torch.mean(raw[lo:hi][m] ** 2) + 1e-6)
+        parts.append(torch.where(m, raw[lo:hi] / rs, torch.zeros_like(raw[lo:hi])))
+    b = torch.cat(parts)
+    (b[torch.tensor(ki)] * torch.tensor(dbk)).sum().backward()
+    got = O.ref_score_prenorm_bwd(a, g, 1e-3, w1, b1, w2, 0.2, pr, cu, ki, kc, dbk, eps=1e-6)
+    for v, t in zip(got, (ta, tw1, tg, tb1, tw2, tb2)):
+        assert np.allclose(v, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_score_prenorm_bwd_fold_and_scale_invariance():
+    """Folding the norm's weight into W1 (W1' = W1 diag(gamma), gamma = ones)
+    leaves da unchanged and gives dW1 = dW1' diag(gamma) and
+    dgamma = sum over hidden units of W1 * dW1'.  With norm_eps = 0 the norm
+    is blind to the scale of a row, so every row of da is orthogonal to its
+    row of a."""
+    x, w1, b1, w2, pr, cu, ki, kc, dbk = _score_bwd_case(67)
+    rng = _rng(68)
+    a = 1.7 * x
+    g = rng.uniform(0.5, 1.5, a.shape[1])
+    da, dw1, dg, db1, dw2, db2 = O.ref_score_prenorm_bwd(a, g, 1e-3, w1, b1, w2, 0.2, pr, cu,
+                                                         ki, kc, dbk, eps=1e-6)
+    fa, fw1, _, fb1, fw2, fb2 = O.ref_score_prenorm_bwd(a, None, 1e-3, w1 * g[None, :], b1, w2,
+                                                        0.2, pr, cu, ki, kc, dbk, eps=1e-6)
+    assert np.allclose(fa, da, rtol=1e-12, atol=1e-14)
+    assert np.allclose(fw1 * g[None, :], dw1, rtol=1e-12, atol=1e-14)
+    assert np.allclose(np.sum(w1 * fw1, axis=0), dg, rtol=1e-12, atol=1e-14)
+    assert np.allclose(fb1, db1, rtol=1e-12) and np.allclose(fw2, dw2, rtol=1e-12)
+    assert abs(fb2 - db2) <= 1e-12 * max(1.0, abs(db2))
+    z, *_ = O.ref_score_prenorm_bwd(a, g, 0.0, w1, b1, w2, 0.2, pr, cu, ki, kc, dbk, eps=1e-6)
+    assert np.max(np.abs(np.sum(z * a, axis=1))) <= 1e-12 * np.max(np.abs(z) * np.abs(a)) * a.shape[1]
+    assert np.max(np.abs(z)) > 1e-3                   # not orthogonal by being zero
+
+
 # softmax normaliser of the gated attention, base 2 (the backward's statistic)
 def test_attn_lse2_closed_forms():
     """Zero queries and zero scores make every visible logit 0, so row i of a
