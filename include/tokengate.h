@@ -271,7 +271,16 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
  *   db2 = sum_k db~_k        dx_k = W1^T dz_k
  *
  * x, dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable, cu_seqlens, n_seq,
- *   eps: as for tg_score (plain rows: the LN2-fused form has no backward).
+ *   eps, norm_eps: as for tg_score, the same values as the forward call.
+ * norm_eps >= 0 (the LN2-fused form, §3 Eq. 1 in front of Eq. 3): x rows
+ *          are the residual a and w1 is W1' = W1 diag(g) with the norm's
+ *          weight folded in.  With inv_k = 1 / sqrt(mean_c a_kc^2 + norm_eps)
+ *          and z_k = inv_k W1' a_k + b1, the outputs are the gradients at a
+ *          and at W1':
+ *            dW1' = sum_k (inv_k dz_k) a_k^T
+ *            dx_k = W1'^T (inv_k dz_k) - c_k a_k,  c_k = inv_k^3 / d * dz_k . (W1' a_k)
+ *          (db1, dw2, db2 unchanged).  The caller unfolds the weight:
+ *          dW1 = dW1' diag(g) and dg_c = sum_j W1[j][c] dW1'[j][c].
  * b_raw    dev [t_in] f32: b~ of the forward (tg_score's b_raw output).
  * kept_idx, kept_cu_seqlens dev: tg_select_topk's outputs; t_kept rows.
  * db_kept  dev [t_kept] f32: gradient w.r.t. the kept scores (the db of
@@ -284,16 +293,16 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
  * f32 rows, and bf16 rows with h != 256 or d % 256 != 0: fp32 arithmetic on
  * the vector ALU.  bf16 rows with h == 256 and d % 256 == 0: dz is recomputed
  * on the matrix cores with the forward's tiling and rounded to bf16 for the
- * dW1 and dx products (fp32 accumulation); db1, dw2 and db2 stay fp32.  Fixed
- * reduction orders on both paths (bitwise reproducible).  Supported:
- * d % 64 == 0, h % 64 == 0, x_row_stride and d < 2^22, x and w1 rows
- * 16-byte aligned.
+ * dW1 and dx products (fp32 accumulation); db1, dw2, db2 and the LN2 term
+ * c_k a_k stay fp32.  Fixed reduction orders on both paths (bitwise
+ * reproducible).  Supported: d % 64 == 0, h % 64 == 0, x_row_stride and
+ * d < 2^22, x and w1 rows 16-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32_t h);
 tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
                        int32_t h, const void* w1, const float* b1, const float* w2,
                        const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq,
-                       float eps, const float* b_raw, const int32_t* kept_idx,
+                       float eps, float norm_eps, const float* b_raw, const int32_t* kept_idx,
                        const int32_t* kept_cu_seqlens, int64_t t_kept, const float* db_kept,
                        float* dx, float* dw1, float* db1, float* dw2, float* db2, void* ws,
                        size_t ws_bytes, tg_stream stream);

@@ -449,13 +449,14 @@ size_t tg_score_bwd_workspace_size(int64_t t_in, int32_t n_seq, int32_t d, int32
 tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t t_in, int32_t d,
                        int32_t h, const void* w1, const float* b1, const float* w2,
                        const uint8_t* prunable, const int32_t* cu_seqlens, int32_t n_seq,
-                       float eps, const float* b_raw, const int32_t* kept_idx,
+                       float eps, float norm_eps, const float* b_raw, const int32_t* kept_idx,
                        const int32_t* kept_cu, int64_t t_kept, const float* db_kept, float* dx,
                        float* dw1, float* db1, float* dw2, float* db2, void* ws, size_t ws_bytes,
                        tg_stream stream) {
   if (t_in < 0 || t_kept < 0 || n_seq < 1 || d < 1 || h < 1)
     return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: bad sizes");
   if (!(eps >= 0.0f)) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: eps must be >= 0");
+  if (norm_eps != norm_eps) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: norm_eps is NaN");
   if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: bad dtype");
   if (x_row_stride < d) return fail(TG_ERR_INVALID_ARG, "tg_score_bwd: x_row_stride < d");
   if (d % 64 != 0 || h % 64 != 0)
@@ -488,7 +489,8 @@ tg_status tg_score_bwd(const void* x, tg_dtype dt, int64_t x_row_stride, int64_t
     if (ce != hipSuccess) return from_hip(ce, "tg_score_bwd contract check");
   }
   hipError_t e = tg::launch_score_bwd(x, (int)dt, x_row_stride, t_in, d, h, w1, b1, w2, prunable,
-                                      cu_seqlens, n_seq, eps, b_raw, kept_idx, kept_cu, t_kept,
+                                      cu_seqlens, n_seq, eps, norm_eps, b_raw, kept_idx,
+                                      kept_cu, t_kept,
                                       db_kept, dx, dw1, db1, dw2, db2, ws, (hipStream_t)stream);
   return from_hip(e, "tg_score_bwd launch");
 }

@@ -80,12 +80,21 @@ struct QkEpi {
   double log2_theta;            // log2 of the rotary base; 0 turns the rotation off
 };
 
+// Row correction of the fp32 form (one K split): Y[row, c] -= c[row] *
+// A[row, c] before the store, A bf16 with rows lda elements apart.
+struct RowCorr {
+  const float* c;               // null: no correction
+  const uint16_t* a;
+  int64_t lda;
+};
+
 template <bool F32OUT, bool WROWS = false, bool QKE = false>
 __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
     uint16_t* __restrict__ k, uint16_t* __restrict__ v, int64_t ldw, int k_per,
-    float* __restrict__ y, int64_t ldy, int64_t ys, int64_t w_rows = 0, QkEpi ep = QkEpi{}) {
+    float* __restrict__ y, int64_t ldy, int64_t ys, int64_t w_rows = 0, QkEpi ep = QkEpi{},
+    RowCorr rc = RowCorr{}) {
   static_assert(F32OUT || !WROWS, "K-major W is for the fp32-output form");
   static_assert(!(F32OUT && QKE), "the q/k epilogue is for the bf16 form");
   __shared__ double s_turns[64];                  // QKE: rotation per position, in turns
@@ -256,9 +265,19 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
       for (int i = 0; i < 16; ++i) {
         const int rr = 4 * i + (lane >> 4), c4 = lane & 15;
         const int64_t row = row0 + 64 * rg + rr;
-        const float4 v4 = *reinterpret_cast<const float4*>(stage + rr * kLd + 4 * c4);
-        if (row < t)
-          *reinterpret_cast<float4*>(y + row * ldy + col0 + 128 * ch + 64 * hf + 4 * c4) = v4;
+        float4 v4 = *reinterpret_cast<const float4*>(stage + rr * kLd + 4 * c4);
+        const int col = col0 + 128 * ch + 64 * hf + 4 * c4;
+        if (row < t) {
+          if (rc.c) {
+            const float cr = rc.c[row];
+            const uint2 av = *reinterpret_cast<const uint2*>(rc.a + row * rc.lda + col);
+            v4.x = fmaf(-cr, __uint_as_float(av.x << 16), v4.x);
+            v4.y = fmaf(-cr, __uint_as_float(av.x & 0xffff0000u), v4.y);
+            v4.z = fmaf(-cr, __uint_as_float(av.y << 16), v4.z);
+            v4.w = fmaf(-cr, __uint_as_float(av.y & 0xffff0000u), v4.w);
+          }
+          *reinterpret_cast<float4*>(y + row * ldy + col) = v4;
+        }
       }
     }
   } else {
@@ -414,8 +433,9 @@ hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const
 
 hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void* w, int64_t ldw,
                                int n, int64_t kdim, int splits, float* y, int64_t ldy,
-                               hipStream_t st) {
+                               hipStream_t st, const float* rowc, const void* a, int64_t lda) {
   if (m == 0) return hipSuccess;
+  if (rowc && (splits != 1 || !a || lda % 4 != 0)) return hipErrorInvalidValue;
   int64_t k_per = (kdim + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const dim3 grid = f32_grid(m, n, splits);
@@ -423,7 +443,8 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
   hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x), xs, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{});
+                     (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{},
+                     RowCorr{rowc, static_cast<const uint16_t*>(a), lda});
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct DzOut {                  // outputs of the backward epilogue (BWD)
   float* dw2p;                  // [blocks][H] per-workgroup sums of dbt * SiLU(z)
   float* db1p;                  // [blocks][H] per-workgroup sums of dz
   float* db2p;                  // [blocks]    per-workgroup sums of dbt
+  float* rowc;                  // [t_in] (LN2 only) each row's c = inv^3 / d * sum_h dz_h acc_h
 };
 
 // Backward epilogue shared by the scorer kernels: z = acc + b1,
@@ -77,14 +78,23 @@ struct DzOut {                  // outputs of the backward epilogue (BWD)
 // tiles, a reduce-scatter over the 32 row lanes (lane n ends with value pair
 // 2n, 2n + 1), then the RG row groups in order through LDS (red: [2][RG][H]
 // floats).  Every thread of the workgroup calls it.
-template <int H, int MTA, int RG>
+// NORM (LN2 in front of the scorer, acc = W1' a of the raw row a, inv the
+// row's 1 / RMS): z = acc inv + b1, and the stored dz is the gradient at the
+// unnormalised product, dz inv, which is what dW1' = dz^T a and the first
+// part of da = (dz inv) W1' - c a take; the row's c = inv^3 / d * sum_h
+// dz_h acc_h (the norm's own derivative) is summed per lane, over the lane
+// halves, then over the HS waves of the row group through srow ([HS][RG][64]
+// floats) and written to bo.rowc.
+template <int H, int MTA, int RG, bool NORM = false, int HS = 1>
 TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, int64_t row0,
                            int64_t wg_row0, int64_t t_in, const float* __restrict__ b1,
                            const float* __restrict__ w2, const DzOut& bo, float* red, int tid,
-                           int nthreads) {
+                           int nthreads, float inv0 = 1.0f, float inv1 = 1.0f, int hh = 0,
+                           float* srow = nullptr, const float* sinv = nullptr, int d = 1) {
   const int lane = tid & 63, n = lane & 31, g = lane >> 5;
   const int64_t ra = row0 + n, rb = row0 + 32 + n;
   const float ga = ra < t_in ? bo.dbt[ra] : 0.0f, gb = rb < t_in ? bo.dbt[rb] : 0.0f;
+  float ca = 0.0f, cb = 0.0f;                       // NORM: sum_h dz_h acc_h of rows ra, rb
 #pragma unroll
   for (int mt = 0; mt < MTA; ++mt) {
     if (mt >= nmt) continue;
@@ -97,14 +107,19 @@ TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, in
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * r4 + e;
         const float bb = b1 ? b1[h0 + e] : 0.0f, ww = w2[h0 + e];
-        const float za = acc[mt][0][r] + bb, zb = acc[mt][1][r] + bb;
+        const float za = NORM ? fmaf(acc[mt][0][r], inv0, bb) : acc[mt][0][r] + bb;
+        const float zb = NORM ? fmaf(acc[mt][1][r], inv1, bb) : acc[mt][1][r] + bb;
         const float sa = 1.0f / (1.0f + __expf(-za)), sb2 = 1.0f / (1.0f + __expf(-zb));
         const float da = ga * ww * sa * fmaf(za, 1.0f - sa, 1.0f);
         const float db = gb * ww * sb2 * fmaf(zb, 1.0f - sb2, 1.0f);
         vw[r] = fmaf(ga, za * sa, gb * zb * sb2);
         vb[r] = da + db;
-        const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)da);
-        const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)db);
+        if constexpr (NORM) {
+          ca = fmaf(da, acc[mt][0][r], ca);
+          cb = fmaf(db, acc[mt][1][r], cb);
+        }
+        const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)(NORM ? da * inv0 : da));
+        const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)(NORM ? db * inv1 : db));
         if (ra < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + ra] = ua;
         if (rb < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + rb] = ub;
         pa[e >> 1] |= (uint32_t)ua << (16 * (e & 1));
@@ -135,7 +150,24 @@ TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, in
       red[(1 * RG + rg) * H + hid] = tb;
     }
   }
+  if constexpr (NORM) {
+    ca += __shfl_xor(ca, 32, 64);
+    cb += __shfl_xor(cb, 32, 64);
+    if (g == 0) {
+      srow[(hh * RG + rg) * 64 + n] = ca;
+      srow[(hh * RG + rg) * 64 + 32 + n] = cb;
+    }
+  }
   __syncthreads();
+  if constexpr (NORM) {
+    if (tid < 64 * RG && wg_row0 + tid < t_in) {
+      float c = 0.0f;
+#pragma unroll
+      for (int k = 0; k < HS; ++k) c += srow[(k * RG + tid / 64) * 64 + tid % 64];
+      const float iv = sinv[tid];
+      bo.rowc[wg_row0 + tid] = c * (iv * iv * iv) / (float)d;
+    }
+  }
   for (int hid = tid; hid < H; hid += nthreads) {
     float a = 0.0f, b = 0.0f;
 #pragma unroll
@@ -370,7 +402,8 @@ __global__ __launch_bounds__(kThreads) void score_mlp_bf16(
 
   if constexpr (BWD) {
     float* red = reinterpret_cast<float*>(&sx[0][0]);          // [2][RG][H], K-loop buffers are free
-    dz_epilogue<H, MTA, RG>(acc, nmt, mt0, rg, row0, wg_row0, t_in, b1, w2, bo, red, tid, kThreads);
+    dz_epilogue<H, MTA, RG, NORM, HS>(acc, nmt, mt0, rg, row0, wg_row0, t_in, b1, w2, bo, red,
+                                      tid, kThreads, inv0, inv1, hh, &sred[0][0][0], sinv, d);
     return;
   }
 
@@ -555,13 +588,14 @@ int64_t n_slots(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 
 
 }  // namespace
 
-// Backward helper: z recomputed with the forward tiling (MT = 8, no LN2),
-// with the backward epilogue.  Returns the number of workgroups (the
-// partial-sum rows) through *blocks.
+// Backward helper: z recomputed with the forward tiling (MT = 8; with LN2
+// when norm_eps >= 0, then also each row's c in rowc), with the backward
+// epilogue.  Returns the number of workgroups (the partial-sum rows)
+// through *blocks.
 hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const void* w1,
                            const float* b1, const float* w2, const float* dbt, void* dz, void* dzt,
-                           int64_t ldt, float* dw2p, float* db1p, float* db2p, int64_t* blocks,
-                           hipStream_t st) {
+                           int64_t ldt, float* dw2p, float* db1p, float* db2p, float norm_eps,
+                           float* rowc, int64_t* blocks, hipStream_t st) {
   int n_cu = 0;
   const hipError_t ce = device_cu_count(&n_cu);
   if (ce != hipSuccess) return ce;
@@ -572,16 +606,21 @@ hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const
   const int64_t nb = (t_in + 64 * rg - 1) / (64 * rg);
   *blocks = nb;
   if (t_in == 0) return hipSuccess;
-  DzOut bo{dbt, static_cast<uint16_t*>(dz), static_cast<uint16_t*>(dzt), ldt, dw2p, db1p, db2p};
+  DzOut bo{dbt, static_cast<uint16_t*>(dz), static_cast<uint16_t*>(dzt), ldt, dw2p, db1p, db2p,
+           rowc};
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* wp = static_cast<const uint16_t*>(w1);
-#define TG_DZ(R)                                                                                \
-  hipLaunchKernelGGL((score_mlp_bf16<8, false, R, true>), dim3((unsigned)nb), dim3(kThreads), 0, \
-                     st, xp, xs, t_in, d, wp, b1, w2, 0.0f, -1.0f, nullptr, nullptr, nullptr, \
-                     0, nullptr, bo)
-  if (rg == 4) TG_DZ(4);
-  else if (rg == 2) TG_DZ(2);
-  else TG_DZ(1);
+#define TG_DZ(N, R)                                                                            \
+  hipLaunchKernelGGL((score_mlp_bf16<8, N, R, true>), dim3((unsigned)nb), dim3(kThreads), 0,  \
+                     st, xp, xs, t_in, d, wp, b1, w2, 0.0f, norm_eps, nullptr, nullptr,       \
+                     nullptr, 0, nullptr, bo)
+  if (norm_eps >= 0.0f) {
+    if (rg == 2) TG_DZ(true, 2);
+    else TG_DZ(true, 1);
+  } else {
+    if (rg == 2) TG_DZ(false, 2);
+    else TG_DZ(false, 1);
+  }
 #undef TG_DZ
   return hipGetLastError();
 }

@@ -28,6 +28,17 @@
 //   sbwd_finish sums the partials.
 // The products are register-blocked micro-GEMMs over padded fp32 LDS tiles,
 // each thread owning 4 x 4 outputs (rows 4ty + r, columns tx + 16c).
+//
+// LN2 in front of the scorer (norm_eps >= 0; x rows are the residual a, W1
+// carries the norm's weight, §3 Eq. 1): with inv = 1 / sqrt(mean_c a_c^2 +
+// norm_eps) per row and z = inv W1 a + b1, the stored dz is dz inv, so the
+// same products give dW1 = sum_j (dz inv)_j a_j^T and the first part of
+//   da_j = W1^T (dz inv)_j - c_j a_j,   c_j = inv^3 / d * sum_h dz_jh (W1 a_j)_h,
+// the second being the derivative of the norm itself.  The matrix-core path
+// takes inv and c from the scorer's epilogue and subtracts c a in the dx
+// product's epilogue; the vector path has a row pass for inv (sbwd_rowinv),
+// per-64-hidden-unit partials of c from sbwd_dz, and the subtraction in
+// sbwd_dx.
 #include <type_traits>
 
 #include "common.h"
@@ -182,7 +193,25 @@ __global__ __launch_bounds__(kThr) void sbwd_kept(const uint8_t* __restrict__ pr
   if (j >= 0 && j < t && pr[j]) dbt[j] = fmaf(db_kept[r], seqc[s].x, dbt[j]);
 }
 
-// ---- dz for 64 tokens x 64 hidden units; z recomputed over d
+// ---- LN2: 1 / RMS of each row, one wave per row (4 rows per block)
+template <typename T>
+__global__ __launch_bounds__(kThr) void sbwd_rowinv(const T* __restrict__ x, int64_t xs, int64_t t,
+                                                    int d, float norm_eps,
+                                                    float* __restrict__ inv) {
+  const int64_t j = (int64_t)blockIdx.x * (kThr / 64) + (threadIdx.x >> 6);
+  if (j >= t) return;
+  float ss = 0.0f;
+  for (int c = threadIdx.x & 63; c < d; c += 64) {
+    const float v = ldf(x + j * xs + c);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) inv[j] = 1.0f / sqrtf(ss / (float)d + norm_eps);
+}
+
+// ---- dz for 64 tokens x 64 hidden units; z recomputed over d.  With inv
+// (LN2): z = inv acc + b1, the stored dz is dz inv, and rowp[blockIdx.y][j]
+// gets this block's sum over its hidden units of dz acc (for c_j).
 template <typename T>
 __global__ __launch_bounds__(kThr) void sbwd_dz(const T* __restrict__ x, int64_t xs, int64_t t,
                                                 int d, int h, const T* __restrict__ w1,
@@ -191,7 +220,9 @@ __global__ __launch_bounds__(kThr) void sbwd_dz(const T* __restrict__ x, int64_t
                                                 const float* __restrict__ dbt,
                                                 float* __restrict__ dz, float* __restrict__ dw2p,
                                                 float* __restrict__ db1p,
-                                                float* __restrict__ db2p) {
+                                                float* __restrict__ db2p,
+                                                const float* __restrict__ inv,
+                                                float* __restrict__ rowp) {
   constexpr int LD = kKC + 4;
   __shared__ __attribute__((aligned(16))) float sx[kT * LD], sw[kT * LD];
   __shared__ float sred[2][16][kT];
@@ -231,15 +262,24 @@ __global__ __launch_bounds__(kThr) void sbwd_dz(const T* __restrict__ x, int64_t
   for (int r = 0; r < 4; ++r) {
     const int64_t j = j0 + 4 * ty + r;
     const float g = j < t ? dbt[j] : 0.0f;
+    const float iv = inv && j < t ? inv[j] : 1.0f;
+    float pc = 0.0f;                                  // LN2: sum over the row's columns of dz acc
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int hid = h0 + tx + 16 * c;
-      const float z = acc[r][c] + (b1 ? b1[hid] : 0.0f);
+      const float z = fmaf(acc[r][c], iv, b1 ? b1[hid] : 0.0f);
       const float sg = 1.0f / (1.0f + expf(-z));
       const float dzv = g * w2[hid] * sg * fmaf(z, 1.0f - sg, 1.0f);
-      if (j < t) dz[j * h + hid] = dzv;
+      if (j < t) dz[j * h + hid] = dzv * iv;
       pu[c] = fmaf(g, z * sg, pu[c]);
       pz[c] += dzv;
+      pc = fmaf(dzv, acc[r][c], pc);
+    }
+    if (inv) {
+      // the 16 threads of a row are 16 consecutive lanes (tx)
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) pc += __shfl_xor(pc, o, 64);
+      if (tx == 0 && j < t) rowp[(int64_t)blockIdx.y * t + j] = pc;
     }
   }
 #pragma unroll
@@ -304,11 +344,15 @@ __global__ __launch_bounds__(kThr) void sbwd_dw1(const T* __restrict__ x, int64_
     for (int c = 0; c < 4; ++c) out[(int64_t)(h0 + 4 * ty + r) * d + c0 + tx + 16 * c] = acc[r][c];
 }
 
-// ---- dx for 64 tokens x 64 columns: dz W1 over the hidden units
+// ---- dx for 64 tokens x 64 columns: dz W1 over the hidden units; with inv
+// (LN2) minus c_j x_j, c_j = inv^3 / d * (sum of the nhb partials in rowp)
 template <typename T>
 __global__ __launch_bounds__(kThr) void sbwd_dx(int64_t t, int d, int h, const T* __restrict__ w1,
                                                 const float* __restrict__ dz,
-                                                float* __restrict__ dx) {
+                                                float* __restrict__ dx,
+                                                const T* __restrict__ x, int64_t xs,
+                                                const float* __restrict__ inv,
+                                                const float* __restrict__ rowp, int nhb) {
   constexpr int LDZ = kT + 4, LDW = kT + 4;
   __shared__ __attribute__((aligned(16))) float szt[kKC * LDZ], sw[kKC * LDW];
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -339,9 +383,19 @@ __global__ __launch_bounds__(kThr) void sbwd_dx(int64_t t, int d, int h, const T
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t j = j0 + 4 * ty + r;
-    if (j < t)
+    if (j < t) {
+      float cj = 0.0f;
+      if (inv) {
+        for (int k = 0; k < nhb; ++k) cj += rowp[(int64_t)k * t + j];
+        const float iv = inv[j];
+        cj *= iv * iv * iv / (float)d;
+      }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dx[j * d + c0 + tx + 16 * c] = acc[r][c];
+      for (int c = 0; c < 4; ++c) {
+        const int col = c0 + tx + 16 * c;
+        dx[j * d + col] = inv ? fmaf(-cj, ldf(x + j * xs + col), acc[r][c]) : acc[r][c];
+      }
+    }
   }
 }
 
@@ -437,7 +491,7 @@ struct Layout {
   int64_t n_tb, per_split, tp;
   int n_split;
   bool mfma;
-  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, dzt, w1t, total;
+  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, inv, rowc, dzt, w1t, total;
 };
 
 Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_cu) {
@@ -477,6 +531,10 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
   L.db1p = off; off += al(sizeof(float) * (size_t)L.n_tb * h);
   L.db2p = off; off += al(sizeof(float) * (size_t)L.n_tb);
   L.dw1p = off; off += al(sizeof(float) * (size_t)L.n_split * h * d);
+  // LN2: each row's 1 / RMS (vector path) and c (matrix-core path: [t];
+  // vector path: partials per 64 hidden units, [h / 64][t])
+  L.inv = off; off += al(sizeof(float) * (size_t)t);
+  L.rowc = off; off += al(sizeof(float) * (size_t)t * (L.mfma ? 1 : h / kT));
   L.dzt = L.w1t = off;
   if (L.mfma) {
     L.dzt = off; off += al(sizeof(uint16_t) * (size_t)h * L.tp);
@@ -489,7 +547,8 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
 template <typename T>
 hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const void* w1v,
                     const float* b1, const float* w2, const uint8_t* pr, const int32_t* cu,
-                    int n_seq, float eps, const float* b_raw, const int32_t* kept_idx,
+                    int n_seq, float eps, float norm_eps, const float* b_raw,
+                    const int32_t* kept_idx,
                     const int32_t* kept_cu, int64_t t_kept, const float* db_kept, float* dx,
                     float* dw1, float* db1, float* dw2, float* db2, void* ws, hipStream_t st) {
   int n_cu = 0;
@@ -508,6 +567,9 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
   const T* w1 = static_cast<const T*>(w1v);
   SqPart* part = reinterpret_cast<SqPart*>(w + L.part);
   double* cpart = reinterpret_cast<double*>(w + L.cpart);
+  const bool ln2 = norm_eps >= 0.0f;
+  float* inv = ln2 ? reinterpret_cast<float*>(w + L.inv) : nullptr;
+  float* rowc = ln2 ? reinterpret_cast<float*>(w + L.rowc) : nullptr;
   hipLaunchKernelGGL(sbwd_part, dim3((unsigned)(n_seq + (t + kCh - 1) / kCh)), dim3(kThr), 0, st,
                      b_raw, pr, cu, n_seq, t, part);
   hipLaunchKernelGGL(sbwd_cpart, dim3((unsigned)(n_seq + (t_kept + kCh - 1) / kCh)), dim3(kThr), 0,
@@ -526,7 +588,7 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
       uint16_t* w1t = reinterpret_cast<uint16_t*>(w + L.w1t);
       int64_t nb = 0;
       hipError_t e = launch_score_dz(x, xs, t, d, w1, b1, w2, dbt, dzb, dzt, L.tp, dw2p, db1p,
-                                     db2p, &nb, st);
+                                     db2p, norm_eps, rowc, &nb, st);
       if (e != hipSuccess) return e;
       if (L.tp > t)
         hipLaunchKernelGGL(fill_zero_u16, dim3((unsigned)((h * (L.tp - t) + 255) / 256)), dim3(256),
@@ -537,20 +599,23 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
       // fp32 partials)
       e = launch_gemm_ab_kmajor_f32(dzt, L.tp, h, x, xs, t, d, L.tp, L.n_split, dw1p, d, st);
       if (e != hipSuccess) return e;
-      // dx[j][c] = sum_h dz[j][h] W1^T[c][h]
+      // dx[j][c] = sum_h dz[j][h] W1^T[c][h]  (LN2: - c_j x[j][c])
       if (dx) {
-        e = launch_gemm_abt_f32(dzb, h, t, w1t, h, d, h, 1, dx, d, st);
+        e = launch_gemm_abt_f32(dzb, h, t, w1t, h, d, h, 1, dx, d, st, rowc, x, xs);
         if (e != hipSuccess) return e;
       }
     }
   } else if (t > 0) {
+    if (ln2)
+      hipLaunchKernelGGL((sbwd_rowinv<T>), dim3((unsigned)((t + kThr / 64 - 1) / (kThr / 64))),
+                         dim3(kThr), 0, st, x, xs, t, d, norm_eps, inv);
     hipLaunchKernelGGL((sbwd_dz<T>), dim3((unsigned)L.n_tb, h / kT), dim3(kThr), 0, st, x, xs, t,
-                       d, h, w1, b1, w2, dbt, dz, dw2p, db1p, db2p);
+                       d, h, w1, b1, w2, dbt, dz, dw2p, db1p, db2p, inv, rowc);
     hipLaunchKernelGGL((sbwd_dw1<T>), dim3(h / kT, d / kT, L.n_split), dim3(kThr), 0, st, x, xs, t,
                        d, h, dz, L.per_split, dw1p);
     if (dx)
       hipLaunchKernelGGL((sbwd_dx<T>), dim3((unsigned)L.n_tb, d / kT), dim3(kThr), 0, st, t, d, h,
-                         w1, dz, dx);
+                         w1, dz, dx, x, xs, inv, rowc, h / kT);
   }
   const int64_t hd = (int64_t)h * d;
   hipLaunchKernelGGL(sbwd_finish, dim3((unsigned)((hd + kThr - 1) / kThr + h + 1)), dim3(kThr), 0, st,
@@ -573,15 +638,15 @@ size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h) {
 
 hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
                             const void* w1, const float* b1, const float* w2, const uint8_t* pr,
-                            const int32_t* cu, int n_seq, float eps, const float* b_raw,
-                            const int32_t* kept_idx, const int32_t* kept_cu, int64_t t_kept,
-                            const float* db_kept, float* dx, float* dw1, float* db1, float* dw2,
-                            float* db2, void* ws, hipStream_t st) {
+                            const int32_t* cu, int n_seq, float eps, float norm_eps,
+                            const float* b_raw, const int32_t* kept_idx, const int32_t* kept_cu,
+                            int64_t t_kept, const float* db_kept, float* dx, float* dw1,
+                            float* db1, float* dw2, float* db2, void* ws, hipStream_t st) {
   if (dt == 1)
-    return launch_t<uint16_t>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, b_raw, kept_idx,
-                              kept_cu, t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
-  return launch_t<float>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, b_raw, kept_idx, kept_cu,
-                         t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
+    return launch_t<uint16_t>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, norm_eps, b_raw,
+                              kept_idx, kept_cu, t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
+  return launch_t<float>(x, xs, t, d, h, w1, b1, w2, pr, cu, n_seq, eps, norm_eps, b_raw, kept_idx,
+                         kept_cu, t_kept, db_kept, dx, dw1, db1, dw2, db2, ws, st);
 }
 
 }  // namespace tg

@@ -282,8 +282,14 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
 def score_bwd(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: torch.Tensor,
               cu_seqlens: torch.Tensor, b_raw: torch.Tensor, kept_idx: torch.Tensor,
               kept_cu: torch.Tensor, db_kept: torch.Tensor, b1: Optional[torch.Tensor] = None,
-              eps: float = 1e-6, want_dx: bool = True, ws: Optional[torch.Tensor] = None):
-    """tg_score_bwd: returns (dx or None, dw1, db1, dw2, db2), all f32."""
+              eps: float = 1e-6, want_dx: bool = True, ws: Optional[torch.Tensor] = None,
+              norm_eps: float = -1.0):
+    """tg_score_bwd: returns (dx or None, dw1, db1, dw2, db2), all f32.
+
+    norm_eps >= 0: x holds the residual rows and the scorer applies the
+    block's second norm (w1 with the norm's weight folded in, as for
+    score); dx is then the gradient at the residual rows and dw1 the one at
+    the folded weight."""
     lib = load()
     _need(x, "x", (torch.bfloat16, torch.float32), 2)
     _need(w1, "w1", x.dtype, 2)
@@ -309,7 +315,8 @@ def score_bwd(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, prunable: tor
     if ws is None:
         ws = workspace(nbytes, x.device)
     st = lib.tg_score_bwd(_p(x), _DT[x.dtype], x.stride(0), t, d, h, _p(w1), _p(b1), _p(w2),
-                          _p(prunable), _p(cu_seqlens), n_seq, float(eps), _p(b_raw),
+                          _p(prunable), _p(cu_seqlens), n_seq, float(eps), float(norm_eps),
+                          _p(b_raw),
                           _p(kept_idx), _p(kept_cu), kept_idx.numel(), _p(db_kept), _p(dx),
                           _p(dw1), _p(db1), _p(dw2), _p(db2), _p(ws),
                           ws.numel() * ws.element_size(), _stream(x.device))

@@ -306,13 +306,14 @@ def test_score_bwd_validation(lib):
     assert lib.tg_score_bwd_workspace_size(-1, 1, 2048, 256) == 0
 
     def sb(dt=1, t=100, d=2048, h=256, xs=2048, n_seq=1, tk=10, eps=1e-6, x=FAKE, ws=FAKE,
-           ws_bytes=1 << 34, dw1=FAKE):
-        return lib.tg_score_bwd(x, dt, xs, t, d, h, FAKE, None, FAKE, FAKE, FAKE, n_seq, eps, FAKE,
-                                FAKE, FAKE, tk, FAKE, None, dw1, FAKE, FAKE, FAKE, ws, ws_bytes,
-                                None)
+           ws_bytes=1 << 34, dw1=FAKE, norm_eps=-1.0):
+        return lib.tg_score_bwd(x, dt, xs, t, d, h, FAKE, None, FAKE, FAKE, FAKE, n_seq, eps,
+                                norm_eps, FAKE, FAKE, FAKE, tk, FAKE, None, dw1, FAKE, FAKE, FAKE,
+                                ws, ws_bytes, None)
     assert sb(t=-1) == 1
     assert sb(n_seq=0) == 1
     assert sb(eps=-1.0) == 1
+    assert sb(norm_eps=float("nan")) == 1
     assert sb(dt=4) == 1
     assert sb(xs=100) == 1
     assert sb(d=2000, xs=2000) == 2
