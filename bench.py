@@ -399,13 +399,19 @@ def main():
         ws_sb = ops.workspace(lib.tg_score_bwd_workspace_size(T, 1, wl.d, wl.h), dev)
         t_sbwd = time_it(lambda: ops.score_bwd(x, w1, w2, pr, cu, b_raw, kept_idx, kept_cu, db_k,
                                                b1=b1, ws=ws_sb), reps=3)
+        # the same with the block's RMSNorm fused in front of the scorer (the
+        # rows taken as residuals): dx is then the gradient at the residual
+        t_sbwd_ln2 = time_it(lambda: ops.score_bwd(x, w1, w2, pr, cu, b_raw, kept_idx, kept_cu,
+                                                   db_k, b1=b1, ws=ws_sb, norm_eps=1e-6), reps=3)
         sbwd_flops = 3 * 2.0 * T * wl.d * wl.h
         sbwd_tf = sbwd_flops / (t_sbwd * 1e-6) / 1e12
         score_bwd = {"kernel": "tg_score_bwd", "us": round(t_sbwd, 1), "tflops": round(sbwd_tf, 1),
                      "bound": "mfma", "peak_tflops": PEAK_BF16_TFLOPS,
                      "frac_of_bf16_peak": round(sbwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "us_ln2_fused": round(t_sbwd_ln2, 1),
                      "note": "131072 tokens, d 2048, h 256, bf16 rows; dz in bf16 for the dW1 and "
-                             "dx products, fp32 outputs; dx included"}
+                             "dx products, fp32 outputs; dx included; us_ln2_fused with the "
+                             "block's RMSNorm in front (norm_eps >= 0)"}
         del db_k, ws_sb
 
         # one decode step after the prefill (tg_gated_decode): the new token's
