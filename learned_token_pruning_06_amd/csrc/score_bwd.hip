@@ -20,7 +20,8 @@
 //   sbwd_part, sbwd_cpart, sbwd_seq   per 2048-token / kept-row chunk, then
 //               per sequence: r, |P| and C (fp64 sums) -> 1/r, C/(|P| r^3)
 //   sbwd_dbt    per token: the normaliser term (every prunable token)
-//   sbwd_kept   per kept row: adds db / r at its token
+//   sbwd_kept   per kept row: db / r plus the normaliser term at its token, in
+//               fp64 (the two nearly cancel in sequences of few prunable tokens)
 //   sbwd_dz     per 64 tokens x 64 hidden units: recomputes z (K = d), writes
 //               dz and the block's dw2, db1, db2 partial sums
 //   sbwd_dw1    per 64 hidden x 64 input columns and token split: dz^T x
@@ -139,12 +140,12 @@ __global__ __launch_bounds__(kThr) void sbwd_cpart(const float* __restrict__ b_r
   if (threadIdx.x == 0) cpart[slot] = (s1[0] + s1[1]) + (s1[2] + s1[3]);
 }
 
-// per sequence: its chunk partials in order -> (1/r, C / (|P| r^3))
+// per sequence: its chunk partials in order -> (1/r, C / (|P| r^3)), in fp64
 __global__ __launch_bounds__(64) void sbwd_seq(const int32_t* __restrict__ cu,
                                                const int32_t* __restrict__ kept_cu,
                                                const SqPart* __restrict__ part,
                                                const double* __restrict__ cpart, float eps,
-                                               float2* __restrict__ seqc) {
+                                               double2* __restrict__ seqc) {
   const int s = blockIdx.x;
   if (threadIdx.x != 0) return;
   const int64_t p0 = slot0_of(cu, s, kCh), p1 = slot0_of(cu, s + 1, kCh);
@@ -156,10 +157,10 @@ __global__ __launch_bounds__(64) void sbwd_seq(const int32_t* __restrict__ cu,
     N += part[i].n;
   }
   for (int64_t i = c0; i < c1; ++i) CC += cpart[i];
-  float2 out = make_float2(0.0f, 0.0f);
+  double2 out = make_double2(0.0, 0.0);
   if (N > 0) {
     const double r = sqrt(SQ / (double)N + (double)eps);
-    out = make_float2((float)(1.0 / r), (float)(CC / ((double)N * r * r * r)));
+    out = make_double2(1.0 / r, CC / ((double)N * r * r * r));
   }
   seqc[s] = out;
 }
@@ -168,29 +169,34 @@ __global__ __launch_bounds__(64) void sbwd_seq(const int32_t* __restrict__ cu,
 __global__ __launch_bounds__(kThr) void sbwd_dbt(const float* __restrict__ b_raw,
                                                  const uint8_t* __restrict__ pr,
                                                  const int32_t* __restrict__ cu, int n_seq,
-                                                 int64_t t, const float2* __restrict__ seqc,
+                                                 int64_t t, const double2* __restrict__ seqc,
                                                  float* __restrict__ dbt) {
   const int64_t j = (int64_t)blockIdx.x * kThr + threadIdx.x;
   if (j >= t) return;
   const int s = seq_of_row(cu, n_seq, j);
   const bool in = s >= 0 && j < cu[s + 1];
-  dbt[j] = (in && pr[j]) ? -b_raw[j] * seqc[s].y : 0.0f;
+  dbt[j] = (in && pr[j]) ? (float)(-(double)b_raw[j] * seqc[s].y) : 0.0f;
 }
 
-// ---- per kept row: db~ += db / r at the kept token (prunable only: b := 0 on prompts)
-__global__ __launch_bounds__(kThr) void sbwd_kept(const uint8_t* __restrict__ pr,
+// ---- per kept row: db~ = db / r - b~ C / (|P| r^3) at the kept token (prunable
+// only: b := 0 on prompts)
+__global__ __launch_bounds__(kThr) void sbwd_kept(const float* __restrict__ b_raw,
+                                                  const uint8_t* __restrict__ pr,
                                                   const int32_t* __restrict__ kept_idx,
                                                   const int32_t* __restrict__ kept_cu, int n_seq,
                                                   int64_t t, int64_t t_kept,
                                                   const float* __restrict__ db_kept,
-                                                  const float2* __restrict__ seqc,
+                                                  const double2* __restrict__ seqc,
                                                   float* __restrict__ dbt) {
   const int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x;
   if (r >= t_kept) return;
   const int s = seq_of_row(kept_cu, n_seq, r);
   if (s < 0 || r >= kept_cu[s + 1]) return;
   const int64_t j = kept_idx[r];
-  if (j >= 0 && j < t && pr[j]) dbt[j] = fmaf(db_kept[r], seqc[s].x, dbt[j]);
+  // the whole value in fp64, rounded once: the two terms nearly cancel when
+  // the sequence has few prunable tokens (one token: db eps / r^3)
+  if (j >= 0 && j < t && pr[j])
+    dbt[j] = (float)fma((double)db_kept[r], seqc[s].x, -(double)b_raw[j] * seqc[s].y);
 }
 
 // ---- LN2: 1 / RMS of each row, one wave per row (4 rows per block)
@@ -522,7 +528,7 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
     L.n_split = ns;
   }
   size_t off = 0;
-  L.seqc = off; off += al(sizeof(float2) * (size_t)n_seq);
+  L.seqc = off; off += al(sizeof(double2) * (size_t)n_seq);
   L.part = off; off += al(sizeof(SqPart) * (size_t)(n_seq + (t + kCh - 1) / kCh));
   L.cpart = off; off += al(sizeof(double) * (size_t)(n_seq + (t_kept + kCh - 1) / kCh));
   L.dbt = off; off += al(sizeof(float) * (size_t)t);
@@ -556,7 +562,7 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
   if (ce != hipSuccess) return ce;
   const Layout L = layout(t, t_kept, n_seq, d, h, std::is_same<T, uint16_t>::value ? 1 : 0, n_cu);
   char* w = static_cast<char*>(ws);
-  float2* seqc = reinterpret_cast<float2*>(w + L.seqc);
+  double2* seqc = reinterpret_cast<double2*>(w + L.seqc);
   float* dbt = reinterpret_cast<float*>(w + L.dbt);
   float* dz = reinterpret_cast<float*>(w + L.dz);
   float* dw2p = reinterpret_cast<float*>(w + L.dw2p);
@@ -580,7 +586,7 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
                        pr, cu, n_seq, t, seqc, dbt);
   if (t_kept > 0)
     hipLaunchKernelGGL(sbwd_kept, dim3((unsigned)((t_kept + kThr - 1) / kThr)), dim3(kThr), 0, st,
-                       pr, kept_idx, kept_cu, n_seq, t, t_kept, db_kept, seqc, dbt);
+                       b_raw, pr, kept_idx, kept_cu, n_seq, t, t_kept, db_kept, seqc, dbt);
   if (L.mfma && t > 0) {
     if constexpr (std::is_same<T, uint16_t>::value) {
       uint16_t* dzb = reinterpret_cast<uint16_t*>(w + L.dz);

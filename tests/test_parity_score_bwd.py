@@ -168,3 +168,32 @@ def test_score_bwd_ln2_deterministic():
     a, b = run(c, "bf16"), run(c, "bf16")
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("norm_eps", [None, 1e-5])
+def test_score_bwd_single_token_sequences(norm_eps):
+    """500 sequences of one token each, all budgets 1.  For a prunable token
+    the two terms of db~ nearly cancel (db eps / r^3 is left, r^2 = b~^2 +
+    eps), so they are formed in fp64 and rounded once.  Besides the usual
+    bars, every row of dx is held to 1e-4 of its own norm: the rows with
+    |b~| >> sqrt(eps) have tiny gradients that rel-L2 over all rows does not
+    see, and an fp32 difference of the two terms measured ~1e-2 on them."""
+    lens, budgets = [1] * 500, [1] * 500
+    tag = "plain" if norm_eps is None else "LN2"
+    say(f"score bwd {tag} f32: 500 sequences of one token")
+    c = sbwd_case(17, 500, 128, 64, lens, budgets, "f32", norm_eps=norm_eps)
+    check(c, "f32")
+    got = run(c, "f32")[0]
+    if norm_eps is None:
+        ref = O.ref_score_bwd(c["x"], c["w1"], c["b1"], c["w2"], c["b2"], c["pr"], c["cu"],
+                              c["kept_idx"], c["kept_cu"], c["db_kept"], eps=EPS)[0]
+    else:
+        ref = O.ref_score_prenorm_bwd(c["x"], None, norm_eps, c["w1"], c["b1"], c["w2"],
+                                      c["b2"], c["pr"], c["cu"], c["kept_idx"], c["kept_cu"],
+                                      c["db_kept"], eps=EPS)[0]
+    rn = np.linalg.norm(ref, axis=1)
+    live = rn > 0
+    assert np.all(np.linalg.norm(got, axis=1)[~live] == 0.0)       # prompt tokens
+    worst = float(np.max(np.linalg.norm(got - ref, axis=1)[live] / rn[live]))
+    say(f"  worst row of dx: {worst:.2e} of its norm")
+    assert worst <= 1e-4
