@@ -80,7 +80,7 @@ struct QkEpi {
   double log2_theta;            // log2 of the rotary base; 0 turns the rotation off
 };
 
-// Row correction of the fp32 form (one K split): Y[row, c] -= c[row] *
+// Row correction of the fp32 form (CORR, one K split): Y[row, c] -= c[row] *
 // A[row, c] before the store, A bf16 with rows lda elements apart.
 struct RowCorr {
   const float* c;               // null: no correction
@@ -88,7 +88,7 @@ struct RowCorr {
   int64_t lda;
 };
 
-template <bool F32OUT, bool WROWS = false, bool QKE = false>
+template <bool F32OUT, bool WROWS = false, bool QKE = false, bool CORR = false>
 __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     RowCorr rc = RowCorr{}) {
   static_assert(F32OUT || !WROWS, "K-major W is for the fp32-output form");
   static_assert(!(F32OUT && QKE), "the q/k epilogue is for the bf16 form");
+  static_assert(F32OUT || !CORR, "the row correction is for the fp32 form");
   __shared__ double s_turns[64];                  // QKE: rotation per position, in turns
   __shared__ float s_norm[2][128];                 // QKE: the q and k norm weights
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
@@ -248,6 +249,9 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     // row, 4 rows per store
     constexpr int kLd = 68;                      // floats per staged row (rows 4 banks apart)
     float* stage = reinterpret_cast<float*>(wv < 4 ? &sx[0][0] : &sw[0][0]) + (wv & 3) * 64 * kLd;
+    // row correction (CORR): once a half is staged, the lane's A values
+    // and row factors are loaded 8 rows at a time ahead of their stores, so
+    // the stores wait for 4 round trips per tile instead of one per row
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -262,21 +266,33 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
                             acc[mt][nt][4 * r4 + 3]);
           }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = 4 * i + (lane >> 4), c4 = lane & 15;
-        const int64_t row = row0 + 64 * rg + rr;
-        float4 v4 = *reinterpret_cast<const float4*>(stage + rr * kLd + 4 * c4);
-        const int col = col0 + 128 * ch + 64 * hf + 4 * c4;
-        if (row < t) {
-          if (rc.c) {
-            const float cr = rc.c[row];
-            const uint2 av = *reinterpret_cast<const uint2*>(rc.a + row * rc.lda + col);
-            v4.x = fmaf(-cr, __uint_as_float(av.x << 16), v4.x);
-            v4.y = fmaf(-cr, __uint_as_float(av.x & 0xffff0000u), v4.y);
-            v4.z = fmaf(-cr, __uint_as_float(av.y << 16), v4.z);
-            v4.w = fmaf(-cr, __uint_as_float(av.y & 0xffff0000u), v4.w);
+      for (int ib = 0; ib < 2; ++ib) {
+        uint2 av[8];
+        float cv[8];
+        if constexpr (CORR) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int64_t row = row0 + 64 * rg + 4 * (8 * ib + j) + (lane >> 4);
+            const int col = col0 + 128 * ch + 64 * hf + 4 * (lane & 15);
+            cv[j] = row < t ? rc.c[row] : 0.0f;
+            av[j] = row < t ? *reinterpret_cast<const uint2*>(rc.a + row * rc.lda + col)
+                            : make_uint2(0u, 0u);
           }
-          *reinterpret_cast<float4*>(y + row * ldy + col) = v4;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * ib + j;
+          const int rr = 4 * i + (lane >> 4), c4 = lane & 15;
+          const int64_t row = row0 + 64 * rg + rr;
+          float4 v4 = *reinterpret_cast<const float4*>(stage + rr * kLd + 4 * c4);
+          const int col = col0 + 128 * ch + 64 * hf + 4 * c4;
+          if constexpr (CORR) {
+            v4.x = fmaf(-cv[j], __uint_as_float(av[j].x << 16), v4.x);
+            v4.y = fmaf(-cv[j], __uint_as_float(av[j].x & 0xffff0000u), v4.y);
+            v4.z = fmaf(-cv[j], __uint_as_float(av[j].y << 16), v4.z);
+            v4.w = fmaf(-cv[j], __uint_as_float(av[j].y & 0xffff0000u), v4.w);
+          }
+          if (row < t) *reinterpret_cast<float4*>(y + row * ldy + col) = v4;
         }
       }
     }
@@ -440,11 +456,17 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const dim3 grid = f32_grid(m, n, splits);
   if (grid.x == 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(x), xs, m, (int)kdim,
-                     static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{},
-                     RowCorr{rowc, static_cast<const uint16_t*>(a), lda});
+  if (rowc)
+    hipLaunchKernelGGL((gemm_abt_bf16<true, false, false, true>), grid, dim3(kThreads), 0, st,
+                       static_cast<const uint16_t*>(x), xs, m, (int)kdim,
+                       static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
+                       (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{},
+                       RowCorr{rowc, static_cast<const uint16_t*>(a), lda});
+  else
+    hipLaunchKernelGGL(gemm_abt_bf16<true>, grid, dim3(kThreads), 0, st,
+                       static_cast<const uint16_t*>(x), xs, m, (int)kdim,
+                       static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
+                       (int)k_per, y, ldy, m * ldy, (int64_t)0, QkEpi{}, RowCorr{});
   return hipGetLastError();
 }
 
