@@ -32,6 +32,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 constexpr int kB = 64;               // queries and keys per tile
 constexpr int kThr = 512;            // 8 waves
@@ -43,15 +44,17 @@ TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 TG_DEVINL uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // acc[32 x 32] += A[32 rows][K] . B'[32 rows][K]^T, k contiguous in both
-template <int KSTEPS>
+// (ZERO: acc = the product, the first step adding to a zero constant)
+template <int KSTEPS, bool ZERO = false>
 TG_DEVINL void mma_abt(floatx16& acc, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                        int lane) {
   const int r = lane & 31, kg = lane >> 5;
+  const floatx16 zero = {};
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     const bf16x8 a = as_bf16x8(ld16(A + r * lda + 16 * s + 8 * kg));
     const bf16x8 b = as_bf16x8(ld16(B + r * ldb + 16 * s + 8 * kg));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, (ZERO && s == 0) ? zero : acc, 0, 0, 0);
   }
 }
 
@@ -101,20 +104,35 @@ TG_DEVINL void load_rows(uint16_t* dst, const uint16_t* __restrict__ src, int64_
 }
 
 // The same rows fetched into registers one iteration ahead, then stored.
+// Buffer loads: the resource starts at the tile's first row of head hd and
+// ends after the sequence's last row of that head, so rows past `len` read
+// zeros with no per-row test, and each thread's byte offsets within a tile
+// are fixed for the kernel (set once by init).
 template <int DH>
 struct Pf {
   static constexpr int N = kB * (DH / 8) / kThr;
   u32x4 r[N];
-  TG_DEVINL void load(const uint16_t* __restrict__ src, int64_t lo, int len, int r0, int H,
-                      int hd) {
+  int off[N];
+  TG_DEVINL void init(int H) {
     constexpr int CPR = DH / 8;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int u = threadIdx.x + i * kThr, row = u / CPR, c = u % CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r0 + row < len) v = ld16(src + ((lo + r0 + row) * H + hd) * (int64_t)DH + 8 * c);
-      r[i] = v;
+      off[i] = (row * H * DH + 8 * c) * 2;
     }
+  }
+  TG_DEVINL void load(const uint16_t* __restrict__ src, int64_t lo, int len, int r0, int H,
+                      int hd) {
+    const int64_t rowel = (int64_t)H * DH;           // elements between token rows
+    const int64_t rows = (int64_t)len - r0;
+    int64_t bytes = rows > 0 ? ((rows - 1) * rowel + DH) * 2 : 0;
+    if (bytes > 0x7fffffff) bytes = 0x7fffffff;     // beyond every offset of a tile
+    const uint16_t* base = src + ((lo + r0) * rowel + (int64_t)hd * DH);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
   }
   TG_DEVINL void store(uint16_t* dst) const {
     constexpr int CPR = DH / 8, LD = DH + 8;
@@ -176,39 +194,47 @@ TG_DEVINL void phase_a(floatx16& acc, int wv, int lane, const uint16_t* sK, cons
   constexpr int LD = DH + 8;
   const int w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
   const int n = lane & 31, g = lane >> 5;
+  if (wv < 4) mma_abt<DH / 16, true>(acc, sK + 32 * kt * LD, LD, sQ + 32 * qt * LD, LD, lane);
+  else mma_abt<DH / 16, true>(acc, sV + 32 * kt * LD, LD, sO + 32 * qt * LD, LD, lane);
+  // the parked half as a vector select of the two halves (a run-time
+  // register index would cost a mode switch and a move per element); key
+  // row crow(8 + j) is crow(j) + 16
+  const floatx8 lo = __builtin_shufflevector(acc, acc, 0, 1, 2, 3, 4, 5, 6, 7);
+  const floatx8 hi = __builtin_shufflevector(acc, acc, 8, 9, 10, 11, 12, 13, 14, 15);
+  const floatx8 park = wv < 4 ? hi : lo;
+  float* xrow = sX + (32 * kt + (wv < 4 ? 16 : 0)) * kLX + 32 * qt + n;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  if (wv < 4) {
-    mma_abt<DH / 16>(acc, sK + 32 * kt * LD, LD, sQ + 32 * qt * LD, LD, lane);
-#pragma unroll
-    for (int j = 8; j < 16; ++j) sX[(32 * kt + crow(j, g)) * kLX + 32 * qt + n] = acc[j];
-  } else {
-    mma_abt<DH / 16>(acc, sV + 32 * kt * LD, LD, sO + 32 * qt * LD, LD, lane);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sX[(32 * kt + crow(j, g)) * kLX + 32 * qt + n] = acc[j];
-  }
+  for (int j = 0; j < 8; ++j) xrow[crow(j, g) * kLX] = park[j];
 }
 
-// After phase A and a barrier: this wave's 8 elements (S, dP) and their key
-// rows within the tile; the lane's query row is 32qt + n.
+// After phase A and a barrier: this wave's 8 elements (S, dP).  Element jj
+// sits at key row kbase + kofs(jj) of the tile (kbase = 32kt + 4g, plus 16
+// on the dP wave, whose elements are registers 8..15); the lane's query row
+// is 32qt + n.
+TG_DEVINL constexpr int kofs(int jj) { return 8 * (jj >> 2) + (jj & 3); }
+
 struct Elems {
   float S[8], dP[8];
-  int kr[8];
+  int kbase;
+  TG_DEVINL int kr(int jj) const { return kbase + kofs(jj); }
 };
 
+// (Vector selects of the two halves of acc: a register index chosen at run
+// time would cost a mode switch and a move per element.)
 TG_DEVINL void gather(const floatx16& acc, int wv, int lane, const float* sX, Elems& e) {
   const int w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
   const int n = lane & 31, g = lane >> 5, qr = 32 * qt + n;
-  const bool s_wave = wv < 4;
+  const bool sw = wv < 4;
+  e.kbase = 32 * kt + 4 * g + (sw ? 0 : 16);
+  const floatx8 lo = __builtin_shufflevector(acc, acc, 0, 1, 2, 3, 4, 5, 6, 7);
+  const floatx8 hi = __builtin_shufflevector(acc, acc, 8, 9, 10, 11, 12, 13, 14, 15);
+  const floatx8 mine = sw ? lo : hi;
+  const float* xr = sX + e.kbase * kLX + qr;
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int j = s_wave ? jj : 8 + jj;
-    const int kr = 32 * kt + crow(j, g);
-    const float x = sX[kr * kLX + qr];
-    const float a = acc[s_wave ? jj : 8 + jj];
-    e.S[jj] = s_wave ? a : x;
-    e.dP[jj] = s_wave ? x : a;
-    e.kr[jj] = kr;
+    const float x = xr[kofs(jj) * kLX];
+    e.S[jj] = sw ? mine[jj] : x;
+    e.dP[jj] = sw ? x : mine[jj];
   }
 }
 
@@ -218,8 +244,8 @@ TG_DEVINL void logits(const Elems& e, float (&l2)[8], int qi, int k0, bool full,
                       const float* sb) {
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const float v = fmaf(c1, e.S[jj], c2 * sb[e.kr[jj]]);
-    l2[jj] = (full || k0 + e.kr[jj] <= qi) ? v : -INFINITY;
+    const float v = fmaf(c1, e.S[jj], c2 * sb[e.kr(jj)]);
+    l2[jj] = (full || k0 + e.kr(jj) <= qi) ? v : -INFINITY;
   }
 }
 
@@ -257,6 +283,8 @@ __global__ __launch_bounds__(kThr) void bwdm_stats(
   const int qr = 32 * qt + n, qi = q0 + qr;
   const int q_end = q0 + kB < sq.len ? q0 + kB : sq.len;
   Pf<DH> pk, pv;                                      // key tile k0 + 64, in flight
+  pk.init(hkv);
+  pv.init(hkv);
   float pb = 0.0f;
   pk.load(k, sq.lo, sq.len, 0, hkv, kvh);
   pv.load(v, sq.lo, sq.len, 0, hkv, kvh);
@@ -414,6 +442,8 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
   const int qfirst = (k0 / kB) * kB;
   const int qlast = ((sq.len - 1) / kB) * kB;
   Pf<DH> pq, po;
+  pq.init(hq);
+  po.init(hq);
   float ptau = 0.0f, plse = 0.0f, pD = 0.0f;
   auto fetch = [&](int hh, int q0) {
     const int h = kvh * G + hh;
@@ -457,7 +487,7 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
         probs(e, l2, slse[qr], sD[qr], P, dl);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const int kr = e.kr[jj];
+          const int kr = e.kr(jj);
           const float ds = dl[jj] * tau;
           sPT[kr * kLP + qr] = f2bf(P[jj]);
           sDT[kr * kLP + qr] = f2bf(ds);
@@ -551,6 +581,8 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
   double accg = 0.0, acct = 0.0;
   const int q_end = q0 + kB < sq.len ? q0 + kB : sq.len;
   Pf<DH> pk, pv;                                      // key tile k0 + 64, in flight
+  pk.init(hkv);
+  pv.init(hkv);
   float pb = 0.0f;
   pk.load(k, sq.lo, sq.len, 0, hkv, kvh);
   pv.load(v, sq.lo, sq.len, 0, hkv, kvh);
@@ -579,14 +611,18 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
       float l2[8], P[8], dl[8];
       logits(e, l2, qi < sq.len ? qi : -1, k0, k0 + kB <= q0 && qi < sq.len, c1, c2, sb);
       probs(e, l2, lse, D, P, dl);
+      // the tile's 8 terms in fp32, then into the fp64 sums
+      float pg = 0.0f, pt = 0.0f;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int kr = e.kr[jj];
+        const int kr = e.kr(jj);
         const float tdl = dl[jj] * tau;
         sDS[qr * kLP + kr] = f2bf(tdl);
-        accg = fma((double)tdl, (double)sb[kr], accg);
-        acct = fma((double)(dl[jj] * lam), (double)fmaf(sm, e.S[jj], gh * sb[kr]), acct);
+        pg = fmaf(tdl, sb[kr], pg);
+        pt = fmaf(dl[jj] * lam, fmaf(sm, e.S[jj], gh * sb[kr]), pt);
       }
+      accg += (double)pg;
+      acct += (double)pt;
     }
     __syncthreads();
     // dQ[q][d] += sum_key dS[q][key] K[key][d]
