@@ -238,14 +238,18 @@ TG_DEVINL void gather(const floatx16& acc, int wv, int lane, const float* sX, El
   }
 }
 
-// log2-domain logits of the 8 elements; -inf where masked.  Tiles wholly
-// below the diagonal and inside the sequence skip the per-element test.
+// log2-domain logits of the 8 elements minus `off` (the row's lse2 where the
+// probabilities follow at once, else 0); -inf where masked.  Tiles wholly
+// below the diagonal and inside the sequence skip the per-element test
+// (lanes where `full` holds for all take no masking branch).
 TG_DEVINL void logits(const Elems& e, float (&l2)[8], int qi, int k0, bool full, float c1, float c2,
-                      const float* sb) {
+                      const float* sb, float off = 0.0f) {
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const float v = fmaf(c1, e.S[jj], c2 * sb[e.kr(jj)]);
-    l2[jj] = (full || k0 + e.kr(jj) <= qi) ? v : -INFINITY;
+  for (int jj = 0; jj < 8; ++jj) l2[jj] = fmaf(c1, e.S[jj], fmaf(c2, sb[e.kr(jj)], -off));
+  if (!full) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (k0 + e.kr(jj) > qi) l2[jj] = -INFINITY;
   }
 }
 
@@ -388,11 +392,12 @@ __global__ __launch_bounds__(256) void bwdm_dsum(const uint16_t* __restrict__ o,
 }
 
 // P and dl = P (dP - D) of this wave's 8 elements
-TG_DEVINL void probs(const Elems& e, const float (&l2)[8], float lse, float D, float (&P)[8],
+// l2 already has the row's lse2 taken off (logits with off = lse2)
+TG_DEVINL void probs(const Elems& e, const float (&l2)[8], float D, float (&P)[8],
                      float (&dl)[8]) {
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    P[jj] = __builtin_amdgcn_exp2f(l2[jj] - lse);     // 0 where masked
+    P[jj] = __builtin_amdgcn_exp2f(l2[jj]);           // 0 where masked
     dl[jj] = P[jj] * (e.dP[jj] - D);
   }
 }
@@ -483,8 +488,8 @@ __global__ __launch_bounds__(kThr) void bwdm_dkdv(
         const float tau = stau[qr];
         float l2[8], P[8], dl[8];
         logits(e, l2, qi < sq.len ? qi : -1, k0, q0 > k0 && qi < sq.len, tau * sm * kLog2e,
-               tau * gh * kLog2e, sb);
-        probs(e, l2, slse[qr], sD[qr], P, dl);
+               tau * gh * kLog2e, sb, slse[qr]);
+        probs(e, l2, sD[qr], P, dl);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int kr = e.kr(jj);
@@ -609,8 +614,8 @@ __global__ __launch_bounds__(kThr) void bwdm_dq(
       Elems e;
       gather(acc, wv, lane, sX, e);
       float l2[8], P[8], dl[8];
-      logits(e, l2, qi < sq.len ? qi : -1, k0, k0 + kB <= q0 && qi < sq.len, c1, c2, sb);
-      probs(e, l2, lse, D, P, dl);
+      logits(e, l2, qi < sq.len ? qi : -1, k0, k0 + kB <= q0 && qi < sq.len, c1, c2, sb, lse);
+      probs(e, l2, D, P, dl);
       // the tile's 8 terms in fp32, then into the fp64 sums
       float pg = 0.0f, pt = 0.0f;
 #pragma unroll
