@@ -2,19 +2,21 @@
 // as the vector-ALU passes: TokenGate §4.2 Eq. 8, with the gain of Eq. 6 and
 // the temperature of Eq. 7; §4.3 names the path into the gate's scores).
 //
-// Three passes over 64 x 64 (query x key) tiles, 8 waves per workgroup, all
-// products on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
-//   bwdm_stats  per (query tile, head): S^T = K.Q^T and dP^T = V.dO^T
-//               (waves 0-3 and 4-7, one 32 x 32 tile each), then the row
-//               log2-sum-exp and D_i = sum_j P_ij dP_ij by an online merge;
-//   bwdm_dkdv   per (key tile, KV head), looping over the group's heads and
-//               the query tiles at or after it: S^T, dP^T as above, then
-//               P^T and dS^T = (tau dl)^T in bf16 in LDS, then
-//               dV += P^T.dO and dK += dS^T.Q (one 32 x 32 tile of each per
-//               wave); the b gradient per KV head from the fp32 dS values;
-//   bwdm_dq     per (query tile, head), looping over key tiles: S^T, dP^T,
-//               dS in bf16, dQ += dS.K; the gain / temperature partial sums
-//               from the fp32 values.
+// Three passes, all products on v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation:
+//   bwdm_stats  per (64-query tile, head), 8 waves: S^T = K.Q^T and
+//               dP^T = V.dO^T (waves 0-3 and 4-7, one 32 x 32 tile each),
+//               then the row log2-sum-exp and D_i = sum_j P_ij dP_ij by an
+//               online merge;
+//   bwdm_kv     per (128-key block, KV head), 4 waves each holding the K and
+//               V rows of 32 keys in registers, looping over the group's
+//               heads and the 64-query tiles at or after the block: S and dP
+//               from the staged Q and dO, P and dS = tau dl in registers
+//               (bf16) as the A operands of dV += P^T.dO and dK += dS^T.Q;
+//               the b gradient per KV head from the fp32 dS values;
+//   bwdm_dq     per (64-query tile, head), 8 waves, looping over key tiles:
+//               S^T, dP^T, dS in bf16, dQ += dS.K; the gain / temperature
+//               partial sums from the fp32 values.
 // The workspace and the final sums (bwd_finish) are shared with the
 // vector-ALU passes.  P and dS enter the dV, dK and dQ products rounded to
 // bf16, as in flash-attention backward passes; the statistics, D, and the
@@ -103,21 +105,34 @@ TG_DEVINL void load_rows(uint16_t* dst, const uint16_t* __restrict__ src, int64_
   }
 }
 
+// Swizzled tile layout for tiles read both row-wise (16-byte reads) and by
+// transposing 8-byte reads: rows of DH + 32 elements (320 B for DH 128,
+// 192 B for DH 64: four consecutive rows start in the four 64-byte quarters
+// of the 256 bytes the LDS serves per cycle, which the transposing reads
+// need), and the 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4),
+// which spreads the 16 rows of a 16-byte read over distinct banks too.
+template <int DH>
+TG_DEVINL constexpr int swz_ld() { return DH + 32; }
+template <int DH>
+TG_DEVINL int swz_off(int row, int chunk) {
+  return row * swz_ld<DH>() + 8 * (chunk ^ ((row >> 2) & 3));
+}
+
 // The same rows fetched into registers one iteration ahead, then stored.
 // Buffer loads: the resource starts at the tile's first row of head hd and
 // ends after the sequence's last row of that head, so rows past `len` read
 // zeros with no per-row test, and each thread's byte offsets within a tile
 // are fixed for the kernel (set once by init).
-template <int DH>
+template <int DH, int NT = kThr>
 struct Pf {
-  static constexpr int N = kB * (DH / 8) / kThr;
+  static constexpr int N = kB * (DH / 8) / NT;
   u32x4 r[N];
   int off[N];
   TG_DEVINL void init(int H) {
     constexpr int CPR = DH / 8;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int u = threadIdx.x + i * kThr, row = u / CPR, c = u % CPR;
+      const int u = threadIdx.x + i * NT, row = u / CPR, c = u % CPR;
       off[i] = (row * H * DH + 8 * c) * 2;
     }
   }
@@ -138,8 +153,17 @@ struct Pf {
     constexpr int CPR = DH / 8, LD = DH + 8;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int u = threadIdx.x + i * kThr, row = u / CPR, c = u % CPR;
+      const int u = threadIdx.x + i * NT, row = u / CPR, c = u % CPR;
       st16(dst + row * LD + 8 * c, r[i]);
+    }
+  }
+  // into the swizzled layout of swz_off
+  TG_DEVINL void store_swz(uint16_t* dst) const {
+    constexpr int CPR = DH / 8;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int u = threadIdx.x + i * NT, row = u / CPR, c = u % CPR;
+      st16(dst + swz_off<DH>(row, c), r[i]);
     }
   }
 };
@@ -402,135 +426,248 @@ TG_DEVINL void probs(const Elems& e, const float (&l2)[8], float D, float (&P)[8
   }
 }
 
-// ---- pass 2: dK, dV and the per-KV-head b gradient, per (key tile, KV head)
+// ---- pass 2: dK, dV and the
+// per-KV-head b gradient, per (block of 128 keys, KV head).  Four waves, one
+// per SIMD; wave w owns keys k0 + 32w .. +32 and holds their K and V rows in
+// registers for the whole pass (the B operands of S = Q.K^T and dP = dO.V^T,
+// keys on the MFMA N axis).  The Q and dO tiles of 64 queries are staged in
+// LDS (two buffers, one barrier per tile) and read twice: row-wise as the A
+// operands of S and dP, and by transposing reads as the B operands of
+// dV += P^T.dO and dK += dS^T.Q.  In the S accumulator lane (n, g) holds key
+// n and queries 8(j/4) + 4g + j%4, so its P and dS values are directly the A
+// operand of those products: K-step kk takes queries 16kk + 8(e/4) + 4g +
+// e%4, and the transposing reads fetch dO and Q rows in that same order.
+// The bias enters S as one more K-step (a selector on the query side, the
+// head's gain * b / s split into two bf16 parts on the key side).
+constexpr int kKB = 128;             // keys per workgroup of this pass
+constexpr int kKvThr = 256;          // 4 waves
+
+TG_DEVINL bool block_of_slot(const int32_t* cu, int n_seq, int64_t t, int64_t slot, int ch,
+                             Seq& sq, int& t0) {
+  const int s = seq_of_slot(cu, n_seq, slot, ch);
+  if (s < 0) return false;
+  sq.lo = cu[s] < t ? cu[s] : t;
+  const int64_t hi = cu[s + 1] < t ? cu[s + 1] : t;
+  sq.len = hi > sq.lo ? (int)(hi - sq.lo) : 0;
+  t0 = (int)(slot - slot0_of(cu, s, ch)) * ch;
+  return t0 < sq.len;
+}
+
+TG_DEVINL uint32_t pack2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int DH>
-__global__ __launch_bounds__(kThr) void bwdm_dkdv(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
-    const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
-    const float* __restrict__ gain, const float* __restrict__ temp, float sm,
-    const float* __restrict__ lse2, const float* __restrict__ dsum, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dbpart, int64_t n_slots) {
-  constexpr int LD = DH + 8, NDT = DH / 32;            // 32-wide d tiles
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
-      sV[kB * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sPT[kB * kLP], sDT[kB * kLP];
-  __shared__ float sX[kB * kLX];
-  __shared__ float stau[kB], slse[kB], sD[kB], sb[kB];
+__global__ __launch_bounds__(kKvThr) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwdm_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+             const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+             const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
+             const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
+             const float* __restrict__ gain, const float* __restrict__ temp, float sm,
+             const float* __restrict__ lse2, const float* __restrict__ dsum,
+             float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbpart,
+             int64_t n_slots) {
+  constexpr int LD = swz_ld<DH>(), KS = DH / 16, NDT = DH / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kB * LD], sO[2][kB * LD];
+  // per query of a staged tile: c = tau s log2(e), lse2 (+inf past the
+  // sequence), D and tau
+  __shared__ __attribute__((aligned(16))) float sC[2][kB], sL[2][kB], sD[2][kB], sT[2][kB];
   Seq sq;
   int k0;
   int64_t slot;
   int kvh, hh0;
   work_item(blockIdx.x, hkv, 1, n_slots, false, slot, kvh, hh0);
-  if (!tile_of_slot(cu, n_seq, t, slot, sq, k0)) return;
+  if (!block_of_slot(cu, n_seq, t, slot, kKB, sq, k0)) return;
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, w4 = wv & 3, qt = w4 >> 1;
-  const int ct = wv & 1, dt = wv >> 1;                  // phase C tile: keys 32ct, d 32dt
-  load_rows<DH>(sK, k, sq.lo, sq.len, k0, hkv, kvh);
-  load_rows<DH>(sV, v, sq.lo, sq.len, k0, hkv, kvh);
-  if (tid < kB) sb[tid] = k0 + tid < sq.len ? kept_b[sq.lo + k0 + tid] : 0.0f;
-  floatx16 aV, aK;
+  const int n = lane & 31, g = lane >> 5;
+  const int kw0 = k0 + 32 * wv;                       // the wave's first key
+  const int len = sq.len;
+
+  // K and V rows of key kw0 + n (B operands: dims 16s + 8g .. +8), zeros past the end
+  u32x4 kf[KS], vf[KS];
+  float bk = 0.0f;
+  {
+    const bool ok = kw0 + n < len;
+    const int64_t row = ((sq.lo + (ok ? kw0 + n : 0)) * hkv + kvh) * (int64_t)DH + 8 * g;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    aV[j] = 0.0f;
-    aK[j] = 0.0f;
-  }
-  float dbacc = 0.0f;
-  // iterations (head hh, query tile q0), query tiles from the last one down
-  // to the diagonal, so that the workgroups of one head group that run
-  // together read the same Q and dO tiles at about the same time; the next
-  // iteration's Q, dO and row scalars are fetched while the current one is
-  // computed
-  const int qfirst = (k0 / kB) * kB;
-  const int qlast = ((sq.len - 1) / kB) * kB;
-  Pf<DH> pq, po;
-  pq.init(hq);
-  po.init(hq);
-  float ptau = 0.0f, plse = 0.0f, pD = 0.0f;
-  auto fetch = [&](int hh, int q0) {
-    const int h = kvh * G + hh;
-    pq.load(q, sq.lo, sq.len, q0, hq, h);
-    po.load(dout, sq.lo, sq.len, q0, hq, h);
-    if (tid < kB) {
-      const int i = q0 + tid;
-      const bool ok = i < sq.len;
-      ptau = ok ? temp[h] * length_lambda(kept_pos, sq.lo + i, i) : 0.0f;
-      plse = ok ? lse2[(int64_t)h * t + sq.lo + i] : 0.0f;
-      pD = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = ok ? ld16(k + row + 16 * s) : (u32x4){0u, 0u, 0u, 0u};
+      vf[s] = ok ? ld16(v + row + 16 * s) : (u32x4){0u, 0u, 0u, 0u};
     }
-  };
-  fetch(0, qlast);
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = kvh * G + hh;
-    const float gh = gain[h];
-    for (int q0 = qlast; q0 >= qfirst; q0 -= kB) {
-      __syncthreads();
-      pq.store(sQ);
-      po.store(sO);
-      if (tid < kB) {
-        stau[tid] = ptau;
-        slse[tid] = plse;
-        sD[tid] = pD;
-      }
-      if (q0 - kB >= qfirst) fetch(hh, q0 - kB);
-      else if (hh + 1 < G) fetch(hh + 1, qlast);
-      __syncthreads();
-      floatx16 acc;
-      phase_a<DH>(acc, wv, lane, sK, sV, sQ, sO, sX);
-      __syncthreads();
-      {
-        const int qr = 32 * qt + n, qi = q0 + qr;
-        Elems e;
-        gather(acc, wv, lane, sX, e);
-        const float tau = stau[qr];
-        float l2[8], P[8], dl[8];
-        logits(e, l2, qi < sq.len ? qi : -1, k0, q0 > k0 && qi < sq.len, tau * sm * kLog2e,
-               tau * gh * kLog2e, sb, slse[qr]);
-        probs(e, l2, sD[qr], P, dl);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int kr = e.kr(jj);
-          const float ds = dl[jj] * tau;
-          sPT[kr * kLP + qr] = f2bf(P[jj]);
-          sDT[kr * kLP + qr] = f2bf(ds);
-          sX[kr * kLX + qr] = ds;                      // fp32, for the b gradient
-        }
-      }
-      __syncthreads();
-      if (dt < NDT) {
-        // dV[key][d] += sum_q P^T[key][q] dO[q][d];  dK[key][d] += sum_q dS^T[key][q] Q[q][d]
-        mma_ab_rows<kB / 16>(aV, sPT + 32 * ct * kLP, kLP, sO + 32 * dt, LD, lane);
-        mma_ab_rows<kB / 16>(aK, sDT + 32 * ct * kLP, kLP, sQ + 32 * dt, LD, lane);
-      }
-      {                                                 // db_j += g_h sum_q tau_q dl_qj
-        const int key = tid >> 3, part = tid & 7;       // 8 threads per key, 8 queries each
-        float cs = 0.0f;
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) cs += sX[key * kLX + 8 * part + qq];
-        cs += __shfl_xor(cs, 1, 64);
-        cs += __shfl_xor(cs, 2, 64);
-        cs += __shfl_xor(cs, 4, 64);
-        dbacc = fmaf(gh, cs, dbacc);                    // every thread of the key holds it
-      }
-    }
+    if (ok) bk = kept_b[sq.lo + kw0 + n];
   }
-  if (dt < NDT) {
-    const int g = lane >> 5;
+  // selector of the bias K-step: query-side columns 0 and 1 (lane half 0)
+  const u32x4 sel = g == 0 ? (u32x4){pack2(1.0f, 1.0f), 0u, 0u, 0u} : (u32x4){0u, 0u, 0u, 0u};
+
+  floatx16 aV[NDT], aK[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int key = k0 + 32 * ct + crow(j, g);
-      if (key < sq.len) {
-        const int64_t off = ((sq.lo + key) * hkv + kvh) * (int64_t)DH + 32 * dt + n;
-        dv[off] = aV[j];
-        dk[off] = sm * aK[j];
+      aV[d][j] = 0.0f;
+      aK[d][j] = 0.0f;
+    }
+  float dbacc = 0.0f;
+
+  // tiles (head hh, query tile q0): per head, from the last query tile down
+  // to the one holding the block's first key; the next tile's rows and
+  // per-query values are fetched while the current one is computed
+  const int qfirst = (k0 / kB) * kB;
+  const int qlast = ((len - 1) / kB) * kB;
+  const int nq = (qlast - qfirst) / kB + 1;
+  const int total = G * nq;
+  Pf<DH, kKvThr> pq, po;
+  pq.init(hq);
+  po.init(hq);
+  float pc = 0.0f, pl = 0.0f, pd = 0.0f, pt = 0.0f;
+  auto fetch = [&](int it) {
+    const int hh = it / nq, q0 = qlast - (it % nq) * kB;
+    const int h = kvh * G + hh;
+    pq.load(q, sq.lo, len, q0, hq, h);
+    po.load(dout, sq.lo, len, q0, hq, h);
+    if (tid < kB) {
+      const int i = q0 + tid;
+      const bool ok = i < len;
+      const float tau = ok ? temp[h] * length_lambda(kept_pos, sq.lo + i, i) : 0.0f;
+      pc = tau * sm * kLog2e;
+      pt = tau;
+      pl = ok ? lse2[(int64_t)h * t + sq.lo + i] : INFINITY;
+      pd = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
+    }
+  };
+  auto stash = [&](int buf) {
+    pq.store_swz(sQ[buf]);
+    po.store_swz(sO[buf]);
+    if (tid < kB) {
+      sC[buf][tid] = pc;
+      sL[buf][tid] = pl;
+      sD[buf][tid] = pd;
+      sT[buf][tid] = pt;
+    }
+  };
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const floatx16 zero = {};
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < total) fetch(it + 1);
+    const int hh = it / nq, q0 = qlast - (it % nq) * kB;
+    const int h = kvh * G + hh;
+    const float gh = gain[h];
+    // bias operand of this head: gain * b / s as a high and a low bf16 part
+    const float beta = gh * bk / sm;
+    const float bhi = (float)(__bf16)beta;
+    const u32x4 bop = g == 0 ? (u32x4){pack2(bhi, beta - bhi), 0u, 0u, 0u} : (u32x4){0u, 0u, 0u, 0u};
+    const uint16_t* qt = sQ[buf];
+    const uint16_t* ot = sO[buf];
+    float dsl = 0.0f;                                 // sum of this lane's dS values
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int qb = q0 + 32 * qh;                    // first query of the half
+      if (kw0 > qb + 31) continue;                    // every key after every query
+      // S' = Q.K^T + bias and dP = dO.V^T for 32 queries x the wave's 32 keys;
+      // A operands: row 32qh + n, chunk 2s + g, stored at chunk (2s + g) ^ fr
+      // with fr = (n / 4) % 4, i.e. 4(s/2) + ((2(s%2)) ^ g ^ fr)
+      floatx16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sel), as_bf16x8(bop),
+                                                              zero, 0, 0, 0);
+      floatx16 pacc = zero;
+      {
+        const int v = g ^ ((n >> 2) & 3);
+        const int row = (32 * qh + n) * LD;
+        const int e0 = row + 8 * v, e1 = row + 8 * (v ^ 2);
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const int o = ((st & 1) ? e1 : e0) + 32 * (st >> 1);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + o)), as_bf16x8(kf[st]),
+                                                         sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ot + o)), as_bf16x8(vf[st]),
+                                                         pacc, 0, 0, 0);
+        }
+      }
+      // element j: query qb + 8(j/4) + 4g + j%4, key kw0 + n; keys after the
+      // query are masked (only halves that reach past the diagonal test)
+      uint32_t pw[8], dw[8];
+      auto elementwise = [&](auto MASKC) {
+        constexpr bool MASK = decltype(MASKC)::value;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi = 32 * qh + 8 * r4 + 4 * g;    // query of j = 4 r4, in the tile
+          const float4 c4 = *reinterpret_cast<const float4*>(&sC[buf][qi]);
+          const float4 l4 = *reinterpret_cast<const float4*>(&sL[buf][qi]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&sD[buf][qi]);
+          const float4 t4 = *reinterpret_cast<const float4*>(&sT[buf][qi]);
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ll[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w}, tt[4] = {t4.x, t4.y, t4.z, t4.w};
+          float P[4], S[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * r4 + e;
+            float l2 = fmaf(cc[e], sacc[j], -ll[e]);
+            if (MASK && kw0 + n > q0 + qi + e) l2 = -INFINITY;
+            P[e] = __builtin_amdgcn_exp2f(l2);
+            S[e] = P[e] * (pacc[j] - dd[e]) * tt[e];
+            dsl += S[e];
+          }
+          pw[2 * r4] = pack2(P[0], P[1]);
+          pw[2 * r4 + 1] = pack2(P[2], P[3]);
+          dw[2 * r4] = pack2(S[0], S[1]);
+          dw[2 * r4 + 1] = pack2(S[2], S[3]);
+        }
+      };
+      if (kw0 + 31 > qb) elementwise(std::true_type{});
+      else elementwise(std::false_type{});
+      // dV += P^T.dO and dK += dS^T.Q over the half's queries: K-step kk is
+      // registers j = 8kk .. +8 (words 4kk .. +4); B rows 16kk + 4g + 0..3 and
+      // 16kk + 8 + 4g + 0..3 of dim 32d + n, by two transposing reads each.
+      // Lane (16-lane group h, i = lane % 16) points at row R + i/4 (R =
+      // 32qh + 16kk + 4g, so (row / 4) % 4 = g, and g ^ 2 eight rows on),
+      // logical chunk 4d + 2h + (i%4)/2, element 4((i%4)%2) within it.
+      {
+        const int h2 = (lane >> 4) & 1, c = lane & 3;
+        const int lrow = 4 * g + ((lane & 15) >> 2);
+        const int t0 = lrow * LD + 8 * ((2 * h2 + (c >> 1)) ^ g) + 4 * (c & 1);
+        const int t1 = (lrow + 8) * LD + 8 * ((2 * h2 + (c >> 1)) ^ g ^ 2) + 4 * (c & 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 pa = as_bf16x8((u32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
+          const bf16x8 da = as_bf16x8((u32x4){dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]});
+          const int rk = (32 * qh + 16 * kk) * LD;
+#pragma unroll
+          for (int d = 0; d < NDT; ++d) {
+            const uint2 o0 = ld_tr4(ot + rk + t0 + 32 * d), o1 = ld_tr4(ot + rk + t1 + 32 * d);
+            const uint2 q0v = ld_tr4(qt + rk + t0 + 32 * d), q1v = ld_tr4(qt + rk + t1 + 32 * d);
+            aV[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                pa, as_bf16x8((u32x4){o0.x, o0.y, o1.x, o1.y}), aV[d], 0, 0, 0);
+            aK[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                da, as_bf16x8((u32x4){q0v.x, q0v.y, q1v.x, q1v.y}), aK[d], 0, 0, 0);
+          }
+        }
       }
     }
+    dbacc = fmaf(gh, dsl, dbacc);
+    if (it + 1 < total) stash(buf ^ 1);
+    __syncthreads();
   }
-  if ((tid & 7) == 0 && k0 + (tid >> 3) < sq.len)
-    dbpart[(int64_t)kvh * t + sq.lo + k0 + (tid >> 3)] = dbacc;
+  // dV, dK rows: register j of lane (n, g) is key kw0 + 8(j/4) + 4g + j%4, dim 32d + n
+#pragma unroll
+  for (int d = 0; d < NDT; ++d)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = kw0 + crow(j, g);
+      if (key < len) {
+        const int64_t off = ((sq.lo + key) * hkv + kvh) * (int64_t)DH + 32 * d + n;
+        dv[off] = aV[d][j];
+        dk[off] = sm * aK[d][j];
+      }
+    }
+  // the b gradient of key kw0 + n: the two lane halves hold its two query halves
+  dbacc += __shfl_xor(dbacc, 32, 64);
+  if (g == 0 && kw0 + n < len) dbpart[(int64_t)kvh * t + sq.lo + kw0 + n] = dbacc;
 }
 
 // ---- pass 3: dQ and the gain / temperature partials, per (query tile, head)
@@ -670,6 +807,7 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 double* gpart, const void* fwd_out, const float* fwd_lse2,
                                 hipStream_t st) {
   const int64_t nq = n_seq + (t + kB - 1) / kB;
+  const int64_t nkb = n_seq + (t + kKB - 1) / kKB;     // key blocks of the dK/dV pass
   const bool saved = fwd_out != nullptr && fwd_lse2 != nullptr;
   const float* lse = saved ? fwd_lse2 : lse2;
   const int64_t dsum_blocks = (t * hq * (dh / 8) + 255) / 256;
@@ -685,9 +823,9 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, \
                        vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2,    \
                        dsum, nq);                                                                \
-  hipLaunchKernelGGL((bwdm_dkdv<DHv>), dim3((unsigned)(nq * hkv)), dim3(kThr), 0, st, qp, kp, vp, \
-                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum,     \
-                     dk, dv, dbpart, nq);                                                        \
+  hipLaunchKernelGGL((bwdm_kv<DHv>), dim3((unsigned)(nkb * hkv)), dim3(kKvThr), 0, st, qp, kp,   \
+                     vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, \
+                     dk, dv, dbpart, nkb);                                                       \
   hipLaunchKernelGGL((bwdm_dq<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, vp,  \
                      op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, dq, \
                      gpart, nq);
