@@ -485,7 +485,8 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* dou
                                               dbpart, gpart, fwd_out, fwd_lse2, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_finish, dim3((unsigned)((t + kThr - 1) / kThr + 1)), dim3(kThr), 0, st,
-                       dbpart, gpart, cu, n_seq, t, hq, hkv, nq, db, dgain, dtemp);
+                       dbpart, gpart, cu, n_seq, t, hq, hkv, attn_bwd_mfma_gslots(t, n_seq), db,
+                       dgain, dtemp);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((bwd_stats<DH, T>), dim3((unsigned)nq, hq), dim3(kThr), 0, st, qp, kp, vp,

@@ -39,7 +39,6 @@ typedef float floatx8 __attribute__((ext_vector_type(8)));
 constexpr int kB = 64;               // queries and keys per tile
 constexpr int kThr = 512;            // 8 waves
 constexpr int kLX = kB + 1;          // fp32 exchange tile stride
-constexpr int kLP = kB + 8;          // bf16 P^T / dS tile stride
 constexpr float kLog2e = 1.4426950408889634f;
 
 TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -69,23 +68,6 @@ TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(
       uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p)));
-}
-
-// acc[32 x 32] += A[32 rows][K] . B[K][32 cols]; A k-contiguous, B row-major
-// (its 32 columns contiguous) in LDS, 8-byte aligned rows: the B operand of
-// lane (n, kg), rows 16s + 8kg .. +8 of column n, is two transposing reads
-template <int KSTEPS>
-TG_DEVINL void mma_ab_rows(floatx16& acc, const uint16_t* A, int lda, const uint16_t* B, int ldb,
-                           int lane) {
-  const int r = lane & 31, kg = lane >> 5;
-  const uint16_t* bp = B + (8 * kg + ((lane & 15) >> 2)) * ldb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const bf16x8 a = as_bf16x8(ld16(A + r * lda + 16 * s + 8 * kg));
-    const uint2 lo = ld_tr4(bp + 16 * s * ldb), hi = ld_tr4(bp + (16 * s + 4) * ldb);
-    const bf16x8 b = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-  }
 }
 
 // C layout of a 32 x 32 tile: register j of lane (n, g) is row 8(j/4) + 4g + j%4, column n
@@ -416,15 +398,6 @@ __global__ __launch_bounds__(256) void bwdm_dsum(const uint16_t* __restrict__ o,
 }
 
 // P and dl = P (dP - D) of this wave's 8 elements
-// l2 already has the row's lse2 taken off (logits with off = lse2)
-TG_DEVINL void probs(const Elems& e, const float (&l2)[8], float D, float (&P)[8],
-                     float (&dl)[8]) {
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    P[jj] = __builtin_amdgcn_exp2f(l2[jj]);           // 0 where masked
-    dl[jj] = P[jj] * (e.dP[jj] - D);
-  }
-}
 
 // ---- pass 2: dK, dV and the
 // per-KV-head b gradient, per (block of 128 keys, KV head).  Four waves, one
@@ -670,134 +643,218 @@ void bwdm_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   if (g == 0 && kw0 + n < len) dbpart[(int64_t)kvh * t + sq.lo + kw0 + n] = dbacc;
 }
 
-// ---- pass 3: dQ and the gain / temperature partials, per (query tile, head)
+// ---- pass 3: dQ and the gain / temperature partials, per (block of 128
+// queries, head).  Four waves, one per SIMD; wave w owns queries q0 + 32w ..
+// +32 and holds their Q and dO rows in registers (the B operands of
+// S^T = K.Q^T and dP^T = V.dO^T, queries on the MFMA N axis), looping over
+// the 64-key tiles up to the block's diagonal.  K and V tiles are staged in
+// LDS (two buffers, one barrier per tile; K in the swizzled layout, as it is
+// also read by transposing reads), with each key's bias A operand (the
+// head's gain * b / s as two bf16 parts) beside them.  In the S^T
+// accumulator lane (n, g) holds query n and keys 8(j/4) + 4g + j%4, so its
+// dS values are directly the A operand of dQ += dS.K (keys in runs of four,
+// matched by transposing reads of K); the query's lse2, D, tau and lambda
+// are per-lane scalars.
+constexpr int kQB = 128;             // queries per workgroup of this pass
+
 template <int DH>
-__global__ __launch_bounds__(kThr) void bwdm_dq(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
-    const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
-    const float* __restrict__ gain, const float* __restrict__ temp, float sm,
-    const float* __restrict__ lse2, const float* __restrict__ dsum, float* __restrict__ dq,
-    double* __restrict__ gpart, int64_t n_slots) {
-  constexpr int LD = DH + 8, NDT = DH / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
-      sV[kB * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[kB * kLP];
-  __shared__ float sX[kB * kLX];
-  __shared__ float stau[kB], slam[kB], slse[kB], sD[kB], sb[kB];
-  __shared__ double sred[2][kThr / 64];
+__global__ __launch_bounds__(kKvThr) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+            const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+            const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
+            const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
+            const float* __restrict__ gain, const float* __restrict__ temp, float sm,
+            const float* __restrict__ lse2, const float* __restrict__ dsum,
+            float* __restrict__ dq, double* __restrict__ gpart, int64_t n_slots) {
+  constexpr int LD = swz_ld<DH>(), KS = DH / 16, NDT = DH / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kB * LD], sV[2][kB * LD];
+  __shared__ __attribute__((aligned(16))) uint32_t sBias[2][kB];   // (hi, lo) bf16 pair per key
+  __shared__ __attribute__((aligned(16))) float sb[2][kB];         // b per key
+  __shared__ double sred[2][kKvThr / 64];
   int64_t slot;
   int kvh, hh;
   work_item(blockIdx.x, hkv, hq / hkv, n_slots, true, slot, kvh, hh);
   const int h = kvh * (hq / hkv) + hh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, w4 = wv & 3, qt = w4 >> 1;
-  const int ct = wv & 1, dt = wv >> 1;                  // phase C: queries 32ct, d 32dt
+  const int n = lane & 31, g = lane >> 5;
   double* gp = gpart + (slot * hq + h) * 2;
   Seq sq;
   int q0;
-  if (!tile_of_slot(cu, n_seq, t, slot, sq, q0)) {
+  if (!block_of_slot(cu, n_seq, t, slot, kQB, sq, q0)) {
     if (tid == 0) {                                    // every slot leaves a partial
       gp[0] = 0.0;
       gp[1] = 0.0;
     }
     return;
   }
+  const int len = sq.len;
+  const int qw0 = q0 + 32 * wv;                       // the wave's first query
+  const int qi = qw0 + n;                             // this lane's query
+  const bool qok = qi < len;
   const float gh = gain[h];
-  if (tid < kB) {
-    const int i = q0 + tid;
-    const bool ok = i < sq.len;
-    const float lam = ok ? length_lambda(kept_pos, sq.lo + i, i) : 0.0f;
-    slam[tid] = lam;
-    stau[tid] = temp[h] * lam;
-    slse[tid] = ok ? lse2[(int64_t)h * t + sq.lo + i] : 0.0f;
-    sD[tid] = ok ? dsum[(sq.lo + i) * hq + h] : 0.0f;
+  // per-lane query values; past the sequence: nothing (lse2 +inf, c 0)
+  float c = 0.0f, lse = INFINITY, D = 0.0f, tau = 0.0f, lam = 0.0f;
+  if (qok) {
+    lam = length_lambda(kept_pos, sq.lo + qi, qi);
+    tau = temp[h] * lam;
+    c = tau * sm * kLog2e;
+    lse = lse2[(int64_t)h * t + sq.lo + qi];
+    D = dsum[(sq.lo + qi) * hq + h];
   }
-  load_rows<DH>(sQ, q, sq.lo, sq.len, q0, hq, h);
-  load_rows<DH>(sO, dout, sq.lo, sq.len, q0, hq, h);
-  floatx16 aQ;
+  // Q and dO rows of query qi (B operands: dims 16s + 8g .. +8)
+  u32x4 qf[KS], of[KS];
+  {
+    const int64_t row = ((sq.lo + (qok ? qi : 0)) * hq + h) * (int64_t)DH + 8 * g;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) aQ[j] = 0.0f;
-  double accg = 0.0, acct = 0.0;
-  const int q_end = q0 + kB < sq.len ? q0 + kB : sq.len;
-  Pf<DH> pk, pv;                                      // key tile k0 + 64, in flight
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = qok ? ld16(q + row + 16 * s) : (u32x4){0u, 0u, 0u, 0u};
+      of[s] = qok ? ld16(dout + row + 16 * s) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+  const u32x4 sel = g == 0 ? (u32x4){pack2(1.0f, 1.0f), 0u, 0u, 0u} : (u32x4){0u, 0u, 0u, 0u};
+
+  floatx16 aQ[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) aQ[d][j] = 0.0f;
+  double dg = 0.0, dt = 0.0;                          // fp64 sums of the per-tile fp32 sums
+
+  const int q_end = q0 + kQB < len ? q0 + kQB : len;
+  const int n_tiles = (q_end + kB - 1) / kB;          // key tiles up to the block's diagonal
+  Pf<DH, kKvThr> pk, pv;
   pk.init(hkv);
   pv.init(hkv);
   float pb = 0.0f;
-  pk.load(k, sq.lo, sq.len, 0, hkv, kvh);
-  pv.load(v, sq.lo, sq.len, 0, hkv, kvh);
-  if (tid < kB) pb = tid < sq.len ? kept_b[sq.lo + tid] : 0.0f;
+  auto fetch = [&](int kt) {
+    pk.load(k, sq.lo, len, kt * kB, hkv, kvh);
+    pv.load(v, sq.lo, len, kt * kB, hkv, kvh);
+    if (tid < kB) pb = kt * kB + tid < len ? kept_b[sq.lo + kt * kB + tid] : 0.0f;
+  };
+  auto stash = [&](int buf) {
+    pk.store_swz(sK[buf]);
+    pv.store_swz(sV[buf]);
+    if (tid < kB) {
+      const float beta = gh * pb / sm;
+      const float bhi = (float)(__bf16)beta;
+      sBias[buf][tid] = pack2(bhi, beta - bhi);
+      sb[buf][tid] = pb;
+    }
+  };
+  fetch(0);
+  stash(0);
   __syncthreads();
-  const int qr = 32 * qt + n, qi = q0 + qr;
-  const float tau = stau[qr], lam = slam[qr], lse = slse[qr], D = sD[qr];
-  const float c1 = tau * sm * kLog2e, c2 = tau * gh * kLog2e;
-  for (int k0 = 0; k0 < q_end; k0 += kB) {
-    __syncthreads();
-    pk.store(sK);
-    pv.store(sV);
-    if (tid < kB) sb[tid] = pb;
-    if (k0 + kB < q_end) {
-      pk.load(k, sq.lo, sq.len, k0 + kB, hkv, kvh);
-      pv.load(v, sq.lo, sq.len, k0 + kB, hkv, kvh);
-      if (tid < kB) pb = k0 + kB + tid < sq.len ? kept_b[sq.lo + k0 + kB + tid] : 0.0f;
-    }
-    __syncthreads();
-    floatx16 acc;
-    phase_a<DH>(acc, wv, lane, sK, sV, sQ, sO, sX);
-    __syncthreads();
-    {
-      Elems e;
-      gather(acc, wv, lane, sX, e);
-      float l2[8], P[8], dl[8];
-      logits(e, l2, qi < sq.len ? qi : -1, k0, k0 + kB <= q0 && qi < sq.len, c1, c2, sb, lse);
-      probs(e, l2, D, P, dl);
-      // the tile's 8 terms in fp32, then into the fp64 sums
-      float pg = 0.0f, pt = 0.0f;
+  const floatx16 zero = {};
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_tiles) fetch(kt + 1);
+    const int k0 = kt * kB;
+    const uint16_t* kt_ = sK[buf];
+    const uint16_t* vt_ = sV[buf];
+    float pg = 0.0f, pt = 0.0f;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int kr = e.kr(jj);
-        const float tdl = dl[jj] * tau;
-        sDS[qr * kLP + kr] = f2bf(tdl);
-        pg = fmaf(tdl, sb[kr], pg);
-        pt = fmaf(dl[jj] * lam, fmaf(sm, e.S[jj], gh * sb[kr]), pt);
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kb0 = k0 + 32 * kh;                   // first key of the half
+      if (kb0 > qw0 + 31) continue;                   // every key after every query
+      // S^T' = K.Q^T + bias and dP^T = V.dO^T for 32 keys x the wave's 32
+      // queries; A operands: key row 32kh + n, chunk 2s + g (swizzled)
+      const u32x4 bia = g == 0 ? (u32x4){sBias[buf][32 * kh + n], 0u, 0u, 0u}
+                               : (u32x4){0u, 0u, 0u, 0u};
+      floatx16 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bia), as_bf16x8(sel),
+                                                              zero, 0, 0, 0);
+      floatx16 pacc = zero;
+      {
+        const int vv = g ^ ((n >> 2) & 3);
+        const int row = (32 * kh + n) * LD;
+        const int e0 = row + 8 * vv, e1 = row + 8 * (vv ^ 2);
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const int o = ((st & 1) ? e1 : e0) + 32 * (st >> 1);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kt_ + o)), as_bf16x8(qf[st]),
+                                                         sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(vt_ + o)), as_bf16x8(of[st]),
+                                                         pacc, 0, 0, 0);
+        }
       }
-      accg += (double)pg;
-      acct += (double)pt;
+      // element j: key kb0 + 8(j/4) + 4g + j%4, query qi
+      uint32_t dw[8];
+      auto elementwise = [&](auto MASKC) {
+        constexpr bool MASK = decltype(MASKC)::value;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int kl = 32 * kh + 8 * r4 + 4 * g;    // key of j = 4 r4, in the tile
+          const float4 b4 = *reinterpret_cast<const float4*>(&sb[buf][kl]);
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+          float S[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * r4 + e;
+            float l2 = fmaf(c, sacc[j], -lse);
+            if (MASK && k0 + kl + e > qi) l2 = -INFINITY;
+            const float P = __builtin_amdgcn_exp2f(l2);
+            const float dl = P * (pacc[j] - D);
+            S[e] = dl * tau;
+            pg = fmaf(S[e], bb[e], pg);
+            pt = fmaf(dl, sacc[j], pt);
+          }
+          dw[2 * r4] = pack2(S[0], S[1]);
+          dw[2 * r4 + 1] = pack2(S[2], S[3]);
+        }
+      };
+      if (kb0 + 31 > qw0) elementwise(std::true_type{});
+      else elementwise(std::false_type{});
+      // dQ += dS.K over the half's keys: K-step kk is registers j = 8kk .. +8;
+      // B rows 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3 of dim 32d + n of
+      // the K tile, by two transposing reads each (swizzled as in bwdm_kv)
+      {
+        const int h2 = (lane >> 4) & 1, cc = lane & 3;
+        const int lrow = 4 * g + ((lane & 15) >> 2);
+        const int t0 = lrow * LD + 8 * ((2 * h2 + (cc >> 1)) ^ g) + 4 * (cc & 1);
+        const int t1 = (lrow + 8) * LD + 8 * ((2 * h2 + (cc >> 1)) ^ g ^ 2) + 4 * (cc & 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 da = as_bf16x8((u32x4){dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]});
+          const int rk = (32 * kh + 16 * kk) * LD;
+#pragma unroll
+          for (int d = 0; d < NDT; ++d) {
+            const uint2 k0v = ld_tr4(kt_ + rk + t0 + 32 * d), k1v = ld_tr4(kt_ + rk + t1 + 32 * d);
+            aQ[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                da, as_bf16x8((u32x4){k0v.x, k0v.y, k1v.x, k1v.y}), aQ[d], 0, 0, 0);
+          }
+        }
+      }
     }
+    dg += (double)pg;
+    dt += (double)pt;
+    if (kt + 1 < n_tiles) stash(buf ^ 1);
     __syncthreads();
-    // dQ[q][d] += sum_key dS[q][key] K[key][d]
-    if (dt < NDT) mma_ab_rows<kB / 16>(aQ, sDS + 32 * ct * kLP, kLP, sK + 32 * dt, LD, lane);
   }
-  if (dt < NDT) {
-    const int g = lane >> 5;
+  // dQ rows: register j of lane (n, g) is query qw0 + 8(j/4) + 4g + j%4, dim 32d + n
+#pragma unroll
+  for (int d = 0; d < NDT; ++d)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int i = q0 + 32 * ct + crow(j, g);
-      if (i < sq.len) dq[((sq.lo + i) * hq + h) * (int64_t)DH + 32 * dt + n] = sm * aQ[j];
+      const int i = qw0 + crow(j, g);
+      if (i < len) dq[((sq.lo + i) * hq + h) * (int64_t)DH + 32 * d + n] = sm * aQ[d][j];
     }
-  }
-  accg = wave_sum(accg);
-  acct = wave_sum(acct);
+  // dgain = sum tau b dl; dtemp = sum lambda z dl with z = s S' (S' = q.k + gain b / s)
+  dg = wave_sum(dg);
+  dt = wave_sum(dt * (double)(lam * sm));
   if (lane == 0) {
-    sred[0][wv] = accg;
-    sred[1][wv] = acct;
+    sred[0][wv] = dg;
+    sred[1][wv] = dt;
   }
   __syncthreads();
   if (tid == 0) {
-    double a = 0.0, b = 0.0;
-#pragma unroll
-    for (int w = 0; w < kThr / 64; ++w) {
-      a += sred[0][w];
-      b += sred[1][w];
-    }
-    gp[0] = a;
-    gp[1] = b;
+    gp[0] = (sred[0][0] + sred[0][1]) + (sred[0][2] + sred[0][3]);
+    gp[1] = (sred[1][0] + sred[1][1]) + (sred[1][2] + sred[1][3]);
   }
 }
 
 }  // namespace
+
+int64_t attn_bwd_mfma_gslots(int64_t t, int n_seq) { return n_seq + (t + kQB - 1) / kQB; }
 
 hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
                                 int64_t t, const float* kept_b, const int32_t* kept_pos,
@@ -808,6 +865,7 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 hipStream_t st) {
   const int64_t nq = n_seq + (t + kB - 1) / kB;
   const int64_t nkb = n_seq + (t + kKB - 1) / kKB;     // key blocks of the dK/dV pass
+  const int64_t nqb = attn_bwd_mfma_gslots(t, n_seq);   // query blocks of the dQ pass
   const bool saved = fwd_out != nullptr && fwd_lse2 != nullptr;
   const float* lse = saved ? fwd_lse2 : lse2;
   const int64_t dsum_blocks = (t * hq * (dh / 8) + 255) / 256;
@@ -826,9 +884,9 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
   hipLaunchKernelGGL((bwdm_kv<DHv>), dim3((unsigned)(nkb * hkv)), dim3(kKvThr), 0, st, qp, kp,   \
                      vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, \
                      dk, dv, dbpart, nkb);                                                       \
-  hipLaunchKernelGGL((bwdm_dq<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, vp,  \
-                     op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, dq, \
-                     gpart, nq);
+  hipLaunchKernelGGL((bwdm_q<DHv>), dim3((unsigned)(nqb * hq)), dim3(kKvThr), 0, st, qp, kp,    \
+                     vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, \
+                     dq, gpart, nqb);
   if (dh == 128) {
     TG_BWDM(128)
   } else if (dh == 64) {

@@ -211,6 +211,9 @@ hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d,
                             float* db2, void* ws, hipStream_t st);
 
 size_t attn_bwd_ws_bytes(int64_t t, int n_seq, int hq, int hkv);
+// slots of the gain / temperature partials the matrix-core dQ pass writes
+// (one per block of its queries; no more than the vector-ALU passes' slots)
+int64_t attn_bwd_mfma_gslots(int64_t t, int n_seq);
 // fwd_out and fwd_lse2 (both or neither; bf16 only): the forward's output
 // and row statistics.  With them D = rowsum(dO . O) replaces the statistics
 // pass and fwd_lse2 is used as the rows' log2-sum-exp.
