@@ -2,31 +2,32 @@
 // as the vector-ALU passes: TokenGate §4.2 Eq. 8, with the gain of Eq. 6 and
 // the temperature of Eq. 7; §4.3 names the path into the gate's scores).
 //
-// Three passes, all products on v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation:
-//   bwdm_stats  per (64-query tile, head), 8 waves: S^T = K.Q^T and
-//               dP^T = V.dO^T (waves 0-3 and 4-7, one 32 x 32 tile each),
-//               then the row log2-sum-exp and D_i = sum_j P_ij dP_ij by an
-//               online merge;
-//   bwdm_kv     per (128-key block, KV head), 4 waves each holding the K and
-//               V rows of 32 keys in registers, looping over the group's
-//               heads and the 64-query tiles at or after the block: S and dP
-//               from the staged Q and dO, P and dS = tau dl in registers
-//               (bf16) as the A operands of dV += P^T.dO and dK += dS^T.Q;
-//               the b gradient per KV head from the fp32 dS values;
-//   bwdm_dq     per (64-query tile, head), 8 waves, looping over key tiles:
-//               S^T, dP^T, dS in bf16, dQ += dS.K; the gain / temperature
-//               partial sums from the fp32 values.
+// Passes, all products on v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+// four waves per workgroup (one per SIMD) holding their own rows' operands
+// in registers:
+//   bwdm_dsum   (with the forward's output and lse2) D_i = dO_i . O_i;
+//   bwdm_q<STATS> (without them) the row log2-sum-exp and D_i by an online
+//               merge, per (128-query block, head);
+//   bwdm_kv     per (128-key block, KV head), waves holding the K and V rows
+//               of 32 keys, looping over the group's heads and the 64-query
+//               tiles at or after the block: S and dP from the staged Q and
+//               dO, P and dS = tau dl in registers (bf16) as the A operands
+//               of dV += P^T.dO and dK += dS^T.Q; the b gradient per KV head
+//               from the fp32 dS values;
+//   bwdm_q      per (128-query block, head), waves holding the Q and dO rows
+//               of 32 queries, looping over the 64-key tiles up to the
+//               diagonal: S^T, dP^T, dS in bf16 as the A operand of
+//               dQ += dS.K; the gain / temperature partial sums from the
+//               fp32 values.
 // The workspace and the final sums (bwd_finish) are shared with the
 // vector-ALU passes.  P and dS enter the dV, dK and dQ products rounded to
 // bf16, as in flash-attention backward passes; the statistics, D, and the
 // score, gain and temperature gradients use the fp32 values.
 //
-// Operand staging: every tile sits in LDS row-major with its contraction
-// index contiguous where it is an A operand or the B' operand of C = A.B'^T
-// (one 16-byte read per lane and K-step); where the contraction runs down
-// the rows of a row-major tile (dO and Q in the dV/dK products, K in dQ)
-// the B operand is two transposing 8-byte reads (ds_read_b64_tr_b16).
+// Operand staging: the Q/dO (or K/V) tiles sit in LDS in a swizzled
+// row-major layout read both ways: 16-byte row reads for the operands whose
+// contraction runs along the row, two transposing 8-byte reads
+// (ds_read_b64_tr_b16) for those whose contraction runs down the rows.
 #include "common.h"
 
 namespace tg {
@@ -34,30 +35,11 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 constexpr int kB = 64;               // queries and keys per tile
-constexpr int kThr = 512;            // 8 waves
-constexpr int kLX = kB + 1;          // fp32 exchange tile stride
 constexpr float kLog2e = 1.4426950408889634f;
 
 TG_DEVINL bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
-TG_DEVINL uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-
-// acc[32 x 32] += A[32 rows][K] . B'[32 rows][K]^T, k contiguous in both
-// (ZERO: acc = the product, the first step adding to a zero constant)
-template <int KSTEPS, bool ZERO = false>
-TG_DEVINL void mma_abt(floatx16& acc, const uint16_t* A, int lda, const uint16_t* B, int ldb,
-                       int lane) {
-  const int r = lane & 31, kg = lane >> 5;
-  const floatx16 zero = {};
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const bf16x8 a = as_bf16x8(ld16(A + r * lda + 16 * s + 8 * kg));
-    const bf16x8 b = as_bf16x8(ld16(B + r * ldb + 16 * s + 8 * kg));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, (ZERO && s == 0) ? zero : acc, 0, 0, 0);
-  }
-}
 
 // 4 consecutive rows of one column per lane by a transposing LDS read
 // (ds_read_b64_tr_b16): within each 16-lane group, output element e of lane
@@ -73,20 +55,6 @@ TG_DEVINL uint2 ld_tr4(const uint16_t* p) {
 // C layout of a 32 x 32 tile: register j of lane (n, g) is row 8(j/4) + 4g + j%4, column n
 TG_DEVINL int crow(int j, int g) { return 8 * (j >> 2) + 4 * g + (j & 3); }
 
-// 64 rows of head `hd` of a [*, H, DH] bf16 tensor, rows past `len` zero,
-// into LDS rows of stride DH + 8
-template <int DH>
-TG_DEVINL void load_rows(uint16_t* dst, const uint16_t* __restrict__ src, int64_t lo, int len,
-                         int r0, int H, int hd) {
-  constexpr int LD = DH + 8, CPR = DH / 8;
-  for (int u = threadIdx.x; u < kB * CPR; u += kThr) {
-    const int r = u / CPR, c = u % CPR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r0 + r < len) v = ld16(src + ((lo + r0 + r) * H + hd) * (int64_t)DH + 8 * c);
-    st16(dst + r * LD + 8 * c, v);
-  }
-}
-
 // Swizzled tile layout for tiles read both row-wise (16-byte reads) and by
 // transposing 8-byte reads: rows of DH + 32 elements (320 B for DH 128,
 // 192 B for DH 64: four consecutive rows start in the four 64-byte quarters
@@ -100,12 +68,13 @@ TG_DEVINL int swz_off(int row, int chunk) {
   return row * swz_ld<DH>() + 8 * (chunk ^ ((row >> 2) & 3));
 }
 
-// The same rows fetched into registers one iteration ahead, then stored.
+// 64 rows of head hd of a [*, H, DH] bf16 tensor fetched into registers one
+// tile ahead, then stored into the swizzled layout.
 // Buffer loads: the resource starts at the tile's first row of head hd and
 // ends after the sequence's last row of that head, so rows past `len` read
 // zeros with no per-row test, and each thread's byte offsets within a tile
 // are fixed for the kernel (set once by init).
-template <int DH, int NT = kThr>
+template <int DH, int NT>
 struct Pf {
   static constexpr int N = kB * (DH / 8) / NT;
   u32x4 r[N];
@@ -131,14 +100,6 @@ struct Pf {
     for (int i = 0; i < N; ++i)
       r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 0));
   }
-  TG_DEVINL void store(uint16_t* dst) const {
-    constexpr int CPR = DH / 8, LD = DH + 8;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int u = threadIdx.x + i * NT, row = u / CPR, c = u % CPR;
-      st16(dst + row * LD + 8 * c, r[i]);
-    }
-  }
   // into the swizzled layout of swz_off
   TG_DEVINL void store_swz(uint16_t* dst) const {
     constexpr int CPR = DH / 8;
@@ -160,17 +121,6 @@ struct Seq {
   int len;
 };
 
-TG_DEVINL bool tile_of_slot(const int32_t* cu, int n_seq, int64_t t, int64_t slot, Seq& sq,
-                            int& t0) {
-  const int s = seq_of_slot(cu, n_seq, slot, kB);
-  if (s < 0) return false;
-  sq.lo = cu[s] < t ? cu[s] : t;
-  const int64_t hi = cu[s + 1] < t ? cu[s + 1] : t;
-  sq.len = hi > sq.lo ? (int)(hi - sq.lo) : 0;
-  t0 = (int)(slot - slot0_of(cu, s, kB)) * kB;
-  return t0 < sq.len;
-}
-
 // Work item of block b in the one-dimensional grids of the three passes.
 // Blocks are dealt round-robin over the 8 XCDs, each with its own L2, so the
 // KV head is taken from the low bits of the block index: with 8 KV heads
@@ -186,191 +136,6 @@ TG_DEVINL void work_item(int64_t b, int hkv, int g_heads, int64_t n_slots, bool 
   hh = (int)(r % g_heads);
   slot = r / g_heads;
   if (reverse) slot = n_slots - 1 - slot;
-}
-
-// Phase A of every pass: waves 0-3 compute S^T = K.Q^T for tile (kt, qt) =
-// (w & 1, w >> 1), waves 4-7 compute dP^T = V.dO^T for the same tile.  The
-// elementwise work is then split evenly: registers 0-7 of a lane (key rows
-// 32kt + 0..15) go to the S wave, registers 8-15 (rows 32kt + 16..31) to the
-// dP wave, so each wave parks the other half of its tile in the fp32
-// exchange tile sX[key][query] (the two halves never overlap).
-template <int DH>
-TG_DEVINL void phase_a(floatx16& acc, int wv, int lane, const uint16_t* sK, const uint16_t* sV,
-                       const uint16_t* sQ, const uint16_t* sO, float* sX) {
-  constexpr int LD = DH + 8;
-  const int w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
-  const int n = lane & 31, g = lane >> 5;
-  if (wv < 4) mma_abt<DH / 16, true>(acc, sK + 32 * kt * LD, LD, sQ + 32 * qt * LD, LD, lane);
-  else mma_abt<DH / 16, true>(acc, sV + 32 * kt * LD, LD, sO + 32 * qt * LD, LD, lane);
-  // the parked half as a vector select of the two halves (a run-time
-  // register index would cost a mode switch and a move per element); key
-  // row crow(8 + j) is crow(j) + 16
-  const floatx8 lo = __builtin_shufflevector(acc, acc, 0, 1, 2, 3, 4, 5, 6, 7);
-  const floatx8 hi = __builtin_shufflevector(acc, acc, 8, 9, 10, 11, 12, 13, 14, 15);
-  const floatx8 park = wv < 4 ? hi : lo;
-  float* xrow = sX + (32 * kt + (wv < 4 ? 16 : 0)) * kLX + 32 * qt + n;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) xrow[crow(j, g) * kLX] = park[j];
-}
-
-// After phase A and a barrier: this wave's 8 elements (S, dP).  Element jj
-// sits at key row kbase + kofs(jj) of the tile (kbase = 32kt + 4g, plus 16
-// on the dP wave, whose elements are registers 8..15); the lane's query row
-// is 32qt + n.
-TG_DEVINL constexpr int kofs(int jj) { return 8 * (jj >> 2) + (jj & 3); }
-
-struct Elems {
-  float S[8], dP[8];
-  int kbase;
-  TG_DEVINL int kr(int jj) const { return kbase + kofs(jj); }
-};
-
-// (Vector selects of the two halves of acc: a register index chosen at run
-// time would cost a mode switch and a move per element.)
-TG_DEVINL void gather(const floatx16& acc, int wv, int lane, const float* sX, Elems& e) {
-  const int w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
-  const int n = lane & 31, g = lane >> 5, qr = 32 * qt + n;
-  const bool sw = wv < 4;
-  e.kbase = 32 * kt + 4 * g + (sw ? 0 : 16);
-  const floatx8 lo = __builtin_shufflevector(acc, acc, 0, 1, 2, 3, 4, 5, 6, 7);
-  const floatx8 hi = __builtin_shufflevector(acc, acc, 8, 9, 10, 11, 12, 13, 14, 15);
-  const floatx8 mine = sw ? lo : hi;
-  const float* xr = sX + e.kbase * kLX + qr;
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const float x = xr[kofs(jj) * kLX];
-    e.S[jj] = sw ? mine[jj] : x;
-    e.dP[jj] = sw ? x : mine[jj];
-  }
-}
-
-// log2-domain logits of the 8 elements minus `off` (the row's lse2 where the
-// probabilities follow at once, else 0); -inf where masked.  Tiles wholly
-// below the diagonal and inside the sequence skip the per-element test
-// (lanes where `full` holds for all take no masking branch).
-TG_DEVINL void logits(const Elems& e, float (&l2)[8], int qi, int k0, bool full, float c1, float c2,
-                      const float* sb, float off = 0.0f) {
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) l2[jj] = fmaf(c1, e.S[jj], fmaf(c2, sb[e.kr(jj)], -off));
-  if (!full) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      if (k0 + e.kr(jj) > qi) l2[jj] = -INFINITY;
-  }
-}
-
-// ---- pass 1: lse2 and D per (query, head)
-template <int DH>
-__global__ __launch_bounds__(kThr) void bwdm_stats(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ kept_b, const int32_t* __restrict__ kept_pos,
-    const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
-    const float* __restrict__ gain, const float* __restrict__ temp, float sm,
-    float* __restrict__ lse2, float* __restrict__ dsum, int64_t n_slots) {
-  constexpr int LD = DH + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kB * LD], sO[kB * LD], sK[kB * LD],
-      sV[kB * LD];
-  __shared__ float sX[kB * kLX];
-  __shared__ float stau[kB], sb[kB], sm_[4][kB], sl_[4][kB], su_[4][kB];
-  Seq sq;
-  int q0;
-  int64_t slot;
-  int kvh, hh;
-  work_item(blockIdx.x, hkv, hq / hkv, n_slots, true, slot, kvh, hh);
-  if (!tile_of_slot(cu, n_seq, t, slot, sq, q0)) return;
-  const int h = kvh * (hq / hkv) + hh;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, g = lane >> 5, w4 = wv & 3, kt = w4 & 1, qt = w4 >> 1;
-  const float gh = gain[h];
-  if (tid < kB)
-    stau[tid] = q0 + tid < sq.len ? temp[h] * length_lambda(kept_pos, sq.lo + q0 + tid, q0 + tid)
-                                  : 0.0f;
-  load_rows<DH>(sQ, q, sq.lo, sq.len, q0, hq, h);
-  load_rows<DH>(sO, dout, sq.lo, sq.len, q0, hq, h);
-  float m = -INFINITY, L = 0.0f, U = 0.0f;            // this lane's query, its keys so far
-  const int qr = 32 * qt + n, qi = q0 + qr;
-  const int q_end = q0 + kB < sq.len ? q0 + kB : sq.len;
-  Pf<DH> pk, pv;                                      // key tile k0 + 64, in flight
-  pk.init(hkv);
-  pv.init(hkv);
-  float pb = 0.0f;
-  pk.load(k, sq.lo, sq.len, 0, hkv, kvh);
-  pv.load(v, sq.lo, sq.len, 0, hkv, kvh);
-  if (tid < kB) pb = tid < sq.len ? kept_b[sq.lo + tid] : 0.0f;
-  __syncthreads();
-  const float tau = stau[qr];
-  const float c1 = tau * sm * kLog2e, c2 = tau * gh * kLog2e;
-  for (int k0 = 0; k0 < q_end; k0 += kB) {
-    __syncthreads();
-    pk.store(sK);
-    pv.store(sV);
-    if (tid < kB) sb[tid] = pb;
-    if (k0 + kB < q_end) {
-      pk.load(k, sq.lo, sq.len, k0 + kB, hkv, kvh);
-      pv.load(v, sq.lo, sq.len, k0 + kB, hkv, kvh);
-      if (tid < kB) pb = k0 + kB + tid < sq.len ? kept_b[sq.lo + k0 + kB + tid] : 0.0f;
-    }
-    __syncthreads();
-    floatx16 acc;
-    phase_a<DH>(acc, wv, lane, sK, sV, sQ, sO, sX);
-    __syncthreads();
-    if (qi < sq.len) {
-      Elems e;
-      gather(acc, wv, lane, sX, e);
-      float l2[8];
-      logits(e, l2, qi, k0, k0 + kB <= q0, c1, c2, sb);
-      float mt = l2[0];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) mt = fmaxf(mt, l2[jj]);
-      if (mt != -INFINITY) {
-        const float mn = fmaxf(m, mt);
-        const float f = __builtin_amdgcn_exp2f(m - mn);
-        L *= f;
-        U *= f;
-        m = mn;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float p = __builtin_amdgcn_exp2f(l2[jj] - mn);
-          L += p;
-          U = fmaf(p, e.dP[jj], U);
-        }
-      }
-    }
-  }
-  // merge the two lane halves, then the four partial states of each query
-  // (two waves per tile x two key halves)
-  const float m2 = __shfl_xor(m, 32, 64), L2 = __shfl_xor(L, 32, 64), U2 = __shfl_xor(U, 32, 64);
-  const float mn = fmaxf(m, m2);
-  if (mn != -INFINITY) {
-    const float f1 = __builtin_amdgcn_exp2f(m - mn), f2 = __builtin_amdgcn_exp2f(m2 - mn);
-    L = L * f1 + L2 * f2;
-    U = U * f1 + U2 * f2;
-    m = mn;
-  }
-  const int part = 2 * kt + (wv >> 2);
-  if (g == 0) {
-    sm_[part][qr] = m;
-    sl_[part][qr] = L;
-    su_[part][qr] = U;
-  }
-  __syncthreads();
-  if (tid < kB && q0 + tid < sq.len) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) mx = fmaxf(mx, sm_[p][tid]);
-    float Lt = 0.0f, Ut = 0.0f;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float f = sm_[p][tid] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sm_[p][tid] - mx);
-      Lt = fmaf(sl_[p][tid], f, Lt);
-      Ut = fmaf(su_[p][tid], f, Ut);
-    }
-    const int64_t row = sq.lo + q0 + tid;
-    lse2[(int64_t)h * t + row] = mx + __log2f(Lt);
-    dsum[row * hq + h] = Ut / Lt;
-  }
 }
 
 // ---- pass 1 from saved forward state: D per (query, head) as dO_i . O_i,
@@ -396,8 +161,6 @@ __global__ __launch_bounds__(256) void bwdm_dsum(const uint16_t* __restrict__ o,
   for (int off = L / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (p < pairs && (threadIdx.x % L) == 0) dsum[p] = acc;
 }
-
-// P and dl = P (dP - D) of this wave's 8 elements
 
 // ---- pass 2: dK, dV and the
 // per-KV-head b gradient, per (block of 128 keys, KV head).  Four waves, one
@@ -655,9 +418,12 @@ void bwdm_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // dS values are directly the A operand of dQ += dS.K (keys in runs of four,
 // matched by transposing reads of K); the query's lse2, D, tau and lambda
 // are per-lane scalars.
+// STATS: pass 1 in the same form (without the forward's saved state): the
+// row statistics lse2 and D = sum_j P_ij dP_ij by an online merge per lane
+// (each lane half holds half of the keys), then across the two halves.
 constexpr int kQB = 128;             // queries per workgroup of this pass
 
-template <int DH>
+template <int DH, bool STATS = false>
 __global__ __launch_bounds__(kKvThr) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
@@ -665,7 +431,8 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             const int32_t* __restrict__ cu, int n_seq, int64_t t, int hq, int hkv,
             const float* __restrict__ gain, const float* __restrict__ temp, float sm,
             const float* __restrict__ lse2, const float* __restrict__ dsum,
-            float* __restrict__ dq, double* __restrict__ gpart, int64_t n_slots) {
+            float* __restrict__ dq, double* __restrict__ gpart, int64_t n_slots,
+            float* __restrict__ lse2_out = nullptr, float* __restrict__ dsum_out = nullptr) {
   constexpr int LD = swz_ld<DH>(), KS = DH / 16, NDT = DH / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kB * LD], sV[2][kB * LD];
   __shared__ __attribute__((aligned(16))) uint32_t sBias[2][kB];   // (hi, lo) bf16 pair per key
@@ -682,7 +449,7 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   Seq sq;
   int q0;
   if (!block_of_slot(cu, n_seq, t, slot, kQB, sq, q0)) {
-    if (tid == 0) {                                    // every slot leaves a partial
+    if (!STATS && tid == 0) {                          // every slot leaves a partial
       gp[0] = 0.0;
       gp[1] = 0.0;
     }
@@ -699,9 +466,12 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     lam = length_lambda(kept_pos, sq.lo + qi, qi);
     tau = temp[h] * lam;
     c = tau * sm * kLog2e;
-    lse = lse2[(int64_t)h * t + sq.lo + qi];
-    D = dsum[(sq.lo + qi) * hq + h];
+    if constexpr (!STATS) {
+      lse = lse2[(int64_t)h * t + sq.lo + qi];
+      D = dsum[(sq.lo + qi) * hq + h];
+    }
   }
+  float sm_m = -INFINITY, sm_l = 0.0f, sm_u = 0.0f;   // STATS: running max, sum, sum of p dP
   // Q and dO rows of query qi (B operands: dims 16s + 8g .. +8)
   u32x4 qf[KS], of[KS];
   {
@@ -778,6 +548,31 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       }
       // element j: key kb0 + 8(j/4) + 4g + j%4, query qi
+      if constexpr (STATS) {
+        const bool mask = kb0 + 31 > qw0;
+        float l2[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          l2[j] = c * sacc[j];
+          if (mask && kb0 + crow(j, g) > qi) l2[j] = -INFINITY;
+          mt = fmaxf(mt, l2[j]);
+        }
+        if (qok && mt != -INFINITY) {
+          const float mn = fmaxf(sm_m, mt);
+          const float f = __builtin_amdgcn_exp2f(sm_m - mn);
+          sm_l *= f;
+          sm_u *= f;
+          sm_m = mn;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float p = __builtin_amdgcn_exp2f(l2[j] - mn);
+            sm_l += p;
+            sm_u = fmaf(p, pacc[j], sm_u);
+          }
+        }
+        continue;
+      }
       uint32_t dw[8];
       auto elementwise = [&](auto MASKC) {
         constexpr bool MASK = decltype(MASKC)::value;
@@ -830,6 +625,21 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (kt + 1 < n_tiles) stash(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (STATS) {
+    // merge the two lane halves (disjoint keys of the same query)
+    const float m2 = __shfl_xor(sm_m, 32, 64), l2s = __shfl_xor(sm_l, 32, 64);
+    const float u2 = __shfl_xor(sm_u, 32, 64);
+    const float mn = fmaxf(sm_m, m2);
+    const float f1 = sm_m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sm_m - mn);
+    const float f2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m2 - mn);
+    const float L = fmaf(sm_l, f1, l2s * f2), U = fmaf(sm_u, f1, u2 * f2);
+    if (g == 0 && qok) {
+      const int64_t row = sq.lo + qi;
+      lse2_out[(int64_t)h * t + row] = mn + __log2f(L);
+      dsum_out[row * hq + h] = U / L;
+    }
+    return;
+  }
   // dQ rows: register j of lane (n, g) is query qw0 + 8(j/4) + 4g + j%4, dim 32d + n
 #pragma unroll
   for (int d = 0; d < NDT; ++d)
@@ -863,7 +673,6 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
                                 float* dsum, float* dq, float* dk, float* dv, float* dbpart,
                                 double* gpart, const void* fwd_out, const float* fwd_lse2,
                                 hipStream_t st) {
-  const int64_t nq = n_seq + (t + kB - 1) / kB;
   const int64_t nkb = n_seq + (t + kKB - 1) / kKB;     // key blocks of the dK/dV pass
   const int64_t nqb = attn_bwd_mfma_gslots(t, n_seq);   // query blocks of the dQ pass
   const bool saved = fwd_out != nullptr && fwd_lse2 != nullptr;
@@ -878,9 +687,9 @@ hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, con
     hipLaunchKernelGGL((bwdm_dsum<DHv>), dim3((unsigned)dsum_blocks), dim3(256), 0, st,          \
                        static_cast<const uint16_t*>(fwd_out), op, t * hq, dsum);                 \
   else                                                                                           \
-    hipLaunchKernelGGL((bwdm_stats<DHv>), dim3((unsigned)(nq * hq)), dim3(kThr), 0, st, qp, kp, \
-                       vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse2,    \
-                       dsum, nq);                                                                \
+    hipLaunchKernelGGL((bwdm_q<DHv, true>), dim3((unsigned)(nqb * hq)), dim3(kKvThr), 0, st, qp, \
+                       kp, vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm,      \
+                       nullptr, nullptr, nullptr, nullptr, nqb, lse2, dsum);                     \
   hipLaunchKernelGGL((bwdm_kv<DHv>), dim3((unsigned)(nkb * hkv)), dim3(kKvThr), 0, st, qp, kp,   \
                      vp, op, kept_b, kept_pos, cu, n_seq, t, hq, hkv, gain, temp, sm, lse, dsum, \
                      dk, dv, dbpart, nkb);                                                       \
