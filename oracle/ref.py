@@ -508,6 +508,75 @@ def ref_gated_attn_bwd(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
     return dq, dk, dv, db, dgain, dtemp
 
 
+def ref_gated_attn_bwd_rows(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, dout,
+                            query_rows, key_rows, sm_scale: Optional[float] = None,
+                            len_scale: str = R.LEN_SCALE, row_block: int = 512):
+    """The gradients of ref_gated_attn_bwd at a sample of rows, for inputs
+    too large for every gradient row: dq at ``query_rows`` and dk, dv, db at
+    ``key_rows`` (global row indices).  The same definitions, evaluated the
+    same way block by block: every query row's softmax and D_i still need all
+    of its keys, but only the sampled rows of dq and columns of the dk, dv
+    and db sums are formed.  Returns (dq [len(query_rows), Hq, dh],
+    dk [len(key_rows), Hkv, dh], dv [len(key_rows), Hkv, dh], db [len(key_rows)]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    kb = np.asarray(kept_b, dtype=np.float64)
+    T, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(dh) if sm_scale is None else float(sm_scale)
+    qrows = np.asarray(query_rows, dtype=np.int64)
+    krows = np.asarray(key_rows, dtype=np.int64)
+    dq = np.zeros((len(qrows), Hq, dh))
+    dk = np.zeros((len(krows), Hkv, dh))
+    dv = np.zeros((len(krows), Hkv, dh))
+    db = np.zeros(len(krows))
+    for s in range(len(kept_cu) - 1):
+        lo, hi = int(kept_cu[s]), int(kept_cu[s + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        qsel = np.nonzero((qrows >= lo) & (qrows < hi))[0]     # positions in query_rows
+        ksel = np.nonzero((krows >= lo) & (krows < hi))[0]
+        if qsel.size == 0 and ksel.size == 0:
+            continue
+        a = np.arange(n)
+        if kept_pos is None:
+            lam = np.ones(n)
+        else:
+            lam = length_factor(a + 1.0, np.asarray(kept_pos[lo:hi], np.float64) + 1.0, len_scale)
+        kl = krows[ksel] - lo                                    # sampled keys, local
+        for h in range(Hq):
+            kvh = h // G
+            K, V = k[lo:hi, kvh, :], v[lo:hi, kvh, :]
+            g = float(gain[h])
+            for r0 in range(0, n, row_block):
+                rr = a[r0:r0 + row_block]
+                last = int(rr[-1]) + 1
+                Q, dO = q[lo + rr, h, :], do[lo + rr, h, :]
+                tau = float(temp[h]) * lam[rr]
+                z = scale * (Q @ K[:last].T) + g * kb[lo:lo + last][None, :]
+                causal = np.arange(last)[None, :] <= rr[:, None]
+                logits = np.where(causal, tau[:, None] * z, -np.inf)
+                P = _softmax_rows(logits)
+                dP = dO @ V[:last].T
+                dl = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+                tdl = tau[:, None] * dl
+                for pos in qsel:
+                    i = int(qrows[pos]) - lo
+                    if r0 <= i < r0 + len(rr):
+                        dq[pos, h, :] = scale * (tdl[i - r0] @ K[:last])
+                for m, j in zip(ksel, kl):
+                    if j < last:
+                        dv[m, kvh, :] += P[:, j] @ dO
+                        dk[m, kvh, :] += scale * (tdl[:, j] @ Q)
+                        db[m] += g * float(np.sum(tdl[:, j]))
+    return dq, dk, dv, db
+
+
 # ---------------------------------------------------------------------------
 # backward of the gate's scorer ([TG] §4.1 Eq. 3 read backwards: the gradient
 # that reaches the kept scores b through the attention flows on to the

@@ -861,6 +861,33 @@ def test_score_prenorm_bwd_fold_and_scale_invariance():
     assert np.max(np.abs(z)) > 1e-3                   # not orthogonal by being zero
 
 
+def test_attn_bwd_rows_match_the_full_backward():
+    """The sampled-rows form gives the full backward's dq rows and dk, dv, db
+    rows exactly (same definitions), across row blocks and sequences, with
+    positions and GQA."""
+    rng = _rng(91)
+    lens = [37, 0, 70, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, hq, hkv, dh = int(cu[-1]), 4, 2, 8
+    q = rng.standard_normal((T, hq, dh))
+    k = rng.standard_normal((T, hkv, dh))
+    v = rng.standard_normal((T, hkv, dh))
+    do = rng.standard_normal((T, hq, dh))
+    kb = rng.standard_normal(T)
+    pos = np.concatenate([np.sort(rng.choice(500, n, replace=False)) for n in lens]).astype(np.int64)
+    gain = rng.uniform(0.5, 1.5, hq)
+    temp = rng.uniform(0.8, 1.2, hq)
+    full = O.ref_gated_attn_bwd(q, k, v, kb, pos, cu, gain, temp, do, row_block=16)
+    qr = [0, 15, 16, 36, 37, 60, 106, 107]
+    kr = [0, 1, 16, 36, 37, 52, 106, 107]
+    dq, dk, dv, db = O.ref_gated_attn_bwd_rows(q, k, v, kb, pos, cu, gain, temp, do, qr, kr,
+                                               row_block=16)
+    assert np.allclose(dq, full[0][qr], rtol=1e-12, atol=1e-13)
+    assert np.allclose(dk, full[1][kr], rtol=1e-12, atol=1e-13)
+    assert np.allclose(dv, full[2][kr], rtol=1e-12, atol=1e-13)
+    assert np.allclose(db, full[3][kr], rtol=1e-12, atol=1e-13)
+
+
 # softmax normaliser of the gated attention, base 2 (the backward's statistic)
 def test_attn_lse2_closed_forms():
     """Zero queries and zero scores make every visible logit 0, so row i of a
