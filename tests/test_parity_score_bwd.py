@@ -197,3 +197,48 @@ def test_score_bwd_single_token_sequences(norm_eps):
     worst = float(np.max(np.linalg.norm(got - ref, axis=1)[live] / rn[live]))
     say(f"  worst row of dx: {worst:.2e} of its norm")
     assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("norm_eps", [None, 1e-6])
+def test_score_bwd_128k_step(norm_eps):
+    """The benchmark's configuration: 131072 tokens (the last 512 prompt
+    tokens), d 2048, h 256, K = 8192, bf16 rows on the matrix-core path; dW1,
+    db1, dw2, db2 in full, dx on 64 sampled rows (first and last rows, tile
+    edges, the last document and first prompt row, random), at the bars of
+    the smaller cases."""
+    T, d, h = 131072, 2048, 256
+    rng = np.random.default_rng(99 if norm_eps is None else 98)
+    tag = "plain" if norm_eps is None else "LN2"
+    say(f"score bwd {tag} bf16: the 128k step, T={T} d={d} h={h} K=8192")
+    c = sbwd_case(21 if norm_eps is None else 22, T, d, h, [T], [8192], "bf16", norm_eps=norm_eps)
+    c["pr"][:] = 1
+    c["pr"][T - 512:] = 0
+    # the kept set and db for this prompt layout (the case drew its own mask)
+    if norm_eps is None:
+        raw = O.ref_score(c["x"], c["w1"], c["b1"], c["w2"], c["b2"])
+    else:
+        raw = O.ref_score_prenorm(c["x"], None, norm_eps, c["w1"], c["b1"], c["w2"], c["b2"])
+    c["raw32"] = raw.astype(np.float32)
+    b, _ = O.ref_normalise(c["raw32"].astype(np.float64), c["pr"], c["cu"], EPS)
+    ki, _, _, kc = O.ref_select(b.astype(np.float32), c["pr"], c["cu"], [8192])
+    c["kept_idx"], c["kept_cu"] = np.asarray(ki, np.int32), np.asarray(kc, np.int32)
+    c["db_kept"] = rng.standard_normal(len(ki)).astype(np.float32)
+    got = run(c, "bf16")
+    if norm_eps is None:
+        *ref, scale = O.ref_score_bwd(c["x"], c["w1"], c["b1"], c["w2"], c["b2"], c["pr"],
+                                      c["cu"], c["kept_idx"], c["kept_cu"], c["db_kept"], eps=EPS,
+                                      error_scales=True)
+    else:
+        da, dw1, _, db1, dw2, db2, scale = O.ref_score_prenorm_bwd(
+            c["x"], None, norm_eps, c["w1"], c["b1"], c["w2"], c["b2"], c["pr"], c["cu"],
+            c["kept_idx"], c["kept_cu"], c["db_kept"], eps=EPS, error_scales=True)
+        ref = [da, dw1, db1, dw2, db2]
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, T - 513, T - 512, T - 1],
+                                     rng.choice(T, 55, replace=False)]))
+    errs = {"dx": rel_l2(got[0][rows], ref[0][rows]), "dw1": rel_l2(got[1], ref[1]),
+            "db1": rel_l2(got[2], ref[2]), "dw2": rel_l2(got[3], ref[3]),
+            "db2": abs(float(got[4][0]) - ref[4]) / (abs(ref[4]) + scale)}
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        bar = 1e-2 if n in ("dx", "dw1") else TOL
+        assert e <= bar, f"{n}: {e:.3e} > {bar}"
