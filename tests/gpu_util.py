@@ -83,6 +83,22 @@ def workload(cfg: int):
     return generate(cfg)
 
 
+# The forward's lse2 (log2 of the softmax normaliser) sums probabilities that
+# were rounded to bf16 before the sum.  bf16 keeps 8 significant bits, so
+# round-to-nearest is within 2^-8 relative per term, and so is the sum of
+# such positive terms: its base-2 log is within log2(1 + 2^-8) = 5.6e-3 of
+# the exact one.  The fp32 logits add an error proportional to their size
+# (the gain term enters as a bf16 hi/lo pair, 2^-18 relative): the bar is
+# |got - ref| <= LSE2_ABS + LSE2_REL |ref|.
+LSE2_ABS = math.log2(1.0 + 2.0 ** -8)
+LSE2_REL = 1e-5
+
+
+def lse2_excess(got, ref):
+    """max over entries of |got - ref| - LSE2_REL |ref| (to compare with LSE2_ABS)."""
+    return float(np.max(np.abs(got - ref) - LSE2_REL * np.abs(ref)))
+
+
 # Attention parity figures.  The global rel-L2 is the bar the workloads are
 # quoted at; per head and per row the same error is measured again, so that
 # a defect confined to one head (each head has its own gain and temperature,

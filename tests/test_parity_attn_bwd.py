@@ -6,7 +6,7 @@ the same way).  fp32 inputs run in fp32 on the vector ALU: for dq, dk, dv
 and db the rel-L2 bar is 1e-5 (fp32 products and sums over <= 2^12 terms,
 with the cancellation in dl = P (dP - D), measure below 1.6e-6).  bf16
 inputs run on the matrix cores, where P and dS enter the dv, dk and dq
-products rounded to bf16 (relative 2^-9 per term): those three take the
+products rounded to bf16 (relative 2^-8 per term): those three take the
 bf16 attention bar, rel-L2 <= 1e-2; db, dgain and dtemp come from the fp32
 values and keep the fp32 bars.  dgain and dtemp are sums of terms of both signs over every
 (query, key) pair of a head, so their bar is relative to the oracle's error

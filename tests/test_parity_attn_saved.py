@@ -2,14 +2,15 @@
 
 tg_gated_attn's optional lse2 output against ref_gated_attn_lse2 (fp64).
 The kernel forms the normaliser from bf16-rounded probabilities (the ones
-that enter P.V, each within 2^-9 relative), so its base-2 log is within
-2^-9 / ln 2 = 2.8e-3 of the exact one, plus the fp32 error of the logits;
-the bar is |got - ref| <= 3e-3 + 1e-5 |ref|.
+that enter P.V, each within 2^-8 relative: bf16 keeps 8 significant bits),
+so its base-2 log is within log2(1 + 2^-8) = 5.6e-3 of the exact one, plus
+the fp32 error of the logits; the bar is |got - ref| <= 5.6e-3 + 1e-5 |ref|
+(gpu_util.LSE2_ABS, LSE2_REL).
 
 tg_gated_attn_bwd with fwd_out and fwd_lse2 against ref_gated_attn_bwd,
 with the saved state taken (a) from the oracle (its output rounded to bf16,
 its lse2 to fp32) and (b) from tg_gated_attn itself, the pipeline a training
-step runs.  D = dout . out then carries out's bf16 rounding (2^-9 relative),
+step runs.  D = dout . out then carries out's bf16 rounding (2^-8 relative),
 which reaches every gradient through dl = P (dP - D): all six take the bf16
 bar, rel-L2 <= 1e-2, and dgain, dtemp the same bar relative to the oracle's
 error scale plus the value."""
@@ -20,7 +21,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import bf16_dev, f32_dev, i32_dev, rel_l2, round_bf16, say
+from gpu_util import (LSE2_ABS, bf16_dev, f32_dev, i32_dev, lse2_excess, rel_l2, round_bf16,
+                      say)
 from test_parity_attn_bwd import NAMES, bwd_case
 from workloads import bf16_to_f64
 
@@ -50,10 +52,10 @@ def test_forward_lse2_matches_oracle(dh, hq, hkv, lens):
     torch.cuda.synchronize()
     got = lse2.cpu().numpy().astype(np.float64).T
     ref = O.ref_gated_attn_lse2(q, k, kb, pos, kc, gain, temp)
-    err = float(np.max(np.abs(got - ref) - 1e-5 * np.abs(ref)))
+    err = lse2_excess(got, ref)
     say(f"  worst |d lse2| beyond 1e-5 |ref|: {err:.2e}")
     assert np.all(np.isfinite(got))
-    assert err <= 3e-3
+    assert err <= LSE2_ABS
 
 
 def _check(got, case, tag):

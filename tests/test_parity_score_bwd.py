@@ -6,7 +6,7 @@ rounded the same way, the forward's raw scores rounded to fp32 as the
 kernel receives them).  fp32 arithmetic (fp32 inputs, or shapes outside the
 matrix-core path): rel-L2 <= 1e-5 for dx, dW1, db1 and dw2 (fp32 sums over
 <= 2^14 terms).  bf16 inputs with h = 256 and d % 256 == 0 run dW1 and dx on
-the matrix cores with dz rounded to bf16 (relative 2^-9 per term): those two
+the matrix cores with dz rounded to bf16 (relative 2^-8 per term): those two
 take the bf16 bar, rel-L2 <= 1e-2; db1 and dw2 come from the fp32 values.
 db2 is a sum of terms of both signs over every prunable token, so its bar
 is |got - ref| <= 1e-5 (|ref| + sum |db~|).
