@@ -217,6 +217,35 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
                         tg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * tg_gated_attn_split -- the same attention (§4.2 Eq. 8, as tg_gated_attn,
+ * same arguments and outputs, bf16 only), balanced for inputs whose query
+ * blocks are few or uneven (short sequences, small budgets, ragged
+ * batches).  A one-workgroup launch first plans the work on the GPU: query
+ * blocks with more key tiles than a workgroup's share of the causal work
+ * are split over the keys into chunks, and all items are sorted by size,
+ * largest first, for the workgroups.  Each chunk leaves its unnormalised
+ * output, running maximum and sum in the workspace, and a last launch merges
+ * them (flash-decoding's split over the keys, applied to the prefill).
+ * ws  dev workspace of >= tg_gated_attn_split_workspace_size(t_kept, n_seq,
+ *     max_kept_seqlen, hq, hkv, dh) bytes (the same max_kept_seqlen as the
+ *     call), 256-byte aligned: the plan (a few bytes per query block) and,
+ *     when blocks are split, the partial results.  Calls that share a
+ *     workspace must not overlap.
+ * How blocks are split depends on the sizes alone (it is planned for a
+ * 256-CU gfx950), so results are bitwise reproducible; rows of split blocks
+ * differ from tg_gated_attn's in the last bits (the merge's order of
+ * additions), the other rows are identical.
+ * ---------------------------------------------------------------------- */
+size_t tg_gated_attn_split_workspace_size(int64_t t_kept, int32_t n_seq, int32_t max_kept_seqlen,
+                                          int32_t hq, int32_t hkv, int32_t dh);
+tg_status tg_gated_attn_split(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                              int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                              const int32_t* kept_cu_seqlens, int32_t n_seq,
+                              int32_t max_kept_seqlen, int32_t hq, int32_t hkv, int32_t dh,
+                              const float* gain, const float* temp, float sm_scale, float* lse2,
+                              void* ws, size_t ws_bytes, tg_stream stream);
+
+/* ------------------------------------------------------------------------
  * tg_gated_attn_bwd -- gradients of tg_gated_attn: the path by which the
  * loss reaches the gate's scores (§4.3: token-gated attention gives top-K a
  * gradient), and the gradients of gain (Eq. 6) and temperature (Eq. 7).

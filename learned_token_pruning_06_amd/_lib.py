@@ -45,6 +45,10 @@ PROTOTYPES = {
     "tg_gated_attn": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp, c_vp,
                                      c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
                                      c_vp, c_vp]),
+    "tg_gated_attn_split_workspace_size": (c_sz, [c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "tg_gated_attn_split": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_vp,
+                                           c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                           c_vp, c_f32, c_vp, c_vp, c_sz, c_vp]),
     "tg_score_bwd_workspace_size": (c_sz, [c_i64, c_i32, c_i32, c_i32]),
     "tg_score_bwd": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_vp, c_vp, c_vp, c_i64,

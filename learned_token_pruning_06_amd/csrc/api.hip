@@ -299,46 +299,99 @@ tg_status tg_qkv_proj_rope(const void* x, tg_dtype dt, int64_t xs, int64_t t, in
 }
 
 // ------------------------------------------------------------- attention
-tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
-                        int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
-                        const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
-                        int32_t hkv, int32_t dh, const float* gain, const float* temp,
-                        float sm_scale, float* lse2, tg_stream stream) {
+}  // extern "C"
+
+namespace {
+// tg_gated_attn and tg_gated_attn_split: checks and launch (ws: the split
+// form's workspace, or null)
+tg_status tg_gated_attn_impl(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                             const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
+                             int32_t hkv, int32_t dh, const float* gain, const float* temp,
+                             float sm_scale, float* lse2, void* ws, tg_stream stream,
+                             const char* who) {
   if (t_kept < 0 || n_seq < 1 || max_len < 0 || hq < 1 || hkv < 1)
-    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: bad sizes");
-  if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: hq %% hkv != 0");
-  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: bad dtype");
-  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: dh must be 64 or 128");
+    return fail(TG_ERR_INVALID_ARG, "%s: bad sizes", who);
+  if (hq % hkv != 0) return fail(TG_ERR_INVALID_ARG, "%s: hq %% hkv != 0", who);
+  if (dt != TG_F32 && dt != TG_BF16) return fail(TG_ERR_INVALID_ARG, "%s: bad dtype", who);
+  if (dh != 64 && dh != 128) return fail(TG_ERR_UNSUPPORTED, "%s: dh must be 64 or 128", who);
   const int g = hq / hkv;
   if (!((g <= 4 && 4 % g == 0) || (g > 4 && g % 4 == 0)))
-    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: hq/hkv must be 1, 2, 4 or a multiple of 4");
-  if (t_kept > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: t_kept too large");
-  if (!kept_cu || !gain || !temp) return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: null pointer");
+    return fail(TG_ERR_UNSUPPORTED, "%s: hq/hkv must be 1, 2, 4 or a multiple of 4", who);
+  if (t_kept > INT32_MAX - 4096) return fail(TG_ERR_UNSUPPORTED, "%s: t_kept too large", who);
+  if (!kept_cu || !gain || !temp) return fail(TG_ERR_INVALID_ARG, "%s: null pointer", who);
   if (t_kept == 0) return ok();
   if (!q || !k || !v || !out || !kept_b)
-    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn: null pointer");
+    return fail(TG_ERR_INVALID_ARG, "%s: null pointer", who);
   if (max_len > t_kept) max_len = (int32_t)t_kept;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
-    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: tensors must be 16-byte aligned");
+    return fail(TG_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned", who);
   if (lse2 && dt != TG_BF16)
-    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 is written by the bf16 path only");
+    return fail(TG_ERR_UNSUPPORTED, "%s: lse2 is written by the bf16 path only", who);
   if (lse2 && !aligned(lse2, 4))
-    return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn: lse2 must be 4-byte aligned");
+    return fail(TG_ERR_UNSUPPORTED, "%s: lse2 must be 4-byte aligned", who);
   if (tg::contract_checks_on()) {
     hipError_t ce = tg::contract_offsets(kept_cu, n_seq, t_kept, TG_CONTRACT_KEPT_OFFSETS,
                                          (hipStream_t)stream);
     if (ce == hipSuccess && kept_pos)
       ce = tg::contract_positions(kept_pos, kept_cu, n_seq, t_kept, (hipStream_t)stream);
-    if (ce != hipSuccess) return from_hip(ce, "tg_gated_attn contract check");
+    if (ce != hipSuccess) return from_hip(ce, who);
   }
   hipError_t e;
   if (dt == TG_BF16)
     e = tg::launch_attn_bf16(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
-                             hkv, dh, gain, temp, sm_scale, lse2, (hipStream_t)stream);
+                             hkv, dh, gain, temp, sm_scale, lse2, (hipStream_t)stream, ws);
   else
     e = tg::launch_attn_f32(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len, hq,
                             hkv, dh, gain, temp, sm_scale, (hipStream_t)stream);
-  return from_hip(e, "tg_gated_attn launch");
+  return from_hip(e, who);
+}
+}  // namespace
+
+extern "C" {
+
+tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                        int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                        const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
+                        int32_t hkv, int32_t dh, const float* gain, const float* temp,
+                        float sm_scale, float* lse2, tg_stream stream) {
+  return tg_gated_attn_impl(q, k, v, dt, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len,
+                            hq, hkv, dh, gain, temp, sm_scale, lse2, nullptr, stream,
+                            "tg_gated_attn");
+}
+
+size_t tg_gated_attn_split_workspace_size(int64_t t_kept, int32_t n_seq, int32_t max_len,
+                                          int32_t hq, int32_t hkv, int32_t dh) {
+  if (t_kept < 0 || n_seq < 1 || max_len < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 ||
+      (dh != 64 && dh != 128))
+    return 0;
+  if (max_len > t_kept) max_len = (int32_t)t_kept;
+  return tg::attn_split_ws_bytes(t_kept, n_seq, max_len, hq, hkv, dh);
+}
+
+tg_status tg_gated_attn_split(const void* q, const void* k, const void* v, tg_dtype dt, void* out,
+                              int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
+                              const int32_t* kept_cu, int32_t n_seq, int32_t max_len, int32_t hq,
+                              int32_t hkv, int32_t dh, const float* gain, const float* temp,
+                              float sm_scale, float* lse2, void* ws, size_t ws_bytes,
+                              tg_stream stream) {
+  if (dt != TG_BF16 && dt != TG_F32)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_split: bad dtype");
+  if (dt != TG_BF16) return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_split: bf16 only");
+  if (t_kept < 0 || n_seq < 1 || max_len < 0 || hq < 1 || hkv < 1)
+    return fail(TG_ERR_INVALID_ARG, "tg_gated_attn_split: bad sizes");
+  const size_t need = tg_gated_attn_split_workspace_size(t_kept, n_seq, max_len, hq, hkv, dh);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(TG_ERR_WORKSPACE, "tg_gated_attn_split: workspace %zu < %zu bytes",
+                  ws ? ws_bytes : (size_t)0, need);
+    if (!aligned(ws, 256))
+      return fail(TG_ERR_UNSUPPORTED, "tg_gated_attn_split: ws must be 256-byte aligned");
+  }
+  // the remaining checks and the launch are tg_gated_attn's
+  return tg_gated_attn_impl(q, k, v, dt, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, max_len,
+                            hq, hkv, dh, gain, temp, sm_scale, lse2, need > 0 ? ws : nullptr,
+                            stream, "tg_gated_attn_split");
 }
 
 // ----------------------------------------------------------------- decode

@@ -137,14 +137,15 @@ struct AttnCfg {
   static constexpr int VTILE = BKV * VROW;       // bf16 per V buffer (row-major)
 };
 
-template <int DH, int HPW, int NWAVE>
+template <int DH, int HPW, int NWAVE, bool SPLIT>
 __device__ __forceinline__ void gated_attn_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int hg, int64_t slot,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale,
-    float* __restrict__ lse2, uint16_t* sk, uint16_t* sv) {
+    float* __restrict__ lse2, uint16_t* sk, uint16_t* sv, int chunk_tiles, int c_max, int chunk,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   constexpr int NTHR = C::NTHR;
   const int tid = threadIdx.x;
@@ -157,6 +158,22 @@ __device__ __forceinline__ void gated_attn_item(
   const int len = (kept_cu[s + 1] < t_kept ? kept_cu[s + 1] : t_kept) - lo;
   const int q0 = (int)(slot - slot0_of(kept_cu, s, C::QB)) * C::QB;
   if (q0 >= len) return;
+  // key tiles [t_lo, t_hi) of this item: chunk `chunk` of chunk_tiles tiles
+  // (the last of the c_max chunks runs to the block's end).  A block of at
+  // most chunk_tiles tiles is one item and writes its output; a longer one
+  // leaves partial results for attn_merge.
+  const int q_end = q0 + C::QB < len ? q0 + C::QB : len;
+  const int n_all = (q_end + BKV - 1) / BKV;
+  int t_lo = 0, t_hi = n_all;
+  bool part = false;
+  if constexpr (SPLIT) {
+    const int64_t t_lo64 = (int64_t)chunk * chunk_tiles;
+    if (t_lo64 >= n_all) return;                 // no keys in this chunk
+    t_lo = (int)t_lo64;
+    t_hi = chunk == c_max - 1 || n_all - t_lo <= chunk_tiles ? n_all : t_lo + chunk_tiles;
+    part = n_all > chunk_tiles;
+  }
+  const int n_tiles = t_hi - t_lo;
 
   const int G = hq / hkv;
   const int kvh = hg / groups_y;
@@ -194,8 +211,6 @@ __device__ __forceinline__ void gated_attn_item(
     qsel[e] = (__bf16)((g == 0 && (e >> 1) == hl) ? 1.0f : 0.0f);
 
   // ---- tile loaders (global -> registers -> LDS), per-thread state fixed up front
-  const int q_end = q0 + C::QB < len ? q0 + C::QB : len;
-  const int n_tiles = (q_end + BKV - 1) / BKV;
   const int64_t kvstride = (int64_t)hkv * DH;     // elements between token rows of k, v
   const uint16_t* kb_ = k + (int64_t)lo * kvstride + (int64_t)kvh * DH;
   const uint16_t* vb_ = v + (int64_t)lo * kvstride + (int64_t)kvh * DH;
@@ -407,19 +422,24 @@ __device__ __forceinline__ void gated_attn_item(
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
   const bool lag = wv >= NWAVE / 2;
-  load_tile(0);
-  store_tile(B0{});
+  // t counts the chunk's tiles from 0; its key tile is t_lo + t, and the
+  // wave needs the first wt of them
+  const int wt = w_tiles - t_lo;
+  if (n_tiles > 0) {
+    load_tile(t_lo);
+    store_tile(B0{});
+  }
   __syncthreads();
   auto step = [&](auto BC, auto BP, auto BN, int t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) load_tile(t_lo + t + 1);
     if (!lag) {
-      if (t < w_tiles) {
-        phase_s(BC, t);
+      if (t < wt) {
+        phase_s(BC, t_lo + t);
         phase_pv(BC);
       }
     } else {
-      if (t >= 1 && t - 1 < w_tiles) phase_pv(BP);
-      if (t < w_tiles) phase_s(BC, t);
+      if (t >= 1 && t - 1 < wt) phase_pv(BP);
+      if (t < wt) phase_s(BC, t_lo + t);
     }
     if (t + 1 < n_tiles) store_tile(BN);
     __syncthreads();
@@ -439,7 +459,7 @@ __device__ __forceinline__ void gated_attn_item(
     step(B2{}, B1{}, B0{}, t + 2);
   }
   // t == n_tiles here; the lagging waves still owe P.V of the last tile
-  if (lag && n_tiles - 1 < w_tiles) {
+  if (lag && n_tiles > 0 && n_tiles - 1 < wt) {
     const int bl = (n_tiles - 1) % 3;
     if (bl == 0)
       phase_pv(B0{});
@@ -452,6 +472,25 @@ __device__ __forceinline__ void gated_attn_item(
   // ---- epilogue: O = O^T / l, one query per lane; d = 32dt + 8(r/4) + 4g + r%4
   const float lt = half_swap_sum(lsum);
   if (!qvalid) return;
+  if (SPLIT && part) {
+    // a part of the keys: the unnormalised O, the running maximum and the
+    // sum it refers to, for the merge (attn_merge).  A wave's rows start at a
+    // multiple of 32 and a tile's keys at a multiple of 64, so every tile the
+    // wave computes begins at or before its first row: each row has a finite
+    // maximum from the chunk's first tile on.  A wave that needs none of the
+    // chunk's tiles leaves (-inf, 0) and O = 0, which the merge weighs 0.
+    const int64_t pr = ((int64_t)chunk * t_kept + lo + qa) * hq + head;
+    if (g == 0) ws_ml[pr] = make_float2(mrun, lt);
+    float* po = ws_o + pr * DH;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * r4 + 4 * g) =
+            make_float4(oacc[dt][4 * r4], oacc[dt][4 * r4 + 1], oacc[dt][4 * r4 + 2],
+                        oacc[dt][4 * r4 + 3]);
+    return;
+  }
   const float inv = 1.0f / lt;
   // optional row statistic for the backward: log2 sum_j exp2(c_i acc_ij), in
   // the units of the exponent, head-major [hq][t_kept] so the 32 queries of
@@ -471,14 +510,16 @@ __device__ __forceinline__ void gated_attn_item(
 }
 
 // two waves per SIMD: at most 256 registers per lane
-template <int DH, int HPW, int NWAVE>
+template <int DH, int HPW, int NWAVE, bool SPLIT>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(2)))
 void gated_attn_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, const float* __restrict__ kept_b,
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
-    const float* __restrict__ temp, float sm_scale, float* __restrict__ lse2) {
+    const float* __restrict__ temp, float sm_scale, float* __restrict__ lse2, int chunk_tiles,
+    int c_max, const int* __restrict__ plan, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   static_assert(NWAVE % HPW == 0 && C::NTHR >= BKV, "workgroup shape");
   __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
@@ -504,21 +545,236 @@ void gated_attn_bf16(
     const int64_t end = slot0_of(kept_cu, n_seq - 1, C::QB) + (last_len + C::QB - 1) / C::QB;
     if (end >= 0 && end < n_real) n_real = end;
   }
-  for (int64_t round = 0;; ++round) {
-    const int64_t rank = round * pj + ((round & 1) ? pj - 1 - jb : jb);
-    if (rank >= n_real) break;
-    gated_attn_item<DH, HPW, NWAVE>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept, hq,
-                                    hkv, groups_y, hg, n_real - 1 - rank, gain, temp, sm_scale,
-                                    lse2, sk, sv);
-    __syncthreads();                               // LDS buffers are reused by the next slot
+  if constexpr (!SPLIT) {
+    for (int64_t round = 0;; ++round) {
+      const int64_t rank = round * pj + ((round & 1) ? pj - 1 - jb : jb);
+      if (rank >= n_real) break;
+      gated_attn_item<DH, HPW, NWAVE, false>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq,
+                                             t_kept, hq, hkv, groups_y, hg, n_real - 1 - rank,
+                                             gain, temp, sm_scale, lse2, sk, sv, 0, 1, 0, nullptr,
+                                             nullptr);
+      __syncthreads();                             // LDS buffers are reused by the next slot
+    }
+  } else {
+    // ---- the split form: the items attn_plan listed (a query block, or one
+    // key chunk of a long one, coded slot * 8 + chunk), largest first, dealt
+    // to the head group's workgroups in snake order
+    const int64_t n_it = plan[0];
+    const int* __restrict__ list = plan + 64;
+    for (int64_t round = 0;; ++round) {
+      const int64_t r = round * pj + ((round & 1) ? pj - 1 - jb : jb);
+      if (r >= n_it) break;
+      const int code = list[r];
+      gated_attn_item<DH, HPW, NWAVE, true>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept,
+                                            hq, hkv, groups_y, hg, code >> 3, gain, temp, sm_scale,
+                                            lse2, sk, sv, chunk_tiles, c_max, code & 7, ws_o,
+                                            ws_ml);
+      __syncthreads();                               // LDS buffers are reused by the next item
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// The plan of a split launch, one workgroup: every query block's items (the
+// block, or its key chunks as gated_attn_item cuts them), sorted by their
+// key tiles, largest first (a counting sort; items of one size in no fixed
+// order, which changes only which workgroup runs them), and the list of
+// split blocks for the merge.  plan[0] = items, plan[1] = split blocks;
+// plan + 64 the items; splits[i] = (first row, rows, chunks) of split block i.
+// ---------------------------------------------------------------------------
+constexpr int kPlanBuckets = 4096;               // item sizes sorted exactly up to 4095 tiles
+
+__global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ kept_cu, int n_seq,
+                                                  int t_kept, int n_slots, int qb,
+                                                  int chunk_tiles, int c_max,
+                                                  int* __restrict__ plan,
+                                                  int4* __restrict__ splits) {
+  __shared__ int cnt[kPlanBuckets];
+  __shared__ int scan[1024];
+  __shared__ int n_split;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBuckets; i += 1024) cnt[i] = 0;
+  if (tid == 0) n_split = 0;
+  __syncthreads();
+  // key tiles of slot's query block (0: no work), its first row and rows
+  auto block_of = [&](int slot, int& row0, int& rows) -> int {
+    const int s = seq_of_slot(kept_cu, n_seq, slot, qb);
+    if (s < 0) return 0;
+    const int lo = kept_cu[s] < t_kept ? kept_cu[s] : t_kept;
+    const int len = (kept_cu[s + 1] < t_kept ? kept_cu[s + 1] : t_kept) - lo;
+    const int q0 = (int)(slot - slot0_of(kept_cu, s, qb)) * qb;
+    if (q0 >= len) return 0;
+    const int q_end = q0 + qb < len ? q0 + qb : len;
+    row0 = lo + q0;
+    rows = q_end - q0;
+    return (q_end + BKV - 1) / BKV;
+  };
+  auto chunks_of = [&](int n_all) {
+    if (n_all <= chunk_tiles) return 1;
+    const int c = (n_all + chunk_tiles - 1) / chunk_tiles;
+    return c < c_max ? c : c_max;
+  };
+  auto tiles_of = [&](int n_all, int j) {
+    const int t_lo = j * chunk_tiles;
+    return (j == c_max - 1 || n_all - t_lo <= chunk_tiles ? n_all : t_lo + chunk_tiles) - t_lo;
+  };
+  // bucket 0 holds the largest items
+  auto bucket = [&](int tiles) {
+    return kPlanBuckets - 1 - (tiles < kPlanBuckets - 1 ? tiles : kPlanBuckets - 1);
+  };
+  for (int slot = tid; slot < n_slots; slot += 1024) {
+    int row0 = 0, rows = 0;
+    const int n_all = block_of(slot, row0, rows);
+    if (n_all == 0) continue;
+    const int nc = chunks_of(n_all);
+    for (int j = 0; j < nc; ++j) atomicAdd(&cnt[bucket(tiles_of(n_all, j))], 1);
+  }
+  __syncthreads();
+  // exclusive prefix sums of the bucket counts: four buckets per thread,
+  // then a scan over the threads
+  int a[4], tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = cnt[4 * tid + i];
+    tot += a[i];
+  }
+  scan[tid] = tot;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int run = scan[tid] - tot;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cnt[4 * tid + i] = run;
+    run += a[i];
+  }
+  const int total = scan[1023];
+  __syncthreads();
+  int* __restrict__ list = plan + 64;
+  for (int slot = tid; slot < n_slots; slot += 1024) {
+    int row0 = 0, rows = 0;
+    const int n_all = block_of(slot, row0, rows);
+    if (n_all == 0) continue;
+    const int nc = chunks_of(n_all);
+    for (int j = 0; j < nc; ++j) list[atomicAdd(&cnt[bucket(tiles_of(n_all, j))], 1)] = slot * 8 + j;
+    if (nc > 1) splits[atomicAdd(&n_split, 1)] = make_int4(row0, rows, nc, 0);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    plan[0] = total;
+    plan[1] = n_split;
+  }
+}
+
+// The key chunks of the split query blocks merged, one wave per (row, head):
+// with each chunk's (m_c, l_c, O_c) (O_c unnormalised, both relative to
+// m_c), M = max m_c, w_c = 2^(m_c - M), O = sum w_c O_c / sum w_c l_c, and
+// the row's lse2 = M + log2(sum w_c l_c).  blockIdx.x: the split block (of
+// attn_plan's list), blockIdx.y: four (row, head) pairs of it.  All of a
+// pair's loads are issued before the first is used.
+constexpr int kMaxChunks = 8;
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ ws_o,
+                                                  const float2* __restrict__ ws_ml,
+                                                  const int* __restrict__ plan,
+                                                  const int4* __restrict__ splits, int t_kept,
+                                                  int hq, uint16_t* __restrict__ out,
+                                                  float* __restrict__ lse2) {
+  constexpr int PER = DH / 64;                     // dims per lane
+  if ((int)blockIdx.x >= plan[1]) return;
+  const int4 sp = splits[blockIdx.x];              // first row, rows, chunks
+  const int pair = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int r = pair / hq;
+  if (r >= sp.y) return;
+  const int head = pair % hq;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)sp.x + r;
+  const int nc = sp.z;
+  float2 ml[kMaxChunks];
+  float o[kMaxChunks][PER];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c < nc) {
+      const int64_t pr = ((int64_t)c * t_kept + row) * hq + head;
+      ml[c] = ws_ml[pr];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[c][i] = ws_o[pr * DH + PER * lane + i];
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (c < nc) M = fmaxf(M, ml[c].x);
+  float L = 0.0f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c < nc) {
+      const float w = ml[c].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[c].x - M);
+      L = fmaf(w, ml[c].y, L);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, o[c][i], acc[i]);
+    }
+  }
+  const float inv = 1.0f / L;
+  uint16_t* op = out + (row * hq + head) * DH + PER * lane;
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    op[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
+  }
+  if (lse2 && lane == 0) lse2[(int64_t)head * t_kept + row] = M + __log2f(L);
+}
+
+// How tg_gated_attn_split divides the keys: query blocks of more than
+// chunk_tiles key tiles are split into chunks of chunk_tiles tiles (at most
+// c_max of them, the last running to the block's end).  chunk_tiles is 1.5
+// times the key tiles per workgroup of a head group when the sequences are
+// as long as max_len allows (the causal work is largest then): fewer, larger
+// chunks than an even share, since every item also pays a fixed cost (its
+// queries and first key tile) and a split row pays the merge.  Workgroups
+// are counted for a full 256-CU gfx950 whatever the device reports: the
+// plan's shape, the workspace size and the results depend on the sizes
+// alone.
+// Chunks are at least kMinChunkTiles tiles, and only blocks of at least
+// twice that many are split: below, the plan and the merge cost more than
+// the shorter critical path saves (measured at 522 and 826 kept rows).
+struct SplitPlan {
+  int chunk_tiles;     // key tiles per chunk (kNoSplit: no block is split)
+  int c_max;           // chunks of the longest block (1: no partial results)
+};
+constexpr int kNoSplit = 1 << 30;
+constexpr int kMinChunkTiles = 8;
+
+// workspace layout of the split form (byte offsets, each 256-aligned)
+struct SplitLayout {
+  size_t list, splits, o, ml, total;
+};
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+SplitLayout split_layout(int64_t t_kept, int64_t n_slots, int c_max, int hq, int dh) {
+  SplitLayout l{};
+  l.list = 0;                                              // 64 header ints + the items
+  l.splits = round256((64 + (size_t)n_slots * c_max) * 4);
+  l.o = l.splits + round256((size_t)n_slots * 16);
+  l.ml = l.o + (c_max > 1 ? (size_t)c_max * t_kept * hq * dh * 4 : 0);
+  l.total = l.ml + (c_max > 1 ? (size_t)c_max * t_kept * hq * 8 : 0);
+  return l;
 }
 
 template <int DH, int HPW, int NWAVE>
 hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                       const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,
                       int n_seq, int hq, int hkv, const float* gain, const float* temp,
-                      float sm_scale, float* lse2, hipStream_t st) {
+                      float sm_scale, float* lse2, const SplitPlan* sp, void* ws,
+                      hipStream_t st) {
   constexpr int QB = AttnCfg<DH, HPW, NWAVE>::QB;
   const int G = hq / hkv;
   const int groups_y = G / HPW;
@@ -529,34 +785,113 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
   int n_cu = 0;
   const hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
+  const int c_max = sp ? sp->c_max : 1;
+  const int chunk_tiles = sp && sp->c_max > 1 ? sp->chunk_tiles : kNoSplit;
+  const int64_t n_items = n_slots * c_max;
   int64_t pj = n_cu / n_hg;
   if (pj < 1) pj = 1;
-  if (pj > n_slots) pj = n_slots;
+  if (pj > n_items) pj = n_items;
   const int64_t blocks = (int64_t)n_hg * pj;
-  if (n_slots > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (n_items > 0x7fffffff / 8 || blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gated_attn_bf16<DH, HPW, NWAVE>), dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st,
+  int* plan = nullptr;
+  int4* splits = nullptr;
+  float* ws_o = nullptr;
+  float2* ws_ml = nullptr;
+  if (sp) {
+    const SplitLayout l = split_layout(t_kept, n_slots, c_max, hq, DH);
+    char* base = static_cast<char*>(ws);
+    plan = reinterpret_cast<int*>(base + l.list);
+    splits = reinterpret_cast<int4*>(base + l.splits);
+    if (c_max > 1) {
+      ws_o = reinterpret_cast<float*>(base + l.o);
+      ws_ml = reinterpret_cast<float2*>(base + l.ml);
+    }
+    hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, st, kept_cu, n_seq, (int)t_kept,
+                       (int)n_slots, QB, chunk_tiles, c_max, plan, splits);
+  }
+  auto kern = sp ? gated_attn_bf16<DH, HPW, NWAVE, true> : gated_attn_bf16<DH, HPW, NWAVE, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NWAVE), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), kept_b, kept_pos,
                      kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, (int)n_slots, gain, temp,
-                     sm_scale, lse2);
+                     sm_scale, lse2, chunk_tiles, c_max, plan, ws_o, ws_ml);
+  if (ws_o) {
+    const int64_t gy = ((int64_t)QB * hq + 3) / 4;
+    if (gy > 65535 || n_slots > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_merge<DH>), dim3((unsigned)n_slots, (unsigned)gy), dim3(256), 0, st,
+                       ws_o, ws_ml, plan, splits, (int)t_kept, hq, static_cast<uint16_t*>(out),
+                       lse2);
+  }
   return hipGetLastError();
+}
+
+// query rows per workgroup of the configuration launch_attn_bf16 picks
+int attn_qb(int hq, int hkv) {
+  const int G = hq / hkv;
+  const int hpw = G >= 4 ? 4 : G;
+  return kAttnWaves * QW / hpw;
+}
+
+// key tiles of one sequence of n rows over its query blocks of qb rows
+int64_t causal_tiles(int64_t n, int64_t qb) {
+  if (n <= 0) return 0;
+  const int64_t nb = (n + qb - 1) / qb;
+  // blocks 0 .. nb-2 are full: block i reaches (i + 1) qb / BKV tiles
+  return qb / BKV * (nb - 1) * nb / 2 + (n + BKV - 1) / BKV;
+}
+
+SplitPlan split_plan(int64_t t_kept, int n_seq, int max_len, int hq, int hkv) {
+  constexpr int n_cu = 256;
+  const int G = hq / hkv;
+  const int hpw = G >= 4 ? 4 : G;
+  const int n_hg = hkv * (G / hpw);
+  SplitPlan p{kNoSplit, 1};
+  const int64_t qb = attn_qb(hq, hkv);
+  const int64_t ml = max_len < 1 ? 1 : (max_len < t_kept ? max_len : (t_kept > 0 ? t_kept : 1));
+  // the most causal work t_kept rows in n_seq sequences of at most ml rows
+  // can hold: as many full-length sequences as fit, then the rest
+  int64_t n_full = t_kept / ml;
+  if (n_full > n_seq) n_full = n_seq;
+  const int64_t rest = t_kept - n_full * ml;
+  const int64_t work = n_full * causal_tiles(ml, qb) + (n_full < n_seq ? causal_tiles(rest, qb) : 0);
+  int64_t pj = n_cu / n_hg;
+  if (pj < 1) pj = 1;
+  int64_t per = (3 * work + 2 * pj - 1) / (2 * pj);
+  const int64_t max_tiles = (ml + BKV - 1) / BKV;
+  if (per < (max_tiles + kMaxChunks - 1) / kMaxChunks) per = (max_tiles + kMaxChunks - 1) / kMaxChunks;
+  if (per < kMinChunkTiles) per = kMinChunkTiles;
+  if (per >= max_tiles || max_tiles < 2 * kMinChunkTiles) return p;
+  p.chunk_tiles = (int)per;
+  p.c_max = (int)((max_tiles + per - 1) / per);
+  return p;
 }
 
 }  // namespace
 
+size_t attn_split_ws_bytes(int64_t t_kept, int n_seq, int max_len, int hq, int hkv, int dh) {
+  const SplitPlan p = split_plan(t_kept, n_seq, max_len, hq, hkv);
+  const int64_t n_slots = n_seq + (t_kept + attn_qb(hq, hkv) - 1) / attn_qb(hq, hkv);
+  return split_layout(t_kept, n_slots, p.c_max, hq, dh).total;
+}
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, int64_t t_kept,
                             const float* kept_b, const int32_t* kept_pos, const int32_t* kept_cu,
                             int n_seq, int max_len, int hq, int hkv, int dh, const float* gain,
-                            const float* temp, float sm_scale, float* lse2, hipStream_t st) {
-  (void)max_len;
+                            const float* temp, float sm_scale, float* lse2, hipStream_t st,
+                            void* ws) {
   if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)dh);
+  SplitPlan plan{};
+  if (ws) plan = split_plan(t_kept, n_seq, max_len, hq, hkv);
+  // one sequence with no block split: its blocks already run largest first
+  // (the plain launch's order), so the plan is skipped
+  const SplitPlan* pp = ws && (plan.c_max > 1 || n_seq > 1) ? &plan : nullptr;
   const int G = hq / hkv;
   const int hpw = G >= 4 ? 4 : G;
 #define TG_ATTN(DHv, HPWv)                                                                     \
   if (dh == DHv && hpw == HPWv)                                                                \
     return launch_cfg<DHv, HPWv, kAttnWaves>(q, k, v, out, t_kept, kept_b, kept_pos, kept_cu, n_seq, hq, \
-                                 hkv, gain, temp, sm_scale, lse2, st);
+                                 hkv, gain, temp, sm_scale, lse2, pp, ws, st);
   TG_ATTN(128, 1) TG_ATTN(128, 2) TG_ATTN(128, 4)
   TG_ATTN(64, 1) TG_ATTN(64, 2) TG_ATTN(64, 4)
 #undef TG_ATTN

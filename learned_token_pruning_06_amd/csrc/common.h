@@ -233,11 +233,16 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
 
 // lse2 (optional, [hq][t_kept]): each row's log2-sum-exp of its scaled
 // logits, the statistic the backward recomputes otherwise
+// ws (optional, attn_split_ws_bytes): with it the workgroups draw their
+// query blocks from a work counter, and blocks with more key tiles than a
+// workgroup's share are split into key chunks whose partial results a second
+// launch merges
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out,
                             int64_t t_kept, const float* kept_b, const int32_t* kept_pos,
                             const int32_t* kept_cu, int n_seq, int max_len, int hq, int hkv,
                             int dh, const float* gain, const float* temp, float sm_scale,
-                            float* lse2, hipStream_t st);
+                            float* lse2, hipStream_t st, void* ws = nullptr);
+size_t attn_split_ws_bytes(int64_t t_kept, int n_seq, int max_len, int hq, int hkv, int dh);
 
 hipError_t launch_attn_f32(const void* q, const void* k, const void* v, void* out,
                            int64_t t_kept, const float* kept_b, const int32_t* kept_pos,

@@ -247,11 +247,14 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
                kept_pos: Optional[torch.Tensor], kept_cu: torch.Tensor, gain: torch.Tensor,
                temp: torch.Tensor, max_len: Optional[int] = None,
                sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-               lse2: Optional[torch.Tensor] = None):
+               lse2: Optional[torch.Tensor] = None, split: bool = False,
+               ws: Optional[torch.Tensor] = None):
     """tg_gated_attn: token-gated causal attention, q [T,Hq,dh], k/v [T,Hkv,dh].
     lse2 (optional, f32 [Hq, T], bf16 only) receives each row's softmax
     normaliser in base 2, which gated_attn_bwd can take instead of
-    recomputing it."""
+    recomputing it.  split=True calls tg_gated_attn_split (bf16 only), which
+    splits the keys of each query block over workgroups when the query
+    blocks are too few; ws is its workspace (allocated when omitted)."""
     lib = load()
     _need(q, "q", (torch.bfloat16, torch.float32), 3)
     _need(k, "k", q.dtype, 3)
@@ -271,8 +274,20 @@ def gated_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kept_b: torch.
     if out is None:
         out = torch.empty_like(q)
     n_seq = kept_cu.numel() - 1
+    ml = int(max_len if max_len else t)
+    if split:
+        nbytes = lib.tg_gated_attn_split_workspace_size(t, n_seq, ml, hq, hkv, dh)
+        if ws is None and nbytes > 0:
+            ws = workspace(nbytes, q.device)
+        st = lib.tg_gated_attn_split(_p(q), _p(k), _p(v), _DT[q.dtype], _p(out), t, _p(kept_b),
+                                     _p(kept_pos), _p(kept_cu), n_seq, ml, hq, hkv, dh, _p(gain),
+                                     _p(temp), float(sm_scale or 0.0), _p(lse2), _p(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(q.device))
+        check("tg_gated_attn_split", st)
+        return out
     st = lib.tg_gated_attn(_p(q), _p(k), _p(v), _DT[q.dtype], _p(out), t, _p(kept_b),
-                           _p(kept_pos), _p(kept_cu), n_seq, int(max_len if max_len else t), hq, hkv,
+                           _p(kept_pos), _p(kept_cu), n_seq, ml, hq, hkv,
                            dh, _p(gain), _p(temp), float(sm_scale or 0.0), _p(lse2),
                            _stream(q.device))
     check("tg_gated_attn", st)

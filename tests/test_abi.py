@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declarations_are_exported(lib):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
         assert name in lib_mod.PROTOTYPES, f"{name} has no Python prototype"
@@ -202,6 +202,37 @@ def test_attn_validation(lib):
     assert at(gain=None) == 1
     assert at(q=ctypes.c_void_p(0x10008)) == 2
     assert at(t=0) == 0                                # empty: nothing launched
+
+
+def test_attn_split_validation(lib):
+    ws_size = lib.tg_gated_attn_split_workspace_size
+    per_row = 16 * (128 * 4 + 8)        # one chunk's partial results of a row
+    # long inputs: no block outweighs a workgroup's share, so the workspace
+    # holds the plan alone (a few bytes per query block), no partial results
+    for t in (131072, 8704):
+        assert 0 < ws_size(t, 1, t, 16, 8, 128) < t * per_row // 64
+    assert ws_size(-1, 1, 10, 16, 8, 128) == 0
+    assert ws_size(100, 1, 100, 16, 8, 96) == 0
+    # a short input splits its longest blocks: the partial results of at
+    # least two chunks per row
+    small = ws_size(2496, 1, 2496, 16, 8, 128)
+    assert small >= 2 * 2496 * per_row
+
+    def sp(dt=1, t=2496, ml=2496, dh=128, ws=FAKE, nbytes=None, lse2=None):
+        if nbytes is None:
+            nbytes = ws_size(t, 1, ml, 16, 8, dh)
+        return lib.tg_gated_attn_split(FAKE, FAKE, FAKE, dt, FAKE, t, FAKE, FAKE, FAKE, 1, ml, 16,
+                                       8, dh, FAKE, FAKE, 0.0, lse2, ws, nbytes, None)
+    assert sp(dt=0) == 2                               # bf16 only
+    assert sp(dt=3) == 1
+    assert sp(t=-1) == 1
+    assert sp(ws=None) == 3                            # workspace needed, none given
+    assert sp(nbytes=small - 1) == 3                   # workspace too small
+    assert sp(ws=ctypes.c_void_p(0x10080)) == 2        # workspace not 256-byte aligned
+    assert sp(dh=96) == 2
+    assert sp(lse2=ctypes.c_void_p(0x10002)) == 2      # misaligned lse2
+    assert sp(t=0, ml=0) == 0                          # empty: nothing launched
+    assert 0 < ws_size(0, 1, 0, 16, 8, 128) < 4096
 
 
 def test_qkv_proj_validation(lib):
