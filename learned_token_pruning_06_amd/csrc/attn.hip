@@ -424,11 +424,12 @@ __device__ __forceinline__ void gated_attn_item(
   const bool lag = wv >= NWAVE / 2;
   // t counts the chunk's tiles from 0; its key tile is t_lo + t, and the
   // wave needs the first wt of them
+  // (n_tiles >= 1: an item has at least one key tile.  The first tile is
+  // loaded and stored unconditionally, so the Q fragment loads above are
+  // complete on every path into the loop and the loop waits for none of them.)
   const int wt = w_tiles - t_lo;
-  if (n_tiles > 0) {
-    load_tile(t_lo);
-    store_tile(B0{});
-  }
+  load_tile(t_lo);
+  store_tile(B0{});
   __syncthreads();
   auto step = [&](auto BC, auto BP, auto BN, int t) {
     if (t + 1 < n_tiles) load_tile(t_lo + t + 1);
@@ -459,7 +460,7 @@ __device__ __forceinline__ void gated_attn_item(
     step(B2{}, B1{}, B0{}, t + 2);
   }
   // t == n_tiles here; the lagging waves still owe P.V of the last tile
-  if (lag && n_tiles > 0 && n_tiles - 1 < wt) {
+  if (lag && n_tiles - 1 < wt) {
     const int bl = (n_tiles - 1) % 3;
     if (bl == 0)
       phase_pv(B0{});
