@@ -79,9 +79,12 @@ def mfma_counters_for(kernel: str, src_files):
 
 def budget_sweep(g, dev, reps=10):
     """The 32k budget sweep: for each of the 8 drawn budgets, tg_select_topk on
-    the preset scores, tg_gather of the kept rows and tg_gated_attn over them
+    the preset scores, tg_gather of the kept rows and the attention over them
     (Q/K/V: seeded stand-ins of the kept shape; the attention's cost depends
-    only on the shapes).  Mean us per call over `reps` back-to-back calls."""
+    only on the shapes).  attn_us is tg_gated_attn_split, the path the step
+    takes (it splits the keys of long query blocks when the blocks are too
+    few for the GPU); attn_plain_us is tg_gated_attn.  Mean us per call over
+    `reps` back-to-back calls (the attention: the lower of two such means)."""
     import numpy as np
     import torch
     from learned_token_pruning_06_amd import ops
@@ -126,10 +129,22 @@ def budget_sweep(g, dev, reps=10):
         o = torch.empty_like(q)
         t_sel = time_it(lambda: ops.select_topk(b, pr, cu, kdev, tk, ki, kp, kb, kc, ws))
         t_gat = time_it(lambda: ops.gather(x, ki, out=xk))
-        t_att = time_it(lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=tk, out=o))
+        ws_a = ops.workspace(
+            lib.tg_gated_attn_split_workspace_size(tk, 1, tk, wl.hq, wl.hkv, wl.dh), dev)
+        # the two attention forms alternate, twice each; each takes the lower
+        # of its two batch means (a clock that is still ramping up would
+        # otherwise favour whichever runs second)
+        ta, tp = [], []
+        for _ in range(2):
+            ta.append(time_it(lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=tk,
+                                                     out=o, split=True, ws=ws_a)))
+            tp.append(time_it(lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=tk,
+                                                     out=o)))
+        t_att, t_pl = min(ta), min(tp)
         fl = 2.0 * wl.dh * wl.hq * tk * (tk + 1)
         rows.append({"k": K, "t_kept": int(tk), "select_us": round(t_sel, 2),
                      "gather_us": round(t_gat, 2), "attn_us": round(t_att, 2),
+                     "attn_plain_us": round(t_pl, 2),
                      "attn_tflops": round(fl / (t_att * 1e-6) / 1e12, 1),
                      "attn_frac_of_bf16_peak": round(fl / (t_att * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)})
     del q_all, k_all, v_all, x
@@ -263,6 +278,11 @@ def main():
     w_all = tb(np.ascontiguousarray(np.concatenate([g["wq"].T, g["wk"].T, g["wv"].T], axis=0)))
     q, k, v = ops.qkv_proj(x_kept, w_all, wl.hq, wl.hkv, wl.dh)
     o = torch.empty_like(q)
+    # the attention takes tg_gated_attn_split: with one long sequence (the
+    # 128k layer) it is the plain launch; short or ragged inputs get their
+    # work planned and the keys of long query blocks split
+    ws_a = ops.workspace(lib.tg_gated_attn_split_workspace_size(t_kept, n_seq, max_kept, wl.hq,
+                                                                wl.hkv, wl.dh), dev)
     torch.cuda.synchronize()
     assert int(kept_cu[-1].item()) == t_kept
 
@@ -280,7 +300,8 @@ def main():
         ops.gather(x, kept_idx, out=x_kept)
         if ev is not None:
             ev[3].record()
-        ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=max_kept, out=o)
+        ops.gated_attn(q, k, v, kept_b, kept_pos, kept_cu, gain, temp, max_len=max_kept, out=o,
+                       split=True, ws=ws_a)
         if ev is not None:
             ev[4].record()
 
