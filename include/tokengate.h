@@ -231,6 +231,10 @@ tg_status tg_gated_attn(const void* q, const void* k, const void* v, tg_dtype dt
  *     call), 256-byte aligned: the plan (a few bytes per query block) and,
  *     when blocks are split, the partial results.  Calls that share a
  *     workspace must not overlap.
+ * max_kept_seqlen steers the split (how long a chunk is, how many a block
+ *     may have); with a wrong one the results are still the attention (a
+ *     block longer than planned has its last chunk run to its end), only
+ *     the balance suffers.
  * How blocks are split depends on the sizes alone (it is planned for a
  * 256-CU gfx950), so results are bitwise reproducible; rows of split blocks
  * differ from tg_gated_attn's in the last bits (the merge's order of

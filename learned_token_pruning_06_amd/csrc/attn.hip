@@ -735,23 +735,27 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ ws_o
 
 // How tg_gated_attn_split divides the keys: query blocks of more than
 // chunk_tiles key tiles are split into chunks of chunk_tiles tiles (at most
-// c_max of them, the last running to the block's end).  chunk_tiles is 1.5
-// times the key tiles per workgroup of a head group when the sequences are
-// as long as max_len allows (the causal work is largest then): fewer, larger
-// chunks than an even share, since every item also pays a fixed cost (its
-// queries and first key tile) and a split row pays the merge.  Workgroups
-// are counted for a full 256-CU gfx950 whatever the device reports: the
-// plan's shape, the workspace size and the results depend on the sizes
-// alone.
-// Chunks are at least kMinChunkTiles tiles, and only blocks of at least
-// twice that many are split: below, the plan and the merge cost more than
-// the shorter critical path saves (measured at 522 and 826 kept rows).
+// c_max of them, the last running to the block's end).  chunk_tiles is a
+// workgroup's share of the causal work (key tiles per workgroup of a head
+// group when the sequences are as long as max_len allows, where the work is
+// largest), so that, sorted largest first, the items fill the workgroups
+// evenly.  Nothing is split when the longest block exceeds that share by
+// less than a quarter: the plan and the merge then cost more than the
+// shorter critical path saves (measured at 7000 kept rows: 110 tiles against
+// a share of 96).  Workgroups are counted for a full 256-CU gfx950 whatever
+// the device reports: the plan's shape, the workspace size and the results
+// depend on the sizes alone.
+// Chunks are at least kMinChunkTiles tiles, and only inputs whose longest
+// block has kMinSplitTiles tiles or more are split: below, the plan and the
+// merge cost more than the shorter critical path saves (measured at 522,
+// 826 and 1100 kept rows).
 struct SplitPlan {
   int chunk_tiles;     // key tiles per chunk (kNoSplit: no block is split)
   int c_max;           // chunks of the longest block (1: no partial results)
 };
 constexpr int kNoSplit = 1 << 30;
 constexpr int kMinChunkTiles = 8;
+constexpr int kMinSplitTiles = 20;
 
 // workspace layout of the split form (byte offsets, each 256-aligned)
 struct SplitLayout {
@@ -858,11 +862,13 @@ SplitPlan split_plan(int64_t t_kept, int n_seq, int max_len, int hq, int hkv) {
   const int64_t work = n_full * causal_tiles(ml, qb) + (n_full < n_seq ? causal_tiles(rest, qb) : 0);
   int64_t pj = n_cu / n_hg;
   if (pj < 1) pj = 1;
-  int64_t per = (3 * work + 2 * pj - 1) / (2 * pj);
+  const int64_t share = (work + pj - 1) / pj;
   const int64_t max_tiles = (ml + BKV - 1) / BKV;
+  if (max_tiles < kMinSplitTiles || 4 * max_tiles <= 5 * share) return p;
+  int64_t per = share;
   if (per < (max_tiles + kMaxChunks - 1) / kMaxChunks) per = (max_tiles + kMaxChunks - 1) / kMaxChunks;
   if (per < kMinChunkTiles) per = kMinChunkTiles;
-  if (per >= max_tiles || max_tiles < 2 * kMinChunkTiles) return p;
+  if (per >= max_tiles) return p;
   p.chunk_tiles = (int)per;
   p.c_max = (int)((max_tiles + per - 1) / per);
   return p;

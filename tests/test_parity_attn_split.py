@@ -66,13 +66,13 @@ def _check_lse2(got, case, tag, sm_scale=None):
 SPLIT_CASES = [
     # seed, kept lengths, hq, hkv, dh (chunk tiles and chunks of the longest
     # block, as planned)
-    (41, [2496], 16, 8, 128),                   # 20 x 2
+    (41, [2496], 16, 8, 128),                   # 14 x 3
     (42, [1, 5, 31, 64, 65, 1300], 16, 8, 128),  # short sequences unsplit, 8 x 3
-    (43, [2496], 8, 8, 128),                    # MHA, 11 x 4
+    (43, [2496], 8, 8, 128),                    # MHA, 8 x 5
     (44, [1800, 0, 77], 4, 1, 64),              # 4 query heads per KV head, dh 64, 8 x 4
-    (45, [2000, 333], 32, 4, 128),              # 8 query heads per KV head, 26 x 2
-    (46, [1100], 16, 8, 128),                   # a budget of the sweep, 8 x 3
-    (47, [1600, 64, 129], 16, 8, 128),          # 9 x 3, last chunk shorter
+    (45, [2000, 333], 32, 4, 128),              # 8 query heads per KV head, 18 x 2
+    (46, [1400], 16, 8, 128),                   # 8 x 3
+    (47, [1600, 64, 129], 16, 8, 128),          # 8 x 4, last chunk shorter
 ]
 
 
@@ -130,18 +130,35 @@ def test_split_leaves_rows_past_the_last_sequence():
     """Rows past kept_cu[n_seq] are left alone, as by tg_gated_attn."""
     from learned_token_pruning_06_amd import ops
     say("attn split: 40 rows past the last sequence untouched")
-    q, k, v, kb, pos, kc, gain, temp = synth_case(50, [1200, 40], 16, 8, 128, "bf16")
+    q, k, v, kb, pos, kc, gain, temp = synth_case(50, [1400, 40], 16, 8, 128, "bf16")
     kc_short = kc[:-1]                                # the 40 rows of the last length dropped
-    assert _has_partials(_ws_bytes(1240, 1, 1200, 16, 8, 128), 1240, 16, 128)
+    assert _has_partials(_ws_bytes(1440, 1, 1400, 16, 8, 128), 1440, 16, 128)
     args = list(_dev_args(q, k, v, kb, pos, kc_short, gain, temp))
     out = torch.full_like(args[0], 7.0)
-    ops.gated_attn(*args, max_len=1200, out=out, split=True)
+    ops.gated_attn(*args, max_len=1400, out=out, split=True)
     torch.cuda.synchronize()
-    tail = out[1200:].float()
+    tail = out[1400:].float()
     assert torch.all(tail == 7.0)
-    want = O.ref_gated_attn(q[:1200], k[:1200], v[:1200], kb[:1200], pos[:1200], kc_short, gain,
+    want = O.ref_gated_attn(q[:1400], k[:1400], v[:1400], kb[:1400], pos[:1400], kc_short, gain,
                             temp)
-    check_attn(to_f64(out[:1200]), want, "bf16", "split, head rows")
+    check_attn(to_f64(out[:1400]), want, "bf16", "split, head rows")
+
+
+def test_split_with_max_len_understated():
+    """max_kept_seqlen below a sequence's real length (a broken promise): the
+    split is planned for the stated length, so the long sequence's blocks
+    have more key tiles than the planned chunks cover and the last chunk
+    runs to the block's end.  The result must still be the attention."""
+    from learned_token_pruning_06_amd import ops
+    say("attn split: max_len 1300 stated for a 2600-row sequence")
+    c = synth_case(52, [300, 2600], 16, 8, 128, "bf16")
+    t = 2900
+    assert _has_partials(_ws_bytes(t, 2, 1300, 16, 8, 128), t, 16, 128)
+    out = ops.gated_attn(*_dev_args(*c), max_len=1300, split=True)
+    torch.cuda.synchronize()
+    q, k, v, kb, pos, kc, gain, temp = c
+    check_attn(to_f64(out), O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp), "bf16",
+               "split, understated max_len")
 
 
 @pytest.mark.parametrize("lens", [[20000], [589, 1602, 3141, 7048], [700, 333, 5, 64]],
