@@ -316,13 +316,29 @@ void bwdm_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int v = g ^ ((n >> 2) & 3);
         const int row = (32 * qh + n) * LD;
         const int e0 = row + 8 * v, e1 = row + 8 * (v ^ 2);
+        // product m: S' (even m, Q row) or dP (odd m, dO row) of K-step m / 2;
+        // its A operand is read four products ahead, the order pinned by
+        // scheduling barriers (one wave per SIMD: nothing else hides the
+        // LDS latency)
+        auto opnd = [&](int m) {
+          const int st = m >> 1;
+          return ld16(((m & 1) ? ot : qt) + ((st & 1) ? e1 : e0) + 32 * (st >> 1));
+        };
+        constexpr int NM = 2 * KS;
+        u32x4 ra[4];
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const int o = ((st & 1) ? e1 : e0) + 32 * (st >> 1);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(qt + o)), as_bf16x8(kf[st]),
-                                                         sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(ot + o)), as_bf16x8(vf[st]),
-                                                         pacc, 0, 0, 0);
+        for (int m = 0; m < 4; ++m) ra[m] = opnd(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m & 1)
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[m % 4]),
+                                                           as_bf16x8(vf[m >> 1]), pacc, 0, 0, 0);
+          else
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[m % 4]),
+                                                           as_bf16x8(kf[m >> 1]), sacc, 0, 0, 0);
+          if (m + 4 < NM) ra[m % 4] = opnd(m + 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // element j: query qb + 8(j/4) + 4g + j%4, key kw0 + n; keys after the
@@ -368,20 +384,35 @@ void bwdm_kv(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int lrow = 4 * g + ((lane & 15) >> 2);
         const int t0 = lrow * LD + 8 * ((2 * h2 + (c >> 1)) ^ g) + 4 * (c & 1);
         const int t1 = (lrow + 8) * LD + 8 * ((2 * h2 + (c >> 1)) ^ g ^ 2) + 4 * (c & 1);
+        // product i: dV (even i, dO rows) or dK (odd i, Q rows) of K-step
+        // kk = (i / 2) / NDT, dims 32 d .. +32 with d = (i / 2) % NDT; its B
+        // operand is read four products ahead, as above
+        auto topnd = [&](int i) {
+          const int pd = i >> 1, kk = pd / NDT, d = pd % NDT;
+          const uint16_t* base = ((i & 1) ? qt : ot) + (32 * qh + 16 * kk) * LD + 32 * d;
+          const uint2 a = ld_tr4(base + t0), b = ld_tr4(base + t1);
+          return (u32x4){a.x, a.y, b.x, b.y};
+        };
+        const bf16x8 pa[2] = {as_bf16x8((u32x4){pw[0], pw[1], pw[2], pw[3]}),
+                              as_bf16x8((u32x4){pw[4], pw[5], pw[6], pw[7]})};
+        const bf16x8 da[2] = {as_bf16x8((u32x4){dw[0], dw[1], dw[2], dw[3]}),
+                              as_bf16x8((u32x4){dw[4], dw[5], dw[6], dw[7]})};
+        constexpr int NP = 4 * NDT;
+        u32x4 rb[4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 pa = as_bf16x8((u32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]});
-          const bf16x8 da = as_bf16x8((u32x4){dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]});
-          const int rk = (32 * qh + 16 * kk) * LD;
+        for (int i = 0; i < 4; ++i) rb[i] = topnd(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < NDT; ++d) {
-            const uint2 o0 = ld_tr4(ot + rk + t0 + 32 * d), o1 = ld_tr4(ot + rk + t1 + 32 * d);
-            const uint2 q0v = ld_tr4(qt + rk + t0 + 32 * d), q1v = ld_tr4(qt + rk + t1 + 32 * d);
-            aV[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                pa, as_bf16x8((u32x4){o0.x, o0.y, o1.x, o1.y}), aV[d], 0, 0, 0);
-            aK[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                da, as_bf16x8((u32x4){q0v.x, q0v.y, q1v.x, q1v.y}), aK[d], 0, 0, 0);
-          }
+        for (int i = 0; i < NP; ++i) {
+          const int pd = i >> 1, kk = pd / NDT, d = pd % NDT;
+          if (i & 1)
+            aK[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], as_bf16x8(rb[i % 4]), aK[d], 0,
+                                                            0, 0);
+          else
+            aV[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], as_bf16x8(rb[i % 4]), aV[d], 0,
+                                                            0, 0);
+          if (i + 4 < NP) rb[i % 4] = topnd(i + 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -538,13 +569,27 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int vv = g ^ ((n >> 2) & 3);
         const int row = (32 * kh + n) * LD;
         const int e0 = row + 8 * vv, e1 = row + 8 * (vv ^ 2);
+        // product m: S^T' (even m, K row) or dP^T (odd m, V row) of K-step
+        // m / 2, its A operand read four products ahead (as in bwdm_kv)
+        auto opnd = [&](int m) {
+          const int st = m >> 1;
+          return ld16(((m & 1) ? vt_ : kt_) + ((st & 1) ? e1 : e0) + 32 * (st >> 1));
+        };
+        constexpr int NM = 2 * KS;
+        u32x4 ra[4];
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const int o = ((st & 1) ? e1 : e0) + 32 * (st >> 1);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(kt_ + o)), as_bf16x8(qf[st]),
-                                                         sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ld16(vt_ + o)), as_bf16x8(of[st]),
-                                                         pacc, 0, 0, 0);
+        for (int m = 0; m < 4; ++m) ra[m] = opnd(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m & 1)
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[m % 4]),
+                                                           as_bf16x8(of[m >> 1]), pacc, 0, 0, 0);
+          else
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ra[m % 4]),
+                                                           as_bf16x8(qf[m >> 1]), sacc, 0, 0, 0);
+          if (m + 4 < NM) ra[m % 4] = opnd(m + 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // element j: key kb0 + 8(j/4) + 4g + j%4, query qi
@@ -607,16 +652,27 @@ void bwdm_q(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int lrow = 4 * g + ((lane & 15) >> 2);
         const int t0 = lrow * LD + 8 * ((2 * h2 + (cc >> 1)) ^ g) + 4 * (cc & 1);
         const int t1 = (lrow + 8) * LD + 8 * ((2 * h2 + (cc >> 1)) ^ g ^ 2) + 4 * (cc & 1);
+        // product i: K-step kk = i / NDT, dims 32 d .. +32 with d = i % NDT;
+        // its B operand read four products ahead
+        auto topnd = [&](int i) {
+          const int kk = i / NDT, d = i % NDT;
+          const uint16_t* base = kt_ + (32 * kh + 16 * kk) * LD + 32 * d;
+          const uint2 a = ld_tr4(base + t0), b = ld_tr4(base + t1);
+          return (u32x4){a.x, a.y, b.x, b.y};
+        };
+        const bf16x8 da[2] = {as_bf16x8((u32x4){dw[0], dw[1], dw[2], dw[3]}),
+                              as_bf16x8((u32x4){dw[4], dw[5], dw[6], dw[7]})};
+        constexpr int NP = 2 * NDT;
+        u32x4 rb[4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 da = as_bf16x8((u32x4){dw[4 * kk], dw[4 * kk + 1], dw[4 * kk + 2], dw[4 * kk + 3]});
-          const int rk = (32 * kh + 16 * kk) * LD;
+        for (int i = 0; i < 4; ++i) rb[i] = topnd(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < NDT; ++d) {
-            const uint2 k0v = ld_tr4(kt_ + rk + t0 + 32 * d), k1v = ld_tr4(kt_ + rk + t1 + 32 * d);
-            aQ[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                da, as_bf16x8((u32x4){k0v.x, k0v.y, k1v.x, k1v.y}), aQ[d], 0, 0, 0);
-          }
+        for (int i = 0; i < NP; ++i) {
+          aQ[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[i / NDT], as_bf16x8(rb[i % 4]),
+                                                                aQ[i % NDT], 0, 0, 0);
+          if (i + 4 < NP) rb[i % 4] = topnd(i + 4);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
