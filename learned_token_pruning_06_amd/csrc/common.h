@@ -186,9 +186,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* out,
 
 size_t score_bwd_ws_bytes(int64_t t, int n_seq, int d, int h);
 hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const void* w1,
-                           const float* b1, const float* w2, const float* dbt, void* dz, void* dzt,
-                           int64_t ldt, float* dw2p, float* db1p, float* db2p, float norm_eps,
-                           float* rowc, int64_t* blocks, hipStream_t st);
+                           const float* b1, const float* w2, const float* dbt, void* dz,
+                           float* dw2p, float* db1p, float* db2p, float norm_eps, float* rowc,
+                           int64_t* blocks, hipStream_t st);
 int64_t score_dz_blocks(int64_t t_in, int n_cu);
 // rowc (optional, splits == 1 only): Y[m, n] -= rowc[m] * A[m, n] after the
 // product, A bf16 with rows lda elements apart (the LN2 term of the scorer's
@@ -197,11 +197,12 @@ hipError_t launch_gemm_abt_f32(const void* x, int64_t xs, int64_t m, const void*
                                int n, int64_t kdim, int splits, float* y, int64_t ldy,
                                hipStream_t st, const float* rowc = nullptr,
                                const void* a = nullptr, int64_t lda = 0);
-// The same with W stored K-major, W[k][n] (rows ldw elements apart, w_rows
-// valid rows): Y[m, n] = sum_k X[m, k] W[k, n] over each split's K range.
-hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const void* w,
-                                     int64_t ldw, int64_t w_rows, int n, int64_t kdim, int splits,
-                                     float* y, int64_t ldy, hipStream_t st);
+// Both operands stored K-major, A[k][m] (rows lda elements apart) and W[k][n]
+// (rows ldw apart), k_rows valid rows in each (later ones read as zeros):
+// Y[m, n] = sum_k A[k, m] W[k, n] over each split's K range; m <= 256.
+hipError_t launch_gemm_atb_kmajor_f32(const void* a, int64_t lda, int64_t m, const void* w,
+                                      int64_t ldw, int64_t k_rows, int n, int64_t kdim,
+                                      int splits, float* y, int64_t ldy, hipStream_t st);
 hipError_t launch_score_bwd(const void* x, int dt, int64_t xs, int64_t t, int d, int h,
                             const void* w1, const float* b1, const float* w2, const uint8_t* pr,
                             const int32_t* cu, int n_seq, float eps, float norm_eps,

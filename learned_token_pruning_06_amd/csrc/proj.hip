@@ -54,6 +54,11 @@ TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // the A operand, 8 consecutive k of one column, is two transposing reads
 // (ds_read_b64_tr_b16): within each 16-lane group, output element e of lane
 // i is element i % 4 of the 8 bytes that lane 4e + i / 4 addresses.
+// XROWS (with WROWS): X is stored K-major too, X[k][m] with rows xs elements
+// apart and the same w_rows valid rows, staged and read like W (the B
+// operand, 8 consecutive k of one row m of the product, by two transposing
+// reads).  Both operands of Y = X^T-as-stored . W then come straight from
+// token-major arrays, e.g. dW1 = dz^T x with dz [T][h] and x [T][d].
 // bf16 per K-major W row: the tile is read only by transposing 8-byte reads,
 // served 32 lanes (256 B) at a time over rows r = 0..3 at byte 32h + 8c, so
 // rows start 64 B apart mod 256 B (576 B) to keep the 32 addresses on
@@ -88,7 +93,8 @@ struct RowCorr {
   int64_t lda;
 };
 
-template <bool F32OUT, bool WROWS = false, bool QKE = false, bool CORR = false>
+template <bool F32OUT, bool WROWS = false, bool QKE = false, bool CORR = false,
+          bool XROWS = false>
 __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     const uint16_t* __restrict__ x, int64_t xs, int64_t t, int d,
     const uint16_t* __restrict__ w, int nq, int nkv, uint16_t* __restrict__ q,
@@ -98,9 +104,10 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   static_assert(F32OUT || !WROWS, "K-major W is for the fp32-output form");
   static_assert(!(F32OUT && QKE), "the q/k epilogue is for the bf16 form");
   static_assert(F32OUT || !CORR, "the row correction is for the fp32 form");
+  static_assert(WROWS || !XROWS, "K-major X goes with K-major W");
   __shared__ double s_turns[64];                  // QKE: rotation per position, in turns
   __shared__ float s_norm[2][128];                 // QKE: the q and k norm weights
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][XROWS ? kBK * kRowW : kTile * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][WROWS ? kBK * kRowW : kTile * kRow];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   int64_t w_bytes = (int64_t)kTile * ldw * 2;   // W rows of this tile (row-major W)
   if constexpr (F32OUT) {                        // this workgroup's K range
     const int64_t kb = (int64_t)bz * k_per;
-    x += kb;
+    x += XROWS ? kb * xs : kb;
     if constexpr (WROWS) {
       w += kb * ldw;
       w_bytes = ((w_rows - kb) < 0 ? 0 : (w_rows - kb)) * ldw * 2 - (int64_t)col0 * 2;
@@ -154,7 +161,11 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   // loaders: thread vector i covers row (tid / 8) + 64 i, 16-byte chunk tid % 8
   // of the K-step, for both X (rows of this tile) and W (its output features)
   const int lrow = tid >> 3, lch = tid & 7;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row0 * xs, (t - row0) * xs * 2);
+  // K-major X: the tile's columns row0 .. of the w_rows - kb valid k rows
+  const int64_t x_krows = XROWS ? (w_rows - (int64_t)bz * k_per) : 0;
+  const __amdgpu_buffer_rsrc_t rx =
+      XROWS ? make_rsrc(x + row0, (x_krows < 0 ? 0 : x_krows) * xs * 2 - row0 * 2)
+            : make_rsrc(x + row0 * xs, (t - row0) * xs * 2);
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(WROWS ? w + col0 : w + (int64_t)col0 * ldw, w_bytes);
   // K-major W: thread vector i covers k-row (tid / 32) + 16 i, 16-byte chunk tid % 32
@@ -162,25 +173,28 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
   int xoff[4], woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    xoff[i] = (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
+    xoff[i] = XROWS ? (int)(((int64_t)(wrow + 16 * i) * xs + 8 * wch) * 2)
+                    : (int)(((int64_t)(lrow + 64 * i) * xs + 8 * lch) * 2);
     woff[i] = WROWS ? (int)(((int64_t)(wrow + 16 * i) * ldw + 8 * wch) * 2)
                     : (int)(((int64_t)(lrow + 64 * i) * ldw + 8 * lch) * 2);
   }
   const int ldst = lrow * kRow + 8 * lch;
   const int wdst = WROWS ? wrow * kRowW + 8 * wch : ldst;
+  const int xdst = XROWS ? wdst : ldst;
   u32x4 xr[4], wr[4];
   auto fetch = [&](int k0) {
     const int wk = WROWS ? (int)(2 * (int64_t)k0 * ldw) : 2 * k0;
+    const int xk = XROWS ? (int)(2 * (int64_t)k0 * xs) : 2 * k0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + 2 * k0, 0, 0));
+      xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i] + xk, 0, 0));
       wr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + wk, 0, 0));
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st16(&sx[buf][ldst + 64 * i * kRow], xr[i]);
+      st16(&sx[buf][xdst + (XROWS ? 16 * i * kRowW : 64 * i * kRow)], xr[i]);
       st16(&sw[buf][wdst + (WROWS ? 16 * i * kRowW : 64 * i * kRow)], wr[i]);
     }
   };
@@ -206,12 +220,21 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     // K-major W: lane (m, g) needs k = 32g + 8s .. +8 of column 128ch + 32mt + m
     const uint16_t* wt = sw[buf] + (32 * g + ((lane & 15) >> 2)) * kRowW + 128 * ch +
                          16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // K-major X: lane (n, g) needs k = 32g + 8s .. +8 of row 64rg + 32i + n
+    const uint16_t* xt = sx[buf] + (32 * g + ((lane & 15) >> 2)) * kRowW + 64 * rg +
+                         16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     // operands of 16-wide substep s + 1 are read from LDS while the MFMAs of
     // substep s run: one read after each MFMA, the order pinned
     bf16x8 bo[2][2], ao[2][4];
     auto ld_op = [&](int s, int c, int i) {
       if (i < 2) {
-        bo[c][i] = as_bf16x8(ld16(xb + 32 * i * kRow + 8 * s));
+        if constexpr (XROWS) {
+          const uint2 lo = ld_tr4(xt + 8 * s * kRowW + 32 * i);
+          const uint2 hi = ld_tr4(xt + (8 * s + 4) * kRowW + 32 * i);
+          bo[c][i] = as_bf16x8((u32x4){lo.x, lo.y, hi.x, hi.y});
+        } else {
+          bo[c][i] = as_bf16x8(ld16(xb + 32 * i * kRow + 8 * s));
+        }
       } else if constexpr (WROWS) {
         const uint2 lo = ld_tr4(wt + 8 * s * kRowW + 32 * (i - 2));
         const uint2 hi = ld_tr4(wt + (8 * s + 4) * kRowW + 32 * (i - 2));
@@ -432,18 +455,19 @@ dim3 f32_grid(int64_t m, int n, int splits) {
   return dim3((unsigned)gx, (unsigned)(n / kTile), (unsigned)splits);
 }
 
-hipError_t launch_gemm_ab_kmajor_f32(const void* x, int64_t xs, int64_t m, const void* w,
-                                     int64_t ldw, int64_t w_rows, int n, int64_t kdim, int splits,
-                                     float* y, int64_t ldy, hipStream_t st) {
+hipError_t launch_gemm_atb_kmajor_f32(const void* a, int64_t lda, int64_t m, const void* w,
+                                      int64_t ldw, int64_t k_rows, int n, int64_t kdim,
+                                      int splits, float* y, int64_t ldy, hipStream_t st) {
   if (m == 0) return hipSuccess;
+  if (m > kTile) return hipErrorInvalidValue;     // one row tile: X's columns are the rows of Y
   int64_t k_per = (kdim + splits - 1) / splits;
   k_per = (k_per + kBK - 1) / kBK * kBK;
   const dim3 grid = f32_grid(m, n, splits);
   if (grid.x == 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_abt_bf16<true, true>), grid, dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(x), xs, m, (int)kdim,
+  hipLaunchKernelGGL((gemm_abt_bf16<true, true, false, false, true>), grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(a), lda, m, (int)kdim,
                      static_cast<const uint16_t*>(w), 0, 0, nullptr, nullptr, nullptr, ldw,
-                     (int)k_per, y, ldy, m * ldy, w_rows, QkEpi{});
+                     (int)k_per, y, ldy, m * ldy, k_rows, QkEpi{}, RowCorr{});
   return hipGetLastError();
 }
 

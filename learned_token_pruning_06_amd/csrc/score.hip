@@ -64,8 +64,6 @@ TG_DEVINL float silu_f(float v) {
 struct DzOut {                  // outputs of the backward epilogue (BWD)
   const float* dbt;             // [t_in] gradient at the raw scores
   uint16_t* dz;                 // [t_in][H] bf16
-  uint16_t* dzt;                // [H][ldt] bf16 (transposed)
-  int64_t ldt;
   float* dw2p;                  // [blocks][H] per-workgroup sums of dbt * SiLU(z)
   float* db1p;                  // [blocks][H] per-workgroup sums of dz
   float* db2p;                  // [blocks]    per-workgroup sums of dbt
@@ -73,7 +71,7 @@ struct DzOut {                  // outputs of the backward epilogue (BWD)
 };
 
 // Backward epilogue shared by the scorer kernels: z = acc + b1,
-// dz = dbt w2 SiLU'(z) (bf16, both layouts) and the workgroup's sums over its
+// dz = dbt w2 SiLU'(z) (bf16, [t_in][H]) and the workgroup's sums over its
 // rows of dbt SiLU(z) and dz for each hidden unit: in-lane over the two row
 // tiles, a reduce-scatter over the 32 row lanes (lane n ends with value pair
 // 2n, 2n + 1), then the RG row groups in order through LDS (red: [2][RG][H]
@@ -120,8 +118,6 @@ TG_DEVINL void dz_epilogue(floatx16 (&acc)[MTA][2], int nmt, int mt0, int rg, in
         }
         const uint16_t ua = __builtin_bit_cast(uint16_t, (__bf16)(NORM ? da * inv0 : da));
         const uint16_t ub = __builtin_bit_cast(uint16_t, (__bf16)(NORM ? db * inv1 : db));
-        if (ra < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + ra] = ua;
-        if (rb < t_in) bo.dzt[(int64_t)(h0 + e) * bo.ldt + rb] = ub;
         pa[e >> 1] |= (uint32_t)ua << (16 * (e & 1));
         pb[e >> 1] |= (uint32_t)ub << (16 * (e & 1));
       }
@@ -593,9 +589,9 @@ int64_t n_slots(int64_t t_in, int n_seq) { return (int64_t)n_seq + (t_in + CH - 
 // epilogue.  Returns the number of workgroups (the partial-sum rows)
 // through *blocks.
 hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const void* w1,
-                           const float* b1, const float* w2, const float* dbt, void* dz, void* dzt,
-                           int64_t ldt, float* dw2p, float* db1p, float* db2p, float norm_eps,
-                           float* rowc, int64_t* blocks, hipStream_t st) {
+                           const float* b1, const float* w2, const float* dbt, void* dz,
+                           float* dw2p, float* db1p, float* db2p, float norm_eps, float* rowc,
+                           int64_t* blocks, hipStream_t st) {
   int n_cu = 0;
   const hipError_t ce = device_cu_count(&n_cu);
   if (ce != hipSuccess) return ce;
@@ -606,8 +602,7 @@ hipError_t launch_score_dz(const void* x, int64_t xs, int64_t t_in, int d, const
   const int64_t nb = (t_in + 64 * rg - 1) / (64 * rg);
   *blocks = nb;
   if (t_in == 0) return hipSuccess;
-  DzOut bo{dbt, static_cast<uint16_t*>(dz), static_cast<uint16_t*>(dzt), ldt, dw2p, db1p, db2p,
-           rowc};
+  DzOut bo{dbt, static_cast<uint16_t*>(dz), dw2p, db1p, db2p, rowc};
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* wp = static_cast<const uint16_t*>(w1);
 #define TG_DZ(N, R)                                                                            \

@@ -483,21 +483,13 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
   }
 }
 
-// zeros in columns [c0, c1) of a [rows][ld] bf16 array
-__global__ __launch_bounds__(256) void fill_zero_u16(uint16_t* __restrict__ p, int64_t rows,
-                                                     int64_t ld, int64_t c0, int64_t c1) {
-  const int64_t w = c1 - c0;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e < rows * w) p[(e / w) * ld + c0 + e % w] = 0;
-}
-
 bool mfma_path(int dt, int d, int h) { return dt == 1 && h == 256 && d % 256 == 0; }
 
 struct Layout {
   int64_t n_tb, per_split, tp;
   int n_split;
   bool mfma;
-  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, inv, rowc, dzt, w1t, total;
+  size_t seqc, part, cpart, dbt, dz, dw2p, db1p, db2p, dw1p, inv, rowc, w1t, total;
 };
 
 Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_cu) {
@@ -541,9 +533,8 @@ Layout layout(int64_t t, int64_t t_kept, int n_seq, int d, int h, int dt, int n_
   // vector path: partials per 64 hidden units, [h / 64][t])
   L.inv = off; off += al(sizeof(float) * (size_t)t);
   L.rowc = off; off += al(sizeof(float) * (size_t)t * (L.mfma ? 1 : h / kT));
-  L.dzt = L.w1t = off;
+  L.w1t = off;
   if (L.mfma) {
-    L.dzt = off; off += al(sizeof(uint16_t) * (size_t)h * L.tp);
     L.w1t = off; off += al(sizeof(uint16_t) * (size_t)d * h);
   }
   L.total = off;
@@ -590,20 +581,16 @@ hipError_t launch_t(const void* xv, int64_t xs, int64_t t, int d, int h, const v
   if (L.mfma && t > 0) {
     if constexpr (std::is_same<T, uint16_t>::value) {
       uint16_t* dzb = reinterpret_cast<uint16_t*>(w + L.dz);
-      uint16_t* dzt = reinterpret_cast<uint16_t*>(w + L.dzt);
       uint16_t* w1t = reinterpret_cast<uint16_t*>(w + L.w1t);
       int64_t nb = 0;
-      hipError_t e = launch_score_dz(x, xs, t, d, w1, b1, w2, dbt, dzb, dzt, L.tp, dw2p, db1p,
-                                     db2p, norm_eps, rowc, &nb, st);
+      hipError_t e = launch_score_dz(x, xs, t, d, w1, b1, w2, dbt, dzb, dw2p, db1p, db2p,
+                                     norm_eps, rowc, &nb, st);
       if (e != hipSuccess) return e;
-      if (L.tp > t)
-        hipLaunchKernelGGL(fill_zero_u16, dim3((unsigned)((h * (L.tp - t) + 255) / 256)), dim3(256),
-                           0, st, dzt, (int64_t)h, L.tp, t, L.tp);
       hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(d / 64), (unsigned)((h + 63) / 64)),
                          dim3(256), 0, st, w1, (int64_t)d, (int64_t)h, (int64_t)d, w1t, (int64_t)h);
-      // dW1[h][c] = sum_j dz^T[h][j] x[j][c]  (x read as stored; token splits,
-      // fp32 partials)
-      e = launch_gemm_ab_kmajor_f32(dzt, L.tp, h, x, xs, t, d, L.tp, L.n_split, dw1p, d, st);
+      // dW1[h][c] = sum_j dz[j][h] x[j][c]  (dz and x both read as stored,
+      // token-major; token splits, fp32 partials; tokens past t read as zeros)
+      e = launch_gemm_atb_kmajor_f32(dzb, h, h, x, xs, t, d, L.tp, L.n_split, dw1p, d, st);
       if (e != hipSuccess) return e;
       // dx[j][c] = sum_h dz[j][h] W1^T[c][h]  (LN2: - c_j x[j][c])
       if (dx) {
