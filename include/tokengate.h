@@ -322,7 +322,7 @@ tg_status tg_gated_attn_bwd(const void* q, const void* k, const void* v, const v
  * dw1 dev [h, d] f32 out; db1, dw2 dev [h] f32 out; db2 dev [1] f32 out.
  * ws       dev workspace of >= tg_score_bwd_workspace_size(t_in, n_seq, d, h)
  *          bytes, 256-byte aligned (it holds dz and, on the matrix-core
- *          path, transposed copies of dz, x and w1).
+ *          path, a transposed copy of w1).
  * f32 rows, and bf16 rows with h != 256 or d % 256 != 0: fp32 arithmetic on
  * the vector ALU.  bf16 rows with h == 256 and d % 256 == 0: dz is recomputed
  * on the matrix cores with the forward's tiling and rounded to bf16 for the
