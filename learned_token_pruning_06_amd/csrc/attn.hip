@@ -145,7 +145,7 @@ __device__ __forceinline__ void gated_attn_item(
     int t_kept, int hq, int hkv, int groups_y, int hg, int64_t slot,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale,
     float* __restrict__ lse2, uint16_t* sk, uint16_t* sv, int chunk_tiles, int c_max, int chunk,
-    float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
+    uint16_t* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   constexpr int NTHR = C::NTHR;
   const int tid = threadIdx.x;
@@ -474,22 +474,26 @@ __device__ __forceinline__ void gated_attn_item(
   const float lt = half_swap_sum(lsum);
   if (!qvalid) return;
   if (SPLIT && part) {
-    // a part of the keys: the unnormalised O, the running maximum and the
-    // sum it refers to, for the merge (attn_merge).  A wave's rows start at a
-    // multiple of 32 and a tile's keys at a multiple of 64, so every tile the
-    // wave computes begins at or before its first row: each row has a finite
-    // maximum from the chunk's first tile on.  A wave that needs none of the
-    // chunk's tiles leaves (-inf, 0) and O = 0, which the merge weighs 0.
+    // a part of the keys: this part's output O_c / l_c (bf16, normalised by
+    // its own sum), the running maximum m_c and the sum l_c, for the merge
+    // (attn_merge).  A wave's rows start at a multiple of 32 and a tile's
+    // keys at a multiple of 64, so every tile the wave computes begins at or
+    // before its first row: each row has a finite maximum from the chunk's
+    // first tile on.  A wave that needs none of the chunk's tiles leaves
+    // (-inf, 0) and O = 0, which the merge weighs 0.
     const int64_t pr = ((int64_t)chunk * t_kept + lo + qa) * hq + head;
     if (g == 0) ws_ml[pr] = make_float2(mrun, lt);
-    float* po = ws_o + pr * DH;
+    const float pinv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* po = ws_o + pr * DH;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4*>(po + 32 * dt + 8 * r4 + 4 * g) =
-            make_float4(oacc[dt][4 * r4], oacc[dt][4 * r4 + 1], oacc[dt][4 * r4 + 2],
-                        oacc[dt][4 * r4 + 3]);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 pk;
+        pk.x = pack_bf16x2(oacc[dt][4 * r4 + 0] * pinv, oacc[dt][4 * r4 + 1] * pinv);
+        pk.y = pack_bf16x2(oacc[dt][4 * r4 + 2] * pinv, oacc[dt][4 * r4 + 3] * pinv);
+        *reinterpret_cast<uint2*>(po + 32 * dt + 8 * r4 + 4 * g) = pk;
+      }
     return;
   }
   const float inv = 1.0f / lt;
@@ -519,7 +523,7 @@ void gated_attn_bf16(
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int n_slots, const float* __restrict__ gain,
     const float* __restrict__ temp, float sm_scale, float* __restrict__ lse2, int chunk_tiles,
-    int c_max, const int* __restrict__ plan, float* __restrict__ ws_o,
+    int c_max, const int* __restrict__ plan, uint16_t* __restrict__ ws_o,
     float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   static_assert(NWAVE % HPW == 0 && C::NTHR >= BKV, "workgroup shape");
@@ -584,6 +588,7 @@ void gated_attn_bf16(
 // plan + 64 the items; splits[i] = (first row, rows, chunks) of split block i.
 // ---------------------------------------------------------------------------
 constexpr int kPlanBuckets = 4096;               // item sizes sorted exactly up to 4095 tiles
+constexpr int kPlanCache = 4096;                 // slots whose block shape is kept between the passes
 
 __global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ kept_cu, int n_seq,
                                                   int t_kept, int n_slots, int qb,
@@ -591,7 +596,8 @@ __global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ ke
                                                   int* __restrict__ plan,
                                                   int4* __restrict__ splits) {
   __shared__ int cnt[kPlanBuckets];
-  __shared__ int scan[1024];
+  __shared__ int3 shape[kPlanCache];               // (key tiles, first row, rows) per slot
+  __shared__ int sh[1024 / 64];
   __shared__ int n_split;
   const int tid = threadIdx.x;
   for (int i = tid; i < kPlanBuckets; i += 1024) cnt[i] = 0;
@@ -626,6 +632,7 @@ __global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ ke
   for (int slot = tid; slot < n_slots; slot += 1024) {
     int row0 = 0, rows = 0;
     const int n_all = block_of(slot, row0, rows);
+    if (slot < kPlanCache) shape[slot] = make_int3(n_all, row0, rows);
     if (n_all == 0) continue;
     const int nc = chunks_of(n_all);
     for (int j = 0; j < nc; ++j) atomicAdd(&cnt[bucket(tiles_of(n_all, j))], 1);
@@ -633,32 +640,32 @@ __global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ ke
   __syncthreads();
   // exclusive prefix sums of the bucket counts: four buckets per thread,
   // then a scan over the threads
+  static_assert(kPlanBuckets == 4 * 1024, "four buckets per thread");
   int a[4], tot = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     a[i] = cnt[4 * tid + i];
     tot += a[i];
   }
-  scan[tid] = tot;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int run = scan[tid] - tot;
+  int total;
+  int run = block_excl_scan<1024>(tot, sh, &total);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     cnt[4 * tid + i] = run;
     run += a[i];
   }
-  const int total = scan[1023];
   __syncthreads();
   int* __restrict__ list = plan + 64;
   for (int slot = tid; slot < n_slots; slot += 1024) {
-    int row0 = 0, rows = 0;
-    const int n_all = block_of(slot, row0, rows);
+    int row0 = 0, rows = 0, n_all;
+    if (slot < kPlanCache) {
+      const int3 sv = shape[slot];
+      n_all = sv.x;
+      row0 = sv.y;
+      rows = sv.z;
+    } else {
+      n_all = block_of(slot, row0, rows);
+    }
     if (n_all == 0) continue;
     const int nc = chunks_of(n_all);
     for (int j = 0; j < nc; ++j) list[atomicAdd(&cnt[bucket(tiles_of(n_all, j))], 1)] = slot * 8 + j;
@@ -672,65 +679,68 @@ __global__ __launch_bounds__(1024) void attn_plan(const int32_t* __restrict__ ke
 }
 
 // The key chunks of the split query blocks merged, one wave per (row, head):
-// with each chunk's (m_c, l_c, O_c) (O_c unnormalised, both relative to
-// m_c), M = max m_c, w_c = 2^(m_c - M), O = sum w_c O_c / sum w_c l_c, and
-// the row's lse2 = M + log2(sum w_c l_c).  blockIdx.x: the split block (of
-// attn_plan's list), blockIdx.y: four (row, head) pairs of it.  All of a
-// pair's loads are issued before the first is used.
+// with each chunk's (m_c, l_c, o_c = O_c / l_c) (O_c and l_c relative to
+// m_c), M = max m_c, w_c = 2^(m_c - M) l_c, O = sum w_c o_c / sum w_c, and
+// the row's lse2 = M + log2(sum w_c).  blockIdx.x: the split block (of
+// attn_plan's list), blockIdx.y: 256 / (DH / 8) of its (row, head) pairs,
+// DH / 8 threads per pair, each merging 8 dims with one 16-byte load per
+// chunk, all issued before the first is used.
 constexpr int kMaxChunks = 8;
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ ws_o,
+__global__ __launch_bounds__(256) void attn_merge(const uint16_t* __restrict__ ws_o,
                                                   const float2* __restrict__ ws_ml,
                                                   const int* __restrict__ plan,
                                                   const int4* __restrict__ splits, int t_kept,
                                                   int hq, uint16_t* __restrict__ out,
                                                   float* __restrict__ lse2) {
-  constexpr int PER = DH / 64;                     // dims per lane
+  constexpr int TPP = DH / 8;                      // threads per (row, head) pair, 8 dims each
+  constexpr int PPB = 256 / TPP;                   // pairs per workgroup
   if ((int)blockIdx.x >= plan[1]) return;
   const int4 sp = splits[blockIdx.x];              // first row, rows, chunks
-  const int pair = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int pair = blockIdx.y * PPB + threadIdx.x / TPP;
+  const int part = threadIdx.x % TPP;              // dims 8 part .. +8
   const int r = pair / hq;
   if (r >= sp.y) return;
   const int head = pair % hq;
-  const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)sp.x + r;
   const int nc = sp.z;
   float2 ml[kMaxChunks];
-  float o[kMaxChunks][PER];
+  u32x4 ov[kMaxChunks];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     if (c < nc) {
       const int64_t pr = ((int64_t)c * t_kept + row) * hq + head;
       ml[c] = ws_ml[pr];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[c][i] = ws_o[pr * DH + PER * lane + i];
+      ov[c] = ld16(ws_o + pr * DH + 8 * part);
     }
   }
   float M = -INFINITY;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c)
     if (c < nc) M = fmaxf(M, ml[c].x);
-  float L = 0.0f, acc[PER];
+  float L = 0.0f, acc[8];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     if (c < nc) {
-      const float w = ml[c].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[c].x - M);
-      L = fmaf(w, ml[c].y, L);
+      const float w =
+          ml[c].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[c].x - M) * ml[c].y;
+      L += w;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, o[c][i], acc[i]);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t wd = ov[c][i >> 1];
+        acc[i] = fmaf(w, __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16)), acc[i]);
+      }
     }
   }
   const float inv = 1.0f / L;
-  uint16_t* op = out + (row * hq + head) * DH + PER * lane;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  } else {
-    op[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
-  }
-  if (lse2 && lane == 0) lse2[(int64_t)head * t_kept + row] = M + __log2f(L);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  st16(out + (row * hq + head) * DH + 8 * part, o);
+  if (lse2 && part == 0) lse2[(int64_t)head * t_kept + row] = M + __log2f(L);
 }
 
 // How tg_gated_attn_split divides the keys: query blocks of more than
@@ -769,7 +779,7 @@ SplitLayout split_layout(int64_t t_kept, int64_t n_slots, int c_max, int hq, int
   l.list = 0;                                              // 64 header ints + the items
   l.splits = round256((64 + (size_t)n_slots * c_max) * 4);
   l.o = l.splits + round256((size_t)n_slots * 16);
-  l.ml = l.o + (c_max > 1 ? (size_t)c_max * t_kept * hq * dh * 4 : 0);
+  l.ml = l.o + (c_max > 1 ? round256((size_t)c_max * t_kept * hq * dh * 2) : 0);
   l.total = l.ml + (c_max > 1 ? (size_t)c_max * t_kept * hq * 8 : 0);
   return l;
 }
@@ -801,7 +811,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
   if (blocks == 0) return hipSuccess;
   int* plan = nullptr;
   int4* splits = nullptr;
-  float* ws_o = nullptr;
+  uint16_t* ws_o = nullptr;
   float2* ws_ml = nullptr;
   if (sp) {
     const SplitLayout l = split_layout(t_kept, n_slots, c_max, hq, DH);
@@ -809,7 +819,7 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
     plan = reinterpret_cast<int*>(base + l.list);
     splits = reinterpret_cast<int4*>(base + l.splits);
     if (c_max > 1) {
-      ws_o = reinterpret_cast<float*>(base + l.o);
+      ws_o = reinterpret_cast<uint16_t*>(base + l.o);
       ws_ml = reinterpret_cast<float2*>(base + l.ml);
     }
     hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, st, kept_cu, n_seq, (int)t_kept,
@@ -822,7 +832,8 @@ hipError_t launch_cfg(const void* q, const void* k, const void* v, void* out, in
                      kept_cu, n_seq, (int)t_kept, hq, hkv, groups_y, (int)n_slots, gain, temp,
                      sm_scale, lse2, chunk_tiles, c_max, plan, ws_o, ws_ml);
   if (ws_o) {
-    const int64_t gy = ((int64_t)QB * hq + 3) / 4;
+    constexpr int PPB = 256 / (DH / 8);            // pairs per merge workgroup
+    const int64_t gy = ((int64_t)QB * hq + PPB - 1) / PPB;
     if (gy > 65535 || n_slots > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_merge<DH>), dim3((unsigned)n_slots, (unsigned)gy), dim3(256), 0, st,
                        ws_o, ws_ml, plan, splits, (int)t_kept, hq, static_cast<uint16_t*>(out),

@@ -206,7 +206,7 @@ def test_attn_validation(lib):
 
 def test_attn_split_validation(lib):
     ws_size = lib.tg_gated_attn_split_workspace_size
-    per_row = 16 * (128 * 4 + 8)        # one chunk's partial results of a row
+    per_row = 16 * (128 * 2 + 8)        # one chunk's partial results of a row
     # long inputs: no block outweighs a workgroup's share, so the workspace
     # holds the plan alone (a few bytes per query block), no partial results
     for t in (131072, 8704):

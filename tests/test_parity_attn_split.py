@@ -31,8 +31,8 @@ def _ws_bytes(t, n_seq, max_len, hq, hkv, dh):
 
 def _has_partials(nbytes, t, hq, dh):
     """The workspace holds partial results (some block is split): at least
-    two chunks' (f32 output, max, sum) per row and head."""
-    return nbytes >= 2 * t * hq * (dh * 4 + 8)
+    two chunks' (bf16 output, f32 max and sum) per row and head."""
+    return nbytes >= 2 * t * hq * (dh * 2 + 8)
 
 
 def _dev_args(q, k, v, kb, pos, kc, gain, temp):
