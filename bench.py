@@ -151,6 +151,70 @@ def budget_sweep(g, dev, reps=10):
     return rows
 
 
+def short_inputs(dev, reps=10):
+    """The attention alone on the kept shapes of the 16k layer (one sequence,
+    2496 kept rows) and of the ragged 4-sequence batch (12380 kept rows):
+    tg_gated_attn_split (the step's path) against tg_gated_attn.  Q/K/V and
+    the kept scores are seeded stand-ins, positions ascending with a stride
+    of 16 (the cost depends on the shapes); the two forms alternate, twice
+    each, and each keeps its lower mean over `reps` back-to-back calls."""
+    import numpy as np
+    import torch
+    from learned_token_pruning_06_amd import ops
+    from workloads import generate, random_qkv
+    lib = ops.load()
+    rows = []
+    for cfg in (1, 4):
+        g = generate(cfg, with_x=False, with_proj=False)
+        wl = g["wl"]
+        cu_h = np.asarray(g["cu_seqlens"], np.int64)
+        n_seq = len(cu_h) - 1
+        npr = [int(g["prunable"][cu_h[s]:cu_h[s + 1]].sum()) for s in range(n_seq)]
+        kc_h, tk = ops.kept_sizes(g["cu_seqlens"], npr, g["budgets"][0])
+        kc_h = np.asarray(kc_h, np.int64)
+        lens = np.diff(kc_h)
+        ml = int(lens.max(initial=0))
+        tb = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        q, k, v = (tb(a) for a in random_qkv(40 + cfg, tk, wl.hq, wl.hkv, wl.dh))
+        rng = np.random.default_rng(40 + cfg)
+        kb = torch.from_numpy(rng.standard_normal(tk).astype(np.float32)).to(dev)
+        pos = np.concatenate([16 * np.arange(n) for n in lens]).astype(np.int32)
+        kp = torch.from_numpy(pos).to(dev)
+        kc = torch.from_numpy(kc_h.astype(np.int32)).to(dev)
+        gain = torch.from_numpy(g["gain"]).to(dev)
+        temp = torch.from_numpy(g["temp"]).to(dev)
+        o = torch.empty_like(q)
+        ws = ops.workspace(lib.tg_gated_attn_split_workspace_size(tk, n_seq, ml, wl.hq, wl.hkv,
+                                                                  wl.dh), dev)
+        fs = {"split": lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=ml, out=o,
+                                              split=True, ws=ws),
+              "plain": lambda: ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=ml, out=o)}
+        best = {}
+        for _ in range(2):
+            for name, f in fs.items():
+                f()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                best[name] = min(best.get(name, 1e30), e0.elapsed_time(e1) / reps * 1e3)
+        fl = 2.0 * wl.dh * wl.hq * float(np.sum(lens * (lens + 1)))
+        rows.append({"workload": WORKLOAD_NAMES[cfg], "t_kept": int(tk),
+                     "kept_seqlens": [int(x) for x in lens], "split_us": round(best["split"], 2),
+                     "plain_us": round(best["plain"], 2),
+                     "split_tflops": round(fl / (best["split"] * 1e-6) / 1e12, 1),
+                     "split_frac_of_bf16_peak": round(fl / (best["split"] * 1e-6) / 1e12 /
+                                                      PEAK_BF16_TFLOPS, 4),
+                     "plain_frac_of_bf16_peak": round(fl / (best["plain"] * 1e-6) / 1e12 /
+                                                      PEAK_BF16_TFLOPS, 4)})
+        del q, k, v
+    return rows
+
+
 def cpu_baseline(g, t_kept_cu, score_chunk=16384):
     """The fp64 oracle on the whole step of the same workload: score and
     normalise all 131072 tokens (x upcast in chunks of score_chunk rows),
@@ -469,9 +533,11 @@ def main():
         del kc, vc
 
     sweep = None
+    short = None
     if lanes:
         # the 32k budget sweep (8 drawn budgets on preset scores) as a lane
         sweep = budget_sweep(generate(2), dev)
+        short = short_inputs(dev)
 
     full = None
     if lanes and not args.no_full_context:
@@ -546,6 +612,7 @@ def main():
         "attn_bwd": attn_bwd,
         "score_bwd": score_bwd,
         "budget_sweep": sweep,
+        "attn_short_inputs": short,
     }
     print(json.dumps(out), flush=True)
 
