@@ -204,3 +204,34 @@ def test_split_16k_workload_all_rows():
     assert _has_partials(nbytes, q.shape[0], q.shape[1], q.shape[2])
     check_attn(got, O.ref_gated_attn(*c), "bf16", "split, 16k workload")
     _check_lse2(lse2, c, "split, 16k workload")
+
+
+def _random_configs(n=10, seed=77):
+    """Seeded random shapes: 1-5 sequences, the longest 1280-1700 rows (at
+    least 20 key tiles, so most draws split), the others 0-1700; every
+    head grouping the attention supports, dh 64 and 128."""
+    rng = np.random.default_rng(seed)
+    heads = [(16, 8, 128), (8, 8, 128), (16, 4, 128), (32, 4, 128), (4, 1, 64), (8, 4, 64)]
+    out = []
+    for i in range(n):
+        n_seq = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 1701, n_seq)]
+        lens[int(rng.integers(0, n_seq))] = int(rng.integers(1280, 1701))
+        hq, hkv, dh = heads[i % len(heads)]
+        out.append((1000 + i, lens, hq, hkv, dh))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_configs(),
+                         ids=[f"r{c[0]}-n{len(c[1])}-g{c[2] // c[3]}-dh{c[4]}"
+                              for c in _random_configs()])
+def test_split_random_shapes(case):
+    seed, lens, hq, hkv, dh = case
+    say(f"attn split (random): seed={seed} lens={lens} hq={hq} hkv={hkv} dh={dh}")
+    c = synth_case(seed, lens, hq, hkv, dh, "bf16", prompt=7)
+    got, lse2, nbytes = _run_split(c)
+    say(f"  partial results: {_has_partials(nbytes, sum(lens), hq, dh)}")
+    q, k, v, kb, pos, kc, gain, temp = c
+    check_attn(got, O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp), "bf16",
+               f"split random {seed}")
+    _check_lse2(lse2, c, f"split random {seed}")
