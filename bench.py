@@ -17,6 +17,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -41,11 +42,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def source_code(text: str) -> str:
+    """The code of a C++/HIP source without its comments and blank lines, so
+    that an edit of the comments alone keeps the counters taken on it."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_sha(names):
+    """Digest of the named kernel sources' code (comments excluded)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "learned_token_pruning_06_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "learned_token_pruning_06_amd", "csrc", n)) as f:
+            h.update(source_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 

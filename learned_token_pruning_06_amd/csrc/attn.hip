@@ -48,6 +48,14 @@
 //    are skipped;
 //  - the running maximum is only moved when it grows by more than 2^8 in
 //    the exponent (exact: the normaliser absorbs the stale maximum).
+//
+// tg_gated_attn_split (the SPLIT instance of the same kernel, for short or
+// ragged inputs): a one-workgroup launch (attn_plan) lists the query
+// blocks, cuts the ones with more key tiles than a workgroup's share of
+// the causal work into key chunks, and sorts all items by size, largest
+// first; the attention deals that list to the workgroups in the same snake
+// order; each chunk leaves a bf16 partial output with its f32 maximum and
+// sum, and attn_merge combines the chunks of each split block.
 #include <type_traits>
 
 #include "common.h"
