@@ -161,3 +161,59 @@ def test_padded_bucket_graph_serves_several_budgets():
             assert e <= 1e-2, f"K={K}: {name} rel-L2 {e:.2e}"
         ref_o = O.ref_gated_attn(qg, kg, vg, want[2], want[1], want[3], g["gain"], g["temp"])
         check_attn(to_f64(o[:tk]), ref_o, "bf16", f"bucket replay K={K}")
+
+
+def test_split_attention_graph_serves_several_lengths():
+    """tg_gated_attn_split captured once for a capacity of 3000 kept rows and
+    replayed for sequences of 2496, 1500, 2999 and again 2496 rows, only
+    kept_cu_seqlens changing on the device between replays.  Its plan runs on
+    the GPU from the device offsets, so each replay splits the blocks it
+    really has.  Each replay must equal an eager split call bit for bit,
+    match the oracle at the bf16 bars, and leave the padding rows alone."""
+    import oracle as O
+    from gpu_util import check_attn, round_bf16, to_f64
+    from learned_token_pruning_06_amd import ops
+    from workloads import bf16_to_f64
+    cap, hq, hkv, dh = 3000, 16, 8, 128
+    rng = np.random.default_rng(91)
+    qh, kh, vh = (round_bf16(rng.standard_normal((cap, n, dh))) for n in (hq, hkv, hkv))
+    kbh = rng.standard_normal(cap).astype(np.float32)
+    posh = (3 * np.arange(cap)).astype(np.int32)
+    gainh = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    temph = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    q, k, v = bf16_dev(qh), bf16_dev(kh), bf16_dev(vh)
+    kb, kp, gain, temp = f32_dev(kbh), i32_dev(posh), f32_dev(gainh), f32_dev(temph)
+    kc = i32_dev(np.array([0, cap], np.int32))
+    lib = ops.load()
+    dev = q.device
+    ws = ops.workspace(lib.tg_gated_attn_split_workspace_size(cap, 1, cap, hq, hkv, dh), dev)
+    o = torch.empty_like(q)
+    o_eager = torch.empty_like(q)
+
+    def attn(out):
+        ops.gated_attn(q, k, v, kb, kp, kc, gain, temp, max_len=cap, out=out, split=True, ws=ws)
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        attn(o)                                   # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn(o)
+    torch.cuda.synchronize()
+    for rep, n in enumerate((2496, 1500, 2999, 2496)):
+        say(f"split graph replay {rep}: {n} kept rows, capacity {cap}")
+        kc[1].fill_(n)                            # eager work between replays
+        o.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        attn(o_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:n].view(torch.int16), o_eager[:n].view(torch.int16)), \
+            f"replay {rep}: differs from the eager call"
+        assert torch.all(o[n:].view(torch.uint8) == 0xA5), f"replay {rep}: padding rows written"
+        want = O.ref_gated_attn(bf16_to_f64(qh[:n]), bf16_to_f64(kh[:n]), bf16_to_f64(vh[:n]),
+                                kbh[:n].astype(np.float64), posh[:n], np.array([0, n]), gainh,
+                                temph)
+        check_attn(to_f64(o[:n]), want, "bf16", f"split graph replay, {n} rows")
