@@ -21,8 +21,8 @@
 //          histogram.  It also records, per chunk, how many tokens are kept
 //          whatever the low digit (prompt tokens, keys above the 20-bit
 //          prefix, or every token when K' = |P|) and the low digits of the
-//          tokens that share the prefix (the candidates).  Block 0 writes
-//          kept_cu_seqlens: a sequence keeps min(K, |P|) + |N| tokens.
+//          tokens that share the prefix (the candidates).  One extra block
+//          writes kept_cu_seqlens: a sequence keeps min(K, |P|) + |N| tokens.
 //   write  each block picks the low digit, hence tau and the number `need`
 //          of tokens equal to tau that are kept (lower index first).  The
 //          chunk's output offset is the earlier chunks' definite keeps plus
@@ -176,10 +176,10 @@ TG_DEVINL Sel sel_start(uint32_t npr, int kb) {
   return st;
 }
 
-// Narrow (prefix, need) with a histogram of NBINS bins, read from global
-// memory (h) or given per thread (c, NBINS / NT bins of thread t, counted
-// from the top: bins NBINS-1 - (t * per + i)).  Block-wide; every thread
-// returns the same result.  Contains barriers.
+// Narrow (prefix, need) with a histogram of NBINS bins given per thread (c,
+// NBINS / NT bins of thread t, counted from the top: bins
+// NBINS-1 - (t * per + i)).  Block-wide; every thread returns the same
+// result.  Contains barriers.
 template <int NBINS, int SHIFT>
 TG_DEVINL void sel_narrow_vals(Sel& st, const uint32_t (&c)[NBINS / NT], int* sh) {
   constexpr int per = NBINS / NT;
@@ -206,18 +206,27 @@ TG_DEVINL void sel_narrow_vals(Sel& st, const uint32_t (&c)[NBINS / NT], int* sh
   __syncthreads();
 }
 
-// The same with the histogram in global memory: read with coalesced 16-byte
-// loads into LDS (stage, NBINS words, 16-byte aligned), then each thread takes
-// its NBINS / NT bins from there.
+// A histogram in global memory, read with coalesced 16-byte loads.  The
+// loads are issued as soon as the sequence is known, next to the block's
+// other independent loads, so they do not add a round trip after the
+// selection state arrives.
+template <int NBINS>
+struct HistRegs {
+  u32x4 v[NBINS / 4 / NT];                     // 16-byte vectors of this thread
+};
+template <int NBINS>
+TG_DEVINL void hist_load(const uint32_t* h, HistRegs<NBINS>& r) {
+#pragma unroll
+  for (int k = 0; k < NBINS / 4 / NT; ++k) r.v[k] = ld16(h + 4 * (threadIdx.x + k * NT));
+}
+
+// Narrow with such a histogram: its vectors go to LDS (stage, NBINS words,
+// 16-byte aligned), then each thread takes its NBINS / NT bins from there.
 template <int NBINS, int SHIFT>
-TG_DEVINL void sel_narrow(Sel& st, const uint32_t* h, uint32_t* stage, int* sh) {
+TG_DEVINL void sel_narrow(Sel& st, const HistRegs<NBINS>& r, uint32_t* stage, int* sh) {
   constexpr int per = NBINS / NT;
-  constexpr int NV = NBINS / 4 / NT;           // 16-byte vectors per thread
-  u32x4 v[NV];
 #pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = ld16(h + 4 * (threadIdx.x + k * NT));
-#pragma unroll
-  for (int k = 0; k < NV; ++k) st16(stage + 4 * (threadIdx.x + k * NT), v[k]);
+  for (int k = 0; k < NBINS / 4 / NT; ++k) st16(stage + 4 * (threadIdx.x + k * NT), r.v[k]);
   __syncthreads();
   uint32_t c[per];
 #pragma unroll
@@ -342,9 +351,10 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
   __shared__ __attribute__((aligned(16))) uint32_t lh[NB1];
   __shared__ int sh[NT / 64 + 2];
   __shared__ uint32_t ncand;
-  if (blockIdx.x == 0) {
-    // kept_cu[s] = sum over earlier sequences of min(K, |P|) + |N|; an empty
-    // sequence was seen by no pass1 block and has |P| = 0
+  if (blockIdx.x == gridDim.x - 1) {
+    // the launch's extra last block, which meets no chunk: kept_cu[s] = sum
+    // over earlier sequences of min(K, |P|) + |N|; an empty sequence was
+    // seen by no pass1 block and has |P| = 0
     int acc = 0;
     for (int base = 0; base < n_seq; base += NT) {
       const int i = base + threadIdx.x;
@@ -362,13 +372,16 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
       acc += tot;
     }
     if (threadIdx.x == 0) kept_cu[n_seq] = acc;
+    return;
   }
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
   Tokens tk;
   load_tokens(b, pr, c, tk);
+  HistRegs<NB1> hr;
+  hist_load<NB1>(w.hist1 + (size_t)c.s * NB1, hr);    // zeros unless the mode is RADIX
   Sel st = w.stage[c.s];
-  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, w.hist1 + (size_t)c.s * NB1, lh, sh);
+  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, hr, lh, sh);
   if (c.ci == 0 && threadIdx.x == 0) w.stage[n_seq + c.s] = st;
   if (st.mode == MODE_RADIX) {
     for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
@@ -426,54 +439,70 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
   if (!locate(cu, n_seq, t_in, c)) return;
   Tokens tk;
   load_tokens(b, pr, c, tk);
+  HistRegs<NB1> hr;
+  hist_load<NB1>(w.hist2 + (size_t)c.s * NB1, hr);    // zeros unless the mode is RADIX
+  // The earlier chunks of the sequence, one thread each: def, ncand and the
+  // short candidate list, the record's last 64 bytes.  The first NT records
+  // are loaded here, beside the histogram, before the state is known.
+  auto rec_ok = [&](int i) {
+    const int64_t sl = c.s0 + i;
+    return i < c.ci && sl >= 0 && sl < (int64_t)gridDim.x;
+  };
+  auto rec_load = [&](int i, u32x4 (&t4)[4]) {
+    const u32x4* tail = reinterpret_cast<const u32x4*>(&w.slot[c.s0 + i].def);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t4[k] = ld16(tail + k);
+  };
+  u32x4 r0[4];
+  const bool has0 = rec_ok(threadIdx.x);
+  if (has0) rec_load(threadIdx.x, r0);
   const int64_t kept0 = kept_cu[c.s];
   Sel st = w.stage[n_seq + c.s];
-  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, w.hist2 + (size_t)c.s * NB1, hs, sh);
+  if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, hr, hs, sh);
   const uint32_t tau = st.prefix;                  // the K'-th largest key (RADIX)
   const uint32_t d2 = tau & 0xfffu;
   const int need = st.mode == MODE_RADIX ? (int)st.need : 0;
-  // the earlier chunks of the sequence: definite keeps, candidates above tau
-  // and candidates equal to tau (one thread per earlier chunk; the candidate
-  // digits are read 32 at a time, four 16-byte loads in flight)
+  // definite keeps, candidates above tau and candidates equal to tau of the
+  // earlier chunks (a long candidate list is read 32 digits at a time, four
+  // 16-byte loads in flight)
   int dsum = 0, gsum = 0, tsum = 0;
-  for (int i = threadIdx.x; i < c.ci; i += NT) {
-    const int64_t sl = c.s0 + i;
-    if (sl < 0 || sl >= (int64_t)gridDim.x) continue;
-    // def, ncand and the short list: the record's last 64 bytes
-    const u32x4* tail = reinterpret_cast<const u32x4*>(&w.slot[sl].def);
-    u32x4 t4[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) t4[k] = ld16(tail + k);
+  auto rec_count = [&](int i, const u32x4 (&t4)[4]) {
     dsum += (int)t4[0][0];
-    if (st.mode == MODE_RADIX) {
-      const int n = (int)(t4[0][1] < (uint32_t)CH ? t4[0][1] : (uint32_t)CH);
-      if (n <= NSMALL) {
+    if (st.mode != MODE_RADIX) return;
+    const int n = (int)(t4[0][1] < (uint32_t)CH ? t4[0][1] : (uint32_t)CH);
+    if (n <= NSMALL) {
 #pragma unroll
-        for (int m = 0; m < NSMALL; ++m) {
-          const uint32_t wd = t4[(2 + m / 2) / 4][(2 + m / 2) % 4];
-          const uint32_t d = (wd >> (16 * (m & 1))) & 0xffffu;
-          gsum += m < n && d > d2;
-          tsum += m < n && d == d2;
-        }
-        continue;
+      for (int m = 0; m < NSMALL; ++m) {
+        const uint32_t wd = t4[(2 + m / 2) / 4][(2 + m / 2) % 4];
+        const uint32_t d = (wd >> (16 * (m & 1))) & 0xffffu;
+        gsum += m < n && d > d2;
+        tsum += m < n && d == d2;
       }
-      const uint16_t* cl = w.cand + (size_t)sl * CH;
-      for (int e0 = 0; e0 < n; e0 += 32) {
-        u32x4 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          v[k] = e0 + 8 * k < n ? ld16(cl + e0 + 8 * k) : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t d = (v[k][m >> 1] >> (16 * (m & 1))) & 0xffffu;
-            const bool ok = e0 + 8 * k + m < n;
-            gsum += ok && d > d2;
-            tsum += ok && d == d2;
-          }
-      }
+      return;
     }
+    const uint16_t* cl = w.cand + (size_t)(c.s0 + i) * CH;
+    for (int e0 = 0; e0 < n; e0 += 32) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = e0 + 8 * k < n ? ld16(cl + e0 + 8 * k) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t d = (v[k][m >> 1] >> (16 * (m & 1))) & 0xffffu;
+          const bool ok = e0 + 8 * k + m < n;
+          gsum += ok && d > d2;
+          tsum += ok && d == d2;
+        }
+    }
+  };
+  if (has0) rec_count(threadIdx.x, r0);
+  for (int i = threadIdx.x + NT; i < c.ci; i += NT) {
+    if (!rec_ok(i)) continue;
+    u32x4 t4[4];
+    rec_load(i, t4);
+    rec_count(i, t4);
   }
   int tot_d, tot_g, tot_t;
   block_excl_scan<NT>(dsum, sh, &tot_d);
@@ -561,10 +590,11 @@ hipError_t launch_select(const float* b, const uint8_t* prunable, const int32_t*
     hipLaunchKernelGGL(sel_pass0, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w);
     hipLaunchKernelGGL(sel_pass1, grid, dim3(NT), 0, st, b, prunable, cu, k, n_seq, t_in, w);
   }
-  // every sequence's kept_cu entry is written by block 0, also when t_in == 0
-  // (the pass1 state it reads is then never used: every sequence is empty)
-  hipLaunchKernelGGL(sel_pass2, dim3((unsigned)(ns > 0 ? ns : 1)), dim3(NT), 0, st, b, prunable, cu,
-                     k, n_seq, t_in, w, kept_cu);
+  // every sequence's kept_cu entry is written by the extra last block, also
+  // when t_in == 0 (the pass1 state it reads is then never used: every
+  // sequence is empty); slot ns lies past every chunk
+  hipLaunchKernelGGL(sel_pass2, dim3((unsigned)(ns + 1)), dim3(NT), 0, st, b, prunable, cu, k,
+                     n_seq, t_in, w, kept_cu);
   if (t_in > 0)
     hipLaunchKernelGGL(sel_write, grid, dim3(NT), 0, st, b, prunable, cu, n_seq, t_in, w, kept_cu,
                        cap, kept_idx, kept_pos, kept_b);
