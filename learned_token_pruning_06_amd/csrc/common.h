@@ -67,15 +67,21 @@ TG_DEVINL float wave_max(float v) {
   return v;
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave (all lanes active): DPP
+// shifts right by 1, 2, 4 and 8 inside each row of 16 lanes (lanes with no
+// source in the row add 0), then each row adds the totals of the rows below
+// it, read from lanes 15, 31 and 47.  No LDS round trips, unlike a shuffle
+// per step.
 TG_DEVINL int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Exclusive prefix sum over a block of NT threads (NT % 64 == 0) in thread

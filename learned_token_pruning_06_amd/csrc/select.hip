@@ -234,6 +234,28 @@ TG_DEVINL void sel_narrow(Sel& st, const HistRegs<NBINS>& r, uint32_t* stage, in
   sel_narrow_vals<NBINS, SHIFT>(st, c, sh);     // starts with a barrier-protected scan
 }
 
+// Block-wide sums of three per-thread counts, every thread gets all three:
+// one exchange of the wave totals (sh3: 3 * NT / 64 ints, not reused by the
+// caller afterwards, so a single barrier suffices).
+TG_DEVINL void block_sum3(int& a, int& b, int& c, int* sh3) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b), ic = wave_incl_scan(c);
+  if (lane == 63) {
+    sh3[w] = ia;
+    sh3[NW + w] = ib;
+    sh3[2 * NW + w] = ic;
+  }
+  __syncthreads();
+  a = b = c = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    a += sh3[i];
+    b += sh3[NW + i];
+    c += sh3[2 * NW + i];
+  }
+}
+
 // ---------------------------------------------------------------- pass 0
 __global__ __launch_bounds__(NT) void sel_pass0(const float* __restrict__ b,
                                                const uint8_t* __restrict__ pr,
@@ -435,6 +457,7 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
                                                float* __restrict__ kept_b) {
   __shared__ __attribute__((aligned(16))) uint32_t hs[NB1];
   __shared__ int sh[NT / 64 + 2];
+  __shared__ int sh3[3 * (NT / 64)];
   Chunk c;
   if (!locate(cu, n_seq, t_in, c)) return;
   Tokens tk;
@@ -504,10 +527,8 @@ __global__ __launch_bounds__(NT) void sel_write(const float* __restrict__ b,
     rec_load(i, t4);
     rec_count(i, t4);
   }
-  int tot_d, tot_g, tot_t;
-  block_excl_scan<NT>(dsum, sh, &tot_d);
-  block_excl_scan<NT>(gsum, sh, &tot_g);
-  block_excl_scan<NT>(tsum, sh, &tot_t);
+  block_sum3(dsum, gsum, tsum, sh3);
+  const int tot_d = dsum, tot_g = gsum, tot_t = tsum;
   const int tie_base = tot_t;
   const int64_t out_base = kept0 + tot_d + tot_g + (tot_t < need ? tot_t : need);
   uint8_t fl[PER];     // 1: kept for sure, 2: tie at tau
