@@ -54,17 +54,55 @@ TG_DEVINL uint32_t score_key(float v) {
 // ---------------------------------------------------------------------------
 // wave / block reductions (wave64)
 // ---------------------------------------------------------------------------
+// DPP move of a value of any size (a multiple of 4 bytes), word by word:
+// CTRL is a full permutation of the lanes of each row of 16
+template <int CTRL, typename T>
+TG_DEVINL T dpp_move(T v) {
+  static_assert(sizeof(T) % 4 == 0, "whole 32-bit words");
+  struct Words {
+    int w[sizeof(T) / 4];
+  };
+  Words a = __builtin_bit_cast(Words, v);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i)
+    a.w[i] = __builtin_amdgcn_update_dpp(0, a.w[i], CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(T, a);
+}
+template <typename T>
+TG_DEVINL T read_lane(T v, int l) {
+  struct Words {
+    int w[sizeof(T) / 4];
+  };
+  Words a = __builtin_bit_cast(Words, v);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) a.w[i] = __builtin_amdgcn_readlane(a.w[i], l);
+  return __builtin_bit_cast(T, a);
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]: lane i <-> i ^ 1
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]: lane i <-> i ^ 2
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within each 16
+
+// Sum over the 64 lanes of a wave (all lanes active), the same value in every
+// lane: DPP butterflies inside each row of 16 lanes (partners i ^ 1, i ^ 2,
+// then the mirrored half row and the mirrored row; both partners add the
+// same two values, so every lane of a row holds the same sum), then the four
+// row sums in a fixed order.  No LDS round trips.
 template <typename T>
 TG_DEVINL T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_move<kDppQuadXor1>(v);
+  v += dpp_move<kDppQuadXor2>(v);
+  v += dpp_move<kDppRowHalfMirror>(v);
+  v += dpp_move<kDppRowMirror>(v);
+  return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 TG_DEVINL float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_move<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_move<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_move<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kDppRowMirror>(v));
+  return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 // inclusive prefix sum over the 64 lanes of a wave (all lanes active): DPP
