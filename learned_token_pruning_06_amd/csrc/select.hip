@@ -338,6 +338,9 @@ __global__ __launch_bounds__(NT) void sel_pass1(const float* __restrict__ b,
   const int kb = kbud[c.s];
   Tokens tk;
   load_tokens(b, pr, c, tk);              // issued before the histogram sums
+  // the middle-digit histogram starts at zero; stage0's barriers order these
+  // stores before the atomics below
+  for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
   int64_t lo, hi;
   seq_range(cu, c.s, t_in, lo, hi);
   const Sel st = stage0(w, kb, c, n_chunks(lo, hi), (int64_t)gridDim.x, red4, sh);
@@ -346,8 +349,6 @@ __global__ __launch_bounds__(NT) void sel_pass1(const float* __restrict__ b,
     w.n_prunable[c.s] = st.npr;
   }
   if (st.mode != MODE_RADIX) return;
-  for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (tk.pr[i]) {
@@ -370,7 +371,8 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
                                                const int32_t* __restrict__ kbud, int n_seq,
                                                int64_t t_in, SelWs w,
                                                int32_t* __restrict__ kept_cu) {
-  __shared__ __attribute__((aligned(16))) uint32_t lh[NB1];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[NB1];   // staging of the middle digit
+  __shared__ uint32_t lc[NB1];                                 // low digits of the candidates
   __shared__ int sh[NT / 64 + 2];
   __shared__ uint32_t ncand;
   if (blockIdx.x == gridDim.x - 1) {
@@ -402,14 +404,14 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
   load_tokens(b, pr, c, tk);
   HistRegs<NB1> hr;
   hist_load<NB1>(w.hist1 + (size_t)c.s * NB1, hr);    // zeros unless the mode is RADIX
+  // the candidates' histogram and count start at zero; the narrowing's
+  // barriers order these stores before the atomics below (which only the
+  // RADIX mode, where it runs, makes), and thread 0 reads ncand itself
+  for (int i = threadIdx.x; i < NB1; i += NT) lc[i] = 0u;
+  if (threadIdx.x == 0) ncand = 0u;
   Sel st = w.stage[c.s];
   if (st.mode == MODE_RADIX) sel_narrow<NB1, 12>(st, hr, lh, sh);
   if (c.ci == 0 && threadIdx.x == 0) w.stage[n_seq + c.s] = st;
-  if (st.mode == MODE_RADIX) {
-    for (int i = threadIdx.x; i < NB1; i += NT) lh[i] = 0u;
-  }
-  if (threadIdx.x == 0) ncand = 0u;
-  __syncthreads();
   uint16_t* cl = w.cand + (size_t)c.slot * CH;
   int def = 0;
 #pragma unroll
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
         ++def;
       } else if (hi20 == st.prefix) {
         const uint32_t d = key & 0xfffu;
-        atomicAdd(&lh[d], 1u);
+        atomicAdd(&lc[d], 1u);
         const uint32_t at = atomicAdd(&ncand, 1u);   // at most CH candidates per chunk
         cl[at] = (uint16_t)d;
         if (at < (uint32_t)NSMALL) w.slot[c.slot].small[at] = (uint16_t)d;
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(NT) void sel_pass2(const float* __restrict__ b,
   if (st.mode == MODE_RADIX) {
     uint32_t* gh = w.hist2 + (size_t)c.s * NB1;
     for (int i = threadIdx.x; i < NB1; i += NT) {
-      const uint32_t v = lh[i];
+      const uint32_t v = lc[i];
       if (v) atomicAdd(gh + i, v);
     }
   }
