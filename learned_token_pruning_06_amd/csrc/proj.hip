@@ -269,7 +269,9 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
     // fp32 rows leave through LDS (the K loop's tiles are free after its last
     // barrier): per half of the wave's columns, the wave's 64 x 64 block goes
     // to its own 16 KB region, then 16 lanes write 256 contiguous bytes of a
-    // row, 4 rows per store
+    // row, 4 rows per store.  The stores are non-temporal: the outputs (dx is
+    // 1 GiB at 131072 rows) stream out once and would otherwise leave dirty
+    // lines in the L2 for the next kernel to write back.
     constexpr int kLd = 68;                      // floats per staged row (rows 4 banks apart)
     float* stage = reinterpret_cast<float*>(wv < 4 ? &sx[0][0] : &sw[0][0]) + (wv & 3) * 64 * kLd;
     // row correction (CORR): once a half is staged, the lane's A values
@@ -315,7 +317,11 @@ __global__ __launch_bounds__(kThreads) void gemm_abt_bf16(
             v4.z = fmaf(-cv[j], __uint_as_float(av[j].y << 16), v4.z);
             v4.w = fmaf(-cv[j], __uint_as_float(av[j].y & 0xffff0000u), v4.w);
           }
-          if (row < t) *reinterpret_cast<float4*>(y + row * ldy + col) = v4;
+          if (row < t) {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 o = {v4.x, v4.y, v4.z, v4.w};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(y + row * ldy + col));
+          }
         }
       }
     }
