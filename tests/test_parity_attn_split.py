@@ -235,3 +235,40 @@ def test_split_random_shapes(case):
     check_attn(got, O.ref_gated_attn(q, k, v, kb, pos, kc, gain, temp), "bf16",
                f"split random {seed}")
     _check_lse2(lse2, c, f"split random {seed}")
+
+
+def test_budget_sweep_every_budget_plain_and_split():
+    """The 32k budget sweep (preset scores with ties and +6 spikes, eight
+    budgets drawn log-uniformly): for every budget, the oracle's kept set and
+    projections, then both tg_gated_attn and tg_gated_attn_split on every
+    kept row against the oracle on the same rounded inputs, and the split
+    form's lse2.  Kept sets of one score vector are nested (ties go to the
+    lower index), so the rows are projected once, for the largest budget.
+    Budgets past 8192 kept document tokens are left to the plain path's
+    largest-budget test (test_parity_attn.py): one sequence that long leaves
+    no block longer than a workgroup's share, so both forms make the same
+    single launch."""
+    from test_parity_attn import run_attn
+    g = workload(2)
+    wl = g["wl"]
+    b = g["b_preset"].astype(np.float32)
+    budgets = [np.asarray(k, np.int32) for k in g["budgets"]]
+    big = max(budgets, key=lambda k: int(k[0]))
+    idx_all, _, _, _ = O.ref_select(b, g["prunable"], g["cu_seqlens"], big)
+    xd = bf16_to_f64(g["x"][idx_all])
+    q_all, k_all, v_all = O.ref_project(xd, bf16_to_f64(g["wq"]), bf16_to_f64(g["wk"]),
+                                        bf16_to_f64(g["wv"]), wl.hq, wl.hkv, wl.dh)
+    q_all, k_all, v_all = (bf16_to_f64(round_bf16(a)) for a in (q_all, k_all, v_all))
+    for kk in budgets:
+        if int(kk[0]) > 8192:
+            continue
+        idx, pos, kb, kc = O.ref_select(b, g["prunable"], g["cu_seqlens"], kk)
+        at = np.searchsorted(idx_all, idx)
+        assert np.array_equal(idx_all[at], idx), "kept sets are nested"
+        c = (q_all[at], k_all[at], v_all[at], kb, pos, kc, g["gain"], g["temp"])
+        say(f"attn sweep: K={int(kk[0])}, {idx.size} kept rows")
+        ref = O.ref_gated_attn(*c)
+        check_attn(run_attn(*c, "bf16"), ref, "bf16", f"sweep K={int(kk[0])}, plain")
+        got, lse2, _ = _run_split(c)
+        check_attn(got, ref, "bf16", f"sweep K={int(kk[0])}, split")
+        _check_lse2(lse2, c, f"sweep K={int(kk[0])}, split")
