@@ -30,10 +30,13 @@
 //  - the softmax normaliser sums the bf16-rounded probabilities that enter
 //    the P.V product (v_dot2 against (1, 1)), so numerator and denominator
 //    carry the same weights;
-//  - K/V/bias tiles rotate through three LDS buffers: tile t+1 is fetched
-//    from HBM into registers (buffer loads whose range ends at the
-//    sequence's last row, so a partial last tile reads zeros) while tile t
-//    is computed;
+//  - K/V tiles rotate through three LDS buffers (one LDS array each): tile
+//    t+1 goes from HBM straight into the LDS (buffer loads that write the
+//    LDS, whose range ends at the sequence's last row, so a partial last
+//    tile reads zeros) while tile t is computed; rows are 2*DH bytes with
+//    their 16-byte chunks permuted per row (XOR swizzle), so the operand
+//    reads hit distinct banks without padding.  The keys' bias columns sit
+//    in a small array of their own, written from registers;
 //  - the two waves that share a SIMD run half a tile apart (one does
 //    S then P.V of tile t, the other P.V of tile t-1 then S of tile t), so
 //    the matrix products of one overlap the softmax of the other;
@@ -117,9 +120,6 @@ TG_DEVINL float dot2_ones(uint32_t w, float acc) {
 TG_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-TG_DEVINL u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 TG_DEVINL float buf_ldf(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -128,21 +128,26 @@ template <int DH, int HPW, int NWAVE>
 struct AttnCfg {
   static constexpr int NTHR = 64 * NWAVE;        // threads per workgroup
   static constexpr int QB = NWAVE * QW / HPW;    // query rows per workgroup
-  static constexpr int KROW = DH + 24;           // K row: DH values, 16 bias columns, 8 pad
-  // V row: DH values, 32 pad.  V is read only by transposing 8-byte reads,
-  // which the LDS serves 32 lanes (256 B) at a time: lanes 0..31 address
-  // rows r = 0..3 at byte 32h + 8c (h = 0, 1; c = 0..3), so rows must start
-  // 64 B apart mod 256 B for the 32 addresses to fall on distinct banks.
-  // (With rows 32 B apart, 27% of the kernel's LDS-active cycles were bank
-  // conflicts.)
-  static constexpr int VROW = DH + 32;
+  static constexpr int KROW = DH;                // K row: DH values (bias columns apart)
+  static constexpr int VROW = DH;                // V row: DH values
   static constexpr int KT = DH / 16;             // MFMA K-steps over the head dim
   static constexpr int DT = DH / 32;             // output tiles over the head dim
-  static constexpr int KVEC = BKV * DH / 8;      // 16-byte vectors per K tile
-  static constexpr int KVPT = (KVEC + NTHR - 1) / NTHR;
-  static constexpr int VVPT = (KVEC + NTHR - 1) / NTHR;  // V: same 16-byte vectors as K
   static constexpr int KTILE = BKV * KROW;       // bf16 per K buffer
-  static constexpr int VTILE = BKV * VROW;       // bf16 per V buffer (row-major)
+  static constexpr int VTILE = BKV * VROW;       // bf16 per V buffer
+  static constexpr int BTILE = BKV * 16;         // bf16 per bias buffer (16 per key)
+  static constexpr int CPR = DH / 8;             // 16-byte chunks per row
+  static constexpr int RPB = 1024 / (2 * DH);    // rows per 1 KB DMA block
+  static constexpr int RW = 256 / (2 * DH);      // rows per 256 B of LDS
+  static constexpr int NBLK = BKV / RPB;         // DMA blocks per tile
+  static constexpr int KDMA = NBLK / NWAVE;      // DMA instructions per wave and tile, each of K and V
+  // Logical 16-byte chunk c of row r is stored at chunk c ^ fk(r) (K) or
+  // c ^ fv(r) (V).  The LDS serves 256 B per cycle.  A K read (16 bytes per
+  // lane) has 16 lanes on 16 rows at one chunk: fk spreads them over the 16
+  // chunk slots of 256 B.  A V read (transposing, 8 bytes per lane) has 32
+  // lanes on 4 rows at chunks 4dt + 0..3: fv moves each of the 4 rows to
+  // its own group of 4 chunks.
+  static __device__ __forceinline__ int fk(int r) { return (r / RW) & (CPR - 1); }
+  static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RW) & (CPR / 4 - 1)); }
 };
 
 template <int DH, int HPW, int NWAVE, bool SPLIT>
@@ -152,10 +157,20 @@ __device__ __forceinline__ void gated_attn_item(
     const int32_t* __restrict__ kept_pos, const int32_t* __restrict__ kept_cu, int n_seq,
     int t_kept, int hq, int hkv, int groups_y, int hg, int64_t slot,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale,
-    float* __restrict__ lse2, uint16_t* sk, uint16_t* sv, int chunk_tiles, int c_max, int chunk,
+    float* __restrict__ lse2, uint16_t* sk0, uint16_t* sk1, uint16_t* sk2, uint16_t* sv0,
+    uint16_t* sv1, uint16_t* sv2, uint16_t* sb, int chunk_tiles, int c_max, int chunk,
     uint16_t* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
-  constexpr int NTHR = C::NTHR;
+  // one LDS array per buffer, so that reads of one buffer need not wait for
+  // the DMA into another
+  auto kbuf = [&](auto BUFC) {
+    constexpr int B = decltype(BUFC)::value;
+    return B == 0 ? sk0 : (B == 1 ? sk1 : sk2);
+  };
+  auto vbuf = [&](auto BUFC) {
+    constexpr int B = decltype(BUFC)::value;
+    return B == 0 ? sv0 : (B == 1 ? sv1 : sv2);
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
@@ -226,25 +241,24 @@ __device__ __forceinline__ void gated_attn_item(
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsc[i] = i < HPW ? gain[hbase + i] / sm_scale : 0.0f;
 
-  // K and V: 16-byte vectors tid + i*NTHR of the tile (row, 8-element
-  // chunk), to LDS row-major with their padded row strides.  Offsets in
-  // global memory are bytes from the tile's first row (rows of k and v are
-  // kvstride elements apart).
-  int koff[C::KVPT], kdst[C::KVPT], vdst[C::KVPT];
+  // K and V tiles by DMA (buffer loads that write the LDS): instruction i of
+  // a wave fills the 1 KB block b = wave + NWAVE * i of the tile, rows
+  // RPB * b .. +RPB; lane l brings row RPB * b + l / CPR into physical chunk
+  // l % CPR, i.e. the logical chunk that the row's swizzle puts there.
+  // Offsets are bytes from the tile's first row in global memory.
+  static_assert(C::NBLK % NWAVE == 0, "DMA blocks per wave");
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  int kvo[C::KDMA], vvo[C::KDMA];
 #pragma unroll
-  for (int i = 0; i < C::KVPT; ++i) {
-    const int kvi = (tid + i * NTHR) % C::KVEC;
-    const int row = kvi / (DH / 8), col = 8 * (kvi % (DH / 8));
-    koff[i] = (row * (int)kvstride + col) * 2;
-    kdst[i] = row * C::KROW + col;
-    vdst[i] = row * C::VROW + col;
+  for (int i = 0; i < C::KDMA; ++i) {
+    const int row = C::RPB * (wvu + NWAVE * i) + lane / C::CPR, p = lane % C::CPR;
+    kvo[i] = (row * (int)kvstride + 8 * (p ^ C::fk(row))) * 2;
+    vvo[i] = (row * (int)kvstride + 8 * (p ^ C::fv(row))) * 2;
   }
   const int boff = (tid % BKV) * 4;
-
-  u32x4 kreg[C::KVPT], vreg[C::KVPT];
   float breg = 0.f;
 
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, auto BUFC) {
     const int kv0 = t * BKV;
     const int rows = len - kv0 < BKV ? len - kv0 : BKV;      // rows of this tile in the sequence
     const int64_t off = (int64_t)kv0 * kvstride;
@@ -252,24 +266,21 @@ __device__ __forceinline__ void gated_attn_item(
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb_ + off, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb_ + off, bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(kept_b + lo + kv0, rows * 4);
+    uint16_t* skb = kbuf(BUFC);
+    uint16_t* svb = vbuf(BUFC);
 #pragma unroll
-    for (int i = 0; i < C::KVPT; ++i)
-      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) kreg[i] = buf_ld16(rk, koff[i]);
+    for (int i = 0; i < C::KDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(skb + (wvu + NWAVE * i) * 512), 16, kvo[i], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < C::KVPT; ++i)
-      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) vreg[i] = buf_ld16(rv, koff[i]);
+    for (int i = 0; i < C::KDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(svb + (wvu + NWAVE * i) * 512), 16, vvo[i], 0, 0, 0);
     breg = buf_ldf(rb, boff);
   };
   auto store_tile = [&](auto BUFC) {
     constexpr int BUF = decltype(BUFC)::value;
-    uint16_t* skb = sk + BUF * C::KTILE;
-    uint16_t* svb = sv + BUF * C::VTILE;
-#pragma unroll
-    for (int i = 0; i < C::KVPT; ++i)
-      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) st16(&skb[kdst[i]], kreg[i]);
-#pragma unroll
-    for (int i = 0; i < C::KVPT; ++i)
-      if (C::KVEC % NTHR == 0 || tid + i * NTHR < C::KVEC) st16(&svb[vdst[i]], vreg[i]);
+    uint16_t* sbb = sb + BUF * C::BTILE;
     if (tid < BKV) {
       // bias columns of key tid: (hi, lo) bf16 parts of gain_h * b / s per head
       uint32_t w[4];
@@ -279,19 +290,31 @@ __device__ __forceinline__ void gated_attn_item(
         const float hi = (float)(__bf16)beta;
         w[i] = i < HPW ? pack_bf16x2(hi, beta - hi) : 0u;
       }
-      st16(&skb[tid * C::KROW + DH], (u32x4){w[0], w[1], w[2], w[3]});
-      st16(&skb[tid * C::KROW + DH + 8], (u32x4){0u, 0u, 0u, 0u});
+      st16(&sbb[tid * 16], (u32x4){w[0], w[1], w[2], w[3]});
+      st16(&sbb[tid * 16 + 8], (u32x4){0u, 0u, 0u, 0u});
     }
   };
 
-  // per-lane LDS operand bases: every fragment read is base + constant offset
-  const uint16_t* klane = sk + n * C::KROW + 8 * g;
+  // per-lane LDS operand offsets: a K read is its row's base plus the
+  // swizzled chunk of its K-step, a V read the lane's column plus the
+  // swizzled output tile
+  const int klane = n * C::KROW;
+  const uint16_t* blane = sb + n * 16 + 8 * g;
+  // physical offset of the lane's K chunk 2 st + g (the row's swizzle; rows
+  // n and n + 32 share it)
+  int kcol[C::KT];
+#pragma unroll
+  for (int st = 0; st < C::KT; ++st) kcol[st] = 8 * ((2 * st + g) ^ C::fk(n));
   // V fragments by transposing reads: within each 16-lane group, lane s
   // points at row 4kg + s/4 (kg = lane/32), columns 16((lane/16)%2) + 4(s%4)
   // .. +4; the read hands lane i of the group the 4 keys of that row block
   // at column 16((lane/16)%2) + i, i.e. the A operand of dim lane%32
-  const uint16_t* vlane =
-      sv + (4 * (lane >> 5) + ((lane & 15) >> 2)) * C::VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vrow = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vlane = vrow * C::VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // column of output tile dt in the lane's rows (16kk and 8 keep the swizzle)
+  int vcol[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) vcol[dt] = 32 * (dt ^ (C::fv(vrow) >> 2));
 
   // ---- running state (one query per lane)
   floatx16 oacc[C::DT];
@@ -313,11 +336,12 @@ __device__ __forceinline__ void gated_attn_item(
   auto phase_s = [&](auto BUFC, int t) {
     constexpr int BUF = decltype(BUFC)::value;
     const int kv0 = t * BKV;
-    const uint16_t* kl = klane + BUF * C::KTILE;
+    const uint16_t* kl = kbuf(BUFC) + klane;
+    const uint16_t* bl = blane + BUF * C::BTILE;
     // K fragment j of the tile: key half j & 1, K-step (j >> 1) - 1 (-1: bias columns)
     auto kfrag = [&](int j) {
       const int st = (j >> 1) - 1;
-      return ld16(kl + 32 * (j & 1) * C::KROW + (st < 0 ? DH : 16 * st));
+      return st < 0 ? ld16(bl + 32 * (j & 1) * 16) : ld16(kl + 32 * (j & 1) * C::KROW + kcol[st < 0 ? 0 : st]);
     };
     constexpr int NK = 2 * (C::KT + 1);          // MFMAs of S^T
     u32x4 kr[4];
@@ -392,11 +416,10 @@ __device__ __forceinline__ void gated_attn_item(
   // (A operand: dim 32dt + n, the 8 keys of K-step kk in P^T's order); the
   // V reads run four MFMAs ahead of their use
   auto phase_pv = [&](auto BUFC) {
-    constexpr int BUF = decltype(BUFC)::value;
-    const uint16_t* vl = vlane + BUF * C::VTILE;
+    const uint16_t* vl = vbuf(BUFC) + vlane;
     // keys 16kk + 4kg + 0..3 and 16kk + 8 + 4kg + 0..3 of dims 32dt + lane%32
     auto vfrag = [&](int i) {
-      const uint16_t* p = vl + 16 * (i / C::DT) * C::VROW + 32 * (i % C::DT);
+      const uint16_t* p = vl + 16 * (i / C::DT) * C::VROW + vcol[i % C::DT];
       const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4i16*)(p));
       const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -436,11 +459,11 @@ __device__ __forceinline__ void gated_attn_item(
   // loaded and stored unconditionally, so the Q fragment loads above are
   // complete on every path into the loop and the loop waits for none of them.)
   const int wt = w_tiles - t_lo;
-  load_tile(t_lo);
+  load_tile(t_lo, B0{});
   store_tile(B0{});
   __syncthreads();
   auto step = [&](auto BC, auto BP, auto BN, int t) {
-    if (t + 1 < n_tiles) load_tile(t_lo + t + 1);
+    if (t + 1 < n_tiles) load_tile(t_lo + t + 1, BN);
     if (!lag) {
       if (t < wt) {
         phase_s(BC, t_lo + t);
@@ -535,8 +558,9 @@ void gated_attn_bf16(
     float2* __restrict__ ws_ml) {
   using C = AttnCfg<DH, HPW, NWAVE>;
   static_assert(NWAVE % HPW == 0 && C::NTHR >= BKV, "workgroup shape");
-  __shared__ __attribute__((aligned(16))) uint16_t sk[NBUF * C::KTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[NBUF * C::VTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk0[C::KTILE], sk1[C::KTILE], sk2[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv0[C::VTILE], sv1[C::VTILE], sv2[C::VTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[NBUF * C::BTILE];
 
   // ---- persistent workgroups: the head group comes from the low bits of the
   // block index (blocks are dealt round-robin over the 8 XCDs, so the blocks
@@ -564,7 +588,7 @@ void gated_attn_bf16(
       if (rank >= n_real) break;
       gated_attn_item<DH, HPW, NWAVE, false>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq,
                                              t_kept, hq, hkv, groups_y, hg, n_real - 1 - rank,
-                                             gain, temp, sm_scale, lse2, sk, sv, 0, 1, 0, nullptr,
+                                             gain, temp, sm_scale, lse2, sk0, sk1, sk2, sv0, sv1, sv2, sb, 0, 1, 0, nullptr,
                                              nullptr);
       __syncthreads();                             // LDS buffers are reused by the next slot
     }
@@ -580,7 +604,7 @@ void gated_attn_bf16(
       const int code = list[r];
       gated_attn_item<DH, HPW, NWAVE, true>(q, k, v, out, kept_b, kept_pos, kept_cu, n_seq, t_kept,
                                             hq, hkv, groups_y, hg, code >> 3, gain, temp, sm_scale,
-                                            lse2, sk, sv, chunk_tiles, c_max, code & 7, ws_o,
+                                            lse2, sk0, sk1, sk2, sv0, sv1, sv2, sb, chunk_tiles, c_max, code & 7, ws_o,
                                             ws_ml);
       __syncthreads();                               // LDS buffers are reused by the next item
     }
